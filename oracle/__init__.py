@@ -1,0 +1,14 @@
+"""Float64 CPU oracle for the RWKV-4 WKV operator.
+
+TEST INFRASTRUCTURE ONLY: used by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.  See wkv_ref.py for
+the sources each function follows and the readings taken where the pages are
+silent.
+"""
+from .wkv_ref import (  # noqa: F401
+    wkv_backward_ref,
+    wkv_direct_ref,
+    wkv_forward_ref,
+    wkv_state_from_sums,
+    wkv_step_ref,
+)

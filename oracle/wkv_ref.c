@@ -1,0 +1,166 @@
+/*
+ * Float64 C twin of the WKV oracle (oracle/wkv_ref.py), for workloads too
+ * large for the numpy loops: the decode-state seeding of 32 x 256 x 4096
+ * lanes and the CPU baseline timing.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py load this library; the HIP product path never
+ * links or calls it, and it shares no code with it.
+ *
+ * It computes the same plain (unscaled) float64 recurrences as the numpy
+ * oracle, one lane (b, c) at a time, lanes spread over OpenMP threads:
+ *
+ *   "RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", sections
+ *   "一句话总结" and "关键设计 2：WKV 算子":
+ *       y_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t})
+ *       A_t = e^{-w} A_{t-1} + e^{k_t} v_t,  B_t = e^{-w} B_{t-1} + e^{k_t}
+ *   with A_0 = B_0 = 0.  The backward is the derivative of the weighted sum
+ *   of "RWKV（Receptance Weighted Key Value）概念", section 3.2, written as
+ *   the reverse recurrences documented in wkv_ref.py (wkv_backward_ref).
+ *
+ * Inputs are float32 arrays (exact copies of the fp32 or bf16-rounded values
+ * the GPU consumes) and are promoted to double; every sum is double.
+ * Layout: k, v, gy, y, dk, dv are [B, T, C] with C fastest; w, u are [C].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int wkv_ref_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Forward.  y (nullable) receives [B,T,C] doubles; A_out, B_out (nullable)
+ * receive the final plain sums [B,C].  Returns the number of threads used. */
+int wkv_ref_forward(int64_t B, int64_t T, int64_t C, const float* w,
+                    const float* u, const float* k, const float* v, double* y,
+                    double* A_out, double* B_out, int nthreads) {
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+#pragma omp for collapse(2) schedule(static)
+#endif
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t c = 0; c < C; ++c) {
+                const double d = exp(-(double)w[c]);
+                const double eu = exp((double)u[c]);
+                double A = 0.0, Bs = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    const int64_t i = (b * T + t) * C + c;
+                    const double ek = exp((double)k[i]);
+                    const double cur = eu * ek;
+                    const double vt = (double)v[i];
+                    if (y) y[i] = (A + cur * vt) / (Bs + cur);
+                    A = d * A + ek * vt;
+                    Bs = d * Bs + ek;
+                }
+                if (A_out) A_out[b * C + c] = A;
+                if (B_out) B_out[b * C + c] = Bs;
+            }
+        }
+#ifdef _OPENMP
+    }
+#endif
+    return used;
+}
+
+/* Backward of L = sum(gy * y).  dk, dv: [B,T,C] doubles; dw, du: [C] doubles
+ * (summed over b and t).  Returns the number of threads used, or -1 when a
+ * scratch allocation fails. */
+int wkv_ref_backward(int64_t B, int64_t T, int64_t C, const float* w,
+                     const float* u, const float* k, const float* v,
+                     const float* gy, double* dk, double* dv, double* dw,
+                     double* du, int nthreads) {
+    int used = 1, failed = 0;
+    double* dw_lane = (double*)calloc((size_t)(B * C), sizeof(double));
+    double* du_lane = (double*)calloc((size_t)(B * C), sizeof(double));
+    if (!dw_lane || !du_lane) {
+        free(dw_lane);
+        free(du_lane);
+        return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double* ys = (double*)malloc((size_t)T * sizeof(double));
+        double* Ds = (double*)malloc((size_t)T * sizeof(double));
+        if (!ys || !Ds) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for collapse(2) schedule(static)
+#endif
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t c = 0; c < C; ++c) {
+                if (!ys || !Ds) continue;
+                const double d = exp(-(double)w[c]);
+                const double eu = exp((double)u[c]);
+                double A = 0.0, Bs = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    const int64_t i = (b * T + t) * C + c;
+                    const double ek = exp((double)k[i]);
+                    const double cur = eu * ek;
+                    const double vt = (double)v[i];
+                    Ds[t] = Bs + cur;
+                    ys[t] = (A + cur * vt) / Ds[t];
+                    A = d * A + ek * vt;
+                    Bs = d * Bs + ek;
+                }
+                double G = 0.0, H = 0.0, Gp = 0.0, Hp = 0.0;
+                double dwl = 0.0, dul = 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    const int64_t i = (b * T + t) * C + c;
+                    const double ek = exp((double)k[i]);
+                    const double pi = eu * ek / Ds[t];
+                    const double gt = (double)gy[i], vt = (double)v[i];
+                    const double yt = ys[t];
+                    const double cur_k = gt * pi * (vt - yt);
+                    dv[i] = gt * pi + ek * G;
+                    dk[i] = cur_k + ek * (vt * G - H);
+                    dul += cur_k;
+                    dwl -= ek * (vt * Gp - Hp);
+                    Gp = d * (Gp + G);
+                    Hp = d * (Hp + H);
+                    G = d * G + gt / Ds[t];
+                    H = d * H + gt * yt / Ds[t];
+                }
+                dw_lane[b * C + c] = dwl;
+                du_lane[b * C + c] = dul;
+            }
+        }
+        free(ys);
+        free(Ds);
+#ifdef _OPENMP
+    }
+#endif
+    for (int64_t c = 0; c < C; ++c) {
+        double sw = 0.0, su = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            sw += dw_lane[b * C + c];
+            su += du_lane[b * C + c];
+        }
+        dw[c] = sw;
+        du[c] = su;
+    }
+    free(dw_lane);
+    free(du_lane);
+    return failed ? -1 : used;
+}
