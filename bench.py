@@ -1,0 +1,249 @@
+"""Benchmark of the WKV operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fwdbwd]
+
+Default workload (the headline): forward + backward of the RWKV-4 WKV
+operator at the 7B-model shape B=8, T=1024, C=4096 with bf16 k, v, gy and
+float32 w, u, outputs and arithmetic.  One step = wkv_forward (saving block
+states) + wkv_backward on one batch of synthetic inputs already resident in
+HBM.  Several copies of the inputs/outputs are rotated so that a step never
+finds its operands in the 256 MB last-level (Infinity) cache.
+
+Prints ONE JSON line (rank 0, N=1) with the throughput in channel*tokens/s,
+the per-kernel roofline of the dominant kernel (HIP events on the stream the
+kernels run on) and the float64 CPU oracle timed on this host.
+
+Other workloads (not the headline, for measurements quoted in the design
+notes): fwd2 (B=8 T=1024 C=768 fp32, fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32,
+forward only), step5 (32 layers x 256 streams x 4096 channels decode step).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "WKV fwd+bwd channel·tokens/s and HBM GB/s (% of peak), B=8 T=1024 C=4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd2", "fwd4", "step5"])
+    ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    return ap.parse_args()
+
+
+def upload(p, dev):
+    import torch
+
+    def up(x, bits=None):
+        if bits is not None:
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+    d = {"w": up(p.w), "u": up(p.u)}
+    for n in ("k", "v", "gy"):
+        if getattr(p, n) is None:
+            continue
+        d[n] = up(getattr(p, n), getattr(p, n + "_bits") if p.dtype == "bf16" else None)
+    return d
+
+
+def cpu_oracle_fwdbwd(p, with_bwd=True):
+    """The float64 numpy oracle (single thread) on the same inputs."""
+    from oracle import wkv_backward_ref, wkv_forward_ref
+
+    t0 = time.perf_counter()
+    wkv_forward_ref(p.w, p.u, p.k, p.v)
+    if with_bwd:
+        wkv_backward_ref(p.w, p.u, p.k, p.v, p.gy)
+    return time.perf_counter() - t0
+
+
+def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops
+
+    dev = torch.device("cuda:0")
+    base = upload(p, dev)
+    B, T, C = p.B, p.T, p.C
+    sets = []
+    for i in range(args.sets):
+        s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
+        s["y"] = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        s["ck"] = ops.new_ckpt(B, T, C, dev)
+        if with_bwd:
+            s["out"] = (torch.empty((B, T, C), dtype=torch.float32, device=dev),
+                        torch.empty((B, T, C), dtype=torch.float32, device=dev),
+                        torch.empty((C,), dtype=torch.float32, device=dev),
+                        torch.empty((C,), dtype=torch.float32, device=dev))
+        sets.append(s)
+    ws_f = torch.empty(max(1, ops.workspace_bytes(0, B, T, C, base["k"].dtype)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, ops.workspace_bytes(1, B, T, C, base["k"].dtype)), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        ops.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=s["y"], ckpt=s["ck"], workspace=ws_f)
+        if ev is not None:
+            ev[1].record()
+        if with_bwd:
+            ops.wkv_backward(s["w"], s["u"], s["k"], s["v"], s["gy"], ckpt=s["ck"], out=s["out"],
+                             workspace=ws_b)
+            if ev is not None:
+                ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, wall clock, synchronised on both sides
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations with HIP events on the stream the kernels run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if with_bwd else 0.0
+
+    n = p.n
+    ms = wall * 1e3 / args.steps
+    value = n / (wall / args.steps)
+    alg_bytes = (bytes_fwd + (bytes_bwd if with_bwd else 0)) * n
+    if with_bwd and bwd_ms >= fwd_ms:
+        dom, dom_ms, dom_bytes = "wkv_backward", bwd_ms, bytes_bwd * n
+    else:
+        dom, dom_ms, dom_bytes = "wkv_forward", fwd_ms, bytes_fwd * n
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC if workload_name == "fwdbwd" else f"WKV {'fwd+bwd' if with_bwd else 'fwd'} channel·tokens/s, {p.name}",
+        "value": value,
+        "unit": "channel·tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": p.name + (" fwd+bwd" if with_bwd else " fwd"), "B": B, "T": T, "C": C,
+                   "in_dtype": p.dtype},
+        "hbm_gbps_algorithmic": alg_bytes / (wall / args.steps) / 1e9,
+        "pct_hbm_peak": 100.0 * alg_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS,
+        "kernel_ms": {"wkv_forward": fwd_ms, "wkv_backward": bwd_ms},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": dom_bytes},
+    }
+    return out
+
+
+def bench_step5(args):
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops, workloads as W
+
+    dev = torch.device("cuda:0")
+    Lr, Bs, C = 32, 256, 4096
+    rng = np.random.default_rng(0)
+    w = torch.from_numpy(np.exp(rng.uniform(-6, 1.5, (Lr, C))).astype(np.float32)).to(dev)
+    u = torch.from_numpy(rng.normal(0, 1, (Lr, C)).astype(np.float32)).to(dev)
+    dp = W.DecodeProblem(Lr, Bs, C, 0, None, None, None, None, seed=0)
+    sets = []
+    for i in range(args.sets):
+        k, v = W.step_inputs_torch(dp, i, dev)
+        a = torch.randn((Lr, Bs, C), device=dev)
+        b = torch.rand((Lr, Bs, C), device=dev) + 0.5
+        p = torch.randn((Lr, Bs, C), device=dev)
+        y = torch.empty((Lr, Bs, C), device=dev)
+        sets.append((k, v, a, b, p, y))
+
+    def step(i):
+        k, v, a, b, p, y = sets[i % len(sets)]
+        ops.wkv_step(w, u, k, v, a, b, p, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    n = Lr * Bs * C
+    achieved = 32 * n / (kms * 1e-3) / 1e9
+    return {
+        "metric": "WKV decode step lane-steps/s, L=32 B=256 C=4096 bf16 k,v",
+        "value": n / (wall / args.steps), "unit": "lane·steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": "wkv4 decode step L=32 B=256 C=4096 bf16"},
+        "roofline": {"bound": "hbm", "kernel": "wkv_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": 32 * n},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1 (the operator "
+                          "shards by batch/channel with no exchange; see the design notes)"}))
+        sys.exit(2)
+    import torch
+
+    from rwkv_wkv_mixing_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.workload == "step5":
+        out = bench_step5(args)
+        print(json.dumps(out), flush=True)
+        return
+    if args.workload == "fwdbwd":
+        p, with_bwd, bf, bb = W.config3(), True, 8, 14
+    elif args.workload == "fwd2":
+        p, with_bwd, bf, bb = W.config2(), True, 12, 20
+    else:
+        p, with_bwd, bf, bb = W.config4(), False, 12, 0
+    out = bench_seq(args, p, with_bwd, args.workload, bf, bb)
+    if not args.no_cpu:
+        cpu_s = cpu_oracle_fwdbwd(p, with_bwd)
+        out["cpu_baseline"] = {"value": p.n / cpu_s, "unit": "channel·tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the whole workload ({p.n} channel*tokens, "
+                                         f"{'fwd+bwd' if with_bwd else 'fwd'}), numpy float64 oracle, "
+                                         f"{cpu_s:.2f} s on one host core"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

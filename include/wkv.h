@@ -1,0 +1,180 @@
+/*
+ * wkv.h - C ABI of the RWKV-4 WKV time-mixing operator for AMD MI355X (gfx950).
+ *
+ * The operator, per channel c of each batch row b, tokens t = 1..T
+ * ("RWKV（Receptance Weighted Key Value）概念", section 3.2; and
+ *  "RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", sections
+ *  "一句话总结" and "关键设计 2：WKV 算子"):
+ *
+ *     y_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t})
+ *     A_t = e^{-w} A_{t-1} + e^{k_t} v_t,    B_t = e^{-w} B_{t-1} + e^{k_t}
+ *     A_0 = B_0 = 0 (empty history)
+ *
+ * w is the per-channel decay RATE (decay factor e^{-w}), u the per-channel
+ * bonus of the current token.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) of the GPU
+ *    that is current on the calling thread.  Tensors are dense, row-major,
+ *    channel dimension fastest: sequences are [B, T, C], decode tensors
+ *    [L, B, C], parameters [C] (or [L, C] for wkv_step).
+ *  - Inputs k, v, gy have dtype WKV_F32 (float) or WKV_BF16 (bfloat16 bits,
+ *    uint16).  w, u, all outputs and all states are float32.
+ *  - Every call only enqueues work on `hip_stream` (a hipStream_t; NULL means
+ *    the default stream) and returns without synchronising.  Errors from
+ *    the kernels themselves surface at the caller's next synchronisation.
+ *  - The library allocates no device memory and keeps no global state:
+ *    scratch memory is the caller's `workspace`, sized by
+ *    wkv_workspace_bytes().  Calls on disjoint buffers are thread-safe.
+ *    Two calls that share a workspace must be ordered (same stream).
+ *  - Status codes: nothing aborts and no exception crosses the ABI.
+ *    WKV_EINVAL    a dimension < 0, or a NULL pointer where data is needed;
+ *    WKV_EDTYPE    unknown input dtype or op;
+ *    WKV_ESIZE     an element or byte count overflows int64, or the lane
+ *                  count (B*C, or L*B*C) reaches 2^39;
+ *    WKV_EALIGN    a pointer not aligned to its element size;
+ *    WKV_EWORKSPACE workspace NULL or smaller than wkv_workspace_bytes();
+ *    WKV_EHIP      a HIP launch or query failed (wkv_last_hip_error() has
+ *                  the HIP message of the last such failure on this thread).
+ *    A call with B, T, C (or L) equal to 0 is a no-op returning WKV_OK,
+ *    except that wkv_backward with C > 0 and B*T == 0 sets dw = du = 0.
+ *  - Numerics: float32 arithmetic with a float32 running log-scale.  The
+ *    decay e^{-w} is applied as a two-term (hi + lo) product so that no
+ *    systematic rounding of the decay builds up over long sequences.
+ *    Results are finite for finite inputs with w >= 0, |u| <= 80 and
+ *    |v| < 2^60; outside that range the math is still defined but may
+ *    overflow.  NaN/Inf inputs propagate.  For decay rates w below ~1e-5
+ *    the per-token float32 rounding of the state itself changes by only a
+ *    few ulps per token and no longer averages out; float32 state then
+ *    limits the forward to roughly 1e-4 relative error on such channels.
+ */
+#ifndef WKV_MI355X_H
+#define WKV_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int wkv_status_t;
+
+enum {
+    WKV_OK = 0,
+    WKV_EINVAL = 1,
+    WKV_EDTYPE = 2,
+    WKV_ESIZE = 3,
+    WKV_EALIGN = 4,
+    WKV_EWORKSPACE = 5,
+    WKV_EHIP = 6
+};
+
+/* dtype of the INPUT sequences k, v, gy. */
+enum { WKV_F32 = 0, WKV_BF16 = 1 };
+
+/* op selector for wkv_workspace_bytes. */
+enum { WKV_OP_FORWARD = 0, WKV_OP_BACKWARD = 1 };
+
+/* Length, in tokens, of the blocks whose start states wkv_forward can save
+ * for wkv_backward (see `ckpt`). */
+#define WKV_CKPT_LEN 64
+
+/* Bytes of scratch memory a call needs (0 is possible).  Returns 0 for
+ * invalid arguments.  The value depends only on (op, B, T, C, in_dtype). */
+size_t wkv_workspace_bytes(int op, int64_t B, int64_t T, int64_t C, int in_dtype);
+
+/* Bytes of a forward-state checkpoint buffer for a [B, T, C] sequence:
+ * 3 float32 per (b, block, c) with ceil(T / WKV_CKPT_LEN) blocks.  The
+ * contents are opaque: only wkv_backward reads them. */
+size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C);
+
+/*
+ * wkv_forward - the whole-sequence (time-parallel) forward.
+ *
+ * Defines: y_t above for every (b, t, c); the history starts empty.
+ *   "RWKV（Receptance Weighted Key Value）概念" section 3.2 (weighted sum),
+ *   equivalently the recurrence of "RWKV - 把 RNN 重新带回 Transformer 时代的
+ *   线性大模型" section "关键设计 2"; section "关键设计 4" names this
+ *   time-parallel mode for training.
+ *
+ * B, T, C   batch rows, tokens, channels (>= 0).
+ * in_dtype  WKV_F32 or WKV_BF16: dtype of k and v.
+ * w, u      [C] float32: decay rate and current-token bonus.
+ * k, v      [B, T, C] keys and values (in_dtype).
+ * y         [B, T, C] float32 output, fully overwritten; must not alias inputs.
+ * ckpt      NULL, or a buffer of wkv_ckpt_bytes(B, T, C) bytes that receives
+ *           the state at the start of each WKV_CKPT_LEN-token block, for a
+ *           later wkv_backward on the same inputs.
+ * workspace wkv_workspace_bytes(WKV_OP_FORWARD, ...) bytes (may be NULL if
+ *           that is 0).  Contents on entry are ignored.
+ */
+wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype,
+                         const float* w, const float* u, const void* k, const void* v,
+                         float* y, void* ckpt, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
+/*
+ * wkv_backward - gradients of L = sum_{b,t,c} gy * y through the forward.
+ *
+ * Defines (derived by differentiating the section-3.2 weighted sum of
+ * "RWKV（Receptance Weighted Key Value）概念"; the pages print no backward):
+ *   dk = dL/dk, dv = dL/dv   [B, T, C] float32, fully overwritten;
+ *   dw = dL/dw, du = dL/du   [C] float32, summed over b and t, overwritten
+ *                            (not accumulated into).
+ * The forward is recomputed on chip from k, v (no saved activations), which
+ * is the fused forward+backward design named on "rwkv-cuda linear attention
+ * gpu" (ainews.cool).  If `ckpt` is non-NULL it must hold what wkv_forward
+ * wrote for exactly these B, T, C, in_dtype, w, u, k, v; the backward then
+ * skips recomputing the block start states.  gy has dtype in_dtype.
+ * dw and du are reduced in a fixed order: results are bitwise reproducible
+ * from run to run on the same GPU.
+ */
+wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype,
+                          const float* w, const float* u, const void* k, const void* v,
+                          const void* gy, float* dk, float* dv, float* dw, float* du,
+                          const void* ckpt, void* workspace, size_t workspace_bytes,
+                          void* hip_stream);
+
+/*
+ * wkv_step - one recurrent-mode (decode) token for L x B independent states.
+ *
+ * Defines ("RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", section
+ * "关键设计 4：双执行模式"; state tuple in section "整体架构"): with the
+ * state carried as (a, b, p), A = a e^p and B = b e^p,
+ *     y  = (A + e^{u+k} v) / (B + e^{u+k})        (from the previous state)
+ *     A' = e^{-w} A + e^{k} v,  B' = e^{-w} B + e^{k}
+ * The exponent p is the stability exponent of that section: it is moved to
+ * the running max max(k, p + ln b) whenever a new key exceeds it by more than
+ * e^22 or b leaves [2^-32, 2^32], so that no exponential overflows; between
+ * such moves the decay is applied to (a, b).  Callers must therefore compare
+ * states through a/b and ln(b) + p, never the raw triples.
+ *
+ * L, B, C   layers, streams, channels (>= 0).  One call advances all L*B
+ *           states by one token.
+ * in_dtype  dtype of k and v.
+ * w, u      [L, C] float32 per-layer parameters.
+ * k, v      [L, B, C] current-token inputs.
+ * y         [L, B, C] float32 output.
+ * a, b, p   [L, B, C] float32 state, read and overwritten in place.  The
+ *           empty state is a = b = 0, p = -1e38 (any p <= -1e30).  Any
+ *           (a e^s, b e^s, p - s) represents the same state.
+ */
+wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype,
+                      const float* w, const float* u, const void* k, const void* v,
+                      float* y, float* a, float* b, float* p, void* hip_stream);
+
+/* Static description of a status code. */
+const char* wkv_status_str(wkv_status_t s);
+
+/* HIP error string of the last WKV_EHIP on this thread ("" if none). */
+const char* wkv_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* wkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV_MI355X_H */

@@ -1,0 +1,167 @@
+// C ABI of the WKV library (declared in include/wkv.h): argument validation,
+// workspace sizing, path selection and kernel launches.  Every check runs on
+// the host before any HIP call, so invalid calls never touch the device.
+#include <stdio.h>
+#include <string.h>
+
+#include "wkv.h"
+#include "wkv_launch.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+wkv_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return WKV_OK;
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s (%d)", hipGetErrorString(e), static_cast<int>(e));
+    return WKV_EHIP;
+}
+
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+    int64_t t;
+    if (__builtin_mul_overflow(a, b, &t)) return false;
+    if (__builtin_mul_overflow(t, c, out)) return false;
+    return true;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool dtype_ok(int dt) { return dt == WKV_F32 || dt == WKV_BF16; }
+
+size_t in_size(int dt) { return dt == WKV_BF16 ? 2 : 4; }
+
+// Largest lane count the 1-D grids index: blocks of 256 threads, grid.x < 2^31.
+constexpr int64_t kMaxLanes = (int64_t{1} << 31) * 256 - 1;
+
+struct Plan {
+    wkv_status_t st;
+    size_t ws_bytes;
+    int64_t N;
+    int64_t nblk;
+};
+
+Plan plan_seq(int op, int64_t B, int64_t T, int64_t C, int dt) {
+    Plan p{WKV_OK, 0, 0, 0};
+    if (B < 0 || T < 0 || C < 0) return Plan{WKV_EINVAL, 0, 0, 0};
+    if (!dtype_ok(dt)) return Plan{WKV_EDTYPE, 0, 0, 0};
+    if (op != WKV_OP_FORWARD && op != WKV_OP_BACKWARD) return Plan{WKV_EDTYPE, 0, 0, 0};
+    if (!mul3(B, T, C, &p.N)) return Plan{WKV_ESIZE, 0, 0, 0};
+    int64_t bytes;
+    if (__builtin_mul_overflow(p.N, int64_t{16}, &bytes)) return Plan{WKV_ESIZE, 0, 0, 0};
+    int64_t lanes;
+    if (__builtin_mul_overflow(B, C, &lanes) || lanes > kMaxLanes) return Plan{WKV_ESIZE, 0, 0, 0};
+    p.nblk = (T + wkv::kCkptLen - 1) / wkv::kCkptLen;
+    if (op == WKV_OP_BACKWARD && p.N > 0) p.ws_bytes = wkv::bwd_seq_workspace_bytes(B, T, C);
+    return p;
+}
+
+__global__ void zero2_kernel(int64_t n, float* a, float* b) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) {
+        a[i] = 0.f;
+        b[i] = 0.f;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wkv_workspace_bytes(int op, int64_t B, int64_t T, int64_t C, int in_dtype) {
+    const Plan p = plan_seq(op, B, T, C, in_dtype);
+    return p.st == WKV_OK ? p.ws_bytes : 0;
+}
+
+size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0) return 0;
+    const int64_t nblk = (T + wkv::kCkptLen - 1) / wkv::kCkptLen;
+    int64_t n;
+    if (!mul3(B, nblk, C, &n)) return 0;
+    if (__builtin_mul_overflow(n, int64_t{12}, &n)) return 0;
+    return static_cast<size_t>(n);
+}
+
+wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                         const float* u, const void* k, const void* v, float* y, void* ckpt,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const Plan p = plan_seq(WKV_OP_FORWARD, B, T, C, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (p.N == 0) return WKV_OK;
+    if (!w || !u || !k || !v || !y) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(k, es) || !aligned(v, es) ||
+        (ckpt && !aligned(ckpt, 4)))
+        return WKV_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return WKV_EWORKSPACE;
+    wkv::FwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, y, ckpt, p.nblk, workspace,
+                   workspace_bytes};
+    return hip_status(wkv::launch_fwd_seq(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                          const float* u, const void* k, const void* v, const void* gy,
+                          float* dk, float* dv, float* dw, float* du, const void* ckpt,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const Plan p = plan_seq(WKV_OP_BACKWARD, B, T, C, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (C == 0) return WKV_OK;
+    if (!dw || !du) return WKV_EINVAL;
+    if (!aligned(dw, 4) || !aligned(du, 4)) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p.N == 0) {  // empty sums: dw = du = 0
+        hipLaunchKernelGGL(zero2_kernel, dim3(static_cast<unsigned>((C + 255) / 256)), dim3(256), 0,
+                           stream, C, dw, du);
+        return hip_status(hipGetLastError());
+    }
+    if (!w || !u || !k || !v || !gy || !dk || !dv) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(dk, 4) || !aligned(dv, 4) ||
+        !aligned(k, es) || !aligned(v, es) || !aligned(gy, es) || (ckpt && !aligned(ckpt, 4)))
+        return WKV_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4)))
+        return WKV_EWORKSPACE;
+    wkv::BwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, gy, dk, dv, dw, du, ckpt, p.nblk,
+                   workspace, workspace_bytes};
+    return hip_status(wkv::launch_bwd_seq(a, stream));
+}
+
+wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype, const float* w,
+                      const float* u, const void* k, const void* v, float* y, float* a, float* b,
+                      float* p, void* hip_stream) {
+    if (L < 0 || B < 0 || C < 0) return WKV_EINVAL;
+    if (!dtype_ok(in_dtype)) return WKV_EDTYPE;
+    int64_t n;
+    if (!mul3(L, B, C, &n)) return WKV_ESIZE;
+    int64_t bytes;
+    if (__builtin_mul_overflow(n, int64_t{16}, &bytes) || n > kMaxLanes) return WKV_ESIZE;
+    if (n == 0) return WKV_OK;
+    if (!w || !u || !k || !v || !y || !a || !b || !p) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(a, 4) || !aligned(b, 4) ||
+        !aligned(p, 4) || !aligned(k, es) || !aligned(v, es))
+        return WKV_EALIGN;
+    const bool vec4 = (C % 4 == 0) && aligned(w, 16) && aligned(u, 16) && aligned(y, 16) &&
+                      aligned(a, 16) && aligned(b, 16) && aligned(p, 16) && aligned(k, 4 * es) &&
+                      aligned(v, 4 * es);
+    wkv::StepArgs s{L, B, C, in_dtype == WKV_BF16, vec4, w, u, k, v, y, a, b, p};
+    return hip_status(wkv::launch_step(s, static_cast<hipStream_t>(hip_stream)));
+}
+
+const char* wkv_status_str(wkv_status_t s) {
+    switch (s) {
+        case WKV_OK: return "ok";
+        case WKV_EINVAL: return "invalid argument (negative dimension or NULL pointer)";
+        case WKV_EDTYPE: return "unknown dtype or op";
+        case WKV_ESIZE: return "size overflow or beyond kernel indexing limits";
+        case WKV_EALIGN: return "pointer not aligned to its element size";
+        case WKV_EWORKSPACE: return "workspace missing or too small";
+        case WKV_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* wkv_last_hip_error(void) { return g_hip_msg; }
+
+const char* wkv_version(void) { return "0.1.0"; }
+
+}  // extern "C"

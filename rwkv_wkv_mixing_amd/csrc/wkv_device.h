@@ -1,0 +1,127 @@
+// Device-side building blocks of the WKV kernels (gfx950).
+//
+// Lane recurrence ("RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型",
+// sections "一句话总结" and "关键设计 2：WKV 算子"):
+//     y_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t})
+//     A_t = d A_{t-1} + e^{k_t} v_t,   B_t = d B_{t-1} + e^{k_t},  d = e^{-w}
+//
+// Representation used on chip.  The state of a lane is (a, b, s) with
+// A = a * 2^s and B = b * 2^s: a float32 log2-scale s plus two float32
+// mantissas ("the stability exponent" of section "关键设计 4", kept in base 2
+// so that every exponential is one v_exp_f32).  Unlike a per-token running
+// max, s only moves on a RESCALE, when a new key would exceed the scale by
+// 2^32 or b leaves [2^-32, 2^32]; in between, the decay is applied to (a, b)
+// as a product with d split into float32 hi + lo parts.  A per-token exponent
+// update p <- p - w would round the same way at every token and act as a
+// systematic error in w that grows with the memory length 1/w; the split
+// product keeps the decay exact to ~2^-48 instead.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr float kL2E = 1.4426950408889634f;   // log2(e)
+constexpr float kLN2 = 0.6931471805599453f;   // ln(2)
+constexpr float kHi = 0x1p32f;               // rescale bounds for b and new terms
+constexpr float kLo = 0x1p-32f;
+constexpr float kBig = 32.0f;                // log2(kHi)
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---- inputs: float32 or bfloat16 (raw bits), widened exactly to float32 ----
+template <typename TIn>
+struct Ld;
+
+template <>
+struct Ld<float> {
+    static __device__ __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
+};
+
+template <>
+struct Ld<uint16_t> {
+    static __device__ __forceinline__ float at(const uint16_t* p, int64_t i) {
+        return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+    }
+};
+
+// ---- per-channel constants -------------------------------------------------
+struct Chan {
+    float dhi, dlo;  // e^{-w} = dhi + dlo (to ~2^-48 relative)
+    float u2;        // u * log2(e)
+};
+
+__device__ __forceinline__ Chan make_chan(float w, float u) {
+    Chan ch;
+    const double dd = exp(-static_cast<double>(w));
+    ch.dhi = static_cast<float>(dd);
+    ch.dlo = static_cast<float>(dd - static_cast<double>(ch.dhi));
+    ch.u2 = u * kL2E;
+    return ch;
+}
+
+// ---- lane state ---------------------------------------------------------------
+struct St {
+    float a, b, s;  // A = a 2^s, B = b 2^s
+};
+
+__device__ __forceinline__ St empty_state() { return St{0.f, 0.f, -INFINITY}; }
+
+// Move the scale so that the new term (k2 = k log2 e) and the state both fit:
+// s' = max(k2, s + log2 b).  Afterwards b <= 1 and the new term is <= 1.
+__device__ __forceinline__ void rescale(St& st, float k2) {
+    const float lvl = st.b > 0.f ? st.s + lg2(st.b) : -INFINITY;
+    const float sn = fmaxf(lvl, k2);
+    const float f = ex2(st.s - sn);
+    st.a *= f;
+    st.b *= f;
+    st.s = sn;
+}
+
+// x = k log2 e - s, rescaling first when the new term or b is out of range.
+__device__ __forceinline__ float key_offset(St& st, float k) {
+    float x = fmaf(k, kL2E, -st.s);
+    if (x > kBig || !(st.b >= kLo) || st.b > kHi) {
+        rescale(st, k * kL2E);
+        x = fmaf(k, kL2E, -st.s);
+    }
+    return x;
+}
+
+// Output of one token from the state before it (robust to any u):
+// z = x + u2 is the log2 weight of the current token relative to 2^s.
+struct Out {
+    float y;
+    float co;  // weight of the history in the normalised fraction (<= 1)
+    float cn;  // weight of the current token (<= 1)
+    float r;   // 1 / (b co + cn)
+};
+
+__device__ __forceinline__ Out token_out(const St& st, float x, float v, const Chan& ch) {
+    const float z = x + ch.u2;
+    const float ez = ex2(-fabsf(z));
+    const bool zp = z > 0.f;
+    Out o;
+    o.co = zp ? ez : 1.f;
+    o.cn = zp ? 1.f : ez;
+    const float D = fmaf(st.b, o.co, o.cn);
+    const float N = fmaf(st.a, o.co, o.cn * v);
+    o.r = rcp(D);
+    o.y = N * o.r;
+    return o;
+}
+
+// Decay-and-add of one token: A <- d A + e^k v, B <- d B + e^k, d = dhi + dlo.
+// Returns e = 2^x = e^{k} / 2^s.
+__device__ __forceinline__ float token_update(St& st, float x, float v, const Chan& ch) {
+    const float e = ex2(x);
+    const float ev = e * v;
+    st.a = fmaf(ch.dhi, st.a, fmaf(ch.dlo, st.a, ev));
+    st.b = fmaf(ch.dhi, st.b, fmaf(ch.dlo, st.b, e));
+    return e;
+}
+
+}  // namespace wkv

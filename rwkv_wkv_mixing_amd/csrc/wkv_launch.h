@@ -1,0 +1,67 @@
+// Host-side launch interface between the C ABI (wkv_api.hip) and the kernel
+// translation units.  Internal to the library; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr int64_t kCkptLen = 64;  // = WKV_CKPT_LEN in include/wkv.h
+
+struct FwdArgs {
+    int64_t B, T, C;
+    bool bf16;
+    const float* w;
+    const float* u;
+    const void* k;
+    const void* v;
+    float* y;
+    void* ckpt;     // nullable
+    int64_t nblk;   // ceil(T / kCkptLen)
+    void* ws;
+    size_t ws_bytes;
+};
+
+struct BwdArgs {
+    int64_t B, T, C;
+    bool bf16;
+    const float* w;
+    const float* u;
+    const void* k;
+    const void* v;
+    const void* gy;
+    float* dk;
+    float* dv;
+    float* dw;
+    float* du;
+    const void* ckpt;  // nullable
+    int64_t nblk;
+    void* ws;
+    size_t ws_bytes;
+};
+
+struct StepArgs {
+    int64_t L, B, C;
+    bool bf16;
+    bool vec4;
+    const float* w;
+    const float* u;
+    const void* k;
+    const void* v;
+    float* y;
+    float* a;
+    float* b;
+    float* p;
+};
+
+// lane-sequential kernels (wkv_seq.hip)
+hipError_t launch_fwd_seq(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_seq(const BwdArgs& a, hipStream_t stream);
+size_t bwd_seq_workspace_bytes(int64_t B, int64_t T, int64_t C);
+
+// decode step (wkv_step.hip)
+hipError_t launch_step(const StepArgs& s, hipStream_t stream);
+
+}  // namespace wkv

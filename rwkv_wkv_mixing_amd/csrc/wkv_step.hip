@@ -1,0 +1,179 @@
+// Recurrent-mode (decode) step: one token for L x B independent WKV states.
+//
+// "RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", section "关键设计 4"
+// (output read from the previous state, then decay-and-add).  The state is
+// (a, b, p) with A = a e^p, B = b e^p.  As in the sequence kernels, the
+// exponent p only moves on a rescale (a new key more than e^22 above it, or
+// b outside [2^-32, 2^32]), where it jumps to the running max
+// max(k, p + ln b); the decay itself is applied to (a, b) as a product with
+// e^{-w} split into float32 hi + lo parts, so no per-token rounding of p - w
+// acts as a systematic change of w.
+//
+// Memory-bound: 32 bytes per lane for bf16 inputs (read a, b, p, k, v; write
+// y, a, b, p).  A thread owns a group of 4 channels (or 1) of one layer for
+// kStreamsPerThread consecutive streams, so the per-channel constants
+// (including the float64 exp that splits e^{-w}) are computed once per group
+// and every access of a wavefront is one contiguous row segment.
+#include "wkv_device.h"
+#include "wkv_launch.h"
+
+namespace wkv {
+
+constexpr int kStreamsPerThread = 16;
+constexpr float kRescaleX = 22.0f;  // e^22 ~ 2^32
+
+struct StepChan {
+    float dhi, dlo, u;
+};
+
+__device__ __forceinline__ StepChan step_chan(float w, float u) {
+    StepChan c;
+    const double dd = exp(-static_cast<double>(w));
+    c.dhi = static_cast<float>(dd);
+    c.dlo = static_cast<float>(dd - static_cast<double>(c.dhi));
+    c.u = u;
+    return c;
+}
+
+// One token on one lane; a, b, p updated in place, returns y.
+__device__ __forceinline__ float step_lane(const StepChan& ch, float k, float v, float& a, float& b,
+                                           float& p) {
+    p = fmaxf(p, -1e38f);  // -inf (empty) behaves as the finite sentinel
+    float x = k - p;
+    if (x > kRescaleX || !(b >= kLo) || b > kHi) {
+        const float lvl = b > 0.f ? p + __logf(b) : -INFINITY;
+        const float pn = fmaxf(lvl, k);
+        const float f = ex2((p - pn) * kL2E);
+        a *= f;
+        b *= f;
+        p = pn;
+        x = k - p;
+    }
+    // output from the state before the token; z = log weight of the token
+    const float z = x + ch.u;
+    const float ez = ex2(-fabsf(z) * kL2E);
+    const bool zp = z > 0.f;
+    const float co = zp ? ez : 1.f;
+    const float cn = zp ? 1.f : ez;
+    const float y = fmaf(a, co, cn * v) * rcp(fmaf(b, co, cn));
+    // decay-and-add
+    const float e = ex2(x * kL2E);
+    a = fmaf(ch.dhi, a, fmaf(ch.dlo, a, e * v));
+    b = fmaf(ch.dhi, b, fmaf(ch.dlo, b, e));
+    return y;
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(256) step_kernel_scalar(int64_t L, int64_t B, int64_t C,
+                                                          int64_t nbt,
+                                                          const float* __restrict__ w,
+                                                          const float* __restrict__ u,
+                                                          const TIn* __restrict__ k,
+                                                          const TIn* __restrict__ v,
+                                                          float* __restrict__ y, float* a,
+                                                          float* b, float* p) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= L * nbt * C) return;
+    const int64_t c = t % C;
+    const int64_t bt = (t / C) % nbt;
+    const int64_t l = t / (C * nbt);
+    const StepChan ch = step_chan(w[l * C + c], u[l * C + c]);
+    const int64_t b_end = (bt + 1) * kStreamsPerThread < B ? (bt + 1) * kStreamsPerThread : B;
+    for (int64_t s = bt * kStreamsPerThread; s < b_end; ++s) {
+        const int64_t i = (l * B + s) * C + c;
+        float aa = a[i], bb = b[i], pp = p[i];
+        y[i] = step_lane(ch, Ld<TIn>::at(k, i), Ld<TIn>::at(v, i), aa, bb, pp);
+        a[i] = aa;
+        b[i] = bb;
+        p[i] = pp;
+    }
+}
+
+template <typename TIn>
+struct Vec4In;
+template <>
+struct Vec4In<float> {
+    using raw = float4;
+    static __device__ __forceinline__ void widen(const raw& r, float out[4]) {
+        out[0] = r.x; out[1] = r.y; out[2] = r.z; out[3] = r.w;
+    }
+};
+template <>
+struct Vec4In<uint16_t> {
+    using raw = uint2;  // 4 bf16
+    static __device__ __forceinline__ void widen(const raw& r, float out[4]) {
+        out[0] = __uint_as_float(r.x << 16);
+        out[1] = __uint_as_float(r.x & 0xffff0000u);
+        out[2] = __uint_as_float(r.y << 16);
+        out[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+};
+
+// 4 channels per thread: C % 4 == 0, float pointers 16-byte aligned, k and v
+// aligned to 4 elements.
+template <typename TIn>
+__global__ void __launch_bounds__(256) step_kernel_vec4(int64_t L, int64_t B, int64_t C,
+                                                        int64_t nbt,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ u,
+                                                        const TIn* __restrict__ k,
+                                                        const TIn* __restrict__ v,
+                                                        float* __restrict__ y, float* a,
+                                                        float* b, float* p) {
+    using V = Vec4In<TIn>;
+    const int64_t C4 = C / 4;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= L * nbt * C4) return;
+    const int64_t c4 = t % C4;
+    const int64_t bt = (t / C4) % nbt;
+    const int64_t l = t / (C4 * nbt);
+    const float4 w4 = reinterpret_cast<const float4*>(w)[l * C4 + c4];
+    const float4 u4 = reinterpret_cast<const float4*>(u)[l * C4 + c4];
+    const StepChan ch[4] = {step_chan(w4.x, u4.x), step_chan(w4.y, u4.y), step_chan(w4.z, u4.z),
+                            step_chan(w4.w, u4.w)};
+    const int64_t b_end = (bt + 1) * kStreamsPerThread < B ? (bt + 1) * kStreamsPerThread : B;
+    for (int64_t s = bt * kStreamsPerThread; s < b_end; ++s) {
+        const int64_t g = (l * B + s) * C4 + c4;
+        float kf[4], vf[4];
+        V::widen(reinterpret_cast<const typename V::raw*>(k)[g], kf);
+        V::widen(reinterpret_cast<const typename V::raw*>(v)[g], vf);
+        const float4 a4 = reinterpret_cast<const float4*>(a)[g];
+        const float4 b4 = reinterpret_cast<const float4*>(b)[g];
+        const float4 p4 = reinterpret_cast<const float4*>(p)[g];
+        float aa[4] = {a4.x, a4.y, a4.z, a4.w};
+        float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        float pp[4] = {p4.x, p4.y, p4.z, p4.w};
+        float yo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yo[j] = step_lane(ch[j], kf[j], vf[j], aa[j], bb[j], pp[j]);
+        reinterpret_cast<float4*>(y)[g] = make_float4(yo[0], yo[1], yo[2], yo[3]);
+        reinterpret_cast<float4*>(a)[g] = make_float4(aa[0], aa[1], aa[2], aa[3]);
+        reinterpret_cast<float4*>(b)[g] = make_float4(bb[0], bb[1], bb[2], bb[3]);
+        reinterpret_cast<float4*>(p)[g] = make_float4(pp[0], pp[1], pp[2], pp[3]);
+    }
+}
+
+template <typename TIn>
+hipError_t launch_step_t(const StepArgs& s, hipStream_t stream) {
+    const int64_t nbt = (s.B + kStreamsPerThread - 1) / kStreamsPerThread;
+    if (s.vec4) {
+        const int64_t threads = s.L * nbt * (s.C / 4);
+        hipLaunchKernelGGL(step_kernel_vec4<TIn>, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                           dim3(256), 0, stream, s.L, s.B, s.C, nbt, s.w, s.u,
+                           static_cast<const TIn*>(s.k), static_cast<const TIn*>(s.v), s.y, s.a,
+                           s.b, s.p);
+    } else {
+        const int64_t threads = s.L * nbt * s.C;
+        hipLaunchKernelGGL(step_kernel_scalar<TIn>,
+                           dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
+                           s.L, s.B, s.C, nbt, s.w, s.u, static_cast<const TIn*>(s.k),
+                           static_cast<const TIn*>(s.v), s.y, s.a, s.b, s.p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs& s, hipStream_t stream) {
+    return s.bf16 ? launch_step_t<uint16_t>(s, stream) : launch_step_t<float>(s, stream);
+}
+
+}  // namespace wkv

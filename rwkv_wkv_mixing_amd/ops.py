@@ -1,0 +1,161 @@
+"""Thin torch binding of the C ABI: argument marshalling only.
+
+Every function takes device tensors, allocates outputs / workspace with torch
+(plumbing), and calls the same-named entry point of librwkv_wkv.so on the
+current HIP stream.  There is no CPU path: host tensors are rejected.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.WKV_F32, torch.bfloat16: L.WKV_BF16}
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(op: int, B: int, T: int, C: int, in_dtype: torch.dtype) -> int:
+    return int(L.lib().wkv_workspace_bytes(op, B, T, C, _DT[in_dtype]))
+
+
+def ckpt_bytes(B: int, T: int, C: int) -> int:
+    return int(L.lib().wkv_ckpt_bytes(B, T, C))
+
+
+def new_ckpt(B: int, T: int, C: int, device) -> torch.Tensor:
+    """Buffer for the forward's block-start states (opaque float32)."""
+    return torch.empty(ckpt_bytes(B, T, C) // 4, dtype=torch.float32, device=device)
+
+
+def _workspace(op, B, T, C, dt, device, workspace):
+    nbytes = workspace_bytes(op, B, T, C, dt)
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None):
+    """y [B,T,C] float32 from w, u [C] float32 and k, v [B,T,C] (float32 or bfloat16)."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    B, T, C = k.shape
+    _need(v, "v", k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, (B, T, C), dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    ws, ws_n = _workspace(L.WKV_OP_FORWARD, B, T, C, k.dtype, dev, workspace)
+    st = L.lib().wkv_forward(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y), _p(ckpt),
+                             _p(ws), ws_n, _stream(dev))
+    L.check("wkv_forward", st)
+    return y
+
+
+def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None):
+    """(dk, dv, dw, du) for L = sum(gy * y).  gy has the dtype of k."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    B, T, C = k.shape
+    _need(v, "v", k.dtype, (B, T, C), dev)
+    _need(gy, "gy", k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    if out is None:
+        dk = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        dv = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        dw = torch.empty((C,), dtype=torch.float32, device=dev)
+        du = torch.empty((C,), dtype=torch.float32, device=dev)
+    else:
+        dk, dv, dw, du = out
+    for t, n, s in ((dk, "dk", (B, T, C)), (dv, "dv", (B, T, C)), (dw, "dw", (C,)), (du, "du", (C,))):
+        _need(t, n, torch.float32, s, dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    ws, ws_n = _workspace(L.WKV_OP_BACKWARD, B, T, C, k.dtype, dev, workspace)
+    st = L.lib().wkv_backward(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(gy), _p(dk),
+                              _p(dv), _p(dw), _p(du), _p(ckpt), _p(ws), ws_n, _stream(dev))
+    L.check("wkv_backward", st)
+    return dk, dv, dw, du
+
+
+def wkv_step(w, u, k, v, a, b, p, *, y=None):
+    """One decode token for [L,B,C] states (a, b, p updated in place); returns y."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    Ln, B, C = k.shape
+    _need(v, "v", k.dtype, (Ln, B, C), dev)
+    _need(w, "w", torch.float32, (Ln, C), dev)
+    _need(u, "u", torch.float32, (Ln, C), dev)
+    for t, n in ((a, "a"), (b, "b"), (p, "p")):
+        _need(t, n, torch.float32, (Ln, B, C), dev)
+    if y is None:
+        y = torch.empty((Ln, B, C), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, (Ln, B, C), dev)
+    st = L.lib().wkv_step(Ln, B, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y), _p(a), _p(b),
+                          _p(p), _stream(dev))
+    L.check("wkv_step", st)
+    return y
+
+
+def empty_state(Ln: int, B: int, C: int, device):
+    """The empty decode state: a = b = 0, p = -1e38."""
+    a = torch.zeros((Ln, B, C), dtype=torch.float32, device=device)
+    b = torch.zeros((Ln, B, C), dtype=torch.float32, device=device)
+    p = torch.full((Ln, B, C), -1e38, dtype=torch.float32, device=device)
+    return a, b, p
+
+
+class WKVFunction(torch.autograd.Function):
+    """Autograd wrapper: saves w, u, k, v and the forward's block-start states;
+    the backward recomputes everything else on chip."""
+
+    @staticmethod
+    def forward(ctx, w, u, k, v):
+        B, T, C = k.shape
+        ckpt = new_ckpt(B, T, C, k.device)
+        y = wkv_forward(w, u, k, v, ckpt=ckpt)
+        ctx.save_for_backward(w, u, k, v, ckpt)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        w, u, k, v, ckpt = ctx.saved_tensors
+        gy = gy.to(k.dtype).contiguous()
+        dk, dv, dw, du = wkv_backward(w, u, k, v, gy, ckpt=ckpt)
+        return dw, du, dk.to(k.dtype), dv.to(v.dtype)
+
+
+def wkv(w, u, k, v):
+    """Differentiable WKV forward (see WKVFunction)."""
+    return WKVFunction.apply(w, u, k, v)

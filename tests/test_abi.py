@@ -1,0 +1,142 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects invalid calls on the host
+before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rwkv_wkv_mixing_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from rwkv_wkv_mixing_amd.build import build
+
+        build()
+    return L.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(wkv_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(L.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.wkv_version().decode() == "0.1.0"
+    for s in range(7):
+        assert len(lib.wkv_status_str(s)) >= 2
+    assert lib.wkv_status_str(99) == b"unknown status"
+    assert lib.wkv_last_hip_error() == b""
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    assert "#define WKV_CKPT_LEN 64" in src and L.WKV_CKPT_LEN == 64
+    for name, val in (("WKV_OK", 0), ("WKV_EINVAL", 1), ("WKV_EDTYPE", 2), ("WKV_ESIZE", 3),
+                      ("WKV_EALIGN", 4), ("WKV_EWORKSPACE", 5), ("WKV_EHIP", 6)):
+        assert re.search(rf"{name} = {val}\b", src), name
+        assert getattr(L, name) == val
+
+
+def test_workspace_and_ckpt_sizes(lib):
+    assert lib.wkv_workspace_bytes(L.WKV_OP_FORWARD, -1, 4, 4, L.WKV_F32) == 0
+    assert lib.wkv_workspace_bytes(L.WKV_OP_FORWARD, 1, 4, 4, 7) == 0
+    assert lib.wkv_workspace_bytes(5, 1, 4, 4, L.WKV_F32) == 0
+    assert lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 0, 4, 4, L.WKV_F32) == 0
+    for dt in (L.WKV_F32, L.WKV_BF16):
+        assert lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 8, 1024, 4096, dt) > 0
+    # overflow of B*T*C
+    assert lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 1 << 30, 1 << 30, 1 << 10, L.WKV_F32) == 0
+    assert lib.wkv_ckpt_bytes(8, 1024, 4096) == 8 * 16 * 4096 * 12
+    assert lib.wkv_ckpt_bytes(1, 65, 3) == 2 * 3 * 12
+    assert lib.wkv_ckpt_bytes(1, 0, 3) == 0
+    assert lib.wkv_ckpt_bytes(-1, 5, 3) == 0
+
+
+P = ctypes.c_void_p
+
+
+def fwd(lib, B, T, C, dt, w, u, k, v, y, ck=None, ws=None, nws=0):
+    return lib.wkv_forward(B, T, C, dt, P(w), P(u), P(k), P(v), P(y), P(ck), P(ws), nws, None)
+
+
+def bwd(lib, B, T, C, dt, w, u, k, v, gy, dk, dv, dw, du, ck=None, ws=None, nws=0):
+    return lib.wkv_backward(B, T, C, dt, P(w), P(u), P(k), P(v), P(gy), P(dk), P(dv), P(dw), P(du),
+                            P(ck), P(ws), nws, None)
+
+
+def step(lib, Ln, B, C, dt, w, u, k, v, y, a, b, p):
+    return lib.wkv_step(Ln, B, C, dt, P(w), P(u), P(k), P(v), P(y), P(a), P(b), P(p), None)
+
+
+A16 = 0x10000  # fake, never dereferenced: every call below fails validation on the host
+
+
+def test_forward_validation(lib):
+    x = A16
+    assert fwd(lib, -1, 4, 4, L.WKV_F32, x, x, x, x, x) == L.WKV_EINVAL
+    assert fwd(lib, 1, 4, 4, 3, x, x, x, x, x) == L.WKV_EDTYPE
+    assert fwd(lib, 1 << 30, 1 << 30, 1 << 10, L.WKV_F32, x, x, x, x, x) == L.WKV_ESIZE
+    assert fwd(lib, 1, 4, 4, L.WKV_F32, None, x, x, x, x) == L.WKV_EINVAL
+    assert fwd(lib, 1, 4, 4, L.WKV_F32, x, x, x, x, None) == L.WKV_EINVAL
+    assert fwd(lib, 1, 4, 4, L.WKV_F32, x, x, x + 2, x, x) == L.WKV_EALIGN
+    assert fwd(lib, 1, 4, 4, L.WKV_BF16, x, x, x + 1, x, x) == L.WKV_EALIGN
+    assert fwd(lib, 1, 4, 4, L.WKV_F32, x, x, x, x, x + 1) == L.WKV_EALIGN
+    # empty problems are no-ops and touch nothing
+    assert fwd(lib, 0, 4, 4, L.WKV_F32, None, None, None, None, None) == L.WKV_OK
+    assert fwd(lib, 3, 0, 4, L.WKV_F32, None, None, None, None, None) == L.WKV_OK
+
+
+def test_backward_validation(lib):
+    x = A16
+    ws_need = lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 1, 4, 4, L.WKV_F32)
+    args = [x] * 9
+    assert bwd(lib, 1, -4, 4, L.WKV_F32, *args) == L.WKV_EINVAL
+    assert bwd(lib, 1, 4, 4, 9, *args) == L.WKV_EDTYPE
+    assert bwd(lib, 1, 4, 4, L.WKV_F32, x, x, x, x, x, x, x, None, x) == L.WKV_EINVAL
+    assert bwd(lib, 1, 4, 4, L.WKV_F32, x, x, x, x, None, x, x, x, x) == L.WKV_EINVAL
+    assert bwd(lib, 1, 4, 4, L.WKV_F32, x, x, x, x, x, x + 2, x, x, x) == L.WKV_EALIGN
+    assert bwd(lib, 1, 4, 4, L.WKV_BF16, x, x, x, x, x + 1, x, x, x, x) == L.WKV_EALIGN
+    if ws_need > 0:
+        assert bwd(lib, 1, 4, 4, L.WKV_F32, *args) == L.WKV_EWORKSPACE
+        assert bwd(lib, 1, 4, 4, L.WKV_F32, *args, ws=x, nws=ws_need - 1) == L.WKV_EWORKSPACE
+    assert bwd(lib, 1, 4, 0, L.WKV_F32, *[None] * 9) == L.WKV_OK
+
+
+def test_step_validation(lib):
+    x = A16
+    args = [x] * 8
+    assert step(lib, -1, 2, 4, L.WKV_F32, *args) == L.WKV_EINVAL
+    assert step(lib, 1, 2, 4, 4, *args) == L.WKV_EDTYPE
+    assert step(lib, 1 << 30, 1 << 30, 1 << 10, L.WKV_F32, *args) == L.WKV_ESIZE
+    assert step(lib, 1, 2, 4, L.WKV_F32, x, x, x, x, x, x, x, None) == L.WKV_EINVAL
+    assert step(lib, 1, 2, 4, L.WKV_F32, x, x, x, x, x, x + 3, x, x) == L.WKV_EALIGN
+    assert step(lib, 0, 2, 4, L.WKV_F32, *[None] * 8) == L.WKV_OK
+
+
+def test_binding_rejects_host_tensors():
+    """There is no CPU path: host tensors are refused before the library is called."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops
+
+    w = torch.ones(4)
+    with pytest.raises(ValueError):
+        ops.wkv_forward(w, w, torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))
+    with pytest.raises(ValueError):
+        ops.wkv_step(torch.ones(1, 4), torch.ones(1, 4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4),
+                     torch.zeros(1, 2, 4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (element passes iff |g - o| <= max(atol, rtol |o|)):
+  fp32 forward   rtol 1e-5, atol 1e-6 (as stated for the fp32 path)
+  bf16 forward   rtol 2e-3 against the oracle on the bf16-rounded inputs,
+                 atol 2e-3 * 1e-2 * RMS(reference) (no atol is stated; a pure
+                 relative bound cannot hold where y crosses zero)
+  backward       rtol 1e-3, atol 1e-3 * 1e-2 * RMS(reference tensor)
+  stress         inputs beyond every stated workload (key spikes of +-100,
+                 |u| up to 30, fp32 inputs with spikes): rtol 1e-4, atol 1e-5
+"""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import bwd_atol, check_close, problem_to_dev, to_dev
+from oracle import wkv_backward_ref, wkv_forward_ref
+from rwkv_wkv_mixing_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def ops():
+    from rwkv_wkv_mixing_amd import ops as O
+
+    return O
+
+
+def run_fwd(p, **kw):
+    d = problem_to_dev(p, DEV)
+    y = ops().wkv_forward(d["w"], d["u"], d["k"], d["v"], **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def run_bwd(p):
+    d = problem_to_dev(p, DEV)
+    dk, dv, dw, du = ops().wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    torch.cuda.synchronize()
+    return dk.cpu().numpy(), dv.cpu().numpy(), dw.cpu().numpy(), du.cpu().numpy()
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.asarray(a, np.float64) ** 2))) if np.size(a) else 0.0
+
+
+def check_fwd(p, y, stress=False):
+    ref = wkv_forward_ref(p.w, p.u, p.k, p.v)
+    if stress:
+        return check_close(f"{p.name} y (stress bound)", y, ref, 1e-4, 1e-5)
+    if p.dtype == "bf16":
+        return check_close(f"{p.name} y (bf16 bound)", y, ref, 2e-3, 2e-5 * rms(ref))
+    return check_close(f"{p.name} y", y, ref, 1e-5, 1e-6)
+
+
+def check_bwd(p, got):
+    rk, rv, rw, ru = wkv_backward_ref(p.w, p.u, p.k, p.v, p.gy)
+    for n, g, r in (("dk", got[0], rk), ("dv", got[1], rv), ("dw", got[2], rw), ("du", got[3], ru)):
+        check_close(f"{p.name} {n}", g, r, 1e-3, bwd_atol(r))
+
+
+# ------------------------------------------------------------- workloads --
+
+def test_config1_forward_backward():
+    p = W.config1()
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p))
+    check_bwd(p, run_bwd(p))
+
+
+def test_config2_forward_backward():
+    p = W.config2()
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p))
+    check_bwd(p, run_bwd(p))
+
+
+def test_config3_forward_backward_bf16():
+    p = W.config3()
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p))
+    check_bwd(p, run_bwd(p))
+
+
+def test_config4_forward_long_context():
+    p = W.config4()
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p))
+
+
+# ------------------------------------------------------------ edge cases --
+
+ODD = [(1, 1, 1), (1, 2, 3), (3, 77, 13), (2, 1000, 129), (1, 4097, 7), (5, 64, 64), (2, 129, 260)]
+
+
+@pytest.mark.parametrize("B,T,C", ODD)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_odd_shapes(B, T, C, dtype):
+    """fp32 cases follow the fp32 workloads (no key spikes); bf16 cases follow
+    the bf16 workload (2% of keys set to +-U(20,40))."""
+    spikes = 0.02 if dtype == "bf16" else 0.0
+    p = W.make_problem(B, T, C, dtype=dtype, seed=B * 1000 + T + C, spike_frac=spikes,
+                       name=f"odd {dtype} B={B} T={T} C={C}")
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p))
+    check_bwd(p, run_bwd(p))
+
+
+@pytest.mark.parametrize("B,T,C", [(2, 1000, 129), (1, 4097, 7), (2, 129, 260)])
+def test_fp32_inputs_with_key_spikes(B, T, C):
+    p = W.make_problem(B, T, C, dtype="f32", seed=B * 1000 + T + C, spike_frac=0.02,
+                       name=f"spiky f32 B={B} T={T} C={C}")
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p), stress=True)
+    check_bwd(p, run_bwd(p))
+
+
+def test_extreme_inputs():
+    """Spikes of +-100 in k (beyond the 2^32 rescale bounds), large |u|, w from 0 to 80."""
+    B, T, C = 2, 600, 12
+    p = W.make_problem(B, T, C, seed=3, spike_frac=0.03, spike_range=(60.0, 100.0), name="extreme")
+    p.w[:] = np.array([0.0, 1e-9, 1e-6, 1e-3, 0.1, 1.0, 5.0, 20.0, 80.0, 1e-4, 2.0, 0.5], np.float32)
+    p.u[:] = np.array([-30, 30, -10, 10, 0, 25, -25, 3, -3, 0.5, 15, -15], np.float32)
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p), stress=True)
+    check_bwd(p, run_bwd(p))
+
+
+def test_zero_length_sequences():
+    O = ops()
+    w = torch.ones(5, device=DEV)
+    u = torch.zeros(5, device=DEV)
+    k = torch.zeros((2, 0, 5), device=DEV)
+    y = O.wkv_forward(w, u, k, k)
+    assert y.shape == (2, 0, 5)
+    dw = torch.full((5,), 7.0, device=DEV)
+    du = torch.full((5,), 7.0, device=DEV)
+    O.wkv_backward(w, u, k, k, k, out=(torch.empty_like(k), torch.empty_like(k), dw, du))
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0) and torch.all(du == 0)
+
+
+def test_every_output_written_and_no_out_of_bounds_writes():
+    """NaN-poisoned outputs must be fully overwritten; guard bands must stay intact."""
+    O = ops()
+    p = W.make_problem(3, 300, 70, seed=11, name="guard")
+    d = problem_to_dev(p, DEV)
+    n = p.n
+    G = 4096
+    buf = torch.full((n + 2 * G,), float("nan"), device=DEV)
+    buf[:G] = 12345.0
+    buf[-G:] = -54321.0
+    y = buf[G:G + n].view(p.B, p.T, p.C)
+    O.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=y)
+    gbuf = torch.full((2 * n + 2 * p.C + 5 * G,), float("nan"), device=DEV)
+    sent = torch.tensor(777.0, device=DEV)
+    offs = [G, 2 * G + n, 3 * G + 2 * n, 4 * G + 2 * n + p.C]
+    views = []
+    for o, size, shape in ((offs[0], n, (p.B, p.T, p.C)), (offs[1], n, (p.B, p.T, p.C)),
+                           (offs[2], p.C, (p.C,)), (offs[3], p.C, (p.C,))):
+        views.append(gbuf[o:o + size].view(*shape))
+    mask = torch.ones_like(gbuf, dtype=torch.bool)
+    for o, size in ((offs[0], n), (offs[1], n), (offs[2], p.C), (offs[3], p.C)):
+        mask[o:o + size] = False
+    gbuf[mask] = sent
+    O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"], out=tuple(views))
+    torch.cuda.synchronize()
+    assert torch.all(buf[:G] == 12345.0) and torch.all(buf[-G:] == -54321.0)
+    assert not torch.isnan(y).any()
+    assert torch.all(gbuf[mask] == sent)
+    for t in views:
+        assert not torch.isnan(t).any()
+    check_fwd(p, y.cpu().numpy())
+
+
+def test_bitwise_deterministic():
+    p = W.make_problem(4, 700, 96, dtype="bf16", seed=12, spike_frac=0.01, name="determinism")
+    d = problem_to_dev(p, DEV)
+    O = ops()
+    y1 = O.wkv_forward(d["w"], d["u"], d["k"], d["v"])
+    y2 = O.wkv_forward(d["w"], d["u"], d["k"], d["v"])
+    g1 = O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    g2 = O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_checkpointed_backward_matches():
+    """Backward fed the forward's block-start states equals the standalone backward."""
+    p = W.make_problem(2, 333, 40, dtype="bf16", seed=13, spike_frac=0.01, name="ckpt")
+    d = problem_to_dev(p, DEV)
+    O = ops()
+    ck = O.new_ckpt(p.B, p.T, p.C, DEV)
+    O.wkv_forward(d["w"], d["u"], d["k"], d["v"], ckpt=ck)
+    g1 = O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"], ckpt=ck)
+    torch.cuda.synchronize()
+    check_bwd(p, [t.cpu().numpy() for t in g1])
+
+
+def test_autograd_function():
+    p = W.make_problem(2, 50, 16, seed=14, name="autograd")
+    d = problem_to_dev(p, DEV)
+    O = ops()
+    k = d["k"].clone().requires_grad_(True)
+    v = d["v"].clone().requires_grad_(True)
+    w = d["w"].clone().requires_grad_(True)
+    u = d["u"].clone().requires_grad_(True)
+    y = O.wkv(w, u, k, v)
+    gy = to_dev(p.gy, DEV)
+    (y * gy).sum().backward()
+    torch.cuda.synchronize()
+    rk, rv, rw, ru = wkv_backward_ref(p.w, p.u, p.k, p.v, p.gy)
+    check_close("autograd dk", k.grad.cpu().numpy(), rk, 1e-3, bwd_atol(rk))
+    check_close("autograd dw", w.grad.cpu().numpy(), rw, 1e-3, bwd_atol(rw))
