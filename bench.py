@@ -14,8 +14,9 @@ the per-kernel roofline of the dominant kernel (HIP events on the stream the
 kernels run on) and the float64 CPU oracle timed on this host.
 
 Other workloads (not the headline, for measurements quoted in the design
-notes): fwd2 (B=8 T=1024 C=768 fp32, fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32,
-forward only), step5 (32 layers x 256 streams x 4096 channels decode step).
+notes): fwd3 (the headline shape, forward only), fwd2 (B=8 T=1024 C=768 fp32,
+fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32, forward only), step5 (32 layers x
+256 streams x 4096 channels decode step).
 """
 from __future__ import annotations
 
@@ -39,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd2", "fwd4", "step5"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -230,6 +231,8 @@ def main():
         return
     if args.workload == "fwdbwd":
         p, with_bwd, bf, bb = W.config3(), True, 8, 14
+    elif args.workload == "fwd3":
+        p, with_bwd, bf, bb = W.config3(), False, 8, 0
     elif args.workload == "fwd2":
         p, with_bwd, bf, bb = W.config2(), True, 12, 20
     else:

@@ -49,7 +49,12 @@ def lib():
         raise RuntimeError(
             f"HIP library not built: {LIB_PATH} is missing; run `python -m rwkv_wkv_mixing_amd.build`"
         )
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(L):
+    """Attach the argument and return types of include/wkv.h to a loaded library."""
     i64, i32, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     L.wkv_workspace_bytes.restype = sz
@@ -68,7 +73,6 @@ def lib():
     L.wkv_last_hip_error.argtypes = []
     L.wkv_version.restype = ctypes.c_char_p
     L.wkv_version.argtypes = []
-    _lib = L
     return L
 
 

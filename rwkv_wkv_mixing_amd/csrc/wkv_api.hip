@@ -52,6 +52,7 @@ Plan plan_seq(int op, int64_t B, int64_t T, int64_t C, int dt) {
     if (__builtin_mul_overflow(B, C, &lanes) || lanes > kMaxLanes) return Plan{WKV_ESIZE, 0, 0, 0};
     p.nblk = (T + wkv::kCkptLen - 1) / wkv::kCkptLen;
     if (op == WKV_OP_BACKWARD && p.N > 0) p.ws_bytes = wkv::bwd_seq_workspace_bytes(B, T, C);
+    if (op == WKV_OP_FORWARD && p.N > 0) p.ws_bytes = wkv::fwd_chunk_workspace_bytes(B, T, C);
     return p;
 }
 
@@ -92,10 +93,11 @@ wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const fl
     if (!aligned(w, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(k, es) || !aligned(v, es) ||
         (ckpt && !aligned(ckpt, 4)))
         return WKV_EALIGN;
-    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return WKV_EWORKSPACE;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
+        return WKV_EWORKSPACE;
     wkv::FwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, y, ckpt, p.nblk, workspace,
                    workspace_bytes};
-    return hip_status(wkv::launch_fwd_seq(a, static_cast<hipStream_t>(hip_stream)));
+    return hip_status(wkv::launch_fwd_chunk(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,

@@ -48,6 +48,43 @@ struct Ld<uint16_t> {
     }
 };
 
+// ---- raw buffer access ----------------------------------------------------------
+// A buffer resource covers [base, base + bytes); loads outside it return 0 and
+// stores outside it are dropped by the hardware, so ragged tails need no
+// branches, and a lane whose offset is kOffNone never touches memory.  The
+// per-token offset is wave-uniform and lives in an SGPR (soffset).
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor
+constexpr uint32_t kOffNone = 0x80000000u;   // voffset that is out of range for every buffer here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             static_cast<int>(kRsrcWord3));
+}
+
+template <typename TIn>
+struct BufLd;
+
+template <>
+struct BufLd<float> {
+    static constexpr int kBytes = 4;
+    static __device__ __forceinline__ float at(Rsrc r, uint32_t voff, uint32_t soff) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+};
+
+template <>
+struct BufLd<uint16_t> {
+    static constexpr int kBytes = 2;
+    static __device__ __forceinline__ float at(Rsrc r, uint32_t voff, uint32_t soff) {
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+    }
+};
+
+__device__ __forceinline__ void buf_store(float v, Rsrc r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
 // ---- per-channel constants -------------------------------------------------
 struct Chan {
     float dhi, dlo;  // e^{-w} = dhi + dlo (to ~2^-48 relative)
@@ -82,9 +119,12 @@ __device__ __forceinline__ void rescale(St& st, float k2) {
 }
 
 // x = k log2 e - s, rescaling first when the new term or b is out of range.
+// The three conditions are folded into one mask so the rare rescale costs a
+// single branch per token.
 __device__ __forceinline__ float key_offset(St& st, float k) {
     float x = fmaf(k, kL2E, -st.s);
-    if (x > kBig || !(st.b >= kLo) || st.b > kHi) {
+    const bool out = (x > kBig) | !(st.b >= kLo) | (st.b > kHi);
+    if (__builtin_expect(out, 0)) {
         rescale(st, k * kL2E);
         x = fmaf(k, kL2E, -st.s);
     }
@@ -112,6 +152,23 @@ __device__ __forceinline__ Out token_out(const St& st, float x, float v, const C
     o.r = rcp(D);
     o.y = N * o.r;
     return o;
+}
+
+// Output of one token when |u| is small enough that the current-token weight
+// e^{u} 2^x cannot overflow (|u| <= kFastU with x <= 32): one multiply instead
+// of the normalised two-branch form.
+constexpr float kFastU = 40.0f;
+
+__device__ __forceinline__ float token_out_fast(const St& st, float e, float v, float eu) {
+    const float E = e * eu;
+    return fmaf(E, v, st.a) * rcp(st.b + E);
+}
+
+// Decay-and-add with e = 2^x already computed.
+__device__ __forceinline__ void token_add(St& st, float e, float v, const Chan& ch) {
+    const float ev = e * v;
+    st.a = fmaf(ch.dhi, st.a, fmaf(ch.dlo, st.a, ev));
+    st.b = fmaf(ch.dhi, st.b, fmaf(ch.dlo, st.b, e));
 }
 
 // Decay-and-add of one token: A <- d A + e^k v, B <- d B + e^k, d = dhi + dlo.

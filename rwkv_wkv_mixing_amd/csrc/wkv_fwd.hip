@@ -1,0 +1,272 @@
+// Chunked (time-split) WKV forward for gfx950.
+//
+// Work decomposition.  A workgroup owns one TILE of 64 channels of one batch
+// row and one time BLOCK of W*L tokens; wave i of the workgroup owns the L
+// tokens [i*L, (i+1)*L) of the block, one channel per lane, so every load and
+// store of a wave is one contiguous 64-channel row segment (128 B for bf16,
+// 256 B for fp32).  The inputs of a sub-chunk stay in registers between the
+// two passes, so HBM sees each input once and each output once.
+//
+//   pass 1  every wave runs its L tokens from the empty state -> summary S_i
+//   scan    wave 0 combines S_0..S_{W-1} in LDS into per-wave prefixes and the
+//           block aggregate, obtains the block's carry-in E from the
+//           preceding blocks of the same tile (decoupled look-back over
+//           global flags, blocks handed out by an atomic ticket in time order
+//           so every awaited block is already running), and publishes the
+//           block's inclusive state
+//   pass 2  every wave re-runs its L tokens from carry-in d^{iL} E + P_i and
+//           writes y (and the saved block-start states for the backward).
+//
+// Chunkwise-parallel execution: "RWKV模型深度研究报告", section 1.4.1;
+// prefix scan: "RWKV（Receptance Weighted Key Value）概念", section 3.4.
+#include "wkv_launch.h"
+#include "wkv_scan.h"
+
+namespace wkv {
+
+struct FwdChunk {
+    int64_t B, T, C;
+    const float* w;
+    const float* u;
+    const void* k;
+    const void* v;
+    float* y;
+    float* ckpt;
+    int64_t nblk_ck;   // blocks of kCkptLen tokens (ckpt layout)
+    int64_t nct;       // channel tiles per batch row
+    int64_t ntiles;    // B * nct
+    int64_t nblocks;   // time blocks per tile
+    uint32_t* counter; // ticket counter (nblocks > 1)
+    uint32_t* error;   // set if a carry wait timed out
+    float* carry;      // [ntiles][nblocks][64][4] inclusive block states + status
+    uint32_t carry_bytes;
+};
+
+// The L tokens of one lane's sub-chunk, held in registers across both passes.
+// bf16: k and v of a token share one 32-bit register (v in the high half).
+template <typename TIn, int L>
+struct SubChunk;
+
+template <int L>
+struct SubChunk<uint16_t, L> {
+    uint32_t kv[L];
+    __device__ __forceinline__ void load(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rk, voff, j * row, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rv, voff, j * row, 0);
+            kv[j] = lo | (hi << 16);
+        }
+    }
+    __device__ __forceinline__ float k(int j) const { return __uint_as_float(kv[j] << 16); }
+    __device__ __forceinline__ float v(int j) const { return __uint_as_float(kv[j] & 0xffff0000u); }
+};
+
+template <int L>
+struct SubChunk<float, L> {
+    float kk[L], vv[L];
+    __device__ __forceinline__ void load(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            kk[j] = BufLd<float>::at(rk, voff, j * row);
+            vv[j] = BufLd<float>::at(rv, voff, j * row);
+        }
+    }
+    __device__ __forceinline__ float k(int j) const { return kk[j]; }
+    __device__ __forceinline__ float v(int j) const { return vv[j]; }
+};
+
+// Pass 2 over a sub-chunk: outputs from the carry-in state.
+template <bool Fast, typename TIn, int L>
+__device__ __forceinline__ void fwd_outputs(St st, const SubChunk<TIn, L>& sc, int nvalid,
+                                            const Chan& ch, float eu, Rsrc ry, uint32_t vout,
+                                            uint32_t row_out) {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        if (j < nvalid) {
+            const float kj = sc.k(j), vj = sc.v(j);
+            const float x = key_offset(st, kj);
+            float yj;
+            if (Fast) {
+                const float e = ex2(x);
+                yj = token_out_fast(st, e, vj, eu);
+                token_add(st, e, vj, ch);
+            } else {
+                yj = token_out(st, x, vj, ch).y;
+                token_update(st, x, vj, ch);
+            }
+            buf_store(yj, ry, vout, j * row_out);
+        }
+    }
+}
+
+template <typename TIn, int L, int W>
+__global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
+    constexpr int ES = BufLd<TIn>::kBytes;
+    __shared__ float sm_a[W][64];
+    __shared__ float sm_b[W][64];
+    __shared__ float sm_s[W][64];
+    __shared__ float sm_e[3][64];  // block carry-in E
+    __shared__ uint32_t sm_ticket;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    int64_t ticket = blockIdx.x;
+    if (P.nblocks > 1) {
+        if (threadIdx.x == 0) sm_ticket = atomicAdd(P.counter, 1u);
+        __syncthreads();
+        ticket = sm_ticket;
+    }
+    const int64_t blk = ticket / P.ntiles;
+    const int64_t tile = ticket - blk * P.ntiles;
+    const int64_t b = tile / P.nct;
+    const int64_t c = (tile - b * P.nct) * 64 + lane;
+    const bool cok = c < P.C;
+    const int64_t tb0 = blk * (int64_t)(L * W);  // first token of the block
+    const int64_t t0 = tb0 + (int64_t)wave * L;  // first token of this wave
+    const int64_t rem = P.T - t0;
+    const int nvalid = rem <= 0 ? 0 : (rem >= L ? L : static_cast<int>(rem));
+    const float wc = cok ? P.w[c] : 0.f;
+    const float uc = cok ? P.u[c] : 0.f;
+    const Chan ch = make_chan(wc, uc);
+    const bool fast = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
+    const float eu = ex2(ch.u2);
+
+    // buffers over this block's rows of batch row b: [tokens tb0 .. min(T, tb0 + W L)) x C
+    const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
+    const int64_t row0 = (b * P.T + tb0) * P.C;
+    const Rsrc rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, (uint32_t)(blk_tokens * P.C * ES));
+    const Rsrc rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, (uint32_t)(blk_tokens * P.C * ES));
+    const Rsrc ry = make_rsrc(P.y + row0, (uint32_t)(blk_tokens * P.C * 4));
+    const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;  // element offset
+    const uint32_t vin = cok ? lin * ES : kOffNone;
+    const uint32_t vout = cok ? lin * 4 : kOffNone;
+    const uint32_t row_in = (uint32_t)(P.C * ES), row_out = (uint32_t)(P.C * 4);
+
+    SubChunk<TIn, L> sc;
+    sc.load(rk, rv, vin, row_in);
+
+    // ---- pass 1: summary from the empty state ----------------------------------
+    St st = empty_state();
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        if (j < nvalid) {
+            const float x = key_offset(st, sc.k(j));
+            token_update(st, x, sc.v(j), ch);
+        }
+    }
+    sm_a[wave][lane] = st.a;
+    sm_b[wave][lane] = st.b;
+    sm_s[wave][lane] = st.s;
+    __syncthreads();
+
+    // ---- scan ------------------------------------------------------------------
+    // every wave: prefix of the sub-chunks before it; the last wave also forms
+    // the block aggregate and fetches / publishes the block carry.
+    const double dL = exp(-static_cast<double>(wc) * L);
+    St pref = empty_state();
+    for (int i = 0; i < wave; ++i) pref = combine(pref, St{sm_a[i][lane], sm_b[i][lane], sm_s[i][lane]}, dL);
+    if (wave == W - 1) {
+        St E = empty_state();
+        if (P.nblocks > 1) {
+            double dTB = 1.0;
+#pragma unroll
+            for (int i = 0; i < W; ++i) dTB *= dL;
+            const Rsrc rc = make_rsrc(P.carry, P.carry_bytes);
+            const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * 16);
+            if (blk > 0) E = wait_state(rc, slot - 64 * 16, P.error);  // block blk-1, same lane
+            if (blk < P.nblocks - 1)  // then this block is full
+                publish_state(rc, slot, combine(E, combine(pref, st, dL), dTB));
+        }
+        sm_e[0][lane] = E.a;
+        sm_e[1][lane] = E.b;
+        sm_e[2][lane] = E.s;
+    }
+    __syncthreads();
+    double dpow = 1.0;
+    for (int i = 0; i < wave; ++i) dpow *= dL;
+    const St s2 = combine(St{sm_e[0][lane], sm_e[1][lane], sm_e[2][lane]}, pref, dpow);
+
+    // ---- pass 2: outputs from the carry-in -------------------------------------
+    if (P.ckpt != nullptr && cok && nvalid > 0 && (t0 % kCkptLen) == 0) {
+        float* cp = P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c;
+        cp[0] = s2.a;
+        cp[P.C] = s2.b;
+        cp[2 * P.C] = s2.s;
+    }
+    if (fast)
+        fwd_outputs<true>(s2, sc, nvalid, ch, eu, ry, vout, row_out);
+    else
+        fwd_outputs<false>(s2, sc, nvalid, ch, eu, ry, vout, row_out);
+}
+
+__global__ void fwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < 2) hdr[i] = 0u;
+    for (int64_t j = i; j < nwords; j += static_cast<int64_t>(gridDim.x) * blockDim.x) carry_words[j] = 0u;
+}
+
+namespace {
+#ifndef WKV_FWD_L
+#define WKV_FWD_L 32
+#endif
+#ifndef WKV_FWD_W
+#define WKV_FWD_W 8
+#endif
+constexpr int kFwdL = WKV_FWD_L;  // tokens per wave (sub-chunk)
+constexpr int kFwdW = WKV_FWD_W;  // waves per workgroup
+
+struct FwdLayout {
+    int64_t nct, ntiles, nblocks;
+    size_t off_carry, carry_bytes, bytes;
+};
+
+FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C) {
+    FwdLayout l{};
+    l.nct = (C + 63) / 64;
+    l.ntiles = B * l.nct;
+    l.nblocks = (T + kFwdL * kFwdW - 1) / (kFwdL * kFwdW);
+    if (l.nblocks <= 1) return l;  // no cross-workgroup carries, no workspace
+    l.off_carry = 256;
+    l.carry_bytes = static_cast<size_t>(l.ntiles * l.nblocks * 64) * 16;
+    l.bytes = l.off_carry + l.carry_bytes;
+    return l;
+}
+}  // namespace
+
+size_t fwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C) { return fwd_layout(B, T, C).bytes; }
+
+template <typename TIn>
+hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
+    const FwdLayout l = fwd_layout(a.B, a.T, a.C);
+    FwdChunk P{};
+    P.B = a.B; P.T = a.T; P.C = a.C;
+    P.w = a.w; P.u = a.u; P.k = a.k; P.v = a.v; P.y = a.y;
+    P.ckpt = static_cast<float*>(a.ckpt);
+    P.nblk_ck = a.nblk;
+    P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+    if (l.nblocks > 1) {
+        char* ws = static_cast<char*>(a.ws);
+        P.counter = reinterpret_cast<uint32_t*>(ws);
+        P.error = P.counter + 1;
+        P.carry = reinterpret_cast<float*>(ws + l.off_carry);
+        P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
+        const int64_t nwords = static_cast<int64_t>(l.carry_bytes / 4);
+        int64_t g = (nwords + 255) / 256;
+        if (g > 4096) g = 4096;
+        hipLaunchKernelGGL(fwd_chunk_init_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream,
+                           P.counter, reinterpret_cast<uint32_t*>(P.carry), nwords);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t grid = l.ntiles * l.nblocks;
+    hipLaunchKernelGGL((fwd_chunk_kernel<TIn, kFwdL, kFwdW>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * kFwdW), 0, stream, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t stream) {
+    return a.bf16 ? launch_fwd_chunk_t<uint16_t>(a, stream) : launch_fwd_chunk_t<float>(a, stream);
+}
+
+}  // namespace wkv

@@ -56,6 +56,10 @@ struct StepArgs {
     float* p;
 };
 
+// chunked forward (wkv_fwd.hip)
+hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t stream);
+size_t fwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C);
+
 // lane-sequential kernels (wkv_seq.hip)
 hipError_t launch_fwd_seq(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_seq(const BwdArgs& a, hipStream_t stream);

@@ -1,0 +1,73 @@
+// Chunk-level combine of WKV states and the decoupled look-back protocol that
+// passes carries between workgroups along time.
+//
+// Chunkwise-parallel execution ("RWKV模型深度研究报告", section 1.4.1: split the
+// sequence into chunks, compute inside each chunk in parallel, pass state
+// between chunks; "RWKV（Receptance Weighted Key Value）概念", section 3.4:
+// parallel prefix scan).  A chunk of n tokens run from the empty state yields a
+// summary S with  state_after = d^n * state_before + S  (the recurrence is a
+// first-order linear one with a constant coefficient, so this map is
+// associative).
+#pragma once
+
+#include "wkv_device.h"
+
+namespace wkv {
+
+// Combine a state X (at the start of an n-token interval) with the summary S
+// of that interval; D = d^n in double, applied as a float32 hi + lo product.
+// The result keeps X's scale unless the summary would not fit (lazy
+// rescale), so the history is multiplied by D only and never by a rounded
+// rescale factor in the common case.
+__device__ __forceinline__ St combine(const St& X, const St& S, double D) {
+    const float Dhi = static_cast<float>(D);
+    const float Dlo = static_cast<float>(D - static_cast<double>(Dhi));
+    const float xa = fmaf(Dhi, X.a, Dlo * X.a);
+    const float xb = fmaf(Dhi, X.b, Dlo * X.b);
+    if (!(S.b > 0.f)) return St{xa, xb, X.s};
+    if (!(xb > 0.f)) return S;
+    float sn = X.s;
+    const float ls = S.s + lg2(S.b);
+    if ((ls > X.s + kBig) | (xb < kLo) | (xb > kHi)) sn = fmaxf(X.s + lg2(xb), ls);
+    const float fx = (sn == X.s) ? 1.f : ex2(X.s - sn);
+    const float fs = ex2(S.s - sn);
+    return St{fmaf(xa, fx, S.a * fs), fmaf(xb, fx, S.b * fs), sn};
+}
+
+// ---- carries between workgroups --------------------------------------------------
+// A chained scan along time: the workgroup of time block j waits for the
+// inclusive state of block j-1 of the same tile and publishes its own.  Each
+// (tile, block, lane) slot is 16 bytes (a, b, s, status) written with ONE
+// 16-byte store and polled with 16-byte loads, both with the system-coherent
+// cache policy (sc0 sc1), which bypasses the per-XCD L2s.  So no release or
+// acquire fence is needed: such fences would write back or invalidate the
+// whole L2 of the XCD on every exchange, which the bandwidth-bound stream of
+// outputs from the other workgroups cannot afford.  Status 0 means "not yet";
+// slots are zeroed by a small kernel before each launch.  Always taking block
+// j-1's state (never a look-back over several aggregates) keeps the rounding,
+// and therefore the result, independent of timing.
+constexpr int kCoherent = 1 | 16;          // sc0 | sc1
+constexpr uint32_t kSpinLimit = 1u << 22;  // bounded wait: a broken protocol cannot hang
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void publish_state(Rsrc r, uint32_t off, const St& st) {
+    const f32x4 v = {st.a, st.b, st.s, __uint_as_float(1u)};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
+}
+
+// Wait for the state published at `off`; after kSpinLimit polls give up,
+// set *error and return the empty state (results are then invalid, but every
+// wave terminates).
+__device__ __forceinline__ St wait_state(Rsrc r, uint32_t off, uint32_t* error) {
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+        if (__float_as_uint(v.w) != 0u) return St{v.x, v.y, v.z};
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return empty_state();
+}
+
+}  // namespace wkv
