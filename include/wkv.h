@@ -38,11 +38,15 @@
  *                  the HIP message of the last such failure on this thread).
  *    A call with B, T, C (or L) equal to 0 is a no-op returning WKV_OK,
  *    except that wkv_backward with C > 0 and B*T == 0 sets dw = du = 0.
- *  - Numerics: float32 arithmetic with a float32 running log-scale.  The
+ *  - Numerics: float32 arithmetic on states (a, b) with an integer log2
+ *    scale s (A = a 2^s, B = b 2^s).  Each key weight is split once as
+ *    e^k = em 2^n (n an integer), so a token's weight has the same float32
+ *    value in every pass and kernel, and changes of scale are exact.  The
  *    decay e^{-w} is applied as a two-term (hi + lo) product so that no
- *    systematic rounding of the decay builds up over long sequences.
- *    Results are finite for finite inputs with w >= 0, |u| <= 80 and
- *    |v| < 2^60; outside that range the math is still defined but may
+ *    systematic rounding of the decay builds up over long sequences.  The
+ *    backward keeps its reverse running sums in float64.  Results are
+ *    finite for finite inputs with w >= 0, |u| <= 80, |v| < 2^60 and
+ *    |k| < 2.9e6; outside that range the math is still defined but may
  *    overflow.  NaN/Inf inputs propagate.  For decay rates w below ~1e-5
  *    the per-token float32 rounding of the state itself changes by only a
  *    few ulps per token and no longer averages out; float32 state then
@@ -78,7 +82,7 @@ enum { WKV_OP_FORWARD = 0, WKV_OP_BACKWARD = 1 };
 
 /* Length, in tokens, of the blocks whose start states wkv_forward can save
  * for wkv_backward (see `ckpt`). */
-#define WKV_CKPT_LEN 64
+#define WKV_CKPT_LEN 16
 
 /* Bytes of scratch memory a call needs (0 is possible).  Returns 0 for
  * invalid arguments.  The value depends only on (op, B, T, C, in_dtype). */

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(PKG, "librwkv_wkv.so")
 WKV_OK, WKV_EINVAL, WKV_EDTYPE, WKV_ESIZE, WKV_EALIGN, WKV_EWORKSPACE, WKV_EHIP = range(7)
 WKV_F32, WKV_BF16 = 0, 1
 WKV_OP_FORWARD, WKV_OP_BACKWARD = 0, 1
-WKV_CKPT_LEN = 64
+WKV_CKPT_LEN = 16
 
 # every symbol include/wkv.h declares
 EXPORTS = (

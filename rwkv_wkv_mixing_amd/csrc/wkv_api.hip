@@ -40,7 +40,7 @@ struct Plan {
     int64_t nblk;
 };
 
-Plan plan_seq(int op, int64_t B, int64_t T, int64_t C, int dt) {
+Plan plan(int op, int64_t B, int64_t T, int64_t C, int dt) {
     Plan p{WKV_OK, 0, 0, 0};
     if (B < 0 || T < 0 || C < 0) return Plan{WKV_EINVAL, 0, 0, 0};
     if (!dtype_ok(dt)) return Plan{WKV_EDTYPE, 0, 0, 0};
@@ -51,7 +51,7 @@ Plan plan_seq(int op, int64_t B, int64_t T, int64_t C, int dt) {
     int64_t lanes;
     if (__builtin_mul_overflow(B, C, &lanes) || lanes > kMaxLanes) return Plan{WKV_ESIZE, 0, 0, 0};
     p.nblk = (T + wkv::kCkptLen - 1) / wkv::kCkptLen;
-    if (op == WKV_OP_BACKWARD && p.N > 0) p.ws_bytes = wkv::bwd_seq_workspace_bytes(B, T, C);
+    if (op == WKV_OP_BACKWARD && p.N > 0) p.ws_bytes = wkv::bwd_chunk_workspace_bytes(B, T, C);
     if (op == WKV_OP_FORWARD && p.N > 0) p.ws_bytes = wkv::fwd_chunk_workspace_bytes(B, T, C);
     return p;
 }
@@ -69,7 +69,7 @@ __global__ void zero2_kernel(int64_t n, float* a, float* b) {
 extern "C" {
 
 size_t wkv_workspace_bytes(int op, int64_t B, int64_t T, int64_t C, int in_dtype) {
-    const Plan p = plan_seq(op, B, T, C, in_dtype);
+    const Plan p = plan(op, B, T, C, in_dtype);
     return p.st == WKV_OK ? p.ws_bytes : 0;
 }
 
@@ -85,7 +85,7 @@ size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
 wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
                          const float* u, const void* k, const void* v, float* y, void* ckpt,
                          void* workspace, size_t workspace_bytes, void* hip_stream) {
-    const Plan p = plan_seq(WKV_OP_FORWARD, B, T, C, in_dtype);
+    const Plan p = plan(WKV_OP_FORWARD, B, T, C, in_dtype);
     if (p.st != WKV_OK) return p.st;
     if (p.N == 0) return WKV_OK;
     if (!w || !u || !k || !v || !y) return WKV_EINVAL;
@@ -104,7 +104,7 @@ wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const f
                           const float* u, const void* k, const void* v, const void* gy,
                           float* dk, float* dv, float* dw, float* du, const void* ckpt,
                           void* workspace, size_t workspace_bytes, void* hip_stream) {
-    const Plan p = plan_seq(WKV_OP_BACKWARD, B, T, C, in_dtype);
+    const Plan p = plan(WKV_OP_BACKWARD, B, T, C, in_dtype);
     if (p.st != WKV_OK) return p.st;
     if (C == 0) return WKV_OK;
     if (!dw || !du) return WKV_EINVAL;
@@ -120,11 +120,11 @@ wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const f
     if (!aligned(w, 4) || !aligned(u, 4) || !aligned(dk, 4) || !aligned(dv, 4) ||
         !aligned(k, es) || !aligned(v, es) || !aligned(gy, es) || (ckpt && !aligned(ckpt, 4)))
         return WKV_EALIGN;
-    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4)))
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
         return WKV_EWORKSPACE;
     wkv::BwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, gy, dk, dv, dw, du, ckpt, p.nblk,
                    workspace, workspace_bytes};
-    return hip_status(wkv::launch_bwd_seq(a, stream));
+    return hip_status(wkv::launch_bwd_chunk(a, stream));
 }
 
 wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype, const float* w,

@@ -1,0 +1,545 @@
+// Chunked (time-split) WKV backward for gfx950.
+//
+// Gradients of L = sum gy * y, derived by differentiating the weighted sum of
+// "RWKV（Receptance Weighted Key Value）概念", section 3.2 (the pages print no
+// backward; the float64 oracle documents the formulas).  The forward is
+// recomputed on chip from the block-start states the forward saved every
+// kCkptLen tokens, in the mean form (history mean m = A/B) so that output
+// differences never come from rounded outputs:
+//     delta = v - m,  pi = e^{u+k}/D,  rho = 2^s/D,  lam = e^k/B_t,  m_t = m + lam delta.
+// The reverse accumulators, scaled by 2^{s}, and the span offsets below are
+// kept in float64 (the per-token terms stay float32): at a dominant token
+// they sum ~10^2 signed terms of order one whose total can be ~10^-3 of
+// that, so their own rounding is kept well under the float32 rounding of
+// the terms; float64 FMAs issue at the rate of unpacked float32 ones on this
+// chip.  What makes the terms consistent with each other is the exact
+// integer-scale arithmetic of the lane state (the weight of a dominant token
+// has one float32 value everywhere).  The accumulators are
+//     G_{t-1}  = d G_t + gy_t rho_t
+//     J_{t-1}  = d (J_t + lam_t delta_t G_t) + gy_t rho_t pi_t delta_t     (J = H - m G)
+//     G'_{t-1} = d (G'_t + G_t)
+//     J'_{t-1} = d (J'_t + J_t + lam_t delta_t (G'_t + G_t))
+// and with e_t = e^{k_t}/2^{s_t}:
+//     dv_t = gy_t pi_t + e_t G_t
+//     dk_t = gy_t pi_t (1 - pi_t) delta_t + e_t ((1 - lam_t) delta_t G_t - J_t)
+// (1 - pi and 1 - lam are formed as rho b and d b / B_t, never by subtraction)
+//     du  += gy_t pi_t (1 - pi_t) delta_t,   dw -= e_t ((1 - lam_t) delta_t G'_t - J'_t).
+//
+// Work decomposition: as the forward, a workgroup owns 64 channels x W*L
+// tokens, wave i owns L tokens.  The reverse carry (G, J, G', J') through n
+// tokens is the affine map
+//     C_start = d^n [[1,0,0,0],[S,1,0,0],[n,0,1,0],[nS,n,S,1]] C_end + c0,
+//     S = sum lam_t delta_t,   c0 = sum_u d^u gr_u (1, P_u + pi_u delta_u, u, u (P_u + pi_u delta_u))
+// (gr_u = gy_u rho_u, P_u = sum_{t<u} lam_t delta_t, u counted from the span's
+// first token).  This form is closed under composition (n and S add), and its
+// offset accumulates in forward time during the recompute, so each wave
+// summarises its span without an extra reverse sweep.  Waves compose the maps
+// of the later waves through LDS; blocks are chained backward in time through
+// the same coherent 32-byte slots as the forward's carries.  dw and du are
+// per-block partial sums, reduced over batch rows and blocks in a fixed order.
+#include "wkv_launch.h"
+#include "wkv_scan.h"
+
+namespace wkv {
+
+struct BwdChunk {
+    int64_t B, T, C;
+    const float* w;
+    const float* u;
+    const void* k;
+    const void* v;
+    const void* gy;
+    float* dk;
+    float* dv;
+    const float* ckpt;
+    int64_t nblk_ck;
+    int64_t nct, ntiles, nblocks;
+    uint32_t* counter;
+    uint32_t* error;
+    float* carry;          // [ntiles][nblocks][64][12]: G, J, G', J' as hi/lo pairs, scale, 3 status words
+    uint32_t carry_bytes;
+    float* part;           // [ntiles][nblocks][2][64]: dw, du partial sums
+};
+
+// Reverse carry at log2-scale sg: the true G is G * 2^{-sg}.
+struct RCarry {
+    double G, J, Gp, Jp;
+    int sg;
+};
+
+// Affine reverse map of a span of n tokens (n = 0: identity).
+struct RMap {
+    double D;     // d^n
+    double S;
+    double c[4];  // offset, at scale so
+    float n;
+    int so;
+};
+
+__device__ __forceinline__ RMap rmap_identity() {
+    RMap m;
+    m.D = 1.0;
+    m.S = 0.0;
+    m.c[0] = m.c[1] = m.c[2] = m.c[3] = 0.0;
+    m.n = 0.f;
+    m.so = 0;
+    return m;
+}
+
+__device__ __forceinline__ RCarry rapply(const RMap& m, const RCarry& X) {
+    if (m.n == 0.f) return X;
+    const double f = ldexp(m.D, m.so - X.sg);
+    const double n = m.n, S = m.S;
+    RCarry r;
+    r.G = fma(f, X.G, m.c[0]);
+    r.J = fma(f, fma(S, X.G, X.J), m.c[1]);
+    r.Gp = fma(f, fma(n, X.G, X.Gp), m.c[2]);
+    r.Jp = fma(f, fma(n * S, X.G, fma(n, X.J, fma(S, X.Gp, X.Jp))), m.c[3]);
+    r.sg = m.so;
+    return r;
+}
+
+// a spans the tokens just before those of b.
+__device__ __forceinline__ RMap rcompose(const RMap& a, const RMap& b) {
+    if (b.n == 0.f) return a;
+    if (a.n == 0.f) return b;
+    const RCarry cb = rapply(a, RCarry{b.c[0], b.c[1], b.c[2], b.c[3], b.so});
+    RMap r;
+    r.D = a.D * b.D;
+    r.n = a.n + b.n;
+    r.S = a.S + b.S;
+    r.c[0] = cb.G;
+    r.c[1] = cb.J;
+    r.c[2] = cb.Gp;
+    r.c[3] = cb.Jp;
+    r.so = a.so;
+    return r;
+}
+
+// A carry crosses workgroups as float hi + lo pairs (about 48 significant
+// bits) in three 16-byte slots, each with its own status word, since the
+// three stores may become visible in any order.
+__device__ __forceinline__ float hi_of(double x) { return static_cast<float>(x); }
+__device__ __forceinline__ float lo_of(double x) {
+    return static_cast<float>(x - static_cast<double>(static_cast<float>(x)));
+}
+__device__ __forceinline__ double join(float hi, float lo) {
+    return static_cast<double>(hi) + static_cast<double>(lo);
+}
+
+constexpr uint32_t kCarrySlot = 48;
+
+__device__ __forceinline__ void publish_carry(Rsrc r, uint32_t off, const RCarry& c) {
+    const float one = __uint_as_float(1u);
+    const f32x4 v0 = {hi_of(c.G), lo_of(c.G), hi_of(c.J), one};
+    const f32x4 v1 = {lo_of(c.J), hi_of(c.Gp), lo_of(c.Gp), one};
+    const f32x4 v2 = {hi_of(c.Jp), lo_of(c.Jp), __int_as_float(c.sg), one};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v0), r, off, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v1), r, off + 16, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v2), r, off + 32, 0, kCoherent);
+}
+
+__device__ __forceinline__ RCarry wait_carry(Rsrc r, uint32_t off, uint32_t* error) {
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        const f32x4 v0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+        const f32x4 v1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kCoherent));
+        const f32x4 v2 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 32, 0, kCoherent));
+        if ((__float_as_uint(v0.w) != 0u) & (__float_as_uint(v1.w) != 0u) & (__float_as_uint(v2.w) != 0u))
+            return RCarry{join(v0.x, v0.y), join(v0.z, v1.x), join(v1.y, v1.z), join(v2.x, v2.y),
+                          __float_as_int(v2.z)};
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return RCarry{0.0, 0.0, 0.0, 0.0, 0};
+}
+
+template <typename TIn, int L>
+struct GyChunk {
+    float g[L];
+    __device__ __forceinline__ void load(Rsrc r, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) g[j] = BufLd<TIn>::at(r, voff, j * row);
+    }
+};
+
+template <typename TIn, int L>
+struct KvChunk;
+
+template <int L>
+struct KvChunk<uint16_t, L> {
+    uint32_t kv[L];
+    __device__ __forceinline__ void load(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rk, voff, j * row, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rv, voff, j * row, 0);
+            kv[j] = lo | (hi << 16);
+        }
+    }
+    __device__ __forceinline__ float k(int j) const { return __uint_as_float(kv[j] << 16); }
+    __device__ __forceinline__ float v(int j) const { return __uint_as_float(kv[j] & 0xffff0000u); }
+};
+
+template <int L>
+struct KvChunk<float, L> {
+    float kk[L], vv[L];
+    __device__ __forceinline__ void load(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            kk[j] = BufLd<float>::at(rk, voff, j * row);
+            vv[j] = BufLd<float>::at(rv, voff, j * row);
+        }
+    }
+    __device__ __forceinline__ float k(int j) const { return kk[j]; }
+    __device__ __forceinline__ float v(int j) const { return vv[j]; }
+};
+
+template <typename TIn, int L, int W>
+__global__ void __launch_bounds__(64 * W) bwd_chunk_kernel(BwdChunk P) {
+    constexpr int ES = BufLd<TIn>::kBytes;
+    __shared__ double sm_mapd[W][5][64];  // S, c0..c3
+    __shared__ float sm_mapn[W][64];
+    __shared__ int sm_maps[W][64];
+    __shared__ double sm_cin[4][64];
+    __shared__ int sm_cin_s[64];
+    __shared__ float sm_red[W][2][64];
+    __shared__ uint32_t sm_ticket;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    int64_t ticket = blockIdx.x;
+    if (P.nblocks > 1) {
+        if (threadIdx.x == 0) sm_ticket = atomicAdd(P.counter, 1u);
+        __syncthreads();
+        ticket = sm_ticket;
+    }
+    const int64_t rblk = ticket / P.ntiles;  // blocks are handed out last-in-time first
+    const int64_t tile = ticket - rblk * P.ntiles;
+    const int64_t blk = P.nblocks - 1 - rblk;
+    const int64_t b = tile / P.nct;
+    const int64_t c = (tile - b * P.nct) * 64 + lane;
+    const bool cok = c < P.C;
+    const int64_t tb0 = blk * (int64_t)(L * W);
+    const int64_t t0 = tb0 + (int64_t)wave * L;
+    const int64_t rem = P.T - t0;
+    const int nvalid = rem <= 0 ? 0 : (rem >= L ? L : static_cast<int>(rem));
+    const float wc = cok ? P.w[c] : 0.f;
+    const float uc = cok ? P.u[c] : 0.f;
+    const Chan ch = make_chan(wc, uc);
+    const bool fast = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
+    const float eu = ex2(ch.u2);
+
+    const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
+    const int64_t row0 = (b * P.T + tb0) * P.C;
+    const uint32_t nin = (uint32_t)(blk_tokens * P.C * ES), nout = (uint32_t)(blk_tokens * P.C * 4);
+    const Rsrc rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, nin);
+    const Rsrc rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, nin);
+    const Rsrc rg = make_rsrc(static_cast<const TIn*>(P.gy) + row0, nin);
+    const Rsrc rdk = make_rsrc(P.dk + row0, nout);
+    const Rsrc rdv = make_rsrc(P.dv + row0, nout);
+    const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;
+    const uint32_t vin = cok ? lin * ES : kOffNone;
+    const uint32_t vout = cok ? lin * 4 : kOffNone;
+    const uint32_t row_in = (uint32_t)(P.C * ES), row_out = (uint32_t)(P.C * 4);
+
+    KvChunk<TIn, L> kv;
+    kv.load(rk, rv, vin, row_in);
+    GyChunk<TIn, L> gy;
+    gy.load(rg, vin, row_in);
+
+    // state at the first token of this wave's span, saved by the forward
+    float m = 0.f, bb = 0.f;
+    int sc = kSEmpty;
+    if (cok && nvalid > 0) {
+        const float* cp = P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c;
+        const float a0 = cp[0], b0 = cp[P.C];
+        bb = b0;
+        sc = static_cast<int>(cp[2 * P.C]);
+        m = b0 > 0.f ? a0 / b0 : 0.f;
+    }
+
+    // ---- forward recompute (mean form) + this span's reverse map -----------------
+    // Per token the reverse sweep needs pi, rho, e and the products
+    //   vy = (1 - pi) delta,  vm = (1 - lam) delta,  ld = lam delta,  pd = pi delta,
+    // where 1 - pi = rho b and 1 - lam = d b / B_t are formed without
+    // cancellation (pi and lam come within an ulp of 1 at dominant tokens).
+    float pi_[L], rho_[L], e_[L], vy_[L], vm_[L], ld_[L], pd_[L];
+    int s_[L];
+    // The span's offset sums cancel like the reverse accumulators: float64.
+    const double dd = exp(-static_cast<double>(wc));
+    double Psum = 0.0, dpow = 1.0, Gs = 0.0, Js = 0.0, Gps = 0.0, Jps = 0.0;
+    int s0 = 0;
+    bool resc = false;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        if (j < nvalid) {
+            const float vj = kv.v(j), gj = gy.g[j];
+            const Key kk = key_split(kv.k(j));
+            const bool out = (kk.n - sc > static_cast<int>(kBig)) | !(bb >= kLo) | (bb > kHi);
+            if (__builtin_expect(out, 0)) {
+                const int lvl = bb > 0.f ? sc + __builtin_amdgcn_frexp_expf(bb) : kSEmpty;
+                const int sn = max(lvl, kk.n);
+                bb = ldx(bb, sc - sn);
+                if (j > 0) {
+                    dpow = ldexp(dpow, sc - sn);
+                    resc = true;
+                }
+                sc = sn;
+            }
+            if (j == 0) s0 = sc;
+            const float e = ldx(kk.em, kk.n - sc);
+            float pi, rho;
+            if (fast) {
+                const float E = e * eu;
+                const float r = rcp(bb + E);
+                pi = E * r;
+                rho = r;
+            } else {
+                const float z = static_cast<float>(kk.n - sc) + kk.f + ch.u2;
+                const float ez = ex2(-fabsf(z));
+                const bool zp = z > 0.f;
+                const float co = zp ? ez : 1.f;
+                const float cn = zp ? 1.f : ez;
+                const float r = rcp(fmaf(bb, co, cn));
+                pi = cn * r;
+                rho = co * r;
+            }
+            const float dl = vj - m;
+            const float vy = (rho * bb) * dl;
+            const float db = fmaf(ch.dhi, bb, ch.dlo * bb);
+            bb = db + e;
+            const float rb = rcp(fmaxf(bb, 1e-37f));
+            const float ld = (e * rb) * dl;
+            const float vm = (db * rb) * dl;
+            const float pd = pi * dl;
+            m += ld;
+            pi_[j] = pi;
+            rho_[j] = rho;
+            e_[j] = e;
+            vy_[j] = vy;
+            vm_[j] = vm;
+            ld_[j] = ld;
+            pd_[j] = pd;
+            s_[j] = sc;
+            // offset of the reverse map: sum_u d^u 2^{s0 - s_u} gr_u (1, P_u + pd_u, u, u (...))
+            const double q = dpow * static_cast<double>(gj * rho);
+            const double t1 = Psum + static_cast<double>(pd);
+            Gs += q;
+            Js = fma(q, t1, Js);
+            Gps = fma(q, static_cast<double>(j), Gps);
+            Jps = fma(q * t1, static_cast<double>(j), Jps);
+            Psum += static_cast<double>(ld);
+            dpow *= dd;
+        }
+    }
+    sm_mapn[wave][lane] = static_cast<float>(nvalid);
+    sm_maps[wave][lane] = s0;
+    sm_mapd[wave][0][lane] = Psum;
+    sm_mapd[wave][1][lane] = Gs;
+    sm_mapd[wave][2][lane] = Js;
+    sm_mapd[wave][3][lane] = Gps;
+    sm_mapd[wave][4][lane] = Jps;
+    __syncthreads();
+
+    // ---- reverse scan: compose the maps of the later waves ------------------------
+    const double dL = exp(-static_cast<double>(wc) * L);
+    auto load_map = [&](int i) {
+        RMap r;
+        r.n = sm_mapn[i][lane];
+        r.so = sm_maps[i][lane];
+        r.S = sm_mapd[i][0][lane];
+        r.c[0] = sm_mapd[i][1][lane];
+        r.c[1] = sm_mapd[i][2][lane];
+        r.c[2] = sm_mapd[i][3][lane];
+        r.c[3] = sm_mapd[i][4][lane];
+        r.D = (r.n == static_cast<float>(L)) ? dL : exp(-static_cast<double>(wc) * r.n);
+        return r;
+    };
+    RMap suf = rmap_identity();
+    for (int i = W - 1; i > wave; --i) suf = rcompose(load_map(i), suf);
+    if (wave == 0) {
+        RCarry cin{0.0, 0.0, 0.0, 0.0, 0};
+        if (P.nblocks > 1) {
+            const Rsrc rc = make_rsrc(P.carry, P.carry_bytes);
+            const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * kCarrySlot);
+            if (blk < P.nblocks - 1) cin = wait_carry(rc, slot + 64 * kCarrySlot, P.error);  // block blk+1
+            if (blk > 0) publish_carry(rc, slot, rapply(rcompose(load_map(0), suf), cin));
+        }
+        sm_cin[0][lane] = cin.G;
+        sm_cin[1][lane] = cin.J;
+        sm_cin[2][lane] = cin.Gp;
+        sm_cin[3][lane] = cin.Jp;
+        sm_cin_s[lane] = cin.sg;
+    }
+    __syncthreads();
+    RCarry C = rapply(suf, RCarry{sm_cin[0][lane], sm_cin[1][lane], sm_cin[2][lane], sm_cin[3][lane],
+                                  sm_cin_s[lane]});
+
+    // ---- reverse pass from the true carry ---------------------------------------
+    float acc_dw = 0.f, acc_du = 0.f;
+    {
+        // bring the carry to the scale of this span's last token
+        int slast = 0;
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+            if (j == nvalid - 1) slast = s_[j];
+        const int dsc = slast - C.sg;
+        double G = ldexp(C.G, dsc), J = ldexp(C.J, dsc), Gp = ldexp(C.Gp, dsc), Jp = ldexp(C.Jp, dsc);
+#pragma unroll
+        for (int j = L - 1; j >= 0; --j) {
+            if (j < nvalid) {
+                const float g = gy.g[j], e = e_[j];
+                const double vm = vm_[j], ld = ld_[j];
+                const float gpi = g * pi_[j];
+                buf_store(fmaf(e, static_cast<float>(G), gpi), rdv, vout, j * row_out);
+                buf_store(fmaf(gpi, vy_[j], e * static_cast<float>(fma(vm, G, -J))), rdk, vout, j * row_out);
+                acc_du = fmaf(gpi, vy_[j], acc_du);
+                acc_dw = fmaf(e, static_cast<float>(fma(vm, Gp, -Jp)), acc_dw);
+                const float gr = g * rho_[j];
+                const double GG = Gp + G;
+                Jp = dd * fma(ld, GG, Jp + J);
+                Gp = dd * GG;
+                J = fma(dd, fma(ld, G, J), static_cast<double>(gr * pd_[j]));
+                G = fma(dd, G, static_cast<double>(gr));
+                if (resc && j > 0) {
+                    if (s_[j - 1] != s_[j]) {
+                        const int ds = s_[j - 1] - s_[j];
+                        G = ldexp(G, ds);
+                        J = ldexp(J, ds);
+                        Gp = ldexp(Gp, ds);
+                        Jp = ldexp(Jp, ds);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- dw, du partial sums of this block (fixed order over waves) -------------
+    sm_red[wave][0][lane] = -acc_dw;
+    sm_red[wave][1][lane] = acc_du;
+    __syncthreads();
+    if (wave == 0) {
+        float sw = 0.f, su = 0.f;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            sw += sm_red[i][0][lane];
+            su += sm_red[i][1][lane];
+        }
+        float* pp = P.part + ((tile * P.nblocks + blk) * 2) * 64 + lane;
+        pp[0] = sw;
+        pp[64] = su;
+    }
+}
+
+__global__ void bwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < 2) hdr[i] = 0u;
+    for (int64_t j = i; j < nwords; j += static_cast<int64_t>(gridDim.x) * blockDim.x) carry_words[j] = 0u;
+}
+
+// dw[c] = sum over batch rows and time blocks (in that fixed order) of the partials.
+__global__ void bwd_chunk_reduce_kernel(int64_t B, int64_t C, int64_t nct, int64_t nblocks,
+                                        const float* __restrict__ part, float* __restrict__ dw,
+                                        float* __restrict__ du) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    const int64_t ct = c / 64, lane = c % 64;
+    float sw = 0.f, su = 0.f;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nblocks; ++j) {
+            const float* pp = part + (((b * nct + ct) * nblocks + j) * 2) * 64 + lane;
+            sw += pp[0];
+            su += pp[64];
+        }
+    dw[c] = sw;
+    du[c] = su;
+}
+
+namespace {
+#ifndef WKV_BWD_L
+#define WKV_BWD_L 16
+#endif
+#ifndef WKV_BWD_W
+#define WKV_BWD_W 8
+#endif
+constexpr int kBwdL = WKV_BWD_L;
+constexpr int kBwdW = WKV_BWD_W;
+static_assert(kBwdL % kCkptLen == 0, "backward spans must start on saved forward states");
+
+struct BwdLayout {
+    int64_t nct, ntiles, nblocks, nblk_ck;
+    size_t off_carry, carry_bytes, off_part, off_ckpt, ckpt_bytes, off_fws, fws_bytes, bytes;
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C) {
+    BwdLayout l{};
+    l.nct = (C + 63) / 64;
+    l.ntiles = B * l.nct;
+    l.nblocks = (T + kBwdL * kBwdW - 1) / (kBwdL * kBwdW);
+    l.nblk_ck = (T + kCkptLen - 1) / kCkptLen;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t off = 256;
+    l.off_carry = off;
+    l.carry_bytes = l.nblocks > 1 ? static_cast<size_t>(l.ntiles * l.nblocks * 64) * kCarrySlot : 0;
+    off = up(off + l.carry_bytes);
+    l.off_part = off;
+    off = up(off + static_cast<size_t>(l.ntiles * l.nblocks * 2 * 64) * 4);
+    l.off_ckpt = off;
+    l.ckpt_bytes = static_cast<size_t>(B * l.nblk_ck * C) * 12;
+    off = up(off + l.ckpt_bytes);
+    l.off_fws = off;
+    l.fws_bytes = fwd_chunk_workspace_bytes(B, T, C);
+    l.bytes = off + l.fws_bytes;
+    return l;
+}
+}  // namespace
+
+size_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C) { return bwd_layout(B, T, C).bytes; }
+
+template <typename TIn>
+hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
+    const BwdLayout l = bwd_layout(a.B, a.T, a.C);
+    char* ws = static_cast<char*>(a.ws);
+    const float* ckpt = static_cast<const float*>(a.ckpt);
+    if (ckpt == nullptr) {  // recompute the block-start states with the forward (no y written)
+        FwdArgs f{a.B, a.T, a.C, a.bf16, a.w, a.u, a.k, a.v, nullptr, ws + l.off_ckpt, l.nblk_ck,
+                  ws + l.off_fws, l.fws_bytes};
+        const hipError_t e = launch_fwd_chunk(f, stream);
+        if (e != hipSuccess) return e;
+        ckpt = reinterpret_cast<const float*>(ws + l.off_ckpt);
+    }
+    BwdChunk P{};
+    P.B = a.B; P.T = a.T; P.C = a.C;
+    P.w = a.w; P.u = a.u; P.k = a.k; P.v = a.v; P.gy = a.gy;
+    P.dk = a.dk; P.dv = a.dv;
+    P.ckpt = ckpt;
+    P.nblk_ck = l.nblk_ck;
+    P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+    P.counter = reinterpret_cast<uint32_t*>(ws);
+    P.error = P.counter + 1;
+    P.carry = reinterpret_cast<float*>(ws + l.off_carry);
+    P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
+    P.part = reinterpret_cast<float*>(ws + l.off_part);
+    if (l.nblocks > 1) {
+        const int64_t nwords = static_cast<int64_t>(l.carry_bytes / 4);
+        int64_t g = (nwords + 255) / 256;
+        if (g > 4096) g = 4096;
+        hipLaunchKernelGGL(bwd_chunk_init_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream,
+                           P.counter, reinterpret_cast<uint32_t*>(P.carry), nwords);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW>), dim3(static_cast<unsigned>(l.ntiles * l.nblocks)),
+                       dim3(64 * kBwdW), 0, stream, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,
+                       stream, a.B, a.C, l.nct, l.nblocks, P.part, a.dw, a.du);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
+    return a.bf16 ? launch_bwd_chunk_t<uint16_t>(a, stream) : launch_bwd_chunk_t<float>(a, stream);
+}
+
+}  // namespace wkv

@@ -6,15 +6,24 @@
 //     A_t = d A_{t-1} + e^{k_t} v_t,   B_t = d B_{t-1} + e^{k_t},  d = e^{-w}
 //
 // Representation used on chip.  The state of a lane is (a, b, s) with
-// A = a * 2^s and B = b * 2^s: a float32 log2-scale s plus two float32
-// mantissas ("the stability exponent" of section "关键设计 4", kept in base 2
-// so that every exponential is one v_exp_f32).  Unlike a per-token running
-// max, s only moves on a RESCALE, when a new key would exceed the scale by
-// 2^32 or b leaves [2^-32, 2^32]; in between, the decay is applied to (a, b)
-// as a product with d split into float32 hi + lo parts.  A per-token exponent
-// update p <- p - w would round the same way at every token and act as a
-// systematic error in w that grows with the memory length 1/w; the split
-// product keeps the decay exact to ~2^-48 instead.
+// A = a * 2^s and B = b * 2^s: an INTEGER log2-scale s plus two float32
+// mantissas ("the stability exponent" of section "关键设计 4", kept in base 2).
+// Unlike a per-token running max, s only moves on a RESCALE, when a new key
+// would exceed the scale by 2^32 or b leaves [2^-32, 2^32]; in between, the
+// decay is applied to (a, b) as a product with d split into float32 hi + lo
+// parts.  A per-token exponent update p <- p - w would round the same way at
+// every token and act as a systematic error in w that grows with the memory
+// length 1/w; the split product keeps the decay exact to ~2^-48 instead.
+//
+// Each key enters as e^k = em * 2^n with the integer n = rint(k log2 e) and
+// em = 2^{k log2 e - n} in [2^-1/2, 2^1/2], a function of k alone.  Because s
+// is an integer, moving a weight or a state to another scale is an exact
+// ldexp: a token's weight carries the same float32 rounding in every pass and
+// kernel that meets it, and joining states of different scales adds no
+// rounding.  (A fractional scale would put the rounding of k log2 e - s, up
+// to 2^-19 relative near |x| = 32, into every weight, differently in every
+// pass; sums that cancel, such as the gradient at a dominant token, amplify
+// such inconsistencies.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +40,7 @@ constexpr float kBig = 32.0f;                // log2(kHi)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float ldx(float x, int e) { return __builtin_amdgcn_ldexpf(x, e); }
 
 // ---- inputs: float32 or bfloat16 (raw bits), widened exactly to float32 ----
 template <typename TIn>
@@ -100,35 +110,53 @@ __device__ __forceinline__ Chan make_chan(float w, float u) {
     return ch;
 }
 
-// ---- lane state ---------------------------------------------------------------
-struct St {
-    float a, b, s;  // A = a 2^s, B = b 2^s
+// ---- keys -----------------------------------------------------------------------
+constexpr float kNMax = 4194304.0f;  // |n| clamp (2^22): keys beyond |k| ~ 2.9e6 saturate
+
+struct Key {
+    float em;  // 2^f, f = k log2 e - n
+    float f;
+    int n;
 };
 
-__device__ __forceinline__ St empty_state() { return St{0.f, 0.f, -INFINITY}; }
+__device__ __forceinline__ Key key_split(float k) {
+    const float n = __builtin_amdgcn_fmed3f(__builtin_rintf(k * kL2E), -kNMax, kNMax);
+    const float f = fmaf(k, kL2E, -n);
+    return Key{ex2(f), f, static_cast<int>(n)};
+}
 
-// Move the scale so that the new term (k2 = k log2 e) and the state both fit:
-// s' = max(k2, s + log2 b).  Afterwards b <= 1 and the new term is <= 1.
-__device__ __forceinline__ void rescale(St& st, float k2) {
-    const float lvl = st.b > 0.f ? st.s + lg2(st.b) : -INFINITY;
-    const float sn = fmaxf(lvl, k2);
-    const float f = ex2(st.s - sn);
-    st.a *= f;
-    st.b *= f;
+// ---- lane state ---------------------------------------------------------------
+constexpr int kSEmpty = -(1 << 29);  // scale of the empty state (a = b = 0)
+
+struct St {
+    float a, b;  // A = a 2^s, B = b 2^s
+    int s;
+};
+
+__device__ __forceinline__ St empty_state() { return St{0.f, 0.f, kSEmpty}; }
+
+// Move the scale to s' = max(n, s + E(b)), b < 2^E(b): afterwards b < 1 and
+// the new weight em 2^(n - s') <= 2^1/2.  Exact (powers of two).
+__device__ __forceinline__ void rescale(St& st, int n) {
+    const int lvl = st.b > 0.f ? st.s + __builtin_amdgcn_frexp_expf(st.b) : kSEmpty;
+    const int sn = max(lvl, n);
+    st.a = ldx(st.a, st.s - sn);
+    st.b = ldx(st.b, st.s - sn);
     st.s = sn;
 }
 
-// x = k log2 e - s, rescaling first when the new term or b is out of range.
-// The three conditions are folded into one mask so the rare rescale costs a
-// single branch per token.
-__device__ __forceinline__ float key_offset(St& st, float k) {
-    float x = fmaf(k, kL2E, -st.s);
-    const bool out = (x > kBig) | !(st.b >= kLo) | (st.b > kHi);
-    if (__builtin_expect(out, 0)) {
-        rescale(st, k * kL2E);
-        x = fmaf(k, kL2E, -st.s);
-    }
-    return x;
+// Rescale first when the new weight or b is out of range; the three
+// conditions are folded into one mask so the rare rescale costs a single
+// branch per token.  Returns the weight e = e^k / 2^s.
+__device__ __forceinline__ float key_weight(St& st, const Key& kk) {
+    const bool out = (kk.n - st.s > static_cast<int>(kBig)) | !(st.b >= kLo) | (st.b > kHi);
+    if (__builtin_expect(out, 0)) rescale(st, kk.n);
+    return ldx(kk.em, kk.n - st.s);
+}
+
+// log2 of the weight relative to 2^s (rounded; used only to normalise outputs).
+__device__ __forceinline__ float key_log2(const St& st, const Key& kk) {
+    return static_cast<float>(kk.n - st.s) + kk.f;
 }
 
 // Output of one token from the state before it (robust to any u):
@@ -155,7 +183,7 @@ __device__ __forceinline__ Out token_out(const St& st, float x, float v, const C
 }
 
 // Output of one token when |u| is small enough that the current-token weight
-// e^{u} 2^x cannot overflow (|u| <= kFastU with x <= 32): one multiply instead
+// e^{u} e cannot overflow (|u| <= kFastU with e <= 2^32): one multiply instead
 // of the normalised two-branch form.
 constexpr float kFastU = 40.0f;
 
@@ -164,21 +192,11 @@ __device__ __forceinline__ float token_out_fast(const St& st, float e, float v, 
     return fmaf(E, v, st.a) * rcp(st.b + E);
 }
 
-// Decay-and-add with e = 2^x already computed.
+// Decay-and-add of one token with weight e: A <- d A + e v, B <- d B + e, d = dhi + dlo.
 __device__ __forceinline__ void token_add(St& st, float e, float v, const Chan& ch) {
     const float ev = e * v;
     st.a = fmaf(ch.dhi, st.a, fmaf(ch.dlo, st.a, ev));
     st.b = fmaf(ch.dhi, st.b, fmaf(ch.dlo, st.b, e));
-}
-
-// Decay-and-add of one token: A <- d A + e^k v, B <- d B + e^k, d = dhi + dlo.
-// Returns e = 2^x = e^{k} / 2^s.
-__device__ __forceinline__ float token_update(St& st, float x, float v, const Chan& ch) {
-    const float e = ex2(x);
-    const float ev = e * v;
-    st.a = fmaf(ch.dhi, st.a, fmaf(ch.dlo, st.a, ev));
-    st.b = fmaf(ch.dhi, st.b, fmaf(ch.dlo, st.b, e));
-    return e;
 }
 
 }  // namespace wkv

@@ -8,12 +8,11 @@
 // two passes, so HBM sees each input once and each output once.
 //
 //   pass 1  every wave runs its L tokens from the empty state -> summary S_i
-//   scan    wave 0 combines S_0..S_{W-1} in LDS into per-wave prefixes and the
-//           block aggregate, obtains the block's carry-in E from the
-//           preceding blocks of the same tile (decoupled look-back over
-//           global flags, blocks handed out by an atomic ticket in time order
-//           so every awaited block is already running), and publishes the
-//           block's inclusive state
+//   scan    through LDS every wave combines S_0..S_{i-1} into its prefix P_i;
+//           the last wave also waits for the inclusive state E of the
+//           previous time block of the same tile (blocks are handed out by an
+//           atomic ticket in time order, so the awaited block is already
+//           running) and publishes this block's inclusive state
 //   pass 2  every wave re-runs its L tokens from carry-in d^{iL} E + P_i and
 //           writes y (and the saved block-start states for the backward).
 //
@@ -76,25 +75,26 @@ struct SubChunk<float, L> {
     __device__ __forceinline__ float v(int j) const { return vv[j]; }
 };
 
-// Pass 2 over a sub-chunk: outputs from the carry-in state.
+// Pass 2 over a sub-chunk: outputs from the carry-in state, and the state
+// before every kCkptLen-th token into ckpt (when given) for the backward.
 template <bool Fast, typename TIn, int L>
 __device__ __forceinline__ void fwd_outputs(St st, const SubChunk<TIn, L>& sc, int nvalid,
                                             const Chan& ch, float eu, Rsrc ry, uint32_t vout,
-                                            uint32_t row_out) {
+                                            uint32_t row_out, float* ckp, int64_t ckstride) {
 #pragma unroll
     for (int j = 0; j < L; ++j) {
         if (j < nvalid) {
-            const float kj = sc.k(j), vj = sc.v(j);
-            const float x = key_offset(st, kj);
-            float yj;
-            if (Fast) {
-                const float e = ex2(x);
-                yj = token_out_fast(st, e, vj, eu);
-                token_add(st, e, vj, ch);
-            } else {
-                yj = token_out(st, x, vj, ch).y;
-                token_update(st, x, vj, ch);
+            if ((j % kCkptLen) == 0 && ckp != nullptr) {
+                float* cp = ckp + (j / kCkptLen) * 3 * ckstride;
+                cp[0] = st.a;
+                cp[ckstride] = st.b;
+                cp[2 * ckstride] = static_cast<float>(st.s);
             }
+            const Key kk = key_split(sc.k(j));
+            const float vj = sc.v(j);
+            const float e = key_weight(st, kk);
+            const float yj = Fast ? token_out_fast(st, e, vj, eu) : token_out(st, key_log2(st, kk), vj, ch).y;
+            token_add(st, e, vj, ch);
             buf_store(yj, ry, vout, j * row_out);
         }
     }
@@ -105,8 +105,9 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     constexpr int ES = BufLd<TIn>::kBytes;
     __shared__ float sm_a[W][64];
     __shared__ float sm_b[W][64];
-    __shared__ float sm_s[W][64];
-    __shared__ float sm_e[3][64];  // block carry-in E
+    __shared__ int sm_s[W][64];
+    __shared__ float sm_e[2][64];  // block carry-in E
+    __shared__ int sm_es[64];
     __shared__ uint32_t sm_ticket;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -137,7 +138,8 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     const int64_t row0 = (b * P.T + tb0) * P.C;
     const Rsrc rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, (uint32_t)(blk_tokens * P.C * ES));
     const Rsrc rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, (uint32_t)(blk_tokens * P.C * ES));
-    const Rsrc ry = make_rsrc(P.y + row0, (uint32_t)(blk_tokens * P.C * 4));
+    // y == nullptr (the backward's state-only run): a zero-size buffer drops every store
+    const Rsrc ry = P.y != nullptr ? make_rsrc(P.y + row0, (uint32_t)(blk_tokens * P.C * 4)) : make_rsrc(nullptr, 0);
     const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;  // element offset
     const uint32_t vin = cok ? lin * ES : kOffNone;
     const uint32_t vout = cok ? lin * 4 : kOffNone;
@@ -151,8 +153,8 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
 #pragma unroll
     for (int j = 0; j < L; ++j) {
         if (j < nvalid) {
-            const float x = key_offset(st, sc.k(j));
-            token_update(st, x, sc.v(j), ch);
+            const float e = key_weight(st, key_split(sc.k(j)));
+            token_add(st, e, sc.v(j), ch);
         }
     }
     sm_a[wave][lane] = st.a;
@@ -180,24 +182,19 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
         }
         sm_e[0][lane] = E.a;
         sm_e[1][lane] = E.b;
-        sm_e[2][lane] = E.s;
+        sm_es[lane] = E.s;
     }
     __syncthreads();
     double dpow = 1.0;
     for (int i = 0; i < wave; ++i) dpow *= dL;
-    const St s2 = combine(St{sm_e[0][lane], sm_e[1][lane], sm_e[2][lane]}, pref, dpow);
+    const St s2 = combine(St{sm_e[0][lane], sm_e[1][lane], sm_es[lane]}, pref, dpow);
 
     // ---- pass 2: outputs from the carry-in -------------------------------------
-    if (P.ckpt != nullptr && cok && nvalid > 0 && (t0 % kCkptLen) == 0) {
-        float* cp = P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c;
-        cp[0] = s2.a;
-        cp[P.C] = s2.b;
-        cp[2 * P.C] = s2.s;
-    }
+    float* ckp = (P.ckpt != nullptr && cok) ? P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c : nullptr;
     if (fast)
-        fwd_outputs<true>(s2, sc, nvalid, ch, eu, ry, vout, row_out);
+        fwd_outputs<true>(s2, sc, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
     else
-        fwd_outputs<false>(s2, sc, nvalid, ch, eu, ry, vout, row_out);
+        fwd_outputs<false>(s2, sc, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
 }
 
 __global__ void fwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {

@@ -8,7 +8,7 @@
 
 namespace wkv {
 
-constexpr int64_t kCkptLen = 64;  // = WKV_CKPT_LEN in include/wkv.h
+constexpr int64_t kCkptLen = 16;  // = WKV_CKPT_LEN in include/wkv.h
 
 struct FwdArgs {
     int64_t B, T, C;
@@ -60,10 +60,9 @@ struct StepArgs {
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t stream);
 size_t fwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C);
 
-// lane-sequential kernels (wkv_seq.hip)
-hipError_t launch_fwd_seq(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_seq(const BwdArgs& a, hipStream_t stream);
-size_t bwd_seq_workspace_bytes(int64_t B, int64_t T, int64_t C);
+// chunked backward (wkv_bwd.hip)
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream);
+size_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C);
 
 // decode step (wkv_step.hip)
 hipError_t launch_step(const StepArgs& s, hipStream_t stream);

@@ -17,8 +17,8 @@ namespace wkv {
 // Combine a state X (at the start of an n-token interval) with the summary S
 // of that interval; D = d^n in double, applied as a float32 hi + lo product.
 // The result keeps X's scale unless the summary would not fit (lazy
-// rescale), so the history is multiplied by D only and never by a rounded
-// rescale factor in the common case.
+// rescale).  Scales are integers, so bringing both terms to the common scale
+// is exact and the only roundings are the decay product and the final sums.
 __device__ __forceinline__ St combine(const St& X, const St& S, double D) {
     const float Dhi = static_cast<float>(D);
     const float Dlo = static_cast<float>(D - static_cast<double>(Dhi));
@@ -26,18 +26,17 @@ __device__ __forceinline__ St combine(const St& X, const St& S, double D) {
     const float xb = fmaf(Dhi, X.b, Dlo * X.b);
     if (!(S.b > 0.f)) return St{xa, xb, X.s};
     if (!(xb > 0.f)) return S;
-    float sn = X.s;
-    const float ls = S.s + lg2(S.b);
-    if ((ls > X.s + kBig) | (xb < kLo) | (xb > kHi)) sn = fmaxf(X.s + lg2(xb), ls);
-    const float fx = (sn == X.s) ? 1.f : ex2(X.s - sn);
-    const float fs = ex2(S.s - sn);
-    return St{fmaf(xa, fx, S.a * fs), fmaf(xb, fx, S.b * fs), sn};
+    int sn = X.s;
+    const int ls = S.s + __builtin_amdgcn_frexp_expf(S.b);  // S.b 2^S.s < 2^ls
+    if ((ls > X.s + static_cast<int>(kBig)) | (xb < kLo) | (xb > kHi))
+        sn = max(X.s + __builtin_amdgcn_frexp_expf(xb), ls);
+    return St{ldx(xa, X.s - sn) + ldx(S.a, S.s - sn), ldx(xb, X.s - sn) + ldx(S.b, S.s - sn), sn};
 }
 
 // ---- carries between workgroups --------------------------------------------------
 // A chained scan along time: the workgroup of time block j waits for the
 // inclusive state of block j-1 of the same tile and publishes its own.  Each
-// (tile, block, lane) slot is 16 bytes (a, b, s, status) written with ONE
+// (tile, block, lane) slot is 16 bytes (a, b, s bits, status) written with ONE
 // 16-byte store and polled with 16-byte loads, both with the system-coherent
 // cache policy (sc0 sc1), which bypasses the per-XCD L2s.  So no release or
 // acquire fence is needed: such fences would write back or invalidate the
@@ -53,7 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void publish_state(Rsrc r, uint32_t off, const St& st) {
-    const f32x4 v = {st.a, st.b, st.s, __uint_as_float(1u)};
+    const f32x4 v = {st.a, st.b, __int_as_float(st.s), __uint_as_float(1u)};
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
 }
 
@@ -63,7 +62,7 @@ __device__ __forceinline__ void publish_state(Rsrc r, uint32_t off, const St& st
 __device__ __forceinline__ St wait_state(Rsrc r, uint32_t off, uint32_t* error) {
     for (uint32_t it = 0; it < kSpinLimit; ++it) {
         const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
-        if (__float_as_uint(v.w) != 0u) return St{v.x, v.y, v.z};
+        if (__float_as_uint(v.w) != 0u) return St{v.x, v.y, __float_as_int(v.z)};
         __builtin_amdgcn_s_sleep(1);
     }
     __hip_atomic_store(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -45,7 +45,7 @@ def test_version_and_status_strings(lib):
 
 def test_header_constants_match_binding():
     src = open(HEADER).read()
-    assert "#define WKV_CKPT_LEN 64" in src and L.WKV_CKPT_LEN == 64
+    assert "#define WKV_CKPT_LEN 16" in src and L.WKV_CKPT_LEN == 16
     for name, val in (("WKV_OK", 0), ("WKV_EINVAL", 1), ("WKV_EDTYPE", 2), ("WKV_ESIZE", 3),
                       ("WKV_EALIGN", 4), ("WKV_EWORKSPACE", 5), ("WKV_EHIP", 6)):
         assert re.search(rf"{name} = {val}\b", src), name
@@ -61,8 +61,8 @@ def test_workspace_and_ckpt_sizes(lib):
         assert lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 8, 1024, 4096, dt) > 0
     # overflow of B*T*C
     assert lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 1 << 30, 1 << 30, 1 << 10, L.WKV_F32) == 0
-    assert lib.wkv_ckpt_bytes(8, 1024, 4096) == 8 * 16 * 4096 * 12
-    assert lib.wkv_ckpt_bytes(1, 65, 3) == 2 * 3 * 12
+    assert lib.wkv_ckpt_bytes(8, 1024, 4096) == 8 * 64 * 4096 * 12
+    assert lib.wkv_ckpt_bytes(1, 17, 3) == 2 * 3 * 12
     assert lib.wkv_ckpt_bytes(1, 0, 3) == 0
     assert lib.wkv_ckpt_bytes(-1, 5, 3) == 0
 
