@@ -16,7 +16,8 @@ kernels run on) and the float64 CPU oracle timed on this host.
 Other workloads (not the headline, for measurements quoted in the design
 notes): fwd3 (the headline shape, forward only), fwd2 (B=8 T=1024 C=768 fp32,
 fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32, forward only), step5 (32 layers x
-256 streams x 4096 channels decode step).
+256 streams x 4096 channels decode step), copy (a plain 1 GiB device-to-device
+copy: the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters).
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -212,6 +213,29 @@ def bench_step5(args):
     }
 
 
+def bench_copy(args):
+    """A plain copy of 1 GiB (reads 1 GiB, writes 1 GiB): HBM counter calibration."""
+    import torch
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nbytes = 2 * 4 * n
+    return {"metric": "device copy GB/s (read + write)", "value": nbytes / (wall / args.steps) / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "copy 1 GiB f32", "bytes_read": 4 * n, "bytes_written": 4 * n}}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -225,8 +249,8 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload == "step5":
-        out = bench_step5(args)
+    if args.workload in ("step5", "copy"):
+        out = bench_step5(args) if args.workload == "step5" else bench_copy(args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

@@ -194,8 +194,88 @@ struct KvChunk<float, L> {
     __device__ __forceinline__ float v(int j) const { return vv[j]; }
 };
 
+// ---- lane recompute in the mean form -------------------------------------------
+// History state (m, b, s): m = A / B, B = b 2^s.
+struct MSt {
+    float m, b;
+    int s;
+};
+
+// What the reverse sweep needs of one token, at the token's scale s:
+// pi = e^{u+k}/D, rho = 2^s/D, e = e^k/2^s, vy = (1-pi)(v-m), vm = (1-lam)(v-m),
+// ld = lam (v-m), pd = pi (v-m), lam = e^k/B_t.
+struct TokQ {
+    float pi, rho, e, vy, vm, ld, pd;
+};
+
+// One token of the general path: lazy exact rescale, current-token
+// normalisation valid for any u (z = log2 of its weight relative to 2^s).
+__device__ __forceinline__ TokQ mean_step(MSt& st, float k, float v, const Chan& ch, float eu, bool fast_out) {
+    const Key kk = key_split(k);
+    const bool out = (kk.n - st.s > static_cast<int>(kBig)) | !(st.b >= kLo) | (st.b > kHi);
+    if (out) {
+        const int lvl = st.b > 0.f ? st.s + __builtin_amdgcn_frexp_expf(st.b) : kSEmpty;
+        const int sn = max(lvl, kk.n);
+        st.b = ldx(st.b, st.s - sn);
+        st.s = sn;
+    }
+    const float e = ldx(kk.em, kk.n - st.s);
+    float pi, rho;
+    if (fast_out) {
+        const float E = e * eu;
+        rho = rcp(st.b + E);
+        pi = E * rho;
+    } else {
+        const float z = static_cast<float>(kk.n - st.s) + kk.f + ch.u2;
+        const float ez = ex2(-fabsf(z));
+        const float co = z > 0.f ? ez : 1.f;
+        const float cn = z > 0.f ? 1.f : ez;
+        const float r = rcp(fmaf(st.b, co, cn));
+        pi = cn * r;
+        rho = co * r;
+    }
+    TokQ q;
+    const float dl = v - st.m;
+    q.pi = pi;
+    q.rho = rho;
+    q.e = e;
+    q.vy = (rho * st.b) * dl;  // (1 - pi) delta without the subtraction
+    const float db = fmaf(ch.dhi, st.b, ch.dlo * st.b);
+    st.b = db + e;
+    const float rb = rcp(fmaxf(st.b, 1e-37f));
+    q.ld = (e * rb) * dl;
+    q.vm = (db * rb) * dl;  // (1 - lam) delta without the subtraction
+    q.pd = pi * dl;
+    st.m += q.ld;
+    return q;
+}
+
+// Per-token running sums of the fast path: float32, or float64 when built with
+// WKV_BWD_ACC_F64=1.
+#ifndef WKV_BWD_ACC_F64
+#define WKV_BWD_ACC_F64 0
+#endif
+#if WKV_BWD_ACC_F64
+using acc_t = double;
+#else
+using acc_t = float;
+#endif
+
+// x * d with d = dhi + dlo (float32: two FMAs, ~2^-48 relative) or d in float64.
+struct Decay {
+    float dhi, dlo;
+    double dd;
+    __device__ __forceinline__ float mul(float x) const { return fmaf(dhi, x, dlo * x); }
+    __device__ __forceinline__ double mul(double x) const { return dd * x; }
+};
+
+
+#ifndef WKV_BWD_OCC
+#define WKV_BWD_OCC 1  // minimum waves per SIMD asked of the register allocator
+#endif
+
 template <typename TIn, int L, int W>
-__global__ void __launch_bounds__(64 * W) bwd_chunk_kernel(BwdChunk P) {
+__global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk P) {
     constexpr int ES = BufLd<TIn>::kBytes;
     __shared__ double sm_mapd[W][5][64];  // S, c0..c3
     __shared__ float sm_mapn[W][64];
@@ -221,14 +301,18 @@ __global__ void __launch_bounds__(64 * W) bwd_chunk_kernel(BwdChunk P) {
     const bool cok = c < P.C;
     const int64_t tb0 = blk * (int64_t)(L * W);
     const int64_t t0 = tb0 + (int64_t)wave * L;
-    const int64_t rem = P.T - t0;
-    const int nvalid = rem <= 0 ? 0 : (rem >= L ? L : static_cast<int>(rem));
+    const bool any_valid = t0 < P.T;
     const float wc = cok ? P.w[c] : 0.f;
     const float uc = cok ? P.u[c] : 0.f;
     const Chan ch = make_chan(wc, uc);
-    const bool fast = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
+    const bool fast_out = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
     const float eu = ex2(ch.u2);
+    const double dd = exp(-static_cast<double>(wc));
+    const Decay dec{ch.dhi, ch.dlo, dd};
 
+    // buffers over this block's rows; tokens past T read as zeros (after every
+    // real token of the span, with gy = 0: they change no real gradient) and
+    // their stores are dropped
     const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
     const int64_t row0 = (b * P.T + tb0) * P.C;
     const uint32_t nin = (uint32_t)(blk_tokens * P.C * ES), nout = (uint32_t)(blk_tokens * P.C * 4);
@@ -247,98 +331,115 @@ __global__ void __launch_bounds__(64 * W) bwd_chunk_kernel(BwdChunk P) {
     GyChunk<TIn, L> gy;
     gy.load(rg, vin, row_in);
 
-    // state at the first token of this wave's span, saved by the forward
-    float m = 0.f, bb = 0.f;
-    int sc = kSEmpty;
-    if (cok && nvalid > 0) {
+    // state before the span's first token, saved by the forward
+    MSt x0{0.f, 0.f, kSEmpty};
+    if (cok && any_valid) {
         const float* cp = P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c;
         const float a0 = cp[0], b0 = cp[P.C];
-        bb = b0;
-        sc = static_cast<int>(cp[2 * P.C]);
-        m = b0 > 0.f ? a0 / b0 : 0.f;
+        x0.s = static_cast<int>(cp[2 * P.C]);
+        x0.b = b0;
+        x0.m = b0 > 0.f ? a0 / b0 : 0.f;
     }
 
-    // ---- forward recompute (mean form) + this span's reverse map -----------------
-    // Per token the reverse sweep needs pi, rho, e and the products
-    //   vy = (1 - pi) delta,  vm = (1 - lam) delta,  ld = lam delta,  pd = pi delta,
-    // where 1 - pi = rho b and 1 - lam = d b / B_t are formed without
-    // cancellation (pi and lam come within an ulp of 1 at dominant tokens).
-    float pi_[L], rho_[L], e_[L], vy_[L], vm_[L], ld_[L], pd_[L];
-    int s_[L];
-    // The span's offset sums cancel like the reverse accumulators: float64.
-    const double dd = exp(-static_cast<double>(wc));
-    double Psum = 0.0, dpow = 1.0, Gs = 0.0, Js = 0.0, Gps = 0.0, Jps = 0.0;
-    int s0 = 0;
-    bool resc = false;
+    // fixed span scale: the larger of the history level and the largest key
+    float kmax = -INFINITY, kmin = INFINITY;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        if (j < nvalid) {
-            const float vj = kv.v(j), gj = gy.g[j];
-            const Key kk = key_split(kv.k(j));
-            const bool out = (kk.n - sc > static_cast<int>(kBig)) | !(bb >= kLo) | (bb > kHi);
-            if (__builtin_expect(out, 0)) {
-                const int lvl = bb > 0.f ? sc + __builtin_amdgcn_frexp_expf(bb) : kSEmpty;
-                const int sn = max(lvl, kk.n);
-                bb = ldx(bb, sc - sn);
-                if (j > 0) {
-                    dpow = ldexp(dpow, sc - sn);
-                    resc = true;
-                }
-                sc = sn;
-            }
-            if (j == 0) s0 = sc;
+        kmax = fmaxf(kmax, kv.k(j));
+        kmin = fminf(kmin, kv.k(j));
+    }
+    const int lvl0 = x0.b > 0.f ? x0.s + __builtin_amdgcn_frexp_expf(x0.b) : kSEmpty;
+    const int sc = max(lvl0, key_split(kmax).n);
+    const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
+    bool fast = fast_out && __all(keys_ok);
+
+    // ---- forward recompute + this span's reverse map ------------------------------
+    // Map offset c0 = sum_u d^u gr_u (1, P_u + pd_u, u, u (P_u + pd_u)) at scale so,
+    // P_u = sum_{t<u} ld_t.  The fast path also keeps, per token, the products
+    // the reverse sweep needs: gpi = gy pi, gvy = gy pi vy, gr = gy rho,
+    // grpd = gy rho pd, e, vm, ld.
+    float a_gpi[L], a_gvy[L], a_gr[L], a_grpd[L], a_e[L], a_vm[L], a_ld[L];
+    acc_t Psum = 0, Gs = 0, Js = 0, Gps = 0, Jps = 0;
+    float acc_du = 0.f;
+    int so = sc;
+    if (fast) {
+        float m = x0.m;
+        float bb = ldx(x0.b, x0.s - sc);
+        float dmin = INFINITY;
+        acc_t dp = 1;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const Key kk = key_split_bounded(kv.k(j));
             const float e = ldx(kk.em, kk.n - sc);
-            float pi, rho;
-            if (fast) {
-                const float E = e * eu;
-                const float r = rcp(bb + E);
-                pi = E * r;
-                rho = r;
-            } else {
-                const float z = static_cast<float>(kk.n - sc) + kk.f + ch.u2;
-                const float ez = ex2(-fabsf(z));
-                const bool zp = z > 0.f;
-                const float co = zp ? ez : 1.f;
-                const float cn = zp ? 1.f : ez;
-                const float r = rcp(fmaf(bb, co, cn));
-                pi = cn * r;
-                rho = co * r;
-            }
-            const float dl = vj - m;
-            const float vy = (rho * bb) * dl;
+            const float E = e * eu;
+            const float den = bb + E;
+            dmin = fminf(dmin, den);
+            const float r = rcp(den);
+            const float pi = E * r;
+            const float dl = kv.v(j) - m;
+            const float vy = (r * bb) * dl;
             const float db = fmaf(ch.dhi, bb, ch.dlo * bb);
             bb = db + e;
-            const float rb = rcp(fmaxf(bb, 1e-37f));
+            dmin = fminf(dmin, bb);  // B_t, the denominator of lam
+            const float rb = rcp(bb);
             const float ld = (e * rb) * dl;
-            const float vm = (db * rb) * dl;
-            const float pd = pi * dl;
+            const float g = gy.g[j];
+            const float gpi = g * pi;
+            const float gr = g * r;
+            a_gpi[j] = gpi;
+            a_gvy[j] = gpi * vy;
+            a_gr[j] = gr;
+            a_grpd[j] = gr * (pi * dl);
+            a_e[j] = e;
+            a_vm[j] = (db * rb) * dl;
+            a_ld[j] = ld;
             m += ld;
-            pi_[j] = pi;
-            rho_[j] = rho;
-            e_[j] = e;
-            vy_[j] = vy;
-            vm_[j] = vm;
-            ld_[j] = ld;
-            pd_[j] = pd;
-            s_[j] = sc;
-            // offset of the reverse map: sum_u d^u 2^{s0 - s_u} gr_u (1, P_u + pd_u, u, u (...))
-            const double q = dpow * static_cast<double>(gj * rho);
-            const double t1 = Psum + static_cast<double>(pd);
+            acc_du = fmaf(gpi, vy, acc_du);
+            const acc_t q = dp * static_cast<acc_t>(gr);
+            const acc_t t1 = fma(q, Psum, dp * static_cast<acc_t>(a_grpd[j]));
             Gs += q;
-            Js = fma(q, t1, Js);
-            Gps = fma(q, static_cast<double>(j), Gps);
-            Jps = fma(q * t1, static_cast<double>(j), Jps);
-            Psum += static_cast<double>(ld);
-            dpow *= dd;
+            Js += t1;
+            Gps = fma(q, static_cast<acc_t>(j), Gps);
+            Jps = fma(t1, static_cast<acc_t>(j), Jps);
+            Psum += static_cast<acc_t>(ld);
+            dp = dec.mul(dp);
+        }
+        fast = __all(dmin >= kTiny);
+    }
+    if (!fast) {
+        Psum = Gs = Js = Gps = Jps = 0;
+        acc_du = 0.f;
+        // general path: per-token rescales; the map is kept at the scale of
+        // the span's first token (after its own rescale, if any)
+        MSt st = x0;
+        double dpd = 1.0;
+#pragma unroll 1
+        for (int j = 0; j < L; ++j) {
+            const int s_before = st.s;
+            const TokQ q = mean_step(st, BufLd<TIn>::at(rk, vin, j * row_in), BufLd<TIn>::at(rv, vin, j * row_in),
+                                     ch, eu, fast_out);
+            if (j == 0) so = st.s;
+            else if (st.s != s_before) dpd = ldexp(dpd, s_before - st.s);
+            const float g = BufLd<TIn>::at(rg, vin, j * row_in);
+            const double gr = static_cast<double>(g * q.rho);
+            const double qq = dpd * gr;
+            const double t1 = qq * (static_cast<double>(Psum) + static_cast<double>(q.pd));
+            Gs += static_cast<acc_t>(qq);
+            Js += static_cast<acc_t>(t1);
+            Gps += static_cast<acc_t>(qq * j);
+            Jps += static_cast<acc_t>(t1 * j);
+            Psum += static_cast<acc_t>(q.ld);
+            acc_du = fmaf(g * q.pi, q.vy, acc_du);
+            dpd *= dd;
         }
     }
-    sm_mapn[wave][lane] = static_cast<float>(nvalid);
-    sm_maps[wave][lane] = s0;
-    sm_mapd[wave][0][lane] = Psum;
-    sm_mapd[wave][1][lane] = Gs;
-    sm_mapd[wave][2][lane] = Js;
-    sm_mapd[wave][3][lane] = Gps;
-    sm_mapd[wave][4][lane] = Jps;
+    sm_mapn[wave][lane] = static_cast<float>(L);
+    sm_maps[wave][lane] = so;
+    sm_mapd[wave][0][lane] = static_cast<double>(Psum);
+    sm_mapd[wave][1][lane] = static_cast<double>(Gs);
+    sm_mapd[wave][2][lane] = static_cast<double>(Js);
+    sm_mapd[wave][3][lane] = static_cast<double>(Gps);
+    sm_mapd[wave][4][lane] = static_cast<double>(Jps);
     __syncthreads();
 
     // ---- reverse scan: compose the maps of the later waves ------------------------
@@ -352,7 +453,7 @@ __global__ void __launch_bounds__(64 * W) bwd_chunk_kernel(BwdChunk P) {
         r.c[1] = sm_mapd[i][2][lane];
         r.c[2] = sm_mapd[i][3][lane];
         r.c[3] = sm_mapd[i][4][lane];
-        r.D = (r.n == static_cast<float>(L)) ? dL : exp(-static_cast<double>(wc) * r.n);
+        r.D = dL;
         return r;
     };
     RMap suf = rmap_identity();
@@ -372,45 +473,61 @@ __global__ void __launch_bounds__(64 * W) bwd_chunk_kernel(BwdChunk P) {
         sm_cin_s[lane] = cin.sg;
     }
     __syncthreads();
-    RCarry C = rapply(suf, RCarry{sm_cin[0][lane], sm_cin[1][lane], sm_cin[2][lane], sm_cin[3][lane],
-                                  sm_cin_s[lane]});
+    const RCarry C = rapply(suf, RCarry{sm_cin[0][lane], sm_cin[1][lane], sm_cin[2][lane], sm_cin[3][lane],
+                                        sm_cin_s[lane]});
 
-    // ---- reverse pass from the true carry ---------------------------------------
-    float acc_dw = 0.f, acc_du = 0.f;
-    {
-        // bring the carry to the scale of this span's last token
-        int slast = 0;
-#pragma unroll
-        for (int j = 0; j < L; ++j)
-            if (j == nvalid - 1) slast = s_[j];
-        const int dsc = slast - C.sg;
-        double G = ldexp(C.G, dsc), J = ldexp(C.J, dsc), Gp = ldexp(C.Gp, dsc), Jp = ldexp(C.Jp, dsc);
+    // ---- reverse sweep from the carry at the span's end ----------------------------
+    float acc_dw = 0.f;
+    if (fast) {
+        acc_t G = static_cast<acc_t>(ldexp(C.G, sc - C.sg)), J = static_cast<acc_t>(ldexp(C.J, sc - C.sg));
+        acc_t Gp = static_cast<acc_t>(ldexp(C.Gp, sc - C.sg)), Jp = static_cast<acc_t>(ldexp(C.Jp, sc - C.sg));
 #pragma unroll
         for (int j = L - 1; j >= 0; --j) {
-            if (j < nvalid) {
-                const float g = gy.g[j], e = e_[j];
-                const double vm = vm_[j], ld = ld_[j];
-                const float gpi = g * pi_[j];
-                buf_store(fmaf(e, static_cast<float>(G), gpi), rdv, vout, j * row_out);
-                buf_store(fmaf(gpi, vy_[j], e * static_cast<float>(fma(vm, G, -J))), rdk, vout, j * row_out);
-                acc_du = fmaf(gpi, vy_[j], acc_du);
-                acc_dw = fmaf(e, static_cast<float>(fma(vm, Gp, -Jp)), acc_dw);
-                const float gr = g * rho_[j];
-                const double GG = Gp + G;
-                Jp = dd * fma(ld, GG, Jp + J);
-                Gp = dd * GG;
-                J = fma(dd, fma(ld, G, J), static_cast<double>(gr * pd_[j]));
-                G = fma(dd, G, static_cast<double>(gr));
-                if (resc && j > 0) {
-                    if (s_[j - 1] != s_[j]) {
-                        const int ds = s_[j - 1] - s_[j];
-                        G = ldexp(G, ds);
-                        J = ldexp(J, ds);
-                        Gp = ldexp(Gp, ds);
-                        Jp = ldexp(Jp, ds);
-                    }
-                }
-            }
+            const float e = a_e[j], vm = a_vm[j];
+            const float Gf = static_cast<float>(G);
+            buf_store(fmaf(e, Gf, a_gpi[j]), rdv, vout, j * row_out);
+            buf_store(fmaf(e, static_cast<float>(fma(static_cast<acc_t>(vm), G, -J)), a_gvy[j]), rdk, vout,
+                      j * row_out);
+            acc_dw = fmaf(e, static_cast<float>(fma(static_cast<acc_t>(vm), Gp, -Jp)), acc_dw);
+            const acc_t ld = static_cast<acc_t>(a_ld[j]);
+            const acc_t GG = Gp + G;
+            Jp = dec.mul(fma(ld, GG, Jp + J));
+            Gp = dec.mul(GG);
+            J = dec.mul(fma(ld, G, J)) + static_cast<acc_t>(a_grpd[j]);
+            G = dec.mul(G) + static_cast<acc_t>(a_gr[j]);
+        }
+    } else {
+        // general path, without per-token arrays: token t's quantities come
+        // from a recompute over the span's first t + 1 tokens (inputs re-read)
+        double G = C.G, J = C.J, Gp = C.Gp, Jp = C.Jp;
+        int sg = C.sg;
+#pragma unroll 1
+        for (int t = L - 1; t >= 0; --t) {
+            MSt st = x0;
+#pragma unroll 1
+            for (int j = 0; j < t; ++j)
+                (void)mean_step(st, BufLd<TIn>::at(rk, vin, j * row_in), BufLd<TIn>::at(rv, vin, j * row_in), ch,
+                                eu, fast_out);
+            const TokQ q = mean_step(st, BufLd<TIn>::at(rk, vin, t * row_in), BufLd<TIn>::at(rv, vin, t * row_in),
+                                     ch, eu, fast_out);
+            const float g = BufLd<TIn>::at(rg, vin, t * row_in);
+            const int ds = st.s - sg;  // bring the carry to this token's scale
+            G = ldexp(G, ds);
+            J = ldexp(J, ds);
+            Gp = ldexp(Gp, ds);
+            Jp = ldexp(Jp, ds);
+            sg = st.s;
+            const float gpi = g * q.pi;
+            buf_store(fmaf(q.e, static_cast<float>(G), gpi), rdv, vout, t * row_out);
+            buf_store(fmaf(gpi, q.vy, q.e * static_cast<float>(fma(static_cast<double>(q.vm), G, -J))), rdk, vout,
+                      t * row_out);
+            acc_dw = fmaf(q.e, static_cast<float>(fma(static_cast<double>(q.vm), Gp, -Jp)), acc_dw);
+            const double gr = static_cast<double>(g * q.rho), ld = q.ld;
+            const double GG = Gp + G;
+            Jp = dd * fma(ld, GG, Jp + J);
+            Gp = dd * GG;
+            J = fma(dd, fma(ld, G, J), gr * static_cast<double>(q.pd));
+            G = fma(dd, G, gr);
         }
     }
 

@@ -125,8 +125,20 @@ __device__ __forceinline__ Key key_split(float k) {
     return Key{ex2(f), f, static_cast<int>(n)};
 }
 
+// The same split for a key already known to satisfy |k log2 e| < kNMax.
+__device__ __forceinline__ Key key_split_bounded(float k) {
+    const float n = __builtin_rintf(k * kL2E);
+    const float f = fmaf(k, kL2E, -n);
+    return Key{ex2(f), f, static_cast<int>(n)};
+}
+
 // ---- lane state ---------------------------------------------------------------
 constexpr int kSEmpty = -(1 << 29);  // scale of the empty state (a = b = 0)
+// Fixed-scale paths hold every denominator they divide by at or above this
+// (relative to their scale); a wave where one falls below redoes its work on
+// the general path.  Terms that underflow next to such a denominator are
+// below float32 resolution anyway.
+constexpr float kTiny = 0x1p-100f;
 
 struct St {
     float a, b;  // A = a 2^s, B = b 2^s

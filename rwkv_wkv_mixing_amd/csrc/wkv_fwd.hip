@@ -4,17 +4,28 @@
 // row and one time BLOCK of W*L tokens; wave i of the workgroup owns the L
 // tokens [i*L, (i+1)*L) of the block, one channel per lane, so every load and
 // store of a wave is one contiguous 64-channel row segment (128 B for bf16,
-// 256 B for fp32).  The inputs of a sub-chunk stay in registers between the
-// two passes, so HBM sees each input once and each output once.
+// 256 B for fp32).  The inputs of a sub-chunk stay in registers, so HBM sees
+// each input once and each output once.
 //
-//   pass 1  every wave runs its L tokens from the empty state -> summary S_i
+//   local   every wave runs its L tokens from the empty state at one fixed
+//           scale (that of its largest key), keeping for every token the
+//           local numerator N_t = A_loc + e^{u+k} v and denominator
+//           D_t = B_loc + e^{u+k}; the end state is the sub-chunk summary S_i
 //   scan    through LDS every wave combines S_0..S_{i-1} into its prefix P_i;
 //           the last wave also waits for the inclusive state E of the
 //           previous time block of the same tile (blocks are handed out by an
 //           atomic ticket in time order, so the awaited block is already
 //           running) and publishes this block's inclusive state
-//   pass 2  every wave re-runs its L tokens from carry-in d^{iL} E + P_i and
-//           writes y (and the saved block-start states for the backward).
+//   output  with X = d^{iL} E + P_i the state before the sub-chunk,
+//           y_t = (N_t + d^j X_A) / (D_t + d^j X_B)  for its j-th token,
+//           and the saved block-start states for the backward.
+//
+// The fixed scale makes the local pass and the output branch-free straight
+// line code.  It needs w >= 0, |u| <= kFastU, a local end state and output
+// denominators no smaller than kTiny, and a carry-in that fits next to the
+// local scale; a wave where any lane misses one of these runs the general path
+// instead (a per-token lazy rescale, then a second recurrence from X), which
+// also covers the current-token normalisation for any u.
 //
 // Chunkwise-parallel execution: "RWKV模型深度研究报告", section 1.4.1;
 // prefix scan: "RWKV（Receptance Weighted Key Value）概念", section 3.4.
@@ -59,6 +70,16 @@ struct SubChunk<uint16_t, L> {
     }
     __device__ __forceinline__ float k(int j) const { return __uint_as_float(kv[j] << 16); }
     __device__ __forceinline__ float v(int j) const { return __uint_as_float(kv[j] & 0xffff0000u); }
+    // Hide the registers' contents from the optimiser (emits no code), so that
+    // values unpacked in one pass are recomputed in the next instead of being
+    // kept alive in extra registers.
+    __device__ __forceinline__ void opaque() {
+#pragma unroll
+        for (int j = 0; j < L; ++j) asm volatile("" : "+v"(kv[j]));
+    }
+    // The same for one token: keeps its unpacking (and what follows from it)
+    // after the previous token's stores instead of hoisted ahead of the loop.
+    __device__ __forceinline__ void opaque(int j) { asm volatile("" : "+v"(kv[j])); }
 };
 
 template <int L>
@@ -73,31 +94,75 @@ struct SubChunk<float, L> {
     }
     __device__ __forceinline__ float k(int j) const { return kk[j]; }
     __device__ __forceinline__ float v(int j) const { return vv[j]; }
+    __device__ __forceinline__ void opaque() {}
+    __device__ __forceinline__ void opaque(int j) { asm volatile("" : "+v"(kk[j]), "+v"(vv[j])); }
 };
 
-// Pass 2 over a sub-chunk: outputs from the carry-in state, and the state
-// before every kCkptLen-th token into ckpt (when given) for the backward.
+// General path over a sub-chunk: outputs from the carry-in state by a second
+// recurrence with per-token rescales, and the state before every kCkptLen-th
+// token into ckpt (when given).  Rare; reads one token at a time so that it
+// adds no registers to the kernel.
 template <bool Fast, typename TIn, int L>
-__device__ __forceinline__ void fwd_outputs(St st, const SubChunk<TIn, L>& sc, int nvalid,
-                                            const Chan& ch, float eu, Rsrc ry, uint32_t vout,
-                                            uint32_t row_out, float* ckp, int64_t ckstride) {
+__device__ __forceinline__ void general_outputs(St st, Rsrc rk, Rsrc rv, uint32_t vin, uint32_t row_in, int nvalid,
+                                                const Chan& ch, float eu, Rsrc ry, uint32_t vout, uint32_t row_out,
+                                                float* ckp, int64_t ckstride) {
+#pragma unroll 1
+    for (int j = 0; j < L; ++j) {
+        if ((j % kCkptLen) == 0 && j < nvalid && ckp != nullptr) {
+            float* cp = ckp + (j / kCkptLen) * 3 * ckstride;
+            cp[0] = st.a;
+            cp[ckstride] = st.b;
+            cp[2 * ckstride] = static_cast<float>(st.s);
+        }
+        const Key kk = key_split(BufLd<TIn>::at(rk, vin, j * row_in));
+        const float vj = BufLd<TIn>::at(rv, vin, j * row_in);
+        const float e = key_weight(st, kk);
+        const float yj = Fast ? token_out_fast(st, e, vj, eu) : token_out(st, key_log2(st, kk), vj, ch).y;
+        token_add(st, e, vj, ch);
+        buf_store(yj, ry, vout, j * row_out);
+    }
+}
+
+constexpr int kCarryAbove = 100;  // max log2 of the carry-in's b (and of a, + 20) above the local scale
+
+// Local pass at the fixed scale sl (>= every key's n): returns the local end
+// state, fills N and D, and keeps the local state before every kCkptLen-th token.
+template <typename TIn, int L>
+__device__ __forceinline__ St local_pass(const SubChunk<TIn, L>& sc, int sl, const Chan& ch, float eu,
+                                         float (&N)[L], float (&D)[L], St (&mid)[L / kCkptLen]) {
+    float a = 0.f, b = 0.f;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        if (j < nvalid) {
-            if ((j % kCkptLen) == 0 && ckp != nullptr) {
-                float* cp = ckp + (j / kCkptLen) * 3 * ckstride;
-                cp[0] = st.a;
-                cp[ckstride] = st.b;
-                cp[2 * ckstride] = static_cast<float>(st.s);
-            }
-            const Key kk = key_split(sc.k(j));
-            const float vj = sc.v(j);
-            const float e = key_weight(st, kk);
-            const float yj = Fast ? token_out_fast(st, e, vj, eu) : token_out(st, key_log2(st, kk), vj, ch).y;
-            token_add(st, e, vj, ch);
-            buf_store(yj, ry, vout, j * row_out);
-        }
+        if (j % kCkptLen == 0 && j > 0) mid[j / kCkptLen] = St{a, b, sl};
+        const Key kk = key_split_bounded(sc.k(j));
+        const float e = ldx(kk.em, kk.n - sl);
+        const float v = sc.v(j);
+        const float E = e * eu;
+        N[j] = fmaf(E, v, a);
+        D[j] = b + E;
+        const float ev = e * v;
+        a = fmaf(ch.dhi, a, fmaf(ch.dlo, a, ev));
+        b = fmaf(ch.dhi, b, fmaf(ch.dlo, b, e));
     }
+    return St{a, b, sl};
+}
+
+// Outputs from the local terms and the carry-in X brought to the local scale;
+// returns the smallest denominator used.
+template <int L>
+__device__ __forceinline__ float corrected_outputs(const St& X, int sl, const float (&N)[L], const float (&D)[L],
+                                                   const Chan& ch, Rsrc ry, uint32_t vout, uint32_t row_out) {
+    const float cA = ldx(X.a, X.s - sl), cB = ldx(X.b, X.s - sl);
+    float dp = 1.f;  // d^j
+    float dmin = INFINITY;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const float den = fmaf(dp, cB, D[j]);
+        dmin = fminf(dmin, den);
+        buf_store(fmaf(dp, cA, N[j]) * rcp(den), ry, vout, j * row_out);
+        dp = fmaf(ch.dhi, dp, ch.dlo * dp);
+    }
+    return dmin;
 }
 
 template <typename TIn, int L, int W>
@@ -148,13 +213,32 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     SubChunk<TIn, L> sc;
     sc.load(rk, rv, vin, row_in);
 
-    // ---- pass 1: summary from the empty state ----------------------------------
-    St st = empty_state();
+    // ---- local pass (fixed scale) or pass 1 (general): summary from the empty state
+    // (tokens past T read as k = v = 0: they follow every real token of the
+    // wave, so they change no real output, and their stores are dropped)
+    float kmax = -INFINITY, kmin = INFINITY;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        if (j < nvalid) {
-            const float e = key_weight(st, key_split(sc.k(j)));
-            token_add(st, e, sc.v(j), ch);
+        kmax = fmaxf(kmax, sc.k(j));
+        kmin = fminf(kmin, sc.k(j));
+    }
+    sc.opaque();
+    const int sl = key_split(kmax).n;
+    const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
+    bool fast_local = __all((wc >= 0.f) & (fabsf(uc) <= kFastU) & keys_ok);
+    float N[L], D[L];
+    St mid[L / kCkptLen];
+    St st = empty_state();
+    if (fast_local) {
+        st = local_pass(sc, sl, ch, eu, N, D, mid);
+        fast_local = __all(st.b >= kTiny);
+    }
+    if (!fast_local) {  // general pass 1, reading one token at a time (rare: kept register-light)
+        st = empty_state();
+#pragma unroll 1
+        for (int j = 0; j < L; ++j) {
+            const float e = key_weight(st, key_split(BufLd<TIn>::at(rk, vin, j * row_in)));
+            token_add(st, e, BufLd<TIn>::at(rv, vin, j * row_in), ch);
         }
     }
     sm_a[wave][lane] = st.a;
@@ -189,12 +273,36 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     for (int i = 0; i < wave; ++i) dpow *= dL;
     const St s2 = combine(St{sm_e[0][lane], sm_e[1][lane], sm_es[lane]}, pref, dpow);
 
-    // ---- pass 2: outputs from the carry-in -------------------------------------
+    // ---- outputs from the carry-in X = s2 ---------------------------------------
     float* ckp = (P.ckpt != nullptr && cok) ? P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c : nullptr;
-    if (fast)
-        fwd_outputs<true>(s2, sc, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
-    else
-        fwd_outputs<false>(s2, sc, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
+    const bool carry_fits = !(s2.b > 0.f) | ((s2.s - sl + __builtin_amdgcn_frexp_expf(s2.b) <= kCarryAbove) &
+                                             (s2.s - sl + __builtin_amdgcn_frexp_expf(s2.a) <= kCarryAbove + 20));
+    bool fast_out = fast_local && __all(carry_fits);
+    if (fast_out && P.y != nullptr) fast_out = __all(corrected_outputs(s2, sl, N, D, ch, ry, vout, row_out) >= kTiny);
+    if (fast_out) {
+        if (ckp != nullptr) {
+            const double dck = exp(-static_cast<double>(wc) * kCkptLen);
+            double dq = 1.0;
+#pragma unroll
+            for (int q = 0; q < L / kCkptLen; ++q) {
+                if (q * kCkptLen < nvalid) {
+                    const St x = q == 0 ? s2 : combine(s2, mid[q], dq);
+                    float* cp = ckp + q * 3 * P.C;
+                    cp[0] = x.a;
+                    cp[P.C] = x.b;
+                    cp[2 * P.C] = static_cast<float>(x.s);
+                }
+                dq *= dck;
+            }
+        }
+    } else {
+        // general path: a second recurrence from X with per-token rescales;
+        // it rewrites every output of the wave
+        if (fast)
+            general_outputs<true, TIn, L>(s2, rk, rv, vin, row_in, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
+        else
+            general_outputs<false, TIn, L>(s2, rk, rv, vin, row_in, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
+    }
 }
 
 __global__ void fwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
@@ -212,6 +320,7 @@ namespace {
 #endif
 constexpr int kFwdL = WKV_FWD_L;  // tokens per wave (sub-chunk)
 constexpr int kFwdW = WKV_FWD_W;  // waves per workgroup
+static_assert(kFwdL % kCkptLen == 0, "sub-chunks must start on saved-state boundaries");
 
 struct FwdLayout {
     int64_t nct, ntiles, nblocks;
