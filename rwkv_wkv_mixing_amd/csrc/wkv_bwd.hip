@@ -274,24 +274,294 @@ struct Decay {
 #define WKV_BWD_OCC 1  // minimum waves per SIMD asked of the register allocator
 #endif
 
+// ---- one wave's span of L tokens ----------------------------------------------
+// Where a span's data lives for one lane.
+struct SpanGeo {
+    Rsrc rk, rv, rg, rdk, rdv;
+    uint32_t vin, vout, row_in, row_out;
+    const float* ck;  // saved state at the span start, or nullptr
+};
+
+// Geometry of wave `wave`'s span in time block `blk` of batch row b (W L tokens
+// per block).  Tokens past T read as zeros and their stores are dropped.
+template <typename TIn, int L, int W>
+__device__ __forceinline__ SpanGeo span_geo(const BwdChunk& P, int64_t b, int64_t c, bool cok, int64_t blk, int wave) {
+    constexpr int ES = BufLd<TIn>::kBytes;
+    const int64_t tb0 = blk * (int64_t)(L * W);
+    const int64_t t0 = tb0 + (int64_t)wave * L;
+    const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
+    const int64_t row0 = (b * P.T + tb0) * P.C;
+    const uint32_t nin = (uint32_t)(blk_tokens * P.C * ES), nout = (uint32_t)(blk_tokens * P.C * 4);
+    SpanGeo g;
+    g.rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, nin);
+    g.rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, nin);
+    g.rg = make_rsrc(static_cast<const TIn*>(P.gy) + row0, nin);
+    g.rdk = make_rsrc(P.dk + row0, nout);
+    g.rdv = make_rsrc(P.dv + row0, nout);
+    const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;
+    g.vin = cok ? lin * ES : kOffNone;
+    g.vout = cok ? lin * 4 : kOffNone;
+    g.row_in = (uint32_t)(P.C * ES);
+    g.row_out = (uint32_t)(P.C * 4);
+    g.ck = (cok && t0 < P.T) ? P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c : nullptr;
+    return g;
+}
+
+// A span's inputs, loaded ahead of use.
+template <typename TIn, int L>
+struct SpanIn {
+    KvChunk<TIn, L> kv;
+    GyChunk<TIn, L> gy;
+    float a0, b0, s0;
+    __device__ __forceinline__ void load(const SpanGeo& g, int64_t C) {
+        kv.load(g.rk, g.rv, g.vin, g.row_in);
+        gy.load(g.rg, g.vin, g.row_in);
+        a0 = 0.f;
+        b0 = 0.f;
+        s0 = static_cast<float>(kSEmpty);
+        if (g.ck != nullptr) {
+            a0 = g.ck[0];
+            b0 = g.ck[C];
+            s0 = g.ck[2 * C];
+        }
+    }
+};
+
+// Forward recompute of a span, its reverse map, and (fast path) the per-token
+// products of the reverse sweep: gpi = gy pi, gvy = gy pi vy, gr = gy rho,
+// grpd = gy rho pd, e, vm, ld.
+template <typename TIn, int L>
+struct Span {
+    float gpi[L], gvy[L], gr[L], grpd[L], e[L], vm[L], ld[L];
+    acc_t Psum, Gs, Js, Gps, Jps;
+    float du;
+    int so;     // scale of the map offsets (and of the whole fast-path sweep)
+    bool fast;  // wave-uniform
+    MSt x0;
+
+    __device__ __forceinline__ void recompute(const SpanIn<TIn, L>& in, const SpanGeo& g, const Chan& ch, float eu,
+                                              const Decay& dec, bool fast_out) {
+        x0.s = static_cast<int>(in.s0);
+        x0.b = in.b0;
+        x0.m = in.b0 > 0.f ? in.a0 / in.b0 : 0.f;
+        // fixed span scale: the larger of the history level and the largest key
+        float kmax = -INFINITY, kmin = INFINITY;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            kmax = fmaxf(kmax, in.kv.k(j));
+            kmin = fminf(kmin, in.kv.k(j));
+        }
+        const int lvl0 = x0.b > 0.f ? x0.s + __builtin_amdgcn_frexp_expf(x0.b) : kSEmpty;
+        const int sc = max(lvl0, key_split(kmax).n);
+        const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
+        fast = fast_out && __all(keys_ok);
+        Psum = Gs = Js = Gps = Jps = 0;
+        du = 0.f;
+        so = sc;
+        if (fast) {
+            float m = x0.m;
+            float bb = ldx(x0.b, x0.s - sc);
+            float dmin = INFINITY;
+            acc_t dp = 1;
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                const Key kk = key_split_bounded(in.kv.k(j));
+                const float ej = ldx(kk.em, kk.n - sc);
+                const float E = ej * eu;
+                const float den = bb + E;
+                dmin = fminf(dmin, den);
+                const float r = rcp(den);
+                const float pi = E * r;
+                const float dl = in.kv.v(j) - m;
+                const float vy = (r * bb) * dl;
+                const float db = fmaf(ch.dhi, bb, ch.dlo * bb);
+                bb = db + ej;
+                dmin = fminf(dmin, bb);  // B_t, the denominator of lam
+                const float rb = rcp(bb);
+                const float ldj = (ej * rb) * dl;
+                const float gj = in.gy.g[j];
+                const float gpij = gj * pi;
+                const float grj = gj * r;
+                gpi[j] = gpij;
+                gvy[j] = gpij * vy;
+                gr[j] = grj;
+                grpd[j] = grj * (pi * dl);
+                e[j] = ej;
+                vm[j] = (db * rb) * dl;
+                ld[j] = ldj;
+                m += ldj;
+                du = fmaf(gpij, vy, du);
+                const acc_t q = dp * static_cast<acc_t>(grj);
+                const acc_t t1 = fma(q, Psum, dp * static_cast<acc_t>(grpd[j]));
+                Gs += q;
+                Js += t1;
+                Gps = fma(q, static_cast<acc_t>(j), Gps);
+                Jps = fma(t1, static_cast<acc_t>(j), Jps);
+                Psum += static_cast<acc_t>(ldj);
+                dp = dec.mul(dp);
+            }
+            fast = __all(dmin >= kTiny);
+        }
+        if (!fast) {
+            // general path: per-token rescales, inputs re-read one token at a
+            // time; the map is kept at the scale of the span's first token
+            Psum = Gs = Js = Gps = Jps = 0;
+            du = 0.f;
+            MSt st = x0;
+            double dpd = 1.0;
+#pragma unroll 1
+            for (int j = 0; j < L; ++j) {
+                const int s_before = st.s;
+                const TokQ q = mean_step(st, BufLd<TIn>::at(g.rk, g.vin, j * g.row_in),
+                                         BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch, eu, fast_out);
+                if (j == 0)
+                    so = st.s;
+                else if (st.s != s_before)
+                    dpd = ldexp(dpd, s_before - st.s);
+                const float gj = BufLd<TIn>::at(g.rg, g.vin, j * g.row_in);
+                const double grj = static_cast<double>(gj * q.rho);
+                const double qq = dpd * grj;
+                const double t1 = qq * (static_cast<double>(Psum) + static_cast<double>(q.pd));
+                Gs += static_cast<acc_t>(qq);
+                Js += static_cast<acc_t>(t1);
+                Gps += static_cast<acc_t>(qq * j);
+                Jps += static_cast<acc_t>(t1 * j);
+                Psum += static_cast<acc_t>(q.ld);
+                du = fmaf(gj * q.pi, q.vy, du);
+                dpd *= dec.dd;
+            }
+        }
+    }
+
+    // Reverse sweep from the carry at the span's end: writes dk, dv and
+    // returns this span's part of -dw.
+    __device__ __forceinline__ float reverse(const RCarry& C, const SpanGeo& g, const Chan& ch, float eu,
+                                             const Decay& dec, bool fast_out) const {
+        float acc_dw = 0.f;
+        if (fast) {
+            acc_t G = static_cast<acc_t>(ldexp(C.G, so - C.sg)), J = static_cast<acc_t>(ldexp(C.J, so - C.sg));
+            acc_t Gp = static_cast<acc_t>(ldexp(C.Gp, so - C.sg)), Jp = static_cast<acc_t>(ldexp(C.Jp, so - C.sg));
+#pragma unroll
+            for (int j = L - 1; j >= 0; --j) {
+                const float ej = e[j], vmj = vm[j];
+                buf_store(fmaf(ej, static_cast<float>(G), gpi[j]), g.rdv, g.vout, j * g.row_out);
+                buf_store(fmaf(ej, static_cast<float>(fma(static_cast<acc_t>(vmj), G, -J)), gvy[j]), g.rdk, g.vout,
+                          j * g.row_out);
+                acc_dw = fmaf(ej, static_cast<float>(fma(static_cast<acc_t>(vmj), Gp, -Jp)), acc_dw);
+                const acc_t ldj = static_cast<acc_t>(ld[j]);
+                const acc_t GG = Gp + G;
+                Jp = dec.mul(fma(ldj, GG, Jp + J));
+                Gp = dec.mul(GG);
+                J = dec.mul(fma(ldj, G, J)) + static_cast<acc_t>(grpd[j]);
+                G = dec.mul(G) + static_cast<acc_t>(gr[j]);
+            }
+        } else {
+            // general path, without per-token arrays: token t's quantities come
+            // from a recompute over the span's first t + 1 tokens
+            double G = C.G, J = C.J, Gp = C.Gp, Jp = C.Jp;
+            int sg = C.sg;
+#pragma unroll 1
+            for (int t = L - 1; t >= 0; --t) {
+                MSt st = x0;
+#pragma unroll 1
+                for (int j = 0; j < t; ++j)
+                    (void)mean_step(st, BufLd<TIn>::at(g.rk, g.vin, j * g.row_in),
+                                    BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch, eu, fast_out);
+                const TokQ q = mean_step(st, BufLd<TIn>::at(g.rk, g.vin, t * g.row_in),
+                                         BufLd<TIn>::at(g.rv, g.vin, t * g.row_in), ch, eu, fast_out);
+                const float gt = BufLd<TIn>::at(g.rg, g.vin, t * g.row_in);
+                const int ds = st.s - sg;  // bring the carry to this token's scale
+                G = ldexp(G, ds);
+                J = ldexp(J, ds);
+                Gp = ldexp(Gp, ds);
+                Jp = ldexp(Jp, ds);
+                sg = st.s;
+                const float gpit = gt * q.pi;
+                buf_store(fmaf(q.e, static_cast<float>(G), gpit), g.rdv, g.vout, t * g.row_out);
+                buf_store(fmaf(gpit, q.vy, q.e * static_cast<float>(fma(static_cast<double>(q.vm), G, -J))), g.rdk,
+                          g.vout, t * g.row_out);
+                acc_dw = fmaf(q.e, static_cast<float>(fma(static_cast<double>(q.vm), Gp, -Jp)), acc_dw);
+                const double grt = static_cast<double>(gt * q.rho), ldt = q.ld;
+                const double GG = Gp + G;
+                Jp = dec.dd * fma(ldt, GG, Jp + J);
+                Gp = dec.dd * GG;
+                J = fma(dec.dd, fma(ldt, G, J), grt * static_cast<double>(q.pd));
+                G = fma(dec.dd, G, grt);
+            }
+        }
+        return acc_dw;
+    }
+};
+
+template <int W>
+struct BwdShared {
+    double mapd[W][5][64];  // S, c0..c3 of each wave's span
+    float mapn[W][64];
+    int maps[W][64];
+    double cin[4][64];      // carry at the block's end
+    int cin_s[64];
+    float red[W][2][64];
+    uint32_t ticket;
+};
+
+template <int W, typename TIn, int L>
+__device__ __forceinline__ void put_map(BwdShared<W>& sm, int wave, int lane, const Span<TIn, L>& sp) {
+    sm.mapn[wave][lane] = static_cast<float>(L);
+    sm.maps[wave][lane] = sp.so;
+    sm.mapd[wave][0][lane] = static_cast<double>(sp.Psum);
+    sm.mapd[wave][1][lane] = static_cast<double>(sp.Gs);
+    sm.mapd[wave][2][lane] = static_cast<double>(sp.Js);
+    sm.mapd[wave][3][lane] = static_cast<double>(sp.Gps);
+    sm.mapd[wave][4][lane] = static_cast<double>(sp.Jps);
+}
+
+template <int W>
+__device__ __forceinline__ RMap get_map(const BwdShared<W>& sm, int i, int lane, double dL) {
+    RMap r;
+    r.n = sm.mapn[i][lane];
+    r.so = sm.maps[i][lane];
+    r.S = sm.mapd[i][0][lane];
+    r.c[0] = sm.mapd[i][1][lane];
+    r.c[1] = sm.mapd[i][2][lane];
+    r.c[2] = sm.mapd[i][3][lane];
+    r.c[3] = sm.mapd[i][4][lane];
+    r.D = dL;
+    return r;
+}
+
+// dw, du of a workgroup: fixed-order sum over its waves into part[slot].
+template <int W>
+__device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P, int64_t slot, int wave, int lane,
+                                             float ndw, float du) {
+    sm.red[wave][0][lane] = -ndw;
+    sm.red[wave][1][lane] = du;
+    lds_sync();
+    if (wave == 0) {
+        float sw = 0.f, su = 0.f;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            sw += sm.red[i][0][lane];
+            su += sm.red[i][1][lane];
+        }
+        float* pp = P.part + slot * 2 * 64 + lane;
+        pp[0] = sw;
+        pp[64] = su;
+    }
+}
+
+// Time-split backward: one workgroup per (tile, time block); blocks are
+// chained backward in time through the coherent carry slots.
 template <typename TIn, int L, int W>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk P) {
-    constexpr int ES = BufLd<TIn>::kBytes;
-    __shared__ double sm_mapd[W][5][64];  // S, c0..c3
-    __shared__ float sm_mapn[W][64];
-    __shared__ int sm_maps[W][64];
-    __shared__ double sm_cin[4][64];
-    __shared__ int sm_cin_s[64];
-    __shared__ float sm_red[W][2][64];
-    __shared__ uint32_t sm_ticket;
+    __shared__ BwdShared<W> sm;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     int64_t ticket = blockIdx.x;
     if (P.nblocks > 1) {
-        if (threadIdx.x == 0) sm_ticket = atomicAdd(P.counter, 1u);
+        if (threadIdx.x == 0) sm.ticket = atomicAdd(P.counter, 1u);
         __syncthreads();
-        ticket = sm_ticket;
+        ticket = sm.ticket;
     }
     const int64_t rblk = ticket / P.ntiles;  // blocks are handed out last-in-time first
     const int64_t tile = ticket - rblk * P.ntiles;
@@ -299,253 +569,94 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     const int64_t b = tile / P.nct;
     const int64_t c = (tile - b * P.nct) * 64 + lane;
     const bool cok = c < P.C;
-    const int64_t tb0 = blk * (int64_t)(L * W);
-    const int64_t t0 = tb0 + (int64_t)wave * L;
-    const bool any_valid = t0 < P.T;
     const float wc = cok ? P.w[c] : 0.f;
     const float uc = cok ? P.u[c] : 0.f;
     const Chan ch = make_chan(wc, uc);
     const bool fast_out = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
     const float eu = ex2(ch.u2);
-    const double dd = exp(-static_cast<double>(wc));
-    const Decay dec{ch.dhi, ch.dlo, dd};
+    const Decay dec{ch.dhi, ch.dlo, ch.dd};
+    const double dL = ipow<L>(ch.dd);
 
-    // buffers over this block's rows; tokens past T read as zeros (after every
-    // real token of the span, with gy = 0: they change no real gradient) and
-    // their stores are dropped
-    const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
-    const int64_t row0 = (b * P.T + tb0) * P.C;
-    const uint32_t nin = (uint32_t)(blk_tokens * P.C * ES), nout = (uint32_t)(blk_tokens * P.C * 4);
-    const Rsrc rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, nin);
-    const Rsrc rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, nin);
-    const Rsrc rg = make_rsrc(static_cast<const TIn*>(P.gy) + row0, nin);
-    const Rsrc rdk = make_rsrc(P.dk + row0, nout);
-    const Rsrc rdv = make_rsrc(P.dv + row0, nout);
-    const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;
-    const uint32_t vin = cok ? lin * ES : kOffNone;
-    const uint32_t vout = cok ? lin * 4 : kOffNone;
-    const uint32_t row_in = (uint32_t)(P.C * ES), row_out = (uint32_t)(P.C * 4);
+    const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
+    SpanIn<TIn, L> in;
+    in.load(g, P.C);
+    Span<TIn, L> sp;
+    sp.recompute(in, g, ch, eu, dec, fast_out);
+    put_map(sm, wave, lane, sp);
+    lds_sync();
 
-    KvChunk<TIn, L> kv;
-    kv.load(rk, rv, vin, row_in);
-    GyChunk<TIn, L> gy;
-    gy.load(rg, vin, row_in);
-
-    // state before the span's first token, saved by the forward
-    MSt x0{0.f, 0.f, kSEmpty};
-    if (cok && any_valid) {
-        const float* cp = P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c;
-        const float a0 = cp[0], b0 = cp[P.C];
-        x0.s = static_cast<int>(cp[2 * P.C]);
-        x0.b = b0;
-        x0.m = b0 > 0.f ? a0 / b0 : 0.f;
-    }
-
-    // fixed span scale: the larger of the history level and the largest key
-    float kmax = -INFINITY, kmin = INFINITY;
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        kmax = fmaxf(kmax, kv.k(j));
-        kmin = fminf(kmin, kv.k(j));
-    }
-    const int lvl0 = x0.b > 0.f ? x0.s + __builtin_amdgcn_frexp_expf(x0.b) : kSEmpty;
-    const int sc = max(lvl0, key_split(kmax).n);
-    const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
-    bool fast = fast_out && __all(keys_ok);
-
-    // ---- forward recompute + this span's reverse map ------------------------------
-    // Map offset c0 = sum_u d^u gr_u (1, P_u + pd_u, u, u (P_u + pd_u)) at scale so,
-    // P_u = sum_{t<u} ld_t.  The fast path also keeps, per token, the products
-    // the reverse sweep needs: gpi = gy pi, gvy = gy pi vy, gr = gy rho,
-    // grpd = gy rho pd, e, vm, ld.
-    float a_gpi[L], a_gvy[L], a_gr[L], a_grpd[L], a_e[L], a_vm[L], a_ld[L];
-    acc_t Psum = 0, Gs = 0, Js = 0, Gps = 0, Jps = 0;
-    float acc_du = 0.f;
-    int so = sc;
-    if (fast) {
-        float m = x0.m;
-        float bb = ldx(x0.b, x0.s - sc);
-        float dmin = INFINITY;
-        acc_t dp = 1;
-#pragma unroll
-        for (int j = 0; j < L; ++j) {
-            const Key kk = key_split_bounded(kv.k(j));
-            const float e = ldx(kk.em, kk.n - sc);
-            const float E = e * eu;
-            const float den = bb + E;
-            dmin = fminf(dmin, den);
-            const float r = rcp(den);
-            const float pi = E * r;
-            const float dl = kv.v(j) - m;
-            const float vy = (r * bb) * dl;
-            const float db = fmaf(ch.dhi, bb, ch.dlo * bb);
-            bb = db + e;
-            dmin = fminf(dmin, bb);  // B_t, the denominator of lam
-            const float rb = rcp(bb);
-            const float ld = (e * rb) * dl;
-            const float g = gy.g[j];
-            const float gpi = g * pi;
-            const float gr = g * r;
-            a_gpi[j] = gpi;
-            a_gvy[j] = gpi * vy;
-            a_gr[j] = gr;
-            a_grpd[j] = gr * (pi * dl);
-            a_e[j] = e;
-            a_vm[j] = (db * rb) * dl;
-            a_ld[j] = ld;
-            m += ld;
-            acc_du = fmaf(gpi, vy, acc_du);
-            const acc_t q = dp * static_cast<acc_t>(gr);
-            const acc_t t1 = fma(q, Psum, dp * static_cast<acc_t>(a_grpd[j]));
-            Gs += q;
-            Js += t1;
-            Gps = fma(q, static_cast<acc_t>(j), Gps);
-            Jps = fma(t1, static_cast<acc_t>(j), Jps);
-            Psum += static_cast<acc_t>(ld);
-            dp = dec.mul(dp);
-        }
-        fast = __all(dmin >= kTiny);
-    }
-    if (!fast) {
-        Psum = Gs = Js = Gps = Jps = 0;
-        acc_du = 0.f;
-        // general path: per-token rescales; the map is kept at the scale of
-        // the span's first token (after its own rescale, if any)
-        MSt st = x0;
-        double dpd = 1.0;
-#pragma unroll 1
-        for (int j = 0; j < L; ++j) {
-            const int s_before = st.s;
-            const TokQ q = mean_step(st, BufLd<TIn>::at(rk, vin, j * row_in), BufLd<TIn>::at(rv, vin, j * row_in),
-                                     ch, eu, fast_out);
-            if (j == 0) so = st.s;
-            else if (st.s != s_before) dpd = ldexp(dpd, s_before - st.s);
-            const float g = BufLd<TIn>::at(rg, vin, j * row_in);
-            const double gr = static_cast<double>(g * q.rho);
-            const double qq = dpd * gr;
-            const double t1 = qq * (static_cast<double>(Psum) + static_cast<double>(q.pd));
-            Gs += static_cast<acc_t>(qq);
-            Js += static_cast<acc_t>(t1);
-            Gps += static_cast<acc_t>(qq * j);
-            Jps += static_cast<acc_t>(t1 * j);
-            Psum += static_cast<acc_t>(q.ld);
-            acc_du = fmaf(g * q.pi, q.vy, acc_du);
-            dpd *= dd;
-        }
-    }
-    sm_mapn[wave][lane] = static_cast<float>(L);
-    sm_maps[wave][lane] = so;
-    sm_mapd[wave][0][lane] = static_cast<double>(Psum);
-    sm_mapd[wave][1][lane] = static_cast<double>(Gs);
-    sm_mapd[wave][2][lane] = static_cast<double>(Js);
-    sm_mapd[wave][3][lane] = static_cast<double>(Gps);
-    sm_mapd[wave][4][lane] = static_cast<double>(Jps);
-    __syncthreads();
-
-    // ---- reverse scan: compose the maps of the later waves ------------------------
-    const double dL = exp(-static_cast<double>(wc) * L);
-    auto load_map = [&](int i) {
-        RMap r;
-        r.n = sm_mapn[i][lane];
-        r.so = sm_maps[i][lane];
-        r.S = sm_mapd[i][0][lane];
-        r.c[0] = sm_mapd[i][1][lane];
-        r.c[1] = sm_mapd[i][2][lane];
-        r.c[2] = sm_mapd[i][3][lane];
-        r.c[3] = sm_mapd[i][4][lane];
-        r.D = dL;
-        return r;
-    };
     RMap suf = rmap_identity();
-    for (int i = W - 1; i > wave; --i) suf = rcompose(load_map(i), suf);
+    for (int i = W - 1; i > wave; --i) suf = rcompose(get_map(sm, i, lane, dL), suf);
     if (wave == 0) {
         RCarry cin{0.0, 0.0, 0.0, 0.0, 0};
         if (P.nblocks > 1) {
             const Rsrc rc = make_rsrc(P.carry, P.carry_bytes);
             const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * kCarrySlot);
             if (blk < P.nblocks - 1) cin = wait_carry(rc, slot + 64 * kCarrySlot, P.error);  // block blk+1
-            if (blk > 0) publish_carry(rc, slot, rapply(rcompose(load_map(0), suf), cin));
+            if (blk > 0) publish_carry(rc, slot, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin));
         }
-        sm_cin[0][lane] = cin.G;
-        sm_cin[1][lane] = cin.J;
-        sm_cin[2][lane] = cin.Gp;
-        sm_cin[3][lane] = cin.Jp;
-        sm_cin_s[lane] = cin.sg;
+        sm.cin[0][lane] = cin.G;
+        sm.cin[1][lane] = cin.J;
+        sm.cin[2][lane] = cin.Gp;
+        sm.cin[3][lane] = cin.Jp;
+        sm.cin_s[lane] = cin.sg;
     }
-    __syncthreads();
-    const RCarry C = rapply(suf, RCarry{sm_cin[0][lane], sm_cin[1][lane], sm_cin[2][lane], sm_cin[3][lane],
-                                        sm_cin_s[lane]});
+    lds_sync();
+    const RCarry C = rapply(suf, RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane],
+                                        sm.cin_s[lane]});
+    const float ndw = sp.reverse(C, g, ch, eu, dec, fast_out);
+    put_partials(sm, P, tile * P.nblocks + blk, wave, lane, ndw, sp.du);
+}
 
-    // ---- reverse sweep from the carry at the span's end ----------------------------
-    float acc_dw = 0.f;
-    if (fast) {
-        acc_t G = static_cast<acc_t>(ldexp(C.G, sc - C.sg)), J = static_cast<acc_t>(ldexp(C.J, sc - C.sg));
-        acc_t Gp = static_cast<acc_t>(ldexp(C.Gp, sc - C.sg)), Jp = static_cast<acc_t>(ldexp(C.Jp, sc - C.sg));
-#pragma unroll
-        for (int j = L - 1; j >= 0; --j) {
-            const float e = a_e[j], vm = a_vm[j];
-            const float Gf = static_cast<float>(G);
-            buf_store(fmaf(e, Gf, a_gpi[j]), rdv, vout, j * row_out);
-            buf_store(fmaf(e, static_cast<float>(fma(static_cast<acc_t>(vm), G, -J)), a_gvy[j]), rdk, vout,
-                      j * row_out);
-            acc_dw = fmaf(e, static_cast<float>(fma(static_cast<acc_t>(vm), Gp, -Jp)), acc_dw);
-            const acc_t ld = static_cast<acc_t>(a_ld[j]);
-            const acc_t GG = Gp + G;
-            Jp = dec.mul(fma(ld, GG, Jp + J));
-            Gp = dec.mul(GG);
-            J = dec.mul(fma(ld, G, J)) + static_cast<acc_t>(a_grpd[j]);
-            G = dec.mul(G) + static_cast<acc_t>(a_gr[j]);
-        }
-    } else {
-        // general path, without per-token arrays: token t's quantities come
-        // from a recompute over the span's first t + 1 tokens (inputs re-read)
-        double G = C.G, J = C.J, Gp = C.Gp, Jp = C.Jp;
-        int sg = C.sg;
-#pragma unroll 1
-        for (int t = L - 1; t >= 0; --t) {
-            MSt st = x0;
-#pragma unroll 1
-            for (int j = 0; j < t; ++j)
-                (void)mean_step(st, BufLd<TIn>::at(rk, vin, j * row_in), BufLd<TIn>::at(rv, vin, j * row_in), ch,
-                                eu, fast_out);
-            const TokQ q = mean_step(st, BufLd<TIn>::at(rk, vin, t * row_in), BufLd<TIn>::at(rv, vin, t * row_in),
-                                     ch, eu, fast_out);
-            const float g = BufLd<TIn>::at(rg, vin, t * row_in);
-            const int ds = st.s - sg;  // bring the carry to this token's scale
-            G = ldexp(G, ds);
-            J = ldexp(J, ds);
-            Gp = ldexp(Gp, ds);
-            Jp = ldexp(Jp, ds);
-            sg = st.s;
-            const float gpi = g * q.pi;
-            buf_store(fmaf(q.e, static_cast<float>(G), gpi), rdv, vout, t * row_out);
-            buf_store(fmaf(gpi, q.vy, q.e * static_cast<float>(fma(static_cast<double>(q.vm), G, -J))), rdk, vout,
-                      t * row_out);
-            acc_dw = fmaf(q.e, static_cast<float>(fma(static_cast<double>(q.vm), Gp, -Jp)), acc_dw);
-            const double gr = static_cast<double>(g * q.rho), ld = q.ld;
-            const double GG = Gp + G;
-            Jp = dd * fma(ld, GG, Jp + J);
-            Gp = dd * GG;
-            J = fma(dd, fma(ld, G, J), gr * static_cast<double>(q.pd));
-            G = fma(dd, G, gr);
-        }
-    }
+// Whole-tile backward: one workgroup walks all time blocks of its tile from
+// the last to the first, keeping the carry in LDS (no cross-workgroup
+// exchange) and loading the next block's inputs while it computes the current
+// one.  Used when there are enough tiles to fill the GPU.
+template <typename TIn, int L, int W>
+__global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
+    __shared__ BwdShared<W> sm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tile = blockIdx.x;
+    const int64_t b = tile / P.nct;
+    const int64_t c = (tile - b * P.nct) * 64 + lane;
+    const bool cok = c < P.C;
+    const float wc = cok ? P.w[c] : 0.f;
+    const float uc = cok ? P.u[c] : 0.f;
+    const Chan ch = make_chan(wc, uc);
+    const bool fast_out = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
+    const float eu = ex2(ch.u2);
+    const Decay dec{ch.dhi, ch.dlo, ch.dd};
+    const double dL = ipow<L>(ch.dd);
 
-    // ---- dw, du partial sums of this block (fixed order over waves) -------------
-    sm_red[wave][0][lane] = -acc_dw;
-    sm_red[wave][1][lane] = acc_du;
-    __syncthreads();
-    if (wave == 0) {
-        float sw = 0.f, su = 0.f;
-#pragma unroll
-        for (int i = 0; i < W; ++i) {
-            sw += sm_red[i][0][lane];
-            su += sm_red[i][1][lane];
+    RCarry cin{0.0, 0.0, 0.0, 0.0, 0};  // carry at the current block's end (same in every wave)
+    float ndw = 0.f, du = 0.f;
+    SpanIn<TIn, L> cur, nxt;
+    cur.load(span_geo<TIn, L, W>(P, b, c, cok, P.nblocks - 1, wave), P.C);
+    for (int64_t blk = P.nblocks - 1; blk >= 0; --blk) {
+        const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
+        if (blk > 0) nxt.load(span_geo<TIn, L, W>(P, b, c, cok, blk - 1, wave), P.C);
+        Span<TIn, L> sp;
+        sp.recompute(cur, g, ch, eu, dec, fast_out);
+        du += sp.du;
+        put_map(sm, wave, lane, sp);
+        lds_sync();
+        RMap suf = rmap_identity();
+        for (int i = W - 1; i > wave; --i) suf = rcompose(get_map(sm, i, lane, dL), suf);
+        if (wave == 0) {
+            const RCarry out = rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin);
+            sm.cin[0][lane] = out.G;
+            sm.cin[1][lane] = out.J;
+            sm.cin[2][lane] = out.Gp;
+            sm.cin[3][lane] = out.Jp;
+            sm.cin_s[lane] = out.sg;
         }
-        float* pp = P.part + ((tile * P.nblocks + blk) * 2) * 64 + lane;
-        pp[0] = sw;
-        pp[64] = su;
+        ndw += sp.reverse(rapply(suf, cin), g, ch, eu, dec, fast_out);
+        lds_sync();
+        cin = RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane], sm.cin_s[lane]};
+        cur = nxt;
     }
+    put_partials(sm, P, tile, wave, lane, ndw, du);
 }
 
 __global__ void bwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
@@ -579,8 +690,12 @@ namespace {
 #ifndef WKV_BWD_W
 #define WKV_BWD_W 8
 #endif
+#ifndef WKV_BWD_TILE_W
+#define WKV_BWD_TILE_W 4
+#endif
 constexpr int kBwdL = WKV_BWD_L;
-constexpr int kBwdW = WKV_BWD_W;
+constexpr int kBwdW = WKV_BWD_W;        // waves per workgroup, time-split kernel
+constexpr int kBwdTileW = WKV_BWD_TILE_W;  // waves per workgroup, whole-tile kernel
 static_assert(kBwdL % kCkptLen == 0, "backward spans must start on saved forward states");
 
 struct BwdLayout {
@@ -631,24 +746,43 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     P.dk = a.dk; P.dv = a.dv;
     P.ckpt = ckpt;
     P.nblk_ck = l.nblk_ck;
-    P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+    P.nct = l.nct; P.ntiles = l.ntiles;
+    P.part = reinterpret_cast<float*>(ws + l.off_part);
+
+    // Enough tiles to give every CU two workgroups: one workgroup per tile
+    // walks the whole sequence (no carries between workgroups).
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (l.ntiles >= 2 * static_cast<int64_t>(ncu)) {
+        P.nblocks = (a.T + kBwdL * kBwdTileW - 1) / (kBwdL * kBwdTileW);
+        hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW>), dim3(static_cast<unsigned>(l.ntiles)),
+                           dim3(64 * kBwdTileW), 0, stream, P);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,
+                           stream, a.B, a.C, l.nct, int64_t{1}, P.part, a.dw, a.du);
+        return hipGetLastError();
+    }
+
+    P.nblocks = l.nblocks;
     P.counter = reinterpret_cast<uint32_t*>(ws);
     P.error = P.counter + 1;
     P.carry = reinterpret_cast<float*>(ws + l.off_carry);
     P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
-    P.part = reinterpret_cast<float*>(ws + l.off_part);
     if (l.nblocks > 1) {
         const int64_t nwords = static_cast<int64_t>(l.carry_bytes / 4);
         int64_t g = (nwords + 255) / 256;
         if (g > 4096) g = 4096;
         hipLaunchKernelGGL(bwd_chunk_init_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream,
                            P.counter, reinterpret_cast<uint32_t*>(P.carry), nwords);
-        const hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW>), dim3(static_cast<unsigned>(l.ntiles * l.nblocks)),
                        dim3(64 * kBwdW), 0, stream, P);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,
                        stream, a.B, a.C, l.nct, l.nblocks, P.part, a.dw, a.du);

@@ -97,17 +97,31 @@ __device__ __forceinline__ void buf_store(float v, Rsrc r, uint32_t voff, uint32
 
 // ---- per-channel constants -------------------------------------------------
 struct Chan {
+    double dd;       // e^{-w}
     float dhi, dlo;  // e^{-w} = dhi + dlo (to ~2^-48 relative)
     float u2;        // u * log2(e)
 };
 
 __device__ __forceinline__ Chan make_chan(float w, float u) {
     Chan ch;
-    const double dd = exp(-static_cast<double>(w));
-    ch.dhi = static_cast<float>(dd);
-    ch.dlo = static_cast<float>(dd - static_cast<double>(ch.dhi));
+    ch.dd = exp(-static_cast<double>(w));
+    ch.dhi = static_cast<float>(ch.dd);
+    ch.dlo = static_cast<float>(ch.dd - static_cast<double>(ch.dhi));
     ch.u2 = u * kL2E;
     return ch;
+}
+
+// x^N by repeated squaring (N a compile-time count: a few float64 multiplies
+// instead of another exp; relative error ~N 2^-53).
+template <int N>
+__device__ __forceinline__ double ipow(double x) {
+    double r = 1.0;
+#pragma unroll
+    for (int n = N; n > 0; n >>= 1) {
+        if (n & 1) r *= x;
+        x *= x;
+    }
+    return r;
 }
 
 // ---- keys -----------------------------------------------------------------------

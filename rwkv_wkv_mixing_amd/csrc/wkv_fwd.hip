@@ -165,93 +165,167 @@ __device__ __forceinline__ float corrected_outputs(const St& X, int sl, const fl
     return dmin;
 }
 
+// Where one wave's sub-chunk lives for one lane.  Tokens past T read as
+// k = v = 0 (they follow every real token of the wave, so they change no real
+// output) and their stores are dropped.
+struct FwdGeo {
+    Rsrc rk, rv, ry;
+    uint32_t vin, vout, row_in, row_out;
+    int nvalid;  // real tokens in the sub-chunk
+    float* ckp;  // saved states of the sub-chunk, or nullptr
+};
+
+template <typename TIn, int L, int W>
+__device__ __forceinline__ FwdGeo fwd_geo(const FwdChunk& P, int64_t b, int64_t c, bool cok, int64_t blk, int wave) {
+    constexpr int ES = BufLd<TIn>::kBytes;
+    const int64_t tb0 = blk * (int64_t)(L * W);  // first token of the block
+    const int64_t t0 = tb0 + (int64_t)wave * L;  // first token of this wave
+    const int64_t rem = P.T - t0;
+    const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
+    const int64_t row0 = (b * P.T + tb0) * P.C;
+    FwdGeo g;
+    g.nvalid = rem <= 0 ? 0 : (rem >= L ? L : static_cast<int>(rem));
+    g.rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, (uint32_t)(blk_tokens * P.C * ES));
+    g.rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, (uint32_t)(blk_tokens * P.C * ES));
+    // y == nullptr (the backward's state-only run): a zero-size buffer drops every store
+    g.ry = P.y != nullptr ? make_rsrc(P.y + row0, (uint32_t)(blk_tokens * P.C * 4)) : make_rsrc(nullptr, 0);
+    const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;  // element offset
+    g.vin = cok ? lin * ES : kOffNone;
+    g.vout = cok ? lin * 4 : kOffNone;
+    g.row_in = (uint32_t)(P.C * ES);
+    g.row_out = (uint32_t)(P.C * 4);
+    g.ckp = (P.ckpt != nullptr && cok && g.nvalid > 0) ? P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c
+                                                       : nullptr;
+    return g;
+}
+
+// One wave's sub-chunk: the local pass (or general pass 1) and, once the
+// carry-in is known, the outputs.
+template <typename TIn, int L>
+struct SubWork {
+    float N[L], D[L];
+    St mid[L / kCkptLen];
+    St st;    // summary: the sub-chunk run from the empty state
+    int sl;   // fixed local scale
+    bool fast_local;
+
+    __device__ __forceinline__ void local(SubChunk<TIn, L>& sc, const FwdGeo& g, const Chan& ch, float eu,
+                                          float wc, float uc) {
+        float kmax = -INFINITY, kmin = INFINITY;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            kmax = fmaxf(kmax, sc.k(j));
+            kmin = fminf(kmin, sc.k(j));
+        }
+        sc.opaque();
+        sl = key_split(kmax).n;
+        const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
+        fast_local = __all((wc >= 0.f) & (fabsf(uc) <= kFastU) & keys_ok);
+        st = empty_state();
+        if (fast_local) {
+            st = local_pass(sc, sl, ch, eu, N, D, mid);
+            fast_local = __all(st.b >= kTiny);
+        }
+        if (!fast_local) {  // general pass 1, reading one token at a time (rare: kept register-light)
+            st = empty_state();
+#pragma unroll 1
+            for (int j = 0; j < L; ++j) {
+                const float e = key_weight(st, key_split(BufLd<TIn>::at(g.rk, g.vin, j * g.row_in)));
+                token_add(st, e, BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch);
+            }
+        }
+    }
+
+    // Outputs (and saved states) from the carry-in X: the fixed-scale
+    // correction, or the general second recurrence when the wave needs it.
+    __device__ __forceinline__ void outputs(const St& X, const FwdGeo& g, const Chan& ch, float eu, bool fast,
+                                            bool want_y, int64_t C) const {
+        const bool carry_fits = !(X.b > 0.f) | ((X.s - sl + __builtin_amdgcn_frexp_expf(X.b) <= kCarryAbove) &
+                                                (X.s - sl + __builtin_amdgcn_frexp_expf(X.a) <= kCarryAbove + 20));
+        bool fast_out = fast_local && __all(carry_fits);
+        if (fast_out && want_y) fast_out = __all(corrected_outputs(X, sl, N, D, ch, g.ry, g.vout, g.row_out) >= kTiny);
+        if (fast_out) {
+            if (g.ckp != nullptr) {
+                const double dck = ipow<kCkptLen>(ch.dd);
+                double dq = 1.0;
+#pragma unroll
+                for (int q = 0; q < L / kCkptLen; ++q) {
+                    if (q * kCkptLen < g.nvalid) {
+                        const St x = q == 0 ? X : combine(X, mid[q], dq);
+                        float* cp = g.ckp + q * 3 * C;
+                        cp[0] = x.a;
+                        cp[C] = x.b;
+                        cp[2 * C] = static_cast<float>(x.s);
+                    }
+                    dq *= dck;
+                }
+            }
+        } else if (fast) {  // general path: rewrites every output of the wave
+            general_outputs<true, TIn, L>(X, g.rk, g.rv, g.vin, g.row_in, g.nvalid, ch, eu, g.ry, g.vout, g.row_out,
+                                          g.ckp, C);
+        } else {
+            general_outputs<false, TIn, L>(X, g.rk, g.rv, g.vin, g.row_in, g.nvalid, ch, eu, g.ry, g.vout, g.row_out,
+                                           g.ckp, C);
+        }
+    }
+};
+
+template <int W>
+struct FwdShared {
+    float a[W][64], b[W][64];
+    int s[W][64];
+    float ea[64], eb[64];  // block carry-in E
+    int es[64];
+    uint32_t ticket;
+};
+
+// Prefix of the summaries of waves 0..wave-1 of a block.
+template <int W>
+__device__ __forceinline__ St wave_prefix(const FwdShared<W>& sm, int wave, int lane, double dL) {
+    St pref = empty_state();
+    for (int i = 0; i < wave; ++i) pref = combine(pref, St{sm.a[i][lane], sm.b[i][lane], sm.s[i][lane]}, dL);
+    return pref;
+}
+
+// Time-split forward: one workgroup per (tile, time block); blocks are
+// chained in time through the coherent carry slots.
 template <typename TIn, int L, int W>
 __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
-    constexpr int ES = BufLd<TIn>::kBytes;
-    __shared__ float sm_a[W][64];
-    __shared__ float sm_b[W][64];
-    __shared__ int sm_s[W][64];
-    __shared__ float sm_e[2][64];  // block carry-in E
-    __shared__ int sm_es[64];
-    __shared__ uint32_t sm_ticket;
+    __shared__ FwdShared<W> sm;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     int64_t ticket = blockIdx.x;
     if (P.nblocks > 1) {
-        if (threadIdx.x == 0) sm_ticket = atomicAdd(P.counter, 1u);
+        if (threadIdx.x == 0) sm.ticket = atomicAdd(P.counter, 1u);
         __syncthreads();
-        ticket = sm_ticket;
+        ticket = sm.ticket;
     }
     const int64_t blk = ticket / P.ntiles;
     const int64_t tile = ticket - blk * P.ntiles;
     const int64_t b = tile / P.nct;
     const int64_t c = (tile - b * P.nct) * 64 + lane;
     const bool cok = c < P.C;
-    const int64_t tb0 = blk * (int64_t)(L * W);  // first token of the block
-    const int64_t t0 = tb0 + (int64_t)wave * L;  // first token of this wave
-    const int64_t rem = P.T - t0;
-    const int nvalid = rem <= 0 ? 0 : (rem >= L ? L : static_cast<int>(rem));
     const float wc = cok ? P.w[c] : 0.f;
     const float uc = cok ? P.u[c] : 0.f;
     const Chan ch = make_chan(wc, uc);
     const bool fast = __all((fabsf(uc) <= kFastU) & (wc >= 0.f));
     const float eu = ex2(ch.u2);
+    const double dL = ipow<L>(ch.dd);
 
-    // buffers over this block's rows of batch row b: [tokens tb0 .. min(T, tb0 + W L)) x C
-    const int64_t blk_tokens = (P.T - tb0) < (int64_t)(L * W) ? (P.T - tb0) : (int64_t)(L * W);
-    const int64_t row0 = (b * P.T + tb0) * P.C;
-    const Rsrc rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, (uint32_t)(blk_tokens * P.C * ES));
-    const Rsrc rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, (uint32_t)(blk_tokens * P.C * ES));
-    // y == nullptr (the backward's state-only run): a zero-size buffer drops every store
-    const Rsrc ry = P.y != nullptr ? make_rsrc(P.y + row0, (uint32_t)(blk_tokens * P.C * 4)) : make_rsrc(nullptr, 0);
-    const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;  // element offset
-    const uint32_t vin = cok ? lin * ES : kOffNone;
-    const uint32_t vout = cok ? lin * 4 : kOffNone;
-    const uint32_t row_in = (uint32_t)(P.C * ES), row_out = (uint32_t)(P.C * 4);
-
+    const FwdGeo g = fwd_geo<TIn, L, W>(P, b, c, cok, blk, wave);
     SubChunk<TIn, L> sc;
-    sc.load(rk, rv, vin, row_in);
-
-    // ---- local pass (fixed scale) or pass 1 (general): summary from the empty state
-    // (tokens past T read as k = v = 0: they follow every real token of the
-    // wave, so they change no real output, and their stores are dropped)
-    float kmax = -INFINITY, kmin = INFINITY;
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        kmax = fmaxf(kmax, sc.k(j));
-        kmin = fminf(kmin, sc.k(j));
-    }
-    sc.opaque();
-    const int sl = key_split(kmax).n;
-    const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
-    bool fast_local = __all((wc >= 0.f) & (fabsf(uc) <= kFastU) & keys_ok);
-    float N[L], D[L];
-    St mid[L / kCkptLen];
-    St st = empty_state();
-    if (fast_local) {
-        st = local_pass(sc, sl, ch, eu, N, D, mid);
-        fast_local = __all(st.b >= kTiny);
-    }
-    if (!fast_local) {  // general pass 1, reading one token at a time (rare: kept register-light)
-        st = empty_state();
-#pragma unroll 1
-        for (int j = 0; j < L; ++j) {
-            const float e = key_weight(st, key_split(BufLd<TIn>::at(rk, vin, j * row_in)));
-            token_add(st, e, BufLd<TIn>::at(rv, vin, j * row_in), ch);
-        }
-    }
-    sm_a[wave][lane] = st.a;
-    sm_b[wave][lane] = st.b;
-    sm_s[wave][lane] = st.s;
+    sc.load(g.rk, g.rv, g.vin, g.row_in);
+    SubWork<TIn, L> sw;
+    sw.local(sc, g, ch, eu, wc, uc);
+    sm.a[wave][lane] = sw.st.a;
+    sm.b[wave][lane] = sw.st.b;
+    sm.s[wave][lane] = sw.st.s;
     __syncthreads();
 
-    // ---- scan ------------------------------------------------------------------
     // every wave: prefix of the sub-chunks before it; the last wave also forms
-    // the block aggregate and fetches / publishes the block carry.
-    const double dL = exp(-static_cast<double>(wc) * L);
-    St pref = empty_state();
-    for (int i = 0; i < wave; ++i) pref = combine(pref, St{sm_a[i][lane], sm_b[i][lane], sm_s[i][lane]}, dL);
+    // the block aggregate and fetches / publishes the block carry
+    const St pref = wave_prefix(sm, wave, lane, dL);
     if (wave == W - 1) {
         St E = empty_state();
         if (P.nblocks > 1) {
@@ -262,47 +336,17 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
             const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * 16);
             if (blk > 0) E = wait_state(rc, slot - 64 * 16, P.error);  // block blk-1, same lane
             if (blk < P.nblocks - 1)  // then this block is full
-                publish_state(rc, slot, combine(E, combine(pref, st, dL), dTB));
+                publish_state(rc, slot, combine(E, combine(pref, sw.st, dL), dTB));
         }
-        sm_e[0][lane] = E.a;
-        sm_e[1][lane] = E.b;
-        sm_es[lane] = E.s;
+        sm.ea[lane] = E.a;
+        sm.eb[lane] = E.b;
+        sm.es[lane] = E.s;
     }
     __syncthreads();
     double dpow = 1.0;
     for (int i = 0; i < wave; ++i) dpow *= dL;
-    const St s2 = combine(St{sm_e[0][lane], sm_e[1][lane], sm_es[lane]}, pref, dpow);
-
-    // ---- outputs from the carry-in X = s2 ---------------------------------------
-    float* ckp = (P.ckpt != nullptr && cok) ? P.ckpt + ((b * P.nblk_ck + t0 / kCkptLen) * 3) * P.C + c : nullptr;
-    const bool carry_fits = !(s2.b > 0.f) | ((s2.s - sl + __builtin_amdgcn_frexp_expf(s2.b) <= kCarryAbove) &
-                                             (s2.s - sl + __builtin_amdgcn_frexp_expf(s2.a) <= kCarryAbove + 20));
-    bool fast_out = fast_local && __all(carry_fits);
-    if (fast_out && P.y != nullptr) fast_out = __all(corrected_outputs(s2, sl, N, D, ch, ry, vout, row_out) >= kTiny);
-    if (fast_out) {
-        if (ckp != nullptr) {
-            const double dck = exp(-static_cast<double>(wc) * kCkptLen);
-            double dq = 1.0;
-#pragma unroll
-            for (int q = 0; q < L / kCkptLen; ++q) {
-                if (q * kCkptLen < nvalid) {
-                    const St x = q == 0 ? s2 : combine(s2, mid[q], dq);
-                    float* cp = ckp + q * 3 * P.C;
-                    cp[0] = x.a;
-                    cp[P.C] = x.b;
-                    cp[2 * P.C] = static_cast<float>(x.s);
-                }
-                dq *= dck;
-            }
-        }
-    } else {
-        // general path: a second recurrence from X with per-token rescales;
-        // it rewrites every output of the wave
-        if (fast)
-            general_outputs<true, TIn, L>(s2, rk, rv, vin, row_in, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
-        else
-            general_outputs<false, TIn, L>(s2, rk, rv, vin, row_in, nvalid, ch, eu, ry, vout, row_out, ckp, P.C);
-    }
+    const St s2 = combine(St{sm.ea[lane], sm.eb[lane], sm.es[lane]}, pref, dpow);
+    sw.outputs(s2, g, ch, eu, fast, P.y != nullptr, P.C);
 }
 
 __global__ void fwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
@@ -351,6 +395,7 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     P.ckpt = static_cast<float*>(a.ckpt);
     P.nblk_ck = a.nblk;
     P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+
     if (l.nblocks > 1) {
         char* ws = static_cast<char*>(a.ws);
         P.counter = reinterpret_cast<uint32_t*>(ws);

@@ -33,6 +33,14 @@ __device__ __forceinline__ St combine(const St& X, const St& S, double D) {
     return St{ldx(xa, X.s - sn) + ldx(S.a, S.s - sn), ldx(xb, X.s - sn) + ldx(S.b, S.s - sn), sn};
 }
 
+// Barrier for LDS traffic only: outstanding global loads (prefetches) and
+// stores stay in flight across it.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- carries between workgroups --------------------------------------------------
 // A chained scan along time: the workgroup of time block j waits for the
 // inclusive state of block j-1 of the same tile and publishes its own.  Each
