@@ -22,6 +22,8 @@ copy: the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters).
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "WKV fwd+bwd channel·tokens/s and HBM GB/s (% of peak), B=8 T=1024 C=4096"
 
 
@@ -63,15 +66,65 @@ def upload(p, dev):
     return d
 
 
-def cpu_oracle_fwdbwd(p, with_bwd=True):
-    """The float64 numpy oracle (single thread) on the same inputs."""
+def cpu_oracle(p, with_bwd=True):
+    """The float64 oracle on the same inputs, timed on this host: the C twin
+    with OpenMP over all lanes (median of 3 runs) and the numpy oracle (one
+    run, effectively one core).  Returns (seconds_c, threads_c, seconds_numpy)."""
     from oracle import wkv_backward_ref, wkv_forward_ref
+    from oracle.ctwin import ctwin_backward, ctwin_forward
 
+    runs, used = [], 0
+    for _ in range(3):
+        t0 = time.perf_counter()
+        used = ctwin_forward(p.w, p.u, p.k, p.v)[3]
+        if with_bwd:
+            ctwin_backward(p.w, p.u, p.k, p.v, p.gy)
+        runs.append(time.perf_counter() - t0)
     t0 = time.perf_counter()
     wkv_forward_ref(p.w, p.u, p.k, p.v)
     if with_bwd:
         wkv_backward_ref(p.w, p.u, p.k, p.v, p.gy)
-    return time.perf_counter() - t0
+    t_np = time.perf_counter() - t0
+    return float(np.median(runs)), int(used), t_np
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources and the C header: a recorded traffic
+    figure applies only to the kernels it was measured on."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "rwkv_wkv_mixing_amd", "csrc", "*")))
+    for f in files + [os.path.join(ROOT, "include", "wkv.h")]:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, call):
+    """HBM bytes per call of `call` recorded in profiles/hbm_traffic_<workload>.md
+    (FETCH_SIZE / WRITE_SIZE counters scaled by the copy-kernel calibration),
+    or None when absent or measured on other kernel sources."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    src, vals = None, {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("source-sha256:"):
+                src = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic-bytes-per-call:"):
+                for item in line.split(":", 1)[1].split():
+                    k, v = item.split("=")
+                    vals[k] = int(v)
+    if src != kernel_source_hash():
+        return None
+    return vals.get(call)
+
+
+def stats_us(ms_list):
+    a = np.asarray(ms_list, np.float64) * 1e3
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
 
 
 def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
@@ -118,23 +171,24 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations with HIP events on the stream the kernels run on
+    # per-call durations with HIP events on the stream the kernels run on
+    # (the ops launch on torch's current stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if with_bwd else 0.0
+    fwd = stats_us([e[0].elapsed_time(e[1]) for e in evs])
+    bwd = stats_us([e[1].elapsed_time(e[2]) for e in evs]) if with_bwd else None
 
     n = p.n
     ms = wall * 1e3 / args.steps
     value = n / (wall / args.steps)
     alg_bytes = (bytes_fwd + (bytes_bwd if with_bwd else 0)) * n
-    if with_bwd and bwd_ms >= fwd_ms:
-        dom, dom_ms, dom_bytes = "wkv_backward", bwd_ms, bytes_bwd * n
+    if with_bwd and bwd["mean"] >= fwd["mean"]:
+        dom, dom_us, dom_bytes = "wkv_backward", bwd["mean"], bytes_bwd * n
     else:
-        dom, dom_ms, dom_bytes = "wkv_forward", fwd_ms, bytes_fwd * n
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        dom, dom_us, dom_bytes = "wkv_forward", fwd["mean"], bytes_fwd * n
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     out = {
         "metric": METRIC if workload_name == "fwdbwd" else f"WKV {'fwd+bwd' if with_bwd else 'fwd'} channel·tokens/s, {p.name}",
         "value": value,
@@ -152,39 +206,43 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
                    "in_dtype": p.dtype},
         "hbm_gbps_algorithmic": alg_bytes / (wall / args.steps) / 1e9,
         "pct_hbm_peak": 100.0 * alg_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS,
-        "kernel_ms": {"wkv_forward": fwd_ms, "wkv_backward": bwd_ms},
+        "call_us": {"wkv_forward": fwd, "wkv_backward": bwd},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(traffic_key(p, with_bwd), dom),
                      "alg_bytes_per_launch": dom_bytes},
     }
     return out
 
 
+def traffic_key(p, with_bwd):
+    return f"{'fwdbwd' if with_bwd else 'fwd'}_{p.dtype}_B{p.B}_T{p.T}_C{p.C}"
+
+
 def bench_step5(args):
+    """Decode step at L=32 layers x B=256 streams x C=4096: per-layer w, u drawn
+    as for the decode workload, fresh bf16 k, v per step (torch's seeded
+    Philox generator, as the decode parity test), states warmed up by 32 steps
+    from the empty state."""
     import torch
 
     from rwkv_wkv_mixing_amd import ops, workloads as W
 
     dev = torch.device("cuda:0")
-    Lr, Bs, C = 32, 256, 4096
-    rng = np.random.default_rng(0)
-    w = torch.from_numpy(np.exp(rng.uniform(-6, 1.5, (Lr, C))).astype(np.float32)).to(dev)
-    u = torch.from_numpy(rng.normal(0, 1, (Lr, C)).astype(np.float32)).to(dev)
-    dp = W.DecodeProblem(Lr, Bs, C, 0, None, None, None, None, seed=0)
-    sets = []
-    for i in range(args.sets):
-        k, v = W.step_inputs_torch(dp, i, dev)
-        a = torch.randn((Lr, Bs, C), device=dev)
-        b = torch.rand((Lr, Bs, C), device=dev) + 0.5
-        p = torch.randn((Lr, Bs, C), device=dev)
-        y = torch.empty((Lr, Bs, C), device=dev)
-        sets.append((k, v, a, b, p, y))
+    dp = W.make_decode(32, 256, 4096, 0, seed=0)  # same w, u draws; no prefix
+    Lr, Bs, C = dp.L, dp.B, dp.C
+    w = torch.from_numpy(dp.w).to(dev)
+    u = torch.from_numpy(dp.u).to(dev)
+    nsets = max(args.sets, 2)
+    kv = [W.step_inputs_torch(dp, i, dev) for i in range(nsets)]
+    a, b, p = ops.empty_state(Lr, Bs, C, dev)
+    y = torch.empty((Lr, Bs, C), device=dev)
 
     def step(i):
-        k, v, a, b, p, y = sets[i % len(sets)]
+        k, v = kv[i % nsets]
         ops.wkv_step(w, u, k, v, a, b, p, y=y)
 
-    for i in range(args.warmup):
+    for i in range(32 + args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -198,19 +256,35 @@ def bench_step5(args):
         step(i)
         evs[i][1].record()
     torch.cuda.synchronize()
-    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    st = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
     n = Lr * Bs * C
-    achieved = 32 * n / (kms * 1e-3) / 1e9
-    return {
+    achieved = 32 * n / (st["mean"] * 1e-6) / 1e9
+    out = {
         "metric": "WKV decode step lane-steps/s, L=32 B=256 C=4096 bf16 k,v",
         "value": n / (wall / args.steps), "unit": "lane·steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": {"workload": "wkv4 decode step L=32 B=256 C=4096 bf16"},
+        "call_us": {"wkv_step": st},
         "roofline": {"bound": "hbm", "kernel": "wkv_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("step_bf16_L32_B256_C4096", "wkv_step"),
                      "alg_bytes_per_launch": 32 * n},
     }
+    if not args.no_cpu:
+        # numpy oracle on a bounded sample: layer 0, all 256 streams, 10 steps
+        from oracle import wkv_step_ref
+
+        kb, vb = [t[0].float().cpu().numpy() for t in kv[0]]
+        sa = np.zeros((Bs, C)); sb = np.zeros((Bs, C)); sp = np.full((Bs, C), -1e38)
+        t0 = time.perf_counter()
+        for _ in range(10):
+            _, sa, sb, sp = wkv_step_ref(dp.w[0], dp.u[0], kb, vb, sa, sb, sp)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 10 * Bs * C / t_np, "unit": "lane·steps/s", "cores": 1, "kind": "oracle",
+                               "sample": f"10 steps of layer 0 x 256 streams x 4096 channels ({10 * Bs * C} "
+                                         f"lane-steps) through the float64 numpy step oracle, {t_np:.2f} s"}
+    return out
 
 
 def bench_copy(args):
@@ -263,12 +337,14 @@ def main():
         p, with_bwd, bf, bb = W.config4(), False, 12, 0
     out = bench_seq(args, p, with_bwd, args.workload, bf, bb)
     if not args.no_cpu:
-        cpu_s = cpu_oracle_fwdbwd(p, with_bwd)
-        out["cpu_baseline"] = {"value": p.n / cpu_s, "unit": "channel·tokens/s", "cores": 1,
+        t_c, threads, t_np = cpu_oracle(p, with_bwd)
+        what = "fwd+bwd" if with_bwd else "fwd"
+        out["cpu_baseline"] = {"value": p.n / t_c, "unit": "channel·tokens/s", "cores": threads,
                                "kind": "oracle",
-                               "sample": f"the whole workload ({p.n} channel*tokens, "
-                                         f"{'fwd+bwd' if with_bwd else 'fwd'}), numpy float64 oracle, "
-                                         f"{cpu_s:.2f} s on one host core"}
+                               "sample": f"the whole workload ({p.n} channel*tokens, {what}) through the float64 "
+                                         f"C oracle with OpenMP over lanes: median of 3 runs, {t_c:.2f} s on "
+                                         f"{threads} threads; the numpy oracle (one core) took {t_np:.2f} s",
+                               "numpy_value": p.n / t_np, "numpy_cores": 1}
     print(json.dumps(out), flush=True)
 
 
