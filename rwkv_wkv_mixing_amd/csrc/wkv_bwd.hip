@@ -345,15 +345,12 @@ struct Span {
         x0.b = in.b0;
         x0.m = in.b0 > 0.f ? in.a0 / in.b0 : 0.f;
         // fixed span scale: the larger of the history level and the largest key
-        float kmax = -INFINITY, kmin = INFINITY;
+        float kmax = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < L; ++j) {
-            kmax = fmaxf(kmax, in.kv.k(j));
-            kmin = fminf(kmin, in.kv.k(j));
-        }
+        for (int j = 0; j < L; ++j) kmax = fmaxf(kmax, in.kv.k(j));
         const int lvl0 = x0.b > 0.f ? x0.s + __builtin_amdgcn_frexp_expf(x0.b) : kSEmpty;
         const int sc = max(lvl0, key_split(kmax).n);
-        const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
+        const bool keys_ok = kmax * kL2E < kNMax;
         fast = fast_out && __all(keys_ok);
         Psum = Gs = Js = Gps = Jps = 0;
         du = 0.f;
@@ -361,12 +358,18 @@ struct Span {
         if (fast) {
             float m = x0.m;
             float bb = ldx(x0.b, x0.s - sc);
-            float dmin = INFINITY;
+            float dmin = INFINITY;  // smallest denominator (D_t and B_t) used
+            const float scf = static_cast<float>(sc);
             acc_t dp = 1;
 #pragma unroll
             for (int j = 0; j < L; ++j) {
-                const Key kk = key_split_bounded(in.kv.k(j));
-                const float ej = ldx(kk.em, kk.n - sc);
+                // e = e^k / 2^sc.  For the key that sets the scale fma(k, log2 e,
+                // -sc) is exactly the key split's fraction, so the weight is
+                // bit-equal to the forward's; a key D binades below the span's
+                // scale is rounded to ~D 2^-24 relative while its share of every
+                // denominator here is ~2^-D (the forward's saved states, where
+                // such a key might dominate later, use the exact split)
+                const float ej = ex2(fmaf(in.kv.k(j), kL2E, -scf));
                 const float E = ej * eu;
                 const float den = bb + E;
                 dmin = fminf(dmin, den);

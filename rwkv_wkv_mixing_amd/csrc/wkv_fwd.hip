@@ -134,6 +134,9 @@ __device__ __forceinline__ St local_pass(const SubChunk<TIn, L>& sc, int sl, con
 #pragma unroll
     for (int j = 0; j < L; ++j) {
         if (j % kCkptLen == 0 && j > 0) mid[j / kCkptLen] = St{a, b, sl};
+        // e = e^k / 2^sl from the key split: exact scaling, no rounding of
+        // k log2 e - sl (an output before the sub-chunk's largest key sums only
+        // keys far below sl, whose weights must not carry that rounding)
         const Key kk = key_split_bounded(sc.k(j));
         const float e = ldx(kk.em, kk.n - sl);
         const float v = sc.v(j);
@@ -211,15 +214,12 @@ struct SubWork {
 
     __device__ __forceinline__ void local(SubChunk<TIn, L>& sc, const FwdGeo& g, const Chan& ch, float eu,
                                           float wc, float uc) {
-        float kmax = -INFINITY, kmin = INFINITY;
+        float kmax = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < L; ++j) {
-            kmax = fmaxf(kmax, sc.k(j));
-            kmin = fminf(kmin, sc.k(j));
-        }
+        for (int j = 0; j < L; ++j) kmax = fmaxf(kmax, sc.k(j));
         sc.opaque();
         sl = key_split(kmax).n;
-        const bool keys_ok = (kmax * kL2E < kNMax) & (kmin * kL2E > -kNMax);
+        const bool keys_ok = kmax * kL2E < kNMax;
         fast_local = __all((wc >= 0.f) & (fabsf(uc) <= kFastU) & keys_ok);
         st = empty_state();
         if (fast_local) {
