@@ -16,8 +16,10 @@ kernels run on) and the float64 CPU oracle timed on this host.
 Other workloads (not the headline, for measurements quoted in the design
 notes): fwd3 (the headline shape, forward only), fwd2 (B=8 T=1024 C=768 fp32,
 fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32, forward only), step5 (32 layers x
-256 streams x 4096 channels decode step), copy (a plain 1 GiB device-to-device
-copy: the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters).
+256 streams x 4096 channels decode step), prefill (the headline shape's forward
+started from a state and returning it, as wkv_forward_state), copy (a plain
+1 GiB device-to-device copy: the calibration kernel for the FETCH_SIZE /
+WRITE_SIZE counters).
 """
 from __future__ import annotations
 
@@ -44,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -127,7 +129,7 @@ def stats_us(ms_list):
             "p90": float(np.percentile(a, 90))}
 
 
-def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
+def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state=False):
     import torch
 
     from rwkv_wkv_mixing_amd import ops
@@ -140,6 +142,8 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
         s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
         s["y"] = torch.empty((B, T, C), dtype=torch.float32, device=dev)
         s["ck"] = ops.new_ckpt(B, T, C, dev)
+        if with_state:  # a prefill: carry a state in and out (in place)
+            s["st"] = ops.wkv_forward(s["w"], s["u"], s["k"], s["v"], return_state=True)[1]
         if with_bwd:
             s["out"] = (torch.empty((B, T, C), dtype=torch.float32, device=dev),
                         torch.empty((B, T, C), dtype=torch.float32, device=dev),
@@ -153,7 +157,9 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd):
         s = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        ops.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=s["y"], ckpt=s["ck"], workspace=ws_f)
+        st = s.get("st")
+        ops.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=s["y"], ckpt=None if st else s["ck"], workspace=ws_f,
+                        state_in=st, state_out=st)
         if ev is not None:
             ev[1].record()
         if with_bwd:
@@ -329,13 +335,16 @@ def main():
         return
     if args.workload == "fwdbwd":
         p, with_bwd, bf, bb = W.config3(), True, 8, 14
-    elif args.workload == "fwd3":
+    elif args.workload in ("fwd3", "prefill"):
         p, with_bwd, bf, bb = W.config3(), False, 8, 0
     elif args.workload == "fwd2":
         p, with_bwd, bf, bb = W.config2(), True, 12, 20
     else:
         p, with_bwd, bf, bb = W.config4(), False, 12, 0
-    out = bench_seq(args, p, with_bwd, args.workload, bf, bb)
+    out = bench_seq(args, p, with_bwd, args.workload, bf, bb, with_state=args.workload == "prefill")
+    if args.workload == "prefill":
+        out["metric"] = "WKV prefill (forward from a state, returning the state) channel·tokens/s, B=8 T=1024 C=4096 bf16"
+        out["config"]["workload"] += " with state in/out"
     if not args.no_cpu:
         t_c, threads, t_np = cpu_oracle(p, with_bwd)
         what = "fwd+bwd" if with_bwd else "fwd"

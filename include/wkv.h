@@ -119,6 +119,34 @@ wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype,
                          void* hip_stream);
 
 /*
+ * wkv_forward_state - wkv_forward from a given state, also returning the state
+ * after the last token.
+ *
+ * Defines: y_t above with A_0 = a_in e^{p_in}, B_0 = b_in e^{p_in} (the
+ * history of an earlier segment) instead of the empty history, and
+ * (a_out, b_out, p_out) with a_out e^{p_out} = A_T, b_out e^{p_out} = B_T.
+ *   "RWKV模型深度研究报告" section 4.4.2 (encode a long input segment by
+ *   segment, carrying the state), and "RWKV - 把 RNN 重新带回 Transformer 时代
+ *   的线性大模型" section "关键设计 4" (the recurrent mode keeps a constant
+ *   per-layer state): a prefill hands its state to wkv_step.
+ *
+ * a_in, b_in, p_in   [B, C] float32, all NULL (empty history) or all set; the
+ *                    representation of wkv_step (any b <= 0 means empty).
+ * a_out, b_out, p_out [B, C] float32, all NULL or all set; written with
+ *                    the state after token T (for T == 0, the input state).
+ *                    They may alias a_in, b_in, p_in (in-place update).
+ * Other arguments as wkv_forward.  A ckpt written here holds states that
+ * include the given history; wkv_backward then returns the gradients of the
+ * T tokens' inputs with that history held fixed (dw omits the decay of the
+ * history itself).
+ */
+wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype,
+                               const float* w, const float* u, const void* k, const void* v, float* y,
+                               const float* a_in, const float* b_in, const float* p_in,
+                               float* a_out, float* b_out, float* p_out,
+                               void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * wkv_backward - gradients of L = sum_{b,t,c} gy * y through the forward.
  *
  * Defines (derived by differentiating the section-3.2 weighted sum of

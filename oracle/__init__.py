@@ -11,4 +11,5 @@ from .wkv_ref import (  # noqa: F401
     wkv_forward_ref,
     wkv_state_from_sums,
     wkv_step_ref,
+    wkv_sums_from_state,
 )

@@ -54,13 +54,16 @@ def _f64(*xs):
     return [np.asarray(x, dtype=np.float64) for x in xs]
 
 
-def wkv_forward_ref(w, u, k, v, return_sums: bool = False):
+def wkv_forward_ref(w, u, k, v, return_sums: bool = False, A0=None, B0=None):
     """Recurrent WKV forward in float64.
 
     [P5] "一句话总结" / "关键设计 2": with d = e^{-w},
         y_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t}),
         A_t = d A_{t-1} + e^{k_t} v_t,   B_t = d B_{t-1} + e^{k_t},
-    and A_0 = B_0 = 0 (the empty history of the [P4] 3.2 sum).
+    and A_0 = B_0 = 0 (the empty history of the [P4] 3.2 sum), or the plain
+    sums A0, B0 [B, C] of an earlier segment when given ([P3] 4.4.2: a long
+    input is encoded segment by segment, the state carrying the history from
+    one segment into the next).
 
     w, u: [C]; k, v: [B, T, C].  Returns y [B, T, C] (and the final plain sums
     A_T, B_T, each [B, C], when ``return_sums``).  The sums are kept unscaled:
@@ -71,8 +74,8 @@ def wkv_forward_ref(w, u, k, v, return_sums: bool = False):
     Bsz, T, C = k.shape
     d = np.exp(-w)
     eu = np.exp(u)
-    A = np.zeros((Bsz, C))
-    Bs = np.zeros((Bsz, C))
+    A = np.zeros((Bsz, C)) if A0 is None else np.array(A0, dtype=np.float64).reshape(Bsz, C)
+    Bs = np.zeros((Bsz, C)) if B0 is None else np.array(B0, dtype=np.float64).reshape(Bsz, C)
     y = np.empty((Bsz, T, C))
     for t in range(T):
         ek = np.exp(k[:, t, :])
@@ -196,6 +199,14 @@ def wkv_step_ref(w, u, k, v, a, b, p):
     f1 = np.exp(pw - p2)
     f2 = np.exp(k - p2)
     return y, f1 * a + f2 * v, f1 * b + f2, p2
+
+
+def wkv_sums_from_state(a, b, p):
+    """Plain sums of a stable state (a, b, p): A = a e^p, B = b e^p (the empty
+    state, b = 0 with a very negative p, gives A = B = 0)."""
+    a, b, p = _f64(a, b, p)
+    f = np.exp(np.maximum(p, -745.0))
+    return np.where(b > 0, a * f, 0.0), np.where(b > 0, b * f, 0.0)
 
 
 def wkv_state_from_sums(A, B):

@@ -21,6 +21,7 @@ EXPORTS = (
     "wkv_workspace_bytes",
     "wkv_ckpt_bytes",
     "wkv_forward",
+    "wkv_forward_state",
     "wkv_backward",
     "wkv_step",
     "wkv_status_str",
@@ -63,6 +64,8 @@ def declare(L):
     L.wkv_ckpt_bytes.argtypes = [i64, i64, i64]
     L.wkv_forward.restype = i32
     L.wkv_forward.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, vp, vp, sz, vp]
+    L.wkv_forward_state.restype = i32
+    L.wkv_forward_state.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_backward.restype = i32
     L.wkv_backward.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_step.restype = i32

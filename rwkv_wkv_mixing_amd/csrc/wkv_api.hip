@@ -82,12 +82,23 @@ size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
     return static_cast<size_t>(n);
 }
 
-wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
-                         const float* u, const void* k, const void* v, float* y, void* ckpt,
-                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                               const float* u, const void* k, const void* v, float* y,
+                               const float* a_in, const float* b_in, const float* p_in, float* a_out,
+                               float* b_out, float* p_out, void* ckpt, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
     const Plan p = plan(WKV_OP_FORWARD, B, T, C, in_dtype);
     if (p.st != WKV_OK) return p.st;
-    if (p.N == 0) return WKV_OK;
+    const bool sin = a_in || b_in || p_in, sout = a_out || b_out || p_out;
+    if ((sin && !(a_in && b_in && p_in)) || (sout && !(a_out && b_out && p_out))) return WKV_EINVAL;
+    if ((sin && (!aligned(a_in, 4) || !aligned(b_in, 4) || !aligned(p_in, 4))) ||
+        (sout && (!aligned(a_out, 4) || !aligned(b_out, 4) || !aligned(p_out, 4))))
+        return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    wkv::FwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, y, ckpt, p.nblk, workspace, workspace_bytes};
+    a.a_in = a_in; a.b_in = b_in; a.p_in = p_in;
+    a.a_out = a_out; a.b_out = b_out; a.p_out = p_out;
+    if (p.N == 0) return T == 0 ? hip_status(wkv::launch_state_passthrough(a, stream)) : WKV_OK;
     if (!w || !u || !k || !v || !y) return WKV_EINVAL;
     const size_t es = in_size(in_dtype);
     if (!aligned(w, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(k, es) || !aligned(v, es) ||
@@ -95,9 +106,14 @@ wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const fl
         return WKV_EALIGN;
     if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
         return WKV_EWORKSPACE;
-    wkv::FwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, y, ckpt, p.nblk, workspace,
-                   workspace_bytes};
-    return hip_status(wkv::launch_fwd_chunk(a, static_cast<hipStream_t>(hip_stream)));
+    return hip_status(wkv::launch_fwd_chunk(a, stream));
+}
+
+wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                         const float* u, const void* k, const void* v, float* y, void* ckpt,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return wkv_forward_state(B, T, C, in_dtype, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, ckpt, workspace, workspace_bytes, hip_stream);
 }
 
 wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,

@@ -50,6 +50,12 @@ struct FwdChunk {
     uint32_t* error;   // set if a carry wait timed out
     float* carry;      // [ntiles][nblocks][64][4] inclusive block states + status
     uint32_t carry_bytes;
+    const float* a_in;  // optional state before token 1, [B, C] each
+    const float* b_in;
+    const float* p_in;
+    float* a_out;       // optional state after token T, [B, C] each
+    float* b_out;
+    float* p_out;
 };
 
 // The L tokens of one lane's sub-chunk, held in registers across both passes.
@@ -328,6 +334,10 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     const St pref = wave_prefix(sm, wave, lane, dL);
     if (wave == W - 1) {
         St E = empty_state();
+        if (blk == 0 && P.a_in != nullptr && cok) {
+            const int64_t i = b * P.C + c;
+            E = state_from_abp(P.a_in[i], P.b_in[i], P.p_in[i]);
+        }
         if (P.nblocks > 1) {
             double dTB = 1.0;
 #pragma unroll
@@ -347,6 +357,42 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     for (int i = 0; i < wave; ++i) dpow *= dL;
     const St s2 = combine(St{sm.ea[lane], sm.eb[lane], sm.es[lane]}, pref, dpow);
     sw.outputs(s2, g, ch, eu, fast, P.y != nullptr, P.C);
+
+    // the state after token T, from the wave that holds it: its carry-in
+    // combined with its summary when the sub-chunk is full, else a re-run of
+    // its real tokens from the carry-in (the padding past T must not enter it)
+    if (P.a_out != nullptr && g.nvalid > 0 && blk * (int64_t)(L * W) + (int64_t)wave * L + g.nvalid == P.T) {
+        St st = s2;
+        if (g.nvalid == L) {
+            st = combine(s2, sw.st, dL);
+        } else {
+#pragma unroll 1
+            for (int j = 0; j < g.nvalid; ++j) {
+                const float e = key_weight(st, key_split(BufLd<TIn>::at(g.rk, g.vin, j * g.row_in)));
+                token_add(st, e, BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch);
+            }
+        }
+        if (cok) {
+            const int64_t i = b * P.C + c;
+            state_to_abp(st, P.a_out[i], P.b_out[i], P.p_out[i]);
+        }
+    }
+}
+
+// T == 0: the state after the (empty) sequence is the state before it.
+__global__ void state_passthrough_kernel(int64_t n, const float* a_in, const float* b_in, const float* p_in,
+                                         float* a_out, float* b_out, float* p_out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float a = 0.f, b = 0.f, p = -1e38f;
+    if (a_in != nullptr) {
+        a = a_in[i];
+        b = b_in[i];
+        p = p_in[i];
+    }
+    a_out[i] = a;
+    b_out[i] = b;
+    p_out[i] = p;
 }
 
 __global__ void fwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
@@ -395,6 +441,8 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     P.ckpt = static_cast<float*>(a.ckpt);
     P.nblk_ck = a.nblk;
     P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+    P.a_in = a.a_in; P.b_in = a.b_in; P.p_in = a.p_in;
+    P.a_out = a.a_out; P.b_out = a.b_out; P.p_out = a.p_out;
 
     if (l.nblocks > 1) {
         char* ws = static_cast<char*>(a.ws);
@@ -413,6 +461,14 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t grid = l.ntiles * l.nblocks;
     hipLaunchKernelGGL((fwd_chunk_kernel<TIn, kFwdL, kFwdW>), dim3(static_cast<unsigned>(grid)),
                        dim3(64 * kFwdW), 0, stream, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_passthrough(const FwdArgs& a, hipStream_t stream) {
+    const int64_t n = a.B * a.C;
+    if (n == 0 || a.a_out == nullptr) return hipSuccess;
+    hipLaunchKernelGGL(state_passthrough_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       n, a.a_in, a.b_in, a.p_in, a.a_out, a.b_out, a.p_out);
     return hipGetLastError();
 }
 

@@ -22,6 +22,14 @@ struct FwdArgs {
     int64_t nblk;   // ceil(T / kCkptLen)
     void* ws;
     size_t ws_bytes;
+    // optional state before token 1 and after token T, each [B, C] (a, b, p as
+    // wkv_step): all three pointers NULL or all set
+    const float* a_in = nullptr;
+    const float* b_in = nullptr;
+    const float* p_in = nullptr;
+    float* a_out = nullptr;
+    float* b_out = nullptr;
+    float* p_out = nullptr;
 };
 
 struct BwdArgs {
@@ -58,6 +66,8 @@ struct StepArgs {
 
 // chunked forward (wkv_fwd.hip)
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t stream);
+// T == 0 with a state: the output state is the input state (or the empty one)
+hipError_t launch_state_passthrough(const FwdArgs& a, hipStream_t stream);
 size_t fwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C);
 
 // chunked backward (wkv_bwd.hip)

@@ -33,6 +33,33 @@ __device__ __forceinline__ St combine(const St& X, const St& S, double D) {
     return St{ldx(xa, X.s - sn) + ldx(S.a, S.s - sn), ldx(xb, X.s - sn) + ldx(S.b, S.s - sn), sn};
 }
 
+// ---- the decode-step state (a, b, p), A = a e^p, B = b e^p ---------------------
+// Conversions to and from the lane state (a, b, s), A = a 2^s.  The integer
+// and fractional parts of p log2 e are split in float64, so the only
+// roundings are those of the float32 results.
+__device__ __forceinline__ St state_from_abp(float a, float b, float p) {
+    if (!(b > 0.f)) return empty_state();  // the empty state (b = 0), whatever p
+    const double q = static_cast<double>(p) * 1.4426950408889634;
+    const double n = floor(fmax(q, -1.0e9));
+    const double f = exp2(q - n);
+    return St{static_cast<float>(a * f), static_cast<float>(b * f), static_cast<int>(n)};
+}
+
+__device__ __forceinline__ void state_to_abp(const St& st, float& a, float& b, float& p) {
+    if (!(st.b > 0.f)) {
+        a = 0.f;
+        b = 0.f;
+        p = -1e38f;
+        return;
+    }
+    const double pd = static_cast<double>(st.s) * 0.6931471805599453;
+    const float pf = static_cast<float>(pd);
+    const double c = exp(pd - static_cast<double>(pf));  // fold the rounding of p into a, b
+    a = static_cast<float>(st.a * c);
+    b = static_cast<float>(st.b * c);
+    p = pf;
+}
+
 // Barrier for LDS traffic only: outstanding global loads (prefetches) and
 // stores stay in flight across it.
 __device__ __forceinline__ void lds_sync() {

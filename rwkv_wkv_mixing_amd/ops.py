@@ -62,8 +62,17 @@ def _workspace(op, B, T, C, dt, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None):
-    """y [B,T,C] float32 from w, u [C] float32 and k, v [B,T,C] (float32 or bfloat16)."""
+def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None, state_in=None, state_out=None,
+                return_state=False):
+    """y [B,T,C] float32 from w, u [C] float32 and k, v [B,T,C] (float32 or bfloat16).
+
+    state_in:  None (empty history) or (a, b, p), each [B, C] float32, in the
+               representation of wkv_step: the state before the first token.
+    state_out: None or (a, b, p) tensors to receive the state after the last
+               token (they may be the state_in tensors).  With
+               return_state=True and no state_out, they are allocated and the
+               call returns (y, (a, b, p)).
+    """
     _need(k, "k", (torch.float32, torch.bfloat16))
     dev = k.device
     B, T, C = k.shape
@@ -75,11 +84,20 @@ def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None):
     _need(y, "y", torch.float32, (B, T, C), dev)
     if ckpt is not None:
         _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    if state_out is None and return_state:
+        state_out = tuple(torch.empty((B, C), dtype=torch.float32, device=dev) for _ in range(3))
+    for name, st3 in (("state_in", state_in), ("state_out", state_out)):
+        if st3 is not None:
+            for t, n in zip(st3, "abp"):
+                _need(t, f"{name}.{n}", torch.float32, (B, C), dev)
+    sin = state_in if state_in is not None else (None, None, None)
+    sout = state_out if state_out is not None else (None, None, None)
     ws, ws_n = _workspace(L.WKV_OP_FORWARD, B, T, C, k.dtype, dev, workspace)
-    st = L.lib().wkv_forward(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y), _p(ckpt),
-                             _p(ws), ws_n, _stream(dev))
-    L.check("wkv_forward", st)
-    return y
+    st = L.lib().wkv_forward_state(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y),
+                                   *[_p(t) for t in sin], *[_p(t) for t in sout], _p(ckpt),
+                                   _p(ws), ws_n, _stream(dev))
+    L.check("wkv_forward_state", st)
+    return (y, state_out) if return_state else y
 
 
 def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None):

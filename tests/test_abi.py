@@ -101,6 +101,26 @@ def test_forward_validation(lib):
     assert fwd(lib, 3, 0, 4, L.WKV_F32, None, None, None, None, None) == L.WKV_OK
 
 
+def fwd_state(lib, B, T, C, dt, w, u, k, v, y, ain=None, bin_=None, pin=None, aout=None, bout=None, pout=None):
+    return lib.wkv_forward_state(B, T, C, dt, P(w), P(u), P(k), P(v), P(y), P(ain), P(bin_), P(pin), P(aout),
+                                 P(bout), P(pout), None, None, 0, None)
+
+
+def test_forward_state_validation(lib):
+    x = A16
+    base = (1, 4, 4, L.WKV_F32, x, x, x, x, x)
+    # the three state pointers of each side are all NULL or all set
+    assert fwd_state(lib, *base, ain=x) == L.WKV_EINVAL
+    assert fwd_state(lib, *base, ain=x, bin_=x) == L.WKV_EINVAL
+    assert fwd_state(lib, *base, bout=x) == L.WKV_EINVAL
+    assert fwd_state(lib, *base, ain=x, bin_=x, pin=x, aout=x, bout=x) == L.WKV_EINVAL
+    assert fwd_state(lib, *base, ain=x, bin_=x, pin=x + 2) == L.WKV_EALIGN
+    assert fwd_state(lib, *base, aout=x + 1, bout=x, pout=x) == L.WKV_EALIGN
+    assert fwd_state(lib, 1, 4, 4, 5, x, x, x, x, x, ain=x, bin_=x, pin=x) == L.WKV_EDTYPE
+    # no lanes: nothing to do, states included
+    assert fwd_state(lib, 0, 4, 4, L.WKV_F32, None, None, None, None, None, x, x, x, x, x, x) == L.WKV_OK
+
+
 def test_backward_validation(lib):
     x = A16
     ws_need = lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 1, 4, 4, L.WKV_F32)

@@ -21,6 +21,7 @@ from oracle import (
     wkv_forward_ref,
     wkv_state_from_sums,
     wkv_step_ref,
+    wkv_sums_from_state,
 )
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "wkv_exact_cases.json")
@@ -293,6 +294,24 @@ def test_resume_from_exported_state():
     for t in range(50, 90):
         y, a, b, p = wkv_step_ref(w, u, k[:, t], v[:, t], a, b, p)
         assert np.allclose(y, y_full[:, t], rtol=1e-12, atol=1e-13)
+
+
+def test_forward_from_initial_state_splits_the_sequence():
+    """A forward over the first T1 tokens, then a forward over the rest started
+    from its final state (passed through another (a, b, p) representation),
+    equals the forward over the whole sequence, outputs and final sums alike;
+    the empty state gives the plain forward."""
+    w, u, k, v, _ = rand_inputs(3, 70, 6, 43, k_std=2.0)
+    y_full, A_full, B_full = wkv_forward_ref(w, u, k, v, return_sums=True)
+    y1, A1, B1 = wkv_forward_ref(w, u, k[:, :25], v[:, :25], return_sums=True)
+    a, b, p = wkv_state_from_sums(A1, B1)
+    A0, B0 = wkv_sums_from_state(a * 3.0, b * 3.0, p - np.log(3.0))
+    y2, A2, B2 = wkv_forward_ref(w, u, k[:, 25:], v[:, 25:], return_sums=True, A0=A0, B0=B0)
+    assert np.allclose(np.concatenate([y1, y2], axis=1), y_full, rtol=1e-12, atol=1e-13)
+    assert np.allclose(A2, A_full, rtol=1e-11) and np.allclose(B2, B_full, rtol=1e-11)
+    Z0, Z1 = wkv_sums_from_state(np.zeros((3, 6)), np.zeros((3, 6)), np.full((3, 6), -1e38))
+    assert np.all(Z0 == 0) and np.all(Z1 == 0)
+    assert np.array_equal(wkv_forward_ref(w, u, k, v, A0=Z0, B0=Z1), wkv_forward_ref(w, u, k, v))
 
 
 def test_step_state_representation_invariance():
