@@ -17,7 +17,9 @@ Other workloads (not the headline, for measurements quoted in the design
 notes): fwd3 (the headline shape, forward only), fwd2 (B=8 T=1024 C=768 fp32,
 fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32, forward only), step5 (32 layers x
 256 streams x 4096 channels decode step), prefill (the headline shape's forward
-started from a state and returning it, as wkv_forward_state), copy (a plain
+started from a state and returning it, as wkv_forward_state), gated (the
+headline with the receptance gate fused: wkv_forward_gated +
+wkv_backward_gated), copy (a plain
 1 GiB device-to-device copy: the calibration kernel for the FETCH_SIZE /
 WRITE_SIZE counters).
 """
@@ -46,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -129,7 +131,7 @@ def stats_us(ms_list):
             "p90": float(np.percentile(a, 90))}
 
 
-def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state=False):
+def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state=False, gated=False):
     import torch
 
     from rwkv_wkv_mixing_amd import ops
@@ -149,6 +151,14 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state
                         torch.empty((B, T, C), dtype=torch.float32, device=dev),
                         torch.empty((C,), dtype=torch.float32, device=dev),
                         torch.empty((C,), dtype=torch.float32, device=dev))
+        if gated:  # receptance and the gradient of the gated output (in place of gy); dr
+            from rwkv_wkv_mixing_amd import workloads as W
+
+            r, rb = W.receptance(p)
+            s["r"] = torch.from_numpy(rb.view(np.int16)).view(torch.bfloat16).to(dev) if rb is not None else \
+                torch.from_numpy(r).to(dev)
+            s["gout"] = s["gy"]
+            s["out"] = s["out"] + (torch.empty((B, T, C), dtype=torch.float32, device=dev),)
         sets.append(s)
     ws_f = torch.empty(max(1, ops.workspace_bytes(0, B, T, C, base["k"].dtype)), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(max(1, ops.workspace_bytes(1, B, T, C, base["k"].dtype)), dtype=torch.uint8, device=dev)
@@ -158,15 +168,22 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state
         if ev is not None:
             ev[0].record()
         st = s.get("st")
-        ops.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=s["y"], ckpt=None if st else s["ck"], workspace=ws_f,
-                        state_in=st, state_out=st)
+        if gated:
+            ops.wkv_forward_gated(s["w"], s["u"], s["k"], s["v"], s["r"], out=s["y"], ckpt=s["ck"], workspace=ws_f)
+        else:
+            ops.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=s["y"], ckpt=None if st else s["ck"],
+                            workspace=ws_f, state_in=st, state_out=st)
         if ev is not None:
             ev[1].record()
-        if with_bwd:
-            ops.wkv_backward(s["w"], s["u"], s["k"], s["v"], s["gy"], ckpt=s["ck"], out=s["out"],
+        if with_bwd and gated:
+            dk, dv, dw, du, dr = s["out"]
+            ops.wkv_backward_gated(s["w"], s["u"], s["k"], s["v"], s["r"], s["gout"], ckpt=s["ck"],
+                                   out=(dk, dv, dr, dw, du), workspace=ws_b)
+        elif with_bwd:
+            ops.wkv_backward(s["w"], s["u"], s["k"], s["v"], s["gy"], ckpt=s["ck"], out=s["out"][:4],
                              workspace=ws_b)
-            if ev is not None:
-                ev[2].record()
+        if with_bwd and ev is not None:
+            ev[2].record()
 
     for i in range(args.warmup):
         step(i)
@@ -337,15 +354,33 @@ def main():
         p, with_bwd, bf, bb = W.config3(), True, 8, 14
     elif args.workload in ("fwd3", "prefill"):
         p, with_bwd, bf, bb = W.config3(), False, 8, 0
+    elif args.workload == "gated":  # + r in both calls, + dr out: 10 and 20 B per channel-token
+        p, with_bwd, bf, bb = W.config3(), True, 10, 20
     elif args.workload == "fwd2":
         p, with_bwd, bf, bb = W.config2(), True, 12, 20
     else:
         p, with_bwd, bf, bb = W.config4(), False, 12, 0
-    out = bench_seq(args, p, with_bwd, args.workload, bf, bb, with_state=args.workload == "prefill")
+    out = bench_seq(args, p, with_bwd, args.workload, bf, bb, with_state=args.workload == "prefill",
+                    gated=args.workload == "gated")
+    if args.workload == "gated":
+        out["metric"] = ("WKV fwd+bwd with the receptance gate fused (sigmoid(r) * wkv) channel·tokens/s, "
+                         "B=8 T=1024 C=4096 bf16")
+        out["config"]["workload"] += " gated"
     if args.workload == "prefill":
         out["metric"] = "WKV prefill (forward from a state, returning the state) channel·tokens/s, B=8 T=1024 C=4096 bf16"
         out["config"]["workload"] += " with state in/out"
-    if not args.no_cpu:
+    if not args.no_cpu and args.workload == "gated":
+        from oracle import wkv_gated_backward_ref, wkv_gated_forward_ref
+
+        r, _ = W.receptance(p)
+        t0 = time.perf_counter()
+        wkv_gated_forward_ref(p.w, p.u, p.k, p.v, r)
+        wkv_gated_backward_ref(p.w, p.u, p.k, p.v, r, p.gy)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": p.n / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole workload ({p.n} channel*tokens, gated fwd+bwd) through the "
+                                         f"float64 numpy oracle on one core, {t_np:.2f} s"}
+    elif not args.no_cpu:
         t_c, threads, t_np = cpu_oracle(p, with_bwd)
         what = "fwd+bwd" if with_bwd else "fwd"
         out["cpu_baseline"] = {"value": p.n / t_c, "unit": "channel·tokens/s", "cores": threads,

@@ -169,6 +169,35 @@ wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype,
                           void* hip_stream);
 
 /*
+ * wkv_forward_gated / wkv_backward_gated - the operator with the receptance
+ * gate of the time-mixing output fused in.
+ *
+ * Defines ("RWKV（Receptance Weighted Key Value）概念", section 3.2: the
+ * time-mixing output is sigmoid(receptance) times wkv, elementwise):
+ *     out_t = sigmoid(r_t) * y_t            (y_t as wkv_forward)
+ * and, for L = sum gout * out, the WKV gradients for gy = gout sigmoid(r)
+ * together with dr = gout * y * sigmoid(r) * (1 - sigmoid(r)).
+ *
+ * r, gout   [B, T, C] in_dtype (r is read by both calls).
+ * out       [B, T, C] float32, fully overwritten.
+ * dk, dv, dr [B, T, C] float32, fully overwritten; dw, du [C] as wkv_backward.
+ * ckpt      as wkv_forward / wkv_backward; the saved states do not depend on
+ *           r, so a ckpt of wkv_forward serves wkv_backward_gated and back.
+ * Other arguments, sizes and errors as wkv_forward / wkv_backward (the same
+ * workspace sizes).  Saves the round trip of y and gy through memory that a
+ * separate gate would cost.
+ */
+wkv_status_t wkv_forward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
+                               const float* w, const float* u, const void* k, const void* v, const void* r,
+                               float* out, void* ckpt, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
+
+wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
+                                const float* w, const float* u, const void* k, const void* v, const void* r,
+                                const void* gout, float* dk, float* dv, float* dr, float* dw, float* du,
+                                const void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * wkv_step - one recurrent-mode (decode) token for L x B independent states.
  *
  * Defines ("RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", section

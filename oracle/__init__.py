@@ -9,6 +9,8 @@ from .wkv_ref import (  # noqa: F401
     wkv_backward_ref,
     wkv_direct_ref,
     wkv_forward_ref,
+    wkv_gated_backward_ref,
+    wkv_gated_forward_ref,
     wkv_state_from_sums,
     wkv_step_ref,
     wkv_sums_from_state,

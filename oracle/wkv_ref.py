@@ -39,7 +39,7 @@ Parity status: every function here is pinned (no "parity unpinned" entries).
 from __future__ import annotations
 
 import numpy as np
-from scipy.special import softmax
+from scipy.special import expit, softmax
 
 __all__ = [
     "wkv_forward_ref",
@@ -87,6 +87,24 @@ def wkv_forward_ref(w, u, k, v, return_sums: bool = False, A0=None, B0=None):
     if return_sums:
         return y, A, Bs
     return y
+
+
+def wkv_gated_forward_ref(w, u, k, v, r):
+    """Time-mixing output with the receptance gate, [P4] section 3.2:
+    out_t = sigmoid(r_t) * wkv_t, elementwise per (b, t, c); r [B, T, C].
+    sigmoid is scipy's ``expit``."""
+    return expit(np.asarray(r, np.float64)) * wkv_forward_ref(w, u, k, v)
+
+
+def wkv_gated_backward_ref(w, u, k, v, r, gout):
+    """Gradients of L = sum(gout * out) through the gate: the WKV gradients of
+    wkv_backward_ref for gy = gout sigmoid(r), and dr = gout y sigmoid(r)
+    sigmoid(-r).  Returns (dk, dv, dr, dw, du)."""
+    r, gout = _f64(r, gout)
+    y = wkv_forward_ref(w, u, k, v)
+    dk, dv, dw, du = wkv_backward_ref(w, u, k, v, gout * expit(r))
+    dr = gout * y * expit(r) * expit(-r)
+    return dk, dv, dr, dw, du
 
 
 def wkv_direct_ref(w, u, k, v):

@@ -23,6 +23,8 @@ EXPORTS = (
     "wkv_forward",
     "wkv_forward_state",
     "wkv_backward",
+    "wkv_forward_gated",
+    "wkv_backward_gated",
     "wkv_step",
     "wkv_status_str",
     "wkv_last_hip_error",
@@ -68,6 +70,10 @@ def declare(L):
     L.wkv_forward_state.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_backward.restype = i32
     L.wkv_backward.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
+    L.wkv_forward_gated.restype = i32
+    L.wkv_forward_gated.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, vp, vp, sz, vp]
+    L.wkv_backward_gated.restype = i32
+    L.wkv_backward_gated.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_step.restype = i32
     L.wkv_step.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, vp]
     L.wkv_status_str.restype = ctypes.c_char_p

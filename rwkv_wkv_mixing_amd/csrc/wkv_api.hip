@@ -109,6 +109,24 @@ wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype, co
     return hip_status(wkv::launch_fwd_chunk(a, stream));
 }
 
+wkv_status_t wkv_forward_gated(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                               const float* u, const void* k, const void* v, const void* r, float* out,
+                               void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const Plan p = plan(WKV_OP_FORWARD, B, T, C, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (p.N == 0) return WKV_OK;
+    if (!w || !u || !k || !v || !r || !out) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(out, 4) || !aligned(k, es) || !aligned(v, es) ||
+        !aligned(r, es) || (ckpt && !aligned(ckpt, 4)))
+        return WKV_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
+        return WKV_EWORKSPACE;
+    wkv::FwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, out, ckpt, p.nblk, workspace, workspace_bytes};
+    a.r = r;
+    return hip_status(wkv::launch_fwd_chunk(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
                          const float* u, const void* k, const void* v, float* y, void* ckpt,
                          void* workspace, size_t workspace_bytes, void* hip_stream) {
@@ -140,6 +158,35 @@ wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const f
         return WKV_EWORKSPACE;
     wkv::BwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, gy, dk, dv, dw, du, ckpt, p.nblk,
                    workspace, workspace_bytes};
+    return hip_status(wkv::launch_bwd_chunk(a, stream));
+}
+
+wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                                const float* u, const void* k, const void* v, const void* r,
+                                const void* gout, float* dk, float* dv, float* dr, float* dw, float* du,
+                                const void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const Plan p = plan(WKV_OP_BACKWARD, B, T, C, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (C == 0) return WKV_OK;
+    if (!dw || !du) return WKV_EINVAL;
+    if (!aligned(dw, 4) || !aligned(du, 4)) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p.N == 0) {  // empty sums: dw = du = 0
+        hipLaunchKernelGGL(zero2_kernel, dim3(static_cast<unsigned>((C + 255) / 256)), dim3(256), 0,
+                           stream, C, dw, du);
+        return hip_status(hipGetLastError());
+    }
+    if (!w || !u || !k || !v || !r || !gout || !dk || !dv || !dr) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(dr, 4) ||
+        !aligned(k, es) || !aligned(v, es) || !aligned(r, es) || !aligned(gout, es) || (ckpt && !aligned(ckpt, 4)))
+        return WKV_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
+        return WKV_EWORKSPACE;
+    wkv::BwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, gout, dk, dv, dw, du, ckpt, p.nblk,
+                   workspace, workspace_bytes};
+    a.r = r;
+    a.dr = dr;
     return hip_status(wkv::launch_bwd_chunk(a, stream));
 }
 

@@ -59,6 +59,8 @@ struct BwdChunk {
     float* carry;          // [ntiles][nblocks][64][12]: G, J, G', J' as hi/lo pairs, scale, 3 status words
     uint32_t carry_bytes;
     float* part;           // [ntiles][nblocks][2][64]: dw, du partial sums
+    const void* r;         // receptance [B, T, C] (gated kernels; gy is then the gradient of sigmoid(r) y)
+    float* dr;             // [B, T, C] gradient of r (gated kernels)
 };
 
 // Reverse carry at log2-scale sg: the true G is G * 2^{-sg}.
@@ -152,15 +154,6 @@ __device__ __forceinline__ RCarry wait_carry(Rsrc r, uint32_t off, uint32_t* err
     __hip_atomic_store(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return RCarry{0.0, 0.0, 0.0, 0.0, 0};
 }
-
-template <typename TIn, int L>
-struct GyChunk {
-    float g[L];
-    __device__ __forceinline__ void load(Rsrc r, uint32_t voff, uint32_t row) {
-#pragma unroll
-        for (int j = 0; j < L; ++j) g[j] = BufLd<TIn>::at(r, voff, j * row);
-    }
-};
 
 template <typename TIn, int L>
 struct KvChunk;
@@ -277,7 +270,7 @@ struct Decay {
 // ---- one wave's span of L tokens ----------------------------------------------
 // Where a span's data lives for one lane.
 struct SpanGeo {
-    Rsrc rk, rv, rg, rdk, rdv;
+    Rsrc rk, rv, rg, rr, rdk, rdv, rdr;
     uint32_t vin, vout, row_in, row_out;
     const float* ck;  // saved state at the span start, or nullptr
 };
@@ -298,6 +291,8 @@ __device__ __forceinline__ SpanGeo span_geo(const BwdChunk& P, int64_t b, int64_
     g.rg = make_rsrc(static_cast<const TIn*>(P.gy) + row0, nin);
     g.rdk = make_rsrc(P.dk + row0, nout);
     g.rdv = make_rsrc(P.dv + row0, nout);
+    g.rr = P.r != nullptr ? make_rsrc(static_cast<const TIn*>(P.r) + row0, nin) : make_rsrc(nullptr, 0);
+    g.rdr = P.dr != nullptr ? make_rsrc(P.dr + row0, nout) : make_rsrc(nullptr, 0);
     const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;
     g.vin = cok ? lin * ES : kOffNone;
     g.vout = cok ? lin * 4 : kOffNone;
@@ -307,11 +302,12 @@ __device__ __forceinline__ SpanGeo span_geo(const BwdChunk& P, int64_t b, int64_
     return g;
 }
 
-// A span's inputs, loaded ahead of use.
-template <typename TIn, int L>
+// A span's inputs, loaded ahead of use (gy holds the output gradient; with
+// the gate, r too).
+template <typename TIn, int L, bool Gated>
 struct SpanIn {
     KvChunk<TIn, L> kv;
-    GyChunk<TIn, L> gy;
+    Chunk1<TIn, L> gy;
     float a0, b0, s0;
     __device__ __forceinline__ void load(const SpanGeo& g, int64_t C) {
         kv.load(g.rk, g.rv, g.vin, g.row_in);
@@ -329,8 +325,9 @@ struct SpanIn {
 
 // Forward recompute of a span, its reverse map, and (fast path) the per-token
 // products of the reverse sweep: gpi = gy pi, gvy = gy pi vy, gr = gy rho,
-// grpd = gy rho pd, e, vm, ld.
-template <typename TIn, int L>
+// grpd = gy rho pd, e, vm, ld.  Gated: gy = gout sigmoid(r) and the recompute
+// also writes dr = gout y sigmoid(r) (1 - sigmoid(r)), y = m + pi (v - m).
+template <typename TIn, int L, bool Gated>
 struct Span {
     float gpi[L], gvy[L], gr[L], grpd[L], e[L], vm[L], ld[L];
     acc_t Psum, Gs, Js, Gps, Jps;
@@ -339,8 +336,11 @@ struct Span {
     bool fast;  // wave-uniform
     MSt x0;
 
-    __device__ __forceinline__ void recompute(const SpanIn<TIn, L>& in, const SpanGeo& g, const Chan& ch, float eu,
-                                              const Decay& dec, bool fast_out) {
+    // rg: the gate's inputs of the span (used when Gated; not part of SpanIn so
+    // that the whole-tile kernel does not double-buffer them)
+    __device__ __forceinline__ void recompute(const SpanIn<TIn, L, Gated>& in, const Chunk1<TIn, L>& rg,
+                                              const SpanGeo& g, const Chan& ch, float eu, const Decay& dec,
+                                              bool fast_out) {
         x0.s = static_cast<int>(in.s0);
         x0.b = in.b0;
         x0.m = in.b0 > 0.f ? in.a0 / in.b0 : 0.f;
@@ -382,7 +382,12 @@ struct Span {
                 dmin = fminf(dmin, bb);  // B_t, the denominator of lam
                 const float rb = rcp(bb);
                 const float ldj = (ej * rb) * dl;
-                const float gj = in.gy.g[j];
+                float gj = in.gy.at(j);
+                if (Gated) {
+                    const Gate gt = gate_of(rg.at(j));
+                    buf_store(gj * fmaf(pi, dl, m) * gt.s * gt.om, g.rdr, g.vout, j * g.row_out);
+                    gj *= gt.s;
+                }
                 const float gpij = gj * pi;
                 const float grj = gj * r;
                 gpi[j] = gpij;
@@ -415,13 +420,19 @@ struct Span {
 #pragma unroll 1
             for (int j = 0; j < L; ++j) {
                 const int s_before = st.s;
+                const float m_before = st.m;
                 const TokQ q = mean_step(st, BufLd<TIn>::at(g.rk, g.vin, j * g.row_in),
                                          BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch, eu, fast_out);
                 if (j == 0)
                     so = st.s;
                 else if (st.s != s_before)
                     dpd = ldexp(dpd, s_before - st.s);
-                const float gj = BufLd<TIn>::at(g.rg, g.vin, j * g.row_in);
+                float gj = BufLd<TIn>::at(g.rg, g.vin, j * g.row_in);
+                if (Gated) {
+                    const Gate gt = gate_of(BufLd<TIn>::at(g.rr, g.vin, j * g.row_in));
+                    buf_store(gj * (m_before + q.pd) * gt.s * gt.om, g.rdr, g.vout, j * g.row_out);
+                    gj *= gt.s;
+                }
                 const double grj = static_cast<double>(gj * q.rho);
                 const double qq = dpd * grj;
                 const double t1 = qq * (static_cast<double>(Psum) + static_cast<double>(q.pd));
@@ -472,7 +483,8 @@ struct Span {
                                     BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch, eu, fast_out);
                 const TokQ q = mean_step(st, BufLd<TIn>::at(g.rk, g.vin, t * g.row_in),
                                          BufLd<TIn>::at(g.rv, g.vin, t * g.row_in), ch, eu, fast_out);
-                const float gt = BufLd<TIn>::at(g.rg, g.vin, t * g.row_in);
+                float gt = BufLd<TIn>::at(g.rg, g.vin, t * g.row_in);
+                if (Gated) gt *= gate_of(BufLd<TIn>::at(g.rr, g.vin, t * g.row_in)).s;
                 const int ds = st.s - sg;  // bring the carry to this token's scale
                 G = ldexp(G, ds);
                 J = ldexp(J, ds);
@@ -507,8 +519,8 @@ struct BwdShared {
     uint32_t ticket;
 };
 
-template <int W, typename TIn, int L>
-__device__ __forceinline__ void put_map(BwdShared<W>& sm, int wave, int lane, const Span<TIn, L>& sp) {
+template <int W, typename TIn, int L, bool Gated>
+__device__ __forceinline__ void put_map(BwdShared<W>& sm, int wave, int lane, const Span<TIn, L, Gated>& sp) {
     sm.mapn[wave][lane] = static_cast<float>(L);
     sm.maps[wave][lane] = sp.so;
     sm.mapd[wave][0][lane] = static_cast<double>(sp.Psum);
@@ -554,7 +566,7 @@ __device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P
 
 // Time-split backward: one workgroup per (tile, time block); blocks are
 // chained backward in time through the coherent carry slots.
-template <typename TIn, int L, int W>
+template <typename TIn, int L, int W, bool Gated>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk P) {
     __shared__ BwdShared<W> sm;
     const int lane = threadIdx.x & 63;
@@ -581,10 +593,12 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     const double dL = ipow<L>(ch.dd);
 
     const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
-    SpanIn<TIn, L> in;
+    SpanIn<TIn, L, Gated> in;
     in.load(g, P.C);
-    Span<TIn, L> sp;
-    sp.recompute(in, g, ch, eu, dec, fast_out);
+    Chunk1<TIn, L> rg;
+    if (Gated) rg.load(g.rr, g.vin, g.row_in);
+    Span<TIn, L, Gated> sp;
+    sp.recompute(in, rg, g, ch, eu, dec, fast_out);
     put_map(sm, wave, lane, sp);
     lds_sync();
 
@@ -615,7 +629,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
 // the last to the first, keeping the carry in LDS (no cross-workgroup
 // exchange) and loading the next block's inputs while it computes the current
 // one.  Used when there are enough tiles to fill the GPU.
-template <typename TIn, int L, int W>
+template <typename TIn, int L, int W, bool Gated>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
     __shared__ BwdShared<W> sm;
     const int lane = threadIdx.x & 63;
@@ -634,13 +648,15 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
 
     RCarry cin{0.0, 0.0, 0.0, 0.0, 0};  // carry at the current block's end (same in every wave)
     float ndw = 0.f, du = 0.f;
-    SpanIn<TIn, L> cur, nxt;
+    SpanIn<TIn, L, Gated> cur, nxt;
     cur.load(span_geo<TIn, L, W>(P, b, c, cok, P.nblocks - 1, wave), P.C);
     for (int64_t blk = P.nblocks - 1; blk >= 0; --blk) {
         const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
         if (blk > 0) nxt.load(span_geo<TIn, L, W>(P, b, c, cok, blk - 1, wave), P.C);
-        Span<TIn, L> sp;
-        sp.recompute(cur, g, ch, eu, dec, fast_out);
+        Chunk1<TIn, L> rg;
+        if (Gated) rg.load(g.rr, g.vin, g.row_in);
+        Span<TIn, L, Gated> sp;
+        sp.recompute(cur, rg, g, ch, eu, dec, fast_out);
         du += sp.du;
         put_map(sm, wave, lane, sp);
         lds_sync();
@@ -751,6 +767,8 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     P.nblk_ck = l.nblk_ck;
     P.nct = l.nct; P.ntiles = l.ntiles;
     P.part = reinterpret_cast<float*>(ws + l.off_part);
+    P.r = a.r;
+    P.dr = a.dr;
 
     // Enough tiles to give every CU two workgroups: one workgroup per tile
     // walks the whole sequence (no carries between workgroups).
@@ -760,8 +778,12 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (l.ntiles >= 2 * static_cast<int64_t>(ncu)) {
         P.nblocks = (a.T + kBwdL * kBwdTileW - 1) / (kBwdL * kBwdTileW);
-        hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW>), dim3(static_cast<unsigned>(l.ntiles)),
-                           dim3(64 * kBwdTileW), 0, stream, P);
+        if (P.r != nullptr)
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true>), dim3(static_cast<unsigned>(l.ntiles)),
+                               dim3(64 * kBwdTileW), 0, stream, P);
+        else
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false>),
+                               dim3(static_cast<unsigned>(l.ntiles)), dim3(64 * kBwdTileW), 0, stream, P);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,
@@ -783,8 +805,12 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW>), dim3(static_cast<unsigned>(l.ntiles * l.nblocks)),
-                       dim3(64 * kBwdW), 0, stream, P);
+    if (P.r != nullptr)
+        hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW, true>),
+                           dim3(static_cast<unsigned>(l.ntiles * l.nblocks)), dim3(64 * kBwdW), 0, stream, P);
+    else
+        hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW, false>),
+                           dim3(static_cast<unsigned>(l.ntiles * l.nblocks)), dim3(64 * kBwdW), 0, stream, P);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,

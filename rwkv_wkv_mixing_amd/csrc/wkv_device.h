@@ -95,6 +95,50 @@ __device__ __forceinline__ void buf_store(float v, Rsrc r, uint32_t voff, uint32
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
 }
 
+// One input over L tokens of a lane (token j at soffset j * row), held in
+// registers: bf16 values two to a register, float32 values one each.
+template <typename TIn, int L>
+struct Chunk1;
+
+template <int L>
+struct Chunk1<uint16_t, L> {
+    uint32_t pk[(L + 1) / 2];
+    __device__ __forceinline__ void load(Rsrc r, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; j += 2) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff, j * row, 0);
+            const uint32_t hi = j + 1 < L ? __builtin_amdgcn_raw_buffer_load_b16(r, voff, (j + 1) * row, 0) : 0u;
+            pk[j / 2] = lo | (hi << 16);
+        }
+    }
+    __device__ __forceinline__ float at(int j) const {
+        return (j & 1) ? __uint_as_float(pk[j / 2] & 0xffff0000u) : __uint_as_float(pk[j / 2] << 16);
+    }
+};
+
+template <int L>
+struct Chunk1<float, L> {
+    float x[L];
+    __device__ __forceinline__ void load(Rsrc r, uint32_t voff, uint32_t row) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) x[j] = BufLd<float>::at(r, voff, j * row);
+    }
+    __device__ __forceinline__ float at(int j) const { return x[j]; }
+};
+
+// Receptance gate ("RWKV（Receptance Weighted Key Value）概念", section 3.2:
+// out = sigmoid(r) wkv).  t = e^{-r}; sigmoid(r) = 1/(1+t) and
+// 1 - sigmoid(r) = t/(1+t), formed without cancellation on either side.
+struct Gate {
+    float s, om;  // sigmoid(r), 1 - sigmoid(r)
+};
+
+__device__ __forceinline__ Gate gate_of(float r) {
+    const float t = ex2(-r * kL2E);
+    const float s = rcp(1.f + t);
+    return Gate{s, t > 1.f ? 1.f - s : t * s};
+}
+
 // ---- per-channel constants -------------------------------------------------
 struct Chan {
     double dd;       // e^{-w}

@@ -50,6 +50,7 @@ struct FwdChunk {
     uint32_t* error;   // set if a carry wait timed out
     float* carry;      // [ntiles][nblocks][64][4] inclusive block states + status
     uint32_t carry_bytes;
+    const void* r;      // receptance [B, T, C] (gated kernels only)
     const float* a_in;  // optional state before token 1, [B, C] each
     const float* b_in;
     const float* p_in;
@@ -108,10 +109,10 @@ struct SubChunk<float, L> {
 // recurrence with per-token rescales, and the state before every kCkptLen-th
 // token into ckpt (when given).  Rare; reads one token at a time so that it
 // adds no registers to the kernel.
-template <bool Fast, typename TIn, int L>
-__device__ __forceinline__ void general_outputs(St st, Rsrc rk, Rsrc rv, uint32_t vin, uint32_t row_in, int nvalid,
-                                                const Chan& ch, float eu, Rsrc ry, uint32_t vout, uint32_t row_out,
-                                                float* ckp, int64_t ckstride) {
+template <bool Fast, bool Gated, typename TIn, int L>
+__device__ __forceinline__ void general_outputs(St st, Rsrc rk, Rsrc rv, Rsrc rr, uint32_t vin, uint32_t row_in,
+                                                int nvalid, const Chan& ch, float eu, Rsrc ry, uint32_t vout,
+                                                uint32_t row_out, float* ckp, int64_t ckstride) {
 #pragma unroll 1
     for (int j = 0; j < L; ++j) {
         if ((j % kCkptLen) == 0 && j < nvalid && ckp != nullptr) {
@@ -123,7 +124,8 @@ __device__ __forceinline__ void general_outputs(St st, Rsrc rk, Rsrc rv, uint32_
         const Key kk = key_split(BufLd<TIn>::at(rk, vin, j * row_in));
         const float vj = BufLd<TIn>::at(rv, vin, j * row_in);
         const float e = key_weight(st, kk);
-        const float yj = Fast ? token_out_fast(st, e, vj, eu) : token_out(st, key_log2(st, kk), vj, ch).y;
+        float yj = Fast ? token_out_fast(st, e, vj, eu) : token_out(st, key_log2(st, kk), vj, ch).y;
+        if (Gated) yj *= gate_of(BufLd<TIn>::at(rr, vin, j * row_in)).s;
         token_add(st, e, vj, ch);
         buf_store(yj, ry, vout, j * row_out);
     }
@@ -156,11 +158,12 @@ __device__ __forceinline__ St local_pass(const SubChunk<TIn, L>& sc, int sl, con
     return St{a, b, sl};
 }
 
-// Outputs from the local terms and the carry-in X brought to the local scale;
-// returns the smallest denominator used.
-template <int L>
+// Outputs from the local terms and the carry-in X brought to the local scale
+// (times sigmoid(r) when gated); returns the smallest denominator used.
+template <bool Gated, typename TIn, int L>
 __device__ __forceinline__ float corrected_outputs(const St& X, int sl, const float (&N)[L], const float (&D)[L],
-                                                   const Chan& ch, Rsrc ry, uint32_t vout, uint32_t row_out) {
+                                                   const Chunk1<TIn, L>& rch, const Chan& ch, Rsrc ry,
+                                                   uint32_t vout, uint32_t row_out) {
     const float cA = ldx(X.a, X.s - sl), cB = ldx(X.b, X.s - sl);
     float dp = 1.f;  // d^j
     float dmin = INFINITY;
@@ -168,7 +171,9 @@ __device__ __forceinline__ float corrected_outputs(const St& X, int sl, const fl
     for (int j = 0; j < L; ++j) {
         const float den = fmaf(dp, cB, D[j]);
         dmin = fminf(dmin, den);
-        buf_store(fmaf(dp, cA, N[j]) * rcp(den), ry, vout, j * row_out);
+        float yj = fmaf(dp, cA, N[j]) * rcp(den);
+        if (Gated) yj *= gate_of(rch.at(j)).s;
+        buf_store(yj, ry, vout, j * row_out);
         dp = fmaf(ch.dhi, dp, ch.dlo * dp);
     }
     return dmin;
@@ -178,7 +183,7 @@ __device__ __forceinline__ float corrected_outputs(const St& X, int sl, const fl
 // k = v = 0 (they follow every real token of the wave, so they change no real
 // output) and their stores are dropped.
 struct FwdGeo {
-    Rsrc rk, rv, ry;
+    Rsrc rk, rv, rr, ry;
     uint32_t vin, vout, row_in, row_out;
     int nvalid;  // real tokens in the sub-chunk
     float* ckp;  // saved states of the sub-chunk, or nullptr
@@ -196,6 +201,8 @@ __device__ __forceinline__ FwdGeo fwd_geo(const FwdChunk& P, int64_t b, int64_t 
     g.nvalid = rem <= 0 ? 0 : (rem >= L ? L : static_cast<int>(rem));
     g.rk = make_rsrc(static_cast<const TIn*>(P.k) + row0, (uint32_t)(blk_tokens * P.C * ES));
     g.rv = make_rsrc(static_cast<const TIn*>(P.v) + row0, (uint32_t)(blk_tokens * P.C * ES));
+    g.rr = P.r != nullptr ? make_rsrc(static_cast<const TIn*>(P.r) + row0, (uint32_t)(blk_tokens * P.C * ES))
+                          : make_rsrc(nullptr, 0);
     // y == nullptr (the backward's state-only run): a zero-size buffer drops every store
     g.ry = P.y != nullptr ? make_rsrc(P.y + row0, (uint32_t)(blk_tokens * P.C * 4)) : make_rsrc(nullptr, 0);
     const uint32_t lin = cok ? (uint32_t)((int64_t)wave * L * P.C + c) : kOffNone;  // element offset
@@ -244,12 +251,14 @@ struct SubWork {
 
     // Outputs (and saved states) from the carry-in X: the fixed-scale
     // correction, or the general second recurrence when the wave needs it.
-    __device__ __forceinline__ void outputs(const St& X, const FwdGeo& g, const Chan& ch, float eu, bool fast,
-                                            bool want_y, int64_t C) const {
+    template <bool Gated>
+    __device__ __forceinline__ void outputs(const St& X, const FwdGeo& g, const Chunk1<TIn, L>& rch, const Chan& ch,
+                                            float eu, bool fast, bool want_y, int64_t C) const {
         const bool carry_fits = !(X.b > 0.f) | ((X.s - sl + __builtin_amdgcn_frexp_expf(X.b) <= kCarryAbove) &
                                                 (X.s - sl + __builtin_amdgcn_frexp_expf(X.a) <= kCarryAbove + 20));
         bool fast_out = fast_local && __all(carry_fits);
-        if (fast_out && want_y) fast_out = __all(corrected_outputs(X, sl, N, D, ch, g.ry, g.vout, g.row_out) >= kTiny);
+        if (fast_out && want_y)
+            fast_out = __all(corrected_outputs<Gated>(X, sl, N, D, rch, ch, g.ry, g.vout, g.row_out) >= kTiny);
         if (fast_out) {
             if (g.ckp != nullptr) {
                 const double dck = ipow<kCkptLen>(ch.dd);
@@ -267,11 +276,11 @@ struct SubWork {
                 }
             }
         } else if (fast) {  // general path: rewrites every output of the wave
-            general_outputs<true, TIn, L>(X, g.rk, g.rv, g.vin, g.row_in, g.nvalid, ch, eu, g.ry, g.vout, g.row_out,
-                                          g.ckp, C);
+            general_outputs<true, Gated, TIn, L>(X, g.rk, g.rv, g.rr, g.vin, g.row_in, g.nvalid, ch, eu, g.ry,
+                                                 g.vout, g.row_out, g.ckp, C);
         } else {
-            general_outputs<false, TIn, L>(X, g.rk, g.rv, g.vin, g.row_in, g.nvalid, ch, eu, g.ry, g.vout, g.row_out,
-                                           g.ckp, C);
+            general_outputs<false, Gated, TIn, L>(X, g.rk, g.rv, g.rr, g.vin, g.row_in, g.nvalid, ch, eu, g.ry,
+                                                  g.vout, g.row_out, g.ckp, C);
         }
     }
 };
@@ -295,8 +304,12 @@ __device__ __forceinline__ St wave_prefix(const FwdShared<W>& sm, int wave, int 
 
 // Time-split forward: one workgroup per (tile, time block); blocks are
 // chained in time through the coherent carry slots.
-template <typename TIn, int L, int W>
-__global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
+#ifndef WKV_FWD_OCC
+#define WKV_FWD_OCC 1  // minimum waves per SIMD asked of the register allocator (ungated kernel)
+#endif
+
+template <typename TIn, int L, int W, bool Gated>
+__global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_kernel(FwdChunk P) {
     __shared__ FwdShared<W> sm;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -319,11 +332,24 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     const float eu = ex2(ch.u2);
     const double dL = ipow<L>(ch.dd);
 
+    // a given state before token 1 is block 0's carry-in: converted here, while
+    // few registers are live, and parked in the LDS words the carry uses
+    const bool state_in = blk == 0 && wave == W - 1 && P.a_in != nullptr;
+    if (state_in) {
+        const int64_t i = b * P.C + (cok ? c : 0);
+        const St E0 = cok ? state_from_abp(P.a_in[i], P.b_in[i], P.p_in[i]) : empty_state();
+        sm.ea[lane] = E0.a;
+        sm.eb[lane] = E0.b;
+        sm.es[lane] = E0.s;
+    }
+
     const FwdGeo g = fwd_geo<TIn, L, W>(P, b, c, cok, blk, wave);
     SubChunk<TIn, L> sc;
     sc.load(g.rk, g.rv, g.vin, g.row_in);
     SubWork<TIn, L> sw;
     sw.local(sc, g, ch, eu, wc, uc);
+    Chunk1<TIn, L> rch;  // the gate's inputs, loaded once the key/value registers are free
+    if (Gated) rch.load(g.rr, g.vin, g.row_in);
     sm.a[wave][lane] = sw.st.a;
     sm.b[wave][lane] = sw.st.b;
     sm.s[wave][lane] = sw.st.s;
@@ -334,10 +360,7 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     const St pref = wave_prefix(sm, wave, lane, dL);
     if (wave == W - 1) {
         St E = empty_state();
-        if (blk == 0 && P.a_in != nullptr && cok) {
-            const int64_t i = b * P.C + c;
-            E = state_from_abp(P.a_in[i], P.b_in[i], P.p_in[i]);
-        }
+        if (state_in) E = St{sm.ea[lane], sm.eb[lane], sm.es[lane]};  // written by this wave above
         if (P.nblocks > 1) {
             double dTB = 1.0;
 #pragma unroll
@@ -356,7 +379,7 @@ __global__ void __launch_bounds__(64 * W) fwd_chunk_kernel(FwdChunk P) {
     double dpow = 1.0;
     for (int i = 0; i < wave; ++i) dpow *= dL;
     const St s2 = combine(St{sm.ea[lane], sm.eb[lane], sm.es[lane]}, pref, dpow);
-    sw.outputs(s2, g, ch, eu, fast, P.y != nullptr, P.C);
+    sw.template outputs<Gated>(s2, g, rch, ch, eu, fast, P.y != nullptr, P.C);
 
     // the state after token T, from the wave that holds it: its carry-in
     // combined with its summary when the sub-chunk is full, else a re-run of
@@ -441,6 +464,7 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     P.ckpt = static_cast<float*>(a.ckpt);
     P.nblk_ck = a.nblk;
     P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+    P.r = a.r;
     P.a_in = a.a_in; P.b_in = a.b_in; P.p_in = a.p_in;
     P.a_out = a.a_out; P.b_out = a.b_out; P.p_out = a.p_out;
 
@@ -459,8 +483,12 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int64_t grid = l.ntiles * l.nblocks;
-    hipLaunchKernelGGL((fwd_chunk_kernel<TIn, kFwdL, kFwdW>), dim3(static_cast<unsigned>(grid)),
-                       dim3(64 * kFwdW), 0, stream, P);
+    if (P.r != nullptr)
+        hipLaunchKernelGGL((fwd_chunk_kernel<TIn, kFwdL, kFwdW, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * kFwdW), 0, stream, P);
+    else
+        hipLaunchKernelGGL((fwd_chunk_kernel<TIn, kFwdL, kFwdW, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * kFwdW), 0, stream, P);
     return hipGetLastError();
 }
 

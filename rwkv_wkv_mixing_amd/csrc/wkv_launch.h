@@ -22,6 +22,8 @@ struct FwdArgs {
     int64_t nblk;   // ceil(T / kCkptLen)
     void* ws;
     size_t ws_bytes;
+    // optional receptance [B, T, C] (in dtype): y becomes sigmoid(r) y
+    const void* r = nullptr;
     // optional state before token 1 and after token T, each [B, C] (a, b, p as
     // wkv_step): all three pointers NULL or all set
     const float* a_in = nullptr;
@@ -48,6 +50,10 @@ struct BwdArgs {
     int64_t nblk;
     void* ws;
     size_t ws_bytes;
+    // optional receptance [B, T, C] (in dtype): gy is then the gradient of
+    // sigmoid(r) y, and dr [B, T, C] float32 receives the gradient of r
+    const void* r = nullptr;
+    float* dr = nullptr;
 };
 
 struct StepArgs {

@@ -35,14 +35,15 @@ __device__ __forceinline__ St combine(const St& X, const St& S, double D) {
 
 // ---- the decode-step state (a, b, p), A = a e^p, B = b e^p ---------------------
 // Conversions to and from the lane state (a, b, s), A = a 2^s.  The integer
-// and fractional parts of p log2 e are split in float64, so the only
-// roundings are those of the float32 results.
+// and fractional parts of p log2 e are split in float64; the factor 2^frac is
+// one float32 exp2 applied to a and b alike, so a/b is unchanged and B carries
+// one float32 rounding.
 __device__ __forceinline__ St state_from_abp(float a, float b, float p) {
     if (!(b > 0.f)) return empty_state();  // the empty state (b = 0), whatever p
     const double q = static_cast<double>(p) * 1.4426950408889634;
     const double n = floor(fmax(q, -1.0e9));
-    const double f = exp2(q - n);
-    return St{static_cast<float>(a * f), static_cast<float>(b * f), static_cast<int>(n)};
+    const float f = ex2(static_cast<float>(q - n));
+    return St{a * f, b * f, static_cast<int>(n)};
 }
 
 __device__ __forceinline__ void state_to_abp(const St& st, float& a, float& b, float& p) {
@@ -54,9 +55,10 @@ __device__ __forceinline__ void state_to_abp(const St& st, float& a, float& b, f
     }
     const double pd = static_cast<double>(st.s) * 0.6931471805599453;
     const float pf = static_cast<float>(pd);
-    const double c = exp(pd - static_cast<double>(pf));  // fold the rounding of p into a, b
-    a = static_cast<float>(st.a * c);
-    b = static_cast<float>(st.b * c);
+    // fold the rounding of p into a, b: e^{pd - pf} = 2^{(pd - pf) log2 e}
+    const float c = ex2(static_cast<float>((pd - static_cast<double>(pf)) * 1.4426950408889634));
+    a = st.a * c;
+    b = st.b * c;
     p = pf;
 }
 

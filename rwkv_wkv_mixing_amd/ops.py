@@ -100,6 +100,52 @@ def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None, state_in=None,
     return (y, state_out) if return_state else y
 
 
+def wkv_forward_gated(w, u, k, v, r, *, out=None, ckpt=None, workspace=None):
+    """out = sigmoid(r) * wkv(w, u, k, v), [B,T,C] float32; r has the dtype of k."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    B, T, C = k.shape
+    for t, n in ((v, "v"), (r, "r")):
+        _need(t, n, k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, T, C), dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    ws, ws_n = _workspace(L.WKV_OP_FORWARD, B, T, C, k.dtype, dev, workspace)
+    st = L.lib().wkv_forward_gated(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(r), _p(out), _p(ckpt),
+                                   _p(ws), ws_n, _stream(dev))
+    L.check("wkv_forward_gated", st)
+    return out
+
+
+def wkv_backward_gated(w, u, k, v, r, gout, *, ckpt=None, out=None, workspace=None):
+    """(dk, dv, dr, dw, du) for L = sum(gout * sigmoid(r) * wkv).  r, gout have the dtype of k."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    B, T, C = k.shape
+    for t, n in ((v, "v"), (r, "r"), (gout, "gout")):
+        _need(t, n, k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    if out is None:
+        out = tuple(torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(3)) + \
+            tuple(torch.empty((C,), dtype=torch.float32, device=dev) for _ in range(2))
+    dk, dv, dr, dw, du = out
+    for t, n, s_ in ((dk, "dk", (B, T, C)), (dv, "dv", (B, T, C)), (dr, "dr", (B, T, C)), (dw, "dw", (C,)),
+                     (du, "du", (C,))):
+        _need(t, n, torch.float32, s_, dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    ws, ws_n = _workspace(L.WKV_OP_BACKWARD, B, T, C, k.dtype, dev, workspace)
+    st = L.lib().wkv_backward_gated(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(r), _p(gout), _p(dk),
+                                    _p(dv), _p(dr), _p(dw), _p(du), _p(ckpt), _p(ws), ws_n, _stream(dev))
+    L.check("wkv_backward_gated", st)
+    return dk, dv, dr, dw, du
+
+
 def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None):
     """(dk, dv, dw, du) for L = sum(gy * y).  gy has the dtype of k."""
     _need(k, "k", (torch.float32, torch.bfloat16))

@@ -68,6 +68,7 @@ class WkvProblem:
     v_bits: np.ndarray | None = None
     gy_bits: np.ndarray | None = None
     note: str = ""
+    seed: int = 0
 
     @property
     def n(self) -> int:
@@ -116,7 +117,7 @@ def make_problem(B, T, C, *, dtype=F32, seed=0, w_range=(-6.0, 1.5), u_std=1.0,
         mag = rng.uniform(spike_range[0], spike_range[1], n).astype(np.float32)
         k[mask] = sign * mag
     gy = _normal(rng, 1.0, (B, T, C)) if with_gy else None
-    return _finish(WkvProblem(name, B, T, C, dtype, w, u, k, v, gy, note=note))
+    return _finish(WkvProblem(name, B, T, C, dtype, w, u, k, v, gy, note=note, seed=seed))
 
 
 # --- the five workloads -----------------------------------------------------
@@ -131,6 +132,18 @@ def config2(seed=0) -> WkvProblem:
     """169M-model shape: B=8, T=1024, C=768, fp32; w = exp(U(-6,1.5)), u, k, v, gy ~ N(0,1)."""
     return make_problem(8, 1024, 768, dtype=F32, seed=seed, w_range=(-6.0, 1.5),
                         name="wkv4 fp32 B=8 T=1024 C=768")
+
+
+def receptance(p: WkvProblem, std: float = 2.0):
+    """Receptance r [B, T, C] for the gated operator: N(0, std) from its own
+    stream (seed, 2), so the other inputs of ``p`` are unchanged; rounded like
+    the problem's inputs.  Returns (r as float32 values, bf16 bits or None)."""
+    rng = np.random.default_rng([p.seed, 2])
+    r = _normal(rng, std, (p.B, p.T, p.C))
+    if p.dtype == BF16:
+        bits, r = bf16_round(r)
+        return r, bits
+    return r, None
 
 
 def config3(seed=0) -> WkvProblem:

@@ -19,6 +19,8 @@ from oracle import (
     wkv_backward_ref,
     wkv_direct_ref,
     wkv_forward_ref,
+    wkv_gated_backward_ref,
+    wkv_gated_forward_ref,
     wkv_state_from_sums,
     wkv_step_ref,
     wkv_sums_from_state,
@@ -312,6 +314,57 @@ def test_forward_from_initial_state_splits_the_sequence():
     Z0, Z1 = wkv_sums_from_state(np.zeros((3, 6)), np.zeros((3, 6)), np.full((3, 6), -1e38))
     assert np.all(Z0 == 0) and np.all(Z1 == 0)
     assert np.array_equal(wkv_forward_ref(w, u, k, v, A0=Z0, B0=Z1), wkv_forward_ref(w, u, k, v))
+
+
+def test_gate_limits_and_half():
+    """sigmoid(r) -> 1 gives the plain output, -> 0 gives zero, r = 0 halves it."""
+    w, u, k, v, _ = rand_inputs(2, 20, 4, 44)
+    y = wkv_forward_ref(w, u, k, v)
+    assert np.allclose(wkv_gated_forward_ref(w, u, k, v, np.full(k.shape, 60.0)), y, rtol=1e-15, atol=0)
+    assert np.all(np.abs(wkv_gated_forward_ref(w, u, k, v, np.full(k.shape, -800.0))) == 0.0)
+    assert np.allclose(wkv_gated_forward_ref(w, u, k, v, np.zeros(k.shape)), 0.5 * y, rtol=1e-15, atol=0)
+
+
+def test_gated_backward_matches_central_differences():
+    w, u, k, v, gy = rand_inputs(1, 12, 3, 45)
+    r = np.random.default_rng(46).normal(0, 2, k.shape)
+    dk, dv, dr, dw, du = wkv_gated_backward_ref(w, u, k, v, r, gy)
+    loss = lambda w_, u_, k_, v_, r_: float(np.sum(gy * wkv_gated_forward_ref(w_, u_, k_, v_, r_)))
+    h = 1e-6
+    for name, arr, grad in (("r", r, dr), ("k", k, dk), ("v", v, dv), ("w", w, dw), ("u", u, du)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args = {"w": w, "u": u, "k": k, "v": v, "r": r}
+            p_, m_ = arr.copy(), arr.copy()
+            p_[idx] += h
+            m_[idx] -= h
+            args[name] = p_
+            lp = loss(args["w"], args["u"], args["k"], args["v"], args["r"])
+            args[name] = m_
+            lm = loss(args["w"], args["u"], args["k"], args["v"], args["r"])
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+def test_gated_backward_matches_autograd_of_direct_definition():
+    """torch float64 autograd (CPU) of sigmoid(r) times the section-3.2 softmax sum."""
+    w, u, k, v, gy = rand_inputs(2, 9, 3, 47)
+    r = np.random.default_rng(48).normal(0, 1.5, k.shape)
+    tw, tu, tk, tv, tr = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (w, u, k, v, r))
+    T = k.shape[1]
+    outs = []
+    for t in range(T):
+        age = torch.arange(t, -1, -1, dtype=torch.float64) - 1.0  # t-1-i for i = 0..t
+        logits = tk[:, : t + 1, :] - age[None, :, None] * tw[None, None, :]
+        logits = torch.cat([logits[:, :t, :], (tu + tk[:, t, :])[:, None, :]], dim=1)
+        wts = torch.softmax(logits, dim=1)
+        outs.append((wts * tv[:, : t + 1, :]).sum(dim=1))
+    out = torch.sigmoid(tr) * torch.stack(outs, dim=1)
+    (out * torch.tensor(gy)).sum().backward()
+    dk, dv, dr, dw, du = wkv_gated_backward_ref(w, u, k, v, r, gy)
+    for g, ref in ((dk, tk.grad), (dv, tv.grad), (dr, tr.grad), (dw, tw.grad), (du, tu.grad)):
+        assert np.allclose(g, ref.numpy(), rtol=1e-10, atol=1e-12)
 
 
 def test_step_state_representation_invariance():
