@@ -627,8 +627,9 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
 
 // Whole-tile backward: one workgroup walks all time blocks of its tile from
 // the last to the first, keeping the carry in LDS (no cross-workgroup
-// exchange) and loading the next block's inputs while it computes the current
-// one.  Used when there are enough tiles to fill the GPU.
+// exchange).  Used when there are enough tiles to fill the GPU.  (Loading the
+// next block's inputs during the current one measured no faster: the two
+// workgroups on each CU already overlap each other's loads.)
 template <typename TIn, int L, int W, bool Gated>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
     __shared__ BwdShared<W> sm;
@@ -648,11 +649,10 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
 
     RCarry cin{0.0, 0.0, 0.0, 0.0, 0};  // carry at the current block's end (same in every wave)
     float ndw = 0.f, du = 0.f;
-    SpanIn<TIn, L, Gated> cur, nxt;
-    cur.load(span_geo<TIn, L, W>(P, b, c, cok, P.nblocks - 1, wave), P.C);
+    SpanIn<TIn, L, Gated> cur;
     for (int64_t blk = P.nblocks - 1; blk >= 0; --blk) {
         const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
-        if (blk > 0) nxt.load(span_geo<TIn, L, W>(P, b, c, cok, blk - 1, wave), P.C);
+        cur.load(g, P.C);
         Chunk1<TIn, L> rg;
         if (Gated) rg.load(g.rr, g.vin, g.row_in);
         Span<TIn, L, Gated> sp;
@@ -673,7 +673,6 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
         ndw += sp.reverse(rapply(suf, cin), g, ch, eu, dec, fast_out);
         lds_sync();
         cin = RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane], sm.cin_s[lane]};
-        cur = nxt;
     }
     put_partials(sm, P, tile, wave, lane, ndw, du);
 }

@@ -91,8 +91,14 @@ struct BufLd<uint16_t> {
     }
 };
 
+// Output stores stream: nothing here reads them back, so they are marked
+// non-temporal (sc0 nt) and do not displace the inputs and carries in L2.
+#ifndef WKV_STORE_AUX
+#define WKV_STORE_AUX 3
+#endif
+
 __device__ __forceinline__ void buf_store(float v, Rsrc r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, WKV_STORE_AUX);
 }
 
 // One input over L tokens of a lane (token j at soffset j * row), held in
