@@ -1,9 +1,9 @@
-"""Float64 CPU oracle for the RWKV-4 WKV operator.
+"""Float64 CPU oracle for the RWKV-4 WKV operator and the token-shift mix.
 
 TEST INFRASTRUCTURE ONLY: used by tests/, __graft_entry__.smoke() and the
-cpu_baseline leg of bench.py, never by the product path.  See wkv_ref.py for
-the sources each function follows and the readings taken where the pages are
-silent.
+cpu_baseline leg of bench.py, never by the product path.  See wkv_ref.py and
+token_shift_ref.py for the sources each function follows and the readings
+taken where the pages are silent.
 """
 from .wkv_ref import (  # noqa: F401
     wkv_backward_ref,
@@ -14,4 +14,9 @@ from .wkv_ref import (  # noqa: F401
     wkv_state_from_sums,
     wkv_step_ref,
     wkv_sums_from_state,
+)
+from .token_shift_ref import (  # noqa: F401
+    shifted_inputs_ref,
+    token_shift_backward_ref,
+    token_shift_ref,
 )
