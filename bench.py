@@ -19,7 +19,9 @@ fwd+bwd), fwd4 (B=1 T=32768 C=4096 fp32, forward only), step5 (32 layers x
 256 streams x 4096 channels decode step), prefill (the headline shape's forward
 started from a state and returning it, as wkv_forward_state), gated (the
 headline with the receptance gate fused: wkv_forward_gated +
-wkv_backward_gated), copy (a plain
+wkv_backward_gated), shift (the token-shift mix that feeds the r, k, v
+projections, wkv_token_shift + wkv_token_shift_backward, M=3 mixes at the
+headline shape in bf16), copy (a plain
 1 GiB device-to-device copy: the calibration kernel for the FETCH_SIZE /
 WRITE_SIZE counters).
 """
@@ -48,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -310,6 +312,90 @@ def bench_step5(args):
     return out
 
 
+def bench_shift(args):
+    """Token-shift mix, forward + backward, of the three time-mixing mixes
+    (M=3) at B=8 T=1024 C=4096 with bf16 x and gout.  Algorithmic bytes per
+    channel-token: forward 2 (x) + 3 x 2 (out); backward 2 (x) + 3 x 2 (gout)
+    + 4 (dx); dmu is M*C floats per call."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops, workloads as W
+
+    dev = torch.device("cuda:0")
+    p = W.shift_config()
+    B, T, C, M = p.B, p.T, p.C, p.M
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    mu = torch.from_numpy(p.mu).to(dev)
+    x0, g0 = up(p.x_bits), up(p.gout_bits)
+    # the forward and the backward read separate copies of x, so that the
+    # backward never finds x in the Infinity Cache after the forward read it
+    # (in a model, the whole network runs between the two)
+    sets = []
+    for i in range(args.sets):
+        sets.append({"xf": x0 if i == 0 else x0.clone(), "xb": x0.clone(), "g": g0 if i == 0 else g0.clone(),
+                     "out": torch.empty((M, B, T, C), dtype=torch.bfloat16, device=dev),
+                     "dx": torch.empty((B, T, C), dtype=torch.float32, device=dev),
+                     "dmu": torch.empty((M, C), dtype=torch.float32, device=dev)})
+    ws = torch.empty(max(1, ops.L.lib().wkv_token_shift_workspace_bytes(B, T, C, M)), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        ops.token_shift(mu, s["xf"], out=s["out"])
+        if ev is not None:
+            ev[1].record()
+        ops.token_shift_backward(mu, s["xb"], s["g"], out=(s["dx"], s["dmu"], None), workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    fwd = stats_us([e[0].elapsed_time(e[1]) for e in evs])
+    bwd = stats_us([e[1].elapsed_time(e[2]) for e in evs])
+    n = B * T * C
+    bytes_f, bytes_b = (2 + 2 * M) * n, (2 + 2 * M + 4) * n
+    dom, dom_us, dom_bytes = ("wkv_token_shift_backward", bwd["mean"], bytes_b) if bwd["mean"] >= fwd["mean"] \
+        else ("wkv_token_shift", fwd["mean"], bytes_f)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    out = {
+        "metric": "token-shift mix fwd+bwd channel·tokens/s, B=8 T=1024 C=4096 M=3 bf16",
+        "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": p.name + " fwd+bwd", "B": B, "T": T, "C": C, "M": M, "in_dtype": p.dtype},
+        "hbm_gbps_algorithmic": (bytes_f + bytes_b) / (wall / args.steps) / 1e9,
+        "pct_hbm_peak": 100.0 * (bytes_f + bytes_b) / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS,
+        "call_us": {"wkv_token_shift": fwd, "wkv_token_shift_backward": bwd},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("shift_bf16_B8_T1024_C4096_M3", dom),
+                     "alg_bytes_per_launch": dom_bytes},
+    }
+    if not args.no_cpu:
+        from oracle import token_shift_backward_ref, token_shift_ref
+
+        t0 = time.perf_counter()
+        token_shift_ref(p.mu, p.x)
+        token_shift_backward_ref(p.mu, p.x, p.gout)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole workload ({n} channel*tokens, M=3, fwd+bwd) through the "
+                                         f"float64 numpy oracle, {t_np:.2f} s"}
+    return out
+
+
 def bench_copy(args):
     """A plain copy of 1 GiB (reads 1 GiB, writes 1 GiB): HBM counter calibration."""
     import torch
@@ -346,8 +432,8 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy"):
-        out = bench_step5(args) if args.workload == "step5" else bench_copy(args)
+    if args.workload in ("step5", "copy", "shift"):
+        out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

@@ -1,5 +1,6 @@
 /*
- * wkv.h - C ABI of the RWKV-4 WKV time-mixing operator for AMD MI355X (gfx950).
+ * wkv.h - C ABI of the RWKV-4 WKV time-mixing operator for AMD MI355X (gfx950),
+ * with the receptance gate and the token-shift mix around it.
  *
  * The operator, per channel c of each batch row b, tokens t = 1..T
  * ("RWKV（Receptance Weighted Key Value）概念", section 3.2; and
@@ -196,6 +197,57 @@ wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
                                 const float* w, const float* u, const void* k, const void* v, const void* r,
                                 const void* gout, float* dk, float* dv, float* dr, float* dw, float* du,
                                 const void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * wkv_token_shift / wkv_token_shift_backward - the token-shift mix that
+ * produces the inputs of the time-mixing projections.
+ *
+ * Defines ("RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", section
+ * "关键设计 1：Token Shift - 给并行投影注入前一时刻", where r, k and v each
+ * project their own mix; "RWKV（Receptance Weighted Key Value）概念", section
+ * 3.3, the same mix before channel mixing), for M mixing vectors mu_j:
+ *     out_j[b, t, c] = mu_j[c] x[b, t, c] + (1 - mu_j[c]) x[b, t-1, c]
+ * where x[b, -1, c] is x_prev[b, c] (the previous input that the state tuple
+ * of section "整体架构" carries from an earlier segment or decode step), or 0
+ * when x_prev is NULL.  Only the elementwise mix: the projections are
+ * ordinary matrix products outside this library.  Evaluated in float32 as
+ * xs + mu (x - xs) with one fused multiply-add.
+ *
+ * B, T, C   batch, tokens, channels (>= 0).  M  number of mixes, 1..4 (3 for
+ *           the time-mixing r, k, v; 2 for channel mixing); else WKV_EINVAL.
+ * in_dtype  dtype of x, x_prev, out and gout.
+ * mu        [M, C] float32 mixing vectors.
+ * x         [B, T, C] input.  x_prev  [B, C] or NULL.  The x_prev of the next
+ *           segment is x[:, T-1, :] of this one (a view; nothing is stored).
+ * out       [M, B, T, C] in_dtype, fully overwritten (bf16: float32 result
+ *           rounded to nearest even).  Must not overlap x or x_prev.
+ *
+ * Backward, for L = sum_j <gout_j, out_j>:
+ *     dx[b, t]    = sum_j mu_j gout_j[b, t] + (1 - mu_j) gout_j[b, t+1]
+ *                   (no t+1 term at t = T-1)
+ *     dmu[j]      = sum_{b,t} gout_j[b, t] (x[b, t] - x[b, t-1])
+ *     dx_prev[b]  = sum_j (1 - mu_j) gout_j[b, 0]
+ * gout      [M, B, T, C] in_dtype.
+ * dx        [B, T, C] float32, fully overwritten; must not overlap an input.
+ * dmu       [M, C] float32, overwritten (summed over b and t, in a fixed
+ *           order: bitwise reproducible).  Set to 0 when B*T == 0.
+ * dx_prev   [B, C] float32 or NULL; overwritten when given (0 when T == 0).
+ * workspace at least wkv_token_shift_workspace_bytes(B, T, C, M) bytes,
+ *           256-byte aligned (partial sums of dmu).
+ * Errors as the other entry points.  Full speed needs C a multiple of 8
+ * (bf16) or 4 (float32) and 16-byte aligned tensors; other shapes take a
+ * one-element-per-thread path with the same results.
+ */
+size_t wkv_token_shift_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M);
+
+wkv_status_t wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, int in_dtype,
+                             const float* mu, const void* x, const void* x_prev, void* out,
+                             void* hip_stream);
+
+wkv_status_t wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, int in_dtype,
+                                      const float* mu, const void* x, const void* x_prev,
+                                      const void* gout, float* dx, float* dmu, float* dx_prev,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * wkv_step - one recurrent-mode (decode) token for L x B independent states.

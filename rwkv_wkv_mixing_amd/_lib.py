@@ -26,6 +26,9 @@ EXPORTS = (
     "wkv_forward_gated",
     "wkv_backward_gated",
     "wkv_step",
+    "wkv_token_shift_workspace_bytes",
+    "wkv_token_shift",
+    "wkv_token_shift_backward",
     "wkv_status_str",
     "wkv_last_hip_error",
     "wkv_version",
@@ -76,6 +79,12 @@ def declare(L):
     L.wkv_backward_gated.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_step.restype = i32
     L.wkv_step.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, vp]
+    L.wkv_token_shift_workspace_bytes.restype = sz
+    L.wkv_token_shift_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.wkv_token_shift.restype = i32
+    L.wkv_token_shift.argtypes = [i64, i64, i64, i64, i32, fp, vp, vp, vp, vp]
+    L.wkv_token_shift_backward.restype = i32
+    L.wkv_token_shift_backward.argtypes = [i64, i64, i64, i64, i32, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
     L.wkv_status_str.restype = ctypes.c_char_p
     L.wkv_status_str.argtypes = [i32]
     L.wkv_last_hip_error.restype = ctypes.c_char_p

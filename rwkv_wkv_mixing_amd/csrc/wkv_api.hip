@@ -56,6 +56,26 @@ Plan plan(int op, int64_t B, int64_t T, int64_t C, int dt) {
     return p;
 }
 
+struct ShiftPlan {
+    wkv_status_t st;
+    int64_t N;
+    size_t ws_bytes;
+};
+
+ShiftPlan shift_plan(int64_t B, int64_t T, int64_t C, int64_t M, int dt) {
+    if (B < 0 || T < 0 || C < 0 || M < 1 || M > 4) return ShiftPlan{WKV_EINVAL, 0, 0};
+    if (!dtype_ok(dt)) return ShiftPlan{WKV_EDTYPE, 0, 0};
+    ShiftPlan p{WKV_OK, 0, 0};
+    int64_t bytes, rows_c, ws;
+    if (!mul3(B, T, C, &p.N) || !mul3(p.N, M, 4, &bytes)) return ShiftPlan{WKV_ESIZE, 0, 0};
+    // grid: at most one block per (row of partials, channel), below 2^31 blocks
+    const int64_t rows = wkv::shift_partial_rows(B, T);
+    if (__builtin_mul_overflow(rows, C, &rows_c) || rows_c >= (int64_t{1} << 31)) return ShiftPlan{WKV_ESIZE, 0, 0};
+    if (!mul3(rows_c, M, 4, &ws)) return ShiftPlan{WKV_ESIZE, 0, 0};
+    p.ws_bytes = static_cast<size_t>(ws);
+    return p;
+}
+
 __global__ void zero2_kernel(int64_t n, float* a, float* b) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < n) {
@@ -210,6 +230,56 @@ wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype, const float
                       aligned(v, 4 * es);
     wkv::StepArgs s{L, B, C, in_dtype == WKV_BF16, vec4, w, u, k, v, y, a, b, p};
     return hip_status(wkv::launch_step(s, static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t wkv_token_shift_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {
+    const ShiftPlan p = shift_plan(B, T, C, M, WKV_F32);
+    return p.st == WKV_OK ? p.ws_bytes : 0;
+}
+
+wkv_status_t wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, int in_dtype, const float* mu,
+                             const void* x, const void* x_prev, void* out, void* hip_stream) {
+    const ShiftPlan p = shift_plan(B, T, C, M, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (p.N == 0) return WKV_OK;
+    if (!mu || !x || !out) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(mu, 4) || !aligned(x, es) || !aligned(out, es) || (x_prev && !aligned(x_prev, es)))
+        return WKV_EALIGN;
+    const bool bf = in_dtype == WKV_BF16;
+    wkv::ShiftArgs a{B, T, C, M, bf, false, mu, x, x_prev, out, nullptr, nullptr, nullptr, nullptr, nullptr};
+    a.vec = C % wkv::shift_vector_width(bf, false) == 0 && aligned(mu, 16) && aligned(x, 16) && aligned(out, 16) &&
+            (!x_prev || aligned(x_prev, 16));
+    return hip_status(wkv::launch_shift_fwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+wkv_status_t wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, int in_dtype,
+                                      const float* mu, const void* x, const void* x_prev, const void* gout,
+                                      float* dx, float* dmu, float* dx_prev, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream) {
+    const ShiftPlan p = shift_plan(B, T, C, M, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (C == 0) return WKV_OK;
+    if (!dmu) return WKV_EINVAL;
+    if (!aligned(dmu, 4) || (dx_prev && !aligned(dx_prev, 4))) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p.N == 0) {  // empty sums: dmu = 0, and no token reads the previous input
+        hipError_t e = wkv::launch_shift_zero(dmu, M * C, stream);
+        if (e == hipSuccess && dx_prev) e = wkv::launch_shift_zero(dx_prev, B * C, stream);
+        return hip_status(e);
+    }
+    if (!mu || !x || !gout || !dx) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(mu, 4) || !aligned(x, es) || !aligned(gout, es) || !aligned(dx, 4) ||
+        (x_prev && !aligned(x_prev, es)))
+        return WKV_EALIGN;
+    if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    const bool bf = in_dtype == WKV_BF16;
+    wkv::ShiftArgs a{B, T, C, M, bf, false, mu, x, x_prev, nullptr, gout, dx, dmu, dx_prev,
+                     static_cast<float*>(workspace)};
+    a.vec = C % wkv::shift_vector_width(bf, true) == 0 && aligned(mu, 16) && aligned(x, 16) && aligned(gout, 16) &&
+            aligned(dx, 16) && (!x_prev || aligned(x_prev, 16)) && (!dx_prev || aligned(dx_prev, 16));
+    return hip_status(wkv::launch_shift_bwd(a, stream));
 }
 
 const char* wkv_status_str(wkv_status_t s) {

@@ -70,6 +70,21 @@ struct StepArgs {
     float* p;
 };
 
+struct ShiftArgs {
+    int64_t B, T, C, M;
+    bool bf16;
+    bool vec;              // 16-byte vectors: C a multiple of 16 / element size, pointers 16-byte aligned
+    const float* mu;       // [M, C]
+    const void* x;         // [B, T, C]
+    const void* x_prev;    // [B, C] or NULL (zeros)
+    void* out;             // forward: [M, B, T, C], dtype of x
+    const void* g;         // backward: [M, B, T, C], dtype of x
+    float* dx;             // backward: [B, T, C]
+    float* dmu;            // backward: [M, C]
+    float* dx_prev;        // backward: [B, C] or NULL
+    float* ws;             // backward: shift_partial_rows(B, T) * M * C floats
+};
+
 // chunked forward (wkv_fwd.hip)
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t stream);
 // T == 0 with a state: the output state is the input state (or the empty one)
@@ -79,6 +94,13 @@ size_t fwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C);
 // chunked backward (wkv_bwd.hip)
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream);
 size_t bwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C);
+
+// token-shift mix (wkv_shift.hip)
+hipError_t launch_shift_fwd(const ShiftArgs& a, hipStream_t stream);
+hipError_t launch_shift_bwd(const ShiftArgs& a, hipStream_t stream);
+hipError_t launch_shift_zero(float* p, int64_t n, hipStream_t stream);
+int64_t shift_partial_rows(int64_t B, int64_t T);
+int shift_vector_width(bool bf16, bool bwd);
 
 // decode step (wkv_step.hip)
 hipError_t launch_step(const StepArgs& s, hipStream_t stream);

@@ -223,3 +223,86 @@ class WKVFunction(torch.autograd.Function):
 def wkv(w, u, k, v):
     """Differentiable WKV forward (see WKVFunction)."""
     return WKVFunction.apply(w, u, k, v)
+
+
+def token_shift(mu, x, *, x_prev=None, out=None):
+    """The M token-shift mixes of x: out[j] = mu[j] * x_t + (1 - mu[j]) * x_{t-1}.
+
+    mu [M, C] float32 (1 <= M <= 4); x [B, T, C] float32 or bfloat16; x_prev
+    [B, C] of x's dtype (the previous segment's last input) or None (zeros).
+    Returns out [M, B, T, C] in x's dtype.
+    """
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    dev = x.device
+    B, T, C = x.shape
+    _need(mu, "mu", torch.float32, None, dev)
+    if mu.dim() != 2 or mu.shape[1] != C:
+        raise ValueError(f"mu has shape {tuple(mu.shape)}, expected (M, {C})")
+    M = mu.shape[0]
+    if x_prev is not None:
+        _need(x_prev, "x_prev", x.dtype, (B, C), dev)
+    if out is None:
+        out = torch.empty((M, B, T, C), dtype=x.dtype, device=dev)
+    _need(out, "out", x.dtype, (M, B, T, C), dev)
+    st = L.lib().wkv_token_shift(B, T, C, M, _DT[x.dtype], _p(mu), _p(x), _p(x_prev), _p(out), _stream(dev))
+    L.check("wkv_token_shift", st)
+    return out
+
+
+def token_shift_backward(mu, x, gout, *, x_prev=None, want_dx_prev=False, out=None, workspace=None):
+    """(dx [B,T,C], dmu [M,C], dx_prev [B,C] or None), float32, for L = sum(gout * token_shift(mu, x, x_prev)).
+
+    gout [M, B, T, C] has x's dtype.  dx_prev is computed when want_dx_prev
+    (or when ``out`` holds a third tensor).
+    """
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    dev = x.device
+    B, T, C = x.shape
+    _need(mu, "mu", torch.float32, None, dev)
+    if mu.dim() != 2 or mu.shape[1] != C:
+        raise ValueError(f"mu has shape {tuple(mu.shape)}, expected (M, {C})")
+    M = mu.shape[0]
+    _need(gout, "gout", x.dtype, (M, B, T, C), dev)
+    if x_prev is not None:
+        _need(x_prev, "x_prev", x.dtype, (B, C), dev)
+    if out is None:
+        out = (torch.empty((B, T, C), dtype=torch.float32, device=dev),
+               torch.empty((M, C), dtype=torch.float32, device=dev),
+               torch.empty((B, C), dtype=torch.float32, device=dev) if want_dx_prev else None)
+    dx, dmu, dxp = out
+    _need(dx, "dx", torch.float32, (B, T, C), dev)
+    _need(dmu, "dmu", torch.float32, (M, C), dev)
+    if dxp is not None:
+        _need(dxp, "dx_prev", torch.float32, (B, C), dev)
+    nbytes = int(L.lib().wkv_token_shift_workspace_bytes(B, T, C, M))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    st = L.lib().wkv_token_shift_backward(B, T, C, M, _DT[x.dtype], _p(mu), _p(x), _p(x_prev), _p(gout), _p(dx),
+                                          _p(dmu), _p(dxp), _p(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(dev))
+    L.check("wkv_token_shift_backward", st)
+    return dx, dmu, dxp
+
+
+class TokenShiftFunction(torch.autograd.Function):
+    """Autograd wrapper of token_shift: saves mu, x (and x_prev)."""
+
+    @staticmethod
+    def forward(ctx, mu, x, x_prev):
+        out = token_shift(mu, x, x_prev=x_prev)
+        ctx.save_for_backward(mu, x, x_prev)
+        return out
+
+    @staticmethod
+    def backward(ctx, gout):
+        mu, x, x_prev = ctx.saved_tensors
+        gout = gout.to(x.dtype).contiguous()
+        dx, dmu, dxp = token_shift_backward(mu, x, gout, x_prev=x_prev, want_dx_prev=x_prev is not None)
+        return dmu, dx.to(x.dtype), None if dxp is None else dxp.to(x.dtype)
+
+
+def token_shift_mix(mu, x, x_prev=None):
+    """Differentiable token_shift (see TokenShiftFunction)."""
+    return TokenShiftFunction.apply(mu, x, x_prev)

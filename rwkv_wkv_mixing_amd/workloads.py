@@ -221,3 +221,56 @@ def step_inputs_torch(dp: DecodeProblem, step: int, device):
     k = torch.randn((dp.L, dp.B, dp.C), generator=g, device=device, dtype=torch.float32)
     v = torch.randn((dp.L, dp.B, dp.C), generator=g, device=device, dtype=torch.float32)
     return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@dataclass
+class ShiftProblem:
+    """Inputs of the token-shift mix: mu [M, C] float32, x [B, T, C], x_prev
+    [B, C] (or None), gout [M, B, T, C].  As for WkvProblem, the float32
+    arrays hold the exact values both sides consume and ``*_bits`` the bf16
+    encodings handed to the GPU."""
+
+    name: str
+    B: int
+    T: int
+    C: int
+    M: int
+    dtype: str
+    mu: np.ndarray
+    x: np.ndarray
+    x_prev: np.ndarray | None
+    gout: np.ndarray
+    x_bits: np.ndarray | None = None
+    x_prev_bits: np.ndarray | None = None
+    gout_bits: np.ndarray | None = None
+
+    def device_inputs(self, name: str) -> np.ndarray:
+        if self.dtype == BF16:
+            return getattr(self, name + "_bits")
+        return getattr(self, name)
+
+
+def make_shift(B, T, C, M, *, dtype=BF16, seed=0, with_prev=True, name="") -> ShiftProblem:
+    """Draw order: mu ~ U(0, 1) (the mixing ratios of the pages lie between
+    the two tokens), x ~ N(0, 1), x_prev ~ N(0, 1) (always drawn, dropped when
+    not wanted), gout ~ N(0, 1); then bf16 rounding of x, x_prev, gout."""
+    rng = np.random.default_rng(seed)
+    mu = rng.uniform(0.0, 1.0, (M, C)).astype(np.float32)
+    x = _normal(rng, 1.0, (B, T, C))
+    xp = _normal(rng, 1.0, (B, C))
+    g = _normal(rng, 1.0, (M, B, T, C))
+    p = ShiftProblem(name or f"shift {dtype} B={B} T={T} C={C} M={M}", B, T, C, M, dtype, mu, x,
+                     xp if with_prev else None, g)
+    if dtype == BF16:
+        p.x_bits, p.x = bf16_round(x)
+        p.gout_bits, p.gout = bf16_round(g)
+        if with_prev:
+            p.x_prev_bits, p.x_prev = bf16_round(xp)
+    return p
+
+
+def shift_config(seed=0) -> ShiftProblem:
+    """The three time-mixing mixes (r, k, v) of a 7B-shaped layer at the bf16
+    training workload's size: B=8, T=1024, C=4096."""
+    return make_shift(8, 1024, 4096, 3, dtype=BF16, seed=seed, with_prev=False,
+                      name="token shift bf16 B=8 T=1024 C=4096 M=3")

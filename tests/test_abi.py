@@ -160,3 +160,51 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         ops.wkv_step(torch.ones(1, 4), torch.ones(1, 4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4),
                      torch.zeros(1, 2, 4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))
+
+
+def shift(lib, B, T, C, M, dt, mu, x, xp, out):
+    return lib.wkv_token_shift(B, T, C, M, dt, P(mu), P(x), P(xp), P(out), None)
+
+
+def shift_bwd(lib, B, T, C, M, dt, mu, x, xp, g, dx, dmu, dxp, ws=None, nws=0):
+    return lib.wkv_token_shift_backward(B, T, C, M, dt, P(mu), P(x), P(xp), P(g), P(dx), P(dmu), P(dxp),
+                                        P(ws), nws, None)
+
+
+def test_token_shift_workspace_size(lib):
+    # partial sums of dmu: one row per (batch row, block of 256 tokens), M * C floats each
+    assert lib.wkv_token_shift_workspace_bytes(8, 1024, 4096, 3) == 8 * 4 * 3 * 4096 * 4
+    assert lib.wkv_token_shift_workspace_bytes(2, 129, 7, 1) == 2 * 1 * 7 * 4
+    assert lib.wkv_token_shift_workspace_bytes(2, 257, 7, 1) == 2 * 2 * 7 * 4
+    assert lib.wkv_token_shift_workspace_bytes(2, 0, 7, 1) == 0
+    assert lib.wkv_token_shift_workspace_bytes(2, 5, 7, 0) == 0   # M out of range
+    assert lib.wkv_token_shift_workspace_bytes(2, 5, 7, 5) == 0
+    assert lib.wkv_token_shift_workspace_bytes(-2, 5, 7, 1) == 0
+    assert lib.wkv_token_shift_workspace_bytes(1 << 30, 1 << 30, 1 << 10, 1) == 0
+
+
+def test_token_shift_validation(lib):
+    x = A16
+    assert shift(lib, 1, 4, 4, 0, L.WKV_F32, x, x, None, x) == L.WKV_EINVAL
+    assert shift(lib, 1, 4, 4, 5, L.WKV_F32, x, x, None, x) == L.WKV_EINVAL
+    assert shift(lib, -1, 4, 4, 3, L.WKV_F32, x, x, None, x) == L.WKV_EINVAL
+    assert shift(lib, 1, 4, 4, 3, 2, x, x, None, x) == L.WKV_EDTYPE
+    assert shift(lib, 1 << 30, 1 << 30, 1 << 10, 3, L.WKV_F32, x, x, None, x) == L.WKV_ESIZE
+    assert shift(lib, 1, 4, 4, 3, L.WKV_F32, None, x, None, x) == L.WKV_EINVAL
+    assert shift(lib, 1, 4, 4, 3, L.WKV_F32, x, x, None, None) == L.WKV_EINVAL
+    assert shift(lib, 1, 4, 4, 3, L.WKV_F32, x, x + 2, None, x) == L.WKV_EALIGN
+    assert shift(lib, 1, 4, 4, 3, L.WKV_BF16, x, x, x + 1, x) == L.WKV_EALIGN
+    assert shift(lib, 1, 4, 4, 3, L.WKV_BF16, x + 2, x, None, x) == L.WKV_EALIGN
+    assert shift(lib, 0, 4, 4, 3, L.WKV_F32, None, None, None, None) == L.WKV_OK
+    assert shift(lib, 2, 0, 4, 3, L.WKV_F32, None, None, None, None) == L.WKV_OK
+    need = lib.wkv_token_shift_workspace_bytes(1, 4, 4, 3)
+    args = [x] * 7
+    assert shift_bwd(lib, 1, 4, 4, 9, L.WKV_F32, *args, ws=x, nws=need) == L.WKV_EINVAL
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, x, x, None, x, x, None, None, ws=x, nws=need) == L.WKV_EINVAL
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, x, x, None, None, x, x, None, ws=x, nws=need) == L.WKV_EINVAL
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, x, x, None, x, x + 2, x, None, ws=x, nws=need) == L.WKV_EALIGN
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, x, x, None, x, x, x, x + 1, ws=x, nws=need) == L.WKV_EALIGN
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, *args) == L.WKV_EWORKSPACE
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, *args, ws=x, nws=need - 1) == L.WKV_EWORKSPACE
+    assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, *args, ws=x + 16, nws=need) == L.WKV_EWORKSPACE
+    assert shift_bwd(lib, 1, 4, 0, 3, L.WKV_F32, *[None] * 7) == L.WKV_OK
