@@ -690,13 +690,34 @@ __global__ void bwd_chunk_reduce_kernel(int64_t B, int64_t C, int64_t nct, int64
     const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (c >= C) return;
     const int64_t ct = c / 64, lane = c % 64;
+    // rows in the order (b, j); the loads of 8 rows issue together, the sums
+    // keep that order (bitwise reproducible)
+    const int64_t nrow = B * nblocks;
+    auto at = [&](int64_t r) {
+        const int64_t b = r / nblocks, j = r - (r / nblocks) * nblocks;
+        return part + (((b * nct + ct) * nblocks + j) * 2) * 64 + lane;
+    };
     float sw = 0.f, su = 0.f;
-    for (int64_t b = 0; b < B; ++b)
-        for (int64_t j = 0; j < nblocks; ++j) {
-            const float* pp = part + (((b * nct + ct) * nblocks + j) * 2) * 64 + lane;
-            sw += pp[0];
-            su += pp[64];
+    int64_t r = 0;
+    for (; r + 8 <= nrow; r += 8) {
+        float w8[8], u8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float* pp = at(r + i);
+            w8[i] = pp[0];
+            u8[i] = pp[64];
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sw += w8[i];
+            su += u8[i];
+        }
+    }
+    for (; r < nrow; ++r) {
+        const float* pp = at(r);
+        sw += pp[0];
+        su += pp[64];
+    }
     dw[c] = sw;
     du[c] = su;
 }

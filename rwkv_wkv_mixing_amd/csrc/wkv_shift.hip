@@ -370,8 +370,17 @@ __global__ __launch_bounds__(kThreads) void shift_reduce_kernel(const float* __r
                                                                  int64_t MC, float* __restrict__ dmu) {
     const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     if (q >= MC) return;
+    // loads of 16 rows issue together; the sum keeps the row order
     float s = 0.f;
-    for (int64_t r = 0; r < rows; ++r) s += ws[r * MC + q];
+    int64_t r = 0;
+    for (; r + 16 <= rows; r += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = ws[(r + i) * MC + q];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += v[i];
+    }
+    for (; r < rows; ++r) s += ws[r * MC + q];
     dmu[q] = s;
 }
 
