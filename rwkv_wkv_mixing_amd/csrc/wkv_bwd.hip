@@ -169,6 +169,10 @@ struct KvChunk<uint16_t, L> {
             kv[j] = lo | (hi << 16);
         }
     }
+    __device__ __forceinline__ void load_lds(const uint16_t (*k)[64], const uint16_t (*v)[64], int lane) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) kv[j] = static_cast<uint32_t>(k[j][lane]) | (static_cast<uint32_t>(v[j][lane]) << 16);
+    }
     __device__ __forceinline__ float k(int j) const { return __uint_as_float(kv[j] << 16); }
     __device__ __forceinline__ float v(int j) const { return __uint_as_float(kv[j] & 0xffff0000u); }
 };
@@ -181,6 +185,13 @@ struct KvChunk<float, L> {
         for (int j = 0; j < L; ++j) {
             kk[j] = BufLd<float>::at(rk, voff, j * row);
             vv[j] = BufLd<float>::at(rv, voff, j * row);
+        }
+    }
+    __device__ __forceinline__ void load_lds(const float (*k)[64], const float (*v)[64], int lane) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            kk[j] = k[j][lane];
+            vv[j] = v[j][lane];
         }
     }
     __device__ __forceinline__ float k(int j) const { return kk[j]; }
@@ -302,6 +313,41 @@ __device__ __forceinline__ SpanGeo span_geo(const BwdChunk& P, int64_t b, int64_
     return g;
 }
 
+// The inputs k, v, gy of one time block staged in LDS: [wave][input][token][channel].
+template <typename TIn, int L, int W>
+struct BwdStage {
+    TIn x[W][3][L][64];
+};
+
+// Start the asynchronous buffer -> LDS copies of wave `wave`'s span of k, v and
+// gy.  Each lane moves 16 bytes and one instruction fills 1 KB of LDS (whole
+// 64-channel rows of 64 * ES / 16 lanes each); the copy of a lane lands at the
+// instruction's LDS base + 16 * lane, which is exactly the [token][channel]
+// layout.  Channels at or past C, and tokens past the block's end, read as
+// zeros (C is a multiple of 16 / ES here, so no 16-byte chunk straddles C).
+// Completion is tracked by vmcnt only: the consumer waits on it explicitly.
+template <typename TIn, int L, int W>
+__device__ __forceinline__ void stage_span(BwdStage<TIn, L, W>& st, const SpanGeo& g, int wave, int lane, int64_t c0,
+                                           int64_t C) {
+    constexpr int ES = sizeof(TIn);
+    constexpr int LPR = 64 * ES / 16;  // lanes per token row
+    constexpr int RPI = 64 / LPR;      // token rows per instruction
+    static_assert(L % RPI == 0, "a span is whole instructions of rows");
+    const int q = lane % LPR;
+    const bool ok = c0 + q * (16 / ES) < C;
+#pragma unroll
+    for (int i = 0; i < L / RPI; ++i) {
+        const int j = i * RPI + lane / LPR;
+        const uint32_t voff = ok ? static_cast<uint32_t>(((int64_t)(wave * L + j) * C + c0) * ES + q * 16) : kOffNone;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rk, (__attribute__((address_space(3))) void*)&st.x[wave][0][i * RPI][0],
+                                                 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rv, (__attribute__((address_space(3))) void*)&st.x[wave][1][i * RPI][0],
+                                                 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rg, (__attribute__((address_space(3))) void*)&st.x[wave][2][i * RPI][0],
+                                                 16, voff, 0, 0, 0);
+    }
+}
+
 // A span's inputs, loaded ahead of use (gy holds the output gradient; with
 // the gate, r too).
 template <typename TIn, int L, bool Gated>
@@ -312,6 +358,9 @@ struct SpanIn {
     __device__ __forceinline__ void load(const SpanGeo& g, int64_t C) {
         kv.load(g.rk, g.rv, g.vin, g.row_in);
         gy.load(g.rg, g.vin, g.row_in);
+        load_ck(g, C);
+    }
+    __device__ __forceinline__ void load_ck(const SpanGeo& g, int64_t C) {
         a0 = 0.f;
         b0 = 0.f;
         s0 = static_cast<float>(kSEmpty);
@@ -320,6 +369,11 @@ struct SpanIn {
             b0 = g.ck[C];
             s0 = g.ck[2 * C];
         }
+    }
+    template <int W>
+    __device__ __forceinline__ void load_lds(const BwdStage<TIn, L, W>& st, int wave, int lane) {
+        kv.load_lds(st.x[wave][0], st.x[wave][1], lane);
+        gy.load_lds(st.x[wave][2], lane);
     }
 };
 
@@ -627,12 +681,20 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
 
 // Whole-tile backward: one workgroup walks all time blocks of its tile from
 // the last to the first, keeping the carry in LDS (no cross-workgroup
-// exchange).  Used when there are enough tiles to fill the GPU.  (Loading the
-// next block's inputs during the current one measured no faster: the two
-// workgroups on each CU already overlap each other's loads.)
-template <typename TIn, int L, int W, bool Gated>
+// exchange).  Used when there are enough tiles to fill the GPU.
+//
+// Staged: while a block is computed, the next block's k, v, gy stream into
+// LDS by asynchronous buffer -> LDS copies (stage_span), and its saved state
+// into three registers, so the loads overlap the arithmetic without holding
+// a second block in registers.  Each wave copies and reads only its own span,
+// so the waits are per wave: vmcnt(0) before reading a block from LDS, and
+// lgkmcnt(0) after, before the next copy may overwrite it.  The copies reach
+// LDS without the compiler seeing them, hence the explicit waits, written as
+// asm statements that also order memory accesses.
+template <typename TIn, int L, int W, bool Gated, bool Staged>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
     __shared__ BwdShared<W> sm;
+    __shared__ BwdStage<TIn, L, W> stage;  // referenced (and allocated) only when Staged
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tile = blockIdx.x;
@@ -649,10 +711,30 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
 
     RCarry cin{0.0, 0.0, 0.0, 0.0, 0};  // carry at the current block's end (same in every wave)
     float ndw = 0.f, du = 0.f;
-    SpanIn<TIn, L, Gated> cur;
+    SpanIn<TIn, L, Gated> cur, nxt;  // nxt: only the next block's saved state (Staged)
+    const int64_t c0 = (tile - b * P.nct) * 64;
+    if constexpr (Staged) {
+        const SpanGeo g0 = span_geo<TIn, L, W>(P, b, c, cok, P.nblocks - 1, wave);
+        stage_span(stage, g0, wave, lane, c0, P.C);
+        nxt.load_ck(g0, P.C);
+    }
     for (int64_t blk = P.nblocks - 1; blk >= 0; --blk) {
         const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
-        cur.load(g, P.C);
+        if constexpr (Staged) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            cur.load_lds(stage, wave, lane);
+            cur.a0 = nxt.a0;
+            cur.b0 = nxt.b0;
+            cur.s0 = nxt.s0;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (blk > 0) {
+                const SpanGeo gn = span_geo<TIn, L, W>(P, b, c, cok, blk - 1, wave);
+                stage_span(stage, gn, wave, lane, c0, P.C);
+                nxt.load_ck(gn, P.C);
+            }
+        } else {
+            cur.load(g, P.C);
+        }
         Chunk1<TIn, L> rg;
         if (Gated) rg.load(g.rr, g.vin, g.row_in);
         Span<TIn, L, Gated> sp;
@@ -732,6 +814,9 @@ namespace {
 #ifndef WKV_BWD_TILE_W
 #define WKV_BWD_TILE_W 4
 #endif
+#ifndef WKV_BWD_STAGE
+#define WKV_BWD_STAGE 1  // whole-tile backward: stage each next block's inputs in LDS
+#endif
 constexpr int kBwdL = WKV_BWD_L;
 constexpr int kBwdW = WKV_BWD_W;        // waves per workgroup, time-split kernel
 constexpr int kBwdTileW = WKV_BWD_TILE_W;  // waves per workgroup, whole-tile kernel
@@ -798,12 +883,19 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (l.ntiles >= 2 * static_cast<int64_t>(ncu)) {
         P.nblocks = (a.T + kBwdL * kBwdTileW - 1) / (kBwdL * kBwdTileW);
-        if (P.r != nullptr)
-            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true>), dim3(static_cast<unsigned>(l.ntiles)),
-                               dim3(64 * kBwdTileW), 0, stream, P);
+        // the LDS-staged loads move 16-byte chunks: whole chunks per row, aligned
+        const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+        const bool staged = WKV_BWD_STAGE && a.C % (16 / static_cast<int64_t>(sizeof(TIn))) == 0 && a16(a.k) &&
+                            a16(a.v) && a16(a.gy);
+        const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * kBwdTileW);
+        if (P.r != nullptr && staged)
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true, true>), grid, block, 0, stream, P);
+        else if (P.r != nullptr)
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true, false>), grid, block, 0, stream, P);
+        else if (staged)
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false, true>), grid, block, 0, stream, P);
         else
-            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false>),
-                               dim3(static_cast<unsigned>(l.ntiles)), dim3(64 * kBwdTileW), 0, stream, P);
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false, false>), grid, block, 0, stream, P);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,

@@ -117,6 +117,15 @@ struct Chunk1<uint16_t, L> {
             pk[j / 2] = lo | (hi << 16);
         }
     }
+    // from a [L][64] block staged in LDS, lane = channel
+    __device__ __forceinline__ void load_lds(const uint16_t (*x)[64], int lane) {
+#pragma unroll
+        for (int j = 0; j < L; j += 2) {
+            const uint32_t lo = x[j][lane];
+            const uint32_t hi = j + 1 < L ? static_cast<uint32_t>(x[j + 1][lane]) : 0u;
+            pk[j / 2] = lo | (hi << 16);
+        }
+    }
     __device__ __forceinline__ float at(int j) const {
         return (j & 1) ? __uint_as_float(pk[j / 2] & 0xffff0000u) : __uint_as_float(pk[j / 2] << 16);
     }
@@ -128,6 +137,10 @@ struct Chunk1<float, L> {
     __device__ __forceinline__ void load(Rsrc r, uint32_t voff, uint32_t row) {
 #pragma unroll
         for (int j = 0; j < L; ++j) x[j] = BufLd<float>::at(r, voff, j * row);
+    }
+    __device__ __forceinline__ void load_lds(const float (*s)[64], int lane) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) x[j] = s[j][lane];
     }
     __device__ __forceinline__ float at(int j) const { return x[j]; }
 };

@@ -203,14 +203,17 @@ def test_checkpointed_backward_matches():
     check_bwd(p, [t.cpu().numpy() for t in g1])
 
 
-@pytest.mark.parametrize("dt,T", [("f32", 77), ("bf16", 77), ("bf16", 1)])
-def test_whole_tile_backward(dt, T):
+@pytest.mark.parametrize("dt,T,extra", [("f32", 77, 17), ("bf16", 77, 17), ("bf16", 1, 17),
+                                         ("f32", 77, 24), ("bf16", 77, 24), ("bf16", 200, 24), ("bf16", 1, 24)])
+def test_whole_tile_backward(dt, T, extra):
     """At >= 2 tiles of 64 channels per CU the backward runs one workgroup per
     tile over the whole sequence; ragged T and a ragged last tile, with and
-    without the forward's saved states."""
+    without the forward's saved states.  C = 64 ncu + 17 takes the per-element
+    loads; C = 64 ncu + 24 (whole 16-byte chunks per row) stages each next
+    block in LDS, with the last tile's chunks past C read as zeros."""
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    C = 64 * ncu + 17  # B = 2 rows of ncu + 1 tiles
-    p = W.make_problem(2, T, C, dtype=dt, seed=21, spike_frac=0.01, name=f"tile {dt} T={T}")
+    C = 64 * ncu + extra  # B = 2 rows of ncu + 1 tiles
+    p = W.make_problem(2, T, C, dtype=dt, seed=21, spike_frac=0.01, name=f"tile {dt} T={T} C={C}")
     print(f"case {p.name} C={C}", flush=True)
     check_bwd(p, run_bwd(p))
     d = problem_to_dev(p, DEV)
