@@ -319,33 +319,13 @@ struct BwdStage {
     TIn x[W][3][L][64];
 };
 
-// Start the asynchronous buffer -> LDS copies of wave `wave`'s span of k, v and
-// gy.  Each lane moves 16 bytes and one instruction fills 1 KB of LDS (whole
-// 64-channel rows of 64 * ES / 16 lanes each); the copy of a lane lands at the
-// instruction's LDS base + 16 * lane, which is exactly the [token][channel]
-// layout.  Channels at or past C, and tokens past the block's end, read as
-// zeros (C is a multiple of 16 / ES here, so no 16-byte chunk straddles C).
-// Completion is tracked by vmcnt only: the consumer waits on it explicitly.
+// Start the asynchronous copies of wave `wave`'s span of k, v and gy into LDS.
 template <typename TIn, int L, int W>
 __device__ __forceinline__ void stage_span(BwdStage<TIn, L, W>& st, const SpanGeo& g, int wave, int lane, int64_t c0,
                                            int64_t C) {
-    constexpr int ES = sizeof(TIn);
-    constexpr int LPR = 64 * ES / 16;  // lanes per token row
-    constexpr int RPI = 64 / LPR;      // token rows per instruction
-    static_assert(L % RPI == 0, "a span is whole instructions of rows");
-    const int q = lane % LPR;
-    const bool ok = c0 + q * (16 / ES) < C;
-#pragma unroll
-    for (int i = 0; i < L / RPI; ++i) {
-        const int j = i * RPI + lane / LPR;
-        const uint32_t voff = ok ? static_cast<uint32_t>(((int64_t)(wave * L + j) * C + c0) * ES + q * 16) : kOffNone;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rk, (__attribute__((address_space(3))) void*)&st.x[wave][0][i * RPI][0],
-                                                 16, voff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rv, (__attribute__((address_space(3))) void*)&st.x[wave][1][i * RPI][0],
-                                                 16, voff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rg, (__attribute__((address_space(3))) void*)&st.x[wave][2][i * RPI][0],
-                                                 16, voff, 0, 0, 0);
-    }
+    stage_rows<TIn, L>(g.rk, st.x[wave][0], int64_t{wave} * L, c0, C, lane);
+    stage_rows<TIn, L>(g.rv, st.x[wave][1], int64_t{wave} * L, c0, C, lane);
+    stage_rows<TIn, L>(g.rg, st.x[wave][2], int64_t{wave} * L, c0, C, lane);
 }
 
 // A span's inputs, loaded ahead of use (gy holds the output gradient; with
@@ -687,10 +667,8 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
 // LDS by asynchronous buffer -> LDS copies (stage_span), and its saved state
 // into three registers, so the loads overlap the arithmetic without holding
 // a second block in registers.  Each wave copies and reads only its own span,
-// so the waits are per wave: vmcnt(0) before reading a block from LDS, and
-// lgkmcnt(0) after, before the next copy may overwrite it.  The copies reach
-// LDS without the compiler seeing them, hence the explicit waits, written as
-// asm statements that also order memory accesses.
+// so the waits are per wave: wait_staged() before reading a block from LDS,
+// and wait_lds_reads() after, before the next copy may overwrite it.
 template <typename TIn, int L, int W, bool Gated, bool Staged>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
     __shared__ BwdShared<W> sm;
@@ -721,12 +699,12 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
     for (int64_t blk = P.nblocks - 1; blk >= 0; --blk) {
         const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
         if constexpr (Staged) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_staged();
             cur.load_lds(stage, wave, lane);
             cur.a0 = nxt.a0;
             cur.b0 = nxt.b0;
             cur.s0 = nxt.s0;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            wait_lds_reads();
             if (blk > 0) {
                 const SpanGeo gn = span_geo<TIn, L, W>(P, b, c, cok, blk - 1, wave);
                 stage_span(stage, gn, wave, lane, c0, P.C);

@@ -101,6 +101,38 @@ __device__ __forceinline__ void buf_store(float v, Rsrc r, uint32_t voff, uint32
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, WKV_STORE_AUX);
 }
 
+// Asynchronous copy of one input's L token rows x 64 channels (rows row0..
+// of a buffer whose rows are C elements, channels c0..c0+63) into LDS laid out
+// [L][64].  Each lane moves 16 bytes (buffer_load ... lds); one instruction
+// fills 1 KB of LDS, and a lane's 16 bytes land at the instruction's LDS base
+// + 16 * lane, which is exactly the [token][channel] order.  Chunks at or past
+// channel C, or past the buffer's end, arrive as zeros.  Needs C * sizeof(TIn)
+// to be a multiple of 16 (no chunk straddles C) and a 16-byte-aligned buffer.
+// The copy is tracked by vmcnt only, not by the compiler: its consumer waits
+// explicitly before reading the LDS rows.
+template <typename TIn, int L>
+__device__ __forceinline__ void stage_rows(Rsrc r, TIn (*dst)[64], int64_t row0, int64_t c0, int64_t C, int lane) {
+    constexpr int ES = sizeof(TIn);
+    constexpr int LPR = 64 * ES / 16;  // lanes per row
+    constexpr int RPI = 64 / LPR;      // rows per instruction
+    static_assert(L % RPI == 0, "whole instructions of rows");
+    const int q = lane % LPR;
+    const bool ok = c0 + q * (16 / ES) < C;
+#pragma unroll
+    for (int i = 0; i < L / RPI; ++i) {
+        const int64_t j = row0 + i * RPI + lane / LPR;
+        const uint32_t voff = ok ? static_cast<uint32_t>((j * C + c0) * ES + q * 16) : kOffNone;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&dst[i * RPI][0], 16, voff,
+                                                 0, 0, 0);
+    }
+}
+
+// Waits on this wave's outstanding copies and loads (before reading staged
+// rows), and on its LDS reads (before a copy may overwrite them).  As asm
+// statements they also keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void wait_staged() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // One input over L tokens of a lane (token j at soffset j * row), held in
 // registers: bf16 values two to a register, float32 values one each.
 template <typename TIn, int L>
