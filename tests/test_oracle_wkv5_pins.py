@@ -1,0 +1,112 @@
+"""Pins for the RWKV-5 matrix-state oracle (oracle/wkv5_ref.py), by routes other
+than its recurrence: the history-sum form with library matrix products, the
+no-decay case as causal linear attention, the infinite-decay limit, the
+one-channel case through scipy's linear filter, an exact worked example,
+splitting a sequence through the state, and invariances."""
+import math
+
+import numpy as np
+import pytest
+from scipy.signal import lfilter
+
+from oracle import wkv5_direct_ref, wkv5_forward_ref
+
+
+def rand(B, T, H, N, seed, w_lo=-3.0, w_hi=1.0):
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(w_lo, w_hi, (H, N)))
+    u = rng.normal(0, 1, (H, N))
+    r, k, v = (rng.normal(0, 1, (B, T, H * N)) for _ in range(3))
+    S0 = rng.normal(0, 1, (B, H, N, N))
+    return w, u, r, k, v, S0
+
+
+@pytest.mark.parametrize("B,T,H,N", [(2, 13, 2, 4), (1, 1, 3, 2), (3, 30, 1, 8)])
+def test_recurrence_equals_history_sum(B, T, H, N):
+    w, u, r, k, v, S0 = rand(B, T, H, N, B + T + H + N)
+    o, _ = wkv5_forward_ref(w, u, r, k, v, H)
+    np.testing.assert_allclose(o, wkv5_direct_ref(w, u, r, k, v, H), rtol=1e-12, atol=1e-12)
+    o, _ = wkv5_forward_ref(w, u, r, k, v, H, S0)
+    np.testing.assert_allclose(o, wkv5_direct_ref(w, u, r, k, v, H, S0), rtol=1e-12, atol=1e-12)
+
+
+def test_no_decay_is_causal_linear_attention():
+    """w = 0, u = 1: o_t = sum_{s <= t} (r_t . k_s) v_s, per head, i.e. tril(R K^T) V."""
+    B, T, H, N = 2, 17, 3, 5
+    _, _, r, k, v, _ = rand(B, T, H, N, 1)
+    o, S = wkv5_forward_ref(np.zeros((H, N)), np.ones((H, N)), r, k, v, H)
+    for h in range(H):
+        sl = slice(h * N, (h + 1) * N)
+        for b in range(B):
+            att = np.tril(r[b, :, sl] @ k[b, :, sl].T)
+            np.testing.assert_allclose(o[b, :, sl], att @ v[b, :, sl], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(S[b, h], k[b, :, sl].T @ v[b, :, sl], rtol=1e-12, atol=1e-12)
+
+
+def test_infinite_decay_keeps_only_the_previous_token():
+    """e^{-w} = 0: the state before token t is k_{t-1}^T v_{t-1} alone."""
+    B, T, H, N = 1, 9, 2, 3
+    _, u, r, k, v, _ = rand(B, T, H, N, 2)
+    o, _ = wkv5_forward_ref(np.full((H, N), 1e4), u, r, k, v, H)
+    for h in range(H):
+        sl = slice(h * N, (h + 1) * N)
+        for t in range(T):
+            exp = (r[0, t, sl] * u[h] * k[0, t, sl]).sum() * v[0, t, sl]
+            if t > 0:
+                exp = exp + (r[0, t, sl] * k[0, t - 1, sl]).sum() * v[0, t - 1, sl]
+            np.testing.assert_allclose(o[0, t, sl], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_one_channel_heads_are_a_linear_filter():
+    """N = 1: s_t = e^{-w} s_{t-1} + k_t v_t (scipy's lfilter), o_t = r_t (s_{t-1} + u k_t v_t)."""
+    B, T, H, N = 2, 40, 3, 1
+    w, u, r, k, v, _ = rand(B, T, H, N, 3)
+    o, S = wkv5_forward_ref(w, u, r, k, v, H)
+    for b in range(B):
+        for h in range(H):
+            x = k[b, :, h] * v[b, :, h]
+            s = lfilter([1.0], [1.0, -math.exp(-w[h, 0])], x)
+            prev = np.concatenate([[0.0], s[:-1]])
+            np.testing.assert_allclose(o[b, :, h], r[b, :, h] * (prev + u[h, 0] * x), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(S[b, h, 0, 0], s[-1], rtol=1e-12)
+
+
+def test_worked_example():
+    # one head, N = 1, decay factor 1/2, u = 3; r = 1, k = (1, 2, 4), v = (1, 1, -1)
+    # o_0 = u k0 v0 = 3;  o_1 = k0 v0 + u k1 v1 = 1 + 6 = 7
+    # o_2 = (1/2) k0 v0 + k1 v1 + u k2 v2 = 0.5 + 2 - 12 = -9.5;  S_2 = 0.25 + 1 - 4 = -2.75
+    w = np.array([[math.log(2.0)]])
+    u = np.array([[3.0]])
+    r = np.ones((1, 3, 1))
+    k = np.array([1.0, 2.0, 4.0]).reshape(1, 3, 1)
+    v = np.array([1.0, 1.0, -1.0]).reshape(1, 3, 1)
+    o, S = wkv5_forward_ref(w, u, r, k, v, 1)
+    np.testing.assert_allclose(o[0, :, 0], [3.0, 7.0, -9.5], rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(S[0, 0, 0, 0], -2.75, rtol=1e-15)
+
+
+def test_split_sequence_through_the_state():
+    B, T, H, N = 2, 25, 2, 4
+    w, u, r, k, v, S0 = rand(B, T, H, N, 4)
+    whole, Sw = wkv5_forward_ref(w, u, r, k, v, H, S0)
+    for t1 in (1, 11, 24):
+        a, Sa = wkv5_forward_ref(w, u, r[:, :t1], k[:, :t1], v[:, :t1], H, S0)
+        b, Sb = wkv5_forward_ref(w, u, r[:, t1:], k[:, t1:], v[:, t1:], H, Sa)
+        np.testing.assert_allclose(np.concatenate([a, b], axis=1), whole, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(Sb, Sw, rtol=1e-12, atol=1e-12)
+
+
+def test_invariances():
+    B, T, H, N = 1, 12, 2, 3
+    w, u, r, k, v, _ = rand(B, T, H, N, 5)
+    o, _ = wkv5_forward_ref(w, u, r, k, v, H)
+    # linear in r and in v; bilinear scaling of k against v
+    np.testing.assert_allclose(wkv5_forward_ref(w, u, 2.5 * r, k, v, H)[0], 2.5 * o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(wkv5_forward_ref(w, u, r, 4.0 * k, 0.25 * v, H)[0], o, rtol=1e-12, atol=1e-12)
+    # heads are independent: head 1's inputs do not reach head 0's outputs
+    r2 = r.copy()
+    r2[:, :, N:] += 1.0
+    k2 = k.copy()
+    k2[:, :, N:] *= -3.0
+    o2, _ = wkv5_forward_ref(w, u, r2, k2, v, H)
+    np.testing.assert_array_equal(o2[:, :, :N], o[:, :, :N])
