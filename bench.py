@@ -21,7 +21,8 @@ started from a state and returning it, as wkv_forward_state), gated (the
 headline with the receptance gate fused: wkv_forward_gated +
 wkv_backward_gated), shift (the token-shift mix that feeds the r, k, v
 projections, wkv_token_shift + wkv_token_shift_backward, M=3 mixes at the
-headline shape in bf16), copy (a plain
+headline shape in bf16), wkv5 (the RWKV-5 matrix-state forward, wkv5_forward,
+at B=8 T=1024 as 64 heads of 64, bf16 r, k, v), copy (a plain
 1 GiB device-to-device copy: the calibration kernel for the FETCH_SIZE /
 WRITE_SIZE counters).
 """
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -396,6 +397,73 @@ def bench_shift(args):
     return out
 
 
+def bench_wkv5(args):
+    """RWKV-5 matrix-state forward at B=8 T=1024 C=4096 (64 heads of 64), bf16
+    r, k, v, float32 output and state, from the zero state, returning the
+    final state.  Algorithmic bytes per channel-token: r, k, v (3 x 2 B) in,
+    o (4 B) out; the final state adds 64 x 4 B per head and batch row."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops, workloads as W
+
+    dev = torch.device("cuda:0")
+    p = W.wkv5_config()
+    B, T, H = p.B, p.T, p.H
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    w, u = torch.from_numpy(p.w).to(dev), torch.from_numpy(p.u).to(dev)
+    base = [up(p.r_bits), up(p.k_bits), up(p.v_bits)]
+    sets = [[t if i == 0 else t.clone() for t in base] for i in range(max(args.sets, 3))]
+    outs = [torch.empty((B, T, 64 * H), device=dev) for _ in sets]
+    sts = [torch.empty((B, H, 64, 64), device=dev) for _ in sets]
+
+    def step(i):
+        r, k, v = sets[i % len(sets)]
+        ops.wkv5_forward(w, u, r, k, v, out=outs[i % len(sets)], state_out=sts[i % len(sets)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    st = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    n = B * T * 64 * H
+    alg = 10 * n + B * H * 64 * 64 * 4
+    achieved = alg / (st["mean"] * 1e-6) / 1e9
+    out = {
+        "metric": "RWKV-5 matrix-state WKV forward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
+        "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": p.name + " fwd", "B": B, "T": T, "H": H, "N": 64},
+        "call_us": {"wkv5_forward": st},
+        "roofline": {"bound": "hbm", "kernel": "wkv5_forward", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("wkv5_bf16_B8_T1024_H64", "wkv5_forward"),
+                     "alg_bytes_per_launch": alg},
+    }
+    if not args.no_cpu:
+        # the float64 numpy oracle on one batch row (all 64 heads, all tokens): 1/8 of the workload
+        from oracle import wkv5_forward_ref
+
+        t0 = time.perf_counter()
+        wkv5_forward_ref(p.w, p.u, p.r[:1], p.k[:1], p.v[:1], H)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": T * 64 * H / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"batch row 0 of the workload (all 64 heads x {T} tokens, "
+                                         f"{T * 64 * H} channel*tokens) through the float64 numpy oracle, "
+                                         f"{t_np:.2f} s"}
+    return out
+
+
 def bench_copy(args):
     """A plain copy of 1 GiB (reads 1 GiB, writes 1 GiB): HBM counter calibration."""
     import torch
@@ -432,8 +500,8 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy", "shift"):
-        out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift}[args.workload](args)
+    if args.workload in ("step5", "copy", "shift", "wkv5"):
+        out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

@@ -1,6 +1,7 @@
 /*
  * wkv.h - C ABI of the RWKV-4 WKV time-mixing operator for AMD MI355X (gfx950),
- * with the receptance gate and the token-shift mix around it.
+ * with the receptance gate and the token-shift mix around it, and the
+ * matrix-state WKV of RWKV-5.
  *
  * The operator, per channel c of each batch row b, tokens t = 1..T
  * ("RWKV（Receptance Weighted Key Value）概念", section 3.2; and
@@ -197,6 +198,39 @@ wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
                                 const float* w, const float* u, const void* k, const void* v, const void* r,
                                 const void* gout, float* dk, float* dv, float* dr, float* dw, float* du,
                                 const void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * wkv5_forward - the multi-head, matrix-state WKV of RWKV-5, forward.
+ *
+ * Defines ("RWKV模型深度研究报告（截至2026年初）", sections 1.3.2 and 1.3.3:
+ * version 5 carries a matrix-valued state per head whose update is a diagonal
+ * decay of the previous state plus a value-key outer product; the
+ * intelliparadigm.com post, section "2.1 WKV的数学表达与实现": channel groups
+ * with their own decay rates; the readout with receptance and the current
+ * token's bonus u follows RWKV-4, "RWKV（Receptance Weighted Key Value）概念",
+ * section 3.2), for each head h of size N = 64 (C = 64 H channels, head h
+ * owning channels 64h .. 64h + 63) and each batch row:
+ *     S_t = diag(e^{-w_h}) S_{t-1} + k_t^T v_t         (S: 64 x 64, key x value)
+ *     o_t = r_t (S_{t-1} + diag(u_h) k_t^T v_t)
+ * computed chunkwise (64 tokens per chunk) with bf16 matrix-core products and
+ * float32 accumulation and state.  Channels decaying faster than e^{-10} per
+ * token keep terms older than one token inside a 16-token block as if their
+ * rate were 10 (an error below e^{-10} of the token's own term).
+ *
+ * B, T, H   batch, tokens, heads (>= 0).  N  head size: must be 64.
+ * in_dtype  WKV_BF16 only (WKV_EDTYPE otherwise).
+ * w, u      [H, 64] float32: decay rates (decay factor e^{-w}) and bonus.
+ * r, k, v   [B, T, 64 H] bf16, 16-byte aligned.
+ * o         [B, T, 64 H] float32, fully overwritten.
+ * s_in      [B, H, 64, 64] float32 state before token 1 (key-major), or NULL
+ *           for the zero state.
+ * s_out     [B, H, 64, 64] float32 state after token T, or NULL; may be s_in
+ *           (updated in place).  With T == 0 it receives s_in (or zeros).
+ * Errors as the other entry points (WKV_EINVAL also for N != 64).
+ */
+wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
+                          const float* w, const float* u, const void* r, const void* k, const void* v,
+                          float* o, const float* s_in, float* s_out, void* hip_stream);
 
 /*
  * wkv_token_shift / wkv_token_shift_backward - the token-shift mix that

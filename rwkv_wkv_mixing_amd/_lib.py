@@ -26,6 +26,7 @@ EXPORTS = (
     "wkv_forward_gated",
     "wkv_backward_gated",
     "wkv_step",
+    "wkv5_forward",
     "wkv_token_shift_workspace_bytes",
     "wkv_token_shift",
     "wkv_token_shift_backward",
@@ -79,6 +80,8 @@ def declare(L):
     L.wkv_backward_gated.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_step.restype = i32
     L.wkv_step.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, vp]
+    L.wkv5_forward.restype = i32
+    L.wkv5_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp]
     L.wkv_token_shift_workspace_bytes.restype = sz
     L.wkv_token_shift_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.wkv_token_shift.restype = i32

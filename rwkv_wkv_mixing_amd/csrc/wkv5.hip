@@ -1,0 +1,303 @@
+// Multi-head matrix-state WKV (RWKV-5), chunkwise-parallel forward on MFMA.
+//
+// Per head (N = 64 channels; "RWKV模型深度研究报告", sections 1.3.2 and 1.3.3:
+// a matrix-valued state with per-channel decay, updated by a diagonal decay
+// and a value-key outer product; the intelliparadigm.com post, section 2.1:
+// channel groups with their own decay rates):
+//     S_t = diag(e^{-w}) S_{t-1} + k_t^T v_t                  (S: key x value)
+//     o_t = r_t (S_{t-1} + diag(u) k_t^T v_t)
+// Chunkwise-parallel form ("RWKV模型深度研究报告", section 1.4.1): a chunk of
+// 64 tokens t0 + tau, tau < 64, starting from the state S0, gives
+//     o_tau = (r_tau . e^{-w tau}) S0                               (inter)
+//           + sum_{sig < tau} (sum_i r_tau,i k_sig,i e^{-w_i (tau-1-sig)}) v_sig
+//           + (sum_i r_tau,i u_i k_tau,i) v_tau                     (intra)
+//     S_end = diag(e^{-w n}) S0 + sum_{sig < n} diag(e^{-w (n-1-sig)}) k_sig^T v_sig
+// with n the chunk's token count.  Every product above is a 64 x 64 x 64 (or
+// smaller) matrix product: bf16 operands on v_mfma_f32_16x16x16_bf16, float32
+// accumulation.  The decay factors are split so that no operand exceeds its
+// inputs: between 16-token blocks P > Q the factor e^{-w (tau-1-sig)} is
+// e^{-w (tau-p0)} e^{-w (p0-1-sig)} with p0 the first token of block P (both
+// <= 1); inside a diagonal block it is e^{-w (tau-c)} e^{w (sig+1-c)} about
+// the block's middle c, with w capped at kWCap there so that neither factor
+// exceeds e^{80} (a channel decaying by more than e^{-10} per token then keeps
+// its older in-block terms at most e^{-10} of the token's own term too large).
+//
+// One workgroup of four waves per (batch row, head) walks the chunks in order.
+// Wave w owns key rows 16w..16w+15 of the state (four 16 x 16 accumulator
+// tiles, float32) and output tokens 16w..16w+15 of each chunk.  The next
+// chunk's r, k, v stream into LDS by asynchronous buffer -> LDS copies while
+// the current one is computed; the state crosses the waves through LDS as
+// bf16, transposed, for the inter-chunk product.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wkv_device.h"
+#include "wkv_launch.h"
+#include "wkv_scan.h"
+
+namespace wkv {
+namespace {
+
+constexpr int kN = 64;       // head size
+constexpr int kLc = 64;      // tokens per chunk
+constexpr int kWaves5 = 4;   // 16 tokens / key rows per wave
+constexpr float kWCap = 10.f;
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+struct Wkv5Shared {
+    uint16_t in[2][3][kLc][kN];  // staged r, k, v of a chunk, [token][channel], two chunks
+    uint16_t st[kN][kN];         // state before the chunk, bf16, [value][key]
+    float pw[kLc + 1][kN];       // e^{-w n}, n = 0..64
+    float pe[17][kN];            // e^{w' m}, m = -8..8, w' = min(w, kWCap)
+    float uu[kN];
+};
+
+__device__ __forceinline__ f4 mfma(s4 a, s4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0); }
+
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+    const f2 p = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf2));
+}
+
+__device__ __forceinline__ s4 pack4(float a, float b, float c, float d) {
+    const uint32_t lo = pk2(a, b), hi = pk2(c, d);
+    s4 r;
+    r[0] = static_cast<short>(lo & 0xffffu);
+    r[1] = static_cast<short>(lo >> 16);
+    r[2] = static_cast<short>(hi & 0xffffu);
+    r[3] = static_cast<short>(hi >> 16);
+    return r;
+}
+
+__device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
+// four consecutive bf16 of an LDS row, widened
+__device__ __forceinline__ f4 row4(const uint16_t* p) {
+    const u16x4 x = *reinterpret_cast<const u16x4*>(p);
+    return f4{bf(x[0]), bf(x[1]), bf(x[2]), bf(x[3])};
+}
+
+__device__ __forceinline__ f4 frow4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+__device__ __forceinline__ s4 mul_pack(f4 x, f4 f) { return pack4(x[0] * f[0], x[1] * f[1], x[2] * f[2], x[3] * f[3]); }
+
+__device__ __forceinline__ s4 as_s4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
+    s4 r;
+    r[0] = static_cast<short>(a);
+    r[1] = static_cast<short>(b);
+    r[2] = static_cast<short>(c);
+    r[3] = static_cast<short>(d);
+    return r;
+}
+
+__global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
+    __shared__ Wkv5Shared sm;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, g = lane >> 4;  // MFMA lane coordinates: row/column l16, k-group g
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / P.H, h = bh - b * P.H;
+    const int64_t C = P.H * kN;
+    const int64_t nch = (P.T + kLc - 1) / kLc;
+
+    // tables of the head's decay powers and bonus
+    for (int q = threadIdx.x; q < (kLc + 1) * kN; q += 64 * kWaves5) {
+        const int n = q / kN, i = q % kN;
+        sm.pw[n][i] = ex2(-P.w[h * kN + i] * static_cast<float>(n) * kL2E);
+    }
+    for (int q = threadIdx.x; q < 17 * kN; q += 64 * kWaves5) {
+        const int m = q / kN - 8, i = q % kN;
+        sm.pe[m + 8][i] = ex2(fminf(P.w[h * kN + i], kWCap) * static_cast<float>(m) * kL2E);
+    }
+    if (threadIdx.x < kN) sm.uu[threadIdx.x] = P.u[h * kN + threadIdx.x];
+
+    // the state: wave wv, tile J, lane (l16, g), element e holds S[16 wv + 4 g + e][16 J + l16]
+    f4 S[4];
+    const int64_t sbase = bh * kN * kN;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[J][e] = P.s_in != nullptr ? P.s_in[sbase + (16 * wv + 4 * g + e) * kN + 16 * J + l16] : 0.f;
+
+    // the rows of head h, batch row b, chunk ch as a buffer: [token][C] bf16, head offset h*64
+    auto chunk_rsrc = [&](const uint16_t* base, int64_t ch) {
+        const int64_t t0 = ch * kLc;
+        const int64_t n = (P.T - t0) < kLc ? (P.T - t0) : kLc;
+        return make_rsrc(base + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((n - 1) * C + kN) * 2));
+    };
+    auto stage = [&](int64_t ch, int buf) {  // wave wv copies rows 16 wv .. 16 wv + 15 of r, k, v
+        const uint16_t* src[3] = {P.r, P.k, P.v};
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            const Rsrc rs = chunk_rsrc(src[a], ch);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = 16 * wv + 8 * i + lane / 8;
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + (lane % 8) * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, 0);
+            }
+        }
+    };
+    auto put_state = [&]() {  // bf16, transposed: st[value][key]
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const uint32_t lo = pk2(S[J][0], S[J][1]), hi = pk2(S[J][2], S[J][3]);
+            uint32_t* p = reinterpret_cast<uint32_t*>(&sm.st[16 * J + l16][16 * wv + 4 * g]);
+            p[0] = lo;
+            p[1] = hi;
+        }
+    };
+
+    stage(0, 0);
+    put_state();
+    const int P0 = 16 * wv;  // first token of this wave's output block, chunk-relative
+
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        const int buf = static_cast<int>(ch & 1);
+        const int64_t t0 = ch * kLc;
+        const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
+        wait_staged();
+        lds_sync();  // this chunk's inputs, the tables and the state are in LDS for every wave
+        if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
+
+        const uint16_t(*R)[kN] = sm.in[buf][0];
+        const uint16_t(*K)[kN] = sm.in[buf][1];
+        const uint16_t(*V)[kN] = sm.in[buf][2];
+        const int tau = P0 + l16;  // this lane's output token (as the m / n index of the products)
+
+        // ---- inter-chunk: O[J] = sum_I (r . e^{-w tau}) S0 --------------------------
+        f4 O[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) O[J] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int c4 = 16 * I + 4 * g;
+            const s4 a = mul_pack(row4(&R[tau][c4]), frow4(&sm.pw[tau][c4]));
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const uint16_t* sp = &sm.st[16 * J + l16][c4];
+                O[J] = mfma(a, as_s4(sp[0], sp[1], sp[2], sp[3]), O[J]);
+            }
+        }
+
+        // ---- values as B operands: Vb[Q][J] holds V[16 Q + 4 g + e][16 J + l16] -------
+        s4 Vb[4][4];
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const int s0 = 16 * Q + 4 * g, j = 16 * J + l16;
+                Vb[Q][J] = as_s4(V[s0][j], V[s0 + 1][j], V[s0 + 2][j], V[s0 + 3][j]);
+            }
+
+        // ---- intra-chunk attention, transposed: At[sig][tau], lane holds
+        //      A[tau = P0 + l16][sig = 16 Q + 4 g + e] (the A operand of A V) -----------
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) {
+            if (Q > wv) break;
+            f4 At = {0.f, 0.f, 0.f, 0.f};
+            const int sig = 16 * Q + l16;  // this lane's key token (m index of K~)
+            if (Q < wv) {  // factors about p0 = P0: e^{-w (tau - p0)}, e^{-w (p0 - 1 - sig)}
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int c4 = 16 * I + 4 * g;
+                    const s4 ka = mul_pack(row4(&K[sig][c4]), frow4(&sm.pw[P0 - 1 - sig][c4]));
+                    const s4 rb = mul_pack(row4(&R[tau][c4]), frow4(&sm.pw[tau - P0][c4]));
+                    At = mfma(ka, rb, At);
+                }
+            } else {  // diagonal block: about c = P0 + 8, w capped; then the bonus on the diagonal
+                f4 Bn = {0.f, 0.f, 0.f, 0.f};
+                const int mid = P0 + 8;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int c4 = 16 * I + 4 * g;
+                    const f4 kr = row4(&K[sig][c4]), rr = row4(&R[tau][c4]);
+                    const s4 ka = mul_pack(kr, frow4(&sm.pe[sig + 1 - mid + 8][c4]));
+                    const s4 rb = mul_pack(rr, frow4(&sm.pe[mid - tau + 8][c4]));
+                    At = mfma(ka, rb, At);
+                    const s4 kp = pack4(kr[0], kr[1], kr[2], kr[3]);
+                    const s4 ru = mul_pack(rr, frow4(&sm.uu[c4]));
+                    Bn = mfma(kp, ru, Bn);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {  // lane holds (sig_local = 4 g + e, tau_local = l16)
+                    const int sl = 4 * g + e;
+                    At[e] = sl < l16 ? At[e] : (sl == l16 ? Bn[e] : 0.f);
+                }
+            }
+            const s4 a = pack4(At[0], At[1], At[2], At[3]);
+#pragma unroll
+            for (int J = 0; J < 4; ++J) O[J] = mfma(a, Vb[Q][J], O[J]);
+        }
+        lds_sync();  // every wave has read the state before it is overwritten
+
+        // ---- state update: S = diag(e^{-w nv}) S + sum_sig (k_sig e^{-w (nv-1-sig)})^T v_sig
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float dn = sm.pw[nv][16 * wv + 4 * g + e];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) S[J][e] *= dn;
+        }
+        const int key = 16 * wv + l16;  // m index of K^T
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) {
+            float kk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * Q + 4 * g + e;
+                const int n = nv - 1 - s;
+                kk[e] = n >= 0 ? bf(K[s][key]) * sm.pw[n >= 0 ? n : 0][key] : 0.f;  // tokens past the chunk's end: 0
+            }
+            const s4 a = pack4(kk[0], kk[1], kk[2], kk[3]);
+#pragma unroll
+            for (int J = 0; J < 4; ++J) S[J] = mfma(a, Vb[Q][J], S[J]);
+        }
+        put_state();
+
+        // ---- outputs: lane holds O[tau = P0 + 4 g + e][16 J + l16] ---------------------
+        const Rsrc ro = make_rsrc(P.o + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t off = static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4);
+                buf_store(O[J][e], ro, off, 0);
+            }
+    }
+
+    if (P.s_out != nullptr) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P.s_out[sbase + (16 * wv + 4 * g + e) * kN + 16 * J + l16] = S[J][e];
+    }
+}
+
+// T == 0: the state after the sequence is the state before it (or zero).
+__global__ void wkv5_state_copy_kernel(const float* s_in, float* s_out, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) s_out[i] = s_in != nullptr ? s_in[i] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hipStream_t stream) {
+    if (n <= 0 || s_out == nullptr || s_in == s_out) return hipSuccess;
+    hipLaunchKernelGGL(wkv5_state_copy_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       s_in, s_out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream) {
+    hipLaunchKernelGGL(wkv5_fwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace wkv

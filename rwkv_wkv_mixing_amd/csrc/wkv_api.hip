@@ -232,6 +232,30 @@ wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype, const float
     return hip_status(wkv::launch_step(s, static_cast<hipStream_t>(hip_stream)));
 }
 
+wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
+                          const float* u, const void* r, const void* k, const void* v, float* o,
+                          const float* s_in, float* s_out, void* hip_stream) {
+    if (B < 0 || T < 0 || H < 0 || N != 64) return WKV_EINVAL;
+    if (!dtype_ok(in_dtype)) return WKV_EDTYPE;
+    if (in_dtype != WKV_BF16) return WKV_EDTYPE;  // the products run on bf16 operands
+    int64_t n, bytes, bh, ns;
+    if (!mul3(B, T, H, &n) || __builtin_mul_overflow(n, int64_t{64 * 4}, &bytes)) return WKV_ESIZE;
+    if (__builtin_mul_overflow(B, H, &bh) || bh >= (int64_t{1} << 31)) return WKV_ESIZE;
+    if (__builtin_mul_overflow(bh, int64_t{64 * 64}, &ns)) return WKV_ESIZE;
+    // one chunk's rows must fit a buffer resource: 64 rows of C = 64 H float32
+    if (H > 0 && 64 * 64 * H * 4 >= (int64_t{1} << 32)) return WKV_ESIZE;
+    if (bh == 0) return WKV_OK;
+    if ((s_in && !aligned(s_in, 4)) || (s_out && !aligned(s_out, 4))) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (T == 0) return hip_status(wkv::launch_wkv5_state_copy(s_in, s_out, ns, stream));
+    if (!w || !u || !r || !k || !v || !o) return WKV_EINVAL;
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return WKV_EALIGN;
+    wkv::Wkv5Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
+                    static_cast<const uint16_t*>(v), o, s_in, s_out};
+    return hip_status(wkv::launch_wkv5_fwd(a, stream));
+}
+
 size_t wkv_token_shift_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {
     const ShiftPlan p = shift_plan(B, T, C, M, WKV_F32);
     return p.st == WKV_OK ? p.ws_bytes : 0;

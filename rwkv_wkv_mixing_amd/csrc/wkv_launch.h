@@ -85,6 +85,18 @@ struct ShiftArgs {
     float* ws;             // backward: shift_partial_rows(B, T) * M * C floats
 };
 
+struct Wkv5Args {
+    int64_t B, T, H;     // head size 64; C = 64 H
+    const float* w;      // [H, 64] decay rates
+    const float* u;      // [H, 64] bonus
+    const uint16_t* r;   // [B, T, C] bf16, 16-byte aligned
+    const uint16_t* k;
+    const uint16_t* v;
+    float* o;            // [B, T, C]
+    const float* s_in;   // [B, H, 64, 64] or NULL (zero state)
+    float* s_out;        // [B, H, 64, 64] or NULL
+};
+
 // chunked forward (wkv_fwd.hip)
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t stream);
 // T == 0 with a state: the output state is the input state (or the empty one)
@@ -101,6 +113,10 @@ hipError_t launch_shift_bwd(const ShiftArgs& a, hipStream_t stream);
 hipError_t launch_shift_zero(float* p, int64_t n, hipStream_t stream);
 int64_t shift_partial_rows(int64_t B, int64_t T);
 int shift_vector_width(bool bf16, bool bwd);
+
+// RWKV-5 matrix-state forward (wkv5.hip)
+hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream);
+hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hipStream_t stream);
 
 // decode step (wkv_step.hip)
 hipError_t launch_step(const StepArgs& s, hipStream_t stream);

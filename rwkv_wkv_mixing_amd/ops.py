@@ -306,3 +306,34 @@ class TokenShiftFunction(torch.autograd.Function):
 def token_shift_mix(mu, x, x_prev=None):
     """Differentiable token_shift (see TokenShiftFunction)."""
     return TokenShiftFunction.apply(mu, x, x_prev)
+
+
+def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None):
+    """RWKV-5 matrix-state WKV: o [B, T, C] float32 from w, u [H, 64] float32 and
+    r, k, v [B, T, C] bfloat16 (C = 64 H).  state_in: [B, H, 64, 64] float32 or
+    None (zero).  state_out: tensor to receive the final state (may be
+    state_in); with return_state and no state_out one is allocated and the
+    call returns (o, state)."""
+    _need(r, "r", torch.bfloat16)
+    dev = r.device
+    B, T, C = r.shape
+    H = w.shape[0] if w.dim() == 2 else C // 64
+    if C != 64 * H:
+        raise ValueError(f"C = {C} is not 64 * H with H = {H}")
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, (B, T, C), dev)
+    _need(w, "w", torch.float32, (H, 64), dev)
+    _need(u, "u", torch.float32, (H, 64), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, T, C), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, 64, 64), dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (B, H, 64, 64), dev)
+    st = L.lib().wkv5_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
+                              _p(state_out), _stream(dev))
+    L.check("wkv5_forward", st)
+    return (out, state_out) if return_state else out

@@ -274,3 +274,45 @@ def shift_config(seed=0) -> ShiftProblem:
     training workload's size: B=8, T=1024, C=4096."""
     return make_shift(8, 1024, 4096, 3, dtype=BF16, seed=seed, with_prev=False,
                       name="token shift bf16 B=8 T=1024 C=4096 M=3")
+
+
+@dataclass
+class Wkv5Problem:
+    """Inputs of the RWKV-5 matrix-state WKV: w, u [H, 64] float32, r, k, v
+    [B, T, 64 H] (float32 values exactly representable in bf16, with their
+    bf16 encodings in ``*_bits``), optional state S0 [B, H, 64, 64]."""
+
+    name: str
+    B: int
+    T: int
+    H: int
+    w: np.ndarray
+    u: np.ndarray
+    r: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    r_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    S0: np.ndarray | None = None
+
+
+def make_wkv5(B, T, H, *, seed=0, w_range=(-4.0, 1.5), kv_std=1.0, with_state=False, name="") -> Wkv5Problem:
+    """Draw order: w = exp(U(lo, hi)) per (head, key channel), u ~ N(0, 1),
+    r, k, v ~ N(0, kv_std) rounded to bf16, then (if wanted) S0 ~ N(0, 1).
+    The rate range gives decay factors from e^{-e^{1.5}} = 0.011 to
+    e^{-e^{-4}} = 0.98 per token."""
+    rng = np.random.default_rng(seed)
+    N = 64
+    w = np.exp(rng.uniform(w_range[0], w_range[1], (H, N))).astype(np.float32)
+    u = _normal(rng, 1.0, (H, N))
+    r_bits, r = bf16_round(_normal(rng, kv_std, (B, T, H * N)))
+    k_bits, k = bf16_round(_normal(rng, kv_std, (B, T, H * N)))
+    v_bits, v = bf16_round(_normal(rng, kv_std, (B, T, H * N)))
+    S0 = _normal(rng, 1.0, (B, H, N, N)) if with_state else None
+    return Wkv5Problem(name or f"wkv5 B={B} T={T} H={H}", B, T, H, w, u, r, k, v, r_bits, k_bits, v_bits, S0)
+
+
+def wkv5_config(seed=0) -> Wkv5Problem:
+    """A 7B-shaped layer in RWKV-5 form: B=8, T=1024, C=4096 as 64 heads of 64."""
+    return make_wkv5(8, 1024, 64, seed=seed, name="wkv5 bf16 B=8 T=1024 H=64 N=64")

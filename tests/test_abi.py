@@ -25,7 +25,7 @@ def lib():
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(wkv_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(wkv[0-9]*_[a-z_0-9]+)\s*\(", src, flags=re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -208,3 +208,23 @@ def test_token_shift_validation(lib):
     assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, *args, ws=x, nws=need - 1) == L.WKV_EWORKSPACE
     assert shift_bwd(lib, 1, 4, 4, 3, L.WKV_F32, *args, ws=x + 16, nws=need) == L.WKV_EWORKSPACE
     assert shift_bwd(lib, 1, 4, 0, 3, L.WKV_F32, *[None] * 7) == L.WKV_OK
+
+
+def wkv5(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None):
+    return lib.wkv5_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), None)
+
+
+def test_wkv5_validation(lib):
+    x = A16
+    args = [x] * 6
+    assert wkv5(lib, 1, 4, 2, 32, L.WKV_BF16, *args) == L.WKV_EINVAL      # head size must be 64
+    assert wkv5(lib, -1, 4, 2, 64, L.WKV_BF16, *args) == L.WKV_EINVAL
+    assert wkv5(lib, 1, 4, 2, 64, L.WKV_F32, *args) == L.WKV_EDTYPE       # bf16 operands only
+    assert wkv5(lib, 1, 4, 2, 64, 7, *args) == L.WKV_EDTYPE
+    assert wkv5(lib, 1 << 30, 1 << 30, 1 << 10, 64, L.WKV_BF16, *args) == L.WKV_ESIZE
+    assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, None, x, x, x) == L.WKV_EINVAL
+    assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x + 2, x, x, x) == L.WKV_EALIGN   # r, k, v 16-byte aligned
+    assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x, x, x, x + 2) == L.WKV_EALIGN
+    assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, *args, si=x + 1) == L.WKV_EALIGN
+    assert wkv5(lib, 0, 4, 2, 64, L.WKV_BF16, *[None] * 6) == L.WKV_OK
+    assert wkv5(lib, 2, 4, 0, 64, L.WKV_BF16, *[None] * 6) == L.WKV_OK

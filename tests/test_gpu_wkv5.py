@@ -1,0 +1,150 @@
+"""GPU parity of the RWKV-5 matrix-state WKV (wkv5_forward) against the float64
+oracle, through the C ABI.
+
+Bound, from the arithmetic of the kernel (bf16 matrix-core operands, float32
+accumulation and state; ub = 2^-8 is the unit roundoff of bf16, whose 8
+significant bits round to nearest within 2^-8 relative): every term of an
+output passes through at most three bf16 roundings (the decay-scaled
+receptance, the decay-scaled key or the bf16 copy of the state, and the
+attention entry), so
+    |o_gpu - o| <= (3 ub (1 + 2^-7) + 2^-17) * o_abs,
+with o_abs the oracle run on |r|, |k|, |v|, |u|, |S0| (every term made
+non-negative: the sum of the terms' magnitudes); 2^-17 covers float32
+accumulation over at most a few hundred terms per stage.  The final state's
+terms pass through one rounding (the scaled key): (ub (1 + 2^-7) + 2^-17) S_abs.
+A dropped term, a wrong decay exponent or a transposed operand exceeds these
+bounds by orders of magnitude (the bounds are ~1.2 % of the magnitudes summed).
+"""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import to_dev
+from oracle import wkv5_forward_ref
+from rwkv_wkv_mixing_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+UB = 2.0 ** -8
+C_O = 3 * UB * (1 + 2.0 ** -7) + 2.0 ** -17
+C_S = UB * (1 + 2.0 ** -7) + 2.0 ** -17
+
+
+def ops():
+    from rwkv_wkv_mixing_amd import ops as O
+
+    return O
+
+
+def check_bound(name, got, ref, bound):
+    g = np.asarray(got, dtype=np.float64)
+    o = np.asarray(ref, dtype=np.float64)
+    assert g.shape == o.shape, (name, g.shape, o.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    err = np.abs(g - o)
+    ratio = err / (np.asarray(bound, dtype=np.float64) + 1e-30)
+    worst = float(ratio.max(initial=0.0))
+    print(f"  {name}: max_abs={float(err.max(initial=0.0)):.3e} worst_err/bound={worst:.3f}", flush=True)
+    if worst > 1.0:
+        idx = np.unravel_index(np.argmax(ratio), ratio.shape)
+        raise AssertionError(f"{name}: {int((ratio > 1).sum())} of {ratio.size} out of bound; worst at {idx}: "
+                             f"got {g[idx]!r} ref {o[idx]!r} bound {np.asarray(bound)[idx]!r}")
+
+
+def dev_inputs(p):
+    bt = lambda bits: to_dev(None, DEV, bits)
+    d = dict(w=to_dev(p.w, DEV), u=to_dev(p.u, DEV), r=bt(p.r_bits), k=bt(p.k_bits), v=bt(p.v_bits))
+    d["S0"] = None if p.S0 is None else to_dev(p.S0, DEV)
+    return d
+
+
+def check(p, o, S, S0=None, name=None):
+    S0 = p.S0 if S0 is None else S0
+    ref_o, ref_S = wkv5_forward_ref(p.w, p.u, p.r, p.k, p.v, p.H, S0)
+    abs_o, abs_S = wkv5_forward_ref(p.w, np.abs(p.u), np.abs(p.r), np.abs(p.k), np.abs(p.v), p.H,
+                                    None if S0 is None else np.abs(S0))
+    name = name or p.name
+    check_bound(f"{name} o", o.cpu().numpy(), ref_o, C_O * abs_o)
+    if S is not None:
+        check_bound(f"{name} state", S.cpu().numpy(), ref_S, C_S * abs_S)
+
+
+SHAPES = [(2, 1, 1), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_shapes(B, T, H, with_state):
+    """Whole and ragged chunks of 64 tokens, one to several heads, from the zero
+    state and from a given one."""
+    p = W.make_wkv5(B, T, H, seed=B * 100 + T + H, with_state=with_state)
+    print(f"case {p.name} state={with_state}", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S)
+
+
+@pytest.mark.parametrize("rates", [(20.0, 80.0), (1e-6, 1e-3), (8.0, 12.0)])
+def test_extreme_decay_rates(rates):
+    """Decay factors from e^{-80} (every older term vanishes) to nearly 1, and
+    around the in-block cap of 10."""
+    p = W.make_wkv5(2, 150, 2, seed=7, with_state=True)
+    p.w[:] = np.exp(np.random.default_rng(8).uniform(np.log(rates[0]), np.log(rates[1]), p.w.shape)).astype(np.float32)
+    print(f"case rates {rates}", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name=f"rates {rates}")
+
+
+def test_split_sequence_through_the_state():
+    p = W.make_wkv5(2, 300, 2, seed=9)
+    print(f"case split {p.name}", flush=True)
+    d = dev_inputs(p)
+    O = ops()
+    for t1 in (1, 64, 100):
+        sl = lambda x, a, b: x[:, a:b].contiguous()
+        o1, S1 = O.wkv5_forward(d["w"], d["u"], sl(d["r"], 0, t1), sl(d["k"], 0, t1), sl(d["v"], 0, t1),
+                                return_state=True)
+        o2, S2 = O.wkv5_forward(d["w"], d["u"], sl(d["r"], t1, 300), sl(d["k"], t1, 300), sl(d["v"], t1, 300),
+                                state_in=S1, state_out=S1, return_state=True)
+        torch.cuda.synchronize()
+        check(p, torch.cat([o1, o2], dim=1), S2, name=f"split at {t1}")
+
+
+def test_zero_length_and_determinism():
+    p = W.make_wkv5(2, 130, 3, seed=10, with_state=True)
+    d = dev_inputs(p)
+    O = ops()
+    z = torch.zeros((2, 0, 192), dtype=torch.bfloat16, device=DEV)
+    S = torch.full((2, 3, 64, 64), 9.0, device=DEV)
+    O.wkv5_forward(d["w"], d["u"], z, z, z, state_in=d["S0"], state_out=S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["S0"])
+    O.wkv5_forward(d["w"], d["u"], z, z, z, state_out=S)
+    torch.cuda.synchronize()
+    assert torch.all(S == 0)
+    a = O.wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    b = O.wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_bench_shape_sampled():
+    """The 7B-shaped layer (B=8, T=1024, 64 heads of 64) in the launch the bench
+    times; heads and batch rows are independent, so the oracle checks a sample
+    of (batch row, head) pairs over the whole sequence."""
+    p = W.wkv5_config()
+    print(f"case {p.name}", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], return_state=True)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    S = S.cpu().numpy()
+    for b, h in ((0, 0), (3, 17), (7, 63)):
+        cs = slice(64 * h, 64 * (h + 1))
+        q = W.Wkv5Problem(f"bench b={b} h={h}", 1, p.T, 1, p.w[h:h + 1], p.u[h:h + 1], p.r[b:b + 1, :, cs],
+                          p.k[b:b + 1, :, cs], p.v[b:b + 1, :, cs], None, None, None)
+        check(q, torch.from_numpy(o[b:b + 1, :, cs]), torch.from_numpy(S[b:b + 1, h:h + 1]))
