@@ -27,7 +27,9 @@
 // tiles, float32) and output tokens 16w..16w+15 of each chunk.  The next
 // chunk's r, k, v stream into LDS by asynchronous buffer -> LDS copies while
 // the current one is computed; the state crosses the waves through LDS as
-// bf16, transposed, for the inter-chunk product.
+// bf16, transposed, for the inter-chunk product.  Two barriers per chunk: one
+// before the chunk's inputs and state are read, one before the state in LDS
+// is overwritten.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,13 +51,24 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
+// LDS rows are read one row per lane (16 lanes at a time), so rows that are a
+// multiple of the bank span would put all 16 reads in the same banks.  The
+// tables and the state are padded by 16 bytes a row; the staged inputs, whose
+// rows the buffer -> LDS copies write back to back, are swizzled instead: the
+// 16-byte chunk q of row t sits in slot q ^ (t & 7) (see sw()).
+constexpr int kPadF = kN + 4;  // float rows
+constexpr int kPadH = kN + 8;  // bf16 rows
+
 struct Wkv5Shared {
-    uint16_t in[2][3][kLc][kN];  // staged r, k, v of a chunk, [token][channel], two chunks
-    uint16_t st[kN][kN];         // state before the chunk, bf16, [value][key]
-    float pw[kLc + 1][kN];       // e^{-w n}, n = 0..64
-    float pe[17][kN];            // e^{w' m}, m = -8..8, w' = min(w, kWCap)
+    uint16_t in[2][3][kLc][kN];  // staged r, k, v of a chunk, [token][swizzled channel], two chunks
+    uint16_t st[kN][kPadH];      // state before the chunk, bf16, [value][key]
+    float pw[kLc + 1][kPadF];    // e^{-w n}, n = 0..64
+    float pe[17][kPadF];         // e^{w' m}, m = -8..8, w' = min(w, kWCap)
     float uu[kN];
 };
+
+// position of channel c in swizzled row t of a staged input
+__device__ __forceinline__ int sw(int t, int c) { return (((c >> 3) ^ (t & 7)) << 3) | (c & 7); }
 
 __device__ __forceinline__ f4 mfma(s4 a, s4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0); }
 
@@ -64,14 +77,11 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf2));
 }
 
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ s4 pack4(float a, float b, float c, float d) {
-    const uint32_t lo = pk2(a, b), hi = pk2(c, d);
-    s4 r;
-    r[0] = static_cast<short>(lo & 0xffffu);
-    r[1] = static_cast<short>(lo >> 16);
-    r[2] = static_cast<short>(hi & 0xffffu);
-    r[3] = static_cast<short>(hi >> 16);
-    return r;
+    const u2 x = {pk2(a, b), pk2(c, d)};
+    return __builtin_bit_cast(s4, x);
 }
 
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
@@ -87,15 +97,14 @@ __device__ __forceinline__ f4 frow4(const float* p) { return *reinterpret_cast<c
 __device__ __forceinline__ s4 mul_pack(f4 x, f4 f) { return pack4(x[0] * f[0], x[1] * f[1], x[2] * f[2], x[3] * f[3]); }
 
 __device__ __forceinline__ s4 as_s4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
-    s4 r;
-    r[0] = static_cast<short>(a);
-    r[1] = static_cast<short>(b);
-    r[2] = static_cast<short>(c);
-    r[3] = static_cast<short>(d);
-    return r;
+    const u16x4 x = {a, b, c, d};
+    return __builtin_bit_cast(s4, x);
 }
 
-__global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
+// four consecutive bf16 of an LDS row as an MFMA operand, unchanged
+__device__ __forceinline__ s4 raw4(const uint16_t* p) { return __builtin_bit_cast(s4, *reinterpret_cast<const u16x4*>(p)); }
+
+__global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     __shared__ Wkv5Shared sm;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -139,7 +148,8 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int row = 16 * wv + 8 * i + lane / 8;
-                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + (lane % 8) * 16);
+                const int q = (lane % 8) ^ (row & 7);  // the global chunk that lands in slot lane % 8
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, 0);
             }
@@ -157,13 +167,16 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
 
     stage(0, 0);
     put_state();
+    wait_staged();
     const int P0 = 16 * wv;  // first token of this wave's output block, chunk-relative
 
+    // Each wave confirms its copy of chunk ch + 1 (issued at the start of chunk
+    // ch) just before storing chunk ch's outputs, so the barrier that opens a
+    // chunk needs no memory wait and the stores drain during the next chunk.
     for (int64_t ch = 0; ch < nch; ++ch) {
         const int buf = static_cast<int>(ch & 1);
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
-        wait_staged();
         lds_sync();  // this chunk's inputs, the tables and the state are in LDS for every wave
         if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
 
@@ -179,11 +192,10 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const int c4 = 16 * I + 4 * g;
-            const s4 a = mul_pack(row4(&R[tau][c4]), frow4(&sm.pw[tau][c4]));
+            const s4 a = mul_pack(row4(&R[tau][sw(tau, c4)]), frow4(&sm.pw[tau][c4]));
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                const uint16_t* sp = &sm.st[16 * J + l16][c4];
-                O[J] = mfma(a, as_s4(sp[0], sp[1], sp[2], sp[3]), O[J]);
+                O[J] = mfma(a, raw4(&sm.st[16 * J + l16][c4]), O[J]);
             }
         }
 
@@ -194,11 +206,18 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 const int s0 = 16 * Q + 4 * g, j = 16 * J + l16;
-                Vb[Q][J] = as_s4(V[s0][j], V[s0 + 1][j], V[s0 + 2][j], V[s0 + 3][j]);
+                Vb[Q][J] = as_s4(V[s0][sw(s0, j)], V[s0 + 1][sw(s0 + 1, j)], V[s0 + 2][sw(s0 + 2, j)],
+                                 V[s0 + 3][sw(s0 + 3, j)]);
             }
 
         // ---- intra-chunk attention, transposed: At[sig][tau], lane holds
         //      A[tau = P0 + l16][sig = 16 Q + 4 g + e] (the A operand of A V) -----------
+        s4 rof[4];  // r_tau e^{-w (tau - P0)}, the off-diagonal blocks' receptance operand
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int c4 = 16 * I + 4 * g;
+            rof[I] = mul_pack(row4(&R[tau][sw(tau, c4)]), frow4(&sm.pw[tau - P0][c4]));
+        }
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q) {
             if (Q > wv) break;
@@ -208,9 +227,8 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     const int c4 = 16 * I + 4 * g;
-                    const s4 ka = mul_pack(row4(&K[sig][c4]), frow4(&sm.pw[P0 - 1 - sig][c4]));
-                    const s4 rb = mul_pack(row4(&R[tau][c4]), frow4(&sm.pw[tau - P0][c4]));
-                    At = mfma(ka, rb, At);
+                    const s4 ka = mul_pack(row4(&K[sig][sw(sig, c4)]), frow4(&sm.pw[P0 - 1 - sig][c4]));
+                    At = mfma(ka, rof[I], At);
                 }
             } else {  // diagonal block: about c = P0 + 8, w capped; then the bonus on the diagonal
                 f4 Bn = {0.f, 0.f, 0.f, 0.f};
@@ -218,11 +236,11 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     const int c4 = 16 * I + 4 * g;
-                    const f4 kr = row4(&K[sig][c4]), rr = row4(&R[tau][c4]);
+                    const f4 kr = row4(&K[sig][sw(sig, c4)]), rr = row4(&R[tau][sw(tau, c4)]);
                     const s4 ka = mul_pack(kr, frow4(&sm.pe[sig + 1 - mid + 8][c4]));
                     const s4 rb = mul_pack(rr, frow4(&sm.pe[mid - tau + 8][c4]));
                     At = mfma(ka, rb, At);
-                    const s4 kp = pack4(kr[0], kr[1], kr[2], kr[3]);
+                    const s4 kp = raw4(&K[sig][sw(sig, c4)]);
                     const s4 ru = mul_pack(rr, frow4(&sm.uu[c4]));
                     Bn = mfma(kp, ru, Bn);
                 }
@@ -253,13 +271,14 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv5_fwd_kernel(Wkv5Args P) {
             for (int e = 0; e < 4; ++e) {
                 const int s = 16 * Q + 4 * g + e;
                 const int n = nv - 1 - s;
-                kk[e] = n >= 0 ? bf(K[s][key]) * sm.pw[n >= 0 ? n : 0][key] : 0.f;  // tokens past the chunk's end: 0
+                kk[e] = n >= 0 ? bf(K[s][sw(s, key)]) * sm.pw[n >= 0 ? n : 0][key] : 0.f;  // past the chunk's end: 0
             }
             const s4 a = pack4(kk[0], kk[1], kk[2], kk[3]);
 #pragma unroll
             for (int J = 0; J < 4; ++J) S[J] = mfma(a, Vb[Q][J], S[J]);
         }
         put_state();
+        wait_staged();
 
         // ---- outputs: lane holds O[tau = P0 + 4 g + e][16 J + l16] ---------------------
         const Rsrc ro = make_rsrc(P.o + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
