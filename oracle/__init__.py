@@ -21,4 +21,4 @@ from .token_shift_ref import (  # noqa: F401
     token_shift_backward_ref,
     token_shift_ref,
 )
-from .wkv5_ref import wkv5_direct_ref, wkv5_forward_ref  # noqa: F401
+from .wkv5_ref import wkv5_backward_ref, wkv5_direct_ref, wkv5_forward_ref  # noqa: F401

@@ -36,13 +36,24 @@ Readings where the pages are silent (each listed in the design doc):
   update on the pages has no normalising denominator;
 * the initial state is zero unless given.
 
+* the backward (derived here by differentiating the recurrence; the pages give
+  none) is for L = sum_t <go_t, o_t>: with the adjoint state
+  G_{t-1} = diag(e^{-w}) G_t + r_t^T go_t (G_{T-1} = 0),
+      dr_t = S_{t-1} go_t^T + u . k_t (v_t . go_t)
+      dk_t = G_t v_t^T + u . r_t (v_t . go_t)
+      dv_t = k_t G_t + (sum_i r_t,i u_i k_t,i) go_t
+      du_i = sum_t r_t,i k_t,i (v_t . go_t)
+      dw_i = -e^{-w_i} sum_t sum_j G_t[i, j] S_{t-1}[i, j]
+      dS0  = G_{-1}
+  (dw, du summed over the batch).
+
 Parity status: every function here is pinned (tests/test_oracle_wkv5_pins.py).
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["wkv5_forward_ref", "wkv5_direct_ref"]
+__all__ = ["wkv5_forward_ref", "wkv5_direct_ref", "wkv5_backward_ref"]
 
 
 def _heads(x, H):
@@ -99,3 +110,37 @@ def wkv5_direct_ref(w, u, r, k, v, H, S0=None):
             rd = r[:, :, h] * np.exp(-w[h][None, None, :] * t[None, :, None])
             o[:, :, h] += rd @ S0h
     return o.reshape(B, T, H * N)
+
+
+def wkv5_backward_ref(w, u, r, k, v, go, H, S0=None):
+    """Gradients of L = sum_t <go_t, o_t> for o = wkv5_forward_ref(w, u, r, k, v, H, S0),
+    in float64: a forward pass keeping every S_{t-1}, then the adjoint state G
+    walked backwards in time.
+
+    Returns (dr, dk, dv [B, T, C], dw, du [H, N] summed over the batch, dS0
+    [B, H, N, N]).
+    """
+    r, k, v, go = (_heads(x, H) for x in (r, k, v, go))
+    B, T, _, N = r.shape
+    w = np.asarray(w, dtype=np.float64).reshape(H, N)
+    u = np.asarray(u, dtype=np.float64).reshape(H, N)
+    d = np.exp(-w)
+    S = np.zeros((B, H, N, N)) if S0 is None else np.array(S0, dtype=np.float64).reshape(B, H, N, N)
+    prev = np.empty((T, B, H, N, N))                                      # S_{t-1}
+    for t in range(T):
+        prev[t] = S
+        S = d[None, :, :, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
+    G = np.zeros((B, H, N, N))
+    dr, dk, dv = (np.empty((B, T, H, N)) for _ in range(3))
+    dw = np.zeros((H, N))
+    du = np.zeros((H, N))
+    for t in range(T - 1, -1, -1):
+        vg = np.einsum("bhj,bhj->bh", v[:, t], go[:, t])                 # v_t . go_t
+        bonus = np.einsum("bhi,hi,bhi->bh", r[:, t], u, k[:, t])
+        dr[:, t] = np.einsum("bhij,bhj->bhi", prev[t], go[:, t]) + u[None] * k[:, t] * vg[..., None]
+        dk[:, t] = np.einsum("bhij,bhj->bhi", G, v[:, t]) + u[None] * r[:, t] * vg[..., None]
+        dv[:, t] = np.einsum("bhi,bhij->bhj", k[:, t], G) + bonus[..., None] * go[:, t]
+        du += np.einsum("bhi,bhi,bh->hi", r[:, t], k[:, t], vg)
+        dw -= d * np.einsum("bhij,bhij->hi", G, prev[t])
+        G = d[None, :, :, None] * G + r[:, t, :, :, None] * go[:, t, :, None, :]
+    return (dr.reshape(B, T, H * N), dk.reshape(B, T, H * N), dv.reshape(B, T, H * N), dw, du, G)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 from scipy.signal import lfilter
 
-from oracle import wkv5_direct_ref, wkv5_forward_ref
+from oracle import wkv5_backward_ref, wkv5_direct_ref, wkv5_forward_ref
 
 
 def rand(B, T, H, N, seed, w_lo=-3.0, w_hi=1.0):
@@ -110,3 +110,56 @@ def test_invariances():
     k2[:, :, N:] *= -3.0
     o2, _ = wkv5_forward_ref(w, u, r2, k2, v, H)
     np.testing.assert_array_equal(o2[:, :, :N], o[:, :, :N])
+
+
+def _torch_direct(w, u, r, k, v, H, S0):
+    """wkv5_direct_ref's history sum written in torch (float64, CPU), for autograd."""
+    import torch
+
+    B, T, C = r.shape
+    N = C // H
+    rh, kh, vh = (x.reshape(B, T, H, N) for x in (r, k, v))
+    t = torch.arange(T, dtype=torch.float64)
+    age = t[:, None] - 1 - t[None, :]
+    mask = (age >= 0).to(torch.float64)
+    outs = []
+    for h in range(H):
+        dec = torch.exp(-w[h][None, None, :] * torch.clamp(age, min=0)[:, :, None]) * mask[:, :, None]
+        A = torch.einsum("bti,tsi,bsi->bts", rh[:, :, h], dec, kh[:, :, h])
+        A = A + torch.einsum("bti,i,bti->bt", rh[:, :, h], u[h], kh[:, :, h])[:, :, None] * torch.eye(T, dtype=torch.float64)
+        o = A @ vh[:, :, h]
+        o = o + (rh[:, :, h] * torch.exp(-w[h][None, None, :] * t[None, :, None])) @ S0[:, h]
+        outs.append(o)
+    return torch.stack(outs, dim=2).reshape(B, T, C)
+
+
+@pytest.mark.parametrize("B,T,H,N", [(2, 11, 2, 4), (1, 1, 2, 3), (1, 20, 1, 6)])
+def test_backward_matches_torch_autograd_of_the_history_sum(B, T, H, N):
+    import torch
+
+    w, u, r, k, v, S0 = rand(B, T, H, N, 11 + T)
+    go = np.random.default_rng(12 + T).normal(0, 1, r.shape)
+    tw, tu, tr, tk, tv, tS = (torch.tensor(x, requires_grad=True) for x in (w, u, r, k, v, S0))
+    (torch.tensor(go) * _torch_direct(tw, tu, tr, tk, tv, H, tS)).sum().backward()
+    dr, dk, dv, dw, du, dS = wkv5_backward_ref(w, u, r, k, v, go, H, S0)
+    for name, got, ref in (("dr", dr, tr), ("dk", dk, tk), ("dv", dv, tv), ("dw", dw, tw), ("du", du, tu),
+                           ("dS0", dS, tS)):
+        np.testing.assert_allclose(got, ref.grad.numpy(), rtol=1e-10, atol=1e-10, err_msg=name)
+
+
+def test_backward_central_differences():
+    B, T, H, N = 1, 7, 2, 3
+    w, u, r, k, v, S0 = rand(B, T, H, N, 13)
+    go = np.random.default_rng(14).normal(0, 1, r.shape)
+    dr, dk, dv, dw, du, dS = wkv5_backward_ref(w, u, r, k, v, go, H, S0)
+    loss = lambda *a: float(np.sum(go * wkv5_forward_ref(*a[:5], H, a[5])[0]))
+    args = [w, u, r, k, v, S0]
+    h = 1e-5
+    for ai, grad, idx in ((0, dw, (1, 2)), (1, du, (0, 1)), (2, dr, (0, 3, 4)), (3, dk, (0, 5, 1)), (4, dv, (0, 0, 5)),
+                          (5, dS, (0, 1, 2, 0))):
+        a_p = [x.copy() for x in args]
+        a_m = [x.copy() for x in args]
+        a_p[ai][idx] += h
+        a_m[ai][idx] -= h
+        fd = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd)), (ai, fd, grad[idx])
