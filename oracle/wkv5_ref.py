@@ -37,8 +37,9 @@ Readings where the pages are silent (each listed in the design doc):
 * the initial state is zero unless given.
 
 * the backward (derived here by differentiating the recurrence; the pages give
-  none) is for L = sum_t <go_t, o_t>: with the adjoint state
-  G_{t-1} = diag(e^{-w}) G_t + r_t^T go_t (G_{T-1} = 0),
+  none) is for L = sum_t <go_t, o_t> + <dS_T, S_T> (dS_T, the gradient of the
+  final state, zero unless given): with the adjoint state
+  G_{t-1} = diag(e^{-w}) G_t + r_t^T go_t (G_{T-1} = dS_T),
       dr_t = S_{t-1} go_t^T + u . k_t (v_t . go_t)
       dk_t = G_t v_t^T + u . r_t (v_t . go_t)
       dv_t = k_t G_t + (sum_i r_t,i u_i k_t,i) go_t
@@ -112,10 +113,11 @@ def wkv5_direct_ref(w, u, r, k, v, H, S0=None):
     return o.reshape(B, T, H * N)
 
 
-def wkv5_backward_ref(w, u, r, k, v, go, H, S0=None):
-    """Gradients of L = sum_t <go_t, o_t> for o = wkv5_forward_ref(w, u, r, k, v, H, S0),
-    in float64: a forward pass keeping every S_{t-1}, then the adjoint state G
-    walked backwards in time.
+def wkv5_backward_ref(w, u, r, k, v, go, H, S0=None, dST=None):
+    """Gradients of L = sum_t <go_t, o_t> + <dST, S_T> for
+    (o, S_T) = wkv5_forward_ref(w, u, r, k, v, H, S0), in float64: a forward
+    pass keeping every S_{t-1}, then the adjoint state G (starting from dST,
+    [B, H, N, N] or None for zero) walked backwards in time.
 
     Returns (dr, dk, dv [B, T, C], dw, du [H, N] summed over the batch, dS0
     [B, H, N, N]).
@@ -130,7 +132,7 @@ def wkv5_backward_ref(w, u, r, k, v, go, H, S0=None):
     for t in range(T):
         prev[t] = S
         S = d[None, :, :, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
-    G = np.zeros((B, H, N, N))
+    G = np.zeros((B, H, N, N)) if dST is None else np.array(dST, dtype=np.float64).reshape(B, H, N, N)
     dr, dk, dv = (np.empty((B, T, H, N)) for _ in range(3))
     dw = np.zeros((H, N))
     du = np.zeros((H, N))

@@ -163,3 +163,54 @@ def test_backward_central_differences():
         a_m[ai][idx] -= h
         fd = (loss(*a_p) - loss(*a_m)) / (2 * h)
         assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd)), (ai, fd, grad[idx])
+
+
+def _torch_final_state(w, k, v, H, S0):
+    """S_T = diag(e^{-w T}) S0 + sum_s diag(e^{-w (T-1-s)}) k_s^T v_s, written as one sum."""
+    import torch
+
+    B, T, C = k.shape
+    N = C // H
+    kh, vh = (x.reshape(B, T, H, N) for x in (k, v))
+    t = torch.arange(T, dtype=torch.float64)
+    dec = torch.exp(-w[None, :, :] * (T - 1 - t)[:, None, None])  # [T, H, N]
+    S = torch.exp(-w * T)[None, :, :, None] * S0
+    return S + torch.einsum("bthi,thi,bthj->bhij", kh, dec, vh)
+
+
+@pytest.mark.parametrize("B,T,H,N", [(2, 9, 2, 4), (1, 1, 1, 3)])
+def test_backward_with_final_state_gradient_matches_autograd(B, T, H, N):
+    """L = <go, o> + <dS_T, S_T>: the final state's gradient enters as the
+    adjoint after the last token."""
+    import torch
+
+    w, u, r, k, v, S0 = rand(B, T, H, N, 21 + T)
+    rng = np.random.default_rng(22 + T)
+    go = rng.normal(0, 1, r.shape)
+    dST = rng.normal(0, 1, S0.shape)
+    tw, tu, tr, tk, tv, tS = (torch.tensor(x, requires_grad=True) for x in (w, u, r, k, v, S0))
+    loss = (torch.tensor(go) * _torch_direct(tw, tu, tr, tk, tv, H, tS)).sum()
+    loss = loss + (torch.tensor(dST) * _torch_final_state(tw, tk, tv, H, tS)).sum()
+    loss.backward()
+    dr, dk, dv, dw, du, dS = wkv5_backward_ref(w, u, r, k, v, go, H, S0, dST)
+    for name, got, ref in (("dr", dr, tr), ("dk", dk, tk), ("dv", dv, tv), ("dw", dw, tw), ("du", du, tu),
+                           ("dS0", dS, tS)):
+        np.testing.assert_allclose(got, ref.grad.numpy(), rtol=1e-10, atol=1e-10, err_msg=name)
+
+
+def test_backward_of_a_split_sequence_chains_through_the_state():
+    """Backward of a sequence cut in two: the second part's dS0 is the first
+    part's dS_T, and the pieces equal the whole sequence's gradients."""
+    B, T, H, N, t1 = 2, 12, 2, 3, 5
+    w, u, r, k, v, S0 = rand(B, T, H, N, 31)
+    go = np.random.default_rng(32).normal(0, 1, r.shape)
+    whole = wkv5_backward_ref(w, u, r, k, v, go, H, S0)
+    _, S1 = wkv5_forward_ref(w, u, r[:, :t1], k[:, :t1], v[:, :t1], H, S0)
+    second = wkv5_backward_ref(w, u, r[:, t1:], k[:, t1:], v[:, t1:], go[:, t1:], H, S1)
+    first = wkv5_backward_ref(w, u, r[:, :t1], k[:, :t1], v[:, :t1], go[:, :t1], H, S0, second[5])
+    for i, name in enumerate(("dr", "dk", "dv")):
+        np.testing.assert_allclose(np.concatenate([first[i], second[i]], axis=1), whole[i], rtol=1e-11, atol=1e-11,
+                                   err_msg=name)
+    np.testing.assert_allclose(first[3] + second[3], whole[3], rtol=1e-11, atol=1e-11, err_msg="dw")
+    np.testing.assert_allclose(first[4] + second[4], whole[4], rtol=1e-11, atol=1e-11, err_msg="du")
+    np.testing.assert_allclose(first[5], whole[5], rtol=1e-11, atol=1e-11, err_msg="dS0")
