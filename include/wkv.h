@@ -232,6 +232,53 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
                           const float* w, const float* u, const void* r, const void* k, const void* v,
                           float* o, const float* s_in, float* s_out, void* hip_stream);
 
+/* Bytes of scratch memory wkv5_backward needs for (B, T, H, N): the bf16
+ * state before every 64-token chunk (B H ceil(T/64) 64 64 2 bytes, rounded up
+ * to 256) plus 2 x 64 float32 per (batch row, head).  0 for invalid
+ * arguments or T == 0. */
+size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
+
+/*
+ * wkv5_backward - gradients of wkv5_forward.
+ *
+ * The pages give no backward; this is the derivative of the recurrence that
+ * wkv5_forward defines, for the loss L = sum_t <go_t, o_t> + <ds_out, S_T>.
+ * With the adjoint state G_T = ds_out (0 when NULL),
+ * G_{t-1} = diag(e^{-w}) G_t + r_t^T go_t:
+ *     dr_t = S_{t-1} go_t^T + u . k_t (v_t . go_t)
+ *     dk_t = G_t v_t^T + u . r_t (v_t . go_t)
+ *     dv_t = k_t G_t + (sum_i r_t,i u_i k_t,i) go_t
+ *     du   = sum_{b,t} r_t . k_t (v_t . go_t)
+ *     dw   = -e^{-w} . sum_{b,t} rowsum(G_t . S_{t-1})
+ *     dS0  = G_0 (before the first token)
+ * The call first recomputes the state before every chunk (a forward pass
+ * without outputs, into the workspace), then walks the chunks backwards with
+ * the same bf16 matrix-core products and float32 accumulation as the forward;
+ * dw and du are summed over the batch in a fixed order (bitwise
+ * reproducible).  Inside a 16-token block, channels with w above 8 use 8 for
+ * terms more than one token apart (as the forward does above 10).
+ *
+ * B, T, H, N, in_dtype, w, u, r, k, v, s_in  as wkv5_forward.
+ * go        [B, T, 64 H] bf16, 16-byte aligned: the gradient of o.
+ * ds_out    [B, H, 64, 64] float32 gradient of the final state, or NULL (zero):
+ *           the ds_in of the next segment when a sequence is split.
+ * dr, dk, dv [B, T, 64 H] float32, fully overwritten.
+ * dw, du    [H, 64] float32, overwritten (zeros when B*T == 0).
+ * ds_in     [B, H, 64, 64] float32 gradient of s_in (key-major), or NULL;
+ *           with B*T == 0 it receives ds_out (or zeros).  It may be the
+ *           ds_out buffer (each workgroup reads its part of ds_out before
+ *           writing the same part of ds_in).
+ * workspace wkv5_backward_workspace_bytes() bytes, 256-byte aligned;
+ *           clobbered.  Not needed when B*T == 0.
+ * Errors as the other entry points (WKV_EINVAL also for N != 64; nothing
+ * is written on an error).
+ */
+wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
+                           const float* w, const float* u, const void* r, const void* k, const void* v,
+                           const void* go, const float* s_in, const float* ds_out, float* dr, float* dk,
+                           float* dv, float* dw, float* du, float* ds_in, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
 /*
  * wkv_token_shift / wkv_token_shift_backward - the token-shift mix that
  * produces the inputs of the time-mixing projections.

@@ -104,6 +104,9 @@ __device__ __forceinline__ s4 as_s4(uint16_t a, uint16_t b, uint16_t c, uint16_t
 // four consecutive bf16 of an LDS row as an MFMA operand, unchanged
 __device__ __forceinline__ s4 raw4(const uint16_t* p) { return __builtin_bit_cast(s4, *reinterpret_cast<const u16x4*>(p)); }
 
+// kOut = false: a state-only pass (no outputs, only the chunk-start states in P.ckpt
+// and the final state), as the backward needs.
+template <bool kOut>
 __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     __shared__ Wkv5Shared sm;
     const int lane = threadIdx.x & 63;
@@ -166,7 +169,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     };
 
     stage(0, 0);
-    put_state();
+    if constexpr (kOut) put_state();
     wait_staged();
     const int P0 = 16 * wv;  // first token of this wave's output block, chunk-relative
 
@@ -179,6 +182,16 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
         lds_sync();  // this chunk's inputs, the tables and the state are in LDS for every wave
         if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
+        if (P.ckpt != nullptr) {  // the state before the chunk, bf16 [key][value], for the backward
+            uint16_t* cp = P.ckpt + (bh * nch + ch) * kN * kN;
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t h2 = pk2(S[J][e], 0.f);
+                    cp[(16 * wv + 4 * g + e) * kN + 16 * J + l16] = static_cast<uint16_t>(h2 & 0xffffu);
+                }
+        }
 
         const uint16_t(*R)[kN] = sm.in[buf][0];
         const uint16_t(*K)[kN] = sm.in[buf][1];
@@ -190,7 +203,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
         for (int J = 0; J < 4; ++J) O[J] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < 4 && kOut; ++I) {
             const int c4 = 16 * I + 4 * g;
             const s4 a = mul_pack(row4(&R[tau][sw(tau, c4)]), frow4(&sm.pw[tau][c4]));
 #pragma unroll
@@ -214,12 +227,12 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
         //      A[tau = P0 + l16][sig = 16 Q + 4 g + e] (the A operand of A V) -----------
         s4 rof[4];  // r_tau e^{-w (tau - P0)}, the off-diagonal blocks' receptance operand
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < 4 && kOut; ++I) {
             const int c4 = 16 * I + 4 * g;
             rof[I] = mul_pack(row4(&R[tau][sw(tau, c4)]), frow4(&sm.pw[tau - P0][c4]));
         }
 #pragma unroll
-        for (int Q = 0; Q < 4; ++Q) {
+        for (int Q = 0; Q < 4 && kOut; ++Q) {
             if (Q > wv) break;
             f4 At = {0.f, 0.f, 0.f, 0.f};
             const int sig = 16 * Q + l16;  // this lane's key token (m index of K~)
@@ -254,7 +267,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
             for (int J = 0; J < 4; ++J) O[J] = mfma(a, Vb[Q][J], O[J]);
         }
-        lds_sync();  // every wave has read the state before it is overwritten
+        if constexpr (kOut) lds_sync();  // every wave has read the state before it is overwritten
 
         // ---- state update: S = diag(e^{-w nv}) S + sum_sig (k_sig e^{-w (nv-1-sig)})^T v_sig
 #pragma unroll
@@ -277,8 +290,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
             for (int J = 0; J < 4; ++J) S[J] = mfma(a, Vb[Q][J], S[J]);
         }
-        put_state();
+        if constexpr (kOut) put_state();
         wait_staged();
+        if constexpr (!kOut) continue;
 
         // ---- outputs: lane holds O[tau = P0 + 4 g + e][16 J + l16] ---------------------
         const Rsrc ro = make_rsrc(P.o + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
@@ -299,6 +313,445 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     }
 }
 
+// ---- backward ---------------------------------------------------------------------
+// For L = sum_t <go_t, o_t> + <dS_T, S_T>, with the adjoint state
+// G_{t-1} = diag(d) G_t + r_t^T go_t (d = e^{-w}; G after the last token is dS_T), per chunk of n tokens with S0 the
+// state before it and G1 the adjoint after it (local indices s, sig, tau < n):
+//     dv_sig = (k_sig . d^{n-1-sig}) G1 + sum_{s >= sig} A[s][sig] go_s     (A: the forward's
+//              attention, its diagonal the bonus sum_i r_s,i u_i k_s,i)
+//     dk_sig = d^{n-1-sig} . (G1 v_sig^T) + sum_{s > sig} C[s][sig] r_s d^{s-1-sig}
+//              + u . r_sig C[sig][sig]                                      (C = GO V^T)
+//     dr_s   = d^s . (S0 go_s^T) + sum_{sig < s} C[s][sig] k_sig d^{s-1-sig} + u . k_s C[s][s]
+//     du    += sum_s r_s . k_s C[s][s]
+//     dw    -= n d^n . rowsum(G1 . S0) + sum_sig (n-1-sig) d^{n-1-sig} . k_sig . (G1 v_sig^T)
+//              + sum_s s d^s . r_s . (S0 go_s^T)
+//              + sum_{sig < s} (s-1-sig) d^{s-1-sig} . r_s . k_sig C[s][sig]
+//     G0     = d^n . G1 + sum_s (r_s . d^s)^T go_s                (the adjoint before the chunk)
+// (dw = -d . sum_t rowsum(G_t . S_{t-1}) expanded over the chunk and multiplied by d).
+// The in-chunk sums are matrix products with the decay split about the later
+// 16-token block's first token (off-diagonal blocks: both factors <= 1) or
+// about the block's middle with w capped at kWCapB (diagonal blocks); lag d^lag
+// splits the same way into (s - p) d^{s-p} d^{p-1-sig} + d^{s-p} (p-1-sig) d^{p-1-sig}.
+constexpr float kWCapB = 8.f;  // keeps every in-block intermediate below e^64 times its inputs
+
+struct Wkv5BwdFinal {         // the per-(batch row, head) sums of dw, du, after the chunk walk
+    float dwa[kN][17];         // rowsum term: [key][lane l16]
+    float dv[kWaves5][4][2][kN];  // [wave][k-group g][dw, du][channel]
+    float dd[kWaves5][kN];     // diagonal blocks' lag-weighted term: [wave][channel]
+};
+
+struct Wkv5BwdShared {
+    union {
+        uint16_t in[4][kLc][kN];  // r, k, v, go of the chunk, [token][swizzled channel]
+        Wkv5BwdFinal fin;
+    };
+    uint16_t gs[kN][kPadH];    // G1, bf16, [key][value]
+    uint16_t ss[kN][kPadH];    // S0, bf16, [key][value]
+    float pw[kLc + 1][kPadF];  // e^{-w n}
+    float pe[17][kPadF];       // e^{w' m}, m = -8..8, w' = min(w, kWCapB)
+    float uu[kN];
+    float cd[kLc];             // C[s][s] = go_s . v_s
+    float cdg[kWaves5][16][17];  // each wave's diagonal block of C, [s][sig], sig < s (float32)
+};
+
+__global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P) {
+    __shared__ Wkv5BwdShared sm;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / P.H, h = bh - b * P.H;
+    const int64_t C = P.H * kN;
+    const int64_t nch = (P.T + kLc - 1) / kLc;
+    const int P0 = 16 * wv;
+
+    for (int q = threadIdx.x; q < (kLc + 1) * kN; q += 64 * kWaves5) {
+        const int n = q / kN, i = q % kN;
+        sm.pw[n][i] = ex2(-P.w[h * kN + i] * static_cast<float>(n) * kL2E);
+    }
+    for (int q = threadIdx.x; q < 17 * kN; q += 64 * kWaves5) {
+        const int m = q / kN - 8, i = q % kN;
+        sm.pe[m + 8][i] = ex2(fminf(P.w[h * kN + i], kWCapB) * static_cast<float>(m) * kL2E);
+    }
+    if (threadIdx.x < kN) sm.uu[threadIdx.x] = P.u[h * kN + threadIdx.x];
+
+    // G: wave wv, tile J, lane (l16, g), element e holds G[16 wv + 4 g + e][16 J + l16];
+    // after the last token it is the final state's gradient (or zero)
+    f4 G[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = P0 + 4 * g + e, j = 16 * J + l16;
+            G[J][e] = P.ds_out != nullptr ? P.ds_out[bh * kN * kN + key * kN + j] : 0.f;
+            sm.gs[key][j] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
+        }
+    float dwv[4] = {0.f, 0.f, 0.f, 0.f}, duv[4] = {0.f, 0.f, 0.f, 0.f};  // channel 16 I + l16
+    float dwk[4] = {0.f, 0.f, 0.f, 0.f};                                  // key P0 + 4 g + e (rowsum term)
+    float dwd = 0.f;                                                      // channel lane (diagonal blocks)
+
+    const uint16_t(*R)[kN] = sm.in[0];
+    const uint16_t(*K)[kN] = sm.in[1];
+    const uint16_t(*V)[kN] = sm.in[2];
+    const uint16_t(*GO)[kN] = sm.in[3];
+    auto rd = [](const uint16_t(*X)[kN], int t, int c) { return bf(X[t][sw(t, c)]); };
+    auto row4s = [](const uint16_t(*X)[kN], int t, int c4) { return row4(&X[t][sw(t, c4)]); };
+    auto raw4s = [](const uint16_t(*X)[kN], int t, int c4) { return raw4(&X[t][sw(t, c4)]); };
+    // four consecutive tokens t0..t0+3 of channel c as a raw operand (a column of a staged input)
+    auto col4 = [](const uint16_t(*X)[kN], int t0, int c) {
+        return as_s4(X[t0][sw(t0, c)], X[t0 + 1][sw(t0 + 1, c)], X[t0 + 2][sw(t0 + 2, c)], X[t0 + 3][sw(t0 + 3, c)]);
+    };
+
+    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        const int64_t t0 = ch * kLc;
+        const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
+        // ---- stage r, k, v, go (swizzled rows) and S0 ------------------------------------
+        const uint16_t* src[4] = {P.r, P.k, P.v, P.go};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const Rsrc rs = make_rsrc(src[a] + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 2));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = P0 + 8 * i + lane / 8;
+                const int q = (lane % 8) ^ (row & 7);
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+            }
+        }
+        {
+            const uint16_t* cp = P.ckpt + (bh * nch + ch) * kN * kN;
+            for (int q = threadIdx.x; q < kN * kN / 4; q += 64 * kWaves5) {  // 4 bf16 at a time
+                const int key = q / (kN / 4), v4 = (q % (kN / 4)) * 4;
+                *reinterpret_cast<u2*>(&sm.ss[key][v4]) = *reinterpret_cast<const u2*>(cp + key * kN + v4);
+            }
+        }
+        wait_staged();
+        lds_sync();
+
+        // ---- C[s][s] of this wave's tokens, from the diagonal block of GO V^T ------------
+        f4 Cpp = {0.f, 0.f, 0.f, 0.f};  // lane: C[s = P0 + 4 g + e][sig = P0 + l16]
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const int j4 = 16 * J + 4 * g;
+            Cpp = mfma(raw4s(GO, P0 + l16, j4), raw4s(V, P0 + l16, j4), Cpp);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * g + e == l16) sm.cd[P0 + l16] = Cpp[e];
+        wait_lds_reads();
+
+        const int sig = P0 + l16;  // this lane's key token as an m / n index
+        // ---- dv: (k . d^{n-1-sig}) G1 + sum_{s >= sig} A[s][sig] go_s -------------------------
+        {
+            f4 D[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) D[J] = f4{0.f, 0.f, 0.f, 0.f};
+            const int nk = nv - 1 - sig;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int c4 = 16 * I + 4 * g;
+                const s4 a = nk >= 0 ? mul_pack(row4s(K, sig, c4), frow4(&sm.pw[nk >= 0 ? nk : 0][c4])) : s4{0, 0, 0, 0};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j = 16 * J + l16;
+                    D[J] = mfma(a, as_s4(sm.gs[c4][j], sm.gs[c4 + 1][j], sm.gs[c4 + 2][j], sm.gs[c4 + 3][j]), D[J]);
+                }
+            }
+#pragma unroll 1
+            for (int Q = 0; Q < 4; ++Q) {
+                if (Q < wv) continue;
+                f4 At = {0.f, 0.f, 0.f, 0.f};  // lane: A[s = 16 Q + 4 g + e][sig = P0 + l16]
+                const int s_m = 16 * Q + l16;  // the s of this lane's A-operand row
+                if (Q > wv) {
+                    const int p0 = 16 * Q;
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        const int c4 = 16 * I + 4 * g;
+                        const s4 ra = mul_pack(row4s(R, s_m, c4), frow4(&sm.pw[s_m - p0][c4]));
+                        const s4 kb = mul_pack(row4s(K, sig, c4), frow4(&sm.pw[p0 - 1 - sig][c4]));
+                        At = mfma(ra, kb, At);
+                    }
+                } else {
+                    f4 Bn = {0.f, 0.f, 0.f, 0.f};
+                    const int mid = P0 + 8;
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        const int c4 = 16 * I + 4 * g;
+                        const f4 rr = row4s(R, s_m, c4), kk = row4s(K, sig, c4);
+                        At = mfma(mul_pack(rr, frow4(&sm.pe[mid - s_m + 8][c4])),
+                                  mul_pack(kk, frow4(&sm.pe[sig + 1 - mid + 8][c4])), At);
+                        Bn = mfma(mul_pack(rr, frow4(&sm.uu[c4])), pack4(kk[0], kk[1], kk[2], kk[3]), Bn);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {  // (s_local = 4 g + e, sig_local = l16): keep s > sig, bonus on s == sig
+                        const int sl = 4 * g + e;
+                        At[e] = sl > l16 ? At[e] : (sl == l16 ? Bn[e] : 0.f);
+                    }
+                }
+                const s4 a = pack4(At[0], At[1], At[2], At[3]);
+#pragma unroll
+                for (int J = 0; J < 4; ++J) D[J] = mfma(a, col4(GO, 16 * Q + 4 * g, 16 * J + l16), D[J]);
+            }
+            const Rsrc rv = make_rsrc(P.dv + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    buf_store(D[J][e], rv, static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4), 0);
+        }
+
+        // ---- dk: d^{n-1-sig} X + sum_{s > sig} C[s][sig] r_s d^{s-1-sig} + u r C[sig][sig] ---
+        {
+            f4 D[4];  // lane: dk[sig = P0 + 4 g + e][i = 16 I + l16]
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {  // X = V G1^T
+                f4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    X = mfma(raw4s(V, sig, j4), raw4(&sm.gs[16 * I + l16][j4]), X);
+                }
+                const int i = 16 * I + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sg = P0 + 4 * g + e, nk = nv - 1 - sg;
+                    const float pk = nk >= 0 ? sm.pw[nk][i] : 0.f;
+                    dwv[I] -= static_cast<float>(nk) * pk * rd(K, sg, i) * X[e];  // (n-1-sig) d^{n-1-sig} k X
+                    X[e] *= pk;
+                }
+                D[I] = X;
+            }
+#pragma unroll 1
+            for (int Q = 0; Q < 4; ++Q) {
+                if (Q < wv) continue;
+                // C block, lane: C[s = 16 Q + 4 g + e][sig = P0 + l16] = the A operand [m = sig][k = s]
+                f4 Cq = {0.f, 0.f, 0.f, 0.f};
+                if (Q == wv) {
+                    Cq = Cpp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e > l16 ? Cq[e] : 0.f;
+                } else {
+#pragma unroll
+                    for (int J = 0; J < 4; ++J) {
+                        const int j4 = 16 * J + 4 * g;
+                        Cq = mfma(raw4s(GO, 16 * Q + l16, j4), raw4s(V, sig, j4), Cq);
+                    }
+                }
+                const s4 a = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
+                const int p0 = 16 * Q, mid = P0 + 8;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int i = 16 * I + l16;
+                    float rb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 16 * Q + 4 * g + e;
+                        rb[e] = rd(R, s, i) * (Q > wv ? sm.pw[s - p0][i] : sm.pe[mid - s + 8][i]);
+                    }
+                    const f4 M = mfma(a, pack4(rb[0], rb[1], rb[2], rb[3]), f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int sg = P0 + 4 * g + e;
+                        D[I][e] += M[e] * (Q > wv ? sm.pw[p0 - 1 - sg][i] : sm.pe[sg + 1 - mid + 8][i]);
+                    }
+                }
+            }
+            const Rsrc rk = make_rsrc(P.dk + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int i = 16 * I + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sg = P0 + 4 * g + e;
+                    const float val = D[I][e] + sm.uu[i] * rd(R, sg, i) * sm.cd[sg];
+                    buf_store(val, rk, static_cast<uint32_t>((sg * C + i) * 4), 0);
+                }
+            }
+        }
+
+        // ---- dr, du: d^s Y + sum_{sig < s} C[s][sig] k_sig d^{s-1-sig} + u k C[s][s] ---------
+        {
+            const int s_n = P0 + l16;  // this lane's s as the n index of V G^T-style products
+            f4 D[4];  // lane: dr[s = P0 + 4 g + e][i = 16 I + l16]
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {  // Y = GO S0^T
+                f4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    Y = mfma(raw4s(GO, s_n, j4), raw4(&sm.ss[16 * I + l16][j4]), Y);
+                }
+                const int i = 16 * I + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = P0 + 4 * g + e;
+                    const float ps = sm.pw[s][i];
+                    dwv[I] -= static_cast<float>(s) * ps * rd(R, s, i) * Y[e];  // s d^s r Y
+                    Y[e] *= ps;
+                }
+                D[I] = Y;
+            }
+#pragma unroll 1
+            for (int Q = 0; Q < 4; ++Q) {
+                if (Q > wv) continue;
+                // lane: C[s = P0 + l16][sig = 16 Q + 4 g + e] (from V_Q GO_P^T), the A operand [m = s][k = sig]
+                f4 Cq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    Cq = mfma(raw4s(V, 16 * Q + l16, j4), raw4s(GO, s_n, j4), Cq);
+                }
+                if (Q == wv) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        Cq[e] = 4 * g + e < l16 ? Cq[e] : 0.f;
+                        sm.cdg[wv][l16][4 * g + e] = Cq[e];
+                    }
+                }
+                const s4 a = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
+                const int mid = P0 + 8;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int i = 16 * I + l16;
+                    float kb[4], kw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {  // k_sig d^{p-1-sig} and (p-1-sig) times it, p = P0 or mid
+                        const int sg = 16 * Q + 4 * g + e;
+                        const int lg = Q < wv ? P0 - 1 - sg : mid - 1 - sg;
+                        const float f = Q < wv ? sm.pw[lg][i] : sm.pe[sg + 1 - mid + 8][i];
+                        kb[e] = rd(K, sg, i) * f;
+                        kw[e] = kb[e] * static_cast<float>(lg);
+                    }
+                    const f4 M1 = mfma(a, pack4(kb[0], kb[1], kb[2], kb[3]), f4{0.f, 0.f, 0.f, 0.f});
+                    if (Q == wv) {  // the diagonal block's lag-weighted dw term is taken elementwise below
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) D[I][e] += M1[e] * sm.pe[mid - (P0 + 4 * g + e) + 8][i];
+                        continue;
+                    }
+                    // off the diagonal both parts of the lag, s - P0 and P0 - 1 - sig, are >= 0
+                    const f4 M2 = mfma(a, pack4(kw[0], kw[1], kw[2], kw[3]), f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = P0 + 4 * g + e;
+                        const int ls = s - P0;
+                        const float f = sm.pw[ls][i];
+                        D[I][e] += M1[e] * f;
+                        dwv[I] -= rd(R, s, i) * f * (static_cast<float>(ls) * M1[e] + M2[e]);
+                    }
+                }
+            }
+            const Rsrc rr = make_rsrc(P.dr + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int i = 16 * I + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = P0 + 4 * g + e;
+                    const float kc = rd(K, s, i) * sm.cd[s];
+                    duv[I] += rd(R, s, i) * kc;
+                    buf_store(D[I][e] + sm.uu[i] * kc, rr, static_cast<uint32_t>((s * C + i) * 4), 0);
+                }
+            }
+        }
+
+        // ---- the lag-weighted dw term inside this wave's block, elementwise with exact weights:
+        //      dw_i -= sum_{sig < s} (s-1-sig) d_i^{s-1-sig} r_s,i k_sig,i C[s][sig]   (lane = channel i)
+        {
+            const int i = lane;
+            float acc = 0.f;
+#pragma unroll 1
+            for (int sl = 2; sl < 16; ++sl) {
+                float t = 0.f;
+#pragma unroll 1
+                for (int sg = 0; sg + 1 < sl; ++sg) {  // lag = sl - 1 - sg >= 1 (lag 0 has weight 0)
+                    const int lag = sl - 1 - sg;
+                    t = fmaf(static_cast<float>(lag) * sm.pw[lag][i] * rd(K, P0 + sg, i), sm.cdg[wv][sl][sg], t);
+                }
+                acc = fmaf(rd(R, P0 + sl, i), t, acc);
+            }
+            dwd -= acc;
+        }
+
+        // ---- the rowsum term of dw, and G0 = d^n G1 + sum_s (r_s d^s)^T go_s ------------------
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = P0 + 4 * g + e;
+            const float dn = sm.pw[nv][key];
+            float acc = 0.f;
+#pragma unroll
+            for (int J = 0; J < 4; ++J) acc += G[J][e] * bf(sm.ss[key][16 * J + l16]);
+            dwk[e] -= static_cast<float>(nv) * dn * acc;
+#pragma unroll
+            for (int J = 0; J < 4; ++J) G[J][e] *= dn;
+        }
+        const int key = P0 + l16;  // the m index of (R^)^T
+#pragma unroll 1
+        for (int Q = 0; Q < 4; ++Q) {
+            float ra[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * Q + 4 * g + e;
+                ra[e] = s < nv ? rd(R, s, key) * sm.pw[s][key] : 0.f;
+            }
+            const s4 a = pack4(ra[0], ra[1], ra[2], ra[3]);
+#pragma unroll
+            for (int J = 0; J < 4; ++J) G[J] = mfma(a, col4(GO, 16 * Q + 4 * g, 16 * J + l16), G[J]);
+        }
+        lds_sync();  // every wave is done with this chunk's G1 and inputs
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.gs[P0 + 4 * g + e][16 * J + l16] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
+    }
+
+    if (P.ds_in != nullptr) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P.ds_in[bh * kN * kN + (P0 + 4 * g + e) * kN + 16 * J + l16] = G[J][e];
+    }
+    // ---- dw, du of this (batch row, head), summed in a fixed order (the inputs' LDS is free) ---
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.fin.dwa[P0 + 4 * g + e][l16] = dwk[e];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        sm.fin.dv[wv][g][0][16 * I + l16] = dwv[I];
+        sm.fin.dv[wv][g][1][16 * I + l16] = duv[I];
+    }
+    sm.fin.dd[wv][lane] = dwd;
+    lds_sync();
+    if (threadIdx.x < kN) {
+        const int i = threadIdx.x;
+        float sw_ = 0.f, su = 0.f;
+        for (int ww = 0; ww < kWaves5; ++ww) {
+            for (int gg = 0; gg < 4; ++gg) {
+                sw_ += sm.fin.dv[ww][gg][0][i];
+                su += sm.fin.dv[ww][gg][1][i];
+            }
+            sw_ += sm.fin.dd[ww][i];
+        }
+        for (int c = 0; c < 16; ++c) sw_ += sm.fin.dwa[i][c];
+        P.part[(bh * 2 + 0) * kN + i] = sw_;
+        P.part[(bh * 2 + 1) * kN + i] = su;
+    }
+}
+
+// dw[h, i], du[h, i] = sum over batch rows (in order) of the per-(batch row, head) partials
+__global__ void wkv5_reduce_kernel(const float* part, int64_t B, int64_t H, float* dw, float* du) {
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (q >= H * kN) return;
+    const int64_t h = q / kN, i = q % kN;
+    float a = 0.f, c = 0.f;
+    for (int64_t b = 0; b < B; ++b) {
+        a += part[((b * H + h) * 2 + 0) * kN + i];
+        c += part[((b * H + h) * 2 + 1) * kN + i];
+    }
+    dw[q] = a;
+    du[q] = c;
+}
+
 // T == 0: the state after the sequence is the state before it (or zero).
 __global__ void wkv5_state_copy_kernel(const float* s_in, float* s_out, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -314,8 +767,22 @@ hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hi
     return hipGetLastError();
 }
 
+hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(wkv5_bwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = a.H * kN;
+    hipLaunchKernelGGL(wkv5_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a.part,
+                       a.B, a.H, a.dw, a.du);
+    return hipGetLastError();
+}
+
 hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL(wkv5_fwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    if (a.o == nullptr) {
+        hipLaunchKernelGGL(wkv5_fwd_kernel<false>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(wkv5_fwd_kernel<true>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 

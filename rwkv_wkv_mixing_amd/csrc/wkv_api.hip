@@ -232,19 +232,54 @@ wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype, const float
     return hip_status(wkv::launch_step(s, static_cast<hipStream_t>(hip_stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks of the RWKV-5 calls; fills the (batch row, head) count,
+// the state element count and the workspace of the backward.
+struct Wkv5Plan {
+    wkv_status_t st;
+    int64_t bh, ns;
+    size_t ckpt_bytes, ws_bytes;
+};
+
+Wkv5Plan wkv5_plan(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype) {
+    Wkv5Plan p{WKV_OK, 0, 0, 0, 0};
+    if (B < 0 || T < 0 || H < 0 || N != 64) return Wkv5Plan{WKV_EINVAL, 0, 0, 0, 0};
+    if (!dtype_ok(in_dtype)) return Wkv5Plan{WKV_EDTYPE, 0, 0, 0, 0};
+    if (in_dtype != WKV_BF16) return Wkv5Plan{WKV_EDTYPE, 0, 0, 0, 0};  // the products run on bf16 operands
+    int64_t n, bytes, ck;
+    if (!mul3(B, T, H, &n) || __builtin_mul_overflow(n, int64_t{64 * 4}, &bytes)) return Wkv5Plan{WKV_ESIZE, 0, 0, 0, 0};
+    if (__builtin_mul_overflow(B, H, &p.bh) || p.bh >= (int64_t{1} << 31)) return Wkv5Plan{WKV_ESIZE, 0, 0, 0, 0};
+    if (__builtin_mul_overflow(p.bh, int64_t{64 * 64}, &p.ns)) return Wkv5Plan{WKV_ESIZE, 0, 0, 0, 0};
+    // one chunk's rows must fit a buffer resource: 64 rows of C = 64 H float32
+    if (H > 0 && 64 * 64 * H * 4 >= (int64_t{1} << 32)) return Wkv5Plan{WKV_ESIZE, 0, 0, 0, 0};
+    // backward workspace: the bf16 state before every 64-token chunk, then 2 x 64
+    // float32 partial sums (dw, du) per (batch row, head)
+    const int64_t nch = (T + 63) / 64;
+    if (!mul3(p.bh, nch, 64 * 64 * 2, &ck) || ck > (int64_t{1} << 60)) return Wkv5Plan{WKV_ESIZE, 0, 0, 0, 0};
+    p.ckpt_bytes = (static_cast<size_t>(ck) + 255) / 256 * 256;
+    p.ws_bytes = T > 0 ? p.ckpt_bytes + static_cast<size_t>(p.bh) * 2 * 64 * 4 : 0;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, WKV_BF16);
+    return p.st == WKV_OK ? p.ws_bytes : 0;
+}
+
 wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                           const float* u, const void* r, const void* k, const void* v, float* o,
                           const float* s_in, float* s_out, void* hip_stream) {
-    if (B < 0 || T < 0 || H < 0 || N != 64) return WKV_EINVAL;
-    if (!dtype_ok(in_dtype)) return WKV_EDTYPE;
-    if (in_dtype != WKV_BF16) return WKV_EDTYPE;  // the products run on bf16 operands
-    int64_t n, bytes, bh, ns;
-    if (!mul3(B, T, H, &n) || __builtin_mul_overflow(n, int64_t{64 * 4}, &bytes)) return WKV_ESIZE;
-    if (__builtin_mul_overflow(B, H, &bh) || bh >= (int64_t{1} << 31)) return WKV_ESIZE;
-    if (__builtin_mul_overflow(bh, int64_t{64 * 64}, &ns)) return WKV_ESIZE;
-    // one chunk's rows must fit a buffer resource: 64 rows of C = 64 H float32
-    if (H > 0 && 64 * 64 * H * 4 >= (int64_t{1} << 32)) return WKV_ESIZE;
-    if (bh == 0) return WKV_OK;
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    const int64_t ns = p.ns;
+    if (p.bh == 0) return WKV_OK;
     if ((s_in && !aligned(s_in, 4)) || (s_out && !aligned(s_out, 4))) return WKV_EALIGN;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (T == 0) return hip_status(wkv::launch_wkv5_state_copy(s_in, s_out, ns, stream));
@@ -254,6 +289,45 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     wkv::Wkv5Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), o, s_in, s_out};
     return hip_status(wkv::launch_wkv5_fwd(a, stream));
+}
+
+wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
+                           const float* u, const void* r, const void* k, const void* v, const void* go,
+                           const float* s_in, const float* ds_out, float* dr, float* dk, float* dv, float* dw,
+                           float* du, float* ds_in, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (H == 0) return WKV_OK;
+    if (!dw || !du) return WKV_EINVAL;
+    if (!aligned(dw, 4) || !aligned(du, 4) || (ds_in && !aligned(ds_in, 4))) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (ds_out && !aligned(ds_out, 4)) return WKV_EALIGN;
+    if (B == 0 || T == 0) {  // empty sums: dw = du = 0, and dS0 = dS_T
+        const int64_t nc = H * 64;
+        hipLaunchKernelGGL(zero2_kernel, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream, nc,
+                           dw, du);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && ds_in != nullptr) e = wkv::launch_wkv5_state_copy(ds_out, ds_in, p.ns, stream);
+        return hip_status(e);
+    }
+    if (!w || !u || !r || !k || !v || !go || !dr || !dk || !dv) return WKV_EINVAL;
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(dr, 4) || !aligned(dk, 4) || !aligned(dv, 4) ||
+        (s_in && !aligned(s_in, 4)) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(go, 16))
+        return WKV_EALIGN;
+    if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    auto* ckpt = static_cast<uint16_t*>(workspace);
+    auto* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ckpt_bytes);
+    const auto* r16 = static_cast<const uint16_t*>(r);
+    const auto* k16 = static_cast<const uint16_t*>(k);
+    const auto* v16 = static_cast<const uint16_t*>(v);
+    // the states before every chunk, recomputed by a state-only forward pass
+    wkv::Wkv5Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
+    fa.ckpt = ckpt;
+    hipError_t e = wkv::launch_wkv5_fwd(fa, stream);
+    if (e != hipSuccess) return hip_status(e);
+    wkv::Wkv5BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), ckpt, ds_out,
+                        dr, dk, dv, part, dw, du, ds_in};
+    return hip_status(wkv::launch_wkv5_bwd(ba, stream));
 }
 
 size_t wkv_token_shift_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {

@@ -95,6 +95,26 @@ struct Wkv5Args {
     float* o;            // [B, T, C]
     const float* s_in;   // [B, H, 64, 64] or NULL (zero state)
     float* s_out;        // [B, H, 64, 64] or NULL
+    uint16_t* ckpt = nullptr;  // [B, H, nchunks, 64, 64] bf16 [key][value]: the state before each chunk, or NULL
+};
+
+struct Wkv5BwdArgs {
+    int64_t B, T, H;
+    const float* w;
+    const float* u;
+    const uint16_t* r;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* go;     // [B, T, C] bf16 gradient of o
+    const uint16_t* ckpt;   // as Wkv5Args::ckpt
+    const float* ds_out;    // [B, H, 64, 64] gradient of the final state, or NULL (zero)
+    float* dr;              // [B, T, C]
+    float* dk;
+    float* dv;
+    float* part;            // [B, H, 2, 64]: dw, du of each (batch row, head)
+    float* dw;              // [H, 64], summed over batch rows
+    float* du;
+    float* ds_in;           // [B, H, 64, 64] gradient of the initial state, or NULL
 };
 
 // chunked forward (wkv_fwd.hip)
@@ -117,6 +137,7 @@ int shift_vector_width(bool bf16, bool bwd);
 // RWKV-5 matrix-state forward (wkv5.hip)
 hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream);
 hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hipStream_t stream);
+hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream);
 
 // decode step (wkv_step.hip)
 hipError_t launch_step(const StepArgs& s, hipStream_t stream);

@@ -337,3 +337,57 @@ def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
                               _p(state_out), _stream(dev))
     L.check("wkv5_forward", st)
     return (out, state_out) if return_state else out
+
+
+def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, workspace=None):
+    """Gradients of sum <go, o> + <grad_state_out, S_T> for
+    (o, S_T) = wkv5_forward(w, u, r, k, v, state_in=state_in, return_state=True):
+    returns (dr, dk, dv [B, T, C] float32, dw, du [H, 64] float32 summed over
+    the batch, ds_in [B, H, 64, 64] float32 or None).  go: [B, T, C] bfloat16."""
+    _need(r, "r", torch.bfloat16)
+    dev = r.device
+    B, T, C = r.shape
+    H = w.shape[0] if w.dim() == 2 else C // 64
+    if C != 64 * H:
+        raise ValueError(f"C = {C} is not 64 * H with H = {H}")
+    for t, n in ((k, "k"), (v, "v"), (go, "go")):
+        _need(t, n, torch.bfloat16, (B, T, C), dev)
+    _need(w, "w", torch.float32, (H, 64), dev)
+    _need(u, "u", torch.float32, (H, 64), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, 64, 64), dev)
+    if grad_state_out is not None:
+        _need(grad_state_out, "grad_state_out", torch.float32, (B, H, 64, 64), dev)
+    dr, dk, dv = (torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(3))
+    dw = torch.empty((H, 64), dtype=torch.float32, device=dev)
+    du = torch.empty((H, 64), dtype=torch.float32, device=dev)
+    ds = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev) if need_state_grad else None
+    lib = L.lib()
+    nbytes = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    st = lib.wkv5_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
+                           _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    L.check("wkv5_backward", st)
+    return dr, dk, dv, dw, du, ds
+
+
+class Wkv5Function(torch.autograd.Function):
+    """Autograd wrapper: o = wkv5_forward(...); backward through wkv5_backward
+    (go rounded to bfloat16 for the matrix-core products)."""
+
+    @staticmethod
+    def forward(ctx, w, u, r, k, v, state_in=None):
+        o = wkv5_forward(w, u, r, k, v, state_in=state_in)
+        ctx.save_for_backward(w, u, r, k, v, state_in)
+        return o
+
+    @staticmethod
+    def backward(ctx, go):
+        w, u, r, k, v, state_in = ctx.saved_tensors
+        dr, dk, dv, dw, du, ds = wkv5_backward(w, u, r, k, v, go.to(torch.bfloat16).contiguous(), state_in=state_in,
+                                               need_state_grad=state_in is not None and ctx.needs_input_grad[5])
+        return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds

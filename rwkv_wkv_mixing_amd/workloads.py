@@ -313,6 +313,13 @@ def make_wkv5(B, T, H, *, seed=0, w_range=(-4.0, 1.5), kv_std=1.0, with_state=Fa
     return Wkv5Problem(name or f"wkv5 B={B} T={T} H={H}", B, T, H, w, u, r, k, v, r_bits, k_bits, v_bits, S0)
 
 
+def wkv5_go(p: Wkv5Problem, *, seed=1, std=1.0) -> tuple[np.ndarray, np.ndarray]:
+    """A gradient of the output for a Wkv5Problem: go ~ N(0, std) of shape
+    [B, T, 64 H], rounded to bf16.  Returns (bits as uint16, values as float32)."""
+    rng = np.random.default_rng(seed)
+    return bf16_round(_normal(rng, std, (p.B, p.T, p.H * 64)))
+
+
 def wkv5_config(seed=0) -> Wkv5Problem:
     """A 7B-shaped layer in RWKV-5 form: B=8, T=1024, C=4096 as 64 heads of 64."""
     return make_wkv5(8, 1024, 64, seed=seed, name="wkv5 bf16 B=8 T=1024 H=64 N=64")

@@ -1,0 +1,218 @@
+"""GPU parity of the RWKV-5 backward (wkv5_backward) against the float64 oracle,
+through the C ABI.
+
+Bound, from the kernel's arithmetic (bf16 matrix-core operands, float32
+accumulation, adjoint state and tables; ub = 2^-8 is the unit roundoff of bf16).
+Every term of dr, dk, dv and dw passes through at most three bf16 roundings:
+  dv: the decay-scaled key, the bf16 copy of the adjoint state G (itself a sum
+      of terms with one rounding, the decay-scaled receptance), or the
+      receptance, the key and the attention entry;
+  dk: the bf16 G (two), or the bf16 C = go v^T entry and the scaled receptance;
+  dr: the bf16 chunk-start state (one rounding in the state-only forward, one
+      to bf16), or the bf16 C entry and the scaled key;
+  dw: G (one) times the bf16 chunk-start state (two), or two as above; its
+      in-block lag-weighted part is float32 elementwise.
+So |x_gpu - x| <= (3 ub (1 + 2^-7) + fp) * x_abs, with x_abs the oracle run
+on |r|, |k|, |v|, |go|, |u|, |S0|, |dS_T| (the sum of the terms' magnitudes)
+and fp = 2^-12 for float32 rounding: products and sums of a few hundred terms
+per chunk and the adjoint state rescaled once per chunk, over up to 16 chunks
+(at most ~2^-14 worst case).  dS0 = G before the first token: one rounding,
+(ub (1 + 2^-7) + fp) x_abs.  du is float32 throughout (exact bf16 products,
+float32 sums of at most a few hundred terms per element): 2^-14 x_abs.
+Inside a 16-token block the decay of channels with w > 8 is taken as 8 for
+terms more than one token apart (dr, dk, dv only); the bound adds the
+difference between the magnitudes with w' = min(w, 8) and with w, which is
+zero unless some w > 8.
+"""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import to_dev
+from oracle import wkv5_backward_ref, wkv5_forward_ref
+from rwkv_wkv_mixing_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+UB = 2.0 ** -8
+FP = 2.0 ** -12
+C3 = 3 * UB * (1 + 2.0 ** -7) + FP
+C1 = UB * (1 + 2.0 ** -7) + FP
+C_DU = 2.0 ** -14
+W_CAP = 8.0
+NAMES = ("dr", "dk", "dv", "dw", "du", "dS0")
+
+
+def ops():
+    from rwkv_wkv_mixing_amd import ops as O
+
+    return O
+
+
+def check_bound(name, got, ref, bound):
+    g = np.asarray(got, dtype=np.float64)
+    o = np.asarray(ref, dtype=np.float64)
+    assert g.shape == o.shape, (name, g.shape, o.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    err = np.abs(g - o)
+    ratio = err / (np.asarray(bound, dtype=np.float64) + 1e-30)
+    worst = float(ratio.max(initial=0.0))
+    print(f"  {name}: max_abs={float(err.max(initial=0.0)):.3e} worst_err/bound={worst:.3f}", flush=True)
+    if worst > 1.0:
+        idx = np.unravel_index(np.argmax(ratio), ratio.shape)
+        raise AssertionError(f"{name}: {int((ratio > 1).sum())} of {ratio.size} out of bound; worst at {idx}: "
+                             f"got {g[idx]!r} ref {o[idx]!r} bound {np.asarray(bound)[idx]!r}")
+
+
+def bounds(w, u, r, k, v, go, H, S0, dST):
+    """Per-element bounds of (dr, dk, dv, dw, du, dS0) as described above."""
+    a = lambda x: None if x is None else np.abs(x)
+    absx = wkv5_backward_ref(w, np.abs(u), np.abs(r), np.abs(k), np.abs(v), np.abs(go), H, a(S0), a(dST))
+    wc = np.minimum(w, W_CAP)
+    if np.array_equal(wc, w):
+        capx = absx
+    else:
+        capx = wkv5_backward_ref(wc, np.abs(u), np.abs(r), np.abs(k), np.abs(v), np.abs(go), H, a(S0), a(dST))
+    out = []
+    for i in range(3):  # dr, dk, dv: rounding on the capped magnitudes plus the cap's own change
+        out.append(C3 * np.abs(capx[i]) + np.abs(capx[i] - absx[i]))
+    out.append(C3 * np.abs(absx[3]))
+    out.append(C_DU * np.abs(absx[4]))
+    out.append(C1 * np.abs(absx[5]))
+    return out
+
+
+def bf16_dev(bits):
+    return to_dev(None, DEV, bits)
+
+
+def run(p, go_bits, dST=None, need_state_grad=True):
+    w, u = to_dev(p.w, DEV), to_dev(p.u, DEV)
+    S0 = None if p.S0 is None else to_dev(p.S0, DEV)
+    gS = None if dST is None else to_dev(dST, DEV)
+    res = ops().wkv5_backward(w, u, bf16_dev(p.r_bits), bf16_dev(p.k_bits), bf16_dev(p.v_bits), bf16_dev(go_bits),
+                              state_in=S0, grad_state_out=gS, need_state_grad=need_state_grad)
+    torch.cuda.synchronize()
+    return [None if x is None else x.cpu().numpy() for x in res]
+
+
+def check(p, go, got, dST=None, name=None):
+    name = name or p.name
+    ref = wkv5_backward_ref(p.w, p.u, p.r, p.k, p.v, go, p.H, p.S0, dST)
+    bnd = bounds(p.w.astype(np.float64), p.u, p.r, p.k, p.v, go, p.H, p.S0, dST)
+    for i, n in enumerate(NAMES):
+        if got[i] is not None:
+            check_bound(f"{name} {n}", got[i], ref[i], bnd[i])
+
+
+SHAPES = [(2, 1, 1), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_shapes(B, T, H, with_state):
+    """Whole and ragged 64-token chunks, one to several heads, from the zero
+    state and from a given one (then also with a final-state gradient)."""
+    p = W.make_wkv5(B, T, H, seed=B * 100 + T + H + 7, with_state=with_state)
+    go_bits, go = W.wkv5_go(p, seed=B + T + H)
+    dST = np.random.default_rng(T).standard_normal((B, H, 64, 64)).astype(np.float32) if with_state else None
+    print(f"case {p.name} state={with_state}", flush=True)
+    check(p, go, run(p, go_bits, dST), dST)
+
+
+@pytest.mark.parametrize("rates", [(20.0, 80.0), (1e-6, 1e-3), (7.0, 12.0), (2.0, 9.0)])
+def test_extreme_decay_rates(rates):
+    """Decay factors from e^{-80} to nearly 1, and around the in-block cap of 8."""
+    p = W.make_wkv5(2, 150, 2, seed=17, with_state=True)
+    p.w[:] = np.exp(np.random.default_rng(18).uniform(np.log(rates[0]), np.log(rates[1]), p.w.shape)).astype(np.float32)
+    go_bits, go = W.wkv5_go(p, seed=19)
+    print(f"case rates {rates}", flush=True)
+    check(p, go, run(p, go_bits), name=f"rates {rates}")
+
+
+def test_full_size_sampled_heads():
+    """B=8, T=1024, 64 heads of 64 (the benchmarked shape, same entry point):
+    every output of two heads against the oracle run on those heads alone
+    (heads are independent; dw, du sum over the batch rows of their head)."""
+    p = W.wkv5_config(seed=3)
+    go_bits, go = W.wkv5_go(p, seed=4)
+    print(f"case {p.name}", flush=True)
+    got = run(p, go_bits, need_state_grad=True)
+    for h in (0, 37):
+        sl = slice(64 * h, 64 * h + 64)
+        sub = W.Wkv5Problem(f"{p.name} head {h}", p.B, p.T, 1, p.w[h:h + 1], p.u[h:h + 1], p.r[:, :, sl], p.k[:, :, sl],
+                            p.v[:, :, sl], None, None, None, None)
+        part = [got[0][:, :, sl], got[1][:, :, sl], got[2][:, :, sl], got[3][h:h + 1], got[4][h:h + 1],
+                got[5][:, h:h + 1]]
+        check(sub, go[:, :, sl], part, name=sub.name)
+
+
+def test_split_sequence_chains_through_the_state():
+    """Forward in two segments carrying the state; backward of the second
+    segment first, its dS0 handed to the first as the final-state gradient:
+    the pieces match the whole sequence's oracle gradients."""
+    p = W.make_wkv5(2, 300, 2, seed=23, with_state=True)
+    go_bits, go = W.wkv5_go(p, seed=24)
+    O = ops()
+    w, u = to_dev(p.w, DEV), to_dev(p.u, DEV)
+    r, k, v, g = (bf16_dev(b) for b in (p.r_bits, p.k_bits, p.v_bits, go_bits))
+    S0 = to_dev(p.S0, DEV)
+    ref = wkv5_backward_ref(p.w, p.u, p.r, p.k, p.v, go, p.H, p.S0)
+    bnd = bounds(p.w.astype(np.float64), p.u, p.r, p.k, p.v, go, p.H, p.S0, None)
+    for t1 in (64, 100):
+        sl = lambda x, a, b: x[:, a:b].contiguous()
+        _, S1 = O.wkv5_forward(w, u, sl(r, 0, t1), sl(k, 0, t1), sl(v, 0, t1), state_in=S0, return_state=True)
+        b2 = O.wkv5_backward(w, u, sl(r, t1, 300), sl(k, t1, 300), sl(v, t1, 300), sl(g, t1, 300), state_in=S1,
+                             need_state_grad=True)
+        b1 = O.wkv5_backward(w, u, sl(r, 0, t1), sl(k, 0, t1), sl(v, 0, t1), sl(g, 0, t1), state_in=S0,
+                             grad_state_out=b2[5], need_state_grad=True)
+        torch.cuda.synchronize()
+        print(f"case split at {t1}", flush=True)
+        for i in range(3):
+            whole = torch.cat([b1[i], b2[i]], dim=1).cpu().numpy()
+            check_bound(f"split {t1} {NAMES[i]}", whole, ref[i], 2 * bnd[i])
+        check_bound(f"split {t1} dw", (b1[3] + b2[3]).cpu().numpy(), ref[3], 2 * bnd[3])
+        check_bound(f"split {t1} du", (b1[4] + b2[4]).cpu().numpy(), ref[4], 2 * bnd[4])
+        check_bound(f"split {t1} dS0", b1[5].cpu().numpy(), ref[5], 2 * bnd[5])
+
+
+def test_empty_inputs_and_determinism():
+    O = ops()
+    p = W.make_wkv5(2, 130, 3, seed=25, with_state=True)
+    go_bits, _ = W.wkv5_go(p, seed=26)
+    a = run(p, go_bits)
+    b = run(p, go_bits)
+    for x, y, n in zip(a, b, NAMES):
+        assert np.array_equal(x, y), f"{n} differs between two identical calls"
+    w, u = to_dev(p.w, DEV), to_dev(p.u, DEV)
+    e = torch.empty((2, 0, 192), dtype=torch.bfloat16, device=DEV)
+    gS = torch.randn((2, 3, 64, 64), device=DEV)
+    dr, dk, dv, dw, du, ds = O.wkv5_backward(w, u, e, e, e, e, grad_state_out=gS, need_state_grad=True)
+    torch.cuda.synchronize()
+    assert dr.shape == (2, 0, 192)
+    assert torch.count_nonzero(dw) == 0 and torch.count_nonzero(du) == 0
+    assert torch.equal(ds, gS), "with no tokens dS0 is the final state's gradient"
+    e0 = torch.empty((0, 5, 192), dtype=torch.bfloat16, device=DEV)
+    _, _, _, dw, du, _ = O.wkv5_backward(w, u, e0, e0, e0, e0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw) == 0 and torch.count_nonzero(du) == 0
+
+
+def test_autograd_function_matches_the_entry_point():
+    """Wkv5Function.backward is wkv5_backward on the same inputs (bf16 go)."""
+    O = ops()
+    p = W.make_wkv5(2, 70, 2, seed=27, with_state=True)
+    go_bits, _ = W.wkv5_go(p, seed=28)
+    w, u = to_dev(p.w, DEV).requires_grad_(), to_dev(p.u, DEV).requires_grad_()
+    r, k, v = (bf16_dev(b).requires_grad_() for b in (p.r_bits, p.k_bits, p.v_bits))
+    S0 = to_dev(p.S0, DEV).requires_grad_()
+    g = bf16_dev(go_bits)
+    o = O.Wkv5Function.apply(w, u, r, k, v, S0)
+    o.backward(g.float())
+    direct = O.wkv5_backward(w.detach(), u.detach(), r.detach(), k.detach(), v.detach(), g, state_in=S0.detach(),
+                             need_state_grad=True)
+    torch.cuda.synchronize()
+    for got, ref, n in ((r.grad, direct[0], "dr"), (k.grad, direct[1], "dk"), (v.grad, direct[2], "dv"),
+                        (w.grad, direct[3], "dw"), (u.grad, direct[4], "du"), (S0.grad, direct[5], "dS0")):
+        assert torch.equal(got.float(), ref.to(got.dtype).float()), n
