@@ -29,6 +29,7 @@ WRITE_SIZE counters).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import glob
 import hashlib
 import json
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -464,6 +465,98 @@ def bench_wkv5(args):
     return out
 
 
+def bench_wkv5_train(args):
+    """RWKV-5 training step at B=8 T=1024 C=4096 (64 heads of 64): the forward
+    saving its chunk-start states, then the backward from them (dr, dk, dv,
+    dw, du).  Algorithmic bytes per channel-token: forward r, k, v in (6 B),
+    o out (4 B), states out (2 B); backward r, k, v, go in (8 B), states in
+    (2 B), dr, dk, dv out (12 B)."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops, workloads as W
+
+    dev = torch.device("cuda:0")
+    p = W.wkv5_config()
+    B, T, H = p.B, p.T, p.H
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    w, u = torch.from_numpy(p.w).to(dev), torch.from_numpy(p.u).to(dev)
+    go_bits, go_vals = W.wkv5_go(p, seed=1)
+    base = [up(p.r_bits), up(p.k_bits), up(p.v_bits), up(go_bits)]
+    sets = [[t if i == 0 else t.clone() for t in base] for i in range(max(args.sets, 2))]
+    C = 64 * H
+    o = torch.empty((B, T, C), device=dev)
+    ck = ops.new_wkv5_ckpt(B, T, H, dev)
+    grads = [torch.empty((B, T, C), device=dev) for _ in range(3)]
+    dw, du = torch.empty((H, 64), device=dev), torch.empty((H, 64), device=dev)
+    from rwkv_wkv_mixing_amd import _lib as L
+    lib = L.lib()
+    nws = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64, 1))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def fwd(i):
+        r, k, v, _ = sets[i % len(sets)]
+        L.check("wkv5_forward", lib.wkv5_forward(B, T, H, 64, L.WKV_BF16, ptr(w), ptr(u), ptr(r), ptr(k), ptr(v),
+                                                 ptr(o), None, None, ptr(ck), stream))
+
+    def bwd(i):
+        r, k, v, g = sets[i % len(sets)]
+        L.check("wkv5_backward", lib.wkv5_backward(B, T, H, 64, L.WKV_BF16, ptr(w), ptr(u), ptr(r), ptr(k), ptr(v),
+                                                   ptr(g), None, None, ptr(grads[0]), ptr(grads[1]), ptr(grads[2]),
+                                                   ptr(dw), ptr(du), None, ptr(ck), ptr(ws), nws, stream))
+
+    for i in range(args.warmup):
+        fwd(i)
+        bwd(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd(i)
+        bwd(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        fwd(i)
+        evs[i][1].record()
+        bwd(i)
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    st_f = stats_us([a.elapsed_time(b) for a, b, _ in evs])
+    st_b = stats_us([b.elapsed_time(c) for _, b, c in evs])
+    n = B * T * C
+    alg_b = 22 * n
+    achieved = alg_b / (st_b["mean"] * 1e-6) / 1e9
+    out = {
+        "metric": "RWKV-5 matrix-state WKV forward+backward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
+        "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": p.name + " fwd+bwd", "B": B, "T": T, "H": H, "N": 64},
+        "call_us": {"wkv5_forward(ckpt)": st_f, "wkv5_backward(ckpt)": st_b},
+        "roofline": {"bound": "hbm", "kernel": "wkv5_backward (backward kernel + dw/du batch sum)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("wkv5train_bf16_B8_T1024_H64", "wkv5_bwd"),
+                     "alg_bytes_per_launch": alg_b},
+    }
+    if not args.no_cpu:
+        # the float64 numpy oracle on batch rows 0 and 1 (all 64 heads, all tokens): forward, then backward
+        from oracle import wkv5_backward_ref, wkv5_forward_ref
+
+        t0 = time.perf_counter()
+        wkv5_forward_ref(p.w, p.u, p.r[:2], p.k[:2], p.v[:2], H)
+        wkv5_backward_ref(p.w, p.u, p.r[:2], p.k[:2], p.v[:2], go_vals[:2], H)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 2 * T * C / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"batch rows 0-1 of the workload (all 64 heads x {T} tokens, {2 * T * C} "
+                                         f"channel*tokens): the float64 numpy oracle's forward and backward, "
+                                         f"{t_np:.2f} s"}
+    return out
+
+
 def bench_copy(args):
     """A plain copy of 1 GiB (reads 1 GiB, writes 1 GiB): HBM counter calibration."""
     import torch
@@ -500,8 +593,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy", "shift", "wkv5"):
-        out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5}[args.workload](args)
+    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train"):
+        out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
+               "wkv5train": bench_wkv5_train}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

@@ -226,17 +226,25 @@ wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
  *           for the zero state.
  * s_out     [B, H, 64, 64] float32 state after token T, or NULL; may be s_in
  *           (updated in place).  With T == 0 it receives s_in (or zeros).
+ * ckpt      NULL, or wkv5_ckpt_bytes() bytes (16-byte aligned) that receive
+ *           the state before every 64-token chunk, for a later wkv5_backward
+ *           on the same inputs (2 bytes per channel and token written).
  * Errors as the other entry points (WKV_EINVAL also for N != 64).
  */
 wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
                           const float* w, const float* u, const void* r, const void* k, const void* v,
-                          float* o, const float* s_in, float* s_out, void* hip_stream);
+                          float* o, const float* s_in, float* s_out, void* ckpt, void* hip_stream);
 
-/* Bytes of scratch memory wkv5_backward needs for (B, T, H, N): the bf16
- * state before every 64-token chunk (B H ceil(T/64) 64 64 2 bytes, rounded up
- * to 256) plus 2 x 64 float32 per (batch row, head).  0 for invalid
- * arguments or T == 0. */
-size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
+/* Bytes of wkv5_forward's chunk-start states for (B, T, H, N): bf16
+ * [B, H, ceil(T/64), 64, 64] (key-major), rounded up to 256.  Opaque to the
+ * caller: only wkv5_backward reads them.  0 for invalid arguments. */
+size_t wkv5_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
+
+/* Bytes of scratch memory wkv5_backward needs: 2 x 64 float32 per (batch
+ * row, head), plus wkv5_ckpt_bytes() when it is called without a ckpt
+ * (have_ckpt == 0) and recomputes the chunk-start states itself.  0 for
+ * invalid arguments or B*T == 0. */
+size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt);
 
 /*
  * wkv5_backward - gradients of wkv5_forward.
@@ -251,8 +259,9 @@ size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N)
  *     du   = sum_{b,t} r_t . k_t (v_t . go_t)
  *     dw   = -e^{-w} . sum_{b,t} rowsum(G_t . S_{t-1})
  *     dS0  = G_0 (before the first token)
- * The call first recomputes the state before every chunk (a forward pass
- * without outputs, into the workspace), then walks the chunks backwards with
+ * The call reads the state before every chunk from ckpt or, when ckpt is NULL,
+ * first recomputes it (a forward pass without outputs, into the workspace),
+ * then walks the chunks backwards with
  * the same bf16 matrix-core products and float32 accumulation as the forward;
  * dw and du are summed over the batch in a fixed order (bitwise
  * reproducible).  Inside a 16-token block, channels with w above 8 use 8 for
@@ -268,15 +277,17 @@ size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N)
  *           with B*T == 0 it receives ds_out (or zeros).  It may be the
  *           ds_out buffer (each workgroup reads its part of ds_out before
  *           writing the same part of ds_in).
- * workspace wkv5_backward_workspace_bytes() bytes, 256-byte aligned;
- *           clobbered.  Not needed when B*T == 0.
+ * ckpt      the ckpt a wkv5_forward call on the same w, u, r, k, v and s_in
+ *           wrote, or NULL (then s_in is read to recompute it).
+ * workspace wkv5_backward_workspace_bytes(..., ckpt != NULL) bytes, 256-byte
+ *           aligned; clobbered.  Not needed when B*T == 0.
  * Errors as the other entry points (WKV_EINVAL also for N != 64; nothing
  * is written on an error).
  */
 wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
                            const float* w, const float* u, const void* r, const void* k, const void* v,
                            const void* go, const float* s_in, const float* ds_out, float* dr, float* dk,
-                           float* dv, float* dw, float* du, float* ds_in, void* workspace,
+                           float* dv, float* dw, float* du, float* ds_in, const void* ckpt, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
 
 /*

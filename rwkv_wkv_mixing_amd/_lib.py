@@ -27,6 +27,7 @@ EXPORTS = (
     "wkv_backward_gated",
     "wkv_step",
     "wkv5_forward",
+    "wkv5_ckpt_bytes",
     "wkv5_backward_workspace_bytes",
     "wkv5_backward",
     "wkv_token_shift_workspace_bytes",
@@ -83,12 +84,14 @@ def declare(L):
     L.wkv_step.restype = i32
     L.wkv_step.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, vp]
     L.wkv5_forward.restype = i32
-    L.wkv5_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp]
+    L.wkv5_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp]
+    L.wkv5_ckpt_bytes.restype = sz
+    L.wkv5_ckpt_bytes.argtypes = [i64, i64, i64, i64]
     L.wkv5_backward_workspace_bytes.restype = sz
-    L.wkv5_backward_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.wkv5_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     L.wkv5_backward.restype = i32
-    L.wkv5_backward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz,
-                                vp]
+    L.wkv5_backward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp, vp,
+                                sz, vp]
     L.wkv_token_shift_workspace_bytes.restype = sz
     L.wkv_token_shift_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.wkv_token_shift.restype = i32

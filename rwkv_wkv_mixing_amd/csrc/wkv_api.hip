@@ -260,7 +260,7 @@ Wkv5Plan wkv5_plan(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype) {
     const int64_t nch = (T + 63) / 64;
     if (!mul3(p.bh, nch, 64 * 64 * 2, &ck) || ck > (int64_t{1} << 60)) return Wkv5Plan{WKV_ESIZE, 0, 0, 0, 0};
     p.ckpt_bytes = (static_cast<size_t>(ck) + 255) / 256 * 256;
-    p.ws_bytes = T > 0 ? p.ckpt_bytes + static_cast<size_t>(p.bh) * 2 * 64 * 4 : 0;
+    p.ws_bytes = T > 0 ? static_cast<size_t>(p.bh) * 2 * 64 * 4 : 0;  // without the chunk-start states
     return p;
 }
 
@@ -268,14 +268,20 @@ Wkv5Plan wkv5_plan(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype) {
 
 extern "C" {
 
-size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N) {
+size_t wkv5_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N) {
     const Wkv5Plan p = wkv5_plan(B, T, H, N, WKV_BF16);
-    return p.st == WKV_OK ? p.ws_bytes : 0;
+    return p.st == WKV_OK ? p.ckpt_bytes : 0;
+}
+
+size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, WKV_BF16);
+    if (p.st != WKV_OK || p.ws_bytes == 0) return 0;
+    return p.ws_bytes + (have_ckpt ? 0 : p.ckpt_bytes);
 }
 
 wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                           const float* u, const void* r, const void* k, const void* v, float* o,
-                          const float* s_in, float* s_out, void* hip_stream) {
+                          const float* s_in, float* s_out, void* ckpt, void* hip_stream) {
     const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
     if (p.st != WKV_OK) return p.st;
     const int64_t ns = p.ns;
@@ -284,17 +290,20 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (T == 0) return hip_status(wkv::launch_wkv5_state_copy(s_in, s_out, ns, stream));
     if (!w || !u || !r || !k || !v || !o) return WKV_EINVAL;
-    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16))
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
     wkv::Wkv5Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), o, s_in, s_out};
+    a.ckpt = static_cast<uint16_t*>(ckpt);
     return hip_status(wkv::launch_wkv5_fwd(a, stream));
 }
 
 wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                            const float* u, const void* r, const void* k, const void* v, const void* go,
                            const float* s_in, const float* ds_out, float* dr, float* dk, float* dv, float* dw,
-                           float* du, float* ds_in, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                           float* du, float* ds_in, const void* ckpt, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
     const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
     if (p.st != WKV_OK) return p.st;
     if (H == 0) return WKV_OK;
@@ -312,20 +321,25 @@ wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
     }
     if (!w || !u || !r || !k || !v || !go || !dr || !dk || !dv) return WKV_EINVAL;
     if (!aligned(w, 4) || !aligned(u, 4) || !aligned(dr, 4) || !aligned(dk, 4) || !aligned(dv, 4) ||
-        (s_in && !aligned(s_in, 4)) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(go, 16))
+        (s_in && !aligned(s_in, 4)) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(go, 16) ||
+        (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
-    if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)) return WKV_EWORKSPACE;
-    auto* ckpt = static_cast<uint16_t*>(workspace);
-    auto* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ckpt_bytes);
+    const size_t need = p.ws_bytes + (ckpt ? 0 : p.ckpt_bytes);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    auto* part = static_cast<float*>(workspace);
     const auto* r16 = static_cast<const uint16_t*>(r);
     const auto* k16 = static_cast<const uint16_t*>(k);
     const auto* v16 = static_cast<const uint16_t*>(v);
-    // the states before every chunk, recomputed by a state-only forward pass
-    wkv::Wkv5Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
-    fa.ckpt = ckpt;
-    hipError_t e = wkv::launch_wkv5_fwd(fa, stream);
-    if (e != hipSuccess) return hip_status(e);
-    wkv::Wkv5BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), ckpt, ds_out,
+    const uint16_t* states = static_cast<const uint16_t*>(ckpt);
+    if (ckpt == nullptr) {  // the states before every chunk, recomputed by a state-only forward pass
+        auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + p.ws_bytes);
+        wkv::Wkv5Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
+        fa.ckpt = tmp;
+        hipError_t e = wkv::launch_wkv5_fwd(fa, stream);
+        if (e != hipSuccess) return hip_status(e);
+        states = tmp;
+    }
+    wkv::Wkv5BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), states, ds_out,
                         dr, dk, dv, part, dw, du, ds_in};
     return hip_status(wkv::launch_wkv5_bwd(ba, stream));
 }

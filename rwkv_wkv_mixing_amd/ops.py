@@ -308,12 +308,22 @@ def token_shift_mix(mu, x, x_prev=None):
     return TokenShiftFunction.apply(mu, x, x_prev)
 
 
-def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None):
+def wkv5_ckpt_bytes(B: int, T: int, H: int) -> int:
+    return int(L.lib().wkv5_ckpt_bytes(B, T, H, 64))
+
+
+def new_wkv5_ckpt(B: int, T: int, H: int, device) -> torch.Tensor:
+    """Buffer for wkv5_forward's chunk-start states (opaque bytes)."""
+    return torch.empty(max(wkv5_ckpt_bytes(B, T, H), 1), dtype=torch.uint8, device=device)
+
+
+def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None):
     """RWKV-5 matrix-state WKV: o [B, T, C] float32 from w, u [H, 64] float32 and
     r, k, v [B, T, C] bfloat16 (C = 64 H).  state_in: [B, H, 64, 64] float32 or
     None (zero).  state_out: tensor to receive the final state (may be
     state_in); with return_state and no state_out one is allocated and the
-    call returns (o, state)."""
+    call returns (o, state).  ckpt: None or a new_wkv5_ckpt() buffer that
+    receives the chunk-start states for wkv5_backward."""
     _need(r, "r", torch.bfloat16)
     dev = r.device
     B, T, C = r.shape
@@ -333,13 +343,18 @@ def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
         state_out = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev)
     if state_out is not None:
         _need(state_out, "state_out", torch.float32, (B, H, 64, 64), dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.uint8, None, dev)
+        if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
+            raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
     st = L.lib().wkv5_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
-                              _p(state_out), _stream(dev))
+                              _p(state_out), _p(ckpt), _stream(dev))
     L.check("wkv5_forward", st)
     return (out, state_out) if return_state else out
 
 
-def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, workspace=None):
+def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, ckpt=None,
+                  workspace=None):
     """Gradients of sum <go, o> + <grad_state_out, S_T> for
     (o, S_T) = wkv5_forward(w, u, r, k, v, state_in=state_in, return_state=True):
     returns (dr, dk, dv [B, T, C] float32, dw, du [H, 64] float32 summed over
@@ -363,13 +378,17 @@ def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need
     du = torch.empty((H, 64), dtype=torch.float32, device=dev)
     ds = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev) if need_state_grad else None
     lib = L.lib()
-    nbytes = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64))
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.uint8, None, dev)
+        if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
+            raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
+    nbytes = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64, int(ckpt is not None)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
     st = lib.wkv5_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
-                           _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(workspace),
+                           _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace),
                            workspace.numel() * workspace.element_size(), _stream(dev))
     L.check("wkv5_backward", st)
     return dr, dk, dv, dw, du, ds
@@ -381,13 +400,16 @@ class Wkv5Function(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, w, u, r, k, v, state_in=None):
-        o = wkv5_forward(w, u, r, k, v, state_in=state_in)
-        ctx.save_for_backward(w, u, r, k, v, state_in)
+        B, T, C = r.shape
+        ckpt = new_wkv5_ckpt(B, T, C // 64, r.device)
+        o = wkv5_forward(w, u, r, k, v, state_in=state_in, ckpt=ckpt)
+        ctx.save_for_backward(w, u, r, k, v, state_in, ckpt)
         return o
 
     @staticmethod
     def backward(ctx, go):
-        w, u, r, k, v, state_in = ctx.saved_tensors
+        w, u, r, k, v, state_in, ckpt = ctx.saved_tensors
         dr, dk, dv, dw, du, ds = wkv5_backward(w, u, r, k, v, go.to(torch.bfloat16).contiguous(), state_in=state_in,
-                                               need_state_grad=state_in is not None and ctx.needs_input_grad[5])
+                                               need_state_grad=state_in is not None and ctx.needs_input_grad[5],
+                                               ckpt=ckpt)
         return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds

@@ -210,8 +210,8 @@ def test_token_shift_validation(lib):
     assert shift_bwd(lib, 1, 4, 0, 3, L.WKV_F32, *[None] * 7) == L.WKV_OK
 
 
-def wkv5(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None):
-    return lib.wkv5_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), None)
+def wkv5(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None, ck=None):
+    return lib.wkv5_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), P(ck), None)
 
 
 def test_wkv5_validation(lib):
@@ -226,5 +226,49 @@ def test_wkv5_validation(lib):
     assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x + 2, x, x, x) == L.WKV_EALIGN   # r, k, v 16-byte aligned
     assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x, x, x, x + 2) == L.WKV_EALIGN
     assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, *args, si=x + 1) == L.WKV_EALIGN
+    assert wkv5(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ck=x + 8) == L.WKV_EALIGN   # ckpt 16-byte aligned
     assert wkv5(lib, 0, 4, 2, 64, L.WKV_BF16, *[None] * 6) == L.WKV_OK
     assert wkv5(lib, 2, 4, 0, 64, L.WKV_BF16, *[None] * 6) == L.WKV_OK
+
+
+def test_wkv5_workspace_sizes(lib):
+    # chunk-start states: bf16 64 x 64 per (batch row, head, 64-token chunk); partial sums: 2 x 64 float32
+    assert lib.wkv5_ckpt_bytes(2, 100, 3, 64) == 2 * 3 * 2 * 64 * 64 * 2
+    assert lib.wkv5_ckpt_bytes(1, 1, 1, 64) == 64 * 64 * 2
+    assert lib.wkv5_ckpt_bytes(1, 1, 1, 32) == 0
+    assert lib.wkv5_backward_workspace_bytes(2, 100, 3, 64, 1) == 2 * 3 * 2 * 64 * 4
+    assert lib.wkv5_backward_workspace_bytes(2, 100, 3, 64, 0) == 2 * 3 * 2 * 64 * 4 + 2 * 3 * 2 * 64 * 64 * 2
+    assert lib.wkv5_backward_workspace_bytes(2, 0, 3, 64, 0) == 0
+    assert lib.wkv5_backward_workspace_bytes(2, 10, 3, 48, 0) == 0
+
+
+def wkv5_bwd(lib, B, T, H, N, dt, w, u, r, k, v, go, dr, dk, dv, dw, du, si=None, dso=None, dsi=None, ck=None,
+             ws=None, nws=0):
+    return lib.wkv5_backward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(go), P(si), P(dso), P(dr), P(dk), P(dv),
+                             P(dw), P(du), P(dsi), P(ck), P(ws), nws, None)
+
+
+def test_wkv5_backward_validation(lib):
+    x = A16
+    args = [x] * 11
+    need = lib.wkv5_backward_workspace_bytes(1, 4, 2, 64, 0)
+    ok = dict(ws=x, nws=need)
+    assert wkv5_bwd(lib, 1, 4, 2, 32, L.WKV_BF16, *args, **ok) == L.WKV_EINVAL       # head size must be 64
+    assert wkv5_bwd(lib, 1, -4, 2, 64, L.WKV_BF16, *args, **ok) == L.WKV_EINVAL
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_F32, *args, **ok) == L.WKV_EDTYPE        # bf16 operands only
+    assert wkv5_bwd(lib, 1 << 30, 1 << 30, 1 << 10, 64, L.WKV_BF16, *args, **ok) == L.WKV_ESIZE
+    assert wkv5_bwd(lib, 1, 4, 0, 64, L.WKV_BF16, *[None] * 11) == L.WKV_OK          # no heads: nothing to do
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args[:9], None, x, **ok) == L.WKV_EINVAL   # dw NULL
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args[:9], x + 2, x, **ok) == L.WKV_EALIGN
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, dso=x + 1, **ok) == L.WKV_EALIGN
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, dsi=x + 1, **ok) == L.WKV_EALIGN
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, None, *args[3:], **ok) == L.WKV_EINVAL  # r NULL
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x, x, x, None, *args[6:], **ok) == L.WKV_EINVAL  # go NULL
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x, x, x, x + 2, *args[6:], **ok) == L.WKV_EALIGN  # go
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ck=x + 8, **ok) == L.WKV_EALIGN
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args) == L.WKV_EWORKSPACE
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=need - 1) == L.WKV_EWORKSPACE
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x + 16, nws=need) == L.WKV_EWORKSPACE
+    # with a ckpt only the partial sums are needed
+    small = lib.wkv5_backward_workspace_bytes(1, 4, 2, 64, 1)
+    assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=small - 1, ck=x) == L.WKV_EWORKSPACE

@@ -216,3 +216,26 @@ def test_autograd_function_matches_the_entry_point():
     for got, ref, n in ((r.grad, direct[0], "dr"), (k.grad, direct[1], "dk"), (v.grad, direct[2], "dv"),
                         (w.grad, direct[3], "dw"), (u.grad, direct[4], "du"), (S0.grad, direct[5], "dS0")):
         assert torch.equal(got.float(), ref.to(got.dtype).float()), n
+
+
+@pytest.mark.parametrize("B,T,H", [(2, 130, 3), (1, 64, 1)])
+def test_forward_ckpt_gives_the_same_backward(B, T, H):
+    """States saved by wkv5_forward (ckpt) and states recomputed by the
+    backward's own state-only pass are the same bits, so both backwards agree
+    exactly; the forward's outputs do not change when it saves them."""
+    O = ops()
+    p = W.make_wkv5(B, T, H, seed=29 + T, with_state=True)
+    go_bits, _ = W.wkv5_go(p, seed=30)
+    w, u = to_dev(p.w, DEV), to_dev(p.u, DEV)
+    r, k, v, g = (bf16_dev(b) for b in (p.r_bits, p.k_bits, p.v_bits, go_bits))
+    S0 = to_dev(p.S0, DEV)
+    ck = O.new_wkv5_ckpt(B, T, H, DEV)
+    o1 = O.wkv5_forward(w, u, r, k, v, state_in=S0, ckpt=ck)
+    o2 = O.wkv5_forward(w, u, r, k, v, state_in=S0)
+    a = O.wkv5_backward(w, u, r, k, v, g, state_in=S0, need_state_grad=True, ckpt=ck)
+    b = O.wkv5_backward(w, u, r, k, v, g, state_in=S0, need_state_grad=True)
+    torch.cuda.synchronize()
+    print(f"case ckpt B={B} T={T} H={H}", flush=True)
+    assert torch.equal(o1, o2)
+    for x, y, n in zip(a, b, NAMES):
+        assert torch.equal(x, y), n
