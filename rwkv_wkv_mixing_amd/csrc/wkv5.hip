@@ -351,7 +351,7 @@ struct Wkv5BwdShared {
     float pe[17][kPadF];       // e^{w' m}, m = -8..8, w' = min(w, kWCapB)
     float uu[kN];
     float cd[kLc];             // C[s][s] = go_s . v_s
-    float cdg[kWaves5][16][17];  // each wave's diagonal block of C, [s][sig], sig < s (float32)
+    float cdg[kWaves5][16][16];  // each wave's diagonal block of C, [s][sig], sig < s (float32)
 };
 
 __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P) {
@@ -397,9 +397,21 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
     auto rd = [](const uint16_t(*X)[kN], int t, int c) { return bf(X[t][sw(t, c)]); };
     auto row4s = [](const uint16_t(*X)[kN], int t, int c4) { return row4(&X[t][sw(t, c4)]); };
     auto raw4s = [](const uint16_t(*X)[kN], int t, int c4) { return raw4(&X[t][sw(t, c4)]); };
-    // four consecutive tokens t0..t0+3 of channel c as a raw operand (a column of a staged input)
-    auto col4 = [](const uint16_t(*X)[kN], int t0, int c) {
-        return as_s4(X[t0][sw(t0, c)], X[t0 + 1][sw(t0 + 1, c)], X[t0 + 2][sw(t0 + 2, c)], X[t0 + 3][sw(t0 + 3, c)]);
+    // tokens t0 + 4 g + e (e = 0..3) of channel c0 + l16 of a staged input (a column), as a raw
+    // operand, by one transposing LDS read: in each group of 16 lanes, lane q reads four
+    // channels of one row and lane j receives element j % 4 of lane 4 e + j / 4's read, so lane
+    // (l16, g) names row t0 + 4 g + l16 / 4, channels c0 + 4 (l16 % 4) .. + 3
+    auto colT = [&](const uint16_t(*X)[kN], int tb, int c0) {
+        const int t = tb + 4 * g + (l16 >> 2), c = c0 + 4 * (l16 & 3);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)&X[t][sw(t, c)]);
+    };
+    auto colTp = [&](const uint16_t(*X)[kPadH], int tb, int c0) {  // the same for a padded, unswizzled tile
+        const int t = tb + 4 * g + (l16 >> 2), c = c0 + 4 * (l16 & 3);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)&X[t][c]);
+    };
+    auto colTf = [&](const uint16_t(*X)[kN], int tb, int c0) {
+        const u16x4 x = __builtin_bit_cast(u16x4, colT(X, tb, c0));
+        return f4{bf(x[0]), bf(x[1]), bf(x[2]), bf(x[3])};
     };
 
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
@@ -441,25 +453,31 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
             if (4 * g + e == l16) sm.cd[P0 + l16] = Cpp[e];
         wait_lds_reads();
 
-        const int sig = P0 + l16;  // this lane's key token as an m / n index
+        // Each part below first builds its small A operands (8 registers a set), then walks
+        // the output's 16-column tiles in a rolled loop with one accumulator, storing each tile;
+        // the per-channel dw / du partials of tile I rotate into slot 0 for its iteration.
+        const int sig = P0 + l16;  // this lane's key token as an m index
+        const int mid = P0 + 8;    // the diagonal block's reference token
+        auto rot = [](float (&x)[4]) {
+            const float t = x[0];
+            x[0] = x[1];
+            x[1] = x[2];
+            x[2] = x[3];
+            x[3] = t;
+        };
         // ---- dv: (k . d^{n-1-sig}) G1 + sum_{s >= sig} A[s][sig] go_s -------------------------
         {
-            f4 D[4];
-#pragma unroll
-            for (int J = 0; J < 4; ++J) D[J] = f4{0.f, 0.f, 0.f, 0.f};
             const int nk = nv - 1 - sig;
+            s4 aK[4];  // [m = sig][k = i]: k_sig,i d_i^{n-1-sig} (zero past the chunk's end)
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const int c4 = 16 * I + 4 * g;
-                const s4 a = nk >= 0 ? mul_pack(row4s(K, sig, c4), frow4(&sm.pw[nk >= 0 ? nk : 0][c4])) : s4{0, 0, 0, 0};
-#pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j = 16 * J + l16;
-                    D[J] = mfma(a, as_s4(sm.gs[c4][j], sm.gs[c4 + 1][j], sm.gs[c4 + 2][j], sm.gs[c4 + 3][j]), D[J]);
-                }
+                aK[I] = nk >= 0 ? mul_pack(row4s(K, sig, c4), frow4(&sm.pw[nk >= 0 ? nk : 0][c4])) : s4{0, 0, 0, 0};
             }
-#pragma unroll 1
+            s4 aA[4];  // aA[Q], Q >= wv: [m = sig][k = s]: A[s = 16 Q + 4 g + e][sig = P0 + l16]
+#pragma unroll
             for (int Q = 0; Q < 4; ++Q) {
+                aA[Q] = s4{0, 0, 0, 0};
                 if (Q < wv) continue;
                 f4 At = {0.f, 0.f, 0.f, 0.f};  // lane: A[s = 16 Q + 4 g + e][sig = P0 + l16]
                 const int s_m = 16 * Q + l16;  // the s of this lane's A-operand row
@@ -474,7 +492,6 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                     }
                 } else {
                     f4 Bn = {0.f, 0.f, 0.f, 0.f};
-                    const int mid = P0 + 8;
 #pragma unroll
                     for (int I = 0; I < 4; ++I) {
                         const int c4 = 16 * I + 4 * g;
@@ -489,43 +506,30 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                         At[e] = sl > l16 ? At[e] : (sl == l16 ? Bn[e] : 0.f);
                     }
                 }
-                const s4 a = pack4(At[0], At[1], At[2], At[3]);
-#pragma unroll
-                for (int J = 0; J < 4; ++J) D[J] = mfma(a, col4(GO, 16 * Q + 4 * g, 16 * J + l16), D[J]);
+                aA[Q] = pack4(At[0], At[1], At[2], At[3]);
             }
             const Rsrc rv = make_rsrc(P.dv + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll 1
+            for (int J = 0; J < 4; ++J) {
+                f4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int J = 0; J < 4; ++J)
+                for (int I = 0; I < 4; ++I) D = mfma(aK[I], colTp(sm.gs, 16 * I, 16 * J), D);
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q)
+                    if (Q >= wv) D = mfma(aA[Q], colT(GO, 16 * Q, 16 * J), D);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    buf_store(D[J][e], rv, static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4), 0);
+                    buf_store(D[e], rv, static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4), 0);
+            }
         }
 
         // ---- dk: d^{n-1-sig} X + sum_{s > sig} C[s][sig] r_s d^{s-1-sig} + u r C[sig][sig] ---
         {
-            f4 D[4];  // lane: dk[sig = P0 + 4 g + e][i = 16 I + l16]
+            s4 aC[4];  // aC[Q], Q >= wv: [m = sig][k = s]: C[s = 16 Q + 4 g + e][sig = P0 + l16], s > sig
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {  // X = V G1^T
-                f4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    X = mfma(raw4s(V, sig, j4), raw4(&sm.gs[16 * I + l16][j4]), X);
-                }
-                const int i = 16 * I + l16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int sg = P0 + 4 * g + e, nk = nv - 1 - sg;
-                    const float pk = nk >= 0 ? sm.pw[nk][i] : 0.f;
-                    dwv[I] -= static_cast<float>(nk) * pk * rd(K, sg, i) * X[e];  // (n-1-sig) d^{n-1-sig} k X
-                    X[e] *= pk;
-                }
-                D[I] = X;
-            }
-#pragma unroll 1
             for (int Q = 0; Q < 4; ++Q) {
+                aC[Q] = s4{0, 0, 0, 0};
                 if (Q < wv) continue;
-                // C block, lane: C[s = 16 Q + 4 g + e][sig = P0 + l16] = the A operand [m = sig][k = s]
                 f4 Cq = {0.f, 0.f, 0.f, 0.f};
                 if (Q == wv) {
                     Cq = Cpp;
@@ -538,65 +542,64 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                         Cq = mfma(raw4s(GO, 16 * Q + l16, j4), raw4s(V, sig, j4), Cq);
                     }
                 }
-                const s4 a = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
-                const int p0 = 16 * Q, mid = P0 + 8;
+                aC[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
+            }
+            const Rsrc rk = make_rsrc(P.dk + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll 1
+            for (int I = 0; I < 4; ++I) {  // lane: dk[sig = P0 + 4 g + e][i = 16 I + l16]
+                const int i = 16 * I + l16;
+                f4 X = {0.f, 0.f, 0.f, 0.f};  // X = V G1^T
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const int i = 16 * I + l16;
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    X = mfma(raw4s(V, sig, j4), raw4(&sm.gs[i][j4]), X);
+                }
+                const f4 kc = colTf(K, P0, 16 * I);
+                f4 D;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sg = P0 + 4 * g + e, nk = nv - 1 - sg;
+                    const float pk = nk >= 0 ? sm.pw[nk][i] : 0.f;
+                    dwv[0] -= static_cast<float>(nk) * pk * kc[e] * X[e];  // (n-1-sig) d^{n-1-sig} k X
+                    D[e] = X[e] * pk;
+                }
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q) {
+                    if (Q < wv) continue;
+                    const int p0 = 16 * Q;
+                    const f4 rc = colTf(R, p0, 16 * I);
                     float rb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int s = 16 * Q + 4 * g + e;
-                        rb[e] = rd(R, s, i) * (Q > wv ? sm.pw[s - p0][i] : sm.pe[mid - s + 8][i]);
+                        const int s = p0 + 4 * g + e;
+                        rb[e] = rc[e] * (Q > wv ? sm.pw[s - p0][i] : sm.pe[mid - s + 8][i]);
                     }
-                    const f4 M = mfma(a, pack4(rb[0], rb[1], rb[2], rb[3]), f4{0.f, 0.f, 0.f, 0.f});
+                    const f4 M = mfma(aC[Q], pack4(rb[0], rb[1], rb[2], rb[3]), f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int sg = P0 + 4 * g + e;
-                        D[I][e] += M[e] * (Q > wv ? sm.pw[p0 - 1 - sg][i] : sm.pe[sg + 1 - mid + 8][i]);
+                        D[e] += M[e] * (Q > wv ? sm.pw[p0 - 1 - sg][i] : sm.pe[sg + 1 - mid + 8][i]);
                     }
                 }
-            }
-            const Rsrc rk = make_rsrc(P.dk + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const int i = 16 * I + l16;
+                const f4 rcp = colTf(R, P0, 16 * I);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sg = P0 + 4 * g + e;
-                    const float val = D[I][e] + sm.uu[i] * rd(R, sg, i) * sm.cd[sg];
-                    buf_store(val, rk, static_cast<uint32_t>((sg * C + i) * 4), 0);
+                    buf_store(D[e] + sm.uu[i] * rcp[e] * sm.cd[sg], rk, static_cast<uint32_t>((sg * C + i) * 4), 0);
                 }
+                rot(dwv);
             }
         }
 
         // ---- dr, du: d^s Y + sum_{sig < s} C[s][sig] k_sig d^{s-1-sig} + u k C[s][s] ---------
         {
-            const int s_n = P0 + l16;  // this lane's s as the n index of V G^T-style products
-            f4 D[4];  // lane: dr[s = P0 + 4 g + e][i = 16 I + l16]
+            const int s_n = P0 + l16;  // this lane's s as the m / n index
+            s4 aR[4];  // aR[Q], Q <= wv: [m = s][k = sig]: C[s = P0 + l16][sig = 16 Q + 4 g + e], sig < s
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {  // Y = GO S0^T
-                f4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    Y = mfma(raw4s(GO, s_n, j4), raw4(&sm.ss[16 * I + l16][j4]), Y);
-                }
-                const int i = 16 * I + l16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = P0 + 4 * g + e;
-                    const float ps = sm.pw[s][i];
-                    dwv[I] -= static_cast<float>(s) * ps * rd(R, s, i) * Y[e];  // s d^s r Y
-                    Y[e] *= ps;
-                }
-                D[I] = Y;
-            }
-#pragma unroll 1
             for (int Q = 0; Q < 4; ++Q) {
+                aR[Q] = s4{0, 0, 0, 0};
                 if (Q > wv) continue;
-                // lane: C[s = P0 + l16][sig = 16 Q + 4 g + e] (from V_Q GO_P^T), the A operand [m = s][k = sig]
-                f4 Cq = {0.f, 0.f, 0.f, 0.f};
+                f4 Cq = {0.f, 0.f, 0.f, 0.f};  // from V_Q GO_P^T
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
                     const int j4 = 16 * J + 4 * g;
@@ -604,69 +607,99 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 }
                 if (Q == wv) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        Cq[e] = 4 * g + e < l16 ? Cq[e] : 0.f;
-                        sm.cdg[wv][l16][4 * g + e] = Cq[e];
-                    }
+                    for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e < l16 ? Cq[e] : 0.f;
+                    *reinterpret_cast<f4*>(&sm.cdg[wv][l16][4 * g]) = Cq;
                 }
-                const s4 a = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
-                const int mid = P0 + 8;
+                aR[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
+            }
+            const Rsrc rr = make_rsrc(P.dr + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll 1
+            for (int I = 0; I < 4; ++I) {  // lane: dr[s = P0 + 4 g + e][i = 16 I + l16]
+                const int i = 16 * I + l16;
+                f4 Y = {0.f, 0.f, 0.f, 0.f};  // Y = GO S0^T
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const int i = 16 * I + l16;
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    Y = mfma(raw4s(GO, s_n, j4), raw4(&sm.ss[i][j4]), Y);
+                }
+                const f4 rc = colTf(R, P0, 16 * I);
+                f4 D;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = P0 + 4 * g + e;
+                    const float ps = sm.pw[s][i];
+                    dwv[0] -= static_cast<float>(s) * ps * rc[e] * Y[e];  // s d^s r Y
+                    D[e] = Y[e] * ps;
+                }
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q) {
+                    if (Q > wv) continue;
+                    const f4 kc = colTf(K, 16 * Q, 16 * I);
                     float kb[4], kw[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {  // k_sig d^{p-1-sig} and (p-1-sig) times it, p = P0 or mid
                         const int sg = 16 * Q + 4 * g + e;
                         const int lg = Q < wv ? P0 - 1 - sg : mid - 1 - sg;
                         const float f = Q < wv ? sm.pw[lg][i] : sm.pe[sg + 1 - mid + 8][i];
-                        kb[e] = rd(K, sg, i) * f;
+                        kb[e] = kc[e] * f;
                         kw[e] = kb[e] * static_cast<float>(lg);
                     }
-                    const f4 M1 = mfma(a, pack4(kb[0], kb[1], kb[2], kb[3]), f4{0.f, 0.f, 0.f, 0.f});
+                    const f4 M1 = mfma(aR[Q], pack4(kb[0], kb[1], kb[2], kb[3]), f4{0.f, 0.f, 0.f, 0.f});
                     if (Q == wv) {  // the diagonal block's lag-weighted dw term is taken elementwise below
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) D[I][e] += M1[e] * sm.pe[mid - (P0 + 4 * g + e) + 8][i];
+                        for (int e = 0; e < 4; ++e) D[e] += M1[e] * sm.pe[mid - (P0 + 4 * g + e) + 8][i];
                         continue;
                     }
                     // off the diagonal both parts of the lag, s - P0 and P0 - 1 - sig, are >= 0
-                    const f4 M2 = mfma(a, pack4(kw[0], kw[1], kw[2], kw[3]), f4{0.f, 0.f, 0.f, 0.f});
+                    const f4 M2 = mfma(aR[Q], pack4(kw[0], kw[1], kw[2], kw[3]), f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int s = P0 + 4 * g + e;
-                        const int ls = s - P0;
+                        const int ls = 4 * g + e;  // s - P0
                         const float f = sm.pw[ls][i];
-                        D[I][e] += M1[e] * f;
-                        dwv[I] -= rd(R, s, i) * f * (static_cast<float>(ls) * M1[e] + M2[e]);
+                        D[e] += M1[e] * f;
+                        dwv[0] -= rc[e] * f * (static_cast<float>(ls) * M1[e] + M2[e]);
                     }
                 }
-            }
-            const Rsrc rr = make_rsrc(P.dr + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const int i = 16 * I + l16;
+                const f4 kcol = colTf(K, P0, 16 * I);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = P0 + 4 * g + e;
-                    const float kc = rd(K, s, i) * sm.cd[s];
-                    duv[I] += rd(R, s, i) * kc;
-                    buf_store(D[I][e] + sm.uu[i] * kc, rr, static_cast<uint32_t>((s * C + i) * 4), 0);
+                    const float kc = kcol[e] * sm.cd[s];
+                    duv[0] += rc[e] * kc;
+                    buf_store(D[e] + sm.uu[i] * kc, rr, static_cast<uint32_t>((s * C + i) * 4), 0);
                 }
+                rot(dwv);
+                rot(duv);
             }
         }
 
         // ---- the lag-weighted dw term inside this wave's block, elementwise with exact weights:
-        //      dw_i -= sum_{sig < s} (s-1-sig) d_i^{s-1-sig} r_s,i k_sig,i C[s][sig]   (lane = channel i)
+        //      dw_i -= sum_{sig < s} (s-1-sig) d_i^{s-1-sig} r_s,i k_sig,i C[s][sig]   (lane = channel i).
+        //      Row s is a 14-term dot product over sig = 0..13 with the weights
+        //      qs[sig] = (s-1-sig) d^{s-1-sig}, a window that slides by one token per row (the
+        //      stored block of C is zero for sig >= s, and lag 0 has weight 0).
         {
             const int i = lane;
+            float kr[14], qs[14];
+#pragma unroll
+            for (int a = 0; a < 14; ++a) {
+                kr[a] = rd(K, P0 + a, i);
+                qs[a] = 0.f;
+            }
             float acc = 0.f;
 #pragma unroll 1
-            for (int sl = 2; sl < 16; ++sl) {
+            for (int sl = 1; sl < 16; ++sl) {
+#pragma unroll
+                for (int a = 13; a > 0; --a) qs[a] = qs[a - 1];
+                qs[0] = static_cast<float>(sl - 1) * sm.pw[sl - 1][i];  // lag sl - 1 for sig = 0
+                const f4* crow = reinterpret_cast<const f4*>(&sm.cdg[wv][sl][0]);
                 float t = 0.f;
-#pragma unroll 1
-                for (int sg = 0; sg + 1 < sl; ++sg) {  // lag = sl - 1 - sg >= 1 (lag 0 has weight 0)
-                    const int lag = sl - 1 - sg;
-                    t = fmaf(static_cast<float>(lag) * sm.pw[lag][i] * rd(K, P0 + sg, i), sm.cdg[wv][sl][sg], t);
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const f4 cv = crow[c4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * c4 + e < 14) t = fmaf(qs[4 * c4 + e] * kr[4 * c4 + e], cv[e], t);
                 }
                 acc = fmaf(rd(R, P0 + sl, i), t, acc);
             }
@@ -689,14 +722,15 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
 #pragma unroll 1
         for (int Q = 0; Q < 4; ++Q) {
             float ra[4];
+            const f4 rc = colTf(R, 16 * Q, P0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = 16 * Q + 4 * g + e;
-                ra[e] = s < nv ? rd(R, s, key) * sm.pw[s][key] : 0.f;
+                ra[e] = s < nv ? rc[e] * sm.pw[s][key] : 0.f;
             }
             const s4 a = pack4(ra[0], ra[1], ra[2], ra[3]);
 #pragma unroll
-            for (int J = 0; J < 4; ++J) G[J] = mfma(a, col4(GO, 16 * Q + 4 * g, 16 * J + l16), G[J]);
+            for (int J = 0; J < 4; ++J) G[J] = mfma(a, colT(GO, 16 * Q, 16 * J), G[J]);
         }
         lds_sync();  // every wave is done with this chunk's G1 and inputs
 #pragma unroll
