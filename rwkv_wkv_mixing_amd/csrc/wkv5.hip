@@ -346,19 +346,21 @@ struct Wkv5BwdShared {
         Wkv5BwdFinal fin;
     };
     uint16_t gs[kN][kPadH];    // G1, bf16, [key][value]
-    uint16_t ss[kN][kPadH];    // S0, bf16, [key][value]
+    uint16_t ss[kN][kN];       // S0, bf16, [key][swizzled value], staged like the inputs
     float pw[kLc + 1][kPadF];  // e^{-w n}
     float pe[17][kPadF];       // e^{w' m}, m = -8..8, w' = min(w, kWCapB)
     float uu[kN];
     float cd[kLc];             // C[s][s] = go_s . v_s
-    float cdg[kWaves5][16][16];  // each wave's diagonal block of C, [s][sig], sig < s (float32)
+    float cdg[kWaves5][16][16];  // each wave's diagonal block of C by lag: [s - 1 - sig][s], lag >= 1 (float32)
 };
 
 __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P) {
     __shared__ Wkv5BwdShared sm;
-    const int lane = threadIdx.x & 63;
+    // lane coordinates; made opaque at the top of every chunk so that the many lane-dependent
+    // LDS addresses are recomputed inside the chunk instead of being held in registers across it
+    int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l16 = lane & 15, g = lane >> 4;
+    int l16 = lane & 15, g = lane >> 4;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / P.H, h = bh - b * P.H;
     const int64_t C = P.H * kN;
@@ -415,6 +417,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
     };
 
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
         // ---- stage r, k, v, go (swizzled rows) and S0 ------------------------------------
@@ -431,11 +434,14 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                     rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
             }
         }
-        {
-            const uint16_t* cp = P.ckpt + (bh * nch + ch) * kN * kN;
-            for (int q = threadIdx.x; q < kN * kN / 4; q += 64 * kWaves5) {  // 4 bf16 at a time
-                const int key = q / (kN / 4), v4 = (q % (kN / 4)) * 4;
-                *reinterpret_cast<u2*>(&sm.ss[key][v4]) = *reinterpret_cast<const u2*>(cp + key * kN + v4);
+        {  // the state before the chunk, 8 KB of [key][value] bf16: rows P0 .. P0 + 15 by this wave
+            const Rsrc rs = make_rsrc(P.ckpt + (bh * nch + ch) * kN * kN, kN * kN * 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = P0 + 8 * i + lane / 8;
+                const int q = (lane % 8) ^ (row & 7);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&sm.ss[P0 + 8 * i][0],
+                                                         16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, 0);
             }
         }
         wait_staged();
@@ -607,8 +613,11 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 }
                 if (Q == wv) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e < l16 ? Cq[e] : 0.f;
-                    *reinterpret_cast<f4*>(&sm.cdg[wv][l16][4 * g]) = Cq;
+                    for (int e = 0; e < 4; ++e) {
+                        Cq[e] = 4 * g + e < l16 ? Cq[e] : 0.f;
+                        const int lag = l16 - 1 - 4 * g - e;  // C[s = P0 + l16][sig = P0 + 4 g + e]
+                        if (lag >= 1) sm.cdg[wv][lag][l16] = Cq[e];
+                    }
                 }
                 aR[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
             }
@@ -620,7 +629,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
                     const int j4 = 16 * J + 4 * g;
-                    Y = mfma(raw4s(GO, s_n, j4), raw4(&sm.ss[i][j4]), Y);
+                    Y = mfma(raw4s(GO, s_n, j4), raw4(&sm.ss[i][sw(i, j4)]), Y);
                 }
                 const f4 rc = colTf(R, P0, 16 * I);
                 f4 D;
@@ -674,34 +683,33 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
         }
 
         // ---- the lag-weighted dw term inside this wave's block, elementwise with exact weights:
-        //      dw_i -= sum_{sig < s} (s-1-sig) d_i^{s-1-sig} r_s,i k_sig,i C[s][sig]   (lane = channel i).
-        //      Row s is a 14-term dot product over sig = 0..13 with the weights
-        //      qs[sig] = (s-1-sig) d^{s-1-sig}, a window that slides by one token per row (the
-        //      stored block of C is zero for sig >= s, and lag 0 has weight 0).
+        //      dw_i -= sum_{sig < s} (s-1-sig) d_i^{s-1-sig} r_s,i k_sig,i C[s][sig]
+        //            = sum_L L d_i^L Z_L,   Z_L = sum_s r_s,i k_{s-1-L},i C[s][s-1-L]
+        //      (lane = channel i; lag 0 has weight 0; the C entries of lag L are row L of cdg)
         {
             const int i = lane;
-            float kr[14], qs[14];
+            float rr[16], kr[14];
 #pragma unroll
-            for (int a = 0; a < 14; ++a) {
-                kr[a] = rd(K, P0 + a, i);
-                qs[a] = 0.f;
-            }
+            for (int a = 0; a < 16; ++a) rr[a] = rd(R, P0 + a, i);
+#pragma unroll
+            for (int a = 0; a < 14; ++a) kr[a] = rd(K, P0 + a, i);
             float acc = 0.f;
-#pragma unroll 1
-            for (int sl = 1; sl < 16; ++sl) {
 #pragma unroll
-                for (int a = 13; a > 0; --a) qs[a] = qs[a - 1];
-                qs[0] = static_cast<float>(sl - 1) * sm.pw[sl - 1][i];  // lag sl - 1 for sig = 0
-                const f4* crow = reinterpret_cast<const f4*>(&sm.cdg[wv][sl][0]);
-                float t = 0.f;
+            for (int L = 1; L < 15; ++L) {
+                const f4* crow = reinterpret_cast<const f4*>(&sm.cdg[wv][L][0]);
+                float z = 0.f;
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4) {
+                    if (4 * c4 + 3 < L + 1) continue;  // s >= L + 1 only
                     const f4 cv = crow[c4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * c4 + e < 14) t = fmaf(qs[4 * c4 + e] * kr[4 * c4 + e], cv[e], t);
+                    for (int e = 0; e < 4; ++e) {
+                        const int sl = 4 * c4 + e;
+                        if (sl >= L + 1) z = fmaf(rr[sl] * kr[sl - 1 - L], cv[e], z);
+                    }
                 }
-                acc = fmaf(rd(R, P0 + sl, i), t, acc);
+                acc = fmaf(static_cast<float>(L) * sm.pw[L][i], z, acc);
+                __builtin_amdgcn_sched_barrier(0);  // keep each lag's loads with it (register pressure)
             }
             dwd -= acc;
         }
@@ -713,7 +721,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
             const float dn = sm.pw[nv][key];
             float acc = 0.f;
 #pragma unroll
-            for (int J = 0; J < 4; ++J) acc += G[J][e] * bf(sm.ss[key][16 * J + l16]);
+            for (int J = 0; J < 4; ++J) acc += G[J][e] * bf(sm.ss[key][sw(key, 16 * J + l16)]);
             dwk[e] -= static_cast<float>(nv) * dn * acc;
 #pragma unroll
             for (int J = 0; J < 4; ++J) G[J][e] *= dn;
