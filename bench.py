@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -465,6 +465,73 @@ def bench_wkv5(args):
     return out
 
 
+def bench_wkv6(args):
+    """RWKV-6 forward (per-token decay) at B=8 T=1024 C=4096 (64 heads of 64):
+    float32 rates w, bf16 r, k, v, float32 output and state, from the zero state,
+    returning the final state.  Algorithmic bytes per channel-token: w (4 B) and
+    r, k, v (3 x 2 B) in, o (4 B) out; the final state adds 64 x 4 B per head
+    and batch row."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops, workloads as W
+
+    dev = torch.device("cuda:0")
+    p = W.wkv6_config()
+    B, T, H = p.B, p.T, p.H
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    u = torch.from_numpy(p.u).to(dev)
+    base = [torch.from_numpy(p.w).to(dev), up(p.r_bits), up(p.k_bits), up(p.v_bits)]
+    sets = [[t if i == 0 else t.clone() for t in base] for i in range(max(args.sets, 3))]
+    outs = [torch.empty((B, T, 64 * H), device=dev) for _ in sets]
+    sts = [torch.empty((B, H, 64, 64), device=dev) for _ in sets]
+
+    def step(i):
+        w, r, k, v = sets[i % len(sets)]
+        ops.wkv6_forward(w, u, r, k, v, out=outs[i % len(sets)], state_out=sts[i % len(sets)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    st = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    n = B * T * 64 * H
+    alg = 14 * n + B * H * 64 * 64 * 4
+    achieved = alg / (st["mean"] * 1e-6) / 1e9
+    out = {
+        "metric": "RWKV-6 matrix-state WKV (per-token decay) forward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
+        "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": p.name + " fwd", "B": B, "T": T, "H": H, "N": 64},
+        "call_us": {"wkv6_forward": st},
+        "roofline": {"bound": "hbm", "kernel": "wkv6_forward", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("wkv6_bf16_B8_T1024_H64", "wkv6_forward"),
+                     "alg_bytes_per_launch": alg},
+    }
+    if not args.no_cpu:
+        # the float64 numpy oracle on the whole workload (8 batch rows x 64 heads x all tokens)
+        from oracle import wkv6_forward_ref
+
+        t0 = time.perf_counter()
+        wkv6_forward_ref(p.w, p.u, p.r, p.k, p.v, H)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole workload ({n} channel*tokens) through the float64 numpy "
+                                         f"oracle, {t_np:.2f} s"}
+    return out
+
+
 def bench_wkv5_train(args):
     """RWKV-5 training step at B=8 T=1024 C=4096 (64 heads of 64): the forward
     saving its chunk-start states, then the backward from them (dr, dk, dv,
@@ -593,9 +660,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train"):
+    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6"):
         out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
-               "wkv5train": bench_wkv5_train}[args.workload](args)
+               "wkv5train": bench_wkv5_train, "wkv6": bench_wkv6}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

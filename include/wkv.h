@@ -235,6 +235,31 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
                           const float* w, const float* u, const void* r, const void* k, const void* v,
                           float* o, const float* s_in, float* s_out, void* ckpt, void* hip_stream);
 
+/*
+ * wkv6_forward - the matrix-state WKV with a per-token (data-dependent) decay,
+ * RWKV-6.
+ *
+ * Defines ("RWKV模型深度研究报告（截至2026年初）", section 1.3.2: RWKV-5 and
+ * RWKV-6 share the matrix-valued state; "RWKV（Receptance Weighted Key Value）
+ * 概念", section 13, and "RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型",
+ * the lineage figure: the sixth generation makes the decay data dependent),
+ * per head of 64 channels and batch row, with w_t a per-token rate:
+ *     S_t = diag(e^{-w_t}) S_{t-1} + k_t^T v_t          (S: 64 x 64, key x value)
+ *     o_t = r_t (S_{t-1} + diag(u_h) k_t^T v_t)
+ * The rates come from whatever projection the model uses (the pages' low-rank
+ * mix); this call takes them as an input.  Computed chunkwise like
+ * wkv5_forward (bf16 matrix-core products, float32 accumulation and state),
+ * from chunk-local cumulative rates in float32.  A rate above 10 acts as 10:
+ * a term's decay across such a token is then at most e^{-10} instead of less.
+ *
+ * B, T, H, N, in_dtype, u, r, k, v, o, s_in, s_out  as wkv5_forward.
+ * w         [B, T, 64 H] float32 rates, >= 0 and finite, 16-byte aligned.
+ * Errors as wkv5_forward.
+ */
+wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
+                          const float* w, const float* u, const void* r, const void* k, const void* v,
+                          float* o, const float* s_in, float* s_out, void* hip_stream);
+
 /* Bytes of wkv5_forward's chunk-start states for (B, T, H, N): bf16
  * [B, H, ceil(T/64), 64, 64] (key-major), rounded up to 256.  Opaque to the
  * caller: only wkv5_backward reads them.  0 for invalid arguments. */

@@ -313,6 +313,245 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     }
 }
 
+// ---- RWKV-6: the same operator with a per-token decay --------------------------------------
+// S_t = diag(e^{-w_t}) S_{t-1} + k_t^T v_t, o_t = r_t (S_{t-1} + diag(u) k_t^T v_t), w [B, T, C].
+// Inside a chunk every decay between two points is e^{-(E[a] - E[b])} with the chunk-local
+// cumulative rate E[t] = sum_{t' < t} w'_t' (t = 0..64) and w' = min(w, kWCap6); the factors are
+// split exactly as for RWKV-5: about the later 16-token block's first token off the diagonal (both
+// factors <= 1) and about the block's middle on it (each factor at most e^{8 kWCap6}).  A rate
+// above kWCap6 acts as kWCap6 (the state then keeps at most e^{-10} of itself at that token
+// instead of less).
+constexpr float kWCap6 = 10.f;
+
+struct Wkv6Shared {
+    uint16_t in[2][3][kLc][kN];  // staged r, k, v of a chunk, [token][swizzled channel], two chunks
+    uint16_t st[kN][kPadH];      // state before the chunk, bf16, [value][key]
+    float E[kLc + 1][kN];        // E[t][i], float4 slot (i / 4) ^ (t & 15) of row t (raw w_{t-1} when staged)
+    float uu[kN];
+};
+
+// position of channel c in row t of the cumulative-rate table
+__device__ __forceinline__ int swE(int t, int c) { return (((c >> 2) ^ (t & 15)) << 2) | (c & 3); }
+
+__device__ __forceinline__ f4 exp_neg4(f4 x) {  // e^{-x}, elementwise
+    return f4{ex2(-x[0] * kL2E), ex2(-x[1] * kL2E), ex2(-x[2] * kL2E), ex2(-x[3] * kL2E)};
+}
+
+__global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
+    __shared__ Wkv6Shared sm;
+    // lane coordinates; made opaque at the top of every chunk so that lane-dependent LDS
+    // addresses are recomputed inside the chunk instead of being held in registers across it
+    int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int l16 = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / P.H, h = bh - b * P.H;
+    const int64_t C = P.H * kN;
+    const int64_t nch = (P.T + kLc - 1) / kLc;
+    const int P0 = 16 * wv;
+
+    if (threadIdx.x < kN) {
+        sm.uu[threadIdx.x] = P.u[h * kN + threadIdx.x];
+        sm.E[0][threadIdx.x] = 0.f;  // row 0 is never staged over
+    }
+    f4 S[4];  // S[J][e] = S[16 wv + 4 g + e][16 J + l16]
+    const int64_t sbase = bh * kN * kN;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[J][e] = P.s_in != nullptr ? P.s_in[sbase + (16 * wv + 4 * g + e) * kN + 16 * J + l16] : 0.f;
+
+    auto chunk_rows = [&](int64_t ch) {
+        const int64_t t0 = ch * kLc;
+        return (P.T - t0) < kLc ? (P.T - t0) : kLc;
+    };
+    auto stage = [&](int64_t ch, int buf) {  // wave wv copies rows 16 wv .. 16 wv + 15 of r, k, v
+        const uint16_t* src[3] = {P.r, P.k, P.v};
+        const int64_t n = chunk_rows(ch);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            const Rsrc rs = make_rsrc(src[a] + ((b * P.T + ch * kLc) * C + h * kN), static_cast<uint32_t>(((n - 1) * C + kN) * 2));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = 16 * wv + 8 * i + lane / 8;
+                const int q = (lane % 8) ^ (row & 7);
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, 0);
+            }
+        }
+    };
+    auto stage_w = [&](int64_t ch) {  // wave wv copies w of tokens 16 wv .. 16 wv + 15 into rows 1 + token
+        const int64_t n = chunk_rows(ch);
+        const Rsrc rs = make_rsrc(P.w + ((b * P.T + ch * kLc) * C + h * kN), static_cast<uint32_t>(((n - 1) * C + kN) * 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * wv + 4 * i + lane / 16;  // token; LDS row t + 1
+            const int q = (lane % 16) ^ ((t + 1) & 15);  // the global 16-byte chunk that lands in slot lane % 16
+            const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(t) * C) * 4 + q * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)&sm.E[16 * wv + 4 * i + 1][0], 16, voff, 0, 0, 0);
+        }
+    };
+    auto put_state = [&]() {  // bf16, transposed: st[value][key]
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const uint32_t lo = pk2(S[J][0], S[J][1]), hi = pk2(S[J][2], S[J][3]);
+            uint32_t* p = reinterpret_cast<uint32_t*>(&sm.st[16 * J + l16][16 * wv + 4 * g]);
+            p[0] = lo;
+            p[1] = hi;
+        }
+    };
+    auto e4 = [&](int t, int c4) { return frow4(&sm.E[t][swE(t, c4)]); };  // E[t][c4 .. c4 + 3]
+    auto e1 = [&](int t, int c) { return sm.E[t][swE(t, c)]; };
+
+    stage(0, 0);
+    stage_w(0);
+    put_state();
+    wait_staged();
+
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
+        const int buf = static_cast<int>(ch & 1);
+        const int64_t t0 = ch * kLc;
+        const int nv = static_cast<int>(chunk_rows(ch));
+        lds_sync();  // this chunk's r, k, v, raw rates and state are in LDS
+        if (wv == 0) {  // E[t + 1] = E[t] + min(w_t, cap), one lane per channel (rows past the chunk hold 0)
+            float acc = 0.f;
+#pragma unroll 16
+            for (int t = 1; t <= kLc; ++t) {
+                float* p = &sm.E[t][swE(t, lane)];
+                acc += fminf(*p, kWCap6);
+                *p = acc;
+            }
+        }
+        lds_sync();  // E ready
+        if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
+
+        const uint16_t(*R)[kN] = sm.in[buf][0];
+        const uint16_t(*K)[kN] = sm.in[buf][1];
+        const uint16_t(*V)[kN] = sm.in[buf][2];
+        const int tau = P0 + l16;  // this lane's output token (as the m / n index of the products)
+
+        // ---- inter-chunk: O[J] = sum_I (r . e^{-E[tau]}) S0 ----------------------------------
+        f4 O[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) O[J] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int c4 = 16 * I + 4 * g;
+            const s4 a = mul_pack(row4(&R[tau][sw(tau, c4)]), exp_neg4(e4(tau, c4)));
+#pragma unroll
+            for (int J = 0; J < 4; ++J) O[J] = mfma(a, raw4(&sm.st[16 * J + l16][c4]), O[J]);
+        }
+
+        // ---- values as B operands: Vb[Q][J] holds V[16 Q + 4 g + e][16 J + l16] -------------
+        s4 Vb[4][4];
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const int s0 = 16 * Q + 4 * g, j = 16 * J + l16;
+                Vb[Q][J] = as_s4(V[s0][sw(s0, j)], V[s0 + 1][sw(s0 + 1, j)], V[s0 + 2][sw(s0 + 2, j)],
+                                 V[s0 + 3][sw(s0 + 3, j)]);
+            }
+
+        // ---- intra-chunk attention, transposed (lane: A[tau = P0 + l16][sig = 16 Q + 4 g + e]) --
+        s4 rof[4];  // r_tau e^{-(E[tau] - E[P0])}, the off-diagonal blocks' receptance operand
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int c4 = 16 * I + 4 * g;
+            rof[I] = mul_pack(row4(&R[tau][sw(tau, c4)]), exp_neg4(e4(tau, c4) - e4(P0, c4)));
+        }
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) {
+            if (Q > wv) break;
+            f4 At = {0.f, 0.f, 0.f, 0.f};
+            const int sig = 16 * Q + l16;  // this lane's key token (m index of K~)
+            if (Q < wv) {  // e^{-(E[P0] - E[sig + 1])}
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int c4 = 16 * I + 4 * g;
+                    const s4 ka = mul_pack(row4(&K[sig][sw(sig, c4)]), exp_neg4(e4(P0, c4) - e4(sig + 1, c4)));
+                    At = mfma(ka, rof[I], At);
+                }
+            } else {  // about mid = P0 + 8: e^{E[sig + 1] - E[mid]} and e^{-(E[tau] - E[mid])}; then the bonus
+                f4 Bn = {0.f, 0.f, 0.f, 0.f};
+                const int mid = P0 + 8;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int c4 = 16 * I + 4 * g;
+                    const f4 kr = row4(&K[sig][sw(sig, c4)]), rr = row4(&R[tau][sw(tau, c4)]);
+                    const f4 em = e4(mid, c4);
+                    const s4 ka = mul_pack(kr, exp_neg4(em - e4(sig + 1, c4)));
+                    const s4 rb = mul_pack(rr, exp_neg4(e4(tau, c4) - em));
+                    At = mfma(ka, rb, At);
+                    Bn = mfma(raw4(&K[sig][sw(sig, c4)]), mul_pack(rr, frow4(&sm.uu[c4])), Bn);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {  // lane holds (sig_local = 4 g + e, tau_local = l16)
+                    const int sl = 4 * g + e;
+                    At[e] = sl < l16 ? At[e] : (sl == l16 ? Bn[e] : 0.f);
+                }
+            }
+            const s4 a = pack4(At[0], At[1], At[2], At[3]);
+#pragma unroll
+            for (int J = 0; J < 4; ++J) O[J] = mfma(a, Vb[Q][J], O[J]);
+        }
+
+        // ---- state update operands, read from E before it is overwritten --------------------------
+        //      S = diag(e^{-E[n]}) S + sum_sig (k_sig e^{-(E[n] - E[sig + 1])})^T v_sig
+        float dn[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dn[e] = ex2(-e1(nv, 16 * wv + 4 * g + e) * kL2E);
+        s4 aS[4];
+        {
+            const int key = 16 * wv + l16;  // m index of K^T
+            const float en = e1(nv, key);
+#pragma unroll
+            for (int Q = 0; Q < 4; ++Q) {
+                float kk[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 16 * Q + 4 * g + e;
+                    kk[e] = s < nv ? bf(K[s][sw(s, key)]) * ex2(-(en - e1(s + 1, key)) * kL2E) : 0.f;
+                }
+                aS[Q] = pack4(kk[0], kk[1], kk[2], kk[3]);
+            }
+        }
+        lds_sync();  // every wave has read the state and E
+        if (ch + 1 < nch) stage_w(ch + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) S[J][e] *= dn[e];
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) S[J] = mfma(aS[Q], Vb[Q][J], S[J]);
+        put_state();
+        wait_staged();
+
+        // ---- outputs: lane holds O[tau = P0 + 4 g + e][16 J + l16] --------------------------------
+        const Rsrc ro = make_rsrc(P.o + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t off = static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4);
+                buf_store(O[J][e], ro, off, 0);
+            }
+    }
+
+    if (P.s_out != nullptr) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P.s_out[sbase + (16 * wv + 4 * g + e) * kN + 16 * J + l16] = S[J][e];
+    }
+}
+
 // ---- backward ---------------------------------------------------------------------
 // For L = sum_t <go_t, o_t> + <dS_T, S_T>, with the adjoint state
 // G_{t-1} = diag(d) G_t + r_t^T go_t (d = e^{-w}; G after the last token is dS_T), per chunk of n tokens with S0 the
@@ -816,6 +1055,11 @@ hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream) {
     const int64_t n = a.H * kN;
     hipLaunchKernelGGL(wkv5_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a.part,
                        a.B, a.H, a.dw, a.du);
+    return hipGetLastError();
+}
+
+hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream) {
+    hipLaunchKernelGGL(wkv6_fwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 

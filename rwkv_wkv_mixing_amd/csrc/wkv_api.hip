@@ -299,6 +299,23 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     return hip_status(wkv::launch_wkv5_fwd(a, stream));
 }
 
+wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
+                          const float* u, const void* r, const void* k, const void* v, float* o,
+                          const float* s_in, float* s_out, void* hip_stream) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (p.bh == 0) return WKV_OK;
+    if ((s_in && !aligned(s_in, 4)) || (s_out && !aligned(s_out, 4))) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (T == 0) return hip_status(wkv::launch_wkv5_state_copy(s_in, s_out, p.ns, stream));
+    if (!w || !u || !r || !k || !v || !o) return WKV_EINVAL;
+    if (!aligned(w, 16) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return WKV_EALIGN;
+    wkv::Wkv6Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
+                    static_cast<const uint16_t*>(v), o, s_in, s_out};
+    return hip_status(wkv::launch_wkv6_fwd(a, stream));
+}
+
 wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                            const float* u, const void* r, const void* k, const void* v, const void* go,
                            const float* s_in, const float* ds_out, float* dr, float* dk, float* dv, float* dw,

@@ -136,6 +136,20 @@ int shift_vector_width(bool bf16, bool bwd);
 
 // RWKV-5 matrix-state forward (wkv5.hip)
 hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream);
+
+struct Wkv6Args {
+    int64_t B, T, H;     // head size 64; C = 64 H
+    const float* w;      // [B, T, C] per-token decay rates (>= 0)
+    const float* u;      // [H, 64] bonus
+    const uint16_t* r;   // [B, T, C] bf16, 16-byte aligned
+    const uint16_t* k;
+    const uint16_t* v;
+    float* o;            // [B, T, C]
+    const float* s_in;   // [B, H, 64, 64] or NULL (zero state)
+    float* s_out;        // [B, H, 64, 64] or NULL
+};
+
+hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream);
 hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hipStream_t stream);
 hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream);
 

@@ -413,3 +413,32 @@ class Wkv5Function(torch.autograd.Function):
                                                need_state_grad=state_in is not None and ctx.needs_input_grad[5],
                                                ckpt=ckpt)
         return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds
+
+
+def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None):
+    """RWKV-6 matrix-state WKV with per-token decay: o [B, T, C] float32 from
+    w [B, T, C] float32 rates (>= 0), u [H, 64] float32 and r, k, v [B, T, C]
+    bfloat16 (C = 64 H); state handling as wkv5_forward."""
+    _need(r, "r", torch.bfloat16)
+    dev = r.device
+    B, T, C = r.shape
+    H = u.shape[0]
+    if C != 64 * H:
+        raise ValueError(f"C = {C} is not 64 * H with H = {H}")
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, (B, T, C), dev)
+    _need(w, "w", torch.float32, (B, T, C), dev)
+    _need(u, "u", torch.float32, (H, 64), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, T, C), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, 64, 64), dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (B, H, 64, 64), dev)
+    st = L.lib().wkv6_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
+                              _p(state_out), _stream(dev))
+    L.check("wkv6_forward", st)
+    return (out, state_out) if return_state else out

@@ -313,6 +313,30 @@ def make_wkv5(B, T, H, *, seed=0, w_range=(-4.0, 1.5), kv_std=1.0, with_state=Fa
     return Wkv5Problem(name or f"wkv5 B={B} T={T} H={H}", B, T, H, w, u, r, k, v, r_bits, k_bits, v_bits, S0)
 
 
+def make_wkv6(B, T, H, *, seed=0, base_range=(-4.0, 1.5), spread=0.5, kv_std=1.0, with_state=False,
+              name="") -> Wkv5Problem:
+    """Inputs of the RWKV-6 operator (a Wkv5Problem whose w is [B, T, 64 H]).
+    Draw order: a base log-rate per (head, key channel) ~ U(lo, hi), then
+    per-token rates w = exp(base + spread * N(0, 1)) (data-dependent decay
+    around each channel's base), u ~ N(0, 1), r, k, v ~ N(0, kv_std) rounded to
+    bf16, then (if wanted) S0 ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    N = 64
+    base = rng.uniform(base_range[0], base_range[1], (H * N,))
+    w = np.exp(base[None, None, :] + spread * rng.standard_normal((B, T, H * N))).astype(np.float32)
+    u = _normal(rng, 1.0, (H, N))
+    r_bits, r = bf16_round(_normal(rng, kv_std, (B, T, H * N)))
+    k_bits, k = bf16_round(_normal(rng, kv_std, (B, T, H * N)))
+    v_bits, v = bf16_round(_normal(rng, kv_std, (B, T, H * N)))
+    S0 = _normal(rng, 1.0, (B, H, N, N)) if with_state else None
+    return Wkv5Problem(name or f"wkv6 B={B} T={T} H={H}", B, T, H, w, u, r, k, v, r_bits, k_bits, v_bits, S0)
+
+
+def wkv6_config(seed=0) -> Wkv5Problem:
+    """A 7B-shaped layer in RWKV-6 form: B=8, T=1024, C=4096 as 64 heads of 64."""
+    return make_wkv6(8, 1024, 64, seed=seed, name="wkv6 bf16 B=8 T=1024 H=64 N=64")
+
+
 def wkv5_go(p: Wkv5Problem, *, seed=1, std=1.0) -> tuple[np.ndarray, np.ndarray]:
     """A gradient of the output for a Wkv5Problem: go ~ N(0, std) of shape
     [B, T, 64 H], rounded to bf16.  Returns (bits as uint16, values as float32)."""

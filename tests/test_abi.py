@@ -272,3 +272,21 @@ def test_wkv5_backward_validation(lib):
     # with a ckpt only the partial sums are needed
     small = lib.wkv5_backward_workspace_bytes(1, 4, 2, 64, 1)
     assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=small - 1, ck=x) == L.WKV_EWORKSPACE
+
+
+def wkv6(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None):
+    return lib.wkv6_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), None)
+
+
+def test_wkv6_validation(lib):
+    x = A16
+    args = [x] * 6
+    assert wkv6(lib, 1, 4, 2, 32, L.WKV_BF16, *args) == L.WKV_EINVAL      # head size must be 64
+    assert wkv6(lib, 1, -4, 2, 64, L.WKV_BF16, *args) == L.WKV_EINVAL
+    assert wkv6(lib, 1, 4, 2, 64, L.WKV_F32, *args) == L.WKV_EDTYPE       # bf16 operands only
+    assert wkv6(lib, 1 << 30, 1 << 30, 1 << 10, 64, L.WKV_BF16, *args) == L.WKV_ESIZE
+    assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, None, x, x, x, x, x) == L.WKV_EINVAL   # w NULL
+    assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, x + 4, x, x, x, x, x) == L.WKV_EALIGN  # w 16-byte aligned
+    assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x + 2, x, x, x) == L.WKV_EALIGN
+    assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, *args, so=x + 1) == L.WKV_EALIGN
+    assert wkv6(lib, 0, 4, 2, 64, L.WKV_BF16, *[None] * 6) == L.WKV_OK

@@ -1,0 +1,196 @@
+"""GPU parity of the RWKV-6 matrix-state WKV with per-token decay (wkv6_forward)
+against the float64 oracle, through the C ABI.
+
+Bound, from the kernel's arithmetic.  As for RWKV-5 (bf16 matrix-core operands,
+float32 accumulation and state; ub = 2^-8): every output term passes through at
+most three bf16 roundings, the final state's through one.  The decay factors
+come from float32 cumulative rates E (sums of up to 64 capped rates): each
+factor e^{-(E[a] - E[b])} is off by at most 2 * 64 * 2^-24 * Emax in its
+exponent, and a term carries at most two factors, so the relative bound gains
+Emax * 2^-16 (Emax the largest in-chunk sum of capped rates).  Rates above 10
+act as 10 in the kernel: the bound adds the difference of the magnitudes with
+w' = min(w, 10) and with w (zero unless some rate exceeds 10), and takes the
+rounding part on the w' magnitudes:
+    |o_gpu - o| <= (3 ub (1 + 2^-7) + 2^-12 + Emax 2^-16) o_abs(w') + (o_abs(w') - o_abs(w))
+with o_abs the oracle on |r|, |k|, |v|, |u|, |S0|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import to_dev
+from oracle import wkv6_forward_ref
+from rwkv_wkv_mixing_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+UB = 2.0 ** -8
+CAP = 10.0
+
+
+def ops():
+    from rwkv_wkv_mixing_amd import ops as O
+
+    return O
+
+
+def check_bound(name, got, ref, bound):
+    g = np.asarray(got, dtype=np.float64)
+    o = np.asarray(ref, dtype=np.float64)
+    assert g.shape == o.shape, (name, g.shape, o.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    err = np.abs(g - o)
+    ratio = err / (np.asarray(bound, dtype=np.float64) + 1e-30)
+    worst = float(ratio.max(initial=0.0))
+    print(f"  {name}: max_abs={float(err.max(initial=0.0)):.3e} worst_err/bound={worst:.3f}", flush=True)
+    if worst > 1.0:
+        idx = np.unravel_index(np.argmax(ratio), ratio.shape)
+        raise AssertionError(f"{name}: {int((ratio > 1).sum())} of {ratio.size} out of bound; worst at {idx}: "
+                             f"got {g[idx]!r} ref {o[idx]!r} bound {np.asarray(bound)[idx]!r}")
+
+
+def emax(w):
+    """Largest sum of capped rates over one channel of one 64-token chunk."""
+    wc = np.minimum(np.asarray(w, np.float64), CAP)
+    B, T, C = wc.shape
+    pad = (-T) % 64
+    wc = np.concatenate([wc, np.zeros((B, pad, C))], axis=1).reshape(B, -1, 64, C)
+    return float(wc.sum(axis=2).max(initial=0.0))
+
+
+def check(p, o, S, name=None):
+    name = name or p.name
+    w = np.asarray(p.w, np.float64)
+    ref_o, ref_S = wkv6_forward_ref(w, p.u, p.r, p.k, p.v, p.H, p.S0)
+    absin = dict(u=np.abs(p.u), r=np.abs(p.r), k=np.abs(p.k), v=np.abs(p.v), H=p.H,
+                 S0=None if p.S0 is None else np.abs(p.S0))
+    abs_o, abs_S = wkv6_forward_ref(w, **absin)
+    wc = np.minimum(w, CAP)
+    cap_o, cap_S = (abs_o, abs_S) if np.array_equal(wc, w) else wkv6_forward_ref(wc, **absin)
+    c_o = 3 * UB * (1 + 2.0 ** -7) + 2.0 ** -12 + emax(w) * 2.0 ** -16
+    c_s = UB * (1 + 2.0 ** -7) + 2.0 ** -12 + emax(w) * 2.0 ** -16
+    check_bound(f"{name} o", o.cpu().numpy(), ref_o, c_o * cap_o + (cap_o - abs_o))
+    if S is not None:
+        check_bound(f"{name} state", S.cpu().numpy(), ref_S, c_s * cap_S + (cap_S - abs_S))
+
+
+def dev_inputs(p):
+    bt = lambda bits: to_dev(None, DEV, bits)
+    d = dict(w=to_dev(p.w, DEV), u=to_dev(p.u, DEV), r=bt(p.r_bits), k=bt(p.k_bits), v=bt(p.v_bits))
+    d["S0"] = None if p.S0 is None else to_dev(p.S0, DEV)
+    return d
+
+
+SHAPES = [(2, 1, 1), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_shapes(B, T, H, with_state):
+    """Whole and ragged 64-token chunks, one to several heads, zero or given state."""
+    p = W.make_wkv6(B, T, H, seed=B * 100 + T + H + 3, with_state=with_state)
+    print(f"case {p.name} state={with_state}", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S)
+
+
+@pytest.mark.parametrize("rates", [(20.0, 80.0), (1e-6, 1e-3), (6.0, 14.0), (0.0, 0.0)])
+def test_extreme_decay_rates(rates):
+    """Per-token rates from 0 (no decay) and nearly 0 to e^{-80}, and across the cap of 10."""
+    p = W.make_wkv6(2, 150, 2, seed=11, with_state=True)
+    rng = np.random.default_rng(12)
+    if rates[1] == 0.0:
+        p.w[:] = 0.0
+    else:
+        p.w[:] = np.exp(rng.uniform(np.log(rates[0]), np.log(rates[1]), p.w.shape)).astype(np.float32)
+    print(f"case rates {rates}", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name=f"rates {rates}")
+
+
+def test_mixed_resets():
+    """Ordinary rates with scattered tokens whose rate is 30 (a near reset), as
+    data-dependent decay produces at boundaries."""
+    p = W.make_wkv6(2, 300, 2, seed=13, with_state=True)
+    mask = np.random.default_rng(14).random(p.w.shape) < 0.02
+    p.w[mask] = 30.0
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name="mixed resets")
+
+
+def test_split_sequence_through_the_state():
+    p = W.make_wkv6(2, 300, 2, seed=15)
+    print(f"case split {p.name}", flush=True)
+    d = dev_inputs(p)
+    O = ops()
+    for t1 in (1, 64, 100):
+        sl = lambda x, a, b: x[:, a:b].contiguous()
+        o1, S1 = O.wkv6_forward(sl(d["w"], 0, t1), d["u"], sl(d["r"], 0, t1), sl(d["k"], 0, t1), sl(d["v"], 0, t1),
+                                return_state=True)
+        o2, S2 = O.wkv6_forward(sl(d["w"], t1, 300), d["u"], sl(d["r"], t1, 300), sl(d["k"], t1, 300),
+                                sl(d["v"], t1, 300), state_in=S1, state_out=S1, return_state=True)
+        torch.cuda.synchronize()
+        check(p, torch.cat([o1, o2], dim=1), S2, name=f"split at {t1}")
+
+
+def test_constant_rates_match_rwkv5_kernel():
+    """With w_t the same for every token the operator is RWKV-5's; both kernels
+    stay within their bounds of the oracle, and here within the sum of them of
+    each other."""
+    p = W.make_wkv5(2, 130, 2, seed=17, with_state=True)
+    d5 = dict(w=to_dev(p.w, DEV), u=to_dev(p.u, DEV))
+    bt = lambda bits: to_dev(None, DEV, bits)
+    r, k, v = bt(p.r_bits), bt(p.k_bits), bt(p.v_bits)
+    S0 = to_dev(p.S0, DEV)
+    w6 = d5["w"].reshape(1, 1, -1).expand(2, 130, -1).contiguous()
+    O = ops()
+    o5 = O.wkv5_forward(d5["w"], d5["u"], r, k, v, state_in=S0)
+    o6 = O.wkv6_forward(w6, d5["u"], r, k, v, state_in=S0)
+    torch.cuda.synchronize()
+    p6 = W.Wkv5Problem("wkv6 as wkv5", p.B, p.T, p.H, w6.cpu().numpy(), p.u, p.r, p.k, p.v, p.r_bits, p.k_bits,
+                       p.v_bits, p.S0)
+    check(p6, o6, None)
+    absx, _ = wkv6_forward_ref(w6.cpu().numpy().astype(np.float64), np.abs(p.u), np.abs(p.r), np.abs(p.k),
+                               np.abs(p.v), p.H, np.abs(p.S0))
+    c5 = 3 * UB * (1 + 2.0 ** -7) + 2.0 ** -17
+    c6 = 3 * UB * (1 + 2.0 ** -7) + 2.0 ** -12 + emax(w6.cpu().numpy()) * 2.0 ** -16
+    check_bound("wkv6 vs wkv5 kernel", o6.cpu().numpy(), o5.cpu().numpy(), (c5 + c6) * absx)
+
+
+def test_zero_length_and_determinism():
+    p = W.make_wkv6(2, 130, 3, seed=19, with_state=True)
+    d = dev_inputs(p)
+    O = ops()
+    z = torch.empty((2, 0, 192), dtype=torch.bfloat16, device=DEV)
+    zw = torch.empty((2, 0, 192), dtype=torch.float32, device=DEV)
+    S = torch.empty((2, 3, 64, 64), device=DEV)
+    O.wkv6_forward(zw, d["u"], z, z, z, state_in=d["S0"], state_out=S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["S0"])
+    a = O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    b = O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_bench_shape_sampled():
+    """B=8, T=1024, 64 heads of 64 (the benchmarked shape, same entry point):
+    every output of two heads against the oracle run on those heads alone."""
+    p = W.wkv6_config(seed=5)
+    print(f"case {p.name}", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], return_state=True)
+    torch.cuda.synchronize()
+    o, S = o.cpu().numpy(), S.cpu().numpy()
+    for h in (0, 41):
+        sl = slice(64 * h, 64 * h + 64)
+        sub = W.Wkv5Problem(f"{p.name} head {h}", p.B, p.T, 1, p.w[:, :, sl], p.u[h:h + 1], p.r[:, :, sl],
+                            p.k[:, :, sl], p.v[:, :, sl], None, None, None, None)
+        check(sub, torch.from_numpy(o[:, :, sl]), torch.from_numpy(S[:, h:h + 1]), name=sub.name)
