@@ -313,6 +313,13 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     }
 }
 
+// Output rows are written 64 bytes of a 128-byte line at a time, the two halves by
+// different tiles; plain write-back stores let L2 join them (non-temporal ones reached
+// memory as up to 1.23x the bytes).
+__device__ __forceinline__ void store_wb(float v, Rsrc r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, 0);
+}
+
 // ---- RWKV-6: the same operator with a per-token decay --------------------------------------
 // S_t = diag(e^{-w_t}) S_{t-1} + k_t^T v_t, o_t = r_t (S_{t-1} + diag(u) k_t^T v_t), w [B, T, C].
 // Inside a chunk every decay between two points is e^{-(E[a] - E[b])} with the chunk-local
@@ -540,7 +547,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t off = static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4);
-                buf_store(O[J][e], ro, off, 0);
+                store_wb(O[J][e], ro, off);
             }
     }
 
@@ -764,7 +771,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                     if (Q >= wv) D = mfma(aA[Q], colT(GO, 16 * Q, 16 * J), D);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    buf_store(D[e], rv, static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4), 0);
+                    store_wb(D[e], rv, static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4));
             }
         }
 
@@ -830,7 +837,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int sg = P0 + 4 * g + e;
-                    buf_store(D[e] + sm.uu[i] * rcp[e] * sm.cd[sg], rk, static_cast<uint32_t>((sg * C + i) * 4), 0);
+                    store_wb(D[e] + sm.uu[i] * rcp[e] * sm.cd[sg], rk, static_cast<uint32_t>((sg * C + i) * 4));
                 }
                 rot(dwv);
             }
@@ -914,7 +921,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                     const int s = P0 + 4 * g + e;
                     const float kc = kcol[e] * sm.cd[s];
                     duv[0] += rc[e] * kc;
-                    buf_store(D[e] + sm.uu[i] * kc, rr, static_cast<uint32_t>((s * C + i) * 4), 0);
+                    store_wb(D[e] + sm.uu[i] * kc, rr, static_cast<uint32_t>((s * C + i) * 4));
                 }
                 rot(dwv);
                 rot(duv);
