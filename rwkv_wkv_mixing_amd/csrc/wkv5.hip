@@ -424,14 +424,23 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>(chunk_rows(ch));
         lds_sync();  // this chunk's r, k, v, raw rates and state are in LDS
-        if (wv == 0) {  // E[t + 1] = E[t] + min(w_t, cap), one lane per channel (rows past the chunk hold 0)
-            float acc = 0.f;
-#pragma unroll 16
-            for (int t = 1; t <= kLc; ++t) {
-                float* p = &sm.E[t][swE(t, lane)];
-                acc += fminf(*p, kWCap6);
-                *p = acc;
+        {  // E[t + 1] = E[t] + min(w_t, cap) (rows past the chunk hold 0): wave wv takes channels
+           // 16 wv .. 16 wv + 15, lane (c, seg) the tokens 16 seg .. 16 seg + 15 of channel c; the
+           // segments' totals are scanned across the four lanes of a channel
+            const int c = 16 * wv + l16, t1 = 16 * g + 1;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
+            float off = 0.f;
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                const float v = __shfl_up(x[15], 16 * k, 64);
+                if (g >= k) off += v;
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sm.E[t1 + i][swE(t1 + i, c)] = x[i] + off;
         }
         lds_sync();  // E ready
         if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
