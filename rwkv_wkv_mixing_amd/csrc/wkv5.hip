@@ -104,6 +104,15 @@ __device__ __forceinline__ s4 as_s4(uint16_t a, uint16_t b, uint16_t c, uint16_t
 // four consecutive bf16 of an LDS row as an MFMA operand, unchanged
 __device__ __forceinline__ s4 raw4(const uint16_t* p) { return __builtin_bit_cast(s4, *reinterpret_cast<const u16x4*>(p)); }
 
+// Tokens tb + 4 g + e (e = 0..3) of channel c0 + l16 of a staged 64 x 64 tile (a column) as a raw
+// MFMA operand, by one transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// q reads four channels of one row and lane j receives element j % 4 of lane 4 e + j / 4's read,
+// so lane (l16, g) names row tb + 4 g + l16 / 4, channels c0 + 4 (l16 % 4) .. + 3.
+__device__ __forceinline__ s4 col_tr(const uint16_t (*X)[kN], int tb, int c0, int l16, int g) {
+    const int t = tb + 4 * g + (l16 >> 2), c = c0 + 4 * (l16 & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)&X[t][sw(t, c)]);
+}
+
 // kOut = false: a state-only pass (no outputs, only the chunk-start states in P.ckpt
 // and the final state), as the backward needs.
 template <bool kOut>
@@ -217,11 +226,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q)
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                const int s0 = 16 * Q + 4 * g, j = 16 * J + l16;
-                Vb[Q][J] = as_s4(V[s0][sw(s0, j)], V[s0 + 1][sw(s0 + 1, j)], V[s0 + 2][sw(s0 + 2, j)],
-                                 V[s0 + 3][sw(s0 + 3, j)]);
-            }
+            for (int J = 0; J < 4; ++J) Vb[Q][J] = col_tr(V, 16 * Q, 16 * J, l16, g);
 
         // ---- intra-chunk attention, transposed: At[sig][tau], lane holds
         //      A[tau = P0 + l16][sig = 16 Q + 4 g + e] (the A operand of A V) -----------
@@ -280,11 +285,12 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q) {
             float kk[4];
+            const u16x4 kc = __builtin_bit_cast(u16x4, col_tr(K, 16 * Q, 16 * wv, l16, g));  // K[s][key]
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = 16 * Q + 4 * g + e;
                 const int n = nv - 1 - s;
-                kk[e] = n >= 0 ? bf(K[s][sw(s, key)]) * sm.pw[n >= 0 ? n : 0][key] : 0.f;  // past the chunk's end: 0
+                kk[e] = n >= 0 ? bf(kc[e]) * sm.pw[n >= 0 ? n : 0][key] : 0.f;  // past the chunk's end: 0
             }
             const s4 a = pack4(kk[0], kk[1], kk[2], kk[3]);
 #pragma unroll
@@ -467,11 +473,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q)
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                const int s0 = 16 * Q + 4 * g, j = 16 * J + l16;
-                Vb[Q][J] = as_s4(V[s0][sw(s0, j)], V[s0 + 1][sw(s0 + 1, j)], V[s0 + 2][sw(s0 + 2, j)],
-                                 V[s0 + 3][sw(s0 + 3, j)]);
-            }
+            for (int J = 0; J < 4; ++J) Vb[Q][J] = col_tr(V, 16 * Q, 16 * J, l16, g);
 
         // ---- intra-chunk attention, transposed (lane: A[tau = P0 + l16][sig = 16 Q + 4 g + e]) --
         s4 rof[4];  // r_tau e^{-(E[tau] - E[P0])}, the off-diagonal blocks' receptance operand
@@ -528,10 +530,11 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
             for (int Q = 0; Q < 4; ++Q) {
                 float kk[4];
+                const u16x4 kc = __builtin_bit_cast(u16x4, col_tr(K, 16 * Q, 16 * wv, l16, g));  // K[s][key]
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = 16 * Q + 4 * g + e;
-                    kk[e] = s < nv ? bf(K[s][sw(s, key)]) * ex2(-(en - e1(s + 1, key)) * kL2E) : 0.f;
+                    kk[e] = s < nv ? bf(kc[e]) * ex2(-(en - e1(s + 1, key)) * kL2E) : 0.f;
                 }
                 aS[Q] = pack4(kk[0], kk[1], kk[2], kk[3]);
             }
