@@ -1,7 +1,8 @@
 /*
  * wkv.h - C ABI of the RWKV-4 WKV time-mixing operator for AMD MI355X (gfx950),
  * with the receptance gate and the token-shift mix around it, and the
- * matrix-state WKV of RWKV-5.
+ * matrix-state WKV of RWKV-5 (forward and backward) and RWKV-6 (per-token
+ * decay, forward).
  *
  * The operator, per channel c of each batch row b, tokens t = 1..T
  * ("RWKV（Receptance Weighted Key Value）概念", section 3.2; and
