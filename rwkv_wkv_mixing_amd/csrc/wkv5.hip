@@ -1,4 +1,5 @@
-// Multi-head matrix-state WKV (RWKV-5), chunkwise-parallel forward on MFMA.
+// Multi-head matrix-state WKV on MFMA: RWKV-5's forward and backward, and RWKV-6's
+// forward (the same state with a per-token decay, further below).
 //
 // Per head (N = 64 channels; "RWKV模型深度研究报告", sections 1.3.2 and 1.3.3:
 // a matrix-valued state with per-channel decay, updated by a diagonal decay
@@ -589,7 +590,14 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 // The in-chunk sums are matrix products with the decay split about the later
 // 16-token block's first token (off-diagonal blocks: both factors <= 1) or
 // about the block's middle with w capped at kWCapB (diagonal blocks); lag d^lag
-// splits the same way into (s - p) d^{s-p} d^{p-1-sig} + d^{s-p} (p-1-sig) d^{p-1-sig}.
+// splits the same way into (s - p) d^{s-p} d^{p-1-sig} + d^{s-p} (p-1-sig) d^{p-1-sig} off the
+// diagonal, where both parts are >= 0; inside a diagonal block the two parts would have opposite
+// signs and cancel, so that term is taken elementwise with the exact weight (s-1-sig) d^{s-1-sig}.
+//
+// One workgroup of four waves per (batch row, head) walks the chunks last to first.  Wave w owns
+// token block w (its rows of dr, dk, dv) and key rows 16w..16w+15 of G, in registers.  Per
+// chunk r, k, v, go and the forward's bf16 chunk-start state arrive by buffer -> LDS copies;
+// G crosses the waves through LDS as bf16 for the next chunk's dv and dk.
 constexpr float kWCapB = 8.f;  // keeps every in-block intermediate below e^64 times its inputs
 
 struct Wkv5BwdFinal {         // the per-(batch row, head) sums of dw, du, after the chunk walk
@@ -713,9 +721,8 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
             Cpp = mfma(raw4s(GO, P0 + l16, j4), raw4s(V, P0 + l16, j4), Cpp);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)  // read back only by this wave (in order)
             if (4 * g + e == l16) sm.cd[P0 + l16] = Cpp[e];
-        wait_lds_reads();
 
         // Each part below first builds its small A operands (8 registers a set), then walks
         // the output's 16-column tiles in a rolled loop with one accumulator, storing each tile;
