@@ -22,4 +22,4 @@ from .token_shift_ref import (  # noqa: F401
     token_shift_ref,
 )
 from .wkv5_ref import wkv5_backward_ref, wkv5_direct_ref, wkv5_forward_ref  # noqa: F401
-from .wkv6_ref import wkv6_direct_ref, wkv6_forward_ref  # noqa: F401
+from .wkv6_ref import wkv6_backward_ref, wkv6_direct_ref, wkv6_forward_ref  # noqa: F401

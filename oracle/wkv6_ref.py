@@ -26,7 +26,13 @@ Readings where the pages are silent (each listed in the design doc):
 * otherwise as RWKV-5 (wkv5_ref.py): heads of N channels, state S (key x value),
       S_t = diag(e^{-w_t}) S_{t-1} + k_t^T v_t
       o_t = r_t (S_{t-1} + diag(u) k_t^T v_t)
-  with the bonus u [H, N] constant, and the zero initial state unless given.
+  with the bonus u [H, N] constant, and the zero initial state unless given;
+* the backward (derived here by differentiating the recurrence; the pages give
+  none) is for L = sum_t <go_t, o_t> + <dS_T, S_T>, with the adjoint state
+  G_{t-1} = diag(e^{-w_t}) G_t + r_t^T go_t (G_{T-1} = dS_T): dr, dk, dv, du
+  and dS0 as for RWKV-5 (wkv5_ref.py), and the rate's gradient per token,
+      dw_t = -e^{-w_t} . rowsum(G_t . S_{t-1})
+  (dw [B, T, C], not summed: each token has its own rate).
 
 Parity status: every function here is pinned (tests/test_oracle_wkv6_pins.py).
 """
@@ -34,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["wkv6_forward_ref", "wkv6_direct_ref"]
+__all__ = ["wkv6_forward_ref", "wkv6_direct_ref", "wkv6_backward_ref"]
 
 
 def _heads(x, H):
@@ -94,3 +100,38 @@ def wkv6_direct_ref(w, u, r, k, v, H, S0=None):
                 S0h = np.asarray(S0, dtype=np.float64).reshape(B, H, N, N)[b, h]
                 o[b, :, h] += (r[b, :, h] * np.exp(-Lb[t])) @ S0h
     return o.reshape(B, T, H * N)
+
+
+def wkv6_backward_ref(w, u, r, k, v, go, H, S0=None, dST=None):
+    """Gradients of L = sum_t <go_t, o_t> + <dST, S_T> for
+    (o, S_T) = wkv6_forward_ref(w, u, r, k, v, H, S0), in float64: a forward
+    pass keeping every S_{t-1}, then the adjoint state G (starting from dST,
+    [B, H, N, N] or None for zero) walked backwards in time.
+
+    Returns (dr, dk, dv, dw [B, T, C], du [H, N] summed over the batch, dS0
+    [B, H, N, N]).
+    """
+    w, r, k, v, go = (_heads(x, H) for x in (w, r, k, v, go))
+    B, T, _, N = r.shape
+    u = np.asarray(u, dtype=np.float64).reshape(H, N)
+    with np.errstate(over="ignore"):
+        d = np.exp(-w)
+    S = np.zeros((B, H, N, N)) if S0 is None else np.array(S0, dtype=np.float64).reshape(B, H, N, N)
+    prev = np.empty((T, B, H, N, N))                                      # S_{t-1}
+    for t in range(T):
+        prev[t] = S
+        S = d[:, t, :, :, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
+    G = np.zeros((B, H, N, N)) if dST is None else np.array(dST, dtype=np.float64).reshape(B, H, N, N)
+    dr, dk, dv, dw = (np.empty((B, T, H, N)) for _ in range(4))
+    du = np.zeros((H, N))
+    for t in range(T - 1, -1, -1):
+        vg = np.einsum("bhj,bhj->bh", v[:, t], go[:, t])                 # v_t . go_t
+        bonus = np.einsum("bhi,hi,bhi->bh", r[:, t], u, k[:, t])
+        dr[:, t] = np.einsum("bhij,bhj->bhi", prev[t], go[:, t]) + u[None] * k[:, t] * vg[..., None]
+        dk[:, t] = np.einsum("bhij,bhj->bhi", G, v[:, t]) + u[None] * r[:, t] * vg[..., None]
+        dv[:, t] = np.einsum("bhi,bhij->bhj", k[:, t], G) + bonus[..., None] * go[:, t]
+        du += np.einsum("bhi,bhi,bh->hi", r[:, t], k[:, t], vg)
+        dw[:, t] = -d[:, t] * np.einsum("bhij,bhij->bhi", G, prev[t])
+        G = d[:, t, :, :, None] * G + r[:, t, :, :, None] * go[:, t, :, None, :]
+    return (dr.reshape(B, T, H * N), dk.reshape(B, T, H * N), dv.reshape(B, T, H * N), dw.reshape(B, T, H * N), du,
+            G)
