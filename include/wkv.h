@@ -1,8 +1,8 @@
 /*
  * wkv.h - C ABI of the RWKV-4 WKV time-mixing operator for AMD MI355X (gfx950),
  * with the receptance gate and the token-shift mix around it, and the
- * matrix-state WKV of RWKV-5 (forward and backward) and RWKV-6 (per-token
- * decay, forward).
+ * matrix-state WKV of RWKV-5 and RWKV-6 (per-token decay), forward and
+ * backward.
  *
  * The operator, per channel c of each batch row b, tokens t = 1..T
  * ("RWKV（Receptance Weighted Key Value）概念", section 3.2; and
@@ -253,13 +253,14 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
  * from chunk-local cumulative rates in float32.  A rate above 10 acts as 10:
  * a term's decay across such a token is then at most e^{-10} instead of less.
  *
- * B, T, H, N, in_dtype, u, r, k, v, o, s_in, s_out  as wkv5_forward.
+ * B, T, H, N, in_dtype, u, r, k, v, o, s_in, s_out, ckpt  as wkv5_forward
+ *           (ckpt: wkv5_ckpt_bytes() bytes, for a later wkv6_backward).
  * w         [B, T, 64 H] float32 rates, >= 0 and finite, 16-byte aligned.
  * Errors as wkv5_forward.
  */
 wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
                           const float* w, const float* u, const void* r, const void* k, const void* v,
-                          float* o, const float* s_in, float* s_out, void* hip_stream);
+                          float* o, const float* s_in, float* s_out, void* ckpt, void* hip_stream);
 
 /* Bytes of wkv5_forward's chunk-start states for (B, T, H, N): bf16
  * [B, H, ceil(T/64), 64, 64] (key-major), rounded up to 256.  Opaque to the
@@ -311,6 +312,43 @@ size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N,
  * is written on an error).
  */
 wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
+                           const float* w, const float* u, const void* r, const void* k, const void* v,
+                           const void* go, const float* s_in, const float* ds_out, float* dr, float* dk,
+                           float* dv, float* dw, float* du, float* ds_in, const void* ckpt, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
+/* Sizes for the RWKV-6 calls: the same layouts as wkv5_ckpt_bytes() and
+ * wkv5_backward_workspace_bytes() (the backward's scratch is only the du
+ * partials and, without a ckpt, the recomputed chunk-start states). */
+size_t wkv6_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
+size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt);
+
+/*
+ * wkv6_backward - gradients of wkv6_forward.
+ *
+ * The pages give no backward; this is the derivative of the recurrence that
+ * wkv6_forward defines, for L = sum_t <go_t, o_t> + <ds_out, S_T>.  With the
+ * adjoint state G_T = ds_out (0 when NULL),
+ * G_{t-1} = diag(e^{-w_t}) G_t + r_t^T go_t, dr, dk, dv, du and dS0 are as for
+ * wkv5_backward, and each token's rate has its own gradient
+ *     dw_t = -e^{-w_t} . rowsum(G_t . S_{t-1})          ([B, T, 64 H], not summed)
+ * Computed chunkwise with the same bf16 matrix-core products and float32
+ * accumulation as the forward; dw_t is assembled from prefix and suffix sums
+ * of non-negative-weight terms inside the chunk (no difference of large sums).
+ * Rates above 10 act as 10, as in the forward: such a token's dw is that of
+ * the operator with the rate 10 (e^{-10} times the adjoint-state product),
+ * not 0, so the cap does not cut the gradient off.
+ *
+ * B, T, H, N, in_dtype, w, u, r, k, v, s_in  as wkv6_forward.
+ * go, ds_out, dr, dk, dv, du, ds_in, workspace  as wkv5_backward
+ *           (workspace: wkv6_backward_workspace_bytes(..., ckpt != NULL)).
+ * dw        [B, T, 64 H] float32, fully overwritten.
+ * ckpt      the ckpt a wkv6_forward call on the same w, u, r, k, v and s_in
+ *           wrote, or NULL (then s_in is read to recompute it).
+ * du is summed over the batch in a fixed order (bitwise reproducible).
+ * Errors as wkv5_backward (nothing is written on an error).
+ */
+wkv_status_t wkv6_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
                            const float* w, const float* u, const void* r, const void* k, const void* v,
                            const void* go, const float* s_in, const float* ds_out, float* dr, float* dk,
                            float* dv, float* dw, float* du, float* ds_in, const void* ckpt, void* workspace,

@@ -31,6 +31,9 @@ EXPORTS = (
     "wkv5_ckpt_bytes",
     "wkv5_backward_workspace_bytes",
     "wkv5_backward",
+    "wkv6_ckpt_bytes",
+    "wkv6_backward_workspace_bytes",
+    "wkv6_backward",
     "wkv_token_shift_workspace_bytes",
     "wkv_token_shift",
     "wkv_token_shift_backward",
@@ -87,13 +90,20 @@ def declare(L):
     L.wkv5_forward.restype = i32
     L.wkv5_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp]
     L.wkv6_forward.restype = i32
-    L.wkv6_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp]
+    L.wkv6_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp]
     L.wkv5_ckpt_bytes.restype = sz
     L.wkv5_ckpt_bytes.argtypes = [i64, i64, i64, i64]
     L.wkv5_backward_workspace_bytes.restype = sz
     L.wkv5_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     L.wkv5_backward.restype = i32
     L.wkv5_backward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp, vp,
+                                sz, vp]
+    L.wkv6_ckpt_bytes.restype = sz
+    L.wkv6_ckpt_bytes.argtypes = [i64, i64, i64, i64]
+    L.wkv6_backward_workspace_bytes.restype = sz
+    L.wkv6_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.wkv6_backward.restype = i32
+    L.wkv6_backward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp, vp,
                                 sz, vp]
     L.wkv_token_shift_workspace_bytes.restype = sz
     L.wkv_token_shift_workspace_bytes.argtypes = [i64, i64, i64, i64]

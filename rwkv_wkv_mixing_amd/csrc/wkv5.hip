@@ -351,6 +351,8 @@ __device__ __forceinline__ f4 exp_neg4(f4 x) {  // e^{-x}, elementwise
     return f4{ex2(-x[0] * kL2E), ex2(-x[1] * kL2E), ex2(-x[2] * kL2E), ex2(-x[3] * kL2E)};
 }
 
+// kOut = false: a state-only pass (the chunk-start states into P.ckpt and the final state).
+template <bool kOut>
 __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
     __shared__ Wkv6Shared sm;
     // lane coordinates; made opaque at the top of every chunk so that lane-dependent LDS
@@ -422,7 +424,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 
     stage(0, 0);
     stage_w(0);
-    put_state();
+    if constexpr (kOut) put_state();
     wait_staged();
 
     for (int64_t ch = 0; ch < nch; ++ch) {
@@ -451,6 +453,14 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         }
         lds_sync();  // E ready
         if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
+        if (P.ckpt != nullptr) {  // the state before the chunk, bf16 [key][value], for the backward
+            uint16_t* cp = P.ckpt + (bh * nch + ch) * kN * kN;
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cp[(16 * wv + 4 * g + e) * kN + 16 * J + l16] = static_cast<uint16_t>(pk2(S[J][e], 0.f) & 0xffffu);
+        }
 
         const uint16_t(*R)[kN] = sm.in[buf][0];
         const uint16_t(*K)[kN] = sm.in[buf][1];
@@ -462,7 +472,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
         for (int J = 0; J < 4; ++J) O[J] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < 4 && kOut; ++I) {
             const int c4 = 16 * I + 4 * g;
             const s4 a = mul_pack(row4(&R[tau][sw(tau, c4)]), exp_neg4(e4(tau, c4)));
 #pragma unroll
@@ -479,12 +489,12 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         // ---- intra-chunk attention, transposed (lane: A[tau = P0 + l16][sig = 16 Q + 4 g + e]) --
         s4 rof[4];  // r_tau e^{-(E[tau] - E[P0])}, the off-diagonal blocks' receptance operand
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < 4 && kOut; ++I) {
             const int c4 = 16 * I + 4 * g;
             rof[I] = mul_pack(row4(&R[tau][sw(tau, c4)]), exp_neg4(e4(tau, c4) - e4(P0, c4)));
         }
 #pragma unroll
-        for (int Q = 0; Q < 4; ++Q) {
+        for (int Q = 0; Q < 4 && kOut; ++Q) {
             if (Q > wv) break;
             f4 At = {0.f, 0.f, 0.f, 0.f};
             const int sig = 16 * Q + l16;  // this lane's key token (m index of K~)
@@ -550,8 +560,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         for (int Q = 0; Q < 4; ++Q)
 #pragma unroll
             for (int J = 0; J < 4; ++J) S[J] = mfma(aS[Q], Vb[Q][J], S[J]);
-        put_state();
+        if constexpr (kOut) put_state();
         wait_staged();
+        if constexpr (!kOut) continue;
 
         // ---- outputs: lane holds O[tau = P0 + 4 g + e][16 J + l16] --------------------------------
         const Rsrc ro = make_rsrc(P.o + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
@@ -1045,6 +1056,545 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
     }
 }
 
+// ---- RWKV-6 backward -----------------------------------------------------------------------
+// The RWKV-5 backward with every decay between two points of a chunk e^{-(E[a] - E[b])} (E the
+// chunk-local cumulative capped rates of the RWKV-6 forward), and the rate's gradient per token,
+//     dw_tau = -e^{-w_tau} rowsum(G_tau . S_{tau-1})
+//            = -[ e^{-E[n]} rowsum(G1 . S0)                                             (a)
+//                 + sum_{sig < tau} q_sig,   q_sig = e^{-(E[n] - E[sig+1])} k_sig . (G1 v_sig^T)   (b)
+//                 + sum_{s > tau} p_s,       p_s = e^{-E[s]} r_s . (S0 go_s^T)                     (c)
+//                 + sum_{sig < tau < s} X[s][sig] ],
+//       X[s][sig] = e^{-(E[s] - E[sig+1])} r_s . k_sig C[s][sig]                                   (d)
+// for the operator with capped rates, as the forward computes it.  (b) and (c) are prefix and
+// suffix sums of per-token terms the dk and dr products already form.  (d) splits by 16-token
+// blocks: whole block pairs on either side of tau's block (F), pairs with one end in tau's block
+// (prefix / suffix sums of the per-block dk and dr terms) and pairs inside it (elementwise).
+// Every piece is a sum of products of the inputs with positive weights: no difference of large
+// sums, which at bf16 precision would swamp the small dw of fast-decaying channels.
+struct Wkv6BwdShared {
+    union {
+        uint16_t in[4][kLc][kN];    // r, k, v, go of the chunk, [token][swizzled channel]
+        float dwt[kLc][kPadF];      // the chunk's dw partials, [token][channel], after its last barrier
+        float fin[kWaves5][4][kN];  // du partials [wave][k-group][channel], after the chunk walk
+    };
+    uint16_t gs[kN][kPadH];         // G1, bf16, [key][value]
+    uint16_t ss[kN][kN];            // S0, bf16, [key][swizzled value]
+    float E[kLc + 1][kN];           // cumulative capped rates, float4 slot (i / 4) ^ (t & 15) of row t
+    float uu[kN];
+    float cd[kLc];                  // C[s][s] = go_s . v_s
+    float cdg[kWaves5][16][16];     // each block's diagonal block of C, [s][sig], sig < s
+    float xa[kN];                   // (a) per channel
+    float xq[kWaves5][kN];          // block totals of q
+    float xp[kWaves5][kN];          // block totals of p
+    float F[kWaves5][kWaves5][kN];  // F[A][B]: sum over sig in block A, s in block B > A of X[s][sig]
+};
+
+// float4 reads and writes of the tables need 16-byte aligned rows (the block's only shared object starts at 0)
+static_assert(offsetof(Wkv6BwdShared, E) % 16 == 0 && offsetof(Wkv6BwdShared, cdg) % 16 == 0 &&
+                  offsetof(Wkv6BwdShared, uu) % 16 == 0 && sizeof(Wkv6BwdShared) <= 80 * 1024,
+              "RWKV-6 backward LDS layout");
+
+// Over the 16 tokens 4 g + e of a wave's block (lanes l16, l16 + 16, l16 + 32, l16 + 48 hold
+// tokens 4 g .. 4 g + 3 of column l16): exclusive prefix and suffix sums of v.
+__device__ __forceinline__ void scan16(const f4& v, int g, f4& pre, f4& suf) {
+    const float t = v[0] + v[1] + v[2] + v[3];
+    float below = 0.f, above = 0.f;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+        const float up = __shfl_up(t, 16 * k, 64), dn = __shfl_down(t, 16 * k, 64);
+        if (g >= k) below += up;
+        if (g + k < 4) above += dn;
+    }
+    pre[0] = below;
+    pre[1] = below + v[0];
+    pre[2] = pre[1] + v[1];
+    pre[3] = pre[2] + v[2];
+    suf[3] = above;
+    suf[2] = above + v[3];
+    suf[1] = suf[2] + v[2];
+    suf[0] = suf[1] + v[1];
+}
+
+// the sum of x over the four k-groups of a column (tokens of a block), in a fixed order
+__device__ __forceinline__ float sum_groups(float x) {
+    const float a = x + __shfl_xor(x, 16, 64);
+    return a + __shfl_xor(a, 32, 64);
+}
+
+__global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P) {
+    __shared__ Wkv6BwdShared sm;
+    // lane coordinates; made opaque at the top of every chunk (as in the RWKV-5 backward)
+    int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int l16 = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / P.H, h = bh - b * P.H;
+    const int64_t C = P.H * kN;
+    const int64_t nch = (P.T + kLc - 1) / kLc;
+    const int P0 = 16 * wv;
+
+    if (threadIdx.x < kN) {
+        sm.uu[threadIdx.x] = P.u[h * kN + threadIdx.x];
+        sm.E[0][threadIdx.x] = 0.f;  // row 0 is never staged over
+    }
+    // G: wave wv, tile J, lane (l16, g), element e holds G[16 wv + 4 g + e][16 J + l16]
+    f4 G[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = P0 + 4 * g + e, j = 16 * J + l16;
+            G[J][e] = P.ds_out != nullptr ? P.ds_out[bh * kN * kN + key * kN + j] : 0.f;
+            sm.gs[key][j] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
+        }
+    float duv[4] = {0.f, 0.f, 0.f, 0.f};  // channel 16 I + l16
+
+    auto rd = [](const uint16_t(*X)[kN], int t, int c) { return bf(X[t][sw(t, c)]); };
+    auto row4s = [](const uint16_t(*X)[kN], int t, int c4) { return row4(&X[t][sw(t, c4)]); };
+    auto raw4s = [](const uint16_t(*X)[kN], int t, int c4) { return raw4(&X[t][sw(t, c4)]); };
+    auto colTp = [&](const uint16_t(*X)[kPadH], int tb, int c0) {  // col_tr for the padded, unswizzled G tile
+        const int t = tb + 4 * g + (l16 >> 2), c = c0 + 4 * (l16 & 3);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)&X[t][c]);
+    };
+    auto colTf = [&](const uint16_t(*X)[kN], int tb, int c0) {
+        const u16x4 x = __builtin_bit_cast(u16x4, col_tr(X, tb, c0, l16, g));
+        return f4{bf(x[0]), bf(x[1]), bf(x[2]), bf(x[3])};
+    };
+    auto e4 = [&](int t, int c4) { return frow4(&sm.E[t][swE(t, c4)]); };  // E[t][c4 .. c4 + 3]
+    auto e1 = [&](int t, int c) { return sm.E[t][swE(t, c)]; };
+    auto xe = [](float x) { return ex2(-x * kL2E); };  // e^{-x}
+    auto rot = [](float (&x)[4]) {
+        const float t = x[0];
+        x[0] = x[1];
+        x[1] = x[2];
+        x[2] = x[3];
+        x[3] = t;
+    };
+    auto rot4 = [](f4 (&x)[4]) {
+        const f4 t = x[0];
+        x[0] = x[1];
+        x[1] = x[2];
+        x[2] = x[3];
+        x[3] = t;
+    };
+
+    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
+        const int64_t t0 = ch * kLc;
+        const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
+        lds_sync();  // the previous chunk's dw assembly has left the input buffer and the tables
+        // ---- stage r, k, v, go (swizzled rows), S0, and the rates into E rows 1 + token ----------
+        const uint16_t* src[4] = {P.r, P.k, P.v, P.go};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const Rsrc rs = make_rsrc(src[a] + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 2));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = P0 + 8 * i + lane / 8;
+                const int q = (lane % 8) ^ (row & 7);
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+            }
+        }
+        {
+            const Rsrc rs = make_rsrc(P.ckpt + (bh * nch + ch) * kN * kN, kN * kN * 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = P0 + 8 * i + lane / 8;
+                const int q = (lane % 8) ^ (row & 7);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&sm.ss[P0 + 8 * i][0],
+                                                         16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, 0);
+            }
+        }
+        {
+            const Rsrc rs = make_rsrc(P.w + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = P0 + 4 * i + lane / 16;  // token; LDS row t + 1
+                const int q = (lane % 16) ^ ((t + 1) & 15);
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(t) * C) * 4 + q * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.E[P0 + 4 * i + 1][0], 16, voff, 0, 0, 0);
+            }
+        }
+        wait_staged();
+        lds_sync();
+        {  // E[t + 1] = E[t] + min(w_t, cap), as in the forward
+            const int c = P0 + l16, t1 = 16 * g + 1;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
+            float off = 0.f;
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                const float v = __shfl_up(x[15], 16 * k, 64);
+                if (g >= k) off += v;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sm.E[t1 + i][swE(t1 + i, c)] = x[i] + off;
+        }
+        lds_sync();  // E ready
+
+        const uint16_t(*R)[kN] = sm.in[0];
+        const uint16_t(*K)[kN] = sm.in[1];
+        const uint16_t(*V)[kN] = sm.in[2];
+        const uint16_t(*GO)[kN] = sm.in[3];
+        const uint16_t(*SS)[kN] = sm.ss;
+
+        // ---- C[s][s] of this wave's tokens -------------------------------------------------------
+        f4 Cpp = {0.f, 0.f, 0.f, 0.f};  // lane: C[s = P0 + 4 g + e][sig = P0 + l16]
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const int j4 = 16 * J + 4 * g;
+            Cpp = mfma(raw4s(GO, P0 + l16, j4), raw4s(V, P0 + l16, j4), Cpp);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // read back only by this wave (in order)
+            if (4 * g + e == l16) sm.cd[P0 + l16] = Cpp[e];
+
+        const int sig = P0 + l16;  // this lane's key token as an m index
+        const int mid = P0 + 8;    // the diagonal block's reference token
+        f4 dwp[4];                 // dw partials, [tile I]: token P0 + 4 g + e, channel 16 I + l16
+#pragma unroll
+        for (int I = 0; I < 4; ++I) dwp[I] = f4{0.f, 0.f, 0.f, 0.f};
+
+        // ---- dv: (k . e^{-(E[n]-E[sig+1])}) G1 + sum_{s >= sig} A[s][sig] go_s ----------------------
+        {
+            const int nk = nv - 1 - sig;
+            s4 aK[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int c4 = 16 * I + 4 * g;
+                aK[I] = nk >= 0 ? mul_pack(row4s(K, sig, c4), exp_neg4(e4(nv, c4) - e4(sig + 1, c4))) : s4{0, 0, 0, 0};
+            }
+            s4 aA[4];  // aA[Q], Q >= wv: [m = sig][k = s]: A[s = 16 Q + 4 g + e][sig]
+#pragma unroll
+            for (int Q = 0; Q < 4; ++Q) {
+                aA[Q] = s4{0, 0, 0, 0};
+                if (Q < wv) continue;
+                f4 At = {0.f, 0.f, 0.f, 0.f};
+                const int s_m = 16 * Q + l16;
+                if (Q > wv) {
+                    const int p0 = 16 * Q;
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        const int c4 = 16 * I + 4 * g;
+                        const f4 ep = e4(p0, c4);
+                        const s4 ra = mul_pack(row4s(R, s_m, c4), exp_neg4(e4(s_m, c4) - ep));
+                        const s4 kb = mul_pack(row4s(K, sig, c4), exp_neg4(ep - e4(sig + 1, c4)));
+                        At = mfma(ra, kb, At);
+                    }
+                } else {
+                    f4 Bn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        const int c4 = 16 * I + 4 * g;
+                        const f4 rr = row4s(R, s_m, c4), kk = row4s(K, sig, c4), em = e4(mid, c4);
+                        At = mfma(mul_pack(rr, exp_neg4(e4(s_m, c4) - em)), mul_pack(kk, exp_neg4(em - e4(sig + 1, c4))), At);
+                        Bn = mfma(mul_pack(rr, frow4(&sm.uu[c4])), pack4(kk[0], kk[1], kk[2], kk[3]), Bn);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int sl = 4 * g + e;
+                        At[e] = sl > l16 ? At[e] : (sl == l16 ? Bn[e] : 0.f);
+                    }
+                }
+                aA[Q] = pack4(At[0], At[1], At[2], At[3]);
+            }
+            const Rsrc rv = make_rsrc(P.dv + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll 1
+            for (int J = 0; J < 4; ++J) {
+                f4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int I = 0; I < 4; ++I) D = mfma(aK[I], colTp(sm.gs, 16 * I, 16 * J), D);
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q)
+                    if (Q >= wv) D = mfma(aA[Q], col_tr(GO, 16 * Q, 16 * J, l16, g), D);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    store_wb(D[e], rv, static_cast<uint32_t>(((P0 + 4 * g + e) * C + 16 * J + l16) * 4));
+            }
+        }
+
+        // ---- dk, with dw's (b) terms q and its column sums toward later blocks -------------------
+        {
+            s4 aC[4];  // aC[Q], Q >= wv: [m = sig][k = s]: C[s = 16 Q + 4 g + e][sig], s > sig
+#pragma unroll
+            for (int Q = 0; Q < 4; ++Q) {
+                aC[Q] = s4{0, 0, 0, 0};
+                if (Q < wv) continue;
+                f4 Cq = {0.f, 0.f, 0.f, 0.f};
+                if (Q == wv) {
+                    Cq = Cpp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e > l16 ? Cq[e] : 0.f;
+                } else {
+#pragma unroll
+                    for (int J = 0; J < 4; ++J) {
+                        const int j4 = 16 * J + 4 * g;
+                        Cq = mfma(raw4s(GO, 16 * Q + l16, j4), raw4s(V, sig, j4), Cq);
+                    }
+                }
+                aC[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
+            }
+            const Rsrc rk = make_rsrc(P.dk + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll 1
+            for (int I = 0; I < 4; ++I) {  // lane: dk[sig = P0 + 4 g + e][i = 16 I + l16]
+                const int i = 16 * I + l16;
+                f4 X = {0.f, 0.f, 0.f, 0.f};  // X = V G1^T
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    X = mfma(raw4s(V, sig, j4), raw4(&sm.gs[i][j4]), X);
+                }
+                const f4 kc = colTf(K, P0, 16 * I);
+                const float en = e1(nv, i);
+                f4 D, q, cs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sg = P0 + 4 * g + e;
+                    const float pk = sg < nv ? xe(en - e1(sg + 1, i)) : 0.f;
+                    D[e] = X[e] * pk;
+                    q[e] = kc[e] * D[e];
+                }
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q) {
+                    if (Q < wv) continue;
+                    const int p0 = 16 * Q;
+                    const int ref = Q > wv ? p0 : mid;  // the split point
+                    const float er = e1(ref, i);
+                    const f4 rc = colTf(R, p0, 16 * I);
+                    float rb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rb[e] = rc[e] * xe(e1(p0 + 4 * g + e, i) - er);
+                    const f4 M = mfma(aC[Q], pack4(rb[0], rb[1], rb[2], rb[3]), f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = M[e] * xe(er - e1(P0 + 4 * g + e + 1, i));
+                        D[e] += t;
+                        if (Q > wv) cs[e] += kc[e] * t;  // pairs reaching a later block
+                    }
+                }
+                const f4 rcp = colTf(R, P0, 16 * I);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sg = P0 + 4 * g + e;
+                    store_wb(D[e] + sm.uu[i] * rcp[e] * sm.cd[sg], rk, static_cast<uint32_t>((sg * C + i) * 4));
+                }
+                f4 pre, suf;
+                scan16(q + cs, g, pre, suf);
+                dwp[0] += pre;
+                const float tq = sum_groups(q[0] + q[1] + q[2] + q[3]);
+                if (g == 0) sm.xq[wv][i] = tq;
+                rot4(dwp);
+            }
+        }
+
+        // ---- dr, du, with dw's (c) terms p and its row sums from earlier blocks --------------------
+        {
+            const int s_n = P0 + l16;
+            s4 aR[4];  // aR[Q], Q <= wv: [m = s][k = sig]: C[s = P0 + l16][sig = 16 Q + 4 g + e], sig < s
+#pragma unroll
+            for (int Q = 0; Q < 4; ++Q) {
+                aR[Q] = s4{0, 0, 0, 0};
+                if (Q > wv) continue;
+                f4 Cq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    Cq = mfma(raw4s(V, 16 * Q + l16, j4), raw4s(GO, s_n, j4), Cq);
+                }
+                if (Q == wv) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e < l16 ? Cq[e] : 0.f;
+                    *reinterpret_cast<f4*>(&sm.cdg[wv][l16][4 * g]) = Cq;  // [s][sig]
+                }
+                aR[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
+            }
+            const Rsrc rr = make_rsrc(P.dr + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll 1
+            for (int I = 0; I < 4; ++I) {  // lane: dr[s = P0 + 4 g + e][i = 16 I + l16]
+                const int i = 16 * I + l16;
+                f4 Y = {0.f, 0.f, 0.f, 0.f};  // Y = GO S0^T
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const int j4 = 16 * J + 4 * g;
+                    Y = mfma(raw4s(GO, s_n, j4), raw4(&SS[i][sw(i, j4)]), Y);
+                }
+                const f4 rc = colTf(R, P0, 16 * I);
+                f4 D, p, rs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    D[e] = Y[e] * xe(e1(P0 + 4 * g + e, i));
+                    p[e] = rc[e] * D[e];
+                }
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q) {
+                    if (Q > wv) continue;
+                    const int ref = Q < wv ? P0 : mid;
+                    const float er = e1(ref, i);
+                    const f4 kc = colTf(K, 16 * Q, 16 * I);
+                    float kb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kb[e] = kc[e] * xe(er - e1(16 * Q + 4 * g + e + 1, i));
+                    const f4 M1 = mfma(aR[Q], pack4(kb[0], kb[1], kb[2], kb[3]), f4{0.f, 0.f, 0.f, 0.f});
+                    float fq = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = M1[e] * xe(e1(P0 + 4 * g + e, i) - er);
+                        D[e] += t;
+                        if (Q < wv) {  // pairs from an earlier block
+                            const float x = rc[e] * t;
+                            rs[e] += x;
+                            fq += x;
+                        }
+                    }
+                    if (Q < wv) {
+                        const float tf = sum_groups(fq);
+                        if (g == 0) sm.F[Q][wv][i] = tf;
+                    }
+                }
+                const f4 kcol = colTf(K, P0, 16 * I);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = P0 + 4 * g + e;
+                    const float kc = kcol[e] * sm.cd[s];
+                    duv[0] += rc[e] * kc;
+                    store_wb(D[e] + sm.uu[i] * kc, rr, static_cast<uint32_t>((s * C + i) * 4));
+                }
+                f4 pre, suf;
+                scan16(p + rs, g, pre, suf);
+                dwp[0] += suf;
+                const float tp = sum_groups(p[0] + p[1] + p[2] + p[3]);
+                if (g == 0) sm.xp[wv][i] = tp;
+                rot4(dwp);
+                rot(duv);
+            }
+        }
+
+        // ---- (a): e^{-E[n]} rowsum(G1 . S0), and G0 = e^{-E[n]} . G1 + sum_s (r_s e^{-E[s]})^T go_s ---
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = P0 + 4 * g + e;
+            const float dn = xe(e1(nv, key));
+            float acc = 0.f;
+#pragma unroll
+            for (int J = 0; J < 4; ++J) acc += G[J][e] * bf(SS[key][sw(key, 16 * J + l16)]);
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            acc += __shfl_xor(acc, 4, 64);
+            acc += __shfl_xor(acc, 8, 64);
+            if (l16 == 0) sm.xa[key] = dn * acc;
+#pragma unroll
+            for (int J = 0; J < 4; ++J) G[J][e] *= dn;
+        }
+        {
+            const int key = P0 + l16;  // the m index of (R^)^T
+#pragma unroll 1
+            for (int Q = 0; Q < 4; ++Q) {
+                float ra[4];
+                const f4 rc = colTf(R, 16 * Q, P0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 16 * Q + 4 * g + e;
+                    ra[e] = s < nv ? rc[e] * xe(e1(s, key)) : 0.f;
+                }
+                const s4 a = pack4(ra[0], ra[1], ra[2], ra[3]);
+#pragma unroll
+                for (int J = 0; J < 4; ++J) G[J] = mfma(a, col_tr(GO, 16 * Q, 16 * J, l16, g), G[J]);
+            }
+        }
+
+        // ---- (d) inside this block, lane = channel: Z[tau] = sum_{sig < tau < s} X[s][sig] ----------
+        float Z[16];
+        {
+            const int i = lane;
+            const float em = e1(mid, i);
+            float rf[16], kg[16];
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                rf[a] = rd(R, P0 + a, i) * xe(e1(P0 + a, i) - em);
+                kg[a] = rd(K, P0 + a, i) * xe(em - e1(P0 + a + 1, i));
+                Z[a] = 0.f;
+            }
+#pragma unroll
+            for (int s = 2; s < 16; ++s) {
+                const f4* crow = reinterpret_cast<const f4*>(&sm.cdg[wv][s][0]);
+                float pre = 0.f;
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    if (4 * c4 + 1 > s - 1) continue;  // sig = tau - 1 <= s - 2
+                    const f4 cv = crow[c4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int tau = 4 * c4 + e + 1;  // pairs sig < tau, taken up to sig = tau - 1
+                        if (tau <= s - 1) {
+                            pre = fmaf(rf[s] * kg[tau - 1], cv[e], pre);
+                            Z[tau] += pre;
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep each row's loads with it (register pressure)
+            }
+        }
+        lds_sync();  // every wave is done with this chunk's G1, inputs, E and block totals are written
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.gs[P0 + 4 * g + e][16 * J + l16] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
+
+        // ---- assemble dw for this block: the partials through LDS to one lane per channel --------
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.dwt[P0 + 4 * g + e][16 * I + l16] = dwp[I][e];
+        {
+            const int i = lane;
+            float base = sm.xa[i];
+            for (int A = 0; A < wv; ++A) base += sm.xq[A][i];
+            for (int B = wv + 1; B < kWaves5; ++B) base += sm.xp[B][i];
+            for (int A = 0; A < wv; ++A)
+                for (int B = wv + 1; B < kWaves5; ++B) base += sm.F[A][B][i];
+            const Rsrc rw = make_rsrc(P.dw + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
+#pragma unroll
+            for (int a = 0; a < 16; ++a)
+                store_wb(-(sm.dwt[P0 + a][i] + Z[a] + base), rw, static_cast<uint32_t>(((P0 + a) * C + i) * 4));
+        }
+    }
+
+    if (P.ds_in != nullptr) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P.ds_in[bh * kN * kN + (P0 + 4 * g + e) * kN + 16 * J + l16] = G[J][e];
+    }
+    // ---- du of this (batch row, head), summed in a fixed order ------------------------------------
+    lds_sync();  // every wave is done with the last chunk's dw assembly
+#pragma unroll
+    for (int I = 0; I < 4; ++I) sm.fin[wv][g][16 * I + l16] = duv[I];
+    lds_sync();
+    if (threadIdx.x < kN) {
+        const int i = threadIdx.x;
+        float su = 0.f;
+        for (int ww = 0; ww < kWaves5; ++ww)
+            for (int gg = 0; gg < 4; ++gg) su += sm.fin[ww][gg][i];
+        P.part[bh * kN + i] = su;
+    }
+}
+
+// du[h, i] = sum over batch rows (in order) of the per-(batch row, head) partials
+__global__ void wkv6_du_reduce_kernel(const float* part, int64_t B, int64_t H, float* du) {
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (q >= H * kN) return;
+    float c = 0.f;
+    for (int64_t b = 0; b < B; ++b) c += part[b * H * kN + q];
+    du[q] = c;
+}
+
 // dw[h, i], du[h, i] = sum over batch rows (in order) of the per-(batch row, head) partials
 __global__ void wkv5_reduce_kernel(const float* part, int64_t B, int64_t H, float* dw, float* du) {
     const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -1084,8 +1634,22 @@ hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_wkv6_bwd(const Wkv6BwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(wkv6_bwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = a.H * kN;
+    hipLaunchKernelGGL(wkv6_du_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       a.part, a.B, a.H, a.du);
+    return hipGetLastError();
+}
+
 hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL(wkv6_fwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    if (a.o == nullptr) {
+        hipLaunchKernelGGL(wkv6_fwd_kernel<false>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(wkv6_fwd_kernel<true>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -301,7 +301,7 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
 
 wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                           const float* u, const void* r, const void* k, const void* v, float* o,
-                          const float* s_in, float* s_out, void* hip_stream) {
+                          const float* s_in, float* s_out, void* ckpt, void* hip_stream) {
     const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
     if (p.st != WKV_OK) return p.st;
     if (p.bh == 0) return WKV_OK;
@@ -309,10 +309,12 @@ wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (T == 0) return hip_status(wkv::launch_wkv5_state_copy(s_in, s_out, p.ns, stream));
     if (!w || !u || !r || !k || !v || !o) return WKV_EINVAL;
-    if (!aligned(w, 16) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16))
+    if (!aligned(w, 16) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
     wkv::Wkv6Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), o, s_in, s_out};
+    a.ckpt = static_cast<uint16_t*>(ckpt);
     return hip_status(wkv::launch_wkv6_fwd(a, stream));
 }
 
@@ -359,6 +361,53 @@ wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
     wkv::Wkv5BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), states, ds_out,
                         dr, dk, dv, part, dw, du, ds_in};
     return hip_status(wkv::launch_wkv5_bwd(ba, stream));
+}
+
+size_t wkv6_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N) { return wkv5_ckpt_bytes(B, T, H, N); }
+
+size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt) {
+    return wkv5_backward_workspace_bytes(B, T, H, N, have_ckpt);
+}
+
+wkv_status_t wkv6_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
+                           const float* u, const void* r, const void* k, const void* v, const void* go,
+                           const float* s_in, const float* ds_out, float* dr, float* dk, float* dv, float* dw,
+                           float* du, float* ds_in, const void* ckpt, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    if (H == 0) return WKV_OK;
+    if (!du) return WKV_EINVAL;
+    if (!aligned(du, 4) || (ds_in && !aligned(ds_in, 4)) || (ds_out && !aligned(ds_out, 4))) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (B == 0 || T == 0) {  // empty sum: du = 0, and dS0 = dS_T (dw has no elements)
+        hipError_t e = wkv::launch_shift_zero(du, H * 64, stream);
+        if (e == hipSuccess && ds_in != nullptr) e = wkv::launch_wkv5_state_copy(ds_out, ds_in, p.ns, stream);
+        return hip_status(e);
+    }
+    if (!w || !u || !r || !k || !v || !go || !dr || !dk || !dv || !dw) return WKV_EINVAL;
+    if (!aligned(w, 16) || !aligned(u, 4) || !aligned(dr, 4) || !aligned(dk, 4) || !aligned(dv, 4) ||
+        !aligned(dw, 4) || (s_in && !aligned(s_in, 4)) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(go, 16) || (ckpt && !aligned(ckpt, 16)))
+        return WKV_EALIGN;
+    const size_t need = p.ws_bytes + (ckpt ? 0 : p.ckpt_bytes);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    auto* part = static_cast<float*>(workspace);
+    const auto* r16 = static_cast<const uint16_t*>(r);
+    const auto* k16 = static_cast<const uint16_t*>(k);
+    const auto* v16 = static_cast<const uint16_t*>(v);
+    const uint16_t* states = static_cast<const uint16_t*>(ckpt);
+    if (ckpt == nullptr) {  // the states before every chunk, recomputed by a state-only forward pass
+        auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + p.ws_bytes);
+        wkv::Wkv6Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
+        fa.ckpt = tmp;
+        hipError_t e = wkv::launch_wkv6_fwd(fa, stream);
+        if (e != hipSuccess) return hip_status(e);
+        states = tmp;
+    }
+    wkv::Wkv6BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), states, ds_out,
+                        dr, dk, dv, dw, part, du, ds_in};
+    return hip_status(wkv::launch_wkv6_bwd(ba, stream));
 }
 
 size_t wkv_token_shift_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {

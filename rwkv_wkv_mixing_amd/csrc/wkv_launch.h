@@ -147,9 +147,31 @@ struct Wkv6Args {
     float* o;            // [B, T, C]
     const float* s_in;   // [B, H, 64, 64] or NULL (zero state)
     float* s_out;        // [B, H, 64, 64] or NULL
+    uint16_t* ckpt = nullptr;  // as Wkv5Args::ckpt
 };
 
 hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream);
+
+struct Wkv6BwdArgs {
+    int64_t B, T, H;
+    const float* w;         // [B, T, C] per-token rates
+    const float* u;
+    const uint16_t* r;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* go;     // [B, T, C] bf16 gradient of o
+    const uint16_t* ckpt;   // as Wkv6Args::ckpt
+    const float* ds_out;    // [B, H, 64, 64] gradient of the final state, or NULL (zero)
+    float* dr;              // [B, T, C]
+    float* dk;
+    float* dv;
+    float* dw;              // [B, T, C], per token
+    float* part;            // [B, H, 64]: du of each (batch row, head)
+    float* du;              // [H, 64]
+    float* ds_in;           // [B, H, 64, 64] or NULL
+};
+
+hipError_t launch_wkv6_bwd(const Wkv6BwdArgs& a, hipStream_t stream);
 hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hipStream_t stream);
 hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream);
 

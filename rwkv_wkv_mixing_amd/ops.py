@@ -415,10 +415,10 @@ class Wkv5Function(torch.autograd.Function):
         return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds
 
 
-def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None):
+def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None):
     """RWKV-6 matrix-state WKV with per-token decay: o [B, T, C] float32 from
     w [B, T, C] float32 rates (>= 0), u [H, 64] float32 and r, k, v [B, T, C]
-    bfloat16 (C = 64 H); state handling as wkv5_forward."""
+    bfloat16 (C = 64 H); state handling and ckpt as wkv5_forward."""
     _need(r, "r", torch.bfloat16)
     dev = r.device
     B, T, C = r.shape
@@ -438,7 +438,73 @@ def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
         state_out = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev)
     if state_out is not None:
         _need(state_out, "state_out", torch.float32, (B, H, 64, 64), dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.uint8, None, dev)
+        if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
+            raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
     st = L.lib().wkv6_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
-                              _p(state_out), _stream(dev))
+                              _p(state_out), _p(ckpt), _stream(dev))
     L.check("wkv6_forward", st)
     return (out, state_out) if return_state else out
+
+
+def wkv6_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, ckpt=None,
+                  workspace=None):
+    """Gradients of sum <go, o> + <grad_state_out, S_T> for
+    (o, S_T) = wkv6_forward(w, u, r, k, v, state_in=state_in, return_state=True):
+    returns (dr, dk, dv, dw [B, T, C] float32 (dw per token), du [H, 64]
+    float32 summed over the batch, ds_in [B, H, 64, 64] float32 or None).
+    go: [B, T, C] bfloat16; ckpt: None or what wkv6_forward wrote."""
+    _need(r, "r", torch.bfloat16)
+    dev = r.device
+    B, T, C = r.shape
+    H = u.shape[0]
+    if C != 64 * H:
+        raise ValueError(f"C = {C} is not 64 * H with H = {H}")
+    for t, n in ((k, "k"), (v, "v"), (go, "go")):
+        _need(t, n, torch.bfloat16, (B, T, C), dev)
+    _need(w, "w", torch.float32, (B, T, C), dev)
+    _need(u, "u", torch.float32, (H, 64), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, 64, 64), dev)
+    if grad_state_out is not None:
+        _need(grad_state_out, "grad_state_out", torch.float32, (B, H, 64, 64), dev)
+    dr, dk, dv, dw = (torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(4))
+    du = torch.empty((H, 64), dtype=torch.float32, device=dev)
+    ds = torch.empty((B, H, 64, 64), dtype=torch.float32, device=dev) if need_state_grad else None
+    lib = L.lib()
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.uint8, None, dev)
+        if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
+            raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
+    nbytes = int(lib.wkv6_backward_workspace_bytes(B, T, H, 64, int(ckpt is not None)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    st = lib.wkv6_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
+                           _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    L.check("wkv6_backward", st)
+    return dr, dk, dv, dw, du, ds
+
+
+class Wkv6Function(torch.autograd.Function):
+    """Autograd wrapper: o = wkv6_forward(...); backward through wkv6_backward
+    (go rounded to bfloat16 for the matrix-core products)."""
+
+    @staticmethod
+    def forward(ctx, w, u, r, k, v, state_in=None):
+        B, T, C = r.shape
+        ckpt = new_wkv5_ckpt(B, T, C // 64, r.device)
+        o = wkv6_forward(w, u, r, k, v, state_in=state_in, ckpt=ckpt)
+        ctx.save_for_backward(w, u, r, k, v, state_in, ckpt)
+        return o
+
+    @staticmethod
+    def backward(ctx, go):
+        w, u, r, k, v, state_in, ckpt = ctx.saved_tensors
+        dr, dk, dv, dw, du, ds = wkv6_backward(w, u, r, k, v, go.to(torch.bfloat16).contiguous(), state_in=state_in,
+                                               need_state_grad=state_in is not None and ctx.needs_input_grad[5],
+                                               ckpt=ckpt)
+        return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds

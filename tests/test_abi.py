@@ -274,8 +274,8 @@ def test_wkv5_backward_validation(lib):
     assert wkv5_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=small - 1, ck=x) == L.WKV_EWORKSPACE
 
 
-def wkv6(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None):
-    return lib.wkv6_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), None)
+def wkv6(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None, ck=None):
+    return lib.wkv6_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), P(ck), None)
 
 
 def test_wkv6_validation(lib):
@@ -289,4 +289,46 @@ def test_wkv6_validation(lib):
     assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, x + 4, x, x, x, x, x) == L.WKV_EALIGN  # w 16-byte aligned
     assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x + 2, x, x, x) == L.WKV_EALIGN
     assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, *args, so=x + 1) == L.WKV_EALIGN
+    assert wkv6(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ck=x + 8) == L.WKV_EALIGN
     assert wkv6(lib, 0, 4, 2, 64, L.WKV_BF16, *[None] * 6) == L.WKV_OK
+
+
+def test_wkv6_backward_sizes(lib):
+    # the RWKV-6 calls share the RWKV-5 layouts of the chunk-start states and partial sums
+    for args in ((2, 100, 3, 64), (1, 1, 1, 64), (1, 1, 1, 32), (2, 0, 3, 64)):
+        assert lib.wkv6_ckpt_bytes(*args) == lib.wkv5_ckpt_bytes(*args)
+        for have in (0, 1):
+            assert lib.wkv6_backward_workspace_bytes(*args, have) == lib.wkv5_backward_workspace_bytes(*args, have)
+
+
+def wkv6_bwd(lib, B, T, H, N, dt, w, u, r, k, v, go, dr, dk, dv, dw, du, si=None, dso=None, dsi=None, ck=None,
+             ws=None, nws=0):
+    return lib.wkv6_backward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(go), P(si), P(dso), P(dr), P(dk), P(dv),
+                             P(dw), P(du), P(dsi), P(ck), P(ws), nws, None)
+
+
+def test_wkv6_backward_validation(lib):
+    x = A16
+    args = [x] * 11
+    need = lib.wkv6_backward_workspace_bytes(1, 4, 2, 64, 0)
+    ok = dict(ws=x, nws=need)
+    assert wkv6_bwd(lib, 1, 4, 2, 32, L.WKV_BF16, *args, **ok) == L.WKV_EINVAL       # head size must be 64
+    assert wkv6_bwd(lib, 1, -4, 2, 64, L.WKV_BF16, *args, **ok) == L.WKV_EINVAL
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_F32, *args, **ok) == L.WKV_EDTYPE        # bf16 operands only
+    assert wkv6_bwd(lib, 1 << 30, 1 << 30, 1 << 10, 64, L.WKV_BF16, *args, **ok) == L.WKV_ESIZE
+    assert wkv6_bwd(lib, 1, 4, 0, 64, L.WKV_BF16, *[None] * 11) == L.WKV_OK          # no heads: nothing to do
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args[:10], None, **ok) == L.WKV_EINVAL    # du NULL
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args[:9], None, x, **ok) == L.WKV_EINVAL  # dw NULL
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args[:9], x + 2, x, **ok) == L.WKV_EALIGN
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x + 4, *args[1:], **ok) == L.WKV_EALIGN   # w 16-byte aligned
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, dso=x + 1, **ok) == L.WKV_EALIGN
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, dsi=x + 1, **ok) == L.WKV_EALIGN
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, None, *args[3:], **ok) == L.WKV_EINVAL  # r NULL
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x, x, x, None, *args[6:], **ok) == L.WKV_EINVAL  # go NULL
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, x, x, x, x, x, x + 2, *args[6:], **ok) == L.WKV_EALIGN  # go
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ck=x + 8, **ok) == L.WKV_EALIGN
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args) == L.WKV_EWORKSPACE
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=need - 1) == L.WKV_EWORKSPACE
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x + 16, nws=need) == L.WKV_EWORKSPACE
+    small = lib.wkv6_backward_workspace_bytes(1, 4, 2, 64, 1)
+    assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=small - 1, ck=x) == L.WKV_EWORKSPACE
