@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -532,46 +532,52 @@ def bench_wkv6(args):
     return out
 
 
-def bench_wkv5_train(args):
-    """RWKV-5 training step at B=8 T=1024 C=4096 (64 heads of 64): the forward
-    saving its chunk-start states, then the backward from them (dr, dk, dv,
-    dw, du).  Algorithmic bytes per channel-token: forward r, k, v in (6 B),
-    o out (4 B), states out (2 B); backward r, k, v, go in (8 B), states in
-    (2 B), dr, dk, dv out (12 B)."""
+def bench_matrix_train(args, gen):
+    """RWKV-5 (gen 5) or RWKV-6 (gen 6) training step at B=8 T=1024 C=4096 (64
+    heads of 64): the forward saving its chunk-start states, then the backward
+    from them (dr, dk, dv, dw, du).  Algorithmic bytes per channel-token:
+    forward r, k, v in (6 B), o out (4 B), states out (2 B); backward r, k, v,
+    go in (8 B), states in (2 B), dr, dk, dv out (12 B); RWKV-6 adds its
+    per-token rates w in (4 B) to both and dw out (4 B) to the backward."""
     import torch
 
     from rwkv_wkv_mixing_amd import ops, workloads as W
 
     dev = torch.device("cuda:0")
-    p = W.wkv5_config()
+    p = W.wkv5_config() if gen == 5 else W.wkv6_config()
     B, T, H = p.B, p.T, p.H
     up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
     w, u = torch.from_numpy(p.w).to(dev), torch.from_numpy(p.u).to(dev)
     go_bits, go_vals = W.wkv5_go(p, seed=1)
-    base = [up(p.r_bits), up(p.k_bits), up(p.v_bits), up(go_bits)]
+    base = [up(p.r_bits), up(p.k_bits), up(p.v_bits), up(go_bits)] + ([w] if gen == 6 else [])
     sets = [[t if i == 0 else t.clone() for t in base] for i in range(max(args.sets, 2))]
     C = 64 * H
     o = torch.empty((B, T, C), device=dev)
     ck = ops.new_wkv5_ckpt(B, T, H, dev)
     grads = [torch.empty((B, T, C), device=dev) for _ in range(3)]
-    dw, du = torch.empty((H, 64), device=dev), torch.empty((H, 64), device=dev)
+    dw = torch.empty((H, 64) if gen == 5 else (B, T, C), device=dev)
+    du = torch.empty((H, 64), device=dev)
     from rwkv_wkv_mixing_amd import _lib as L
     lib = L.lib()
-    nws = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64, 1))
+    f_fwd, f_bwd = (lib.wkv5_forward, lib.wkv5_backward) if gen == 5 else (lib.wkv6_forward, lib.wkv6_backward)
+    n_fwd, n_bwd = f"wkv{gen}_forward", f"wkv{gen}_backward"
+    nws = int((lib.wkv5_backward_workspace_bytes if gen == 5 else lib.wkv6_backward_workspace_bytes)(B, T, H, 64, 1))
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
     def fwd(i):
-        r, k, v, _ = sets[i % len(sets)]
-        L.check("wkv5_forward", lib.wkv5_forward(B, T, H, 64, L.WKV_BF16, ptr(w), ptr(u), ptr(r), ptr(k), ptr(v),
-                                                 ptr(o), None, None, ptr(ck), stream))
+        r, k, v, _, *rest = sets[i % len(sets)]
+        ww = rest[0] if rest else w
+        L.check(n_fwd, f_fwd(B, T, H, 64, L.WKV_BF16, ptr(ww), ptr(u), ptr(r), ptr(k), ptr(v), ptr(o), None, None,
+                             ptr(ck), stream))
 
     def bwd(i):
-        r, k, v, g = sets[i % len(sets)]
-        L.check("wkv5_backward", lib.wkv5_backward(B, T, H, 64, L.WKV_BF16, ptr(w), ptr(u), ptr(r), ptr(k), ptr(v),
-                                                   ptr(g), None, None, ptr(grads[0]), ptr(grads[1]), ptr(grads[2]),
-                                                   ptr(dw), ptr(du), None, ptr(ck), ptr(ws), nws, stream))
+        r, k, v, g, *rest = sets[i % len(sets)]
+        ww = rest[0] if rest else w
+        L.check(n_bwd, f_bwd(B, T, H, 64, L.WKV_BF16, ptr(ww), ptr(u), ptr(r), ptr(k), ptr(v), ptr(g), None, None,
+                             ptr(grads[0]), ptr(grads[1]), ptr(grads[2]), ptr(dw), ptr(du), None, ptr(ck), ptr(ws),
+                             nws, stream))
 
     for i in range(args.warmup):
         fwd(i)
@@ -595,27 +601,31 @@ def bench_wkv5_train(args):
     st_f = stats_us([a.elapsed_time(b) for a, b, _ in evs])
     st_b = stats_us([b.elapsed_time(c) for _, b, c in evs])
     n = B * T * C
-    alg_b = 22 * n
+    alg_b = (22 if gen == 5 else 30) * n
     achieved = alg_b / (st_b["mean"] * 1e-6) / 1e9
+    what = "RWKV-5 matrix-state WKV" if gen == 5 else "RWKV-6 matrix-state WKV (per-token decay)"
     out = {
-        "metric": "RWKV-5 matrix-state WKV forward+backward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
+        "metric": f"{what} forward+backward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
         "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": {"workload": p.name + " fwd+bwd", "B": B, "T": T, "H": H, "N": 64},
-        "call_us": {"wkv5_forward(ckpt)": st_f, "wkv5_backward(ckpt)": st_b},
-        "roofline": {"bound": "hbm", "kernel": "wkv5_backward (backward kernel + dw/du batch sum)",
+        "call_us": {f"{n_fwd}(ckpt)": st_f, f"{n_bwd}(ckpt)": st_b},
+        "roofline": {"bound": "hbm", "kernel": f"{n_bwd} (backward kernel + du{'/dw' if gen == 5 else ''} batch sum)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("wkv5train_bf16_B8_T1024_H64", "wkv5_bwd"),
+                     "traffic": recorded_traffic(f"wkv{gen}train_bf16_B8_T1024_H64", f"wkv{gen}_bwd"),
                      "alg_bytes_per_launch": alg_b},
     }
     if not args.no_cpu:
         # the float64 numpy oracle on batch rows 0 and 1 (all 64 heads, all tokens): forward, then backward
-        from oracle import wkv5_backward_ref, wkv5_forward_ref
+        import oracle
 
+        fw, bw = ((oracle.wkv5_forward_ref, oracle.wkv5_backward_ref) if gen == 5 else
+                  (oracle.wkv6_forward_ref, oracle.wkv6_backward_ref))
+        ws_ = p.w if gen == 5 else p.w[:2]
         t0 = time.perf_counter()
-        wkv5_forward_ref(p.w, p.u, p.r[:2], p.k[:2], p.v[:2], H)
-        wkv5_backward_ref(p.w, p.u, p.r[:2], p.k[:2], p.v[:2], go_vals[:2], H)
+        fw(ws_, p.u, p.r[:2], p.k[:2], p.v[:2], H)
+        bw(ws_, p.u, p.r[:2], p.k[:2], p.v[:2], go_vals[:2], H)
         t_np = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": 2 * T * C / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
                                "sample": f"batch rows 0-1 of the workload (all 64 heads x {T} tokens, {2 * T * C} "
@@ -660,9 +670,10 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6"):
+    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train"):
         out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
-               "wkv5train": bench_wkv5_train, "wkv6": bench_wkv6}[args.workload](args)
+               "wkv5train": lambda a: bench_matrix_train(a, 5), "wkv6": bench_wkv6,
+               "wkv6train": lambda a: bench_matrix_train(a, 6)}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

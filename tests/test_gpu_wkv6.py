@@ -194,3 +194,19 @@ def test_bench_shape_sampled():
         sub = W.Wkv5Problem(f"{p.name} head {h}", p.B, p.T, 1, p.w[:, :, sl], p.u[h:h + 1], p.r[:, :, sl],
                             p.k[:, :, sl], p.v[:, :, sl], None, None, None, None)
         check(sub, torch.from_numpy(o[:, :, sl]), torch.from_numpy(S[:, h:h + 1]), name=sub.name)
+
+
+@pytest.mark.parametrize("rates", [None, (6.0, 14.0)])
+def test_capped_rates_are_the_operator(rates):
+    """Rates above 10 act as 10: against the oracle run on min(w, 10) the
+    outputs stay within the rounding bound alone (no allowance for the cap)."""
+    p = W.make_wkv6(3, 129, 4, seed=47, with_state=True)
+    if rates is not None:
+        rng = np.random.default_rng(48)
+        p.w[:] = np.exp(rng.uniform(np.log(rates[0]), np.log(rates[1]), p.w.shape)).astype(np.float32)
+    assert (p.w > CAP).any()
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    pc = W.Wkv5Problem("capped", p.B, p.T, p.H, np.minimum(p.w, CAP), p.u, p.r, p.k, p.v, None, None, None, p.S0)
+    check(pc, o, S, name=f"capped {rates}")

@@ -262,3 +262,21 @@ def test_full_size_sampled_heads():
         part = [got[0][:, :, sl], got[1][:, :, sl], got[2][:, :, sl], got[3][:, :, sl], got[4][h:h + 1],
                 got[5][:, h:h + 1]]
         check(sub, go[:, :, sl], part, name=sub.name)
+
+
+@pytest.mark.parametrize("rates", [None, (6.0, 14.0)])
+def test_capped_rates_are_the_operator(rates):
+    """Rates above 10 act as 10: against the oracle run on min(w, 10) the
+    outputs stay within the rounding bound alone (no allowance for the cap),
+    on the default rate mix (a few rates above 10) and on rates around 10."""
+    p = W.make_wkv6(3, 129, 4, seed=43, with_state=True)
+    if rates is not None:
+        rng = np.random.default_rng(44)
+        p.w[:] = np.exp(rng.uniform(np.log(rates[0]), np.log(rates[1]), p.w.shape)).astype(np.float32)
+    assert (p.w > CAP).any()
+    go_bits, go = W.wkv5_go(p, seed=45)
+    dST = np.random.default_rng(46).standard_normal((3, 4, 64, 64)).astype(np.float32)
+    got = run(dev_inputs(p, go_bits, dST))
+    wc = np.minimum(p.w.astype(np.float64), CAP)
+    pc = W.Wkv5Problem("capped", p.B, p.T, p.H, wc, p.u, p.r, p.k, p.v, None, None, None, p.S0)
+    check(pc, go, got, dST, name=f"capped {rates}")
