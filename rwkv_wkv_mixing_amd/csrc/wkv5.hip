@@ -330,7 +330,8 @@ __device__ __forceinline__ void store_wb(float v, Rsrc r, uint32_t voff) {
 // ---- RWKV-6: the same operator with a per-token decay --------------------------------------
 // S_t = diag(e^{-w_t}) S_{t-1} + k_t^T v_t, o_t = r_t (S_{t-1} + diag(u) k_t^T v_t), w [B, T, C].
 // Inside a chunk every decay between two points is e^{-(E[a] - E[b])} with the chunk-local
-// cumulative rate E[t] = sum_{t' < t} w'_t' (t = 0..64) and w' = min(w, kWCap6); the factors are
+// cumulative rate E[t] = sum_{t' < t} w'_t' (t = 0..64) and w' = min(w, kWCap6).  The table holds
+// log2(e) E[t], so that each factor is one exp2 of a difference of two entries; the factors are
 // split exactly as for RWKV-5: about the later 16-token block's first token off the diagonal (both
 // factors <= 1) and about the block's middle on it (each factor at most e^{8 kWCap6}).  A rate
 // above kWCap6 acts as kWCap6 (the state then keeps at most e^{-10} of itself at that token
@@ -347,8 +348,8 @@ struct Wkv6Shared {
 // position of channel c in row t of the cumulative-rate table
 __device__ __forceinline__ int swE(int t, int c) { return (((c >> 2) ^ (t & 15)) << 2) | (c & 3); }
 
-__device__ __forceinline__ f4 exp_neg4(f4 x) {  // e^{-x}, elementwise
-    return f4{ex2(-x[0] * kL2E), ex2(-x[1] * kL2E), ex2(-x[2] * kL2E), ex2(-x[3] * kL2E)};
+__device__ __forceinline__ f4 exp2_neg4(f4 x) {  // 2^{-x}, elementwise: e^{-x} for base-2 table entries
+    return f4{ex2(-x[0]), ex2(-x[1]), ex2(-x[2]), ex2(-x[3])};
 }
 
 // kOut = false: a state-only pass (the chunk-start states into P.ckpt and the final state).
@@ -433,13 +434,13 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>(chunk_rows(ch));
         lds_sync();  // this chunk's r, k, v, raw rates and state are in LDS
-        {  // E[t + 1] = E[t] + min(w_t, cap) (rows past the chunk hold 0): wave wv takes channels
+        {  // E[t + 1] = E[t] + min(w_t, cap), in base-2 units (rows past the chunk hold 0): wave wv takes channels
            // 16 wv .. 16 wv + 15, lane (c, seg) the tokens 16 seg .. 16 seg + 15 of channel c; the
            // segments' totals are scanned across the four lanes of a channel
             const int c = 16 * wv + l16, t1 = 16 * g + 1;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6);
+            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6) * kL2E;
 #pragma unroll
             for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
             float off = 0.f;
@@ -474,7 +475,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
         for (int I = 0; I < 4 && kOut; ++I) {
             const int c4 = 16 * I + 4 * g;
-            const s4 a = mul_pack(row4(&R[tau][sw(tau, c4)]), exp_neg4(e4(tau, c4)));
+            const s4 a = mul_pack(row4(&R[tau][sw(tau, c4)]), exp2_neg4(e4(tau, c4)));
 #pragma unroll
             for (int J = 0; J < 4; ++J) O[J] = mfma(a, raw4(&sm.st[16 * J + l16][c4]), O[J]);
         }
@@ -491,7 +492,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
         for (int I = 0; I < 4 && kOut; ++I) {
             const int c4 = 16 * I + 4 * g;
-            rof[I] = mul_pack(row4(&R[tau][sw(tau, c4)]), exp_neg4(e4(tau, c4) - e4(P0, c4)));
+            rof[I] = mul_pack(row4(&R[tau][sw(tau, c4)]), exp2_neg4(e4(tau, c4) - e4(P0, c4)));
         }
 #pragma unroll
         for (int Q = 0; Q < 4 && kOut; ++Q) {
@@ -502,7 +503,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     const int c4 = 16 * I + 4 * g;
-                    const s4 ka = mul_pack(row4(&K[sig][sw(sig, c4)]), exp_neg4(e4(P0, c4) - e4(sig + 1, c4)));
+                    const s4 ka = mul_pack(row4(&K[sig][sw(sig, c4)]), exp2_neg4(e4(P0, c4) - e4(sig + 1, c4)));
                     At = mfma(ka, rof[I], At);
                 }
             } else {  // about mid = P0 + 8: e^{E[sig + 1] - E[mid]} and e^{-(E[tau] - E[mid])}; then the bonus
@@ -513,8 +514,8 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
                     const int c4 = 16 * I + 4 * g;
                     const f4 kr = row4(&K[sig][sw(sig, c4)]), rr = row4(&R[tau][sw(tau, c4)]);
                     const f4 em = e4(mid, c4);
-                    const s4 ka = mul_pack(kr, exp_neg4(em - e4(sig + 1, c4)));
-                    const s4 rb = mul_pack(rr, exp_neg4(e4(tau, c4) - em));
+                    const s4 ka = mul_pack(kr, exp2_neg4(em - e4(sig + 1, c4)));
+                    const s4 rb = mul_pack(rr, exp2_neg4(e4(tau, c4) - em));
                     At = mfma(ka, rb, At);
                     Bn = mfma(raw4(&K[sig][sw(sig, c4)]), mul_pack(rr, frow4(&sm.uu[c4])), Bn);
                 }
@@ -533,7 +534,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         //      S = diag(e^{-E[n]}) S + sum_sig (k_sig e^{-(E[n] - E[sig + 1])})^T v_sig
         float dn[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dn[e] = ex2(-e1(nv, 16 * wv + 4 * g + e) * kL2E);
+        for (int e = 0; e < 4; ++e) dn[e] = ex2(-e1(nv, 16 * wv + 4 * g + e));
         s4 aS[4];
         {
             const int key = 16 * wv + l16;  // m index of K^T
@@ -545,7 +546,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = 16 * Q + 4 * g + e;
-                    kk[e] = s < nv ? bf(kc[e]) * ex2(-(en - e1(s + 1, key)) * kL2E) : 0.f;
+                    kk[e] = s < nv ? bf(kc[e]) * ex2(e1(s + 1, key) - en) : 0.f;
                 }
                 aS[Q] = pack4(kk[0], kk[1], kk[2], kk[3]);
             }
@@ -1162,7 +1163,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
     };
     auto e4 = [&](int t, int c4) { return frow4(&sm.E[t][swE(t, c4)]); };  // E[t][c4 .. c4 + 3]
     auto e1 = [&](int t, int c) { return sm.E[t][swE(t, c)]; };
-    auto xe = [](float x) { return ex2(-x * kL2E); };  // e^{-x}
+    auto xe = [](float x) { return ex2(-x); };  // e^{-x} for x a difference of (base-2) table entries
     auto rot = [](float (&x)[4]) {
         const float t = x[0];
         x[0] = x[1];
@@ -1220,11 +1221,11 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
         }
         wait_staged();
         lds_sync();
-        {  // E[t + 1] = E[t] + min(w_t, cap), as in the forward
+        {  // E[t + 1] = E[t] + min(w_t, cap) in base-2 units, as in the forward
             const int c = P0 + l16, t1 = 16 * g + 1;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6);
+            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6) * kL2E;
 #pragma unroll
             for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
             float off = 0.f;
@@ -1268,7 +1269,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const int c4 = 16 * I + 4 * g;
-                aK[I] = nk >= 0 ? mul_pack(row4s(K, sig, c4), exp_neg4(e4(nv, c4) - e4(sig + 1, c4))) : s4{0, 0, 0, 0};
+                aK[I] = nk >= 0 ? mul_pack(row4s(K, sig, c4), exp2_neg4(e4(nv, c4) - e4(sig + 1, c4))) : s4{0, 0, 0, 0};
             }
             s4 aA[4];  // aA[Q], Q >= wv: [m = sig][k = s]: A[s = 16 Q + 4 g + e][sig]
 #pragma unroll
@@ -1283,8 +1284,8 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                     for (int I = 0; I < 4; ++I) {
                         const int c4 = 16 * I + 4 * g;
                         const f4 ep = e4(p0, c4);
-                        const s4 ra = mul_pack(row4s(R, s_m, c4), exp_neg4(e4(s_m, c4) - ep));
-                        const s4 kb = mul_pack(row4s(K, sig, c4), exp_neg4(ep - e4(sig + 1, c4)));
+                        const s4 ra = mul_pack(row4s(R, s_m, c4), exp2_neg4(e4(s_m, c4) - ep));
+                        const s4 kb = mul_pack(row4s(K, sig, c4), exp2_neg4(ep - e4(sig + 1, c4)));
                         At = mfma(ra, kb, At);
                     }
                 } else {
@@ -1293,7 +1294,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                     for (int I = 0; I < 4; ++I) {
                         const int c4 = 16 * I + 4 * g;
                         const f4 rr = row4s(R, s_m, c4), kk = row4s(K, sig, c4), em = e4(mid, c4);
-                        At = mfma(mul_pack(rr, exp_neg4(e4(s_m, c4) - em)), mul_pack(kk, exp_neg4(em - e4(sig + 1, c4))), At);
+                        At = mfma(mul_pack(rr, exp2_neg4(e4(s_m, c4) - em)), mul_pack(kk, exp2_neg4(em - e4(sig + 1, c4))), At);
                         Bn = mfma(mul_pack(rr, frow4(&sm.uu[c4])), pack4(kk[0], kk[1], kk[2], kk[3]), Bn);
                     }
 #pragma unroll
