@@ -660,8 +660,8 @@ def bench_copy(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1 (the operator "
-                          "shards by batch/channel with no exchange; see the design notes)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; use --gpus 1 (the operator "
+                          "shards by batch row or channel with no exchange between GPUs)"}))
         sys.exit(2)
     import torch
 

@@ -22,7 +22,7 @@ Sources (page title, then section):
 Only the elementwise mix is computed here; the projections W_r, W_k, W_v are
 ordinary matrix products outside this operator.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * before the first token the previous input is zero, unless the caller passes
   the last input of an earlier segment (the state tuple's x);

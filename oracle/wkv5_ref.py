@@ -23,7 +23,7 @@ Sources (page title, then section):
   (decay factor e^{-w}), the current token's bonus u, and the receptance that
   decides how much of the history a token receives.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * heads: C = H * N channels, head h owning channels h*N .. h*N + N - 1; the
   state of a head is an N x N matrix S (key index i, value index j);

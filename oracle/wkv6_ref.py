@@ -18,7 +18,7 @@ Sources (page title, then section):
 * the intelliparadigm.com post, section 3.1 (the table of versions): v6's change
   is a dynamic decay adjustment.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * the decay rate becomes a per-token input: w [B, T, C] >= 0, decay factor
   e^{-w_t} applied to the key rows of the state at token t; whatever produces it

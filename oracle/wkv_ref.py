@@ -24,7 +24,7 @@ Sources (page title, then section):
   first from the undecayed state, then decay-and-add) and the remark that real
   implementations carry a stability exponent p.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * initial state is empty: the history sum over i = 1..t-1 is empty at t = 1;
 * the stability-exponent update rule (not given on the pages) is the running

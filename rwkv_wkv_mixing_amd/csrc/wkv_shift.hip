@@ -29,8 +29,7 @@
 namespace wkv {
 namespace {
 
-// Launch shapes (measured on MI355X with operands cold in HBM; see the
-// design notes): the forward writes three times what it reads and prefers
+// Launch shapes (measured on MI355X with operands cold in HBM): the forward writes three times what it reads and prefers
 // wide blocks of short runs; the backward holds M + 1 inputs per token and
 // prefers 8-byte bf16 vectors (fewer registers, more waves) and long runs.
 #ifndef WKV_SHIFT_FWD_CV
