@@ -1075,12 +1075,14 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
 struct Wkv6BwdShared {
     union {
         uint16_t in[4][kLc][kN];    // r, k, v, go of the chunk, [token][swizzled channel]
-        float dwt[kLc][kPadF];      // the chunk's dw partials, [token][channel], after its last barrier
         float fin[kWaves5][4][kN];  // du partials [wave][k-group][channel], after the chunk walk
     };
     uint16_t gs[kN][kPadH];         // G1, bf16, [key][value]
     uint16_t ss[kN][kN];            // S0, bf16, [key][swizzled value]
-    float E[kLc + 1][kN];           // cumulative capped rates, float4 slot (i / 4) ^ (t & 15) of row t
+    union {
+        float E[kLc + 1][kN];       // cumulative capped rates, float4 slot (i / 4) ^ (t & 15) of row t
+        float dwt[kLc][kN];         // the chunk's dw partials, [token][channel], after its last barrier
+    };
     float uu[kN];
     float cd[kLc];                  // C[s][s] = go_s . v_s
     float cdg[kWaves5][16][16];     // each block's diagonal block of C, [s][sig], sig < s
@@ -1136,7 +1138,6 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
 
     if (threadIdx.x < kN) {
         sm.uu[threadIdx.x] = P.u[h * kN + threadIdx.x];
-        sm.E[0][threadIdx.x] = 0.f;  // row 0 is never staged over
     }
     // G: wave wv, tile J, lane (l16, g), element e holds G[16 wv + 4 g + e][16 J + l16]
     f4 G[4];
@@ -1179,12 +1180,11 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
         x[3] = t;
     };
 
-    for (int64_t ch = nch - 1; ch >= 0; --ch) {
-        asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
-        const int64_t t0 = ch * kLc;
+    // chunk c's r, k, v, go (swizzled rows) and its start state S0, by buffer -> LDS copies; wave wv
+    // copies rows 16 wv .. 16 wv + 15 of each
+    auto stage_inputs = [&](int64_t c) {
+        const int64_t t0 = c * kLc;
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
-        lds_sync();  // the previous chunk's dw assembly has left the input buffer and the tables
-        // ---- stage r, k, v, go (swizzled rows), S0, and the rates into E rows 1 + token ----------
         const uint16_t* src[4] = {P.r, P.k, P.v, P.go};
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -1199,7 +1199,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
             }
         }
         {
-            const Rsrc rs = make_rsrc(P.ckpt + (bh * nch + ch) * kN * kN, kN * kN * 2);
+            const Rsrc rs = make_rsrc(P.ckpt + (bh * nch + c) * kN * kN, kN * kN * 2);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int row = P0 + 8 * i + lane / 8;
@@ -1208,6 +1208,16 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                                                          16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, 0);
             }
         }
+    };
+
+    stage_inputs(nch - 1);
+    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
+        const int64_t t0 = ch * kLc;
+        const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
+        lds_sync();  // the previous chunk's dw assembly has left the rate table
+        // ---- the rates into E rows 1 + token (this chunk's r, k, v, go and S0 are already on the way)
+        if (threadIdx.x < kN) sm.E[0][threadIdx.x] = 0.f;  // the dw partials overwrote row 0
         {
             const Rsrc rs = make_rsrc(P.w + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 4));
 #pragma unroll
@@ -1542,6 +1552,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
             }
         }
         lds_sync();  // every wave is done with this chunk's G1, inputs, E and block totals are written
+        if (ch > 0) stage_inputs(ch - 1);  // the next chunk's inputs load during the dw assembly
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
