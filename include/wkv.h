@@ -26,6 +26,9 @@
  *  - Every call only enqueues work on `hip_stream` (a hipStream_t; NULL means
  *    the default stream) and returns without synchronising.  Errors from
  *    the kernels themselves surface at the caller's next synchronisation.
+ *    No call allocates, synchronises or enqueues a memset or copy node, so
+ *    the calls may be captured in a HIP graph and replayed (the scratch they
+ *    clear is cleared by kernels).
  *  - The library allocates no device memory and keeps no global state:
  *    scratch memory is the caller's `workspace`, sized by
  *    wkv_workspace_bytes().  Calls on disjoint buffers are thread-safe.
