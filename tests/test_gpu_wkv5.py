@@ -148,3 +148,16 @@ def test_bench_shape_sampled():
         q = W.Wkv5Problem(f"bench b={b} h={h}", 1, p.T, 1, p.w[h:h + 1], p.u[h:h + 1], p.r[b:b + 1, :, cs],
                           p.k[b:b + 1, :, cs], p.v[b:b + 1, :, cs], None, None, None)
         check(q, torch.from_numpy(o[b:b + 1, :, cs]), torch.from_numpy(S[b:b + 1, h:h + 1]))
+
+
+def test_long_sequence_slow_decay():
+    """4,096 tokens (64 chunks) with decay rates 1e-4 to 1e-2, so the state
+    carries most of its history through every chunk: float32 rounding of the
+    carried state accumulates most here."""
+    p = W.make_wkv5(1, 4096, 1, seed=31, with_state=True)
+    p.w[:] = np.exp(np.random.default_rng(32).uniform(np.log(1e-4), np.log(1e-2), p.w.shape)).astype(np.float32)
+    print(f"case {p.name} slow decay", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name="long slow decay")

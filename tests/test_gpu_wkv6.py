@@ -210,3 +210,15 @@ def test_capped_rates_are_the_operator(rates):
     torch.cuda.synchronize()
     pc = W.Wkv5Problem("capped", p.B, p.T, p.H, np.minimum(p.w, CAP), p.u, p.r, p.k, p.v, None, None, None, p.S0)
     check(pc, o, S, name=f"capped {rates}")
+
+
+def test_long_sequence_slow_decay():
+    """4,096 tokens (64 chunks) with per-token rates 1e-4 to 1e-2: the state
+    carries most of its history through every chunk."""
+    p = W.make_wkv6(1, 4096, 1, seed=33, with_state=True)
+    p.w[:] = np.exp(np.random.default_rng(34).uniform(np.log(1e-4), np.log(1e-2), p.w.shape)).astype(np.float32)
+    print(f"case {p.name} slow decay", flush=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name="long slow decay")
