@@ -59,6 +59,21 @@ def dev_inputs(p):
     return d
 
 
+
+NORM_TOL = 2.0 ** -6
+
+
+def check_norm(name, got, ref):
+    """Normwise accuracy on random inputs: ||got - ref|| <= 2^-6 ||ref||.  Not a rounding bound:
+    it checks that the errors do not add up coherently, which a magnitude-sum bound cannot see
+    where a signed sum cancels."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    nr, ne = float(np.linalg.norm(r)), float(np.linalg.norm(g - r))
+    print(f"  {name}: normwise relative error {ne / nr if nr else ne:.2e}", flush=True)
+    assert (ne == 0.0) if nr == 0.0 else (ne <= NORM_TOL * nr), (name, ne, nr)
+
+
 def check(p, o, S, S0=None, name=None):
     S0 = p.S0 if S0 is None else S0
     ref_o, ref_S = wkv5_forward_ref(p.w, p.u, p.r, p.k, p.v, p.H, S0)
@@ -66,8 +81,10 @@ def check(p, o, S, S0=None, name=None):
                                     None if S0 is None else np.abs(S0))
     name = name or p.name
     check_bound(f"{name} o", o.cpu().numpy(), ref_o, C_O * abs_o)
+    check_norm(f"{name} o", o.cpu().numpy(), ref_o)
     if S is not None:
         check_bound(f"{name} state", S.cpu().numpy(), ref_S, C_S * abs_S)
+        check_norm(f"{name} state", S.cpu().numpy(), ref_S)
 
 
 SHAPES = [(2, 1, 1), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]

@@ -97,13 +97,31 @@ def run(p, go_bits, dST=None, need_state_grad=True):
     return [None if x is None else x.cpu().numpy() for x in res]
 
 
+
+NORM_TOL = 2.0 ** -6
+
+
+def check_norm(name, got, ref):
+    """Normwise accuracy on random inputs: ||got - ref|| <= 2^-6 ||ref|| (exactly 0 where ref is).
+    Not a rounding bound: it checks that the errors do not add up coherently, which the
+    magnitude-sum bound cannot see where a signed sum cancels (a summed dw, a long sequence)."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    nr, ne = float(np.linalg.norm(r)), float(np.linalg.norm(g - r))
+    print(f"  {name}: normwise relative error {ne / nr if nr else ne:.2e}", flush=True)
+    assert (ne == 0.0) if nr == 0.0 else (ne <= NORM_TOL * nr), (name, ne, nr)
+
+
 def check(p, go, got, dST=None, name=None):
+    """Every output within its rounding bound, and within 2^-6 of the oracle in the norm (the
+    in-block rate cap of 8 moves only terms two or more tokens apart, far below that)."""
     name = name or p.name
     ref = wkv5_backward_ref(p.w, p.u, p.r, p.k, p.v, go, p.H, p.S0, dST)
     bnd = bounds(p.w.astype(np.float64), p.u, p.r, p.k, p.v, go, p.H, p.S0, dST)
     for i, n in enumerate(NAMES):
         if got[i] is not None:
             check_bound(f"{name} {n}", got[i], ref[i], bnd[i])
+            check_norm(f"{name} {n}", got[i], ref[i])
 
 
 SHAPES = [(2, 1, 1), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]
@@ -250,14 +268,6 @@ def test_long_sequence_slow_decay():
     go_bits, go = W.wkv5_go(p, seed=37)
     dST = np.random.default_rng(38).standard_normal((1, 1, 64, 64)).astype(np.float32)
     print(f"case {p.name} slow decay", flush=True)
-    got = run(p, go_bits, dST)
-    check(p, go, got, dST, name="long slow decay")
-    # Over 4,096 slowly decaying tokens the terms' summed magnitudes dwarf the signed results, so the
-    # bound above is loose; on these random inputs the rounding errors do not add up coherently, and
-    # every output also stays within 2^-6 of the oracle in the norm (an accuracy check on random
-    # inputs that catches a systematic error the magnitude bound would let through, not a bound).
-    ref = wkv5_backward_ref(np.asarray(p.w, np.float64), p.u, p.r, p.k, p.v, go, p.H, p.S0, dST)
-    for n, g, r in zip(NAMES, got, ref):
-        rel = float(np.linalg.norm(np.asarray(g, np.float64) - r) / np.linalg.norm(r))
-        print(f"  long slow decay {n}: normwise relative error {rel:.2e}", flush=True)
-        assert rel <= 2.0 ** -6, (n, rel)
+    # over 4,096 slowly decaying tokens the terms' summed magnitudes dwarf the signed results (dw
+    # most of all), so here the normwise check in check() is what holds the gradients to bf16 accuracy
+    check(p, go, run(p, go_bits, dST), dST, name="long slow decay")

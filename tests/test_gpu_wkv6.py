@@ -59,6 +59,21 @@ def emax(w):
     return float(wc.sum(axis=2).max(initial=0.0))
 
 
+
+NORM_TOL = 2.0 ** -6
+
+
+def check_norm(name, got, ref):
+    """Normwise accuracy on random inputs: ||got - ref|| <= 2^-6 ||ref||.  Not a rounding bound:
+    it checks that the errors do not add up coherently, which a magnitude-sum bound cannot see
+    where a signed sum cancels."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    nr, ne = float(np.linalg.norm(r)), float(np.linalg.norm(g - r))
+    print(f"  {name}: normwise relative error {ne / nr if nr else ne:.2e}", flush=True)
+    assert (ne == 0.0) if nr == 0.0 else (ne <= NORM_TOL * nr), (name, ne, nr)
+
+
 def check(p, o, S, name=None):
     name = name or p.name
     w = np.asarray(p.w, np.float64)
@@ -71,8 +86,12 @@ def check(p, o, S, name=None):
     c_o = 3 * UB * (1 + 2.0 ** -7) + 2.0 ** -12 + emax(w) * 2.0 ** -16
     c_s = UB * (1 + 2.0 ** -7) + 2.0 ** -12 + emax(w) * 2.0 ** -16
     check_bound(f"{name} o", o.cpu().numpy(), ref_o, c_o * cap_o + (cap_o - abs_o))
+    # normwise, against the operator the kernel computes (rates capped at 10)
+    refc_o, refc_S = (ref_o, ref_S) if np.array_equal(wc, w) else wkv6_forward_ref(wc, p.u, p.r, p.k, p.v, p.H, p.S0)
+    check_norm(f"{name} o", o.cpu().numpy(), refc_o)
     if S is not None:
         check_bound(f"{name} state", S.cpu().numpy(), ref_S, c_s * cap_S + (cap_S - abs_S))
+        check_norm(f"{name} state", S.cpu().numpy(), refc_S)
 
 
 def dev_inputs(p):
