@@ -1,13 +1,16 @@
-"""The RWKV-5/6 backward parity tests would catch plausible kernel mistakes
-(CPU).  Each mistake is planted in a copy of the backward recurrence written
+"""The RWKV-5/6 forward and backward parity tests would catch plausible kernel
+mistakes (CPU).  Each mistake is planted in a copy of the backward recurrence written
 here (never in the product path); the copy's outputs are held to exactly the
 criteria the GPU tests apply to the kernel: the per-element rounding bound and
 the normwise check.  Every planted mistake must fail at least one of them,
 and the unaltered copy must pass both."""
 import numpy as np
 import pytest
+import torch  # CPU tensors only: the GPU tests' forward check() reads its inputs back with .cpu()
 
+import test_gpu_wkv5 as F5
 import test_gpu_wkv5_bwd as G5
+import test_gpu_wkv6 as F6
 import test_gpu_wkv6_bwd as G6
 from oracle import wkv5_backward_ref, wkv6_backward_ref
 from rwkv_wkv_mixing_amd import workloads as W
@@ -118,3 +121,63 @@ def test_planted_mistake_is_caught(gen, kind):
     ratio, norm = caught(as_gen(gen, backward_copy(wt, p.u, p.r, p.k, p.v, go, p.H, p.S0, dST, kind)), ref, bnd)
     print(f"RWKV-{gen} {kind}: worst error / bound {ratio:.3g}, normwise {norm:.3g}", flush=True)
     assert ratio > 1.0 or norm > G6.NORM_TOL, (kind, ratio, norm)
+
+
+# ---- the forwards ---------------------------------------------------------------------------
+
+FWD_KINDS = ["no_bonus", "decay_before_read", "state_transposed", "bonus_without_u", "previous_rate"]
+
+
+def forward_copy(wt, u, r, k, v, H, S0, kind):
+    """The forward recurrence with per-token rates wt [B, T, C] and, unless kind
+    is None, one planted mistake.  Returns (o [B, T, C], S_T)."""
+    hd = lambda x: np.asarray(x, np.float64).reshape(x.shape[0], x.shape[1], H, -1)
+    wt, r, k, v = (hd(x) for x in (wt, r, k, v))
+    B, T, _, N = r.shape
+    u = np.asarray(u, np.float64).reshape(H, N)
+    d = np.exp(-wt)
+    S = np.zeros((B, H, N, N)) if S0 is None else np.array(S0, np.float64).reshape(B, H, N, N)
+    o = np.empty((B, T, H, N))
+    for t in range(T):
+        kv = k[:, t, :, :, None] * v[:, t, :, None, :]
+        dt = d[:, t - 1] if (kind == "previous_rate" and t > 0) else d[:, t]
+        if kind == "decay_before_read":
+            S = dt[..., None] * S
+        read = np.swapaxes(S, -1, -2) if kind == "state_transposed" else S
+        uu = np.ones_like(u) if kind == "bonus_without_u" else u
+        cur = 0.0 if kind == "no_bonus" else uu[None, :, :, None] * kv
+        o[:, t] = np.einsum("bhi,bhij->bhj", r[:, t], read + cur)
+        S = (S if kind == "decay_before_read" else dt[..., None] * S) + kv
+    return o.reshape(B, T, H * N), S
+
+
+def fwd_case(gen):
+    if gen == 5:
+        p = W.make_wkv5(2, 130, 1, seed=61, with_state=True)
+        wt = np.broadcast_to(p.w.reshape(1, 1, -1), (p.B, p.T, p.H * 64)).astype(np.float64)
+    else:
+        p = W.make_wkv6(2, 130, 1, seed=62, with_state=True)
+        p.w[:] = np.minimum(p.w, 10.0)
+        wt = p.w.astype(np.float64)
+    return p, wt
+
+
+def fwd_check(gen, p, o, S):
+    (F5 if gen == 5 else F6).check(p, torch.from_numpy(o), torch.from_numpy(S), name=f"RWKV-{gen} planted")
+
+
+@pytest.mark.parametrize("gen", [5, 6])
+def test_unaltered_forward_copy_passes(gen):
+    p, wt = fwd_case(gen)
+    fwd_check(gen, p, *forward_copy(wt, p.u, p.r, p.k, p.v, p.H, p.S0, None))
+
+
+FWD_CASES = [(g, k) for g in (5, 6) for k in FWD_KINDS if not (g == 5 and k == "previous_rate")]
+
+
+@pytest.mark.parametrize("gen,kind", FWD_CASES)
+def test_planted_forward_mistake_is_caught(gen, kind):
+    p, wt = fwd_case(gen)
+    o, S = forward_copy(wt, p.u, p.r, p.k, p.v, p.H, p.S0, kind)
+    with pytest.raises(AssertionError):
+        fwd_check(gen, p, o, S)
