@@ -341,7 +341,7 @@ constexpr float kWCap6 = 10.f;
 struct Wkv6Shared {
     uint16_t in[2][3][kLc][kN];  // staged r, k, v of a chunk, [token][swizzled channel], two chunks
     uint16_t st[kN][kPadH];      // state before the chunk, bf16, [value][key]
-    float E[kLc + 1][kN];        // E[t][i], float4 slot (i / 4) ^ (t & 15) of row t (raw w_{t-1} when staged)
+    float E[kLc + 1][kN];        // E[t][i], float4 slot (i / 4) ^ (t & 15) of row t
     float uu[kN];
 };
 
@@ -399,17 +399,15 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
             }
         }
     };
-    auto stage_w = [&](int64_t ch) {  // wave wv copies w of tokens 16 wv .. 16 wv + 15 into rows 1 + token
+    // the rates one lane scans, straight into registers a chunk ahead: lane (l16, g) of wave wv takes
+    // channel 16 wv + l16 over tokens 16 g .. 16 g + 15 (zeros past the sequence, by the range check)
+    auto load_w = [&](int64_t ch, float (&x)[16]) {
         const int64_t n = chunk_rows(ch);
         const Rsrc rs = make_rsrc(P.w + ((b * P.T + ch * kLc) * C + h * kN), static_cast<uint32_t>(((n - 1) * C + kN) * 4));
+        const uint32_t v0 = static_cast<uint32_t>((static_cast<int64_t>(16 * g) * C + 16 * wv + l16) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * wv + 4 * i + lane / 16;  // token; LDS row t + 1
-            const int q = (lane % 16) ^ ((t + 1) & 15);  // the global 16-byte chunk that lands in slot lane % 16
-            const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(t) * C) * 4 + q * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)&sm.E[16 * wv + 4 * i + 1][0], 16, voff, 0, 0, 0);
-        }
+        for (int i = 0; i < 16; ++i)
+            x[i] = BufLd<float>::at(rs, v0 + static_cast<uint32_t>(i * C * 4), 0);
     };
     auto put_state = [&]() {  // bf16, transposed: st[value][key]
 #pragma unroll
@@ -423,8 +421,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
     auto e4 = [&](int t, int c4) { return frow4(&sm.E[t][swE(t, c4)]); };  // E[t][c4 .. c4 + 3]
     auto e1 = [&](int t, int c) { return sm.E[t][swE(t, c)]; };
 
+    float wn[16];  // the rates of the chunk about to be scanned
     stage(0, 0);
-    stage_w(0);
+    load_w(0, wn);
     if constexpr (kOut) put_state();
     wait_staged();
 
@@ -433,14 +432,15 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         const int buf = static_cast<int>(ch & 1);
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>(chunk_rows(ch));
-        lds_sync();  // this chunk's r, k, v, raw rates and state are in LDS
-        {  // E[t + 1] = E[t] + min(w_t, cap), in base-2 units (rows past the chunk hold 0): wave wv takes channels
-           // 16 wv .. 16 wv + 15, lane (c, seg) the tokens 16 seg .. 16 seg + 15 of channel c; the
-           // segments' totals are scanned across the four lanes of a channel
+        lds_sync();  // this chunk's r, k, v and state are in LDS, and every wave is done with the last E
+        {  // E[t + 1] = E[t] + min(w_t, cap), in base-2 units (zero rates past the chunk): wave wv takes
+           // channels 16 wv .. 16 wv + 15, lane (c, seg) the tokens 16 seg .. 16 seg + 15 of channel c
+           // (its rates already in registers); the segments' totals are scanned across the four lanes
+           // of a channel
             const int c = 16 * wv + l16, t1 = 16 * g + 1;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = fminf(sm.E[t1 + i][swE(t1 + i, c)], kWCap6) * kL2E;
+            for (int i = 0; i < 16; ++i) x[i] = fminf(wn[i], kWCap6) * kL2E;
 #pragma unroll
             for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
             float off = 0.f;
@@ -452,6 +452,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sm.E[t1 + i][swE(t1 + i, c)] = x[i] + off;
         }
+        if (ch + 1 < nch) load_w(ch + 1, wn);  // a whole chunk to arrive
         lds_sync();  // E ready
         if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
         if (P.ckpt != nullptr) {  // the state before the chunk, bf16 [key][value], for the backward
@@ -552,7 +553,6 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
             }
         }
         lds_sync();  // every wave has read the state and E
-        if (ch + 1 < nch) stage_w(ch + 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
