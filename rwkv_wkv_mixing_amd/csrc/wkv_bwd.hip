@@ -313,19 +313,21 @@ __device__ __forceinline__ SpanGeo span_geo(const BwdChunk& P, int64_t b, int64_
     return g;
 }
 
-// The inputs k, v, gy of one time block staged in LDS: [wave][input][token][channel].
-template <typename TIn, int L, int W>
+// The inputs k, v, gy (and, NI = 4, the gate's r) of one time block staged in LDS:
+// [wave][input][token][channel].
+template <typename TIn, int L, int W, int NI = 3>
 struct BwdStage {
-    TIn x[W][3][L][64];
+    TIn x[W][NI][L][64];
 };
 
-// Start the asynchronous copies of wave `wave`'s span of k, v and gy into LDS.
-template <typename TIn, int L, int W>
-__device__ __forceinline__ void stage_span(BwdStage<TIn, L, W>& st, const SpanGeo& g, int wave, int lane, int64_t c0,
-                                           int64_t C) {
+// Start the asynchronous copies of wave `wave`'s span of k, v, gy (and r) into LDS.
+template <typename TIn, int L, int W, int NI>
+__device__ __forceinline__ void stage_span(BwdStage<TIn, L, W, NI>& st, const SpanGeo& g, int wave, int lane,
+                                           int64_t c0, int64_t C) {
     stage_rows<TIn, L>(g.rk, st.x[wave][0], int64_t{wave} * L, c0, C, lane);
     stage_rows<TIn, L>(g.rv, st.x[wave][1], int64_t{wave} * L, c0, C, lane);
     stage_rows<TIn, L>(g.rg, st.x[wave][2], int64_t{wave} * L, c0, C, lane);
+    if constexpr (NI == 4) stage_rows<TIn, L>(g.rr, st.x[wave][3], int64_t{wave} * L, c0, C, lane);
 }
 
 // A span's inputs, loaded ahead of use (gy holds the output gradient; with
@@ -350,8 +352,8 @@ struct SpanIn {
             s0 = g.ck[2 * C];
         }
     }
-    template <int W>
-    __device__ __forceinline__ void load_lds(const BwdStage<TIn, L, W>& st, int wave, int lane) {
+    template <int W, int NI>
+    __device__ __forceinline__ void load_lds(const BwdStage<TIn, L, W, NI>& st, int wave, int lane) {
         kv.load_lds(st.x[wave][0], st.x[wave][1], lane);
         gy.load_lds(st.x[wave][2], lane);
     }
@@ -663,16 +665,19 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
 // the last to the first, keeping the carry in LDS (no cross-workgroup
 // exchange).  Used when there are enough tiles to fill the GPU.
 //
-// Staged: while a block is computed, the next block's k, v, gy stream into
-// LDS by asynchronous buffer -> LDS copies (stage_span), and its saved state
+// Staged: while a block is computed, the next block's k, v, gy (and, gated with
+// bf16 inputs, r) stream into LDS by asynchronous buffer -> LDS copies
+// (stage_span), and its saved state
 // into three registers, so the loads overlap the arithmetic without holding
 // a second block in registers.  Each wave copies and reads only its own span,
 // so the waits are per wave: wait_staged() before reading a block from LDS,
 // and wait_lds_reads() after, before the next copy may overwrite it.
 template <typename TIn, int L, int W, bool Gated, bool Staged>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
+    // r joins the staged inputs when it is bf16 (as float32 it would cost the second workgroup per CU)
+    constexpr int kNI = (Gated && sizeof(TIn) == 2) ? 4 : 3;
     __shared__ BwdShared<W> sm;
-    __shared__ BwdStage<TIn, L, W> stage;  // referenced (and allocated) only when Staged
+    __shared__ BwdStage<TIn, L, W, kNI> stage;  // referenced (and allocated) only when Staged
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tile = blockIdx.x;
@@ -698,9 +703,11 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
     }
     for (int64_t blk = P.nblocks - 1; blk >= 0; --blk) {
         const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
+        Chunk1<TIn, L> rg;
         if constexpr (Staged) {
             wait_staged();
             cur.load_lds(stage, wave, lane);
+            if constexpr (kNI == 4) rg.load_lds(stage.x[wave][3], lane);
             cur.a0 = nxt.a0;
             cur.b0 = nxt.b0;
             cur.s0 = nxt.s0;
@@ -713,8 +720,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
         } else {
             cur.load(g, P.C);
         }
-        Chunk1<TIn, L> rg;
-        if (Gated) rg.load(g.rr, g.vin, g.row_in);
+        if constexpr (Gated && !(Staged && kNI == 4)) rg.load(g.rr, g.vin, g.row_in);
         Span<TIn, L, Gated> sp;
         sp.recompute(cur, rg, g, ch, eu, dec, fast_out);
         du += sp.du;
@@ -864,7 +870,7 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
         // the LDS-staged loads move 16-byte chunks: whole chunks per row, aligned
         const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
         const bool staged = WKV_BWD_STAGE && a.C % (16 / static_cast<int64_t>(sizeof(TIn))) == 0 && a16(a.k) &&
-                            a16(a.v) && a16(a.gy);
+                            a16(a.v) && a16(a.gy) && (P.r == nullptr || sizeof(TIn) != 2 || a16(P.r));
         const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * kBwdTileW);
         if (P.r != nullptr && staged)
             hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true, true>), grid, block, 0, stream, P);

@@ -65,6 +65,16 @@ def test_gated_whole_tile_backward():
     run_and_check(p, r, rb, with_ckpt=True)
 
 
+def test_gated_whole_tile_staged_ragged():
+    """The whole-tile backward with its inputs (r included, bf16) staged in LDS: C a whole number
+    of 16-byte rows, a ragged last time block, saved states reused."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    p = W.make_problem(2, 77, 64 * ncu, dtype="bf16", seed=63, spike_frac=0.01, name="gated tile staged bf16")
+    r, rb = W.receptance(p)
+    print(f"case {p.name}", flush=True)
+    run_and_check(p, r, rb, with_ckpt=True)
+
+
 def test_gated_config3_shape():
     p = W.config3()
     r, rb = W.receptance(p)
