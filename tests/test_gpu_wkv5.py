@@ -178,3 +178,25 @@ def test_long_sequence_slow_decay():
     o, S = ops().wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
     torch.cuda.synchronize()
     check(p, o, S, name="long slow decay")
+
+
+def test_decode_steps_in_place():
+    """Decoding: 40 single-token calls, each carrying the state in place (state_in = state_out),
+    equal the oracle over the 40 tokens.  One token takes the float32 one-token kernel: each term
+    of an output is exact up to float32 rounding of a 64-term sum and of the state carried over
+    the steps, so |o - ref| <= (64 + 2 T) 2^-24 o_abs, and the same for the state."""
+    p = W.make_wkv5(3, 40, 2, seed=71, with_state=True)
+    d = dev_inputs(p)
+    O = ops()
+    S = d["S0"].clone()
+    outs = []
+    for t in range(p.T):
+        sl = lambda x: x[:, t:t + 1].contiguous()
+        outs.append(O.wkv5_forward(d["w"], d["u"], sl(d["r"]), sl(d["k"]), sl(d["v"]), state_in=S, state_out=S))
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1).cpu().numpy()
+    ref_o, ref_S = wkv5_forward_ref(p.w, p.u, p.r, p.k, p.v, p.H, p.S0)
+    abs_o, abs_S = wkv5_forward_ref(p.w, np.abs(p.u), np.abs(p.r), np.abs(p.k), np.abs(p.v), p.H, np.abs(p.S0))
+    c = (64 + 2 * p.T) * 2.0 ** -24
+    check_bound("decode o", o, ref_o, c * abs_o)
+    check_bound("decode state", S.cpu().numpy(), ref_S, c * abs_S)

@@ -241,3 +241,51 @@ def test_long_sequence_slow_decay():
     o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
     torch.cuda.synchronize()
     check(p, o, S, name="long slow decay")
+
+
+def test_decode_steps_in_place():
+    """Decoding: 40 single-token calls, each carrying the state in place, equal the oracle over
+    the 40 tokens on the capped rates (the one-token kernel treats a rate above 10 as 10, as the
+    chunked one does); float32 throughout: |o - ref| <= (64 + 2 T) 2^-24 o_abs."""
+    p = W.make_wkv6(3, 40, 2, seed=73, with_state=True)
+    p.w[:, ::5] = 30.0  # a few tokens above the cap
+    d = dev_inputs(p)
+    O = ops()
+    S = d["S0"].clone()
+    outs = []
+    for t in range(p.T):
+        sl = lambda x: x[:, t:t + 1].contiguous()
+        outs.append(O.wkv6_forward(sl(d["w"]), d["u"], sl(d["r"]), sl(d["k"]), sl(d["v"]), state_in=S, state_out=S))
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1).cpu().numpy()
+    wc = np.minimum(p.w.astype(np.float64), CAP)
+    ref_o, ref_S = wkv6_forward_ref(wc, p.u, p.r, p.k, p.v, p.H, p.S0)
+    abs_o, abs_S = wkv6_forward_ref(wc, np.abs(p.u), np.abs(p.r), np.abs(p.k), np.abs(p.v), p.H, np.abs(p.S0))
+    c = (64 + 2 * p.T) * 2.0 ** -24
+    check_bound("decode o", o, ref_o, c * abs_o)
+    check_bound("decode state", S.cpu().numpy(), ref_S, c * abs_S)
+
+
+def test_decode_step_bench_shape_and_saved_state():
+    """One token for 256 streams x 64 heads (the decode bench's shape) with a saved state: the
+    saved state is the bf16 rounding of state_in, and two heads' outputs and states match the
+    oracle within the one-token bound."""
+    B, H = 256, 64
+    p = W.make_wkv6(B, 1, H, seed=75, with_state=True)
+    d = dev_inputs(p)
+    O = ops()
+    ck = O.new_wkv5_ckpt(B, 1, H, DEV)
+    o, S = O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True, ckpt=ck)
+    torch.cuda.synchronize()
+    saved = ck[: B * H * 64 * 64 * 2].view(torch.bfloat16).float().reshape(B, H, 64, 64)
+    assert torch.equal(saved, d["S0"].to(torch.bfloat16).float())
+    o, S = o.cpu().numpy(), S.cpu().numpy()
+    c = (64 + 2) * 2.0 ** -24
+    for h in (0, 37):
+        sl = slice(64 * h, 64 * h + 64)
+        wc = np.minimum(p.w[:, :, sl].astype(np.float64), CAP)
+        args = (p.u[h:h + 1], p.r[:, :, sl], p.k[:, :, sl], p.v[:, :, sl], 1, p.S0[:, h:h + 1])
+        ref_o, ref_S = wkv6_forward_ref(wc, *args)
+        abs_o, abs_S = wkv6_forward_ref(wc, *(np.abs(x) if isinstance(x, np.ndarray) else x for x in args))
+        check_bound(f"decode bench shape head {h} o", o[:, :, sl], ref_o, c * abs_o)
+        check_bound(f"decode bench shape head {h} state", S[:, h:h + 1], ref_S, c * abs_S)
