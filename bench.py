@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -311,6 +311,87 @@ def bench_step5(args):
         out["cpu_baseline"] = {"value": 10 * Bs * C / t_np, "unit": "lane·steps/s", "cores": 1, "kind": "oracle",
                                "sample": f"10 steps of layer 0 x 256 streams x 4096 channels ({10 * Bs * C} "
                                          f"lane-steps) through the float64 numpy step oracle, {t_np:.2f} s"}
+    return out
+
+
+def bench_wkv6_decode(args):
+    """RWKV-6 decoding: one token through 32 layers for 256 streams, 64 heads of 64 each (C=4096):
+    per layer one wkv6_forward call with T = 1 carrying that layer's float32 state in place (the
+    one-token kernel).  Rates w = exp(U(-4, 1.5) + 0.5 N(0, 1)) in float32, r, k, v ~ N(0, 1) in
+    bf16, drawn on the device from a seeded generator (two rotated sets per layer); the states
+    start at zero and are warmed up by the warmup steps.  Algorithmic bytes per call: the state
+    read and written (2 x 16 KB per stream and head), plus w (4 B), r, k, v (6 B) in and o (4 B)
+    out per channel."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops
+
+    dev = torch.device("cuda:0")
+    Ln, B, H = 32, 256, 64
+    C = 64 * H
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    base = torch.rand((Ln, 1, 1, C), generator=g, device=dev) * 5.5 - 4.0
+    u = [torch.randn((H, 64), generator=g, device=dev) for _ in range(Ln)]
+    sets = []
+    for _ in range(2):
+        w = torch.exp(base + 0.5 * torch.randn((Ln, B, 1, C), generator=g, device=dev))
+        rkv = [torch.randn((Ln, B, 1, C), generator=g, device=dev).to(torch.bfloat16) for _ in range(3)]
+        sets.append((w, *rkv))
+    S = [torch.zeros((B, H, 64, 64), device=dev) for _ in range(Ln)]
+    o = torch.empty((B, 1, C), device=dev)
+
+    def layer(i, l):
+        w, r, k, v = sets[i % 2]
+        ops.wkv6_forward(w[l], u[l], r[l], k[l], v[l], state_in=S[l], state_out=S[l], out=o)
+
+    def step(i):
+        for l in range(Ln):
+            layer(i, l)
+
+    for i in range(max(args.warmup, 2)):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        layer(i, i % Ln)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    st = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    alg = B * H * 64 * 64 * 4 * 2 + B * C * (4 + 6 + 4)
+    achieved = alg / (st["mean"] * 1e-6) / 1e9
+    n = Ln * B * C
+    out = {
+        "metric": "RWKV-6 matrix-state WKV decode channel-steps/s, 32 layers x 256 streams x 64 heads of 64",
+        "value": n / (wall / args.steps), "unit": "channel·steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": "wkv6 decode L=32 B=256 H=64 N=64 bf16 r,k,v"},
+        "call_us": {"wkv6_forward(T=1)": st},
+        "roofline": {"bound": "hbm", "kernel": "wkv6_forward (one-token kernel)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("wkv6decode_L32_B256_H64", "wkv6_step"),
+                     "alg_bytes_per_launch": alg},
+    }
+    if not args.no_cpu:
+        # the float64 numpy oracle on a bounded sample: one token of layer 0 for 64 of the streams
+        from oracle import wkv6_forward_ref
+
+        w, r, k, v = (x[0, :64].float().cpu().numpy() for x in sets[0])
+        S0 = S[0][:64].cpu().numpy()
+        t0 = time.perf_counter()
+        wkv6_forward_ref(np.minimum(w, 10.0), u[0].cpu().numpy(), r, k, v, H, S0)
+        t_np = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 64 * C / t_np, "unit": "channel·steps/s", "cores": 1, "kind": "oracle",
+                               "sample": f"one token of layer 0 for 64 streams x 64 heads ({64 * C} channel-steps) "
+                                         f"through the float64 numpy oracle, {t_np:.2f} s"}
     return out
 
 
@@ -670,10 +751,10 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train"):
+    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode"):
         out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
                "wkv5train": lambda a: bench_matrix_train(a, 5), "wkv6": bench_wkv6,
-               "wkv6train": lambda a: bench_matrix_train(a, 6)}[args.workload](args)
+               "wkv6train": lambda a: bench_matrix_train(a, 6), "wkv6decode": bench_wkv6_decode}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":
