@@ -219,10 +219,11 @@ wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
  * computed chunkwise (64 tokens per chunk) with bf16 matrix-core products and
  * float32 accumulation and state.  Channels decaying faster than e^{-10} per
  * token keep terms older than one token inside a 16-token block as if their
- * rate were 10 (an error below e^{-10} of the token's own term).  A single
- * token (T = 1: decoding, the state carried from call to call) is computed by
- * a one-token kernel in float32 when s_in, s_out, o and ckpt are 16-byte
- * aligned (NULL counts as aligned); it moves only the state and the token.
+ * rate were 10 (an error below e^{-10} of the token's own term).  Up to 16
+ * tokens (decoding with the state carried from call to call, short
+ * continuations) are computed token by token in float32 with the state held
+ * in registers, when s_in, s_out, o and ckpt are 16-byte aligned (NULL counts
+ * as aligned): the state makes one trip through memory.
  *
  * B, T, H   batch, tokens, heads (>= 0).  N  head size: must be 64.
  * in_dtype  WKV_BF16 only (WKV_EDTYPE otherwise).
@@ -256,7 +257,7 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
  * The rates come from whatever projection the model uses (the pages' low-rank
  * mix); this call takes them as an input.  Computed chunkwise like
  * wkv5_forward (bf16 matrix-core products, float32 accumulation and state),
- * from chunk-local cumulative rates in float32; a single token as in
+ * from chunk-local cumulative rates in float32; up to 16 tokens as in
  * wkv5_forward (float32, when aligned).  A rate above 10 acts as 10: a term's
  * decay across such a token is then at most e^{-10} instead of less.
  *

@@ -1656,9 +1656,10 @@ hipError_t launch_wkv6_bwd(const Wkv6BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// ---- one token (decoding): the state in, updated, out ------------------------------------------
-// For T = 1 the chunked kernels would run their 64-token machinery for one token; a step is bound by
-// reading and writing the 64 x 64 float32 state of each (batch row, head).  Per (batch row, head):
+// ---- a few tokens (decoding): the state in, updated token by token in registers, out ------------
+// For short T the chunked kernels would run their 64-token machinery for a handful of tokens; a
+// decode step is bound by reading and writing the 64 x 64 float32 state of each (batch row, head).
+// Per (batch row, head) and token, in order:
 //     o_j = sum_i r_i S_ij + (sum_i r_i u_i k_i) v_j,    S <- diag(e^{-w_i}) S + k^T v
 // in float32 (RWKV-5: w [H, 64]; RWKV-6: the token's rates [B, 1, C], a rate above kWCap6 acting as
 // kWCap6 as in the chunked kernel).  One wave per (batch row, head): lane (q, g) owns columns
@@ -1666,7 +1667,7 @@ hipError_t launch_wkv6_bwd(const Wkv6BwdArgs& a, hipStream_t stream) {
 // coalesced over four whole rows; a column's sum meets across its four lanes by shuffles in a fixed
 // order.  Needs the state, o and the saved state 16-byte aligned (else the chunked kernel runs).
 struct Wkv56StepArgs {
-    int64_t B, H;
+    int64_t B, T, H;
     const float* w;  // RWKV-5: [H, 64]; RWKV-6: [B, C]
     const float* u;
     const uint16_t* r;
@@ -1680,73 +1681,82 @@ struct Wkv56StepArgs {
 
 template <bool kPerToken>
 __global__ void __launch_bounds__(256) wkv56_step_kernel(Wkv56StepArgs P) {
-    __shared__ float tab[4][3][kN];  // per wave: r, k, decay factor of each key channel
+    __shared__ float tab[4][3][kN];  // per wave: r, k, decay factor of each key channel (one token)
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + wv;
     if (bh >= P.B * P.H) return;  // a whole wave; the kernel has no barrier
     const int64_t b = bh / P.H, h = bh - b * P.H;
     const int64_t C = P.H * kN;
-    const int64_t xi = b * C + h * kN;  // this (batch row, head) in the token's [B, C] rows
     const int q = lane & 15, g = lane >> 4;
-
-    const float rl = bf(P.r[xi + lane]), kl = bf(P.k[xi + lane]);
-    const float wl = kPerToken ? fminf(P.w[xi + lane], kWCap6) : P.w[h * kN + lane];
-    tab[wv][0][lane] = rl;
-    tab[wv][1][lane] = kl;
-    tab[wv][2][lane] = ex2(-wl * kL2E);
-    float bonus = rl * P.u[h * kN + lane] * kl;  // sum over the wave's 64 key channels, fixed order
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) bonus += __shfl_xor(bonus, m, 64);
-    const u16x4 vq = *reinterpret_cast<const u16x4*>(P.v + xi + 4 * q);
-    const float vj[4] = {bf(vq[0]), bf(vq[1]), bf(vq[2]), bf(vq[3])};
 
     // every row is loaded before anything is stored: the loads issue together although s_out, ckpt
     // and s_in may alias as far as the compiler knows (and s_out may be s_in)
-    const float* srow = P.s_in + bh * kN * kN + g * kN + 4 * q;  // row g, columns 4q ..
+    const int64_t e0 = bh * kN * kN + g * kN + 4 * q;  // element (row g, column 4q) of the state
     f4 x[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-        x[m] = P.s_in != nullptr ? *reinterpret_cast<const f4*>(srow + 4 * m * kN) : f4{0.f, 0.f, 0.f, 0.f};
-    const int64_t e0 = bh * kN * kN + g * kN + 4 * q;  // element (row g, column 4q) of the state
-    f4 op = {0.f, 0.f, 0.f, 0.f};
+        x[m] = P.s_in != nullptr ? *reinterpret_cast<const f4*>(P.s_in + e0 + 4 * m * kN) : f4{0.f, 0.f, 0.f, 0.f};
+    if (P.ckpt != nullptr) {  // the state before the (only) chunk
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int i = g + 4 * m;
-        const float ri = tab[wv][0][i], ki = tab[wv][1][i], di = tab[wv][2][i];
-        op += ri * x[m];
-        if (P.ckpt != nullptr)
+        for (int m = 0; m < 16; ++m)
             *reinterpret_cast<uint2*>(P.ckpt + e0 + 4 * m * kN) = uint2{pk2(x[m][0], x[m][1]), pk2(x[m][2], x[m][3])};
-        if (P.s_out != nullptr) {
-            f4 y;
+    }
+    const float ul = P.u[h * kN + lane];
+#pragma unroll 1
+    for (int64_t t = 0; t < P.T; ++t) {
+        const int64_t xi = (b * P.T + t) * C + h * kN;  // this token of this (batch row, head)
+        const float rl = bf(P.r[xi + lane]), kl = bf(P.k[xi + lane]);
+        const float wl = kPerToken ? fminf(P.w[xi + lane], kWCap6) : P.w[h * kN + lane];
+        tab[wv][0][lane] = rl;
+        tab[wv][1][lane] = kl;
+        tab[wv][2][lane] = ex2(-wl * kL2E);
+        float bonus = rl * ul * kl;  // sum over the wave's 64 key channels, fixed order
 #pragma unroll
-            for (int c = 0; c < 4; ++c) y[c] = fmaf(di, x[m][c], ki * vj[c]);
-            *reinterpret_cast<f4*>(P.s_out + e0 + 4 * m * kN) = y;
+        for (int m = 1; m < 64; m <<= 1) bonus += __shfl_xor(bonus, m, 64);
+        const u16x4 vq = *reinterpret_cast<const u16x4*>(P.v + xi + 4 * q);
+        const float vj[4] = {bf(vq[0]), bf(vq[1]), bf(vq[2]), bf(vq[3])};
+        f4 op = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int i = g + 4 * m;
+            const float ri = tab[wv][0][i], ki = tab[wv][1][i], di = tab[wv][2][i];
+            op += ri * x[m];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[m][c] = fmaf(di, x[m][c], ki * vj[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            op[c] += __shfl_xor(op[c], 16, 64);
+            op[c] += __shfl_xor(op[c], 32, 64);
+        }
+        if (P.o != nullptr && g == 0) {
+            f4 oo;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) oo[c] = fmaf(bonus, vj[c], op[c]);
+            *reinterpret_cast<f4*>(P.o + xi + 4 * q) = oo;
         }
     }
+    if (P.s_out != nullptr) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        op[c] += __shfl_xor(op[c], 16, 64);
-        op[c] += __shfl_xor(op[c], 32, 64);
-    }
-    if (P.o != nullptr && g == 0) {
-        f4 oo;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) oo[c] = fmaf(bonus, vj[c], op[c]);
-        *reinterpret_cast<f4*>(P.o + xi + 4 * q) = oo;
+        for (int m = 0; m < 16; ++m) *reinterpret_cast<f4*>(P.s_out + e0 + 4 * m * kN) = x[m];
     }
 }
 
-// whether one token may take the step kernel: its 16-byte accesses need aligned state, outputs
-// and saved state
+#ifndef WKV_STEP_MAX_T
+#define WKV_STEP_MAX_T 16
+#endif
+// whether a call may take the token-by-token kernel: few enough tokens that the state's one trip
+// through HBM outweighs the per-token arithmetic, and aligned state, outputs and saved state for
+// its 16-byte accesses
 bool step_ok(int64_t T, const void* o, const void* s_in, const void* s_out, const void* ckpt) {
     const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    return T == 1 && a16(o) && a16(s_in) && a16(s_out) && a16(ckpt);
+    return T >= 1 && T <= WKV_STEP_MAX_T && a16(o) && a16(s_in) && a16(s_out) && a16(ckpt);
 }
 
 template <bool kPerToken, class A>
 hipError_t launch_step(const A& a, hipStream_t stream) {
-    const Wkv56StepArgs s{a.B, a.H, a.w, a.u, a.r, a.k, a.v, a.o, a.s_in, a.s_out, a.ckpt};
+    const Wkv56StepArgs s{a.B, a.T, a.H, a.w, a.u, a.r, a.k, a.v, a.o, a.s_in, a.s_out, a.ckpt};
     hipLaunchKernelGGL(wkv56_step_kernel<kPerToken>, dim3(static_cast<unsigned>((a.B * a.H + 3) / 4)), dim3(256), 0,
                        stream, s);
     return hipGetLastError();

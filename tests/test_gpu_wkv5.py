@@ -200,3 +200,20 @@ def test_decode_steps_in_place():
     c = (64 + 2 * p.T) * 2.0 ** -24
     check_bound("decode o", o, ref_o, c * abs_o)
     check_bound("decode state", S.cpu().numpy(), ref_S, c * abs_S)
+
+
+@pytest.mark.parametrize("T", [2, 5, 16, 17])
+def test_few_tokens(T):
+    """Up to 16 tokens take the token-by-token kernel (float32: within (64 + 2T) 2^-24 of the
+    magnitudes); 17 takes the chunked one (its bound)."""
+    p = W.make_wkv5(3, T, 2, seed=80 + T, with_state=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv5_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name=f"T={T}")
+    if T <= 16:
+        ref_o, ref_S = wkv5_forward_ref(p.w, p.u, p.r, p.k, p.v, p.H, p.S0)
+        abs_o, abs_S = wkv5_forward_ref(p.w, np.abs(p.u), np.abs(p.r), np.abs(p.k), np.abs(p.v), p.H, np.abs(p.S0))
+        c = (64 + 2 * T) * 2.0 ** -24
+        check_bound(f"T={T} o (float32)", o.cpu().numpy(), ref_o, c * abs_o)
+        check_bound(f"T={T} state (float32)", S.cpu().numpy(), ref_S, c * abs_S)

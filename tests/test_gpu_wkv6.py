@@ -289,3 +289,22 @@ def test_decode_step_bench_shape_and_saved_state():
         abs_o, abs_S = wkv6_forward_ref(wc, *(np.abs(x) if isinstance(x, np.ndarray) else x for x in args))
         check_bound(f"decode bench shape head {h} o", o[:, :, sl], ref_o, c * abs_o)
         check_bound(f"decode bench shape head {h} state", S[:, h:h + 1], ref_S, c * abs_S)
+
+
+@pytest.mark.parametrize("T", [2, 5, 16, 17])
+def test_few_tokens(T):
+    """Up to 16 tokens take the token-by-token kernel (float32, rates capped at 10 as in the
+    chunked kernel: within (64 + 2T) 2^-24 of the magnitudes on the capped rates); 17 takes the
+    chunked one (its bound)."""
+    p = W.make_wkv6(3, T, 2, seed=90 + T, with_state=True)
+    d = dev_inputs(p)
+    o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], return_state=True)
+    torch.cuda.synchronize()
+    check(p, o, S, name=f"T={T}")
+    if T <= 16:
+        wc = np.minimum(p.w.astype(np.float64), CAP)
+        ref_o, ref_S = wkv6_forward_ref(wc, p.u, p.r, p.k, p.v, p.H, p.S0)
+        abs_o, abs_S = wkv6_forward_ref(wc, np.abs(p.u), np.abs(p.r), np.abs(p.k), np.abs(p.v), p.H, np.abs(p.S0))
+        c = (64 + 2 * T) * 2.0 ** -24
+        check_bound(f"T={T} o (float32)", o.cpu().numpy(), ref_o, c * abs_o)
+        check_bound(f"T={T} state (float32)", S.cpu().numpy(), ref_S, c * abs_S)

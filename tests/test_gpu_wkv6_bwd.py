@@ -142,7 +142,7 @@ def check(p, go, got, dST=None, name=None):
             check_norm(f"{name} {n}", got[i], refc[i])
 
 
-SHAPES = [(2, 1, 1), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]
+SHAPES = [(2, 1, 1), (2, 5, 2), (1, 63, 2), (2, 64, 1), (1, 65, 1), (2, 200, 3), (1, 1000, 2), (3, 129, 4)]
 
 
 @pytest.mark.parametrize("B,T,H", SHAPES)
