@@ -651,7 +651,7 @@ def bench_matrix_train(args, gen):
         r, k, v, _, *rest = sets[i % len(sets)]
         ww = rest[0] if rest else w
         L.check(n_fwd, f_fwd(B, T, H, 64, L.WKV_BF16, ptr(ww), ptr(u), ptr(r), ptr(k), ptr(v), ptr(o), None, None,
-                             ptr(ck), stream))
+                             ptr(ck), None, 0, stream))
 
     def bwd(i):
         r, k, v, g, *rest = sets[i % len(sets)]

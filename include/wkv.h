@@ -237,11 +237,23 @@ wkv_status_t wkv_backward_gated(int64_t B, int64_t T, int64_t C, int in_dtype,
  * ckpt      NULL, or wkv5_ckpt_bytes() bytes (16-byte aligned) that receive
  *           the state before every 64-token chunk, for a later wkv5_backward
  *           on the same inputs (2 bytes per channel and token written).
+ * workspace NULL (no time split), or wkv5_forward_workspace_bytes() bytes,
+ *           256-byte aligned (WKV_EWORKSPACE otherwise); clobbered.
  * Errors as the other entry points (WKV_EINVAL also for N != 64).
  */
 wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
                           const float* w, const float* u, const void* r, const void* k, const void* v,
-                          float* o, const float* s_in, float* s_out, void* ckpt, void* hip_stream);
+                          float* o, const float* s_in, float* s_out, void* ckpt, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of the optional scratch of wkv5_forward / wkv6_forward: nonzero only when
+ * there are fewer than 256 (batch row, head) pairs and at least 4 chunks, where
+ * the calls split each sequence into segments run in parallel (a state-only
+ * pass per segment, the segments' start states chained in float32, then the
+ * outputs of every segment from its start; r, k, v are read twice).  0 for
+ * invalid arguments or when no split would be made. */
+size_t wkv5_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
+size_t wkv6_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
 
 /*
  * wkv6_forward - the matrix-state WKV with a per-token (data-dependent) decay,
@@ -261,14 +273,15 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
  * wkv5_forward (float32, when aligned).  A rate above 10 acts as 10: a term's
  * decay across such a token is then at most e^{-10} instead of less.
  *
- * B, T, H, N, in_dtype, u, r, k, v, o, s_in, s_out, ckpt  as wkv5_forward
+ * B, T, H, N, in_dtype, u, r, k, v, o, s_in, s_out, ckpt, workspace  as wkv5_forward
  *           (ckpt: wkv5_ckpt_bytes() bytes, for a later wkv6_backward).
  * w         [B, T, 64 H] float32 rates, >= 0 and finite, 16-byte aligned.
  * Errors as wkv5_forward.
  */
 wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
                           const float* w, const float* u, const void* r, const void* k, const void* v,
-                          float* o, const float* s_in, float* s_out, void* ckpt, void* hip_stream);
+                          float* o, const float* s_in, float* s_out, void* ckpt, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
 
 /* Bytes of wkv5_forward's chunk-start states for (B, T, H, N): bf16
  * [B, H, ceil(T/64), 64, 64] (key-major), rounded up to 256.  Opaque to the

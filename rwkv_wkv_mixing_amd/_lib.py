@@ -28,6 +28,8 @@ EXPORTS = (
     "wkv_step",
     "wkv5_forward",
     "wkv6_forward",
+    "wkv5_forward_workspace_bytes",
+    "wkv6_forward_workspace_bytes",
     "wkv5_ckpt_bytes",
     "wkv5_backward_workspace_bytes",
     "wkv5_backward",
@@ -88,9 +90,13 @@ def declare(L):
     L.wkv_step.restype = i32
     L.wkv_step.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, vp]
     L.wkv5_forward.restype = i32
-    L.wkv5_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp]
+    L.wkv5_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv6_forward.restype = i32
-    L.wkv6_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp]
+    L.wkv6_forward.argtypes = [i64, i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, vp, vp, sz, vp]
+    L.wkv5_forward_workspace_bytes.restype = sz
+    L.wkv5_forward_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.wkv6_forward_workspace_bytes.restype = sz
+    L.wkv6_forward_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.wkv5_ckpt_bytes.restype = sz
     L.wkv5_ckpt_bytes.argtypes = [i64, i64, i64, i64]
     L.wkv5_backward_workspace_bytes.restype = sz

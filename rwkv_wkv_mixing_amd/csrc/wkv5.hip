@@ -122,7 +122,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, g = lane >> 4;  // MFMA lane coordinates: row/column l16, k-group g
-    const int64_t bh = blockIdx.x;
+    // time split (P.nseg > 1): this workgroup runs segment seg of (batch row, head) bh
+    const int64_t seg = blockIdx.x % P.nseg;
+    const int64_t bh = blockIdx.x / P.nseg;
     const int64_t b = bh / P.H, h = bh - b * P.H;
     const int64_t C = P.H * kN;
     const int64_t nch = (P.T + kLc - 1) / kLc;
@@ -140,7 +142,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
 
     // the state: wave wv, tile J, lane (l16, g), element e holds S[16 wv + 4 g + e][16 J + l16]
     f4 S[4];
-    const int64_t sbase = bh * kN * kN;
+    const int64_t ch_lo = P.nseg > 1 ? seg * P.cps : 0;
+    const int64_t ch_hi = P.nseg > 1 && ch_lo + P.cps < nch ? ch_lo + P.cps : nch;
+    const int64_t sbase = (bh * P.nseg + seg) * kN * kN;  // this segment's start and end state
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -178,7 +182,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
         }
     };
 
-    stage(0, 0);
+    stage(ch_lo, 0);
     if constexpr (kOut) put_state();
     wait_staged();
     const int P0 = 16 * wv;  // first token of this wave's output block, chunk-relative
@@ -186,12 +190,12 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     // Each wave confirms its copy of chunk ch + 1 (issued at the start of chunk
     // ch) just before storing chunk ch's outputs, so the barrier that opens a
     // chunk needs no memory wait and the stores drain during the next chunk.
-    for (int64_t ch = 0; ch < nch; ++ch) {
-        const int buf = static_cast<int>(ch & 1);
+    for (int64_t ch = ch_lo; ch < ch_hi; ++ch) {
+        const int buf = static_cast<int>((ch - ch_lo) & 1);
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
         lds_sync();  // this chunk's inputs, the tables and the state are in LDS for every wave
-        if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
+        if (ch + 1 < ch_hi) stage(ch + 1, buf ^ 1);
         if (P.ckpt != nullptr) {  // the state before the chunk, bf16 [key][value], for the backward
             uint16_t* cp = P.ckpt + (bh * nch + ch) * kN * kN;
 #pragma unroll
@@ -361,7 +365,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
     int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int l16 = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    // time split (P.nseg > 1): this workgroup runs segment seg of (batch row, head) bh
+    const int64_t seg = blockIdx.x % P.nseg;
+    const int64_t bh = blockIdx.x / P.nseg;
     const int64_t b = bh / P.H, h = bh - b * P.H;
     const int64_t C = P.H * kN;
     const int64_t nch = (P.T + kLc - 1) / kLc;
@@ -372,7 +378,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         sm.E[0][threadIdx.x] = 0.f;  // row 0 is never staged over
     }
     f4 S[4];  // S[J][e] = S[16 wv + 4 g + e][16 J + l16]
-    const int64_t sbase = bh * kN * kN;
+    const int64_t ch_lo = P.nseg > 1 ? seg * P.cps : 0;
+    const int64_t ch_hi = P.nseg > 1 && ch_lo + P.cps < nch ? ch_lo + P.cps : nch;
+    const int64_t sbase = (bh * P.nseg + seg) * kN * kN;  // this segment's start and end state
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -422,14 +430,15 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
     auto e1 = [&](int t, int c) { return sm.E[t][swE(t, c)]; };
 
     float wn[16];  // the rates of the chunk about to be scanned
-    stage(0, 0);
-    load_w(0, wn);
+    stage(ch_lo, 0);
+    load_w(ch_lo, wn);
     if constexpr (kOut) put_state();
     wait_staged();
 
-    for (int64_t ch = 0; ch < nch; ++ch) {
+    float rsum = 0.f;  // wave 0, lane = channel: the segment's summed capped rates (log2 e units)
+    for (int64_t ch = ch_lo; ch < ch_hi; ++ch) {
         asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
-        const int buf = static_cast<int>(ch & 1);
+        const int buf = static_cast<int>((ch - ch_lo) & 1);
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>(chunk_rows(ch));
         lds_sync();  // this chunk's r, k, v and state are in LDS, and every wave is done with the last E
@@ -452,9 +461,10 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sm.E[t1 + i][swE(t1 + i, c)] = x[i] + off;
         }
-        if (ch + 1 < nch) load_w(ch + 1, wn);  // a whole chunk to arrive
+        if (ch + 1 < ch_hi) load_w(ch + 1, wn);  // a whole chunk to arrive
         lds_sync();  // E ready
-        if (ch + 1 < nch) stage(ch + 1, buf ^ 1);
+        if (P.seg_rates != nullptr && wv == 0) rsum += sm.E[nv][swE(nv, lane)];
+        if (ch + 1 < ch_hi) stage(ch + 1, buf ^ 1);
         if (P.ckpt != nullptr) {  // the state before the chunk, bf16 [key][value], for the backward
             uint16_t* cp = P.ckpt + (bh * nch + ch) * kN * kN;
 #pragma unroll
@@ -576,6 +586,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
             }
     }
 
+    if (P.seg_rates != nullptr && wv == 0) P.seg_rates[(bh * P.nseg + seg) * kN + lane] = rsum;
     if (P.s_out != nullptr) {
 #pragma unroll
         for (int J = 0; J < 4; ++J)
@@ -1762,23 +1773,74 @@ hipError_t launch_step(const A& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- time split: the segments' start states ---------------------------------------------------
+// With few (batch row, head) pairs the forwards split each sequence into segments: a state-only
+// pass runs every segment from the zero state (its local end state L_s, and for RWKV-6 its summed
+// rates), this kernel chains them in order, start_0 = S0 and start_{s+1} = D_s start_s + L_s with
+// D_s the segment's total decay per key row (the recurrence is linear in the state), and the
+// output pass runs every segment from its start.  One thread per state element, float32.
+__global__ void wkv56_seg_chain_kernel(SegChainArgs P) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= P.BH * kN * kN) return;
+    const int64_t bh = idx / (kN * kN);
+    const int e = static_cast<int>(idx - bh * kN * kN), i = e / kN;  // key row i
+    const int64_t h = bh % P.H;
+    float S = P.s_in != nullptr ? P.s_in[idx] : 0.f;
+    for (int64_t s = 0; s < P.nseg; ++s) {
+        const int64_t q = (bh * P.nseg + s) * kN * kN + e;
+        P.start[q] = S;
+        float dl;  // the segment's decay exponent in log2 units
+        if (P.rates6 != nullptr) {
+            dl = P.rates6[(bh * P.nseg + s) * kN + i];
+        } else {
+            const int64_t t0 = s * P.cps * kLc;
+            const int64_t t1 = P.T < t0 + P.cps * kLc ? P.T : t0 + P.cps * kLc;
+            dl = P.w5[h * kN + i] * kL2E * static_cast<float>(t1 - t0);
+        }
+        S = fmaf(ex2(-dl), S, P.loc[q]);
+    }
+    if (P.s_out != nullptr) P.s_out[idx] = S;
+}
+
+hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t stream) {
+    const int64_t n = a.BH * kN * kN;
+    hipLaunchKernelGGL(wkv56_seg_chain_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Segments per sequence: only below one workgroup per CU (256 pairs), about 512 workgroups in
+// all, and at least two chunks per segment.
+int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps) {
+    const int64_t nch = (T + kLc - 1) / kLc;
+    *cps = nch;
+    if (BH <= 0 || BH >= 256 || nch < 4) return 1;
+    int64_t want = (512 + BH - 1) / BH;
+    if (want > nch / 2) want = nch / 2;
+    if (want < 2) return 1;
+    const int64_t c = (nch + want - 1) / want;
+    *cps = c;
+    return (nch + c - 1) / c;
+}
+
 hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream) {
-    if (step_ok(a.T, a.o, a.s_in, a.s_out, a.ckpt)) return launch_step<true>(a, stream);
+    if (a.nseg == 1 && step_ok(a.T, a.o, a.s_in, a.s_out, a.ckpt)) return launch_step<true>(a, stream);
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * a.nseg));
     if (a.o == nullptr) {
-        hipLaunchKernelGGL(wkv6_fwd_kernel<false>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+        hipLaunchKernelGGL(wkv6_fwd_kernel<false>, grid, dim3(64 * kWaves5), 0, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(wkv6_fwd_kernel<true>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    hipLaunchKernelGGL(wkv6_fwd_kernel<true>, grid, dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream) {
-    if (step_ok(a.T, a.o, a.s_in, a.s_out, a.ckpt)) return launch_step<false>(a, stream);
+    if (a.nseg == 1 && step_ok(a.T, a.o, a.s_in, a.s_out, a.ckpt)) return launch_step<false>(a, stream);
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * a.nseg));
     if (a.o == nullptr) {
-        hipLaunchKernelGGL(wkv5_fwd_kernel<false>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+        hipLaunchKernelGGL(wkv5_fwd_kernel<false>, grid, dim3(64 * kWaves5), 0, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(wkv5_fwd_kernel<true>, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    hipLaunchKernelGGL(wkv5_fwd_kernel<true>, grid, dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -279,9 +279,69 @@ size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N,
     return p.ws_bytes + (have_ckpt ? 0 : p.ckpt_bytes);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The time split of a matrix-state forward (few (batch row, head) pairs): a state-only pass over every
+// segment from the zero state, the chain of the segments' start states, then the outputs of every
+// segment from its start.  ws holds [BH, nseg, 64, 64] local end states, the same for the start
+// states, and (RWKV-6) [BH, nseg, 64] summed rates.
+template <class A, hipError_t (*Launch)(const A&, hipStream_t)>
+hipError_t run_split(const A& a, bool per_token, const float* w5, int64_t nseg, int64_t cps, void* ws,
+                     hipStream_t stream) {
+    const int64_t bh = a.B * a.H;
+    float* loc = static_cast<float*>(ws);
+    float* start = loc + bh * nseg * 64 * 64;
+    float* rates = start + bh * nseg * 64 * 64;
+    A p1 = a;  // state-only, from the zero state, each segment's end state into loc
+    p1.o = nullptr;
+    p1.s_in = nullptr;
+    p1.s_out = loc;
+    p1.ckpt = nullptr;
+    p1.nseg = nseg;
+    p1.cps = cps;
+    p1.seg_rates = per_token ? rates : nullptr;
+    hipError_t e = Launch(p1, stream);
+    if (e != hipSuccess) return e;
+    const wkv::SegChainArgs c{bh, a.H, a.T, nseg, cps, per_token ? nullptr : w5, per_token ? rates : nullptr,
+                              a.s_in, loc, start, a.s_out};
+    e = wkv::launch_seg_chain(c, stream);
+    if (e != hipSuccess) return e;
+    A p3 = a;  // the outputs (and saved states) of every segment from its start
+    p3.s_in = start;
+    p3.s_out = nullptr;
+    p3.nseg = nseg;
+    p3.cps = cps;
+    p3.seg_rates = nullptr;
+    return Launch(p3, stream);
+}
+
+size_t split_bytes(int64_t B, int64_t T, int64_t H, int64_t* nseg, int64_t* cps) {
+    *nseg = wkv::wkv56_segments(B * H, T, cps);
+    if (*nseg <= 1) return 0;
+    return static_cast<size_t>(B * H * *nseg) * (2 * 64 * 64 + 64) * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wkv5_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, WKV_BF16);
+    if (p.st != WKV_OK || p.bh == 0) return 0;
+    int64_t nseg, cps;
+    return split_bytes(B, T, H, &nseg, &cps);
+}
+
+size_t wkv6_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N) {
+    return wkv5_forward_workspace_bytes(B, T, H, N);
+}
+
 wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                           const float* u, const void* r, const void* k, const void* v, float* o,
-                          const float* s_in, float* s_out, void* ckpt, void* hip_stream) {
+                          const float* s_in, float* s_out, void* ckpt, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
     const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
     if (p.st != WKV_OK) return p.st;
     const int64_t ns = p.ns;
@@ -293,15 +353,21 @@ wkv_status_t wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     if (!aligned(w, 4) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) ||
         (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
+    int64_t nseg = 1, cps = 0;
+    const size_t need = split_bytes(B, T, H, &nseg, &cps);
+    if (workspace && (workspace_bytes < need || !aligned(workspace, 256))) return WKV_EWORKSPACE;
     wkv::Wkv5Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), o, s_in, s_out};
     a.ckpt = static_cast<uint16_t*>(ckpt);
+    if (workspace && nseg > 1)
+        return hip_status(run_split<wkv::Wkv5Args, wkv::launch_wkv5_fwd>(a, false, w, nseg, cps, workspace, stream));
     return hip_status(wkv::launch_wkv5_fwd(a, stream));
 }
 
 wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                           const float* u, const void* r, const void* k, const void* v, float* o,
-                          const float* s_in, float* s_out, void* ckpt, void* hip_stream) {
+                          const float* s_in, float* s_out, void* ckpt, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
     const Wkv5Plan p = wkv5_plan(B, T, H, N, in_dtype);
     if (p.st != WKV_OK) return p.st;
     if (p.bh == 0) return WKV_OK;
@@ -312,9 +378,14 @@ wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     if (!aligned(w, 16) || !aligned(u, 4) || !aligned(o, 4) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) ||
         (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
+    int64_t nseg = 1, cps = 0;
+    const size_t need = split_bytes(B, T, H, &nseg, &cps);
+    if (workspace && (workspace_bytes < need || !aligned(workspace, 256))) return WKV_EWORKSPACE;
     wkv::Wkv6Args a{B, T, H, w, u, static_cast<const uint16_t*>(r), static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), o, s_in, s_out};
     a.ckpt = static_cast<uint16_t*>(ckpt);
+    if (workspace && nseg > 1)
+        return hip_status(run_split<wkv::Wkv6Args, wkv::launch_wkv6_fwd>(a, true, nullptr, nseg, cps, workspace, stream));
     return hip_status(wkv::launch_wkv6_fwd(a, stream));
 }
 

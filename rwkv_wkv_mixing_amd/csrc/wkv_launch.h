@@ -96,7 +96,27 @@ struct Wkv5Args {
     const float* s_in;   // [B, H, 64, 64] or NULL (zero state)
     float* s_out;        // [B, H, 64, 64] or NULL
     uint16_t* ckpt = nullptr;  // [B, H, nchunks, 64, 64] bf16 [key][value]: the state before each chunk, or NULL
+    // time split: nseg > 1 runs segment s of (batch row, head) bh as workgroup bh * nseg + s over
+    // chunks [s cps, (s + 1) cps), with s_in / s_out then [B * H, nseg, 64, 64] (the segments' own
+    // start and end states); the saved states keep their global chunk index
+    int64_t nseg = 1, cps = 0;
+    float* seg_rates = nullptr;  // RWKV-6 only: [B * H, nseg, 64] each segment's summed capped rates (log2 e units)
 };
+
+// The segments' start states from their local end states (time split), and the final state.
+struct SegChainArgs {
+    int64_t BH, H, T, nseg, cps;
+    const float* w5;         // RWKV-5: [H, 64] rates, or NULL
+    const float* rates6;     // RWKV-6: [BH, nseg, 64] summed capped rates (log2 e units), or NULL
+    const float* s_in;       // [BH, 64, 64] or NULL (zero)
+    const float* loc;        // [BH, nseg, 64, 64] each segment's end state from the zero state
+    float* start;            // [BH, nseg, 64, 64] each segment's start state
+    float* s_out;            // [BH, 64, 64] or NULL
+};
+
+hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t stream);
+// segments for a time split of B * H (batch row, head) pairs over T tokens (1: no split)
+int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps);
 
 struct Wkv5BwdArgs {
     int64_t B, T, H;
@@ -148,6 +168,8 @@ struct Wkv6Args {
     const float* s_in;   // [B, H, 64, 64] or NULL (zero state)
     float* s_out;        // [B, H, 64, 64] or NULL
     uint16_t* ckpt = nullptr;  // as Wkv5Args::ckpt
+    int64_t nseg = 1, cps = 0;   // as Wkv5Args
+    float* seg_rates = nullptr;
 };
 
 hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream);

@@ -317,13 +317,15 @@ def new_wkv5_ckpt(B: int, T: int, H: int, device) -> torch.Tensor:
     return torch.empty(max(wkv5_ckpt_bytes(B, T, H), 1), dtype=torch.uint8, device=device)
 
 
-def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None):
+def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None, workspace=None, split=True):
     """RWKV-5 matrix-state WKV: o [B, T, C] float32 from w, u [H, 64] float32 and
     r, k, v [B, T, C] bfloat16 (C = 64 H).  state_in: [B, H, 64, 64] float32 or
     None (zero).  state_out: tensor to receive the final state (may be
     state_in); with return_state and no state_out one is allocated and the
     call returns (o, state).  ckpt: None or a new_wkv5_ckpt() buffer that
-    receives the chunk-start states for wkv5_backward."""
+    receives the chunk-start states for wkv5_backward.  With few (batch row, head) pairs
+    the call splits each sequence into segments run in parallel, in a workspace it allocates
+    (or is given); split=False keeps the whole sequence in one workgroup per pair."""
     _need(r, "r", torch.bfloat16)
     dev = r.device
     B, T, C = r.shape
@@ -347,8 +349,12 @@ def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
         _need(ckpt, "ckpt", torch.uint8, None, dev)
         if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
             raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
+    nws = int(L.lib().wkv5_forward_workspace_bytes(B, T, H, 64)) if split else 0
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     st = L.lib().wkv5_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
-                              _p(state_out), _p(ckpt), _stream(dev))
+                              _p(state_out), _p(ckpt), _p(workspace),
+                              0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
     L.check("wkv5_forward", st)
     return (out, state_out) if return_state else out
 
@@ -415,10 +421,10 @@ class Wkv5Function(torch.autograd.Function):
         return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds
 
 
-def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None):
+def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None, workspace=None, split=True):
     """RWKV-6 matrix-state WKV with per-token decay: o [B, T, C] float32 from
     w [B, T, C] float32 rates (>= 0), u [H, 64] float32 and r, k, v [B, T, C]
-    bfloat16 (C = 64 H); state handling and ckpt as wkv5_forward."""
+    bfloat16 (C = 64 H); state handling, ckpt, workspace and split as wkv5_forward."""
     _need(r, "r", torch.bfloat16)
     dev = r.device
     B, T, C = r.shape
@@ -442,8 +448,12 @@ def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
         _need(ckpt, "ckpt", torch.uint8, None, dev)
         if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
             raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
+    nws = int(L.lib().wkv6_forward_workspace_bytes(B, T, H, 64)) if split else 0
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     st = L.lib().wkv6_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
-                              _p(state_out), _p(ckpt), _stream(dev))
+                              _p(state_out), _p(ckpt), _p(workspace),
+                              0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
     L.check("wkv6_forward", st)
     return (out, state_out) if return_state else out
 

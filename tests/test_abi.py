@@ -211,7 +211,7 @@ def test_token_shift_validation(lib):
 
 
 def wkv5(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None, ck=None):
-    return lib.wkv5_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), P(ck), None)
+    return lib.wkv5_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), P(ck), None, 0, None)
 
 
 def test_wkv5_validation(lib):
@@ -275,7 +275,7 @@ def test_wkv5_backward_validation(lib):
 
 
 def wkv6(lib, B, T, H, N, dt, w, u, r, k, v, o, si=None, so=None, ck=None):
-    return lib.wkv6_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), P(ck), None)
+    return lib.wkv6_forward(B, T, H, N, dt, P(w), P(u), P(r), P(k), P(v), P(o), P(si), P(so), P(ck), None, 0, None)
 
 
 def test_wkv6_validation(lib):
@@ -332,3 +332,19 @@ def test_wkv6_backward_validation(lib):
     assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x + 16, nws=need) == L.WKV_EWORKSPACE
     small = lib.wkv6_backward_workspace_bytes(1, 4, 2, 64, 1)
     assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=small - 1, ck=x) == L.WKV_EWORKSPACE
+
+
+def test_matrix_forward_split_workspace(lib):
+    # a split only below 256 (batch row, head) pairs and from 4 chunks: local and start states
+    # (2 x 64 x 64 float32) and summed rates (64 float32) per pair and segment
+    assert lib.wkv5_forward_workspace_bytes(8, 1024, 64, 64) == 0       # 512 pairs: no split
+    assert lib.wkv5_forward_workspace_bytes(1, 192, 2, 64) == 0         # 3 chunks: no split
+    assert lib.wkv5_forward_workspace_bytes(1, 1000, 2, 64) == 2 * 8 * (2 * 64 * 64 + 64) * 4  # 8 segments of 2 chunks
+    assert lib.wkv5_forward_workspace_bytes(1, 1000, 2, 32) == 0
+    assert lib.wkv6_forward_workspace_bytes(1, 1000, 2, 64) == lib.wkv5_forward_workspace_bytes(1, 1000, 2, 64)
+    x = A16
+    need = lib.wkv5_forward_workspace_bytes(1, 1000, 2, 64)
+    for fn in (lib.wkv5_forward, lib.wkv6_forward):
+        args = [P(x)] * 6
+        assert fn(1, 1000, 2, 64, L.WKV_BF16, *args, None, None, None, P(x), need - 1, None) == L.WKV_EWORKSPACE
+        assert fn(1, 1000, 2, 64, L.WKV_BF16, *args, None, None, None, P(x + 16), need, None) == L.WKV_EWORKSPACE

@@ -308,3 +308,24 @@ def test_few_tokens(T):
         c = (64 + 2 * T) * 2.0 ** -24
         check_bound(f"T={T} o (float32)", o.cpu().numpy(), ref_o, c * abs_o)
         check_bound(f"T={T} state (float32)", S.cpu().numpy(), ref_S, c * abs_S)
+
+
+def test_time_split_long_sequence():
+    """Few (batch row, head) pairs: the sequence splits into segments run in parallel (here 8 of
+    2 chunks); outputs and final state within the bound, the state carried in place, and the
+    saved chunk-start states within one bf16 rounding of the unsplit run's."""
+    p = W.make_wkv6(1, 1000, 2, seed=101, with_state=True)
+    assert ops().L.lib().wkv6_forward_workspace_bytes(1, 1000, 2, 64) > 0
+    d = dev_inputs(p)
+    O = ops()
+    cks, outs = [], []
+    for split in (True, False):
+        S = d["S0"].clone()
+        ck = O.new_wkv5_ckpt(1, 1000, 2, DEV)
+        o = O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=S, state_out=S, ckpt=ck, split=split)
+        torch.cuda.synchronize()
+        check(p, o, S, name=f"split={split}")
+        n = 2 * 16 * 64 * 64
+        cks.append(ck[: 2 * n].view(torch.bfloat16).float())
+        outs.append(o)
+    assert torch.allclose(cks[0], cks[1], rtol=2.0 ** -7, atol=1e-30)

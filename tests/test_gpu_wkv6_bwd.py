@@ -165,7 +165,7 @@ def test_with_forward_ckpt_matches_recompute():
     d = dev_inputs(p, go_bits)
     O = ops()
     ck = O.new_wkv5_ckpt(2, 300, 2, DEV)
-    O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], ckpt=ck)
+    O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], ckpt=ck, split=False)
     a = run(d, ckpt=ck)
     b = run(d)
     for n, x, y in zip(NAMES, a, b):
@@ -315,3 +315,16 @@ def test_long_sequence_slow_decay():
     # the terms' summed magnitudes dwarf the signed results here, so the normwise check in check()
     # is what holds the gradients to bf16 accuracy
     check(p, go, run(dev_inputs(p, go_bits, dST)), dST, name="long slow decay")
+
+
+def test_backward_from_time_split_forward():
+    """One long sequence with two heads: the forward runs split into segments, and the backward
+    from the chunk-start states it saved stays within the bounds of the oracle."""
+    p = W.make_wkv6(1, 1000, 2, seed=103, with_state=True)
+    go_bits, go = W.wkv5_go(p, seed=104)
+    d = dev_inputs(p, go_bits)
+    O = ops()
+    assert O.L.lib().wkv6_forward_workspace_bytes(1, 1000, 2, 64) > 0
+    ck = O.new_wkv5_ckpt(1, 1000, 2, DEV)
+    O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], ckpt=ck)
+    check(p, go, run(d, ckpt=ck), name="from the split forward")
