@@ -139,12 +139,14 @@ def test_decode_step_graph_replays_equal_eager():
             assert torch.equal(x1, x2), f"step {t}: {n} differs from the eager step"
 
 
+@pytest.mark.parametrize("T", [150, 300])
 @pytest.mark.parametrize("gen", [5, 6])
-def test_matrix_state_graph_replays_equal_eager(gen):
+def test_matrix_state_graph_replays_equal_eager(gen, T):
     """RWKV-5 / RWKV-6: the forward saving its chunk-start states, then the
-    backward from them, with a given initial state and final-state gradient."""
+    backward from them, with a given initial state and final-state gradient
+    (at 300 tokens the forward splits the sequence into segments)."""
     O = ops()
-    B, T, H = 2, 150, 2
+    B, H = 2, 2
     mk = W.make_wkv5 if gen == 5 else W.make_wkv6
     probs = [mk(B, T, H, seed=90 + i, with_state=True) for i in range(3)]
     gos = [W.wkv5_go(q, seed=95 + i)[0] for i, q in enumerate(probs)]
@@ -175,9 +177,13 @@ def test_matrix_state_graph_replays_equal_eager(gen):
             dst.copy_(bf16_dev(src))
         g.replay()
         torch.cuda.synchronize()
-        got = [o.clone(), ST.clone()] + [x.clone() for x in res["g"]]
-        eo, eS = fwd(w, u, r, k, v, state_in=S0, return_state=True)
-        ref = [eo, eS] + list(bwd(w, u, r, k, v, go, state_in=S0, grad_state_out=dST, need_state_grad=True))
+        got = [o.clone(), ST.clone(), ck.clone()] + [x.clone() for x in res["g"]]
+        # the eager pair also goes through saved states: a backward without them
+        # recomputes the chunk-start states unsplit, which may round differently
+        eck = O.new_wkv5_ckpt(B, T, H, DEV)
+        eo, eS = fwd(w, u, r, k, v, state_in=S0, return_state=True, ckpt=eck)
+        ref = [eo, eS, eck] + list(bwd(w, u, r, k, v, go, state_in=S0, grad_state_out=dST, need_state_grad=True,
+                                       ckpt=eck))
         torch.cuda.synchronize()
-        for n, a, b in zip(("o", "S_T", "dr", "dk", "dv", "dw", "du", "dS0"), got, ref):
+        for n, a, b in zip(("o", "S_T", "ckpt", "dr", "dk", "dv", "dw", "du", "dS0"), got, ref):
             assert torch.equal(a, b), f"RWKV-{gen} replay {i}: {n} differs from the eager call"
