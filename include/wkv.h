@@ -289,10 +289,17 @@ wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
 size_t wkv5_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
 
 /* Bytes of scratch memory wkv5_backward needs: 2 x 64 float32 per (batch
- * row, head), plus wkv5_ckpt_bytes() when it is called without a ckpt
- * (have_ckpt == 0) and recomputes the chunk-start states itself.  0 for
- * invalid arguments or B*T == 0. */
-size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt);
+ * row, head), plus wkv5_ckpt_bytes() when it is called without a ckpt and
+ * recomputes the chunk-start states itself.  With fewer than 256 (batch row,
+ * head) pairs and at least 4 chunks the backward splits each sequence into
+ * segments run in parallel (the forward's time split, applied to the adjoint
+ * state), which needs per segment another 2 x 64 float32 per pair plus
+ * (2 x 64 x 64 + 64) float32 per pair.  flags: WKV_WS_HAVE_CKPT when a ckpt
+ * will be passed; WKV_WS_NO_SPLIT for the smaller size that runs unsplit.
+ * 0 for invalid arguments or B*T == 0. */
+#define WKV_WS_HAVE_CKPT 1
+#define WKV_WS_NO_SPLIT 2
+size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int flags);
 
 /*
  * wkv5_backward - gradients of wkv5_forward.
@@ -327,8 +334,11 @@ size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N,
  *           writing the same part of ds_in).
  * ckpt      the ckpt a wkv5_forward call on the same w, u, r, k, v and s_in
  *           wrote, or NULL (then s_in is read to recompute it).
- * workspace wkv5_backward_workspace_bytes(..., ckpt != NULL) bytes, 256-byte
- *           aligned; clobbered.  Not needed when B*T == 0.
+ * workspace wkv5_backward_workspace_bytes(..., flags) bytes, 256-byte
+ *           aligned; clobbered.  Not needed when B*T == 0.  At least the
+ *           size without WKV_WS_NO_SPLIT: the time split (when the shape
+ *           asks for one); else at least the WKV_WS_NO_SPLIT size: unsplit.
+ *           The two orders of summation agree to rounding, not bitwise.
  * Errors as the other entry points (WKV_EINVAL also for N != 64; nothing
  * is written on an error).
  */
@@ -342,7 +352,7 @@ wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
  * wkv5_backward_workspace_bytes() (the backward's scratch is only the du
  * partials and, without a ckpt, the recomputed chunk-start states). */
 size_t wkv6_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
-size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt);
+size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int flags);
 
 /*
  * wkv6_backward - gradients of wkv6_forward.
@@ -362,7 +372,8 @@ size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N,
  *
  * B, T, H, N, in_dtype, w, u, r, k, v, s_in  as wkv6_forward.
  * go, ds_out, dr, dk, dv, du, ds_in, workspace  as wkv5_backward
- *           (workspace: wkv6_backward_workspace_bytes(..., ckpt != NULL)).
+ *           (workspace: wkv6_backward_workspace_bytes(..., flags), time split
+ *           as there).
  * dw        [B, T, 64 H] float32, fully overwritten.
  * ckpt      the ckpt a wkv6_forward call on the same w, u, r, k, v and s_in
  *           wrote, or NULL (then s_in is read to recompute it).

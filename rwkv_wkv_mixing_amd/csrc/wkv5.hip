@@ -650,11 +650,16 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
     int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int l16 = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    const int64_t seg = blockIdx.x % P.nseg, bh = blockIdx.x / P.nseg;
     const int64_t b = bh / P.H, h = bh - b * P.H;
     const int64_t C = P.H * kN;
     const int64_t nch = (P.T + kLc - 1) / kLc;
     const int P0 = 16 * wv;
+    // time split: this workgroup walks chunks ch_lo .. ch_hi - 1 of its segment from the adjoint after it
+    const int64_t ch_lo = P.nseg > 1 ? seg * P.cps : 0;
+    const int64_t ch_hi = P.nseg > 1 && ch_lo + P.cps < nch ? ch_lo + P.cps : nch;
+    const float* g_end = P.nseg > 1 ? P.gstart + (bh * P.nseg + seg) * kN * kN
+                                    : (P.ds_out != nullptr ? P.ds_out + bh * kN * kN : nullptr);
 
     for (int q = threadIdx.x; q < (kLc + 1) * kN; q += 64 * kWaves5) {
         const int n = q / kN, i = q % kN;
@@ -674,7 +679,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int key = P0 + 4 * g + e, j = 16 * J + l16;
-            G[J][e] = P.ds_out != nullptr ? P.ds_out[bh * kN * kN + key * kN + j] : 0.f;
+            G[J][e] = g_end != nullptr ? g_end[key * kN + j] : 0.f;
             sm.gs[key][j] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
         }
     float dwv[4] = {0.f, 0.f, 0.f, 0.f}, duv[4] = {0.f, 0.f, 0.f, 0.f};  // channel 16 I + l16
@@ -705,7 +710,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
         return f4{bf(x[0]), bf(x[1]), bf(x[2]), bf(x[3])};
     };
 
-    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+    for (int64_t ch = ch_hi - 1; ch >= ch_lo; --ch) {
         asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
@@ -1036,7 +1041,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 sm.gs[P0 + 4 * g + e][16 * J + l16] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
     }
 
-    if (P.ds_in != nullptr) {
+    if (P.ds_in != nullptr && seg == 0) {
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -1063,8 +1068,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
             sw_ += sm.fin.dd[ww][i];
         }
         for (int c = 0; c < 16; ++c) sw_ += sm.fin.dwa[i][c];
-        P.part[(bh * 2 + 0) * kN + i] = sw_;
-        P.part[(bh * 2 + 1) * kN + i] = su;
+        const int64_t row = seg * P.B * P.H + bh;
+        P.part[(row * 2 + 0) * kN + i] = sw_;
+        P.part[(row * 2 + 1) * kN + i] = su;
     }
 }
 
@@ -1141,11 +1147,16 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
     int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int l16 = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    const int64_t seg = blockIdx.x % P.nseg, bh = blockIdx.x / P.nseg;
     const int64_t b = bh / P.H, h = bh - b * P.H;
     const int64_t C = P.H * kN;
     const int64_t nch = (P.T + kLc - 1) / kLc;
     const int P0 = 16 * wv;
+    // time split: this workgroup walks chunks ch_lo .. ch_hi - 1 of its segment from the adjoint after it
+    const int64_t ch_lo = P.nseg > 1 ? seg * P.cps : 0;
+    const int64_t ch_hi = P.nseg > 1 && ch_lo + P.cps < nch ? ch_lo + P.cps : nch;
+    const float* g_end = P.nseg > 1 ? P.gstart + (bh * P.nseg + seg) * kN * kN
+                                    : (P.ds_out != nullptr ? P.ds_out + bh * kN * kN : nullptr);
 
     if (threadIdx.x < kN) {
         sm.uu[threadIdx.x] = P.u[h * kN + threadIdx.x];
@@ -1157,7 +1168,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int key = P0 + 4 * g + e, j = 16 * J + l16;
-            G[J][e] = P.ds_out != nullptr ? P.ds_out[bh * kN * kN + key * kN + j] : 0.f;
+            G[J][e] = g_end != nullptr ? g_end[key * kN + j] : 0.f;
             sm.gs[key][j] = static_cast<uint16_t>(pk2(G[J][e], 0.f) & 0xffffu);
         }
     float duv[4] = {0.f, 0.f, 0.f, 0.f};  // channel 16 I + l16
@@ -1221,8 +1232,8 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
         }
     };
 
-    stage_inputs(nch - 1);
-    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+    stage_inputs(ch_hi - 1);
+    for (int64_t ch = ch_hi - 1; ch >= ch_lo; --ch) {
         asm volatile("" : "+v"(lane), "+v"(l16), "+v"(g));
         const int64_t t0 = ch * kLc;
         const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
@@ -1563,7 +1574,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
             }
         }
         lds_sync();  // every wave is done with this chunk's G1, inputs, E and block totals are written
-        if (ch > 0) stage_inputs(ch - 1);  // the next chunk's inputs load during the dw assembly
+        if (ch > ch_lo) stage_inputs(ch - 1);  // the next chunk's inputs load during the dw assembly
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -1589,7 +1600,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
         }
     }
 
-    if (P.ds_in != nullptr) {
+    if (P.ds_in != nullptr && seg == 0) {
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -1605,7 +1616,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
         float su = 0.f;
         for (int ww = 0; ww < kWaves5; ++ww)
             for (int gg = 0; gg < 4; ++gg) su += sm.fin[ww][gg][i];
-        P.part[bh * kN + i] = su;
+        P.part[(seg * P.B * P.H + bh) * kN + i] = su;
     }
 }
 
@@ -1648,22 +1659,22 @@ hipError_t launch_wkv5_state_copy(const float* s_in, float* s_out, int64_t n, hi
 }
 
 hipError_t launch_wkv5_bwd(const Wkv5BwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(wkv5_bwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    hipLaunchKernelGGL(wkv5_bwd_kernel, dim3(static_cast<unsigned>(a.B * a.H * a.nseg)), dim3(64 * kWaves5), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = a.H * kN;
     hipLaunchKernelGGL(wkv5_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a.part,
-                       a.B, a.H, a.dw, a.du);
+                       a.B * a.nseg, a.H, a.dw, a.du);  // (segment, batch row) partials
     return hipGetLastError();
 }
 
 hipError_t launch_wkv6_bwd(const Wkv6BwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(wkv6_bwd_kernel, dim3(static_cast<unsigned>(a.B * a.H)), dim3(64 * kWaves5), 0, stream, a);
+    hipLaunchKernelGGL(wkv6_bwd_kernel, dim3(static_cast<unsigned>(a.B * a.H * a.nseg)), dim3(64 * kWaves5), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = a.H * kN;
     hipLaunchKernelGGL(wkv6_du_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                       a.part, a.B, a.H, a.du);
+                       a.part, a.B * a.nseg, a.H, a.du);
     return hipGetLastError();
 }
 
@@ -1773,12 +1784,126 @@ hipError_t launch_step(const A& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- time split of the backwards: each segment's adjoint from a zero adjoint after it ------------
+// The adjoint recurrence G_{t-1} = diag(d_t) G_t + r_t^T go_t is linear in G: over a segment the
+// adjoint before it is D G_after + L, D the segment's total decay per key row and L what the segment
+// alone gives from G_after = 0.  This kernel forms L per (batch row, head, segment), walking the
+// segment's chunks last to first with the backwards' own chunk update
+//     G0 = diag(e^{-E[n]}) G1 + sum_s (r_s . e^{-E[s]})^T go_s
+// (E[s] the rates of the chunk's tokens before s: RWKV-5 w s; RWKV-6 summed, each capped at kWCap6
+// as the forward caps it) on bf16 matrix-core products with float32 accumulation; for RWKV-6 it
+// also writes the segment's summed rates (log2 e units) for the chain.  One 4-wave workgroup per
+// (batch row, head, segment); wave w owns key rows 16 w .. 16 w + 15 of L, as in the backwards.
+struct AdjLocalShared {
+    uint16_t in[2][kLc][kN];   // r, go of the chunk, [token][swizzled channel]
+    float f[kLc + 1][kPadF];   // e^{-E[t]}, t = 0 .. 64, per channel
+    float blk[kWaves5][kN];    // RWKV-6: each wave's 16-token rate sums
+};
+
+template <bool kPerToken>
+__global__ void __launch_bounds__(64 * kWaves5) wkv56_adj_local_kernel(AdjLocalArgs P) {
+    __shared__ AdjLocalShared sm;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t seg = blockIdx.x % P.nseg, bh = blockIdx.x / P.nseg;
+    const int64_t b = bh / P.H, h = bh - b * P.H;
+    const int64_t C = P.H * kN;
+    const int64_t nch = (P.T + kLc - 1) / kLc;
+    const int64_t ch_lo = seg * P.cps;
+    const int64_t ch_hi = ch_lo + P.cps < nch ? ch_lo + P.cps : nch;
+    const int P0 = 16 * wv;
+    f4 G[4];  // G[J][e] = L[P0 + 4 g + e][16 J + l16]
+#pragma unroll
+    for (int J = 0; J < 4; ++J) G[J] = f4{0.f, 0.f, 0.f, 0.f};
+    float rsum = 0.f;  // RWKV-6, last wave: channel lane's summed capped rates over the segment
+
+    for (int64_t ch = ch_hi - 1; ch >= ch_lo; --ch) {
+        const int64_t t0 = ch * kLc;
+        const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
+        lds_sync();  // every wave is done with the previous chunk's inputs and table
+        const uint16_t* src[2] = {P.r, P.go};
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {  // rows past the sequence's end read as zero (buffer range)
+            const Rsrc rs = make_rsrc(src[a] + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 2));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = P0 + 8 * i + lane / 8;
+                const int q = (lane % 8) ^ (row & 7);
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+            }
+        }
+        if (kPerToken) {  // wave w: tokens P0 .. P0 + 15 of channel lane, prefix-summed, then offset
+            const float* wr = P.w + (b * P.T + t0 + P0) * C + h * kN + lane;
+            float x[16];
+#pragma unroll
+            for (int a = 0; a < 16; ++a) x[a] = P0 + a < nv ? fminf(wr[a * C], kWCap6) * kL2E : 0.f;
+#pragma unroll
+            for (int a = 1; a < 16; ++a) x[a] += x[a - 1];
+            sm.blk[wv][lane] = x[15];
+            lds_sync();
+            float off = 0.f;
+            for (int A = 0; A < wv; ++A) off += sm.blk[A][lane];
+#pragma unroll
+            for (int a = 0; a < 16; ++a) sm.f[P0 + a + 1][lane] = ex2(-(x[a] + off));
+            if (wv == kWaves5 - 1) rsum += x[15] + off;  // the chunk's total (tokens past nv add 0)
+        } else {
+            const float wl = P.w[h * kN + lane] * kL2E;
+#pragma unroll
+            for (int a = 0; a < 16; ++a) sm.f[P0 + a + 1][lane] = ex2(-wl * static_cast<float>(P0 + a + 1));
+        }
+        if (wv == 0) sm.f[0][lane] = 1.f;
+        wait_staged();
+        lds_sync();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float dn = sm.f[nv][P0 + 4 * g + e];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) G[J][e] *= dn;
+        }
+        const int key = P0 + l16;
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) {
+            const u16x4 rx = __builtin_bit_cast(u16x4, col_tr(sm.in[0], 16 * Q, P0, l16, g));  // r[16 Q + 4 g + e][key]
+            float ra[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * Q + 4 * g + e;
+                ra[e] = s < nv ? bf(rx[e]) * sm.f[s][key] : 0.f;
+            }
+            const s4 a = pack4(ra[0], ra[1], ra[2], ra[3]);
+#pragma unroll
+            for (int J = 0; J < 4; ++J) G[J] = mfma(a, col_tr(sm.in[1], 16 * Q, 16 * J, l16, g), G[J]);
+        }
+    }
+    float* lo = P.loc + (bh * P.nseg + seg) * kN * kN;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo[(P0 + 4 * g + e) * kN + 16 * J + l16] = G[J][e];
+    if (kPerToken && wv == kWaves5 - 1) P.rates[(bh * P.nseg + seg) * kN + lane] = rsum;
+}
+
+hipError_t launch_adj_local(const AdjLocalArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * a.nseg));
+    if (a.per_token)
+        hipLaunchKernelGGL(wkv56_adj_local_kernel<true>, grid, dim3(64 * kWaves5), 0, stream, a);
+    else
+        hipLaunchKernelGGL(wkv56_adj_local_kernel<false>, grid, dim3(64 * kWaves5), 0, stream, a);
+    return hipGetLastError();
+}
+
 // ---- time split: the segments' start states ---------------------------------------------------
 // With few (batch row, head) pairs the forwards split each sequence into segments: a state-only
 // pass runs every segment from the zero state (its local end state L_s, and for RWKV-6 its summed
 // rates), this kernel chains them in order, start_0 = S0 and start_{s+1} = D_s start_s + L_s with
 // D_s the segment's total decay per key row (the recurrence is linear in the state), and the
-// output pass runs every segment from its start.  One thread per state element, float32.
+// output pass runs every segment from its start.  The backwards' adjoint obeys the same kind of
+// recurrence backwards in time, G_before = D_s G_after + L_s (L_s from wkv56_adj_local_kernel), so
+// with reverse set the chain runs last segment first from s_in = the final state's gradient and
+// start receives the adjoint after each segment.  One thread per state element, float32.
 __global__ void wkv56_seg_chain_kernel(SegChainArgs P) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= P.BH * kN * kN) return;
@@ -1786,7 +1911,8 @@ __global__ void wkv56_seg_chain_kernel(SegChainArgs P) {
     const int e = static_cast<int>(idx - bh * kN * kN), i = e / kN;  // key row i
     const int64_t h = bh % P.H;
     float S = P.s_in != nullptr ? P.s_in[idx] : 0.f;
-    for (int64_t s = 0; s < P.nseg; ++s) {
+    for (int64_t n = 0; n < P.nseg; ++n) {
+        const int64_t s = P.reverse ? P.nseg - 1 - n : n;
         const int64_t q = (bh * P.nseg + s) * kN * kN + e;
         P.start[q] = S;
         float dl;  // the segment's decay exponent in log2 units

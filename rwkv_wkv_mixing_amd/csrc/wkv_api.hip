@@ -273,12 +273,6 @@ size_t wkv5_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N) {
     return p.st == WKV_OK ? p.ckpt_bytes : 0;
 }
 
-size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt) {
-    const Wkv5Plan p = wkv5_plan(B, T, H, N, WKV_BF16);
-    if (p.st != WKV_OK || p.ws_bytes == 0) return 0;
-    return p.ws_bytes + (have_ckpt ? 0 : p.ckpt_bytes);
-}
-
 }  // extern "C"
 
 namespace {
@@ -321,6 +315,49 @@ size_t split_bytes(int64_t B, int64_t T, int64_t H, int64_t* nseg, int64_t* cps)
     *nseg = wkv::wkv56_segments(B * H, T, cps);
     if (*nseg <= 1) return 0;
     return static_cast<size_t>(B * H * *nseg) * (2 * 64 * 64 + 64) * 4;
+}
+
+// The matrix-state backwards' workspace: the dw / du partials of every (segment, batch row, head);
+// with a time split, the forward split's [BH, nseg, 64, 64] x 2 + [BH, nseg, 64] region (local and
+// chained adjoints and summed rates; a recompute of the chunk-start states uses it first); without a
+// ckpt, the recomputed chunk-start states.  Every offset is a multiple of 256 bytes.
+struct BwdLayout {
+    int64_t nseg = 1, cps = 0;
+    size_t split_off = 0, ckpt_off = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const Wkv5Plan& p, int64_t B, int64_t T, int64_t H, bool split, bool have_ckpt) {
+    BwdLayout l;
+    const size_t sb = split ? split_bytes(B, T, H, &l.nseg, &l.cps) : 0;
+    if (sb == 0) l.nseg = 1;
+    l.split_off = p.ws_bytes * static_cast<size_t>(l.nseg);
+    l.ckpt_off = l.split_off + sb;
+    l.total = l.ckpt_off + (have_ckpt ? 0 : p.ckpt_bytes);
+    return l;
+}
+
+// A backward with a time split (nseg > 1): every segment's local adjoint, the chain of the adjoints
+// after the segments (last first, from ds_out), then the backward of every segment from its own.
+template <class BA, hipError_t (*Launch)(const BA&, hipStream_t)>
+hipError_t run_bwd(BA ba, const BwdLayout& l, bool per_token, void* ws, hipStream_t stream) {
+    if (l.nseg > 1) {
+        const int64_t bh = ba.B * ba.H;
+        float* loc = reinterpret_cast<float*>(static_cast<char*>(ws) + l.split_off);
+        float* gend = loc + bh * l.nseg * 64 * 64;
+        float* rates = gend + bh * l.nseg * 64 * 64;
+        const wkv::AdjLocalArgs al{ba.B, ba.T, ba.H, l.nseg, l.cps, ba.w, per_token, ba.r, ba.go, loc, rates};
+        hipError_t e = wkv::launch_adj_local(al, stream);
+        if (e != hipSuccess) return e;
+        wkv::SegChainArgs c{bh, ba.H, ba.T, l.nseg, l.cps, per_token ? nullptr : ba.w, per_token ? rates : nullptr,
+                            ba.ds_out, loc, gend, nullptr};
+        c.reverse = 1;
+        e = wkv::launch_seg_chain(c, stream);
+        if (e != hipSuccess) return e;
+        ba.nseg = l.nseg;
+        ba.cps = l.cps;
+        ba.gstart = gend;
+    }
+    return Launch(ba, stream);
 }
 
 }  // namespace
@@ -389,6 +426,12 @@ wkv_status_t wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dty
     return hip_status(wkv::launch_wkv6_fwd(a, stream));
 }
 
+size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int flags) {
+    const Wkv5Plan p = wkv5_plan(B, T, H, N, WKV_BF16);
+    if (p.st != WKV_OK || p.ws_bytes == 0) return 0;
+    return bwd_layout(p, B, T, H, !(flags & WKV_WS_NO_SPLIT), (flags & WKV_WS_HAVE_CKPT) != 0).total;
+}
+
 wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
                            const float* u, const void* r, const void* k, const void* v, const void* go,
                            const float* s_in, const float* ds_out, float* dr, float* dk, float* dv, float* dw,
@@ -414,30 +457,35 @@ wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
         (s_in && !aligned(s_in, 4)) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(go, 16) ||
         (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
-    const size_t need = p.ws_bytes + (ckpt ? 0 : p.ckpt_bytes);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    if (!workspace || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    const BwdLayout full = bwd_layout(p, B, T, H, true, ckpt != nullptr);
+    const BwdLayout l = workspace_bytes >= full.total ? full : bwd_layout(p, B, T, H, false, ckpt != nullptr);
+    if (workspace_bytes < l.total) return WKV_EWORKSPACE;
     auto* part = static_cast<float*>(workspace);
+    void* split_ws = static_cast<char*>(workspace) + l.split_off;
     const auto* r16 = static_cast<const uint16_t*>(r);
     const auto* k16 = static_cast<const uint16_t*>(k);
     const auto* v16 = static_cast<const uint16_t*>(v);
     const uint16_t* states = static_cast<const uint16_t*>(ckpt);
     if (ckpt == nullptr) {  // the states before every chunk, recomputed by a state-only forward pass
-        auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + p.ws_bytes);
+        auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + l.ckpt_off);
         wkv::Wkv5Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
         fa.ckpt = tmp;
-        hipError_t e = wkv::launch_wkv5_fwd(fa, stream);
+        hipError_t e = l.nseg > 1 ? run_split<wkv::Wkv5Args, wkv::launch_wkv5_fwd>(fa, false, w, l.nseg, l.cps,
+                                                                                    split_ws, stream)
+                                  : wkv::launch_wkv5_fwd(fa, stream);
         if (e != hipSuccess) return hip_status(e);
         states = tmp;
     }
     wkv::Wkv5BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), states, ds_out,
                         dr, dk, dv, part, dw, du, ds_in};
-    return hip_status(wkv::launch_wkv5_bwd(ba, stream));
+    return hip_status(run_bwd<wkv::Wkv5BwdArgs, wkv::launch_wkv5_bwd>(ba, l, false, workspace, stream));
 }
 
 size_t wkv6_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N) { return wkv5_ckpt_bytes(B, T, H, N); }
 
-size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int have_ckpt) {
-    return wkv5_backward_workspace_bytes(B, T, H, N, have_ckpt);
+size_t wkv6_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N, int flags) {
+    return wkv5_backward_workspace_bytes(B, T, H, N, flags);
 }
 
 wkv_status_t wkv6_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype, const float* w,
@@ -461,24 +509,29 @@ wkv_status_t wkv6_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
         !aligned(dw, 4) || (s_in && !aligned(s_in, 4)) || !aligned(r, 16) || !aligned(k, 16) || !aligned(v, 16) ||
         !aligned(go, 16) || (ckpt && !aligned(ckpt, 16)))
         return WKV_EALIGN;
-    const size_t need = p.ws_bytes + (ckpt ? 0 : p.ckpt_bytes);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    if (!workspace || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    const BwdLayout full = bwd_layout(p, B, T, H, true, ckpt != nullptr);
+    const BwdLayout l = workspace_bytes >= full.total ? full : bwd_layout(p, B, T, H, false, ckpt != nullptr);
+    if (workspace_bytes < l.total) return WKV_EWORKSPACE;
     auto* part = static_cast<float*>(workspace);
+    void* split_ws = static_cast<char*>(workspace) + l.split_off;
     const auto* r16 = static_cast<const uint16_t*>(r);
     const auto* k16 = static_cast<const uint16_t*>(k);
     const auto* v16 = static_cast<const uint16_t*>(v);
     const uint16_t* states = static_cast<const uint16_t*>(ckpt);
     if (ckpt == nullptr) {  // the states before every chunk, recomputed by a state-only forward pass
-        auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + p.ws_bytes);
+        auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + l.ckpt_off);
         wkv::Wkv6Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
         fa.ckpt = tmp;
-        hipError_t e = wkv::launch_wkv6_fwd(fa, stream);
+        hipError_t e = l.nseg > 1 ? run_split<wkv::Wkv6Args, wkv::launch_wkv6_fwd>(fa, true, nullptr, l.nseg, l.cps,
+                                                                                    split_ws, stream)
+                                  : wkv::launch_wkv6_fwd(fa, stream);
         if (e != hipSuccess) return hip_status(e);
         states = tmp;
     }
     wkv::Wkv6BwdArgs ba{B, T, H, w, u, r16, k16, v16, static_cast<const uint16_t*>(go), states, ds_out,
                         dr, dk, dv, dw, part, du, ds_in};
-    return hip_status(wkv::launch_wkv6_bwd(ba, stream));
+    return hip_status(run_bwd<wkv::Wkv6BwdArgs, wkv::launch_wkv6_bwd>(ba, l, true, workspace, stream));
 }
 
 size_t wkv_token_shift_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {

@@ -112,9 +112,24 @@ struct SegChainArgs {
     const float* loc;        // [BH, nseg, 64, 64] each segment's end state from the zero state
     float* start;            // [BH, nseg, 64, 64] each segment's start state
     float* s_out;            // [BH, 64, 64] or NULL
+    int reverse = 0;         // 1: the backwards' adjoint chain, last segment first (start = the adjoint after it)
 };
 
 hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t stream);
+
+// time split of the matrix-state backwards: every segment's adjoint before it from a zero adjoint
+// after it (and, per token rates, the segment's summed capped rates in log2 e units)
+struct AdjLocalArgs {
+    int64_t B, T, H, nseg, cps;
+    const float* w;          // RWKV-5: [H, 64]; RWKV-6: [B, T, C] per-token rates
+    bool per_token;          // RWKV-6
+    const uint16_t* r;
+    const uint16_t* go;
+    float* loc;              // [BH, nseg, 64, 64]
+    float* rates;            // [BH, nseg, 64] (per_token only)
+};
+
+hipError_t launch_adj_local(const AdjLocalArgs& a, hipStream_t stream);
 // segments for a time split of B * H (batch row, head) pairs over T tokens (1: no split)
 int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps);
 
@@ -131,10 +146,12 @@ struct Wkv5BwdArgs {
     float* dr;              // [B, T, C]
     float* dk;
     float* dv;
-    float* part;            // [B, H, 2, 64]: dw, du of each (batch row, head)
+    float* part;            // [nseg, B, H, 2, 64]: dw, du of each (segment, batch row, head)
     float* dw;              // [H, 64], summed over batch rows
     float* du;
     float* ds_in;           // [B, H, 64, 64] gradient of the initial state, or NULL
+    int64_t nseg = 1, cps = 0;      // time split: segments per sequence, chunks per segment
+    const float* gstart = nullptr;  // nseg > 1: [B H, nseg, 64, 64] the adjoint after each segment
 };
 
 // chunked forward (wkv_fwd.hip)
@@ -188,9 +205,11 @@ struct Wkv6BwdArgs {
     float* dk;
     float* dv;
     float* dw;              // [B, T, C], per token
-    float* part;            // [B, H, 64]: du of each (batch row, head)
+    float* part;            // [nseg, B, H, 64]: du of each (segment, batch row, head)
     float* du;              // [H, 64]
     float* ds_in;           // [B, H, 64, 64] or NULL
+    int64_t nseg = 1, cps = 0;      // as Wkv5BwdArgs
+    const float* gstart = nullptr;
 };
 
 hipError_t launch_wkv6_bwd(const Wkv6BwdArgs& a, hipStream_t stream);

@@ -360,11 +360,14 @@ def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
 
 
 def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, ckpt=None,
-                  workspace=None):
+                  workspace=None, split=True):
     """Gradients of sum <go, o> + <grad_state_out, S_T> for
     (o, S_T) = wkv5_forward(w, u, r, k, v, state_in=state_in, return_state=True):
     returns (dr, dk, dv [B, T, C] float32, dw, du [H, 64] float32 summed over
-    the batch, ds_in [B, H, 64, 64] float32 or None).  go: [B, T, C] bfloat16."""
+    the batch, ds_in [B, H, 64, 64] float32 or None).  go: [B, T, C] bfloat16.
+    split: with few (batch row, head) pairs, run the sequence's segments in
+    parallel (the adjoint state chained between them); False keeps one
+    workgroup per pair walking the whole sequence."""
     _need(r, "r", torch.bfloat16)
     dev = r.device
     B, T, C = r.shape
@@ -388,14 +391,17 @@ def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need
         _need(ckpt, "ckpt", torch.uint8, None, dev)
         if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
             raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
-    nbytes = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64, int(ckpt is not None)))
+    flags = (1 if ckpt is not None else 0) | (0 if split else 2)  # WKV_WS_HAVE_CKPT, WKV_WS_NO_SPLIT
+    nbytes = int(lib.wkv5_backward_workspace_bytes(B, T, H, 64, flags))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    # without split the call is told only the unsplit size, so it never splits
+    wsz = workspace.numel() * workspace.element_size() if split else nbytes
     st = lib.wkv5_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
                            _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(dev))
+                           wsz, _stream(dev))
     L.check("wkv5_backward", st)
     return dr, dk, dv, dw, du, ds
 
@@ -459,7 +465,7 @@ def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
 
 
 def wkv6_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, ckpt=None,
-                  workspace=None):
+                  workspace=None, split=True):
     """Gradients of sum <go, o> + <grad_state_out, S_T> for
     (o, S_T) = wkv6_forward(w, u, r, k, v, state_in=state_in, return_state=True):
     returns (dr, dk, dv, dw [B, T, C] float32 (dw per token), du [H, 64]
@@ -487,14 +493,17 @@ def wkv6_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need
         _need(ckpt, "ckpt", torch.uint8, None, dev)
         if ckpt.numel() < wkv5_ckpt_bytes(B, T, H):
             raise ValueError(f"ckpt has {ckpt.numel()} bytes, needs {wkv5_ckpt_bytes(B, T, H)}")
-    nbytes = int(lib.wkv6_backward_workspace_bytes(B, T, H, 64, int(ckpt is not None)))
+    flags = (1 if ckpt is not None else 0) | (0 if split else 2)  # WKV_WS_HAVE_CKPT, WKV_WS_NO_SPLIT
+    nbytes = int(lib.wkv6_backward_workspace_bytes(B, T, H, 64, flags))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    # without split the call is told only the unsplit size, so it never splits
+    wsz = workspace.numel() * workspace.element_size() if split else nbytes
     st = lib.wkv6_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
                            _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(dev))
+                           wsz, _stream(dev))
     L.check("wkv6_backward", st)
     return dr, dk, dv, dw, du, ds
 

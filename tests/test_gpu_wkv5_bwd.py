@@ -87,12 +87,12 @@ def bf16_dev(bits):
     return to_dev(None, DEV, bits)
 
 
-def run(p, go_bits, dST=None, need_state_grad=True):
+def run(p, go_bits, dST=None, need_state_grad=True, split=True):
     w, u = to_dev(p.w, DEV), to_dev(p.u, DEV)
     S0 = None if p.S0 is None else to_dev(p.S0, DEV)
     gS = None if dST is None else to_dev(dST, DEV)
     res = ops().wkv5_backward(w, u, bf16_dev(p.r_bits), bf16_dev(p.k_bits), bf16_dev(p.v_bits), bf16_dev(go_bits),
-                              state_in=S0, grad_state_out=gS, need_state_grad=need_state_grad)
+                              state_in=S0, grad_state_out=gS, need_state_grad=need_state_grad, split=split)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu().numpy() for x in res]
 
@@ -257,6 +257,31 @@ def test_forward_ckpt_gives_the_same_backward(B, T, H):
     assert torch.equal(o1, o2)
     for x, y, n in zip(a, b, NAMES):
         assert torch.equal(x, y), n
+
+
+SPLIT_TOL = 2.0 ** -9
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1000, 2), (2, 200, 3), (1, 4100, 1)])
+def test_backward_time_split_matches_unsplit(B, T, H):
+    """Few (batch row, head) pairs: the backward runs the sequence's segments in parallel, each
+    from the adjoint after it (chained from the segments' local adjoints).  Both the split and the
+    unsplit backward are within the oracle's bounds, and they agree in the norm to 2^-9 (only the
+    order of the float32 sums differs; a bf16 rounding of the adjoint may flip)."""
+    p = W.make_wkv5(B, T, H, seed=41 + T, with_state=True)
+    go_bits, go = W.wkv5_go(p, seed=42)
+    dST = np.random.default_rng(43).standard_normal((B, H, 64, 64)).astype(np.float32)
+    lib = ops().L.lib()
+    assert lib.wkv5_backward_workspace_bytes(B, T, H, 64, 0) > lib.wkv5_backward_workspace_bytes(B, T, H, 64, 2)
+    print(f"case split backward {p.name}", flush=True)
+    a = run(p, go_bits, dST, split=True)
+    b = run(p, go_bits, dST, split=False)
+    check(p, go, a, dST, name="split")
+    for n, x, y in zip(NAMES, a, b):
+        g_, r_ = np.asarray(x, np.float64), np.asarray(y, np.float64)
+        ne, nr = float(np.linalg.norm(g_ - r_)), float(np.linalg.norm(r_))
+        print(f"  split vs unsplit {n}: {ne / nr if nr else ne:.2e}", flush=True)
+        assert ne <= SPLIT_TOL * nr, (n, ne, nr)
 
 
 def test_long_sequence_slow_decay():

@@ -104,9 +104,9 @@ def dev_inputs(p, go_bits, dST=None):
     return d
 
 
-def run(d, need_state_grad=True, ckpt=None):
+def run(d, need_state_grad=True, ckpt=None, split=True):
     res = ops().wkv6_backward(d["w"], d["u"], d["r"], d["k"], d["v"], d["go"], state_in=d["S0"],
-                              grad_state_out=d["dST"], need_state_grad=need_state_grad, ckpt=ckpt)
+                              grad_state_out=d["dST"], need_state_grad=need_state_grad, ckpt=ckpt, split=split)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu().numpy() for x in res]
 
@@ -166,8 +166,8 @@ def test_with_forward_ckpt_matches_recompute():
     O = ops()
     ck = O.new_wkv5_ckpt(2, 300, 2, DEV)
     O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], state_in=d["S0"], ckpt=ck, split=False)
-    a = run(d, ckpt=ck)
-    b = run(d)
+    a = run(d, ckpt=ck, split=False)  # unsplit both: the recompute is then the same unsplit state pass
+    b = run(d, split=False)
     for n, x, y in zip(NAMES, a, b):
         assert np.array_equal(x, y), n
     check(p, go, a, name="with ckpt")
@@ -315,6 +315,31 @@ def test_long_sequence_slow_decay():
     # the terms' summed magnitudes dwarf the signed results here, so the normwise check in check()
     # is what holds the gradients to bf16 accuracy
     check(p, go, run(dev_inputs(p, go_bits, dST)), dST, name="long slow decay")
+
+
+SPLIT_TOL = 2.0 ** -9
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1000, 2), (2, 200, 3), (1, 4100, 1)])
+def test_backward_time_split_matches_unsplit(B, T, H):
+    """Few (batch row, head) pairs: the backward runs the sequence's segments in parallel, each
+    from the adjoint after it (chained with the segments' summed capped rates).  Both the split
+    and the unsplit backward are within the oracle's bounds, and they agree in the norm to 2^-9."""
+    p = W.make_wkv6(B, T, H, seed=45 + T, with_state=True)
+    go_bits, go = W.wkv5_go(p, seed=46)
+    dST = np.random.default_rng(47).standard_normal((B, H, 64, 64)).astype(np.float32)
+    d = dev_inputs(p, go_bits, dST)
+    lib = ops().L.lib()
+    assert lib.wkv6_backward_workspace_bytes(B, T, H, 64, 0) > lib.wkv6_backward_workspace_bytes(B, T, H, 64, 2)
+    print(f"case split backward {p.name}", flush=True)
+    a = run(d, split=True)
+    b = run(d, split=False)
+    check(p, go, a, dST, name="split")
+    for n, x, y in zip(NAMES, a, b):
+        g_, r_ = np.asarray(x, np.float64), np.asarray(y, np.float64)
+        ne, nr = float(np.linalg.norm(g_ - r_)), float(np.linalg.norm(r_))
+        print(f"  split vs unsplit {n}: {ne / nr if nr else ne:.2e}", flush=True)
+        assert ne <= SPLIT_TOL * nr, (n, ne, nr)
 
 
 def test_backward_from_time_split_forward():
