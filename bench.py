@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long", "wkv6long"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -613,10 +613,11 @@ def bench_wkv6(args):
     return out
 
 
-def bench_matrix_train(args, gen):
+def bench_matrix_train(args, gen, long=False):
     """RWKV-5 (gen 5) or RWKV-6 (gen 6) training step at B=8 T=1024 C=4096 (64
-    heads of 64): the forward saving its chunk-start states, then the backward
-    from them (dr, dk, dv, dw, du).  Algorithmic bytes per channel-token:
+    heads of 64), or with long=True one sequence of T=32768 (both calls then
+    split the sequence in time): the forward saving its chunk-start states, then
+    the backward from them (dr, dk, dv, dw, du).  Algorithmic bytes per channel-token:
     forward r, k, v in (6 B), o out (4 B), states out (2 B); backward r, k, v,
     go in (8 B), states in (2 B), dr, dk, dv out (12 B); RWKV-6 adds its
     per-token rates w in (4 B) to both and dw out (4 B) to the backward."""
@@ -625,7 +626,10 @@ def bench_matrix_train(args, gen):
     from rwkv_wkv_mixing_amd import ops, workloads as W
 
     dev = torch.device("cuda:0")
-    p = W.wkv5_config() if gen == 5 else W.wkv6_config()
+    if long:
+        p = (W.make_wkv5 if gen == 5 else W.make_wkv6)(1, 32768, 64, seed=0, name=f"wkv{gen} bf16 B=1 T=32768 H=64 N=64")
+    else:
+        p = W.wkv5_config() if gen == 5 else W.wkv6_config()
     B, T, H = p.B, p.T, p.H
     up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
     w, u = torch.from_numpy(p.w).to(dev), torch.from_numpy(p.u).to(dev)
@@ -644,6 +648,8 @@ def bench_matrix_train(args, gen):
     n_fwd, n_bwd = f"wkv{gen}_forward", f"wkv{gen}_backward"
     nws = int((lib.wkv5_backward_workspace_bytes if gen == 5 else lib.wkv6_backward_workspace_bytes)(B, T, H, 64, 1))
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    nwf = int((lib.wkv5_forward_workspace_bytes if gen == 5 else lib.wkv6_forward_workspace_bytes)(B, T, H, 64))
+    wsf = torch.empty(max(nwf, 1), dtype=torch.uint8, device=dev)  # the forward's time split (0 bytes: none)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -651,7 +657,7 @@ def bench_matrix_train(args, gen):
         r, k, v, _, *rest = sets[i % len(sets)]
         ww = rest[0] if rest else w
         L.check(n_fwd, f_fwd(B, T, H, 64, L.WKV_BF16, ptr(ww), ptr(u), ptr(r), ptr(k), ptr(v), ptr(o), None, None,
-                             ptr(ck), None, 0, stream))
+                             ptr(ck), ptr(wsf) if nwf else None, nwf, stream))
 
     def bwd(i):
         r, k, v, g, *rest = sets[i % len(sets)]
@@ -686,7 +692,7 @@ def bench_matrix_train(args, gen):
     achieved = alg_b / (st_b["mean"] * 1e-6) / 1e9
     what = "RWKV-5 matrix-state WKV" if gen == 5 else "RWKV-6 matrix-state WKV (per-token decay)"
     out = {
-        "metric": f"{what} forward+backward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
+        "metric": f"{what} forward+backward channel·tokens/s, B={B} T={T} H={H} N=64 bf16",
         "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -694,24 +700,28 @@ def bench_matrix_train(args, gen):
         "call_us": {f"{n_fwd}(ckpt)": st_f, f"{n_bwd}(ckpt)": st_b},
         "roofline": {"bound": "hbm", "kernel": f"{n_bwd} (backward kernel + du{'/dw' if gen == 5 else ''} batch sum)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(f"wkv{gen}train_bf16_B8_T1024_H64", f"wkv{gen}_bwd"),
+                     "traffic": None if long else recorded_traffic(f"wkv{gen}train_bf16_B8_T1024_H64", f"wkv{gen}_bwd"),
                      "alg_bytes_per_launch": alg_b},
     }
     if not args.no_cpu:
-        # the float64 numpy oracle on batch rows 0 and 1 (all 64 heads, all tokens): forward, then backward
+        # the float64 numpy oracle on batch rows 0 and 1 (all 64 heads; the long sequence: its first
+        # 2048 tokens): forward, then backward
         import oracle
 
         fw, bw = ((oracle.wkv5_forward_ref, oracle.wkv5_backward_ref) if gen == 5 else
                   (oracle.wkv6_forward_ref, oracle.wkv6_backward_ref))
-        ws_ = p.w if gen == 5 else p.w[:2]
+        rows, ts = (slice(0, 1), slice(0, 2048)) if long else (slice(0, 2), slice(0, T))
+        cut = lambda x: x[rows, ts]
+        ws_ = p.w if gen == 5 else cut(p.w)
+        n_s = cut(p.r).shape[0] * cut(p.r).shape[1] * C
         t0 = time.perf_counter()
-        fw(ws_, p.u, p.r[:2], p.k[:2], p.v[:2], H)
-        bw(ws_, p.u, p.r[:2], p.k[:2], p.v[:2], go_vals[:2], H)
+        fw(ws_, p.u, cut(p.r), cut(p.k), cut(p.v), H)
+        bw(ws_, p.u, cut(p.r), cut(p.k), cut(p.v), cut(go_vals), H)
         t_np = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": 2 * T * C / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"batch rows 0-1 of the workload (all 64 heads x {T} tokens, {2 * T * C} "
-                                         f"channel*tokens): the float64 numpy oracle's forward and backward, "
-                                         f"{t_np:.2f} s"}
+        what_s = "batch row 0, tokens 0-2047" if long else f"batch rows 0-1 (all {T} tokens)"
+        out["cpu_baseline"] = {"value": n_s / t_np, "unit": "channel·tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{what_s} of the workload, all 64 heads ({n_s} channel*tokens): the "
+                                         f"float64 numpy oracle's forward and backward, {t_np:.2f} s"}
     return out
 
 
@@ -751,10 +761,13 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode"):
+    if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long",
+                         "wkv6long"):
         out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
                "wkv5train": lambda a: bench_matrix_train(a, 5), "wkv6": bench_wkv6,
-               "wkv6train": lambda a: bench_matrix_train(a, 6), "wkv6decode": bench_wkv6_decode}[args.workload](args)
+               "wkv6train": lambda a: bench_matrix_train(a, 6), "wkv6decode": bench_wkv6_decode,
+               "wkv5long": lambda a: bench_matrix_train(a, 5, long=True),
+               "wkv6long": lambda a: bench_matrix_train(a, 6, long=True)}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     if args.workload == "fwdbwd":

@@ -1795,9 +1795,9 @@ hipError_t launch_step(const A& a, hipStream_t stream) {
 // also writes the segment's summed rates (log2 e units) for the chain.  One 4-wave workgroup per
 // (batch row, head, segment); wave w owns key rows 16 w .. 16 w + 15 of L, as in the backwards.
 struct AdjLocalShared {
-    uint16_t in[2][kLc][kN];   // r, go of the chunk, [token][swizzled channel]
-    float f[kLc + 1][kPadF];   // e^{-E[t]}, t = 0 .. 64, per channel
-    float blk[kWaves5][kN];    // RWKV-6: each wave's 16-token rate sums
+    uint16_t in[2][2][kLc][kN];  // [buffer][r, go] of a chunk, [token][swizzled channel]
+    float f[kLc + 1][kPadF];     // e^{-E[t]}, t = 0 .. 64, per channel
+    float blk[kWaves5][kN];      // RWKV-6: each wave's 16-token rate sums
 };
 
 template <bool kPerToken>
@@ -1813,50 +1813,71 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv56_adj_local_kernel(AdjLocalA
     const int64_t ch_lo = seg * P.cps;
     const int64_t ch_hi = ch_lo + P.cps < nch ? ch_lo + P.cps : nch;
     const int P0 = 16 * wv;
+    auto chunk_len = [&](int64_t c) { return static_cast<int>((P.T - c * kLc) < kLc ? (P.T - c * kLc) : kLc); };
+    // chunk c's r and go into buffer q by buffer -> LDS copies (wave w: rows 16 w .. 16 w + 15; rows
+    // past the sequence's end read as zero through the buffer range)
+    auto stage = [&](int64_t c, int q) {
+        const int nvc = chunk_len(c);
+        const uint16_t* src[2] = {P.r, P.go};
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const Rsrc rs = make_rsrc(src[a] + ((b * P.T + c * kLc) * C + h * kN), static_cast<uint32_t>(((nvc - 1) * C + kN) * 2));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = P0 + 8 * i + lane / 8;
+                const int sq = (lane % 8) ^ (row & 7);
+                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + sq * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[q][a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+            }
+        }
+    };
+    // RWKV-6: chunk c's rates of tokens P0 .. P0 + 15, channel lane, into registers (0 past its end)
+    auto load_w = [&](int64_t c, float (&x)[16]) {
+        const int nvc = chunk_len(c);
+        const float* wr = P.w + (b * P.T + c * kLc + P0) * C + h * kN + lane;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) x[a] = P0 + a < nvc ? wr[a * C] : 0.f;
+    };
+
     f4 G[4];  // G[J][e] = L[P0 + 4 g + e][16 J + l16]
 #pragma unroll
     for (int J = 0; J < 4; ++J) G[J] = f4{0.f, 0.f, 0.f, 0.f};
     float rsum = 0.f;  // RWKV-6, last wave: channel lane's summed capped rates over the segment
+    float xw[16];      // RWKV-6: the current chunk's rates
+    stage(ch_hi - 1, 0);
+    if (kPerToken) {
+        load_w(ch_hi - 1, xw);
+    } else {  // RWKV-5: the same table for every chunk
+        const float wl = P.w[h * kN + lane] * kL2E;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) sm.f[P0 + a + 1][lane] = ex2(-wl * static_cast<float>(P0 + a + 1));
+    }
+    if (wv == 0) sm.f[0][lane] = 1.f;
 
     for (int64_t ch = ch_hi - 1; ch >= ch_lo; --ch) {
-        const int64_t t0 = ch * kLc;
-        const int nv = static_cast<int>((P.T - t0) < kLc ? (P.T - t0) : kLc);
-        lds_sync();  // every wave is done with the previous chunk's inputs and table
-        const uint16_t* src[2] = {P.r, P.go};
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {  // rows past the sequence's end read as zero (buffer range)
-            const Rsrc rs = make_rsrc(src[a] + ((b * P.T + t0) * C + h * kN), static_cast<uint32_t>(((nv - 1) * C + kN) * 2));
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = P0 + 8 * i + lane / 8;
-                const int q = (lane % 8) ^ (row & 7);
-                const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
-            }
-        }
-        if (kPerToken) {  // wave w: tokens P0 .. P0 + 15 of channel lane, prefix-summed, then offset
-            const float* wr = P.w + (b * P.T + t0 + P0) * C + h * kN + lane;
+        const int nv = chunk_len(ch);
+        const int q = static_cast<int>((ch_hi - 1 - ch) & 1);
+        if (kPerToken) {  // E[t + 1] = E[t] + min(w_t, cap) log2 e: 16-token prefix sums, then the offsets
             float x[16];
 #pragma unroll
-            for (int a = 0; a < 16; ++a) x[a] = P0 + a < nv ? fminf(wr[a * C], kWCap6) * kL2E : 0.f;
+            for (int a = 0; a < 16; ++a) x[a] = fminf(xw[a], kWCap6) * kL2E;
 #pragma unroll
             for (int a = 1; a < 16; ++a) x[a] += x[a - 1];
             sm.blk[wv][lane] = x[15];
-            lds_sync();
+            lds_sync();  // also: every wave is done with the previous chunk's table
             float off = 0.f;
             for (int A = 0; A < wv; ++A) off += sm.blk[A][lane];
 #pragma unroll
             for (int a = 0; a < 16; ++a) sm.f[P0 + a + 1][lane] = ex2(-(x[a] + off));
             if (wv == kWaves5 - 1) rsum += x[15] + off;  // the chunk's total (tokens past nv add 0)
-        } else {
-            const float wl = P.w[h * kN + lane] * kL2E;
-#pragma unroll
-            for (int a = 0; a < 16; ++a) sm.f[P0 + a + 1][lane] = ex2(-wl * static_cast<float>(P0 + a + 1));
         }
-        if (wv == 0) sm.f[0][lane] = 1.f;
         wait_staged();
-        lds_sync();
+        lds_sync();  // this chunk's inputs and table are in LDS; the other buffer is free
+        if (ch > ch_lo) {  // the next chunk loads while this one is computed
+            stage(ch - 1, q ^ 1);
+            if (kPerToken) load_w(ch - 1, xw);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float dn = sm.f[nv][P0 + 4 * g + e];
@@ -1866,7 +1887,7 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv56_adj_local_kernel(AdjLocalA
         const int key = P0 + l16;
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q) {
-            const u16x4 rx = __builtin_bit_cast(u16x4, col_tr(sm.in[0], 16 * Q, P0, l16, g));  // r[16 Q + 4 g + e][key]
+            const u16x4 rx = __builtin_bit_cast(u16x4, col_tr(sm.in[q][0], 16 * Q, P0, l16, g));  // r[16 Q + 4 g + e][key]
             float ra[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1875,7 +1896,7 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv56_adj_local_kernel(AdjLocalA
             }
             const s4 a = pack4(ra[0], ra[1], ra[2], ra[3]);
 #pragma unroll
-            for (int J = 0; J < 4; ++J) G[J] = mfma(a, col_tr(sm.in[1], 16 * Q, 16 * J, l16, g), G[J]);
+            for (int J = 0; J < 4; ++J) G[J] = mfma(a, col_tr(sm.in[q][1], 16 * Q, 16 * J, l16, g), G[J]);
         }
     }
     float* lo = P.loc + (bh * P.nseg + seg) * kN * kN;
