@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     auto stage = [&](int64_t ch, int buf) {  // wave wv copies rows 16 wv .. 16 wv + 15 of r, k, v
         const uint16_t* src[3] = {P.r, P.k, P.v};
 #pragma unroll
-        for (int a = 0; a < 3; ++a) {
+        for (int a = kOut ? 0 : 1; a < 3; ++a) {  // a state-only pass needs no r
             const Rsrc rs = chunk_rsrc(src[a], ch);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -395,7 +395,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
         const uint16_t* src[3] = {P.r, P.k, P.v};
         const int64_t n = chunk_rows(ch);
 #pragma unroll
-        for (int a = 0; a < 3; ++a) {
+        for (int a = kOut ? 0 : 1; a < 3; ++a) {  // a state-only pass needs no r
             const Rsrc rs = make_rsrc(src[a] + ((b * P.T + ch * kLc) * C + h * kN), static_cast<uint32_t>(((n - 1) * C + kN) * 2));
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
