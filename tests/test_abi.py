@@ -334,6 +334,24 @@ def test_wkv6_backward_validation(lib):
     assert wkv6_bwd(lib, 1, 4, 2, 64, L.WKV_BF16, *args, ws=x, nws=small - 1, ck=x) == L.WKV_EWORKSPACE
 
 
+def test_matrix_backward_split_workspace(lib):
+    # 1 x 1000 x 2 heads: 8 segments of 2 chunks.  Split size = the dw/du partials (2 x 64 float32
+    # per pair) for every segment + the forward split's region; WKV_WS_NO_SPLIT (2) = one set of
+    # partials; without WKV_WS_HAVE_CKPT (1) both add the recomputed chunk-start states
+    B, T, H = 1, 1000, 2
+    full = lib.wkv5_backward_workspace_bytes(B, T, H, 64, 1)
+    flat = lib.wkv5_backward_workspace_bytes(B, T, H, 64, 3)
+    assert flat == B * H * 2 * 64 * 4
+    assert full == 8 * flat + lib.wkv5_forward_workspace_bytes(B, T, H, 64)
+    assert lib.wkv5_backward_workspace_bytes(B, T, H, 64, 0) == full + lib.wkv5_ckpt_bytes(B, T, H, 64)
+    assert lib.wkv5_backward_workspace_bytes(B, T, H, 64, 2) == flat + lib.wkv5_ckpt_bytes(B, T, H, 64)
+    assert full % 256 == 0 and flat % 256 == 0
+    assert lib.wkv6_backward_workspace_bytes(B, T, H, 64, 1) == full
+    # 512 pairs (or 3 chunks): no split, one size whatever the flags
+    for shape in ((8, 1024, 64), (1, 192, 2)):
+        assert lib.wkv5_backward_workspace_bytes(*shape, 64, 1) == lib.wkv5_backward_workspace_bytes(*shape, 64, 3)
+
+
 def test_matrix_forward_split_workspace(lib):
     # a split only below 256 (batch row, head) pairs and from 4 chunks: local and start states
     # (2 x 64 x 64 float32) and summed rates (64 float32) per pair and segment
