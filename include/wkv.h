@@ -290,7 +290,7 @@ size_t wkv5_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t N);
 
 /* Bytes of scratch memory wkv5_backward needs: 2 x 64 float32 per (batch
  * row, head), plus wkv5_ckpt_bytes() when it is called without a ckpt and
- * recomputes the chunk-start states itself.  With fewer than 256 (batch row,
+ * recomputes the chunk-start states itself.  With at most 256 (batch row,
  * head) pairs and at least 4 chunks the backward splits each sequence into
  * segments run in parallel (the forward's time split, applied to the adjoint
  * state), which needs per segment another 2 x 64 float32 per pair plus

@@ -1955,12 +1955,13 @@ hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Segments per sequence: only below one workgroup per CU (256 pairs), about 512 workgroups in
-// all, and at least two chunks per segment.
-int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps) {
+// Segments per sequence: only for at most max_bh pairs, about 512 workgroups in all (two per CU
+// fit at once), and at least two chunks per segment.  Measured: at 256 pairs two segments make the
+// backwards 1.4x faster but not the forwards; at 384 pairs (768 workgroups) both get slower.
+int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps, int64_t max_bh) {
     const int64_t nch = (T + kLc - 1) / kLc;
     *cps = nch;
-    if (BH <= 0 || BH >= 256 || nch < 4) return 1;
+    if (BH <= 0 || BH > max_bh || nch < 4) return 1;
     int64_t want = (512 + BH - 1) / BH;
     if (want > nch / 2) want = nch / 2;
     if (want < 2) return 1;

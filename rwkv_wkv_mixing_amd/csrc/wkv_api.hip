@@ -311,8 +311,8 @@ hipError_t run_split(const A& a, bool per_token, const float* w5, int64_t nseg, 
     return Launch(p3, stream);
 }
 
-size_t split_bytes(int64_t B, int64_t T, int64_t H, int64_t* nseg, int64_t* cps) {
-    *nseg = wkv::wkv56_segments(B * H, T, cps);
+size_t split_bytes(int64_t B, int64_t T, int64_t H, int64_t* nseg, int64_t* cps, int64_t max_bh = 255) {
+    *nseg = wkv::wkv56_segments(B * H, T, cps, max_bh);
     if (*nseg <= 1) return 0;
     return static_cast<size_t>(B * H * *nseg) * (2 * 64 * 64 + 64) * 4;
 }
@@ -328,7 +328,7 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(const Wkv5Plan& p, int64_t B, int64_t T, int64_t H, bool split, bool have_ckpt) {
     BwdLayout l;
-    const size_t sb = split ? split_bytes(B, T, H, &l.nseg, &l.cps) : 0;
+    const size_t sb = split ? split_bytes(B, T, H, &l.nseg, &l.cps, 256) : 0;
     if (sb == 0) l.nseg = 1;
     l.split_off = p.ws_bytes * static_cast<size_t>(l.nseg);
     l.ckpt_off = l.split_off + sb;

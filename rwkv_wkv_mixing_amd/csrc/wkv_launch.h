@@ -130,8 +130,9 @@ struct AdjLocalArgs {
 };
 
 hipError_t launch_adj_local(const AdjLocalArgs& a, hipStream_t stream);
-// segments for a time split of B * H (batch row, head) pairs over T tokens (1: no split)
-int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps);
+// segments for a time split of B * H (batch row, head) pairs over T tokens (1: no split); the
+// forwards split below 256 pairs, the backwards up to 256
+int64_t wkv56_segments(int64_t BH, int64_t T, int64_t* cps, int64_t max_bh = 255);
 
 struct Wkv5BwdArgs {
     int64_t B, T, H;

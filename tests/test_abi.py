@@ -347,6 +347,9 @@ def test_matrix_backward_split_workspace(lib):
     assert lib.wkv5_backward_workspace_bytes(B, T, H, 64, 2) == flat + lib.wkv5_ckpt_bytes(B, T, H, 64)
     assert full % 256 == 0 and flat % 256 == 0
     assert lib.wkv6_backward_workspace_bytes(B, T, H, 64, 1) == full
+    # 256 pairs: the backward splits (2 segments), the forward does not
+    assert lib.wkv5_forward_workspace_bytes(4, 1024, 64, 64) == 0
+    assert lib.wkv5_backward_workspace_bytes(4, 1024, 64, 64, 1) > lib.wkv5_backward_workspace_bytes(4, 1024, 64, 64, 3)
     # 512 pairs (or 3 chunks): no split, one size whatever the flags
     for shape in ((8, 1024, 64), (1, 192, 2)):
         assert lib.wkv5_backward_workspace_bytes(*shape, 64, 1) == lib.wkv5_backward_workspace_bytes(*shape, 64, 3)

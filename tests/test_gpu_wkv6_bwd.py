@@ -320,7 +320,7 @@ def test_long_sequence_slow_decay():
 SPLIT_TOL = 2.0 ** -9
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 1000, 2), (2, 200, 3), (1, 4100, 1)])
+@pytest.mark.parametrize("B,T,H", [(1, 1000, 2), (2, 200, 3), (1, 4100, 1), (4, 256, 64)])
 def test_backward_time_split_matches_unsplit(B, T, H):
     """Few (batch row, head) pairs: the backward runs the sequence's segments in parallel, each
     from the adjoint after it (chained with the segments' summed capped rates).  Both the split
