@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long", "wkv6long"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long", "wkv6long", "stream"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -748,6 +748,96 @@ def bench_copy(args):
             "config": {"workload": "copy 1 GiB f32", "bytes_read": 4 * n, "bytes_written": 4 * n}}
 
 
+STREAM_MIXES = ((1, 0), (0, 1), (1, 1), (3, 4), (1, 3), (2, 1), (3, 2))
+
+
+def bench_stream(args):
+    """The HBM streaming ceiling: hand-written 16-byte-vector kernels
+    (rwkv_wkv_mixing_amd/stream/stream.hip) that read NR arrays and write NW
+    arrays elementwise, for the read:write mixes of the WKV kernels, swept over
+    grids of 256 to 32,768 workgroups of 256 threads (and one workgroup per
+    256 x U vectors), 1, 2 or 4 vectors in flight per thread and array, with
+    and without the non-temporal hint.  Two traffic volumes per launch: 512 MB
+    (the scale of one WKV call) and 2 GB.  Four rotated operand sets (more
+    than 1 GB in all for 512 MB launches) keep launches from hitting the
+    256 MB Infinity Cache.  Each configuration: 2 untimed launches, then the
+    median of `--steps` (at least 10) HIP-event timings on the launching
+    stream.  The reported rate counts bytes read plus bytes written."""
+    import torch
+
+    from rwkv_wkv_mixing_amd.build import STREAM_LIB
+
+    if not os.path.exists(STREAM_LIB):
+        raise RuntimeError(f"{STREAM_LIB} is missing; run __graft_entry__.build()")
+    L = ctypes.CDLL(STREAM_LIB)
+    L.wkv_stream_launch.restype = ctypes.c_int
+    L.wkv_stream_launch.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                         ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.empty(1024 * 4, dtype=torch.int32, device=dev)
+    reps = max(10, args.steps)
+    table = []
+    for total in (512 << 20, 2048 << 20):
+        for nr, nw in STREAM_MIXES:
+            n16 = total // 16 // (nr + nw)
+            nsets = 4
+            arrs = [[torch.zeros(n16 * 4, dtype=torch.int32, device=dev) for _ in range(nr + nw)]
+                    for _ in range(nsets)]
+            ptrs = []
+            for s in arrs:
+                ins = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in s[:nr]])
+                outs = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in s[nr:]])
+                ptrs.append((ins, outs))
+            best = None
+            rows = []
+            for unroll in (1, 2, 4):
+                full = (n16 + 256 * unroll - 1) // (256 * unroll)
+                for nt in (0, 1):
+                    for grid in sorted({256, 512, 1024, 2048, 4096, 8192, 16384, 32768, full}):
+                        if grid > full:
+                            continue
+
+                        def launch(i):
+                            ins, outs = ptrs[i % nsets]
+                            rc = L.wkv_stream_launch(nr, nw, unroll, nt, grid, 256, ins, outs, n16,
+                                                     ctypes.c_void_p(sink.data_ptr()), sptr)
+                            if rc != 0:
+                                raise RuntimeError(f"wkv_stream_launch failed: {rc}")
+
+                        for i in range(2):
+                            launch(i)
+                        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                               for _ in range(reps)]
+                        for i in range(reps):
+                            evs[i][0].record(stream)
+                            launch(i)
+                            evs[i][1].record(stream)
+                        torch.cuda.synchronize()
+                        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+                        gbps = (nr + nw) * n16 * 16 / (us * 1e-6) / 1e9
+                        rows.append({"unroll": unroll, "nt": nt, "grid": grid, "us": round(us, 2),
+                                     "gbps": round(gbps, 1)})
+                        if best is None or gbps > best["gbps"]:
+                            best = {"unroll": unroll, "nt": nt, "grid": grid, "us": round(us, 2),
+                                    "gbps": round(gbps, 1)}
+            del arrs, ptrs
+            torch.cuda.empty_cache()
+            table.append({"read": nr, "write": nw, "bytes": (nr + nw) * n16 * 16, "best": best, "sweep": rows})
+            print(f"stream {nr}:{nw} {total >> 20} MB: best {best}", file=sys.stderr, flush=True)
+    copy = [t for t in table if t["read"] == 1 and t["write"] == 1 and t["bytes"] <= (512 << 20)][0]
+    return {"metric": "HBM streaming ceiling GB/s (read + write bytes), best over grids and variants",
+            "value": copy["best"]["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 2,
+            "ms_per_step": copy["best"]["us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+            "config": {"workload": "stream 1:1 copy of 512 MB (value); the table covers every mix"},
+            "peak": HBM_PEAK_GBPS,
+            "ceiling": [{"read": t["read"], "write": t["write"], "bytes": t["bytes"], **t["best"],
+                         "frac_of_peak": round(t["best"]["gbps"] / HBM_PEAK_GBPS, 4)} for t in table],
+            "sweep": table}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -762,8 +852,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long",
-                         "wkv6long"):
+                         "wkv6long", "stream"):
         out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
+               "stream": bench_stream,
                "wkv5train": lambda a: bench_matrix_train(a, 5), "wkv6": bench_wkv6,
                "wkv6train": lambda a: bench_matrix_train(a, 6), "wkv6decode": bench_wkv6_decode,
                "wkv5long": lambda a: bench_matrix_train(a, 5, long=True),

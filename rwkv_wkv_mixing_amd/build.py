@@ -21,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librwkv_wkv.so")
+STREAM_SRC = os.path.join(PKG, "stream", "stream.hip")
+STREAM_LIB = os.path.join(PKG, "librwkv_stream.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
@@ -71,5 +73,18 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_stream(verbose: bool = False) -> str:
+    """Compile the streaming-ceiling kernels (stream/stream.hip) into
+    librwkv_stream.so: measurement only, not part of the operator library."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    obj = _compile(STREAM_SRC, verbose)
+    tmp = STREAM_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp]
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    os.replace(tmp, STREAM_LIB)
+    return STREAM_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_stream(verbose="-v" in sys.argv))

@@ -405,7 +405,8 @@ struct Span {
                 // scale is rounded to ~D 2^-24 relative while its share of every
                 // denominator here is ~2^-D (the forward's saved states, where
                 // such a key might dominate later, use the exact split)
-                const float ej = ex2(fmaf(in.kv.k(j), kL2E, -scf));
+                const float kj = in.kv.k(j);
+                const float ej = ex2(fmaf(kj, kL2E_lo, fmaf(kj, kL2E, -scf)));
                 const float E = ej * eu;
                 const float den = bb + E;
                 dmin = fminf(dmin, den);
@@ -725,7 +726,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
         sp.recompute(cur, rg, g, ch, eu, dec, fast_out);
         du += sp.du;
         put_map(sm, wave, lane, sp);
-        lds_sync();
+        lds_sync_lgkm();
         RMap suf = rmap_identity();
         for (int i = W - 1; i > wave; --i) suf = rcompose(get_map(sm, i, lane, dL), suf);
         if (wave == 0) {
@@ -737,7 +738,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
             sm.cin_s[lane] = out.sg;
         }
         ndw += sp.reverse(rapply(suf, cin), g, ch, eu, dec, fast_out);
-        lds_sync();
+        lds_sync_lgkm();
         cin = RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane], sm.cin_s[lane]};
     }
     put_partials(sm, P, tile, wave, lane, ndw, du);

@@ -31,7 +31,12 @@
 
 namespace wkv {
 
-constexpr float kL2E = 1.4426950408889634f;   // log2(e)
+constexpr float kL2E = 1.4426950408889634f;   // log2(e), rounded to float32
+// log2(e) - kL2E: the float32 constant is 1.3e-8 relative short, which would
+// put 5e-7 relative error into the weight of a key of 40; k log2 e is formed
+// as fma(k, kL2E, k kL2E_lo) (exact to ~2^-24 of the product) wherever a key
+// becomes a weight.
+constexpr float kL2E_lo = 1.925963033500011e-08f;
 constexpr float kLN2 = 0.6931471805599453f;   // ln(2)
 constexpr float kHi = 0x1p32f;               // rescale bounds for b and new terms
 constexpr float kLo = 0x1p-32f;
@@ -202,7 +207,7 @@ __device__ __forceinline__ Chan make_chan(float w, float u) {
     ch.dd = exp(-static_cast<double>(w));
     ch.dhi = static_cast<float>(ch.dd);
     ch.dlo = static_cast<float>(ch.dd - static_cast<double>(ch.dhi));
-    ch.u2 = u * kL2E;
+    ch.u2 = fmaf(u, kL2E, u * kL2E_lo);
     return ch;
 }
 
@@ -230,14 +235,14 @@ struct Key {
 
 __device__ __forceinline__ Key key_split(float k) {
     const float n = __builtin_amdgcn_fmed3f(__builtin_rintf(k * kL2E), -kNMax, kNMax);
-    const float f = fmaf(k, kL2E, -n);
+    const float f = fmaf(k, kL2E_lo, fmaf(k, kL2E, -n));
     return Key{ex2(f), f, static_cast<int>(n)};
 }
 
 // The same split for a key already known to satisfy |k log2 e| < kNMax.
 __device__ __forceinline__ Key key_split_bounded(float k) {
     const float n = __builtin_rintf(k * kL2E);
-    const float f = fmaf(k, kL2E, -n);
+    const float f = fmaf(k, kL2E_lo, fmaf(k, kL2E, -n));
     return Key{ex2(f), f, static_cast<int>(n)};
 }
 

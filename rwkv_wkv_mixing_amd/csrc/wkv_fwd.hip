@@ -254,8 +254,18 @@ struct SubWork {
     template <bool Gated>
     __device__ __forceinline__ void outputs(const St& X, const FwdGeo& g, const Chunk1<TIn, L>& rch, const Chan& ch,
                                             float eu, bool fast, bool want_y, int64_t C) const {
-        const bool carry_fits = !(X.b > 0.f) | ((X.s - sl + __builtin_amdgcn_frexp_expf(X.b) <= kCarryAbove) &
-                                                (X.s - sl + __builtin_amdgcn_frexp_expf(X.a) <= kCarryAbove + 20));
+        // The carry enters token j as d^j X, with d^j a float32 running product.
+        // Where d^j falls below float32's normal range its absolute error is
+        // 2^-150, so the carry term X_B d^j (X_B < 2^lvl at the local scale)
+        // is off by up to 2^(lvl - 150) against a denominator of at least
+        // kTiny = 2^-100: the fast path then also needs lvl <= 24 (error below
+        // 2^-26 of the denominator, and of |A/B| in the numerator); otherwise
+        // the general path rescales per token.
+        const int lvl = X.s - sl + __builtin_amdgcn_frexp_expf(X.b);
+        const bool dp_normal = ipow<L - 1>(ch.dd) >= 0x1p-125;
+        const bool carry_fits =
+            !(X.b > 0.f) | ((lvl <= kCarryAbove) & (X.s - sl + __builtin_amdgcn_frexp_expf(X.a) <= kCarryAbove + 20) &
+                            (dp_normal | (lvl <= 24)));
         bool fast_out = fast_local && __all(carry_fits);
         if (fast_out && want_y)
             fast_out = __all(corrected_outputs<Gated>(X, sl, N, D, rch, ch, g.ry, g.vout, g.row_out) >= kTiny);
@@ -402,6 +412,208 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
     }
 }
 
+
+// Whole-tile forward (bf16 inputs): one workgroup per (batch row, 64-channel
+// tile) walks the time blocks of its tile in order, so the carry between
+// blocks stays in the workgroup: no carry slots, tickets or workspace.  Used
+// when there are enough tiles to give every CU two workgroups.
+//
+// Per block of W L tokens (wave i owning tokens [iL, (i+1)L)):
+//   stage   the next block's k and v stream into LDS by asynchronous buffer ->
+//           LDS copies (16 bytes per lane, stage_rows) while this block is
+//           computed; a wave reads its own rows of the staged block into
+//           registers, waits for those LDS reads, then starts the copies of its
+//           next rows into the same LDS rows.  The copies are not tracked by the
+//           compiler: wait_staged() before the LDS reads, wait_lds_reads()
+//           before the next copies.
+//   local   every wave runs its L tokens from the empty state at the fixed
+//           scale of its largest key, keeping the local numerator and
+//           denominator of every token (as the time-split kernel);
+//   scan    the last wave walks the block's W summaries in order from the
+//           block's carry-in, X_{i+1} = d^L X_i + S_i (W combines per block,
+//           in float64, so that a saved state is rounded to float32 once
+//           however many combines carried it), and leaves every wave's
+//           carry-in X_i in LDS; it keeps X_W, the next block's carry-in;
+//   output  y = (N + d^j X_A) / (D + d^j X_B) as the time-split kernel.
+// bf16 inputs carry 2^-8 relative rounding and their outputs a 2e-3 bound, so
+// inside a sub-chunk the key weight is one exp2 of k log2 e - scale (two FMAs,
+// log2 e in two words) and the decay one float32 product per token; the
+// carries between sub-chunks keep the exact decay powers.  (The float32 path keeps the
+// exact key split and the two-term decay of the time-split kernel.)
+// Barriers fence LDS only (lds_sync_lgkm): the staged copies and the output
+// stores stay in flight across them.
+template <int L, int W>
+struct FwdStage {
+    uint16_t x[W][2][L][64];  // [wave][k, v][token][channel]
+};
+
+template <int W>
+struct TileShared {
+    float sa[W][64], sb[W][64];  // wave summaries
+    int ss[W][64];
+    float xa[W][64], xb[W][64];  // wave carry-ins
+    int xs[W][64];
+};
+
+template <int L>
+struct TileWork {
+    float N[L], D[L];
+    St st;   // summary of the sub-chunk from the empty state
+    int sl;  // fixed local scale
+    bool fast_local;
+
+    // kv: k in the low, v in the high half of each word (bf16 bits)
+    __device__ __forceinline__ void local(const uint32_t (&kv)[L], const FwdGeo& g, const Chan& ch, float eu,
+                                          float d, bool lane_ok) {
+        float kmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < L; ++j) kmax = fmaxf(kmax, __uint_as_float(kv[j] << 16));
+        sl = key_split(kmax).n;
+        fast_local = __all(lane_ok & (kmax * kL2E < kNMax));
+        if (fast_local) {
+            const float slf = static_cast<float>(sl);
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                const float kj = __uint_as_float(kv[j] << 16);
+                const float vj = __uint_as_float(kv[j] & 0xffff0000u);
+                const float e = ex2(fmaf(kj, kL2E_lo, fmaf(kj, kL2E, -slf)));
+                const float E = e * eu;
+                N[j] = fmaf(E, vj, a);
+                D[j] = b + E;
+                a = fmaf(d, a, e * vj);
+                b = fmaf(d, b, e);
+            }
+            st = St{a, b, sl};
+            fast_local = __all(b >= kTiny);
+        }
+        if (!fast_local) {  // general pass 1, reading one token at a time (rare: kept register-light)
+            st = empty_state();
+#pragma unroll 1
+            for (int j = 0; j < L; ++j) {
+                const float e = key_weight(st, key_split(BufLd<uint16_t>::at(g.rk, g.vin, j * g.row_in)));
+                token_add(st, e, BufLd<uint16_t>::at(g.rv, g.vin, j * g.row_in), ch);
+            }
+        }
+    }
+
+    // Outputs (and the saved state at the sub-chunk's start) from the carry-in X.
+    template <bool Gated>
+    __device__ __forceinline__ void outputs(const St& X, const FwdGeo& g, const Chunk1<uint16_t, L>& rch,
+                                            const Chan& ch, float eu, bool fast, bool want_y, int64_t C) const {
+        static_assert(L == kCkptLen, "one saved state per sub-chunk");
+        const int lvl = X.s - sl + __builtin_amdgcn_frexp_expf(X.b);
+        const bool dp_normal = ipow<L - 1>(ch.dd) >= 0x1p-125;  // see SubWork::outputs
+        const bool carry_fits =
+            !(X.b > 0.f) | ((lvl <= kCarryAbove) & (X.s - sl + __builtin_amdgcn_frexp_expf(X.a) <= kCarryAbove + 20) &
+                            (dp_normal | (lvl <= 24)));
+        bool fast_out = fast_local && __all(carry_fits);
+        if (fast_out && want_y)
+            fast_out = __all(corrected_outputs<Gated>(X, sl, N, D, rch, ch, g.ry, g.vout, g.row_out) >= kTiny);
+        if (fast_out) {
+            if (g.ckp != nullptr) {
+                g.ckp[0] = X.a;
+                g.ckp[C] = X.b;
+                g.ckp[2 * C] = static_cast<float>(X.s);
+            }
+        } else if (fast) {  // general path: rewrites every output of the wave
+            general_outputs<true, Gated, uint16_t, L>(X, g.rk, g.rv, g.rr, g.vin, g.row_in, g.nvalid, ch, eu, g.ry,
+                                                      g.vout, g.row_out, g.ckp, C);
+        } else {
+            general_outputs<false, Gated, uint16_t, L>(X, g.rk, g.rv, g.rr, g.vin, g.row_in, g.nvalid, ch, eu,
+                                                       g.ry, g.vout, g.row_out, g.ckp, C);
+        }
+    }
+};
+
+template <int L, int W, bool Gated>
+__global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
+    __shared__ TileShared<W> sm;
+    __shared__ FwdStage<L, W> stage;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tile = blockIdx.x;
+    const int64_t b = tile / P.nct;
+    const int64_t c0 = (tile - b * P.nct) * 64;
+    const int64_t c = c0 + lane;
+    const bool cok = c < P.C;
+    const float wc = cok ? P.w[c] : 0.f;
+    const float uc = cok ? P.u[c] : 0.f;
+    const Chan ch = make_chan(wc, uc);
+    const bool lane_ok = (wc >= 0.f) & (fabsf(uc) <= kFastU);
+    const bool fast = __all(lane_ok);
+    const float eu = ex2(ch.u2);
+    const float d = static_cast<float>(ch.dd);
+    const double dL = ipow<L>(ch.dd);
+
+    // the scanning wave's running carry, in float64: the state before the current block
+    StD E = to_d(empty_state());
+    if (wave == W - 1 && P.a_in != nullptr && cok) {
+        const int64_t i = b * P.C + c;
+        E = to_d(state_from_abp(P.a_in[i], P.b_in[i], P.p_in[i]));
+    }
+
+    {
+        const FwdGeo g0 = fwd_geo<uint16_t, L, W>(P, b, c, cok, 0, wave);
+        stage_rows<uint16_t, L>(g0.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
+        stage_rows<uint16_t, L>(g0.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
+    }
+    for (int64_t blk = 0; blk < P.nblocks; ++blk) {
+        const FwdGeo g = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk, wave);
+        uint32_t kv[L];
+        wait_staged();
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+            kv[j] = static_cast<uint32_t>(stage.x[wave][0][j][lane]) |
+                    (static_cast<uint32_t>(stage.x[wave][1][j][lane]) << 16);
+        wait_lds_reads();
+        if (blk + 1 < P.nblocks) {
+            const FwdGeo gn = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk + 1, wave);
+            stage_rows<uint16_t, L>(gn.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
+            stage_rows<uint16_t, L>(gn.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
+        }
+        TileWork<L> tw;
+        tw.local(kv, g, ch, eu, d, lane_ok);
+        Chunk1<uint16_t, L> rch;  // the gate's inputs, read from global memory
+        if (Gated) rch.load(g.rr, g.vin, g.row_in);
+        sm.sa[wave][lane] = tw.st.a;
+        sm.sb[wave][lane] = tw.st.b;
+        sm.ss[wave][lane] = tw.st.s;
+        lds_sync_lgkm();
+        if (wave == W - 1) {
+            StD X = E;
+#pragma unroll 1
+            for (int i = 0; i < W; ++i) {
+                const St xf = to_f(X);
+                sm.xa[i][lane] = xf.a;
+                sm.xb[i][lane] = xf.b;
+                sm.xs[i][lane] = xf.s;
+                X = combine_d(X, St{sm.sa[i][lane], sm.sb[i][lane], sm.ss[i][lane]}, dL);
+            }
+            E = X;
+        }
+        lds_sync_lgkm();
+        const St Xw{sm.xa[wave][lane], sm.xb[wave][lane], sm.xs[wave][lane]};
+        tw.template outputs<Gated>(Xw, g, rch, ch, eu, fast, P.y != nullptr, P.C);
+        if (P.a_out != nullptr && g.nvalid > 0 && blk * (int64_t)(L * W) + (int64_t)wave * L + g.nvalid == P.T) {
+            St st = Xw;
+            if (g.nvalid == L) {
+                st = combine(Xw, tw.st, dL);
+            } else {
+#pragma unroll 1
+                for (int j = 0; j < g.nvalid; ++j) {
+                    const float e = key_weight(st, key_split(BufLd<uint16_t>::at(g.rk, g.vin, j * g.row_in)));
+                    token_add(st, e, BufLd<uint16_t>::at(g.rv, g.vin, j * g.row_in), ch);
+                }
+            }
+            if (cok) {
+                const int64_t i = b * P.C + c;
+                state_to_abp(st, P.a_out[i], P.b_out[i], P.p_out[i]);
+            }
+        }
+    }
+}
+
 // T == 0: the state after the (empty) sequence is the state before it.
 __global__ void state_passthrough_kernel(int64_t n, const float* a_in, const float* b_in, const float* p_in,
                                          float* a_out, float* b_out, float* p_out) {
@@ -433,7 +645,15 @@ namespace {
 #endif
 constexpr int kFwdL = WKV_FWD_L;  // tokens per wave (sub-chunk)
 constexpr int kFwdW = WKV_FWD_W;  // waves per workgroup
-static_assert(kFwdL % kCkptLen == 0, "sub-chunks must start on saved-state boundaries");
+#ifndef WKV_FWD_TILE_L
+#define WKV_FWD_TILE_L 16
+#endif
+#ifndef WKV_FWD_TILE_W
+#define WKV_FWD_TILE_W 8
+#endif
+constexpr int kTileL = WKV_FWD_TILE_L;  // whole-tile kernel: tokens per wave
+constexpr int kTileW = WKV_FWD_TILE_W;  // whole-tile kernel: waves per workgroup
+static_assert(kFwdL % kCkptLen == 0 && kTileL % kCkptLen == 0, "sub-chunks must start on saved-state boundaries");
 
 struct FwdLayout {
     int64_t nct, ntiles, nblocks;
@@ -455,6 +675,10 @@ FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C) {
 
 size_t fwd_chunk_workspace_bytes(int64_t B, int64_t T, int64_t C) { return fwd_layout(B, T, C).bytes; }
 
+#ifndef WKV_FWD_TILE
+#define WKV_FWD_TILE 1  // whole-tile forward where there are enough tiles
+#endif
+
 template <typename TIn>
 hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     const FwdLayout l = fwd_layout(a.B, a.T, a.C);
@@ -468,6 +692,26 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     P.a_in = a.a_in; P.b_in = a.b_in; P.p_in = a.p_in;
     P.a_out = a.a_out; P.b_out = a.b_out; P.p_out = a.p_out;
 
+    // Enough tiles to give every CU two workgroups, and rows of whole 16-byte
+    // chunks for the LDS staging: one workgroup per tile walks the sequence.
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    (void)a16;
+    if constexpr (sizeof(TIn) == 2) {
+        if (WKV_FWD_TILE && l.ntiles >= 2 * static_cast<int64_t>(ncu) && a.C % 8 == 0 && a16(a.k) && a16(a.v)) {
+            P.nblocks = (a.T + kTileL * kTileW - 1) / (kTileL * kTileW);
+            const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * kTileW);
+            if (P.r != nullptr)
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, true>), grid, block, 0, stream, P);
+            else
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, false>), grid, block, 0, stream, P);
+            return hipGetLastError();
+        }
+    }
+
     if (l.nblocks > 1) {
         char* ws = static_cast<char*>(a.ws);
         P.counter = reinterpret_cast<uint32_t*>(ws);
@@ -479,7 +723,7 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
         if (g > 4096) g = 4096;
         hipLaunchKernelGGL(fwd_chunk_init_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream,
                            P.counter, reinterpret_cast<uint32_t*>(P.carry), nwords);
-        const hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t grid = l.ntiles * l.nblocks;

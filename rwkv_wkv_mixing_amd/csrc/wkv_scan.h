@@ -15,22 +15,63 @@
 namespace wkv {
 
 // Combine a state X (at the start of an n-token interval) with the summary S
-// of that interval; D = d^n in double, applied as a float32 hi + lo product.
-// The result keeps X's scale unless the summary would not fit (lazy
+// of that interval; D = d^n in double.  D is split into its mantissa, applied
+// as a float32 hi + lo product, and its binary exponent, which joins X's
+// integer scale: a decay far below float32's normal range (fast channels over
+// many tokens) keeps full precision instead of passing through a denormal.
+// The result keeps that scale unless the summary would not fit (lazy
 // rescale).  Scales are integers, so bringing both terms to the common scale
 // is exact and the only roundings are the decay product and the final sums.
 __device__ __forceinline__ St combine(const St& X, const St& S, double D) {
-    const float Dhi = static_cast<float>(D);
-    const float Dlo = static_cast<float>(D - static_cast<double>(Dhi));
+    const double Dm = __builtin_amdgcn_frexp_mant(D);  // D = Dm 2^De, Dm in [0.5, 1) (0 for D = 0)
+    const int De = __builtin_amdgcn_frexp_exp(D);
+    const float Dhi = static_cast<float>(Dm);
+    const float Dlo = static_cast<float>(Dm - static_cast<double>(Dhi));
     const float xa = fmaf(Dhi, X.a, Dlo * X.a);
     const float xb = fmaf(Dhi, X.b, Dlo * X.b);
-    if (!(S.b > 0.f)) return St{xa, xb, X.s};
+    const int xs = X.s + De;
+    if (!(S.b > 0.f)) return St{xa, xb, xs};
     if (!(xb > 0.f)) return S;
-    int sn = X.s;
+    int sn = xs;
     const int ls = S.s + __builtin_amdgcn_frexp_expf(S.b);  // S.b 2^S.s < 2^ls
-    if ((ls > X.s + static_cast<int>(kBig)) | (xb < kLo) | (xb > kHi))
-        sn = max(X.s + __builtin_amdgcn_frexp_expf(xb), ls);
-    return St{ldx(xa, X.s - sn) + ldx(S.a, S.s - sn), ldx(xb, X.s - sn) + ldx(S.b, S.s - sn), sn};
+    if ((ls > xs + static_cast<int>(kBig)) | (xb < kLo) | (xb > kHi))
+        sn = max(xs + __builtin_amdgcn_frexp_expf(xb), ls);
+    return St{ldx(xa, xs - sn) + ldx(S.a, S.s - sn), ldx(xb, xs - sn) + ldx(S.b, S.s - sn), sn};
+}
+
+// A carried state in float64, (a, b) at the integer scale s, for a running
+// carry that passes many combines: each combine in float32 rounds the carry
+// twice, and along a slowly decaying channel those roundings compound into the
+// saved states (a few 1e-7 relative after a few dozen combines), which the
+// backward's gradient sums of many terms then pick up.  In float64 the carry
+// is rounded to float32 once, where it is used.
+struct StD {
+    double a, b;
+    int s;
+};
+
+__device__ __forceinline__ StD to_d(const St& x) { return StD{x.a, x.b, x.s}; }
+__device__ __forceinline__ St to_f(const StD& x) {
+    return St{static_cast<float>(x.a), static_cast<float>(x.b), x.s};
+}
+
+// X d^n + S with X in float64 (D = d^n); the result is renormalised to
+// b in [0.5, 1) so that neither sum can leave float64's range.
+__device__ __forceinline__ StD combine_d(const StD& X, const St& S, double D) {
+    const double xa = X.a * D, xb = X.b * D;
+    if (!(S.b > 0.f)) {
+        if (!(xb > 0.0)) return StD{0.0, 0.0, kSEmpty};
+        const int e = __builtin_amdgcn_frexp_exp(xb);
+        return StD{ldexp(xa, -e), ldexp(xb, -e), X.s + e};
+    }
+    if (!(xb > 0.0)) {
+        const int e = __builtin_amdgcn_frexp_expf(S.b);
+        return StD{ldexp(static_cast<double>(S.a), -e), ldexp(static_cast<double>(S.b), -e), S.s + e};
+    }
+    const int sn = max(X.s + __builtin_amdgcn_frexp_exp(xb), S.s + __builtin_amdgcn_frexp_expf(S.b));
+    const double a = ldexp(xa, X.s - sn) + ldexp(static_cast<double>(S.a), S.s - sn);
+    const double b = ldexp(xb, X.s - sn) + ldexp(static_cast<double>(S.b), S.s - sn);
+    return StD{a, b, sn};
 }
 
 // ---- the decode-step state (a, b, p), A = a e^p, B = b e^p ---------------------
@@ -68,6 +109,18 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// LDS barrier that waits only on this wave's LDS operations (lgkmcnt).  A
+// workgroup fence on LDS also waits for every asynchronous buffer -> LDS copy
+// in flight (vmcnt), since those write LDS too; in the staged kernels each
+// wave copies rows that only it reads (after its own wait), so their barriers
+// need not wait for the copies, which then stay in flight across them.  The
+// memory clobbers keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_sync_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // ---- carries between workgroups --------------------------------------------------

@@ -51,13 +51,14 @@ __device__ __forceinline__ float step_lane(const StepChan& ch, float k, float v,
     }
     // output from the state before the token; z = log weight of the token
     const float z = x + ch.u;
-    const float ez = ex2(-fabsf(z) * kL2E);
+    const float az = fabsf(z);
+    const float ez = ex2(-fmaf(az, kL2E, az * kL2E_lo));
     const bool zp = z > 0.f;
     const float co = zp ? ez : 1.f;
     const float cn = zp ? 1.f : ez;
     const float y = fmaf(a, co, cn * v) * rcp(fmaf(b, co, cn));
     // decay-and-add
-    const float e = ex2(x * kL2E);
+    const float e = ex2(fmaf(x, kL2E, x * kL2E_lo));
     a = fmaf(ch.dhi, a, fmaf(ch.dlo, a, e * v));
     b = fmaf(ch.dhi, b, fmaf(ch.dlo, b, e));
     return y;

@@ -130,6 +130,30 @@ def test_extreme_inputs():
     check_bwd(p, run_bwd(p))
 
 
+@pytest.mark.parametrize("C", [64, None])
+def test_fast_decay_after_key_spike(C):
+    """A key spike of 90-100 followed by a fast decay: decays over a wave's span
+    (d^16, d^32) that fall below float32's normal range while the decayed spike
+    still dominates later outputs.  w spans 2.5-8 per token; the spikes sit at
+    every offset inside a span.  C = 64 takes the time-split kernel; C = 64 ncu +
+    24 (bf16, enough tiles) the whole-tile one.  Stress bound."""
+    if C is None:
+        C = 64 * torch.cuda.get_device_properties(0).multi_processor_count + 24
+    dtype = "f32" if C == 64 else "bf16"
+    p = W.make_problem(1 if C == 64 else 2, 640, C, dtype=dtype, seed=31, name=f"fast decay spikes C={C}")
+    p.w[:] = np.linspace(2.5, 8.0, C).astype(np.float32)
+    spk = np.zeros(p.k.shape, bool)
+    for i in range(0, 640, 37):  # one spike every 37 tokens, at every offset mod 16 and 32
+        spk[:, i, :] = True
+    p.k = np.where(spk, np.float32(96.0) + (np.arange(C) % 5).astype(np.float32), p.k).astype(np.float32)
+    if dtype == "bf16":
+        from rwkv_wkv_mixing_amd.workloads import bf16_round
+
+        p.k_bits, p.k = bf16_round(p.k)
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p), stress=True)
+
+
 def test_zero_length_sequences():
     O = ops()
     w = torch.ones(5, device=DEV)
