@@ -164,8 +164,8 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state
             s["gout"] = s["gy"]
             s["out"] = s["out"] + (torch.empty((B, T, C), dtype=torch.float32, device=dev),)
         sets.append(s)
-    ws_f = torch.empty(max(1, ops.workspace_bytes(0, B, T, C, base["k"].dtype)), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(1, ops.workspace_bytes(1, B, T, C, base["k"].dtype)), dtype=torch.uint8, device=dev)
+    ws_f = ops.new_workspace(0, B, T, C, base["k"].dtype, dev)
+    ws_b = ops.new_workspace(1, B, T, C, base["k"].dtype, dev)
 
     def step(i, ev=None):
         s = sets[i % len(sets)]

@@ -29,10 +29,19 @@
  *    No call allocates, synchronises or enqueues a memset or copy node, so
  *    the calls may be captured in a HIP graph and replayed (the scratch they
  *    clear is cleared by kernels).
- *  - The library allocates no device memory and keeps no global state:
- *    scratch memory is the caller's `workspace`, sized by
- *    wkv_workspace_bytes().  Calls on disjoint buffers are thread-safe.
- *    Two calls that share a workspace must be ordered (same stream).
+ *  - The library allocates no device memory and keeps no global state
+ *    (apart from the test hook wkv_debug_spin_limit): scratch memory is the
+ *    caller's `workspace`, sized by wkv_workspace_bytes().  Calls on disjoint
+ *    buffers are thread-safe.  Two calls that share a workspace must be
+ *    ordered (same stream).
+ *  - A wkv_forward / wkv_backward workspace must hold zeros before its FIRST
+ *    call (hipMemset once after allocating it, or torch.zeros), and the
+ *    caller must not write it between calls.  Every call leaves it ready for
+ *    the next: its counters back at zero, its generation advanced (the
+ *    carries between workgroups are tagged with the call's generation instead
+ *    of being cleared on every call, which would take a kernel of its own).
+ *    The first 16 bytes are a header; bytes 4..7 are an error word that the
+ *    calls only ever set: read it with wkv_workspace_status().
  *  - Status codes: nothing aborts and no exception crosses the ABI.
  *    WKV_EINVAL    a dimension < 0, or a NULL pointer where data is needed;
  *    WKV_EDTYPE    unknown input dtype or op;
@@ -42,15 +51,26 @@
  *    WKV_EWORKSPACE workspace NULL or smaller than wkv_workspace_bytes();
  *    WKV_EHIP      a HIP launch or query failed (wkv_last_hip_error() has
  *                  the HIP message of the last such failure on this thread).
+ *    WKV_ETIMEOUT  returned by wkv_workspace_status() only: a wait between
+ *                  workgroups gave up since the word was last cleared, so
+ *                  the outputs of the call(s) since then are invalid.
  *    A call with B, T, C (or L) equal to 0 is a no-op returning WKV_OK,
  *    except that wkv_backward with C > 0 and B*T == 0 sets dw = du = 0.
  *  - Numerics: float32 arithmetic on states (a, b) with an integer log2
- *    scale s (A = a 2^s, B = b 2^s).  Each key weight is split once as
- *    e^k = em 2^n (n an integer), so a token's weight has the same float32
- *    value in every pass and kernel, and changes of scale are exact.  The
- *    decay e^{-w} is applied as a two-term (hi + lo) product so that no
- *    systematic rounding of the decay builds up over long sequences.  The
- *    backward keeps its reverse running sums in float64.  Results are
+ *    scale s (A = a 2^s, B = b 2^s), so changes of scale are exact; k log2 e
+ *    is formed with log2 e in two float32 words.  Carries between sub-chunks
+ *    use float64 decay powers d^n, split into mantissa and binary exponent.
+ *    With float32 inputs, and in the backward, each key weight is split once
+ *    as e^k = em 2^n (n an integer) and the decay e^{-w} is applied per token
+ *    as a two-term (hi + lo) product, so that no systematic rounding of the
+ *    decay builds up over long sequences.  The bf16-input forward at shapes
+ *    with two or more 64-channel tiles per CU (one workgroup per tile) weighs
+ *    keys by one exp2 at its sub-chunk's scale, decays within a 16-token
+ *    sub-chunk by a float32 product, and carries the state between sub-chunks
+ *    in float64 (its saved states are rounded to float32 once).  The
+ *    backward keeps its per-token reverse running sums in float32 (float64
+ *    when the library is built with WKV_BWD_ACC_F64=1) and composes its span
+ *    maps and the carries between workgroups in float64.  Results are
  *    finite for finite inputs with w >= 0, |u| <= 80, |v| < 2^60 and
  *    |k| < 2.9e6; outside that range the math is still defined but may
  *    overflow.  NaN/Inf inputs propagate.  For decay rates w below ~1e-5
@@ -77,7 +97,8 @@ enum {
     WKV_ESIZE = 3,
     WKV_EALIGN = 4,
     WKV_EWORKSPACE = 5,
-    WKV_EHIP = 6
+    WKV_EHIP = 6,
+    WKV_ETIMEOUT = 7
 };
 
 /* dtype of the INPUT sequences k, v, gy. */
@@ -117,7 +138,8 @@ size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C);
  *           the state at the start of each WKV_CKPT_LEN-token block, for a
  *           later wkv_backward on the same inputs.
  * workspace wkv_workspace_bytes(WKV_OP_FORWARD, ...) bytes (may be NULL if
- *           that is 0).  Contents on entry are ignored.
+ *           that is 0), 256-byte aligned, zero-filled before its first call
+ *           (see the conventions above).
  */
 wkv_status_t wkv_forward(int64_t B, int64_t T, int64_t C, int in_dtype,
                          const float* w, const float* u, const void* k, const void* v,
@@ -464,6 +486,35 @@ wkv_status_t wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M
 wkv_status_t wkv_step(int64_t L, int64_t B, int64_t C, int in_dtype,
                       const float* w, const float* u, const void* k, const void* v,
                       float* y, float* a, float* b, float* p, void* hip_stream);
+
+/*
+ * wkv_workspace_status - the error word of a wkv_forward / wkv_backward
+ * (or the gated calls') workspace.
+ *
+ * Where a call splits a sequence over workgroups chained in time (few 64-channel
+ * tiles: B*C small next to the GPU, or float32 inputs), each workgroup waits for
+ * its predecessor's carry.  A wait is bounded: after wkv_debug_spin_limit()
+ * polls (default 2^22, about a second) it gives up so that every kernel ends,
+ * and sets the error word in the workspace header.  A workspace that was not
+ * zero-filled before its first call sets it too.  The word is sticky.
+ *
+ * Synchronises hip_stream, then reads the word (a 4-byte device-to-host copy;
+ * not for use inside HIP graph capture).  Returns WKV_OK if it is clear,
+ * WKV_ETIMEOUT if it is set (the outputs written since it was last cleared
+ * are invalid), and clears it when `clear` is nonzero.  WKV_EINVAL for a NULL
+ * workspace, WKV_EWORKSPACE for fewer than 8 bytes or a workspace not
+ * 256-byte aligned, WKV_EHIP if the copy fails.
+ */
+wkv_status_t wkv_workspace_status(const void* workspace, size_t workspace_bytes, int clear, void* hip_stream);
+
+/*
+ * wkv_debug_spin_limit - test hook: sets the number of polls after which a
+ * wait between workgroups gives up (process-wide; applies to calls launched
+ * afterwards) and returns the previous value.  0 makes every such wait give up
+ * at once, so a test can check that the error word is set and reported while
+ * every kernel still runs to its end.  Not for production use.
+ */
+uint32_t wkv_debug_spin_limit(uint32_t polls);
 
 /* Static description of a status code. */
 const char* wkv_status_str(wkv_status_t s);

@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librwkv_wkv.so")
 
-WKV_OK, WKV_EINVAL, WKV_EDTYPE, WKV_ESIZE, WKV_EALIGN, WKV_EWORKSPACE, WKV_EHIP = range(7)
+WKV_OK, WKV_EINVAL, WKV_EDTYPE, WKV_ESIZE, WKV_EALIGN, WKV_EWORKSPACE, WKV_EHIP, WKV_ETIMEOUT = range(8)
 WKV_F32, WKV_BF16 = 0, 1
 WKV_OP_FORWARD, WKV_OP_BACKWARD = 0, 1
 WKV_CKPT_LEN = 16
@@ -39,6 +39,8 @@ EXPORTS = (
     "wkv_token_shift_workspace_bytes",
     "wkv_token_shift",
     "wkv_token_shift_backward",
+    "wkv_workspace_status",
+    "wkv_debug_spin_limit",
     "wkv_status_str",
     "wkv_last_hip_error",
     "wkv_version",
@@ -117,6 +119,10 @@ def declare(L):
     L.wkv_token_shift.argtypes = [i64, i64, i64, i64, i32, fp, vp, vp, vp, vp]
     L.wkv_token_shift_backward.restype = i32
     L.wkv_token_shift_backward.argtypes = [i64, i64, i64, i64, i32, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
+    L.wkv_workspace_status.restype = i32
+    L.wkv_workspace_status.argtypes = [vp, sz, i32, vp]
+    L.wkv_debug_spin_limit.restype = ctypes.c_uint32
+    L.wkv_debug_spin_limit.argtypes = [ctypes.c_uint32]
     L.wkv_status_str.restype = ctypes.c_char_p
     L.wkv_status_str.argtypes = [i32]
     L.wkv_last_hip_error.restype = ctypes.c_char_p

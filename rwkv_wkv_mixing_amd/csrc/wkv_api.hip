@@ -4,10 +4,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "wkv.h"
 #include "wkv_launch.h"
 
 namespace {
+
+std::atomic<uint32_t> g_spin_limit{1u << 22};
 
 thread_local char g_hip_msg[256] = "";
 
@@ -53,6 +57,7 @@ Plan plan(int op, int64_t B, int64_t T, int64_t C, int dt) {
     p.nblk = (T + wkv::kCkptLen - 1) / wkv::kCkptLen;
     if (op == WKV_OP_BACKWARD && p.N > 0) p.ws_bytes = wkv::bwd_chunk_workspace_bytes(B, T, C);
     if (op == WKV_OP_FORWARD && p.N > 0) p.ws_bytes = wkv::fwd_chunk_workspace_bytes(B, T, C);
+    if (p.ws_bytes == SIZE_MAX) return Plan{WKV_ESIZE, 0, 0, 0};
     return p;
 }
 
@@ -85,6 +90,8 @@ __global__ void zero2_kernel(int64_t n, float* a, float* b) {
 }
 
 }  // namespace
+
+uint32_t wkv::spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
 
 extern "C" {
 
@@ -593,9 +600,30 @@ const char* wkv_status_str(wkv_status_t s) {
         case WKV_EALIGN: return "pointer not aligned to its element size";
         case WKV_EWORKSPACE: return "workspace missing or too small";
         case WKV_EHIP: return "HIP launch failed";
+        case WKV_ETIMEOUT: return "a wait between workgroups gave up (outputs invalid), or the workspace was not "
+                                  "zero-filled before its first use";
         default: return "unknown status";
     }
 }
+
+wkv_status_t wkv_workspace_status(const void* workspace, size_t workspace_bytes, int clear, void* hip_stream) {
+    if (!workspace) return WKV_EINVAL;
+    if (workspace_bytes < 8 || !aligned(workspace, 256)) return WKV_EWORKSPACE;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const char* err = static_cast<const char*>(workspace) + offsetof(wkv::CallHdrLayout, error);
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, err, sizeof(word), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e == hipSuccess && clear && word != 0u) {
+        const uint32_t zero = 0u;
+        e = hipMemcpyAsync(const_cast<char*>(err), &zero, sizeof(zero), hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    }
+    if (e != hipSuccess) return hip_status(e);
+    return word == 0u ? WKV_OK : WKV_ETIMEOUT;
+}
+
+uint32_t wkv_debug_spin_limit(uint32_t polls) { return g_spin_limit.exchange(polls, std::memory_order_relaxed); }
 
 const char* wkv_last_hip_error(void) { return g_hip_msg; }
 

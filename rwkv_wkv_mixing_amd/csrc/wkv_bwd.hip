@@ -54,8 +54,12 @@ struct BwdChunk {
     const float* ckpt;
     int64_t nblk_ck;
     int64_t nct, ntiles, nblocks;
-    uint32_t* counter;
-    uint32_t* error;
+    CallHdr* hdr;          // workspace header: tickets, error word, generation (time-split kernel)
+    uint32_t spin;         // polls before a carry wait gives up
+    uint32_t* ct_count;    // [nct] workgroups of each channel tile that have stored their partials
+    int64_t npb;           // partial rows per tile: time blocks (time-split kernel) or 1 (whole-tile)
+    float* dw;             // [C] outputs, written by the last workgroup of each channel tile
+    float* du;
     float* carry;          // [ntiles][nblocks][64][12]: G, J, G', J' as hi/lo pairs, scale, 3 status words
     uint32_t carry_bytes;
     float* part;           // [ntiles][nblocks][2][64]: dw, du partial sums
@@ -131,8 +135,8 @@ __device__ __forceinline__ double join(float hi, float lo) {
 
 constexpr uint32_t kCarrySlot = 48;
 
-__device__ __forceinline__ void publish_carry(Rsrc r, uint32_t off, const RCarry& c) {
-    const float one = __uint_as_float(1u);
+__device__ __forceinline__ void publish_carry(Rsrc r, uint32_t off, const RCarry& c, uint32_t tag) {
+    const float one = __uint_as_float(tag);
     const f32x4 v0 = {hi_of(c.G), lo_of(c.G), hi_of(c.J), one};
     const f32x4 v1 = {lo_of(c.J), hi_of(c.Gp), lo_of(c.Gp), one};
     const f32x4 v2 = {hi_of(c.Jp), lo_of(c.Jp), __int_as_float(c.sg), one};
@@ -141,17 +145,17 @@ __device__ __forceinline__ void publish_carry(Rsrc r, uint32_t off, const RCarry
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v2), r, off + 32, 0, kCoherent);
 }
 
-__device__ __forceinline__ RCarry wait_carry(Rsrc r, uint32_t off, uint32_t* error) {
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+__device__ __forceinline__ RCarry wait_carry(Rsrc r, uint32_t off, uint32_t tag, uint32_t spin, CallHdr* h) {
+    for (uint32_t it = 0; it < spin; ++it) {
         const f32x4 v0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
         const f32x4 v1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kCoherent));
         const f32x4 v2 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 32, 0, kCoherent));
-        if ((__float_as_uint(v0.w) != 0u) & (__float_as_uint(v1.w) != 0u) & (__float_as_uint(v2.w) != 0u))
+        if ((__float_as_uint(v0.w) == tag) & (__float_as_uint(v1.w) == tag) & (__float_as_uint(v2.w) == tag))
             return RCarry{join(v0.x, v0.y), join(v0.z, v1.x), join(v1.y, v1.z), join(v2.x, v2.y),
                           __float_as_int(v2.z)};
         __builtin_amdgcn_s_sleep(1);
     }
-    __hip_atomic_store(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    hdr_flag(h, kErrWait);
     return RCarry{0.0, 0.0, 0.0, 0.0, 0};
 }
 
@@ -553,7 +557,7 @@ struct BwdShared {
     double cin[4][64];      // carry at the block's end
     int cin_s[64];
     float red[W][2][64];
-    uint32_t ticket;
+    uint32_t ticket, tag;
 };
 
 template <int W, typename TIn, int L, bool Gated>
@@ -581,24 +585,72 @@ __device__ __forceinline__ RMap get_map(const BwdShared<W>& sm, int i, int lane,
     return r;
 }
 
-// dw, du of a workgroup: fixed-order sum over its waves into part[slot].
+// dw, du of a workgroup: fixed-order sum over its waves into part[slot], then
+// the fold over the channel tile's workgroups.  Each of the `rows` workgroups
+// of channel tile ct stores its partials with system-coherent stores, waits
+// for them to complete, then counts itself in ct_count[ct]; the one that
+// counts last sums the tile's partials in the fixed order (batch row, time
+// block) with coherent loads, writes dw and du, and returns the count to zero
+// (so a workspace needs zeros before its first call only).  The order of the
+// sum does not depend on which workgroup finishes last: results are bitwise
+// reproducible.
 template <int W>
-__device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P, int64_t slot, int wave, int lane,
-                                             float ndw, float du) {
+__device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P, int64_t b, int64_t ct,
+                                             int64_t blk, int wave, int lane, float ndw, float du) {
     sm.red[wave][0][lane] = -ndw;
     sm.red[wave][1][lane] = du;
     lds_sync();
-    if (wave == 0) {
-        float sw = 0.f, su = 0.f;
+    if (wave != 0) return;
+    float sw = 0.f, su = 0.f;
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
-            sw += sm.red[i][0][lane];
-            su += sm.red[i][1][lane];
-        }
-        float* pp = P.part + slot * 2 * 64 + lane;
-        pp[0] = sw;
-        pp[64] = su;
+    for (int i = 0; i < W; ++i) {
+        sw += sm.red[i][0][lane];
+        su += sm.red[i][1][lane];
     }
+    const int64_t rows = P.B * P.npb;
+    const uint32_t row_bytes = 2 * 64 * 4;
+    const Rsrc rp = make_rsrc(P.part, static_cast<uint32_t>(P.ntiles * P.npb) * row_bytes);
+    auto row_off = [&](int64_t bb, int64_t j) {
+        return static_cast<uint32_t>(((bb * P.nct + ct) * P.npb + j) * row_bytes + lane * 4);
+    };
+    const uint32_t off = row_off(b, blk);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sw), rp, off, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(su), rp, off + 64 * 4, 0, kCoherent);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(P.ct_count + ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev + 1 != static_cast<uint32_t>(rows)) return;
+    // last of the tile's workgroups: fixed-order sum, 8 rows' loads in flight at a time
+    float tw = 0.f, tu = 0.f;
+    int64_t r = 0;
+    for (; r + 8 <= rows; r += 8) {
+        float w8[8], u8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t bb = (r + i) / P.npb, j = (r + i) - bb * P.npb;
+            const uint32_t o = row_off(bb, j);
+            w8[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, kCoherent));
+            u8[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o + 64 * 4, 0, kCoherent));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            tw += w8[i];
+            tu += u8[i];
+        }
+    }
+    for (; r < rows; ++r) {
+        const int64_t bb = r / P.npb, j = r - bb * P.npb;
+        const uint32_t o = row_off(bb, j);
+        tw += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, kCoherent));
+        tu += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o + 64 * 4, 0, kCoherent));
+    }
+    const int64_t c = ct * 64 + lane;
+    if (c < P.C) {
+        P.dw[c] = tw;
+        P.du[c] = tu;
+    }
+    if (lane == 0) __hip_atomic_store(P.ct_count + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Time-split backward: one workgroup per (tile, time block); blocks are
@@ -610,10 +662,19 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     int64_t ticket = blockIdx.x;
+    uint32_t tag = 0;
     if (P.nblocks > 1) {
-        if (threadIdx.x == 0) sm.ticket = atomicAdd(P.counter, 1u);
+        if (threadIdx.x == 0) {
+            sm.ticket = call_ticket(P.hdr, &sm.tag);
+            if (sm.ticket >= gridDim.x) hdr_flag(P.hdr, kErrTicket);  // a workspace not zeroed before first use
+        }
         __syncthreads();
         ticket = sm.ticket;
+        tag = sm.tag;
+        if (ticket >= gridDim.x) {  // uniform per workgroup: nothing to compute
+            if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
+            return;
+        }
     }
     const int64_t rblk = ticket / P.ntiles;  // blocks are handed out last-in-time first
     const int64_t tile = ticket - rblk * P.ntiles;
@@ -646,8 +707,8 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
         if (P.nblocks > 1) {
             const Rsrc rc = make_rsrc(P.carry, P.carry_bytes);
             const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * kCarrySlot);
-            if (blk < P.nblocks - 1) cin = wait_carry(rc, slot + 64 * kCarrySlot, P.error);  // block blk+1
-            if (blk > 0) publish_carry(rc, slot, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin));
+            if (blk < P.nblocks - 1) cin = wait_carry(rc, slot + 64 * kCarrySlot, tag, P.spin, P.hdr);  // block blk+1
+            if (blk > 0) publish_carry(rc, slot, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin), tag);
         }
         sm.cin[0][lane] = cin.G;
         sm.cin[1][lane] = cin.J;
@@ -659,7 +720,12 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     const RCarry C = rapply(suf, RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane],
                                         sm.cin_s[lane]});
     const float ndw = sp.reverse(C, g, ch, eu, dec, fast_out);
-    put_partials(sm, P, tile * P.nblocks + blk, wave, lane, ndw, sp.du);
+    const int64_t ct = tile - b * P.nct;
+    put_partials(sm, P, b, ct, blk, wave, lane, ndw, sp.du);
+    if (P.nblocks > 1) {  // every wave is past its carry traffic
+        __syncthreads();
+        if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
+    }
 }
 
 // Whole-tile backward: one workgroup walks all time blocks of its tile from
@@ -741,52 +807,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
         lds_sync_lgkm();
         cin = RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane], sm.cin_s[lane]};
     }
-    put_partials(sm, P, tile, wave, lane, ndw, du);
-}
-
-__global__ void bwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < 2) hdr[i] = 0u;
-    for (int64_t j = i; j < nwords; j += static_cast<int64_t>(gridDim.x) * blockDim.x) carry_words[j] = 0u;
-}
-
-// dw[c] = sum over batch rows and time blocks (in that fixed order) of the partials.
-__global__ void bwd_chunk_reduce_kernel(int64_t B, int64_t C, int64_t nct, int64_t nblocks,
-                                        const float* __restrict__ part, float* __restrict__ dw,
-                                        float* __restrict__ du) {
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (c >= C) return;
-    const int64_t ct = c / 64, lane = c % 64;
-    // rows in the order (b, j); the loads of 8 rows issue together, the sums
-    // keep that order (bitwise reproducible)
-    const int64_t nrow = B * nblocks;
-    auto at = [&](int64_t r) {
-        const int64_t b = r / nblocks, j = r - (r / nblocks) * nblocks;
-        return part + (((b * nct + ct) * nblocks + j) * 2) * 64 + lane;
-    };
-    float sw = 0.f, su = 0.f;
-    int64_t r = 0;
-    for (; r + 8 <= nrow; r += 8) {
-        float w8[8], u8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float* pp = at(r + i);
-            w8[i] = pp[0];
-            u8[i] = pp[64];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sw += w8[i];
-            su += u8[i];
-        }
-    }
-    for (; r < nrow; ++r) {
-        const float* pp = at(r);
-        sw += pp[0];
-        su += pp[64];
-    }
-    dw[c] = sw;
-    du[c] = su;
+    put_partials(sm, P, b, tile - b * P.nct, 0, wave, lane, ndw, du);
 }
 
 namespace {
@@ -809,7 +830,7 @@ static_assert(kBwdL % kCkptLen == 0, "backward spans must start on saved forward
 
 struct BwdLayout {
     int64_t nct, ntiles, nblocks, nblk_ck;
-    size_t off_carry, carry_bytes, off_part, off_ckpt, ckpt_bytes, off_fws, fws_bytes, bytes;
+    size_t off_ct, off_carry, carry_bytes, off_part, off_ckpt, ckpt_bytes, off_fws, fws_bytes, bytes;
 };
 
 BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C) {
@@ -819,7 +840,9 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C) {
     l.nblocks = (T + kBwdL * kBwdW - 1) / (kBwdL * kBwdW);
     l.nblk_ck = (T + kCkptLen - 1) / kCkptLen;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    size_t off = 256;
+    size_t off = 256;  // CallHdr
+    l.off_ct = off;    // per channel tile partial counts
+    off = up(off + static_cast<size_t>(l.nct) * 4);
     l.off_carry = off;
     l.carry_bytes = l.nblocks > 1 ? static_cast<size_t>(l.ntiles * l.nblocks * 64) * kCarrySlot : 0;
     off = up(off + l.carry_bytes);
@@ -831,6 +854,10 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C) {
     l.off_fws = off;
     l.fws_bytes = fwd_chunk_workspace_bytes(B, T, C);
     l.bytes = off + l.fws_bytes;
+    // carries and partials are addressed through 32-bit buffer resources
+    if (l.carry_bytes > 0xffffffffull || static_cast<size_t>(l.ntiles * l.nblocks) * 512 > 0xffffffffull ||
+        l.fws_bytes == SIZE_MAX)
+        l.bytes = SIZE_MAX;
     return l;
 }
 }  // namespace
@@ -859,6 +886,11 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     P.part = reinterpret_cast<float*>(ws + l.off_part);
     P.r = a.r;
     P.dr = a.dr;
+    P.ct_count = reinterpret_cast<uint32_t*>(ws + l.off_ct);
+    P.dw = a.dw;
+    P.du = a.du;
+    P.hdr = reinterpret_cast<CallHdr*>(ws);
+    P.spin = spin_limit();
 
     // Enough tiles to give every CU two workgroups: one workgroup per tile
     // walks the whole sequence (no carries between workgroups).
@@ -868,6 +900,7 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (l.ntiles >= 2 * static_cast<int64_t>(ncu)) {
         P.nblocks = (a.T + kBwdL * kBwdTileW - 1) / (kBwdL * kBwdTileW);
+        P.npb = 1;
         // the LDS-staged loads move 16-byte chunks: whole chunks per row, aligned
         const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
         const bool staged = WKV_BWD_STAGE && a.C % (16 / static_cast<int64_t>(sizeof(TIn))) == 0 && a16(a.k) &&
@@ -881,37 +914,19 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false, true>), grid, block, 0, stream, P);
         else
             hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false, false>), grid, block, 0, stream, P);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,
-                           stream, a.B, a.C, l.nct, int64_t{1}, P.part, a.dw, a.du);
         return hipGetLastError();
     }
 
     P.nblocks = l.nblocks;
-    P.counter = reinterpret_cast<uint32_t*>(ws);
-    P.error = P.counter + 1;
+    P.npb = l.nblocks;
     P.carry = reinterpret_cast<float*>(ws + l.off_carry);
     P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
-    if (l.nblocks > 1) {
-        const int64_t nwords = static_cast<int64_t>(l.carry_bytes / 4);
-        int64_t g = (nwords + 255) / 256;
-        if (g > 4096) g = 4096;
-        hipLaunchKernelGGL(bwd_chunk_init_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream,
-                           P.counter, reinterpret_cast<uint32_t*>(P.carry), nwords);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     if (P.r != nullptr)
         hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW, true>),
                            dim3(static_cast<unsigned>(l.ntiles * l.nblocks)), dim3(64 * kBwdW), 0, stream, P);
     else
         hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW, false>),
                            dim3(static_cast<unsigned>(l.ntiles * l.nblocks)), dim3(64 * kBwdW), 0, stream, P);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_chunk_reduce_kernel, dim3(static_cast<unsigned>((a.C + 255) / 256)), dim3(256), 0,
-                       stream, a.B, a.C, l.nct, l.nblocks, P.part, a.dw, a.du);
     return hipGetLastError();
 }
 

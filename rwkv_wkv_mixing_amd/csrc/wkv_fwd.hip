@@ -15,7 +15,8 @@
 //           the last wave also waits for the inclusive state E of the
 //           previous time block of the same tile (blocks are handed out by an
 //           atomic ticket in time order, so the awaited block is already
-//           running) and publishes this block's inclusive state
+//           running) and publishes this block's inclusive state, tagged with
+//           the call's generation (wkv_scan.h)
 //   output  with X = d^{iL} E + P_i the state before the sub-chunk,
 //           y_t = (N_t + d^j X_A) / (D_t + d^j X_B)  for its j-th token,
 //           and the saved block-start states for the backward.
@@ -46,9 +47,9 @@ struct FwdChunk {
     int64_t nct;       // channel tiles per batch row
     int64_t ntiles;    // B * nct
     int64_t nblocks;   // time blocks per tile
-    uint32_t* counter; // ticket counter (nblocks > 1)
-    uint32_t* error;   // set if a carry wait timed out
-    float* carry;      // [ntiles][nblocks][64][4] inclusive block states + status
+    CallHdr* hdr;      // workspace header: tickets, error word, generation (nblocks > 1)
+    uint32_t spin;     // polls before a carry wait gives up
+    float* carry;      // [ntiles][nblocks][64][4] inclusive block states + tag
     uint32_t carry_bytes;
     const void* r;      // receptance [B, T, C] (gated kernels only)
     const float* a_in;  // optional state before token 1, [B, C] each
@@ -301,7 +302,7 @@ struct FwdShared {
     int s[W][64];
     float ea[64], eb[64];  // block carry-in E
     int es[64];
-    uint32_t ticket;
+    uint32_t ticket, tag;
 };
 
 // Prefix of the summaries of waves 0..wave-1 of a block.
@@ -325,10 +326,19 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     int64_t ticket = blockIdx.x;
+    uint32_t tag = 0;
     if (P.nblocks > 1) {
-        if (threadIdx.x == 0) sm.ticket = atomicAdd(P.counter, 1u);
+        if (threadIdx.x == 0) {
+            sm.ticket = call_ticket(P.hdr, &sm.tag);
+            if (sm.ticket >= gridDim.x) hdr_flag(P.hdr, kErrTicket);  // a workspace not zeroed before first use
+        }
         __syncthreads();
         ticket = sm.ticket;
+        tag = sm.tag;
+        if (ticket >= gridDim.x) {  // uniform per workgroup: nothing to compute
+            if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
+            return;
+        }
     }
     const int64_t blk = ticket / P.ntiles;
     const int64_t tile = ticket - blk * P.ntiles;
@@ -377,9 +387,9 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
             for (int i = 0; i < W; ++i) dTB *= dL;
             const Rsrc rc = make_rsrc(P.carry, P.carry_bytes);
             const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * 16);
-            if (blk > 0) E = wait_state(rc, slot - 64 * 16, P.error);  // block blk-1, same lane
+            if (blk > 0) E = wait_state(rc, slot - 64 * 16, tag, P.spin, P.hdr);  // block blk-1, same lane
             if (blk < P.nblocks - 1)  // then this block is full
-                publish_state(rc, slot, combine(E, combine(pref, sw.st, dL), dTB));
+                publish_state(rc, slot, combine(E, combine(pref, sw.st, dL), dTB), tag);
         }
         sm.ea[lane] = E.a;
         sm.eb[lane] = E.b;
@@ -409,6 +419,10 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
             const int64_t i = b * P.C + c;
             state_to_abp(st, P.a_out[i], P.b_out[i], P.p_out[i]);
         }
+    }
+    if (P.nblocks > 1) {  // every wave is past its carry traffic
+        __syncthreads();
+        if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
     }
 }
 
@@ -630,12 +644,6 @@ __global__ void state_passthrough_kernel(int64_t n, const float* a_in, const flo
     p_out[i] = p;
 }
 
-__global__ void fwd_chunk_init_kernel(uint32_t* hdr, uint32_t* carry_words, int64_t nwords) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < 2) hdr[i] = 0u;
-    for (int64_t j = i; j < nwords; j += static_cast<int64_t>(gridDim.x) * blockDim.x) carry_words[j] = 0u;
-}
-
 namespace {
 #ifndef WKV_FWD_L
 #define WKV_FWD_L 32
@@ -666,9 +674,10 @@ FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C) {
     l.ntiles = B * l.nct;
     l.nblocks = (T + kFwdL * kFwdW - 1) / (kFwdL * kFwdW);
     if (l.nblocks <= 1) return l;  // no cross-workgroup carries, no workspace
-    l.off_carry = 256;
+    l.off_carry = 256;  // CallHdr
     l.carry_bytes = static_cast<size_t>(l.ntiles * l.nblocks * 64) * 16;
     l.bytes = l.off_carry + l.carry_bytes;
+    if (l.carry_bytes > 0xffffffffull) l.bytes = SIZE_MAX;  // carries are addressed through a 32-bit buffer resource
     return l;
 }
 }  // namespace
@@ -714,17 +723,10 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
 
     if (l.nblocks > 1) {
         char* ws = static_cast<char*>(a.ws);
-        P.counter = reinterpret_cast<uint32_t*>(ws);
-        P.error = P.counter + 1;
+        P.hdr = reinterpret_cast<CallHdr*>(ws);
+        P.spin = spin_limit();
         P.carry = reinterpret_cast<float*>(ws + l.off_carry);
         P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
-        const int64_t nwords = static_cast<int64_t>(l.carry_bytes / 4);
-        int64_t g = (nwords + 255) / 256;
-        if (g > 4096) g = 4096;
-        hipLaunchKernelGGL(fwd_chunk_init_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream,
-                           P.counter, reinterpret_cast<uint32_t*>(P.carry), nwords);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
     }
     const int64_t grid = l.ntiles * l.nblocks;
     if (P.r != nullptr)

@@ -10,6 +10,16 @@ namespace wkv {
 
 constexpr int64_t kCkptLen = 16;  // = WKV_CKPT_LEN in include/wkv.h
 
+// Polls a wait for a carry between workgroups makes before it gives up and
+// flags the workspace's error word (wkv_debug_spin_limit sets it; default 2^22).
+uint32_t spin_limit();
+
+// Header at the start of a wkv_forward / wkv_backward workspace (the device
+// code's CallHdr in wkv_scan.h has this layout).
+struct CallHdrLayout {
+    uint32_t ticket, error, done, gen;
+};
+
 struct FwdArgs {
     int64_t B, T, C;
     bool bf16;

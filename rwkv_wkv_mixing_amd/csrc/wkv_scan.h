@@ -10,7 +10,10 @@
 // associative).
 #pragma once
 
+#include <stddef.h>
+
 #include "wkv_device.h"
+#include "wkv_launch.h"
 
 namespace wkv {
 
@@ -126,36 +129,82 @@ __device__ __forceinline__ void lds_sync_lgkm() {
 // ---- carries between workgroups --------------------------------------------------
 // A chained scan along time: the workgroup of time block j waits for the
 // inclusive state of block j-1 of the same tile and publishes its own.  Each
-// (tile, block, lane) slot is 16 bytes (a, b, s bits, status) written with ONE
+// (tile, block, lane) slot is 16 bytes (a, b, s bits, tag) written with ONE
 // 16-byte store and polled with 16-byte loads, both with the system-coherent
 // cache policy (sc0 sc1), which bypasses the per-XCD L2s.  So no release or
 // acquire fence is needed: such fences would write back or invalidate the
 // whole L2 of the XCD on every exchange, which the bandwidth-bound stream of
-// outputs from the other workgroups cannot afford.  Status 0 means "not yet";
-// slots are zeroed by a small kernel before each launch.  Always taking block
-// j-1's state (never a look-back over several aggregates) keeps the rounding,
-// and therefore the result, independent of timing.
-constexpr int kCoherent = 1 | 16;          // sc0 | sc1
-constexpr uint32_t kSpinLimit = 1u << 22;  // bounded wait: a broken protocol cannot hang
+// outputs from the other workgroups cannot afford.  Always taking block j-1's
+// state (never a look-back over several aggregates) keeps the rounding, and
+// therefore the result, independent of timing.
+//
+// Slots are not cleared between calls: a slot is valid when its tag equals
+// the call's tag, drawn from the generation word of the workspace header, so
+// what an earlier call left behind never matches.  The header (CallHdr) holds
+// the ticket counter, a sticky error word, a count of finished workgroups and
+// the generation; the last workgroup of a call to finish returns the two
+// counters to zero and advances the generation.  A workspace therefore has to
+// hold zeros before its first call only.
+constexpr int kCoherent = 1 | 16;  // sc0 | sc1
+
+struct CallHdr {
+    uint32_t ticket;  // next ticket of this call
+    uint32_t error;   // sticky: bit 0 a carry wait gave up, bit 1 a ticket out of range
+    uint32_t done;    // workgroups of this call that have finished
+    uint32_t gen;     // call generation; tag = gen + 1 (never 0)
+};
+static_assert(sizeof(CallHdr) == sizeof(CallHdrLayout) && offsetof(CallHdr, error) == offsetof(CallHdrLayout, error),
+              "one header layout");
+
+constexpr uint32_t kErrWait = 1u;
+constexpr uint32_t kErrTicket = 2u;
+
+__device__ __forceinline__ uint32_t hdr_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void hdr_flag(CallHdr* h, uint32_t bits) {
+    __hip_atomic_fetch_or(&h->error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One thread per workgroup, first: this workgroup's ticket and the call's tag.
+__device__ __forceinline__ uint32_t call_ticket(CallHdr* h, uint32_t* tag) {
+    const uint32_t t = __hip_atomic_fetch_add(&h->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *tag = hdr_load(&h->gen) + 1u;
+    return t;
+}
+
+// One thread per workgroup, after all of the workgroup's carry traffic (and
+// after call_ticket): the last of `groups` workgroups resets the counters and
+// advances the generation so that the next call's tag differs from this one's.
+__device__ __forceinline__ void call_done(CallHdr* h, uint32_t groups, uint32_t tag) {
+    const uint32_t d = __hip_atomic_fetch_add(&h->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d + 1u == groups) {
+        __hip_atomic_store(&h->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&h->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&h->gen, tag == 0xffffffffu ? 0u : tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void publish_state(Rsrc r, uint32_t off, const St& st) {
-    const f32x4 v = {st.a, st.b, __int_as_float(st.s), __uint_as_float(1u)};
+__device__ __forceinline__ void publish_state(Rsrc r, uint32_t off, const St& st, uint32_t tag) {
+    const f32x4 v = {st.a, st.b, __int_as_float(st.s), __uint_as_float(tag)};
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
 }
 
-// Wait for the state published at `off`; after kSpinLimit polls give up,
-// set *error and return the empty state (results are then invalid, but every
-// wave terminates).
-__device__ __forceinline__ St wait_state(Rsrc r, uint32_t off, uint32_t* error) {
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+// Wait for the state published at `off` with this call's tag; after `spin`
+// polls give up, flag the header's error word and return the empty state
+// (results are then invalid, but every wave terminates; the caller reads the
+// word through wkv_workspace_status).
+__device__ __forceinline__ St wait_state(Rsrc r, uint32_t off, uint32_t tag, uint32_t spin, CallHdr* h) {
+    for (uint32_t it = 0; it < spin; ++it) {
         const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
-        if (__float_as_uint(v.w) != 0u) return St{v.x, v.y, __float_as_int(v.z)};
+        if (__float_as_uint(v.w) == tag) return St{v.x, v.y, __float_as_int(v.z)};
         __builtin_amdgcn_s_sleep(1);
     }
-    __hip_atomic_store(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    hdr_flag(h, kErrWait);
     return empty_state();
 }
 

@@ -51,12 +51,32 @@ def new_ckpt(B: int, T: int, C: int, device) -> torch.Tensor:
     return torch.empty(ckpt_bytes(B, T, C) // 4, dtype=torch.float32, device=device)
 
 
+def new_workspace(op: int, B: int, T: int, C: int, in_dtype: torch.dtype, device) -> torch.Tensor:
+    """A zero-filled workspace for wkv_forward (op 0) or wkv_backward (op 1) at
+    this shape.  It may be reused by later calls of the same op on the same
+    stream (each call leaves it ready for the next); it must not be written
+    in between."""
+    return torch.zeros(max(workspace_bytes(op, B, T, C, in_dtype), 1), dtype=torch.uint8, device=device)
+
+
+def workspace_status(workspace: torch.Tensor, clear: bool = False) -> int:
+    """Synchronise the current stream and read the workspace's error word:
+    WKV_OK, or WKV_ETIMEOUT if a wait between workgroups gave up (or the
+    workspace was not zero-filled before its first call) since it was last
+    cleared; then the outputs written since are invalid."""
+    st = int(L.lib().wkv_workspace_status(_p(workspace), workspace.numel() * workspace.element_size(),
+                                          1 if clear else 0, _stream(workspace.device)))
+    if st not in (L.WKV_OK, L.WKV_ETIMEOUT):
+        L.check("wkv_workspace_status", st)
+    return st
+
+
 def _workspace(op, B, T, C, dt, device, workspace):
     nbytes = workspace_bytes(op, B, T, C, dt)
     if nbytes == 0:
         return None, 0
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace is None:  # zero-filled: a workspace must hold zeros before its first call
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
     return workspace, workspace.numel() * workspace.element_size()

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.wkv_version().decode() == "0.1.0"
-    for s in range(7):
+    for s in range(8):
         assert len(lib.wkv_status_str(s)) >= 2
     assert lib.wkv_status_str(99) == b"unknown status"
     assert lib.wkv_last_hip_error() == b""
@@ -47,7 +47,7 @@ def test_header_constants_match_binding():
     src = open(HEADER).read()
     assert "#define WKV_CKPT_LEN 16" in src and L.WKV_CKPT_LEN == 16
     for name, val in (("WKV_OK", 0), ("WKV_EINVAL", 1), ("WKV_EDTYPE", 2), ("WKV_ESIZE", 3),
-                      ("WKV_EALIGN", 4), ("WKV_EWORKSPACE", 5), ("WKV_EHIP", 6)):
+                      ("WKV_EALIGN", 4), ("WKV_EWORKSPACE", 5), ("WKV_EHIP", 6), ("WKV_ETIMEOUT", 7)):
         assert re.search(rf"{name} = {val}\b", src), name
         assert getattr(L, name) == val
 
@@ -369,3 +369,34 @@ def test_matrix_forward_split_workspace(lib):
         args = [P(x)] * 6
         assert fn(1, 1000, 2, 64, L.WKV_BF16, *args, None, None, None, P(x), need - 1, None) == L.WKV_EWORKSPACE
         assert fn(1, 1000, 2, 64, L.WKV_BF16, *args, None, None, None, P(x + 16), need, None) == L.WKV_EWORKSPACE
+
+
+def test_workspace_status_validation(lib):
+    """Rejected on the host, before any HIP call: NULL, too small, misaligned."""
+    buf = ctypes.create_string_buffer(1024)
+    base = ctypes.addressof(buf)
+    aligned = (base + 255) // 256 * 256
+    assert lib.wkv_workspace_status(None, 256, 0, None) == L.WKV_EINVAL
+    assert lib.wkv_workspace_status(ctypes.c_void_p(aligned), 4, 0, None) == L.WKV_EWORKSPACE
+    assert lib.wkv_workspace_status(ctypes.c_void_p(aligned + 16), 256, 0, None) == L.WKV_EWORKSPACE
+
+
+def test_debug_spin_limit_exchanges():
+    lib = L.lib()
+    old = lib.wkv_debug_spin_limit(5)
+    assert old == 1 << 22
+    assert lib.wkv_debug_spin_limit(old) == 5
+    assert lib.wkv_debug_spin_limit(old) == old
+
+
+def test_carry_regions_beyond_32_bit_addressing_are_rejected(lib):
+    """Carries between workgroups are addressed through 32-bit buffer resources:
+    a shape whose carry region would pass 4 GiB gets no workspace size and the
+    calls return WKV_ESIZE before touching any pointer."""
+    T = 1 << 30  # one 64-channel tile, 2^22 blocks of 256 tokens: 4 GiB of 16-byte slots
+    assert lib.wkv_workspace_bytes(L.WKV_OP_FORWARD, 1, T, 64, L.WKV_BF16) == 0
+    assert lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 1, T, 64, L.WKV_BF16) == 0
+    p = ctypes.c_void_p(256)
+    assert lib.wkv_forward(1, T, 64, L.WKV_BF16, p, p, p, p, p, None, p, 1 << 20, None) == L.WKV_ESIZE
+    assert lib.wkv_backward(1, T, 64, L.WKV_BF16, p, p, p, p, p, p, p, p, p, None, p, 1 << 20, None) == L.WKV_ESIZE
+    assert lib.wkv_workspace_bytes(L.WKV_OP_FORWARD, 1, T // 8, 64, L.WKV_BF16) > 0

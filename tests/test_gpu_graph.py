@@ -55,8 +55,8 @@ def test_forward_backward_graph_replays_equal_eager():
     ck = O.new_ckpt(B, T, C, DEV)
     grads = (torch.empty((B, T, C), device=DEV), torch.empty((B, T, C), device=DEV), torch.empty(C, device=DEV),
              torch.empty(C, device=DEV))
-    wsf = torch.empty(max(O.workspace_bytes(0, B, T, C, torch.bfloat16), 1), dtype=torch.uint8, device=DEV)
-    wsb = torch.empty(max(O.workspace_bytes(1, B, T, C, torch.bfloat16), 1), dtype=torch.uint8, device=DEV)
+    wsf = O.new_workspace(0, B, T, C, torch.bfloat16, DEV)
+    wsb = O.new_workspace(1, B, T, C, torch.bfloat16, DEV)
 
     def step():
         O.wkv_forward(w, u, k, v, y=y, ckpt=ck, workspace=wsf)
@@ -89,8 +89,8 @@ def test_gated_graph_replays_equal_eager():
     k, v, gy, r = bf16_dev(p0.k_bits), bf16_dev(p0.v_bits), bf16_dev(p0.gy_bits), bf16_dev(rbits[0])
     out = torch.empty((B, T, C), device=DEV)
     ck = O.new_ckpt(B, T, C, DEV)
-    wsf = torch.empty(max(O.workspace_bytes(0, B, T, C, torch.bfloat16), 1), dtype=torch.uint8, device=DEV)
-    wsb = torch.empty(max(O.workspace_bytes(1, B, T, C, torch.bfloat16), 1), dtype=torch.uint8, device=DEV)
+    wsf = O.new_workspace(0, B, T, C, torch.bfloat16, DEV)
+    wsb = O.new_workspace(1, B, T, C, torch.bfloat16, DEV)
     res = {}
 
     def step():
