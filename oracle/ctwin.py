@@ -49,6 +49,9 @@ def load_ctwin():
     lib.wkv_ref_forward.argtypes = [i64, i64, i64, fp, fp, fp, fp, dp, dp, dp, i32]
     lib.wkv_ref_backward.restype = i32
     lib.wkv_ref_backward.argtypes = [i64, i64, i64, fp, fp, fp, fp, fp, dp, dp, dp, dp, i32]
+    vp = ctypes.c_void_p
+    lib.wkv_ref_step.restype = i32
+    lib.wkv_ref_step.argtypes = [i64, i64, i64, fp, fp, vp, vp, i32, dp, dp, dp, i32]
     _lib = lib
     return lib
 
@@ -96,3 +99,26 @@ def ctwin_backward(w, u, k, v, gy, nthreads=0):
     if used < 0:
         raise MemoryError("oracle C twin: scratch allocation failed")
     return dk, dv, dw, du, used
+
+
+def ctwin_step(w, u, k, v, A, Bs, want_y=True, nthreads=0):
+    """One float64 decode step of the C twin for [L, B, C] lanes, in place on the
+    plain sums A, Bs (float64 [L, B, C], C-contiguous).  w, u: [L, C]; k, v:
+    float32 values or uint16 bf16 bits, [L, B, C].  Returns (y or None,
+    threads_used)."""
+    lib = load_ctwin()
+    w, u = _f32c(w), _f32c(u)
+    bf16 = k.dtype == np.uint16
+    if not bf16:
+        k, v = _f32c(k), _f32c(v)
+    k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    assert A.dtype == np.float64 and Bs.dtype == np.float64 and A.flags.c_contiguous and Bs.flags.c_contiguous
+    Ln, Bsz, C = k.shape
+    assert A.shape == k.shape == v.shape == Bs.shape and w.shape == u.shape == (Ln, C)
+    y = np.empty((Ln, Bsz, C)) if want_y else None
+    used = lib.wkv_ref_step(Ln, Bsz, C, _fptr(w), _fptr(u), k.ctypes.data_as(ctypes.c_void_p),
+                            v.ctypes.data_as(ctypes.c_void_p), 1 if bf16 else 0, _dptr(A), _dptr(Bs), _dptr(y),
+                            int(nthreads))
+    if used < 0:
+        raise MemoryError("oracle C twin: scratch allocation failed")
+    return y, used

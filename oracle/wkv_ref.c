@@ -1,7 +1,8 @@
 /*
  * Float64 C twin of the WKV oracle (oracle/wkv_ref.py), for workloads too
  * large for the numpy loops: the decode-state seeding of 32 x 256 x 4096
- * lanes and the CPU baseline timing.
+ * lanes, the 1000 decode steps of every one of those lanes, and the CPU
+ * baseline timing.
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
  * cpu_baseline leg of bench.py load this library; the HIP product path never
@@ -163,4 +164,78 @@ int wkv_ref_backward(int64_t B, int64_t T, int64_t C, const float* w,
     free(dw_lane);
     free(du_lane);
     return failed ? -1 : used;
+}
+
+/* bf16 bits -> float32 value (exact: bf16 is the top half of a float32). */
+static inline float bf16_value(uint16_t x) {
+    union {
+        uint32_t u;
+        float f;
+    } c;
+    c.u = (uint32_t)x << 16;
+    return c.f;
+}
+
+/* One recurrent-mode (decode) token for L x B x C lanes, on the plain float64
+ * sums of the state, A (numerator) and B (denominator):
+ *
+ *   "RWKV - 把 RNN 重新带回 Transformer 时代的线性大模型", section
+ *   "关键设计 4" (recurrent mode: the output reads the state before the
+ *   token, the token then enters with its own weight) and "关键设计 2":
+ *       y  = (A + e^{u+k} v) / (B + e^{u+k})
+ *       A' = e^{-w} A + e^{k} v,      B' = e^{-w} B + e^{k}
+ *
+ * The same plain recurrence as wkv_ref_forward (so T steps from A = B = 0
+ * are that forward), without the running-max rescale of the numpy step
+ * oracle: these sums stay far inside float64's range for the decode
+ * workloads (|k| of a few units).
+ *
+ * w, u: [L, C] float32.  k, v: [L, B, C] as float32 values (bf16 == 0) or as
+ * bf16 bits (bf16 != 0).  A, Bs: [L, B, C] doubles, read and updated in
+ * place.  y (nullable): [L, B, C] doubles.  Returns the number of threads
+ * used, or -1 when a scratch allocation fails. */
+int wkv_ref_step(int64_t L, int64_t B, int64_t C, const float* w, const float* u, const void* k, const void* v,
+                 int bf16, double* A, double* Bs, double* y, int nthreads) {
+    int used = 1;
+    double* dtab = (double*)malloc((size_t)(L * C) * sizeof(double));
+    double* eutab = (double*)malloc((size_t)(L * C) * sizeof(double));
+    if (!dtab || !eutab) {
+        free(dtab);
+        free(eutab);
+        return -1;
+    }
+    for (int64_t i = 0; i < L * C; ++i) {  /* per (layer, channel): e^{-w}, e^{u} */
+        dtab[i] = exp(-(double)w[i]);
+        eutab[i] = exp((double)u[i]);
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+#pragma omp for collapse(2) schedule(static)
+#endif
+        for (int64_t l = 0; l < L; ++l) {
+            for (int64_t b = 0; b < B; ++b) {
+                for (int64_t c = 0; c < C; ++c) {
+                    const int64_t i = (l * B + b) * C + c;
+                    const double d = dtab[l * C + c];
+                    const double eu = eutab[l * C + c];
+                    const double kt = bf16 ? (double)bf16_value(((const uint16_t*)k)[i]) : (double)((const float*)k)[i];
+                    const double vt = bf16 ? (double)bf16_value(((const uint16_t*)v)[i]) : (double)((const float*)v)[i];
+                    const double ek = exp(kt);
+                    const double cur = eu * ek;
+                    if (y) y[i] = (A[i] + cur * vt) / (Bs[i] + cur);
+                    A[i] = d * A[i] + ek * vt;
+                    Bs[i] = d * Bs[i] + ek;
+                }
+            }
+        }
+#ifdef _OPENMP
+    }
+#endif
+    free(dtab);
+    free(eutab);
+    return used;
 }

@@ -98,12 +98,20 @@ def _config5_initial_state(dp):
 
 def test_config5_decode_1000_steps():
     """32 layers x 256 streams x 4096 channels, state from a T=512 oracle prefix,
-    then 1000 steps of fresh bf16 k, v; a fixed sample of lanes is checked
-    against the float64 oracle at every step, and the final state too."""
+    then 1000 steps of fresh bf16 k, v.  Every one of the 33,554,432 lanes is
+    stepped by the float64 C oracle (plain sums A, B from the same float32
+    starting state as the GPU): y is compared on every lane at every 10th step
+    and the last, the final state on every lane (a/b and ln b + p).  A fixed
+    sample of 8,192 lanes is also checked at every step against the numpy
+    running-max step oracle."""
+    from oracle.ctwin import ctwin_step
+
     O = ops()
-    print("case config5 decode L=32 B=256 C=4096, 1000 steps", flush=True)
+    print("case config5 decode L=32 B=256 C=4096, 1000 steps, every lane", flush=True)
     dp = W.config5()
     a0, b0, p0 = _config5_initial_state(dp)
+    A = a0.astype(np.float64) * np.exp(p0.astype(np.float64))
+    Bs = b0.astype(np.float64) * np.exp(p0.astype(np.float64))
     w = to_dev(dp.w, DEV)
     u = to_dev(dp.u, DEV)
     a, b, p = to_dev(a0, DEV), to_dev(b0, DEV), to_dev(p0, DEV)
@@ -116,29 +124,54 @@ def test_config5_decode_1000_steps():
     sw, su = dp.w[l_idx, c_idx], dp.u[l_idx, c_idx]
     ra, rb, rp = (a0.reshape(-1)[idx].astype(np.float64), b0.reshape(-1)[idx].astype(np.float64),
                   p0.reshape(-1)[idx].astype(np.float64))
-    worst_y = 0.0
+    kh = torch.empty((dp.L, dp.B, dp.C), dtype=torch.int16, pin_memory=True)
+    vh = torch.empty_like(kh, pin_memory=True)
+    yh = torch.empty((dp.L, dp.B, dp.C), dtype=torch.float32, pin_memory=True)
+    worst_y = worst_all = 0.0
     worst_y32 = 0.0
     atol = None
+    checked = 0
     for step in range(1000):
         k, v = W.step_inputs_torch(dp, step, DEV)
         y = O.wkv_step(w, u, k, v, a, b, p)
-        ks = k.view(-1)[idx_t].float().cpu().numpy()
-        vs = v.view(-1)[idx_t].float().cpu().numpy()
+        kh.copy_(k.view(torch.int16))
+        vh.copy_(v.view(torch.int16))
+        full = step % 10 == 9 or step == 999
+        if full:
+            yh.copy_(y)
+        torch.cuda.synchronize()
+        kb, vb = kh.numpy().view(np.uint16), vh.numpy().view(np.uint16)
+        yr_all, _ = ctwin_step(dp.w, dp.u, kb, vb, A, Bs, want_y=full)
+        # the sample, against the running-max oracle
+        ks = kb.reshape(-1)[idx].astype(np.uint32) << 16
+        vs = vb.reshape(-1)[idx].astype(np.uint32) << 16
         ys = y.view(-1)[idx_t].cpu().numpy()
-        ry, ra, rb, rp = wkv_step_ref(sw, su, ks, vs, ra, rb, rp)
-        err = np.abs(ys - ry)
+        ry, ra, rb, rp = wkv_step_ref(sw, su, ks.view(np.float32), vs.view(np.float32), ra, rb, rp)
         if atol is None:  # RMS of the reference output, fixed from the first step
             atol = 2e-5 * float(np.sqrt(np.mean(ry ** 2)))
+        err = np.abs(ys - ry)
         tol = np.maximum(atol, 2e-3 * np.abs(ry))
         worst_y = max(worst_y, float(np.max(err / tol)))
         worst_y32 = max(worst_y32, float(np.max(err / np.maximum(1e-6, 1e-5 * np.abs(ry)))))
-        assert np.all(err <= tol), f"step {step}: y out of the 2e-3 bound (worst {np.max(err / tol):.3f})"
-        if step % 250 == 0:
-            print(f"  step {step}: worst err/tol (2e-3 bound) {worst_y:.3e}, (fp32 bound) {worst_y32:.3e}", flush=True)
+        assert np.all(err <= tol), f"step {step}: sampled y out of the 2e-3 bound (worst {np.max(err / tol):.3f})"
+        if full:  # every lane
+            yg = yh.numpy()
+            ratio = np.abs(yg - yr_all) / np.maximum(atol, 2e-3 * np.abs(yr_all))
+            r = float(ratio.max())
+            worst_all = max(worst_all, r)
+            checked += 1
+            assert r <= 1.0, (f"step {step}: {int((ratio > 1).sum())} of {n} lanes out of the 2e-3 bound, "
+                              f"worst {r:.3f} at {np.unravel_index(np.argmax(ratio), ratio.shape)}")
+        if step % 100 == 99:
+            print(f"  step {step + 1}: every-lane worst err/tol {worst_all:.3e} ({checked} steps checked); "
+                  f"sample worst {worst_y:.3e} (fp32 bound {worst_y32:.3e})", flush=True)
     torch.cuda.synchronize()
-    ga = a.view(-1)[idx_t].cpu().numpy().astype(np.float64)
-    gb = b.view(-1)[idx_t].cpu().numpy().astype(np.float64)
-    gp = p.view(-1)[idx_t].cpu().numpy().astype(np.float64)
-    check_close("config5 final a/b", ga / gb, ra / rb, 1e-4, 1e-4)
-    check_close("config5 final ln b + p", np.log(gb) + gp, np.log(rb) + rp, 1e-4, 1e-4)
-    print(f"  y worst err/tol over 1000 steps: 2e-3 bound {worst_y:.3e}; fp32 bound {worst_y32:.3e}")
+    assert checked == 100
+    ga, gb, gp = (t.cpu().numpy().astype(np.float64) for t in (a, b, p))
+    check_close("config5 final a/b (every lane)", ga / gb, A / Bs, 1e-4, 1e-4)
+    check_close("config5 final ln b + p (every lane)", np.log(gb) + gp, np.log(Bs), 1e-4, 1e-4)
+    ga, gb, gp = ga.reshape(-1)[idx], gb.reshape(-1)[idx], gp.reshape(-1)[idx]
+    check_close("config5 final a/b (sample, running-max oracle)", ga / gb, ra / rb, 1e-4, 1e-4)
+    check_close("config5 final ln b + p (sample)", np.log(gb) + gp, np.log(rb) + rp, 1e-4, 1e-4)
+    print(f"  y worst err/tol: every lane (100 steps) {worst_all:.3e}; sample (1000 steps) {worst_y:.3e}; "
+          f"sample against the fp32 bound {worst_y32:.3e}")

@@ -149,21 +149,31 @@ def test_extreme_decay_rates(rates):
     check(p, go, run(p, go_bits), name=f"rates {rates}")
 
 
-def test_full_size_sampled_heads():
+def test_full_size_every_head():
     """B=8, T=1024, 64 heads of 64 (the benchmarked shape, same entry point):
-    every output of two heads against the oracle run on those heads alone
-    (heads are independent; dw, du sum over the batch rows of their head)."""
+    every gradient of every (batch row, head) against the oracle, one batch row
+    (all 64 heads) at a time; dw and du, summed over the batch rows, against
+    the oracle's sums over the rows (and the bounds summed likewise)."""
     p = W.wkv5_config(seed=3)
     go_bits, go = W.wkv5_go(p, seed=4)
     print(f"case {p.name}", flush=True)
     got = run(p, go_bits, need_state_grad=True)
-    for h in (0, 37):
-        sl = slice(64 * h, 64 * h + 64)
-        sub = W.Wkv5Problem(f"{p.name} head {h}", p.B, p.T, 1, p.w[h:h + 1], p.u[h:h + 1], p.r[:, :, sl], p.k[:, :, sl],
-                            p.v[:, :, sl], None, None, None, None)
-        part = [got[0][:, :, sl], got[1][:, :, sl], got[2][:, :, sl], got[3][h:h + 1], got[4][h:h + 1],
-                got[5][:, h:h + 1]]
-        check(sub, go[:, :, sl], part, name=sub.name)
+    sums = {3: [0.0, 0.0], 4: [0.0, 0.0]}  # dw, du: (oracle, bound) summed over the rows
+    for b in range(p.B):
+        sub = W.Wkv5Problem(f"{p.name} row {b}", 1, p.T, p.H, p.w, p.u, p.r[b:b + 1], p.k[b:b + 1], p.v[b:b + 1],
+                            None, None, None, None)
+        gb = go[b:b + 1]
+        ref = wkv5_backward_ref(sub.w, sub.u, sub.r, sub.k, sub.v, gb, sub.H)
+        bnd = bounds(sub.w.astype(np.float64), sub.u, sub.r, sub.k, sub.v, gb, sub.H, None, None)
+        for i in (0, 1, 2, 5):
+            check_bound(f"{sub.name} {NAMES[i]}", got[i][b:b + 1], ref[i], bnd[i])
+            check_norm(f"{sub.name} {NAMES[i]}", got[i][b:b + 1], ref[i])
+        for i in (3, 4):
+            sums[i][0] = sums[i][0] + ref[i]
+            sums[i][1] = sums[i][1] + bnd[i]
+    for i in (3, 4):
+        check_bound(f"{p.name} {NAMES[i]} (all rows)", got[i], sums[i][0], sums[i][1])
+        check_norm(f"{p.name} {NAMES[i]} (all rows)", got[i], sums[i][0])
 
 
 def test_split_sequence_chains_through_the_state():

@@ -199,20 +199,20 @@ def test_zero_length_and_determinism():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_bench_shape_sampled():
+def test_bench_shape_every_head():
     """B=8, T=1024, 64 heads of 64 (the benchmarked shape, same entry point):
-    every output of two heads against the oracle run on those heads alone."""
+    every output and the final state of every (batch row, head) against the
+    oracle, one batch row (all 64 heads) at a time."""
     p = W.wkv6_config(seed=5)
     print(f"case {p.name}", flush=True)
     d = dev_inputs(p)
     o, S = ops().wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], return_state=True)
     torch.cuda.synchronize()
     o, S = o.cpu().numpy(), S.cpu().numpy()
-    for h in (0, 41):
-        sl = slice(64 * h, 64 * h + 64)
-        sub = W.Wkv5Problem(f"{p.name} head {h}", p.B, p.T, 1, p.w[:, :, sl], p.u[h:h + 1], p.r[:, :, sl],
-                            p.k[:, :, sl], p.v[:, :, sl], None, None, None, None)
-        check(sub, torch.from_numpy(o[:, :, sl]), torch.from_numpy(S[:, h:h + 1]), name=sub.name)
+    for b in range(p.B):
+        sub = W.Wkv5Problem(f"{p.name} row {b}", 1, p.T, p.H, p.w[b:b + 1], p.u, p.r[b:b + 1], p.k[b:b + 1],
+                            p.v[b:b + 1], None, None, None, None)
+        check(sub, torch.from_numpy(o[b:b + 1]), torch.from_numpy(S[b:b + 1]), name=sub.name)
 
 
 @pytest.mark.parametrize("rates", [None, (6.0, 14.0)])

@@ -263,11 +263,12 @@ def test_autograd_function():
         check_bound(f"autograd {n}", got[i].cpu().numpy(), ref[i], b)
 
 
-def test_full_size_sampled_heads():
+def test_full_size_every_head():
     """B=8, T=1024, 64 heads of 64 (the benchmarked shape and call sequence: the
     forward saves its chunk-start states, the backward reads them): every
-    output of two heads against the oracle run on those heads alone (heads are
-    independent; du sums over the batch rows of its head)."""
+    gradient of every (batch row, head) against the oracle, one batch row (all
+    64 heads) at a time; du, summed over the batch rows, against the oracle's
+    sum over the rows (and the bound summed likewise)."""
     p = W.wkv6_config(seed=5)
     go_bits, go = W.wkv5_go(p, seed=6)
     print(f"case {p.name}", flush=True)
@@ -276,13 +277,23 @@ def test_full_size_sampled_heads():
     ck = O.new_wkv5_ckpt(p.B, p.T, p.H, DEV)
     O.wkv6_forward(d["w"], d["u"], d["r"], d["k"], d["v"], ckpt=ck)
     got = run(d, need_state_grad=True, ckpt=ck)
-    for h in (0, 41):
-        sl = slice(64 * h, 64 * h + 64)
-        sub = W.Wkv5Problem(f"{p.name} head {h}", p.B, p.T, 1, p.w[:, :, sl], p.u[h:h + 1], p.r[:, :, sl],
-                            p.k[:, :, sl], p.v[:, :, sl], None, None, None, None)
-        part = [got[0][:, :, sl], got[1][:, :, sl], got[2][:, :, sl], got[3][:, :, sl], got[4][h:h + 1],
-                got[5][:, h:h + 1]]
-        check(sub, go[:, :, sl], part, name=sub.name)
+    du_ref = du_refc = du_bnd = 0.0
+    for b in range(p.B):
+        name = f"{p.name} row {b}"
+        w = np.asarray(p.w[b:b + 1], np.float64)
+        args = (p.u, p.r[b:b + 1], p.k[b:b + 1], p.v[b:b + 1], go[b:b + 1], p.H, None, None)
+        ref = wkv6_backward_ref(w, *args)
+        bnd = bounds(w, *args)
+        wc = np.minimum(w, CAP)
+        refc = ref if np.array_equal(wc, w) else wkv6_backward_ref(wc, *args)
+        for i in (0, 1, 2, 3, 5):
+            check_bound(f"{name} {NAMES[i]}", got[i][b:b + 1], ref[i], bnd[i])
+            check_norm(f"{name} {NAMES[i]}", got[i][b:b + 1], refc[i])
+        du_ref = du_ref + ref[4]
+        du_refc = du_refc + refc[4]
+        du_bnd = du_bnd + bnd[4]
+    check_bound(f"{p.name} du (all rows)", got[4], du_ref, du_bnd)
+    check_norm(f"{p.name} du (all rows)", got[4], du_refc)
 
 
 @pytest.mark.parametrize("rates", [None, (6.0, 14.0)])

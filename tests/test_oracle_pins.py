@@ -399,6 +399,60 @@ def test_ctwin_matches_numpy_oracle(ctwin):
         assert np.allclose(a_, b_, rtol=1e-12, atol=1e-12)
 
 
+def test_ctwin_step_from_empty_state_is_the_forward(ctwin):
+    """T steps of the C twin's decode step from A = B = 0 give the C twin's (and
+    the numpy oracle's) forward, outputs and final sums, per layer."""
+    from oracle.ctwin import ctwin_forward, ctwin_step
+
+    Ln, Bsz, T, C = 2, 3, 60, 7
+    rng = np.random.default_rng(41)
+    w = np.exp(rng.uniform(-6, 1.5, (Ln, C))).astype(np.float32)
+    u = rng.normal(0, 1, (Ln, C)).astype(np.float32)
+    k = rng.normal(0, 2, (Ln, Bsz, T, C)).astype(np.float32)
+    v = rng.normal(0, 1, (Ln, Bsz, T, C)).astype(np.float32)
+    A = np.zeros((Ln, Bsz, C)); Bs = np.zeros((Ln, Bsz, C))
+    ys = []
+    for t in range(T):
+        y, used = ctwin_step(w, u, k[:, :, t], v[:, :, t], A, Bs)
+        ys.append(y)
+    assert used >= 1
+    y = np.stack(ys, axis=2)
+    for l in range(Ln):
+        yf, Af, Bf, _ = ctwin_forward(w[l], u[l], k[l], v[l], want_sums=True)
+        assert np.allclose(y[l], yf, rtol=1e-13, atol=1e-14)
+        assert np.allclose(A[l], Af, rtol=1e-13, atol=1e-13) and np.allclose(Bs[l], Bf, rtol=1e-13)
+        yr = wkv_forward_ref(w[l], u[l], k[l], v[l])
+        assert np.allclose(y[l], yr, rtol=1e-12, atol=1e-13)
+
+
+def test_ctwin_step_matches_running_max_step(ctwin):
+    """From arbitrary states (a, b, p) the plain-sum C step and the running-max
+    numpy step (pinned above) agree: outputs, and the new state through a/b and
+    ln b + p; bf16-bit inputs give what their float32 values give."""
+    from oracle.ctwin import ctwin_step
+    from rwkv_wkv_mixing_amd.workloads import bf16_round
+
+    Ln, Bsz, C = 3, 4, 33
+    rng = np.random.default_rng(42)
+    w = np.exp(rng.uniform(-6, 1.5, (Ln, C))).astype(np.float32)
+    u = rng.normal(0, 1, (Ln, C)).astype(np.float32)
+    a = rng.normal(0, 1, (Ln, Bsz, C))
+    b = np.exp(rng.normal(0, 1, (Ln, Bsz, C)))
+    p = rng.normal(0, 4, (Ln, Bsz, C))
+    kb, k = bf16_round(rng.normal(0, 2, (Ln, Bsz, C)).astype(np.float32))
+    vb, v = bf16_round(rng.normal(0, 1, (Ln, Bsz, C)).astype(np.float32))
+    A = a * np.exp(p)
+    Bs = b * np.exp(p)
+    A2, B2 = A.copy(), Bs.copy()
+    y, _ = ctwin_step(w, u, k, v, A, Bs)
+    y2, _ = ctwin_step(w, u, kb, vb, A2, B2)
+    assert np.array_equal(y, y2) and np.array_equal(A, A2) and np.array_equal(Bs, B2)
+    ry, ra, rb, rp = wkv_step_ref(w[:, None], u[:, None], k, v, a, b, p)
+    assert np.allclose(y, ry, rtol=1e-12, atol=1e-13)
+    assert np.allclose(A / Bs, ra / rb, rtol=1e-12, atol=1e-13)
+    assert np.allclose(np.log(Bs), np.log(rb) + rp, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------- planted mistakes -------
 
 def _mutant_forward(w, u, k, v, kind):
