@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long", "wkv6long", "stream"])
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "fwd3", "fwd2", "fwd4", "step5", "copy", "prefill", "gated", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long", "wkv6long", "stream", "step1"])
     ap.add_argument("--sets", type=int, default=3, help="rotated operand copies (cache eviction)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     return ap.parse_args()
@@ -228,6 +228,7 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_note": f"float32 arithmetic, states and outputs; inputs k, v, gy in {p.dtype}",
         "data": "synthetic",
         "config": {"workload": p.name + (" fwd+bwd" if with_bwd else " fwd"), "B": B, "T": T, "C": C,
                    "in_dtype": p.dtype},
@@ -312,6 +313,93 @@ def bench_step5(args):
                                "sample": f"10 steps of layer 0 x 256 streams x 4096 channels ({10 * Bs * C} "
                                          f"lane-steps) through the float64 numpy step oracle, {t_np:.2f} s"}
     return out
+
+
+def bench_step1(args):
+    """Decode at the in-model shape: one wkv_step call per layer (L=1, B=256
+    streams, C=4096), 32 layers per token, each layer with its own w, u and
+    state (drawn as for the decode workload).  Timed two ways: eagerly (32
+    launches per token) and as a HIP graph of the 32 calls captured once and
+    replayed.  Algorithmic bytes per call: 32 B per lane (k, v 4, state 12 in;
+    y 4, state 12 out) = 33.5 MB, 4.2 us at 8 TB/s: the call is launch-bound
+    unless the launches are amortised."""
+    import torch
+
+    from rwkv_wkv_mixing_amd import ops, workloads as W
+
+    dev = torch.device("cuda:0")
+    dp = W.make_decode(32, 256, 4096, 0, seed=0)
+    Ln, Bs, C = dp.L, dp.B, dp.C
+    w = torch.from_numpy(dp.w).to(dev)
+    u = torch.from_numpy(dp.u).to(dev)
+    nsets = max(args.sets, 2)
+    kv = [W.step_inputs_torch(dp, i, dev) for i in range(nsets)]
+    a, b, p = ops.empty_state(Ln, Bs, C, dev)
+    y = torch.empty((Ln, Bs, C), device=dev)
+    views = []
+    for s in range(nsets):
+        k, v = kv[s]
+        views.append([(w[l:l + 1], u[l:l + 1], k[l:l + 1], v[l:l + 1], a[l:l + 1], b[l:l + 1], p[l:l + 1],
+                       y[l:l + 1]) for l in range(Ln)])
+
+    def token(s):
+        for (wl, ul, kl, vl, al, bl, pl, yl) in views[s % nsets]:
+            ops.wkv_step(wl, ul, kl, vl, al, bl, pl, y=yl)
+
+    for i in range(32 + args.warmup):
+        token(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        token(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        token(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    eager = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    # the same 32 calls captured once per operand set and replayed
+    graphs = []
+    for s in range(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            token(s)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - t0
+    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        gevs[i][0].record()
+        graphs[i % nsets].replay()
+        gevs[i][1].record()
+    torch.cuda.synchronize()
+    graph = stats_us([e0.elapsed_time(e1) for e0, e1 in gevs])
+    n_layer = Bs * C
+    per_call = eager["mean"] / Ln
+    achieved = 32 * n_layer / (per_call * 1e-6) / 1e9
+    return {
+        "metric": "WKV decode step at the in-model shape (one layer per call), lane-steps/s, L=1 B=256 C=4096 bf16 k,v",
+        "value": Ln * n_layer / (wall / args.steps), "unit": "lane·steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "wkv4 decode, 32 layers x one wkv_step call (L=1 B=256 C=4096 bf16) per token"},
+        "call_us": {"token_32_calls_eager": eager, "token_32_calls_graph": graph,
+                    "per_call_eager": per_call, "per_call_graph": graph["mean"] / Ln},
+        "graph_value": Ln * n_layer / (gwall / args.steps),
+        "roofline": {"bound": "hbm", "kernel": "wkv_step (L=1)", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": 32 * n_layer,
+                     "graph_achieved": 32 * n_layer / (graph["mean"] / Ln * 1e-6) / 1e9},
+    }
 
 
 def bench_wkv6_decode(args):
@@ -524,7 +612,7 @@ def bench_wkv5(args):
         "metric": "RWKV-5 matrix-state WKV forward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
         "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "dtype_note": "bf16 matrix-core operands, float32 accumulation and state",
         "data": "synthetic", "config": {"workload": p.name + " fwd", "B": B, "T": T, "H": H, "N": 64},
         "call_us": {"wkv5_forward": st},
         "roofline": {"bound": "hbm", "kernel": "wkv5_forward", "achieved": achieved, "peak": HBM_PEAK_GBPS,
@@ -592,7 +680,7 @@ def bench_wkv6(args):
         "metric": "RWKV-6 matrix-state WKV (per-token decay) forward channel·tokens/s, B=8 T=1024 H=64 N=64 bf16",
         "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "dtype_note": "bf16 matrix-core operands, float32 accumulation and state",
         "data": "synthetic", "config": {"workload": p.name + " fwd", "B": B, "T": T, "H": H, "N": 64},
         "call_us": {"wkv6_forward": st},
         "roofline": {"bound": "hbm", "kernel": "wkv6_forward", "achieved": achieved, "peak": HBM_PEAK_GBPS,
@@ -695,7 +783,7 @@ def bench_matrix_train(args, gen, long=False):
         "metric": f"{what} forward+backward channel·tokens/s, B={B} T={T} H={H} N=64 bf16",
         "value": n / (wall / args.steps), "unit": "channel·tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "dtype_note": "bf16 matrix-core operands, float32 accumulation and state",
         "data": "synthetic", "config": {"workload": p.name + " fwd+bwd", "B": B, "T": T, "H": H, "N": 64},
         "call_us": {f"{n_fwd}(ckpt)": st_f, f"{n_bwd}(ckpt)": st_b},
         "roofline": {"bound": "hbm", "kernel": f"{n_bwd} (backward kernel + du{'/dw' if gen == 5 else ''} batch sum)",
@@ -852,9 +940,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     if args.workload in ("step5", "copy", "shift", "wkv5", "wkv5train", "wkv6", "wkv6train", "wkv6decode", "wkv5long",
-                         "wkv6long", "stream"):
+                         "wkv6long", "stream", "step1"):
         out = {"step5": bench_step5, "copy": bench_copy, "shift": bench_shift, "wkv5": bench_wkv5,
-               "stream": bench_stream,
+               "stream": bench_stream, "step1": bench_step1,
                "wkv5train": lambda a: bench_matrix_train(a, 5), "wkv6": bench_wkv6,
                "wkv6train": lambda a: bench_matrix_train(a, 6), "wkv6decode": bench_wkv6_decode,
                "wkv5long": lambda a: bench_matrix_train(a, 5, long=True),

@@ -7,14 +7,15 @@
 // kCkptLen tokens, in the mean form (history mean m = A/B) so that output
 // differences never come from rounded outputs:
 //     delta = v - m,  pi = e^{u+k}/D,  rho = 2^s/D,  lam = e^k/B_t,  m_t = m + lam delta.
-// The reverse accumulators, scaled by 2^{s}, and the span offsets below are
-// kept in float64 (the per-token terms stay float32): at a dominant token
-// they sum ~10^2 signed terms of order one whose total can be ~10^-3 of
-// that, so their own rounding is kept well under the float32 rounding of
-// the terms; float64 FMAs issue at the rate of unpacked float32 ones on this
-// chip.  What makes the terms consistent with each other is the exact
-// integer-scale arithmetic of the lane state (the weight of a dominant token
-// has one float32 value everywhere).  The accumulators are
+// The per-token reverse accumulators, scaled by 2^{s}, run in float32
+// (float64 when built with WKV_BWD_ACC_F64=1, which measured no better once
+// the states were exact); the span maps, their composition and the carries
+// between workgroups are float64.  At a dominant token the gradient sums
+// ~10^2 signed terms of order one whose total can be ~10^-3 of that; what
+// keeps those terms consistent with each other is the exact integer-scale
+// arithmetic of the lane state and a key weight formed the same way in every
+// pass (k log2 e in two words, scaled by an integer power of two).  The
+// accumulators are
 //     G_{t-1}  = d G_t + gy_t rho_t
 //     J_{t-1}  = d (J_t + lam_t delta_t G_t) + gy_t rho_t pi_t delta_t     (J = H - m G)
 //     G'_{t-1} = d (G'_t + G_t)

@@ -11,15 +11,20 @@
 //
 // Memory-bound: 32 bytes per lane for bf16 inputs (read a, b, p, k, v; write
 // y, a, b, p).  A thread owns a group of 4 channels (or 1) of one layer for
-// kStreamsPerThread consecutive streams, so the per-channel constants
-// (including the float64 exp that splits e^{-w}) are computed once per group
-// and every access of a wavefront is one contiguous row segment.
+// `spt` consecutive streams, so the per-channel constants (including the
+// float64 exp that splits e^{-w}) are computed once per group and every
+// access of a wavefront is one contiguous row segment.  spt is chosen at
+// launch: up to kMaxStreamsPerThread while that still leaves kThreadsPerCu
+// threads per CU (all 32 layers of a decode token in one call), down to 1 for
+// one layer per call (the in-model use), where 16 would leave three CUs in
+// four idle.
 #include "wkv_device.h"
 #include "wkv_launch.h"
 
 namespace wkv {
 
-constexpr int kStreamsPerThread = 16;
+constexpr int64_t kMaxStreamsPerThread = 16;
+constexpr int64_t kThreadsPerCu = 2048;
 constexpr float kRescaleX = 22.0f;  // e^22 ~ 2^32
 
 struct StepChan {
@@ -66,7 +71,7 @@ __device__ __forceinline__ float step_lane(const StepChan& ch, float k, float v,
 
 template <typename TIn>
 __global__ void __launch_bounds__(256) step_kernel_scalar(int64_t L, int64_t B, int64_t C,
-                                                          int64_t nbt,
+                                                          int64_t nbt, int64_t spt,
                                                           const float* __restrict__ w,
                                                           const float* __restrict__ u,
                                                           const TIn* __restrict__ k,
@@ -79,8 +84,8 @@ __global__ void __launch_bounds__(256) step_kernel_scalar(int64_t L, int64_t B, 
     const int64_t bt = (t / C) % nbt;
     const int64_t l = t / (C * nbt);
     const StepChan ch = step_chan(w[l * C + c], u[l * C + c]);
-    const int64_t b_end = (bt + 1) * kStreamsPerThread < B ? (bt + 1) * kStreamsPerThread : B;
-    for (int64_t s = bt * kStreamsPerThread; s < b_end; ++s) {
+    const int64_t b_end = (bt + 1) * spt < B ? (bt + 1) * spt : B;
+    for (int64_t s = bt * spt; s < b_end; ++s) {
         const int64_t i = (l * B + s) * C + c;
         float aa = a[i], bb = b[i], pp = p[i];
         y[i] = step_lane(ch, Ld<TIn>::at(k, i), Ld<TIn>::at(v, i), aa, bb, pp);
@@ -114,7 +119,7 @@ struct Vec4In<uint16_t> {
 // aligned to 4 elements.
 template <typename TIn>
 __global__ void __launch_bounds__(256) step_kernel_vec4(int64_t L, int64_t B, int64_t C,
-                                                        int64_t nbt,
+                                                        int64_t nbt, int64_t spt,
                                                         const float* __restrict__ w,
                                                         const float* __restrict__ u,
                                                         const TIn* __restrict__ k,
@@ -132,8 +137,8 @@ __global__ void __launch_bounds__(256) step_kernel_vec4(int64_t L, int64_t B, in
     const float4 u4 = reinterpret_cast<const float4*>(u)[l * C4 + c4];
     const StepChan ch[4] = {step_chan(w4.x, u4.x), step_chan(w4.y, u4.y), step_chan(w4.z, u4.z),
                             step_chan(w4.w, u4.w)};
-    const int64_t b_end = (bt + 1) * kStreamsPerThread < B ? (bt + 1) * kStreamsPerThread : B;
-    for (int64_t s = bt * kStreamsPerThread; s < b_end; ++s) {
+    const int64_t b_end = (bt + 1) * spt < B ? (bt + 1) * spt : B;
+    for (int64_t s = bt * spt; s < b_end; ++s) {
         const int64_t g = (l * B + s) * C4 + c4;
         float kf[4], vf[4];
         V::widen(reinterpret_cast<const typename V::raw*>(k)[g], kf);
@@ -156,18 +161,25 @@ __global__ void __launch_bounds__(256) step_kernel_vec4(int64_t L, int64_t B, in
 
 template <typename TIn>
 hipError_t launch_step_t(const StepArgs& s, hipStream_t stream) {
-    const int64_t nbt = (s.B + kStreamsPerThread - 1) / kStreamsPerThread;
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t groups = s.L * s.B * (s.vec4 ? s.C / 4 : s.C);  // (layer, stream, channel group) items
+    int64_t spt = groups / (static_cast<int64_t>(ncu) * kThreadsPerCu);
+    spt = spt < 1 ? 1 : (spt > kMaxStreamsPerThread ? kMaxStreamsPerThread : spt);
+    const int64_t nbt = (s.B + spt - 1) / spt;
     if (s.vec4) {
         const int64_t threads = s.L * nbt * (s.C / 4);
         hipLaunchKernelGGL(step_kernel_vec4<TIn>, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                           dim3(256), 0, stream, s.L, s.B, s.C, nbt, s.w, s.u,
+                           dim3(256), 0, stream, s.L, s.B, s.C, nbt, spt, s.w, s.u,
                            static_cast<const TIn*>(s.k), static_cast<const TIn*>(s.v), s.y, s.a,
                            s.b, s.p);
     } else {
         const int64_t threads = s.L * nbt * s.C;
         hipLaunchKernelGGL(step_kernel_scalar<TIn>,
                            dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
-                           s.L, s.B, s.C, nbt, s.w, s.u, static_cast<const TIn*>(s.k),
+                           s.L, s.B, s.C, nbt, spt, s.w, s.u, static_cast<const TIn*>(s.k),
                            static_cast<const TIn*>(s.v), s.y, s.a, s.b, s.p);
     }
     return hipGetLastError();

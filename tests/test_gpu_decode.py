@@ -77,6 +77,41 @@ def test_state_representation_invariance():
         check_close("step ln b + p", lden, np.log(rb) + rp, 1e-5, 1e-5)
 
 
+@pytest.mark.parametrize("Ln,B,C", [(1, 256, 4096), (16, 100, 4096), (32, 256, 4096), (3, 5, 70)])
+def test_stream_grouping_every_lane(Ln, B, C):
+    """The launch gives each thread 1 to 16 consecutive streams (fewer when a
+    call has fewer layers, so that the grid still fills the GPU): one layer
+    per call (1 stream per thread), 16 x 100 streams (3 per thread, the last
+    group ragged), 32 x 256 (16), and a per-element shape.  Five steps from a
+    random state against the float64 C oracle step on every lane: y at the
+    bf16-input bound, the state through a/b and ln b + p at 1e-4."""
+    from oracle.ctwin import ctwin_step
+    from rwkv_wkv_mixing_amd.workloads import bf16_round
+
+    rng = np.random.default_rng(Ln * 1000 + B + C)
+    w = np.exp(rng.uniform(-6, 1.5, (Ln, C))).astype(np.float32)
+    u = rng.normal(0, 1, (Ln, C)).astype(np.float32)
+    a0 = rng.normal(0, 1, (Ln, B, C)).astype(np.float32)
+    b0 = np.exp(rng.normal(0, 1, (Ln, B, C))).astype(np.float32)
+    p0 = rng.normal(0, 3, (Ln, B, C)).astype(np.float32)
+    A = a0.astype(np.float64) * np.exp(p0.astype(np.float64))
+    Bs = b0.astype(np.float64) * np.exp(p0.astype(np.float64))
+    O = ops()
+    a, b, p = to_dev(a0, DEV), to_dev(b0, DEV), to_dev(p0, DEV)
+    wd, ud = to_dev(w, DEV), to_dev(u, DEV)
+    print(f"case grouping L={Ln} B={B} C={C}", flush=True)
+    for step in range(5):
+        kb, kf = bf16_round(rng.normal(0, 1, (Ln, B, C)).astype(np.float32))
+        vb, vf = bf16_round(rng.normal(0, 1, (Ln, B, C)).astype(np.float32))
+        y = O.wkv_step(wd, ud, to_dev(None, DEV, kb), to_dev(None, DEV, vb), a, b, p).cpu().numpy()
+        yr, _ = ctwin_step(w, u, kb, vb, A, Bs)
+        check_close(f"grouping L={Ln} B={B} C={C} step {step} y", y, yr, 2e-3,
+                    2e-5 * float(np.sqrt(np.mean(yr ** 2))))
+    ga, gb, gp = (t.cpu().numpy().astype(np.float64) for t in (a, b, p))
+    check_close("grouping final a/b", ga / gb, A / Bs, 1e-4, 1e-4)
+    check_close("grouping final ln b + p", np.log(gb) + gp, np.log(Bs), 1e-4, 1e-4)
+
+
 def _config5_initial_state(dp):
     """Oracle forward (float64 C twin) over the shared T=512 prefix, per layer."""
     from oracle.ctwin import build_ctwin, ctwin_forward, LIB
