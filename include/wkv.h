@@ -355,7 +355,12 @@ size_t wkv5_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t N,
  *           ds_out buffer (each workgroup reads its part of ds_out before
  *           writing the same part of ds_in).
  * ckpt      the ckpt a wkv5_forward call on the same w, u, r, k, v and s_in
- *           wrote, or NULL (then s_in is read to recompute it).
+ *           wrote, or NULL (then s_in is read to recompute it).  The
+ *           recompute splits time exactly where wkv5_forward given its
+ *           workspace does (below 256 pairs), so with the full workspace its
+ *           states are the bits such a forward saves and both gradients agree
+ *           bit for bit; with the WKV_WS_NO_SPLIT size it matches a forward
+ *           run without a workspace.
  * workspace wkv5_backward_workspace_bytes(..., flags) bytes, 256-byte
  *           aligned; clobbered.  Not needed when B*T == 0.  At least the
  *           size without WKV_WS_NO_SPLIT: the time split (when the shape

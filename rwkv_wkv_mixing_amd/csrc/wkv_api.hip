@@ -343,6 +343,10 @@ BwdLayout bwd_layout(const Wkv5Plan& p, int64_t B, int64_t T, int64_t H, bool sp
     return l;
 }
 
+// The backward splits up to 256 pairs, the forward below 256: the recompute of the chunk-start
+// states takes the forward's own rule, so its states are the bits a forward given a workspace saves.
+bool recompute_split(const BwdLayout& l, int64_t B, int64_t H) { return l.nseg > 1 && B * H < 256; }
+
 // A backward with a time split (nseg > 1): every segment's local adjoint, the chain of the adjoints
 // after the segments (last first, from ds_out), then the backward of every segment from its own.
 template <class BA, hipError_t (*Launch)(const BA&, hipStream_t)>
@@ -478,9 +482,9 @@ wkv_status_t wkv5_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
         auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + l.ckpt_off);
         wkv::Wkv5Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
         fa.ckpt = tmp;
-        hipError_t e = l.nseg > 1 ? run_split<wkv::Wkv5Args, wkv::launch_wkv5_fwd>(fa, false, w, l.nseg, l.cps,
-                                                                                    split_ws, stream)
-                                  : wkv::launch_wkv5_fwd(fa, stream);
+        hipError_t e = recompute_split(l, B, H)
+                           ? run_split<wkv::Wkv5Args, wkv::launch_wkv5_fwd>(fa, false, w, l.nseg, l.cps, split_ws, stream)
+                           : wkv::launch_wkv5_fwd(fa, stream);
         if (e != hipSuccess) return hip_status(e);
         states = tmp;
     }
@@ -530,9 +534,9 @@ wkv_status_t wkv6_backward(int64_t B, int64_t T, int64_t H, int64_t N, int in_dt
         auto* tmp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + l.ckpt_off);
         wkv::Wkv6Args fa{B, T, H, w, u, r16, k16, v16, nullptr, s_in, nullptr};
         fa.ckpt = tmp;
-        hipError_t e = l.nseg > 1 ? run_split<wkv::Wkv6Args, wkv::launch_wkv6_fwd>(fa, true, nullptr, l.nseg, l.cps,
-                                                                                    split_ws, stream)
-                                  : wkv::launch_wkv6_fwd(fa, stream);
+        hipError_t e = recompute_split(l, B, H)
+                           ? run_split<wkv::Wkv6Args, wkv::launch_wkv6_fwd>(fa, true, nullptr, l.nseg, l.cps, split_ws, stream)
+                           : wkv::launch_wkv6_fwd(fa, stream);
         if (e != hipSuccess) return hip_status(e);
         states = tmp;
     }
