@@ -98,7 +98,8 @@ enum {
     WKV_EALIGN = 4,
     WKV_EWORKSPACE = 5,
     WKV_EHIP = 6,
-    WKV_ETIMEOUT = 7
+    WKV_ETIMEOUT = 7,
+    WKV_ESCRATCH = 8
 };
 
 /* dtype of the INPUT sequences k, v, gy. */
@@ -173,6 +174,37 @@ wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype,
                                const float* a_in, const float* b_in, const float* p_in,
                                float* a_out, float* b_out, float* p_out,
                                void* ckpt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * wkv_forward_state_noalloc - wkv_forward_state for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * The same kernels and results, bit for bit, as wkv_forward_state with a
+ * zero-filled workspace of its own; the workspace is instead a static device
+ * array inside the library, one per GPU it runs on, of WKV_STATIC_SCRATCH_BYTES
+ * bytes, held until the process ends.  The call allocates nothing and makes no
+ * allocating call; its first call on a device looks up that device's copy of
+ * the array (a symbol lookup, no allocation).
+ *
+ * Arguments, layouts and ownership as wkv_forward_state, without workspace and
+ * workspace_bytes.  Errors as wkv_forward_state, and WKV_ESCRATCH (nothing is
+ * launched) when wkv_workspace_bytes(WKV_OP_FORWARD, B, T, C, in_dtype) exceeds
+ * WKV_STATIC_SCRATCH_BYTES (B*T*C must stay below 2^29: 2 x 32768 x 4096
+ * fits, 4 x 32768 x 4096 does not).
+ *
+ * Every call on one GPU shares that GPU's array, whose header and carries the
+ * last call leaves ready for the next: calls on one GPU must not overlap in
+ * time (issue them on one stream, or order the streams); overlapping calls
+ * race, and their outputs are then invalid.  A wait between workgroups that
+ * gives up (see wkv_debug_spin_limit) flags the array's own error word, which
+ * no call reports: wkv_workspace_status needs a workspace of the caller's.
+ */
+#define WKV_STATIC_SCRATCH_BYTES (32u << 20)
+wkv_status_t wkv_forward_state_noalloc(int64_t B, int64_t T, int64_t C, int in_dtype,
+                                       const float* w, const float* u, const void* k, const void* v,
+                                       float* y, const float* a_in, const float* b_in, const float* p_in,
+                                       float* a_out, float* b_out, float* p_out, void* ckpt, void* hip_stream);
 
 /*
  * wkv_backward - gradients of L = sum_{b,t,c} gy * y through the forward.

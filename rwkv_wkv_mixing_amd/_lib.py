@@ -11,7 +11,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librwkv_wkv.so")
 
-WKV_OK, WKV_EINVAL, WKV_EDTYPE, WKV_ESIZE, WKV_EALIGN, WKV_EWORKSPACE, WKV_EHIP, WKV_ETIMEOUT = range(8)
+WKV_OK, WKV_EINVAL, WKV_EDTYPE, WKV_ESIZE, WKV_EALIGN, WKV_EWORKSPACE, WKV_EHIP, WKV_ETIMEOUT, WKV_ESCRATCH = range(9)
+WKV_STATIC_SCRATCH_BYTES = 32 << 20
 WKV_F32, WKV_BF16 = 0, 1
 WKV_OP_FORWARD, WKV_OP_BACKWARD = 0, 1
 WKV_CKPT_LEN = 16
@@ -22,6 +23,7 @@ EXPORTS = (
     "wkv_ckpt_bytes",
     "wkv_forward",
     "wkv_forward_state",
+    "wkv_forward_state_noalloc",
     "wkv_backward",
     "wkv_forward_gated",
     "wkv_backward_gated",
@@ -83,6 +85,8 @@ def declare(L):
     L.wkv_forward.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, vp, vp, sz, vp]
     L.wkv_forward_state.restype = i32
     L.wkv_forward_state.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp, sz, vp]
+    L.wkv_forward_state_noalloc.restype = i32
+    L.wkv_forward_state_noalloc.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp]
     L.wkv_backward.restype = i32
     L.wkv_backward.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.wkv_forward_gated.restype = i32

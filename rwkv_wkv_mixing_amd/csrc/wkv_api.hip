@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "wkv.h"
 #include "wkv_launch.h"
@@ -109,13 +110,51 @@ size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
     return static_cast<size_t>(n);
 }
 
-wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
-                               const float* u, const void* k, const void* v, float* y,
-                               const float* a_in, const float* b_in, const float* p_in, float* a_out,
-                               float* b_out, float* p_out, void* ckpt, void* workspace,
-                               size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+// Scratch of wkv_forward_state_noalloc, one copy per GPU the library runs on, held until the process
+// ends.  Static storage: zero when the code object loads, which is all the workspace protocol needs
+// before a first call (the last workgroup of every call returns the header to zero, and carry slots
+// are tagged with the call's generation).  Host code never passes `scratch` itself to a kernel: its
+// device address, taken once per device, is kept in g_scratch_ptr.
+constexpr size_t kStaticScratchBytes = WKV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, its address looked up on the first use on that device.
+hipError_t static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (ptr == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return hipSuccess;
+}
+
+// wkv_forward_state on the caller's workspace, or (use_static) on this device's static scratch.
+wkv_status_t forward_state(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w, const float* u,
+                           const void* k, const void* v, float* y, const float* a_in, const float* b_in,
+                           const float* p_in, float* a_out, float* b_out, float* p_out, void* ckpt,
+                           void* workspace, size_t workspace_bytes, bool use_static, void* hip_stream) {
     const Plan p = plan(WKV_OP_FORWARD, B, T, C, in_dtype);
     if (p.st != WKV_OK) return p.st;
+    if (use_static && p.ws_bytes > kStaticScratchBytes) return WKV_ESCRATCH;
     const bool sin = a_in || b_in || p_in, sout = a_out || b_out || p_out;
     if ((sin && !(a_in && b_in && p_in)) || (sout && !(a_out && b_out && p_out))) return WKV_EINVAL;
     if ((sin && (!aligned(a_in, 4) || !aligned(b_in, 4) || !aligned(p_in, 4))) ||
@@ -131,9 +170,35 @@ wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype, co
     if (!aligned(w, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(k, es) || !aligned(v, es) ||
         (ckpt && !aligned(ckpt, 4)))
         return WKV_EALIGN;
-    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
+    if (use_static && p.ws_bytes > 0) {
+        const hipError_t e = static_scratch(&a.ws);
+        if (e != hipSuccess) return hip_status(e);
+        a.ws_bytes = kStaticScratchBytes;
+    } else if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256))) {
         return WKV_EWORKSPACE;
+    }
     return hip_status(wkv::launch_fwd_chunk(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+wkv_status_t wkv_forward_state(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                               const float* u, const void* k, const void* v, float* y,
+                               const float* a_in, const float* b_in, const float* p_in, float* a_out,
+                               float* b_out, float* p_out, void* ckpt, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+    return forward_state(B, T, C, in_dtype, w, u, k, v, y, a_in, b_in, p_in, a_out, b_out, p_out, ckpt, workspace,
+                         workspace_bytes, false, hip_stream);
+}
+
+wkv_status_t wkv_forward_state_noalloc(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                                       const float* u, const void* k, const void* v, float* y,
+                                       const float* a_in, const float* b_in, const float* p_in, float* a_out,
+                                       float* b_out, float* p_out, void* ckpt, void* hip_stream) {
+    return forward_state(B, T, C, in_dtype, w, u, k, v, y, a_in, b_in, p_in, a_out, b_out, p_out, ckpt, nullptr, 0,
+                         true, hip_stream);
 }
 
 wkv_status_t wkv_forward_gated(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
@@ -606,6 +671,7 @@ const char* wkv_status_str(wkv_status_t s) {
         case WKV_EHIP: return "HIP launch failed";
         case WKV_ETIMEOUT: return "a wait between workgroups gave up (outputs invalid), or the workspace was not "
                                   "zero-filled before its first use";
+        case WKV_ESCRATCH: return "the problem needs more scratch memory than the library's static buffer holds";
         default: return "unknown status";
     }
 }

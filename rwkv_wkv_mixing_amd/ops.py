@@ -120,6 +120,32 @@ def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None, state_in=None,
     return (y, state_out) if return_state else y
 
 
+def wkv_forward_state_noalloc(w, u, k, v, y, *, ckpt=None, state_in=None, state_out=None):
+    """wkv_forward for callers that cannot allocate: every buffer is the
+    caller's (y [B,T,C] float32 included), and the workspace is the library's
+    static scratch, shared by all calls on the GPU (calls on one GPU must not
+    overlap in time).  Arguments as wkv_forward; returns y."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    B, T, C = k.shape
+    _need(v, "v", k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    _need(y, "y", torch.float32, (B, T, C), dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    for name, st3 in (("state_in", state_in), ("state_out", state_out)):
+        if st3 is not None:
+            for t, n in zip(st3, "abp"):
+                _need(t, f"{name}.{n}", torch.float32, (B, C), dev)
+    sin = state_in if state_in is not None else (None, None, None)
+    sout = state_out if state_out is not None else (None, None, None)
+    st = L.lib().wkv_forward_state_noalloc(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y),
+                                           *[_p(t) for t in sin], *[_p(t) for t in sout], _p(ckpt), _stream(dev))
+    L.check("wkv_forward_state_noalloc", st)
+    return y
+
+
 def wkv_forward_gated(w, u, k, v, r, *, out=None, ckpt=None, workspace=None):
     """out = sigmoid(r) * wkv(w, u, k, v), [B,T,C] float32; r has the dtype of k."""
     _need(k, "k", (torch.float32, torch.bfloat16))

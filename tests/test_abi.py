@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.wkv_version().decode() == "0.1.0"
-    for s in range(8):
+    for s in range(9):
         assert len(lib.wkv_status_str(s)) >= 2
     assert lib.wkv_status_str(99) == b"unknown status"
     assert lib.wkv_last_hip_error() == b""
@@ -47,7 +47,8 @@ def test_header_constants_match_binding():
     src = open(HEADER).read()
     assert "#define WKV_CKPT_LEN 16" in src and L.WKV_CKPT_LEN == 16
     for name, val in (("WKV_OK", 0), ("WKV_EINVAL", 1), ("WKV_EDTYPE", 2), ("WKV_ESIZE", 3),
-                      ("WKV_EALIGN", 4), ("WKV_EWORKSPACE", 5), ("WKV_EHIP", 6), ("WKV_ETIMEOUT", 7)):
+                      ("WKV_EALIGN", 4), ("WKV_EWORKSPACE", 5), ("WKV_EHIP", 6), ("WKV_ETIMEOUT", 7),
+                      ("WKV_ESCRATCH", 8)):
         assert re.search(rf"{name} = {val}\b", src), name
         assert getattr(L, name) == val
 
@@ -379,6 +380,22 @@ def test_workspace_status_validation(lib):
     assert lib.wkv_workspace_status(None, 256, 0, None) == L.WKV_EINVAL
     assert lib.wkv_workspace_status(ctypes.c_void_p(aligned), 4, 0, None) == L.WKV_EWORKSPACE
     assert lib.wkv_workspace_status(ctypes.c_void_p(aligned + 16), 256, 0, None) == L.WKV_EWORKSPACE
+
+
+def test_noalloc_forward_validation(lib):
+    """The forward on the library's static scratch rejects on the host, before
+    any HIP call: a problem whose workspace exceeds the static array
+    (WKV_ESCRATCH), and the checks of wkv_forward_state."""
+    f = lib.wkv_forward_state_noalloc
+    nul = [None] * 12
+    assert lib.wkv_workspace_bytes(L.WKV_OP_FORWARD, 4, 32768, 4096, L.WKV_BF16) > L.WKV_STATIC_SCRATCH_BYTES
+    assert lib.wkv_workspace_bytes(L.WKV_OP_FORWARD, 2, 32768, 4096, L.WKV_BF16) <= L.WKV_STATIC_SCRATCH_BYTES
+    assert f(4, 32768, 4096, L.WKV_BF16, *nul, None) == L.WKV_ESCRATCH
+    assert f(2, 32768, 4096, L.WKV_BF16, *nul, None) == L.WKV_EINVAL
+    assert f(1, 8, 4, 7, *nul, None) == L.WKV_EDTYPE
+    assert f(-1, 8, 4, L.WKV_F32, *nul, None) == L.WKV_EINVAL
+    assert f(1, 0, 4, L.WKV_F32, *nul, None) == L.WKV_OK  # nothing to do, no state: no launch
+    assert "#define WKV_STATIC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
 
 
 def test_debug_spin_limit_exchanges():
