@@ -8,13 +8,16 @@ taken where the pages are silent.
 """
 from .wkv_ref import (  # noqa: F401
     wkv_backward_ref,
+    wkv_backward_state_ref,
     wkv_direct_ref,
     wkv_forward_ref,
     wkv_gated_backward_ref,
     wkv_gated_forward_ref,
     wkv_state_from_sums,
+    wkv_state_grads_from_sums,
     wkv_step_ref,
     wkv_sums_from_state,
+    wkv_sums_grads_from_state,
 )
 from .token_shift_ref import (  # noqa: F401
     shifted_inputs_ref,

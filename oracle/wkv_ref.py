@@ -23,6 +23,8 @@ Sources (page title, then section):
   the state *before* token t; "关键设计 4：双执行模式": the decode step (output
   first from the undecayed state, then decay-and-add) and the remark that real
   implementations carry a stability exponent p.
+* [P3] "RWKV模型深度研究报告", section 4.4.2: a long input is encoded segment by
+  segment, the state carrying the history from one segment into the next.
 
 Readings where the pages are silent:
 
@@ -33,6 +35,12 @@ Readings where the pages are silent:
 * the backward formulas are derived here by differentiating the [P4] sum; the
   pages give none.  Pinned by finite differences and by autograd of the
   direct definition, see tests/test_oracle_pins.py.
+* a segment's backward through carried state (wkv_backward_state_ref) is the
+  derivative of its outputs and of the state it hands on: the loss is
+  sum(gy y) + sum(gA A_T) + sum(gB B_T), with (gA, gB) the gradient a later
+  segment returns for the plain sums it started from.  Gradients of the
+  stable representation (a, b, p) follow by the chain rule through
+  A = a e^p, B = b e^p (wkv_state_grads_from_sums, wkv_sums_grads_from_state).
 
 Parity status: every function here is pinned (no "parity unpinned" entries).
 """
@@ -45,6 +53,9 @@ __all__ = [
     "wkv_forward_ref",
     "wkv_direct_ref",
     "wkv_backward_ref",
+    "wkv_backward_state_ref",
+    "wkv_state_grads_from_sums",
+    "wkv_sums_grads_from_state",
     "wkv_step_ref",
     "wkv_state_from_sums",
 ]
@@ -187,6 +198,100 @@ def wkv_backward_ref(w, u, k, v, gy):
         H = d * H + gt * yt / D[:, t, :]
     assert np.isfinite(dk).all() and np.isfinite(dv).all()
     return dk, dv, dw, du
+
+
+def wkv_backward_state_ref(w, u, k, v, gy, A0=None, B0=None, gA=None, gB=None):
+    """Gradients through a segment that starts from a given history and hands
+    its state on ([P3] 4.4.2), in float64:
+
+        L = sum(gy * y) + sum(gA * A_T) + sum(gB * B_T),
+
+    with y and the final plain sums (A_T, B_T) those of wkv_forward_ref from the
+    initial sums (A0, B0) (zeros when None), and (gA, gB) the gradient of the
+    loss with respect to (A_T, B_T) (zeros when None).
+
+    Reverse mode written out on the [P5] recurrence, one token at a time, with
+    d = e^{-w}, D_t = B_{t-1} + e^{u+k_t} and the adjoints (ga, gb) of the state
+    after each token, starting from (gA, gB) after the last:
+      the state update A_t = d A_{t-1} + e^{k_t} v_t, B_t = d B_{t-1} + e^{k_t}
+        gives v_t the part ga e^{k_t}, k_t the part e^{k_t} (ga v_t + gb),
+        w the part -d (ga A_{t-1} + gb B_{t-1}), and passes (d ga, d gb) back;
+      the output y_t = (A_{t-1} + e^{u+k_t} v_t) / D_t
+        gives v_t the part gy_t e^{u+k_t} / D_t, k_t and u the part
+        gy_t e^{u+k_t} (v_t - y_t) / D_t, and adds gy_t / D_t and
+        -gy_t y_t / D_t to the adjoints of A_{t-1} and B_{t-1}.
+    Returns dk, dv [B, T, C], dw, du [C] and dA0, dB0 [B, C] (the adjoints of
+    the initial sums).
+    """
+    w, u, k, v, gy = _f64(w, u, k, v, gy)
+    Bsz, T, C = k.shape
+    d = np.exp(-w)
+    eu = np.exp(u)
+    A = np.zeros((Bsz, C)) if A0 is None else np.array(A0, dtype=np.float64).reshape(Bsz, C)
+    Bs = np.zeros((Bsz, C)) if B0 is None else np.array(B0, dtype=np.float64).reshape(Bsz, C)
+    A_before = np.empty((Bsz, T, C))  # the sums before each token
+    B_before = np.empty((Bsz, T, C))
+    y = np.empty((Bsz, T, C))
+    D = np.empty((Bsz, T, C))
+    for t in range(T):
+        A_before[:, t, :] = A
+        B_before[:, t, :] = Bs
+        ek = np.exp(k[:, t, :])
+        cur = eu * ek
+        D[:, t, :] = Bs + cur
+        y[:, t, :] = (A + cur * v[:, t, :]) / D[:, t, :]
+        A = d * A + ek * v[:, t, :]
+        Bs = d * Bs + ek
+    ga = np.zeros((Bsz, C)) if gA is None else np.array(gA, dtype=np.float64).reshape(Bsz, C)
+    gb = np.zeros((Bsz, C)) if gB is None else np.array(gB, dtype=np.float64).reshape(Bsz, C)
+    dk = np.zeros((Bsz, T, C))
+    dv = np.zeros((Bsz, T, C))
+    dw = np.zeros(C)
+    du = np.zeros(C)
+    for t in range(T - 1, -1, -1):
+        ek = np.exp(k[:, t, :])
+        cur = eu * ek
+        vt, yt, gt, Dt = v[:, t, :], y[:, t, :], gy[:, t, :], D[:, t, :]
+        # the state update of token t
+        dv[:, t, :] += ga * ek
+        dk[:, t, :] += ek * (ga * vt + gb)
+        dw -= (d * (ga * A_before[:, t, :] + gb * B_before[:, t, :])).sum(axis=0)
+        ga_prev = d * ga
+        gb_prev = d * gb
+        # the output of token t
+        dv[:, t, :] += gt * cur / Dt
+        dky = gt * cur * (vt - yt) / Dt
+        dk[:, t, :] += dky
+        du += dky.sum(axis=0)
+        ga = ga_prev + gt / Dt
+        gb = gb_prev - gt * yt / Dt
+    assert np.isfinite(dk).all() and np.isfinite(dv).all()
+    return dk, dv, dw, du, ga, gb
+
+
+def wkv_state_grads_from_sums(a, b, p, dA, dB):
+    """Gradient of the loss with respect to a stable state (a, b, p), from its
+    gradient (dA, dB) with respect to the plain sums it stands for,
+    A = a e^p, B = b e^p: ga = e^p dA, gb = e^p dB, gp = a ga + b gb.  An empty
+    state (b <= 0, the empty history whatever a and p hold) is a constant: all
+    three are zero."""
+    a, b, p, dA, dB = _f64(a, b, p, dA, dB)
+    live = b > 0
+    f = np.where(live, np.exp(np.where(live, p, 0.0)), 0.0)
+    ga = f * dA
+    gb = f * dB
+    return ga, gb, a * ga + b * gb
+
+
+def wkv_sums_grads_from_state(ga, gb, p):
+    """Gradient (gA, gB) with respect to the plain sums (A, B) = (a e^p, b e^p)
+    from the gradient (ga, gb) with respect to (a, b) at that p:
+    gA = ga e^{-p}, gB = gb e^{-p}.  (The gradient with respect to p is then
+    a ga + b gb for any loss that depends on the state only through the sums,
+    so it carries nothing more.)"""
+    ga, gb, p = _f64(ga, gb, p)
+    f = np.exp(-p)
+    return ga * f, gb * f
 
 
 def wkv_step_ref(w, u, k, v, a, b, p):
