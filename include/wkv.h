@@ -229,6 +229,51 @@ wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype,
                           void* hip_stream);
 
 /*
+ * wkv_backward_state - gradients through a segment that starts from a given
+ * state and hands its state on: the backward of wkv_forward_state.
+ *
+ * Defines (derived; the pages print no backward): with the history A_0, B_0
+ * of (a_in, b_in, p_in) and the handed-on sums A_T, B_T, the gradients of
+ *     L = sum_{b,t,c} gy * y + sum_{b,c} (gA A_T + gB B_T),
+ * where gA = ga_out e^{-p_out}, gB = gb_out e^{-p_out} are the gradient of L
+ * with respect to (a_out, b_out) as wkv_forward_state wrote them, carried to
+ * the plain sums they stand for.  Carrying the state from segment to segment is
+ * "RWKV模型深度研究报告" section 4.4.2; run backwards, the gradients the later
+ * segment returns for its given state are this segment's (ga_out, gb_out).
+ *   dk, dv [B, T, C] and dw, du [C] as wkv_backward; dw includes the decay of
+ *   the given history itself (e^{-w t} A_0 before every token t).
+ *   ga_in, gb_in, gp_in [B, C]: the gradient of L with respect to a_in, b_in,
+ *   p_in (A_0 = a_in e^{p_in}, B_0 = b_in e^{p_in}): e^{p_in} dL/dA_0,
+ *   e^{p_in} dL/dB_0 and a_in ga_in + b_in gb_in.  An empty given state
+ *   (b_in <= 0) is a constant: zeros.
+ * No gradient of p_out is taken: for a loss that depends on the handed-on
+ * state only through the sums it stands for it is a_out ga_out + b_out gb_out.
+ *
+ * a_in, b_in, p_in     the state wkv_forward_state was given, or all NULL
+ *                      (the empty history).
+ * ga_out, gb_out, p_out [B, C] float32, all NULL (no gradient on the handed-on
+ *                      state) or all set; p_out is the p_out that
+ *                      wkv_forward_state wrote.
+ * ga_in, gb_in, gp_in  [B, C] float32, all NULL or all set (then a_in is
+ *                      required); fully overwritten.  They must not alias
+ *                      other arguments.
+ * ckpt                 NULL, or what wkv_forward_state wrote for these inputs
+ *                      and this given state.
+ * Other arguments, workspace (wkv_workspace_bytes(WKV_OP_BACKWARD, ...)) and
+ * errors as wkv_backward.  With every state argument NULL this is
+ * wkv_backward.  With T == 0: dw = du = 0 and the handed-on state's gradient
+ * passes back to the given state.
+ */
+wkv_status_t wkv_backward_state(int64_t B, int64_t T, int64_t C, int in_dtype,
+                                const float* w, const float* u, const void* k, const void* v,
+                                const void* gy, const float* a_in, const float* b_in, const float* p_in,
+                                const float* ga_out, const float* gb_out, const float* p_out,
+                                float* dk, float* dv, float* dw, float* du,
+                                float* ga_in, float* gb_in, float* gp_in,
+                                const void* ckpt, void* workspace, size_t workspace_bytes,
+                                void* hip_stream);
+
+/*
  * wkv_forward_gated / wkv_backward_gated - the operator with the receptance
  * gate of the time-mixing output fused in.
  *

@@ -25,6 +25,7 @@ EXPORTS = (
     "wkv_forward_state",
     "wkv_forward_state_noalloc",
     "wkv_backward",
+    "wkv_backward_state",
     "wkv_forward_gated",
     "wkv_backward_gated",
     "wkv_step",
@@ -89,6 +90,9 @@ def declare(L):
     L.wkv_forward_state_noalloc.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp]
     L.wkv_backward.restype = i32
     L.wkv_backward.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
+    L.wkv_backward_state.restype = i32
+    L.wkv_backward_state.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                     fp, fp, fp, vp, vp, sz, vp]
     L.wkv_forward_gated.restype = i32
     L.wkv_forward_gated.argtypes = [i64, i64, i64, i32, fp, fp, vp, vp, vp, fp, vp, vp, sz, vp]
     L.wkv_backward_gated.restype = i32

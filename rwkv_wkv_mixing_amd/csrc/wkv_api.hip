@@ -82,6 +82,24 @@ ShiftPlan shift_plan(int64_t B, int64_t T, int64_t C, int64_t M, int dt) {
     return p;
 }
 
+// T == 0 through carried state: the handed-on state is the given one, so its gradient passes back,
+// from the representation at p_out to that at p_in (zeros for an empty given state).
+__global__ void state_grad_passthrough_kernel(int64_t n, const float* a_in, const float* b_in, const float* p_in,
+                                              const float* ga_out, const float* gb_out, const float* p_out,
+                                              float* ga_in, float* gb_in, float* gp_in) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    double ga = 0.0, gb = 0.0;
+    if (ga_out != nullptr && b_in[i] > 0.f && p_out[i] > -1e30f) {
+        const double f = exp(static_cast<double>(p_in[i]) - static_cast<double>(p_out[i]));
+        ga = ga_out[i] * f;
+        gb = gb_out[i] * f;
+    }
+    ga_in[i] = static_cast<float>(ga);
+    gb_in[i] = static_cast<float>(gb);
+    gp_in[i] = static_cast<float>(fma(static_cast<double>(a_in[i]), ga, static_cast<double>(b_in[i]) * gb));
+}
+
 __global__ void zero2_kernel(int64_t n, float* a, float* b) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < n) {
@@ -250,6 +268,52 @@ wkv_status_t wkv_backward(int64_t B, int64_t T, int64_t C, int in_dtype, const f
         return WKV_EWORKSPACE;
     wkv::BwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, gy, dk, dv, dw, du, ckpt, p.nblk,
                    workspace, workspace_bytes};
+    return hip_status(wkv::launch_bwd_chunk(a, stream));
+}
+
+wkv_status_t wkv_backward_state(int64_t B, int64_t T, int64_t C, int in_dtype, const float* w,
+                                const float* u, const void* k, const void* v, const void* gy,
+                                const float* a_in, const float* b_in, const float* p_in, const float* ga_out,
+                                const float* gb_out, const float* p_out, float* dk, float* dv, float* dw,
+                                float* du, float* ga_in, float* gb_in, float* gp_in, const void* ckpt,
+                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const Plan p = plan(WKV_OP_BACKWARD, B, T, C, in_dtype);
+    if (p.st != WKV_OK) return p.st;
+    const bool sin = a_in || b_in || p_in, sout = ga_out || gb_out || p_out, gin = ga_in || gb_in || gp_in;
+    if ((sin && !(a_in && b_in && p_in)) || (sout && !(ga_out && gb_out && p_out)) ||
+        (gin && !(ga_in && gb_in && gp_in)) || (gin && !sin))
+        return WKV_EINVAL;
+    const float* st4[9] = {a_in, b_in, p_in, ga_out, gb_out, p_out, ga_in, gb_in, gp_in};
+    for (const float* q : st4)
+        if (q && !aligned(q, 4)) return WKV_EALIGN;
+    if (C == 0) return WKV_OK;
+    if (!dw || !du) return WKV_EINVAL;
+    if (!aligned(dw, 4) || !aligned(du, 4)) return WKV_EALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p.N == 0) {  // empty sums: dw = du = 0; with T == 0 the state's gradient passes back
+        hipLaunchKernelGGL(zero2_kernel, dim3(static_cast<unsigned>((C + 255) / 256)), dim3(256), 0,
+                           stream, C, dw, du);
+        hipError_t e = hipGetLastError();
+        const int64_t n = B * C;
+        if (e == hipSuccess && gin && n > 0) {
+            hipLaunchKernelGGL(state_grad_passthrough_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                               0, stream, n, a_in, b_in, p_in, ga_out, gb_out, p_out, ga_in, gb_in, gp_in);
+            e = hipGetLastError();
+        }
+        return hip_status(e);
+    }
+    if (!w || !u || !k || !v || !gy || !dk || !dv) return WKV_EINVAL;
+    const size_t es = in_size(in_dtype);
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(dk, 4) || !aligned(dv, 4) ||
+        !aligned(k, es) || !aligned(v, es) || !aligned(gy, es) || (ckpt && !aligned(ckpt, 4)))
+        return WKV_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 256)))
+        return WKV_EWORKSPACE;
+    wkv::BwdArgs a{B, T, C, in_dtype == WKV_BF16, w, u, k, v, gy, dk, dv, dw, du, ckpt, p.nblk,
+                   workspace, workspace_bytes};
+    a.a_in = a_in; a.b_in = b_in; a.p_in = p_in;
+    a.ga_out = ga_out; a.gb_out = gb_out; a.p_out = p_out;
+    a.ga_in = ga_in; a.gb_in = gb_in; a.gp_in = gp_in;
     return hip_status(wkv::launch_bwd_chunk(a, stream));
 }
 

@@ -66,6 +66,18 @@ struct BwdChunk {
     float* part;           // [ntiles][nblocks][2][64]: dw, du partial sums
     const void* r;         // receptance [B, T, C] (gated kernels; gy is then the gradient of sigmoid(r) y)
     float* dr;             // [B, T, C] gradient of r (gated kernels)
+    // backward through carried state (St kernels), each [B, C] or NULL: the state given before the
+    // first token (a, b, p), the gradient (ga, gb) of the state handed on after the last token at the
+    // p the forward wrote, and the gradients of the given state
+    const float* a_in;
+    const float* b_in;
+    const float* p_in;
+    const float* ga_out;
+    const float* gb_out;
+    const float* p_out;
+    float* ga_in;
+    float* gb_in;
+    float* gp_in;
 };
 
 // Reverse carry at log2-scale sg: the true G is G * 2^{-sg}.
@@ -368,6 +380,13 @@ struct SpanIn {
 // products of the reverse sweep: gpi = gy pi, gvy = gy pi vy, gr = gy rho,
 // grpd = gy rho pd, e, vm, ld.  Gated: gy = gout sigmoid(r) and the recompute
 // also writes dr = gout y sigmoid(r) (1 - sigmoid(r)), y = m + pi (v - m).
+// The gradient of the state a backward through carried state hands on, as gradients of the plain
+// sums: gA = ga 2^{-s}, gB = gb 2^{-s} (zero: no gradient).
+struct Seed {
+    float ga = 0.f, gb = 0.f;
+    int s = 0;
+};
+
 template <typename TIn, int L, bool Gated>
 struct Span {
     float gpi[L], gvy[L], gr[L], grpd[L], e[L], vm[L], ld[L];
@@ -376,12 +395,20 @@ struct Span {
     int so;     // scale of the map offsets (and of the whole fast-path sweep)
     bool fast;  // wave-uniform
     MSt x0;
+    float mT;  // the mean after the span's last token (the handed-on state's, in the span ending at T)
 
     // rg: the gate's inputs of the span (used when Gated; not part of SpanIn so
     // that the whole-tile kernel does not double-buffer them)
+    //
+    // Inj (backward through carried state, the span holding token T as its token tcut, 0 < tcut < L):
+    // the tokens from T on read as zeros (gy = 0 included) and add nothing; the handed-on state's
+    // gradient sd joins as the reverse seed of token tcut, so that the carry before that token is
+    // (G, J) = (gA, -gB - m_T gA) with m_T the mean before it.  Through gr and grpd it reaches the
+    // map's offsets and the reverse sweep without further code.
+    template <bool Inj = false>
     __device__ __forceinline__ void recompute(const SpanIn<TIn, L, Gated>& in, const Chunk1<TIn, L>& rg,
                                               const SpanGeo& g, const Chan& ch, float eu, const Decay& dec,
-                                              bool fast_out) {
+                                              bool fast_out, int tcut = 0, const Seed& sd = Seed{}) {
         x0.s = static_cast<int>(in.s0);
         x0.b = in.b0;
         x0.m = in.b0 > 0.f ? in.a0 / in.b0 : 0.f;
@@ -402,6 +429,11 @@ struct Span {
             float dmin = INFINITY;  // smallest denominator (D_t and B_t) used
             const float scf = static_cast<float>(sc);
             acc_t dp = 1;
+            float xg = 0.f, xb = 0.f;  // Inj: gA and gB at the span's scale
+            if (Inj && tcut > 0) {
+                xg = ldx(sd.ga, sc - sd.s);
+                xb = ldx(sd.gb, sc - sd.s);
+            }
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 // e = e^k / 2^sc.  For the key that sets the scale fma(k, log2 e,
@@ -431,11 +463,16 @@ struct Span {
                     gj *= gt.s;
                 }
                 const float gpij = gj * pi;
-                const float grj = gj * r;
+                float grj = gj * r;
+                float grpdj = grj * (pi * dl);
+                if (Inj && j == tcut) {  // wave-uniform (tcut 0: no seed in this span)
+                    grj += xg;
+                    grpdj -= fmaf(m, xg, xb);
+                }
                 gpi[j] = gpij;
                 gvy[j] = gpij * vy;
                 gr[j] = grj;
-                grpd[j] = grj * (pi * dl);
+                grpd[j] = grpdj;
                 e[j] = ej;
                 vm[j] = (db * rb) * dl;
                 ld[j] = ldj;
@@ -451,6 +488,7 @@ struct Span {
                 dp = dec.mul(dp);
             }
             fast = __all(dmin >= kTiny);
+            mT = m;
         }
         if (!fast) {
             // general path: per-token rescales, inputs re-read one token at a
@@ -477,22 +515,35 @@ struct Span {
                 }
                 const double grj = static_cast<double>(gj * q.rho);
                 const double qq = dpd * grj;
-                const double t1 = qq * (static_cast<double>(Psum) + static_cast<double>(q.pd));
-                Gs += static_cast<acc_t>(qq);
+                double t1 = qq * (static_cast<double>(Psum) + static_cast<double>(q.pd));
+                double qi = qq;
+                if (Inj && tcut > 0 && j == tcut) {  // the seed at this token's scale
+                    const double xg = ldexp(static_cast<double>(sd.ga), st.s - sd.s);
+                    const double xb = ldexp(static_cast<double>(sd.gb), st.s - sd.s);
+                    qi += dpd * xg;
+                    t1 += dpd * (xg * static_cast<double>(Psum) - fma(static_cast<double>(m_before), xg, xb));
+                }
+                Gs += static_cast<acc_t>(qi);
                 Js += static_cast<acc_t>(t1);
-                Gps += static_cast<acc_t>(qq * j);
+                Gps += static_cast<acc_t>(qi * j);
                 Jps += static_cast<acc_t>(t1 * j);
                 Psum += static_cast<acc_t>(q.ld);
                 du = fmaf(gj * q.pi, q.vy, du);
                 dpd *= dec.dd;
             }
+            mT = st.m;
         }
     }
 
     // Reverse sweep from the carry at the span's end: writes dk, dv and
     // returns this span's part of -dw.
+    //
+    // St: tcut and sd as recompute's (the general path, which recomputes every token, seeds token
+    // tcut again here).
+    template <bool St = false>
     __device__ __forceinline__ float reverse(const RCarry& C, const SpanGeo& g, const Chan& ch, float eu,
-                                             const Decay& dec, bool fast_out) const {
+                                             const Decay& dec, bool fast_out, int tcut = 0,
+                                             const Seed& sd = Seed{}) const {
         float acc_dw = 0.f;
         if (fast) {
             acc_t G = static_cast<acc_t>(ldexp(C.G, so - C.sg)), J = static_cast<acc_t>(ldexp(C.J, so - C.sg));
@@ -523,6 +574,7 @@ struct Span {
                 for (int j = 0; j < t; ++j)
                     (void)mean_step(st, BufLd<TIn>::at(g.rk, g.vin, j * g.row_in),
                                     BufLd<TIn>::at(g.rv, g.vin, j * g.row_in), ch, eu, fast_out);
+                const float m_before = st.m;
                 const TokQ q = mean_step(st, BufLd<TIn>::at(g.rk, g.vin, t * g.row_in),
                                          BufLd<TIn>::at(g.rv, g.vin, t * g.row_in), ch, eu, fast_out);
                 float gt = BufLd<TIn>::at(g.rg, g.vin, t * g.row_in);
@@ -544,6 +596,12 @@ struct Span {
                 Gp = dec.dd * GG;
                 J = fma(dec.dd, fma(ldt, G, J), grt * static_cast<double>(q.pd));
                 G = fma(dec.dd, G, grt);
+                if (St && tcut > 0 && t == tcut) {  // the carry before token tcut: the seed (G, J were zero)
+                    const double xg = ldexp(static_cast<double>(sd.ga), sg - sd.s);
+                    const double xb = ldexp(static_cast<double>(sd.gb), sg - sd.s);
+                    G += xg;
+                    J -= fma(static_cast<double>(m_before), xg, xb);
+                }
             }
         }
         return acc_dw;
@@ -561,15 +619,24 @@ struct BwdShared {
     uint32_t ticket, tag;
 };
 
+// x: added to the span's offsets (St: the handed-on state's carry carried back to the span's start).
 template <int W, typename TIn, int L, bool Gated>
-__device__ __forceinline__ void put_map(BwdShared<W>& sm, int wave, int lane, const Span<TIn, L, Gated>& sp) {
+__device__ __forceinline__ void put_map(BwdShared<W>& sm, int wave, int lane, const Span<TIn, L, Gated>& sp,
+                                        const RCarry* x = nullptr) {
     sm.mapn[wave][lane] = static_cast<float>(L);
     sm.maps[wave][lane] = sp.so;
     sm.mapd[wave][0][lane] = static_cast<double>(sp.Psum);
-    sm.mapd[wave][1][lane] = static_cast<double>(sp.Gs);
-    sm.mapd[wave][2][lane] = static_cast<double>(sp.Js);
-    sm.mapd[wave][3][lane] = static_cast<double>(sp.Gps);
-    sm.mapd[wave][4][lane] = static_cast<double>(sp.Jps);
+    if (x == nullptr) {
+        sm.mapd[wave][1][lane] = static_cast<double>(sp.Gs);
+        sm.mapd[wave][2][lane] = static_cast<double>(sp.Js);
+        sm.mapd[wave][3][lane] = static_cast<double>(sp.Gps);
+        sm.mapd[wave][4][lane] = static_cast<double>(sp.Jps);
+    } else {
+        sm.mapd[wave][1][lane] = static_cast<double>(sp.Gs) + x->G;
+        sm.mapd[wave][2][lane] = static_cast<double>(sp.Js) + x->J;
+        sm.mapd[wave][3][lane] = static_cast<double>(sp.Gps) + x->Gp;
+        sm.mapd[wave][4][lane] = static_cast<double>(sp.Jps) + x->Jp;
+    }
 }
 
 template <int W>
@@ -654,9 +721,92 @@ __device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P
     if (lane == 0) __hip_atomic_store(P.ct_count + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- backward through carried state (St kernels) --------------------------------
+constexpr double kL2Ed = 1.4426950408889634;  // log2(e)
+
+// The handed-on state's gradient (ga, gb) at the p_T the forward wrote, as gradients of the plain
+// sums (A_T, B_T): gA = ga e^{-p_T} = ga 2^{-q}, q = p_T log2 e, split as (ga 2^{n - q}) 2^{-n}.
+__device__ __forceinline__ Seed load_seed(const BwdChunk& P, int64_t i, bool cok) {
+    Seed sd;
+    if (!cok || P.ga_out == nullptr) return sd;
+    const float pT = P.p_out[i];
+    if (!(pT > -1e30f)) return sd;  // an empty handed-on state
+    const double q = static_cast<double>(pT) * kL2Ed;
+    const double n = rint(q);
+    const float f = ex2(static_cast<float>(n - q));
+    sd.ga = P.ga_out[i] * f;
+    sd.gb = P.gb_out[i] * f;
+    sd.s = static_cast<int>(n);
+    return sd;
+}
+
+// A span ending exactly at T: the seed as the carry at its end, (G, J) = (gA, -gB - m_T gA) at the
+// span's scale, and that carry taken back to the span's start by the span's own map without its
+// offsets (added to the offsets, so earlier spans and blocks receive it).
+template <typename TIn, int L, bool Gated>
+__device__ __forceinline__ RCarry end_seed(const Span<TIn, L, Gated>& sp, const Seed& sd, double dL, RCarry* back) {
+    const double xg = ldexp(static_cast<double>(sd.ga), sp.so - sd.s);
+    const double xb = ldexp(static_cast<double>(sd.gb), sp.so - sd.s);
+    const RCarry X{xg, -fma(static_cast<double>(sp.mT), xg, xb), 0.0, 0.0, sp.so};
+    RMap m = rmap_identity();
+    m.D = dL;
+    m.S = static_cast<double>(sp.Psum);
+    m.n = static_cast<float>(L);
+    m.so = sp.so;
+    *back = rapply(m, X);
+    return X;
+}
+
+// C + X (X's scale brought to C's).
+__device__ __forceinline__ RCarry add_carry(const RCarry& C, const RCarry& X) {
+    const int d = C.sg - X.sg;
+    return RCarry{C.G + ldexp(X.G, d), C.J + ldexp(X.J, d), C.Gp + ldexp(X.Gp, d), C.Jp + ldexp(X.Jp, d), C.sg};
+}
+
+// The gradients of the given state (a, b, p) from the reverse carry C0 before the first token and
+// the history mean m0: for the plain sums dA = G and dB = -(J + m0 G), so ga = e^p dA, gb = e^p dB
+// and gp = a ga + b gb = -B J (B = b e^p).  Returns the history's part of dw, B J' (its decay before
+// every token).  An empty given state (b <= 0) is a constant: zeros.
+__device__ __forceinline__ float state_grads(const BwdChunk& P, int64_t i, bool cok, const RCarry& C0, float m0) {
+    if (!cok || P.a_in == nullptr) return 0.f;
+    const float bi = P.b_in[i];
+    float ga = 0.f, gb = 0.f, gp = 0.f, hist = 0.f;
+    if (bi > 0.f) {
+        const double f = exp2(static_cast<double>(P.p_in[i]) * kL2Ed - static_cast<double>(C0.sg));
+        ga = static_cast<float>(C0.G * f);
+        gb = static_cast<float>(-fma(static_cast<double>(m0), C0.G, C0.J) * f);
+        gp = static_cast<float>(-static_cast<double>(bi) * C0.J * f);
+        hist = static_cast<float>(static_cast<double>(bi) * C0.Jp * f);
+    }
+    if (P.ga_in != nullptr) {
+        P.ga_in[i] = ga;
+        P.gb_in[i] = gb;
+        P.gp_in[i] = gp;
+    }
+    return hist;
+}
+
+// St: T - t0 for the span of wave `wave` in time block blk that holds token T-1 (1..L: token T is
+// its token tcut, or its end when tcut = L), else 0.
+template <int L, int W>
+__device__ __forceinline__ int span_cut(int64_t T, int64_t blk, int wave) {
+    const int64_t left = T - (blk * static_cast<int64_t>(L * W) + static_cast<int64_t>(wave) * L);
+    return (left > 0 && left <= L) ? static_cast<int>(left) : 0;
+}
+
+// One span's recompute, with the seed where the span holds token T (St).
+template <bool St, typename TIn, int L, bool Gated>
+__device__ __forceinline__ void span_recompute(Span<TIn, L, Gated>& sp, const SpanIn<TIn, L, Gated>& in,
+                                               const Chunk1<TIn, L>& rg, const SpanGeo& g, const Chan& ch, float eu,
+                                               const Decay& dec, bool fast_out, int tcut, const Seed& sd) {
+    sp.template recompute<St>(in, rg, g, ch, eu, dec, fast_out, tcut < L ? tcut : 0, sd);
+}
+
 // Time-split backward: one workgroup per (tile, time block); blocks are
-// chained backward in time through the coherent carry slots.
-template <typename TIn, int L, int W, bool Gated>
+// chained backward in time through the coherent carry slots.  St: through
+// carried state (the handed-on state's gradient joins at token T; block 0
+// returns the given state's gradients and adds the history's part of dw).
+template <typename TIn, int L, int W, bool Gated, bool St = false>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk P) {
     __shared__ BwdShared<W> sm;
     const int lane = threadIdx.x & 63;
@@ -697,12 +847,22 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     Chunk1<TIn, L> rg;
     if (Gated) rg.load(g.rr, g.vin, g.row_in);
     Span<TIn, L, Gated> sp;
-    sp.recompute(in, rg, g, ch, eu, dec, fast_out);
-    put_map(sm, wave, lane, sp);
+    const int tcut = St ? span_cut<L, W>(P.T, blk, wave) : 0;
+    const Seed sd = (St && tcut > 0) ? load_seed(P, b * P.C + c, cok) : Seed{};
+    span_recompute<St>(sp, in, rg, g, ch, eu, dec, fast_out, tcut, sd);
+    RCarry X{0.0, 0.0, 0.0, 0.0, 0};  // St, the span ending at T: the seed at its end
+    if (St && tcut == L) {  // wave-uniform
+        RCarry back;
+        X = end_seed(sp, sd, dL, &back);
+        put_map(sm, wave, lane, sp, &back);
+    } else {
+        put_map(sm, wave, lane, sp);
+    }
     lds_sync();
 
     RMap suf = rmap_identity();
     for (int i = W - 1; i > wave; --i) suf = rcompose(get_map(sm, i, lane, dL), suf);
+    float hist = 0.f;
     if (wave == 0) {
         RCarry cin{0.0, 0.0, 0.0, 0.0, 0};
         if (P.nblocks > 1) {
@@ -711,6 +871,8 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
             if (blk < P.nblocks - 1) cin = wait_carry(rc, slot + 64 * kCarrySlot, tag, P.spin, P.hdr);  // block blk+1
             if (blk > 0) publish_carry(rc, slot, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin), tag);
         }
+        if (St && blk == 0)  // the carry before the first token
+            hist = state_grads(P, b * P.C + c, cok, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin), sp.x0.m);
         sm.cin[0][lane] = cin.G;
         sm.cin[1][lane] = cin.J;
         sm.cin[2][lane] = cin.Gp;
@@ -718,9 +880,10 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
         sm.cin_s[lane] = cin.sg;
     }
     lds_sync();
-    const RCarry C = rapply(suf, RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane],
-                                        sm.cin_s[lane]});
-    const float ndw = sp.reverse(C, g, ch, eu, dec, fast_out);
+    RCarry C = rapply(suf, RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane],
+                                  sm.cin_s[lane]});
+    if (St && tcut == L) C = add_carry(C, X);
+    const float ndw = sp.template reverse<St>(C, g, ch, eu, dec, fast_out, tcut < L ? tcut : 0, sd) - hist;
     const int64_t ct = tile - b * P.nct;
     put_partials(sm, P, b, ct, blk, wave, lane, ndw, sp.du);
     if (P.nblocks > 1) {  // every wave is past its carry traffic
@@ -740,7 +903,9 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
 // a second block in registers.  Each wave copies and reads only its own span,
 // so the waits are per wave: wait_staged() before reading a block from LDS,
 // and wait_lds_reads() after, before the next copy may overwrite it.
-template <typename TIn, int L, int W, bool Gated, bool Staged>
+//
+// St: through carried state, as the time-split kernel.
+template <typename TIn, int L, int W, bool Gated, bool Staged, bool St = false>
 __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk P) {
     // r joins the staged inputs when it is bf16 (as float32 it would cost the second workgroup per CU)
     constexpr int kNI = (Gated && sizeof(TIn) == 2) ? 4 : 3;
@@ -762,6 +927,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
 
     RCarry cin{0.0, 0.0, 0.0, 0.0, 0};  // carry at the current block's end (same in every wave)
     float ndw = 0.f, du = 0.f;
+    float m0 = 0.f;  // St: the mean at the span's start (at the end of the loop: before the first token)
     SpanIn<TIn, L, Gated> cur, nxt;  // nxt: only the next block's saved state (Staged)
     const int64_t c0 = (tile - b * P.nct) * 64;
     if constexpr (Staged) {
@@ -790,9 +956,19 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
         }
         if constexpr (Gated && !(Staged && kNI == 4)) rg.load(g.rr, g.vin, g.row_in);
         Span<TIn, L, Gated> sp;
-        sp.recompute(cur, rg, g, ch, eu, dec, fast_out);
+        const int tcut = St ? span_cut<L, W>(P.T, blk, wave) : 0;
+        const Seed sd = (St && tcut > 0) ? load_seed(P, b * P.C + c, cok) : Seed{};
+        span_recompute<St>(sp, cur, rg, g, ch, eu, dec, fast_out, tcut, sd);
         du += sp.du;
-        put_map(sm, wave, lane, sp);
+        RCarry X{0.0, 0.0, 0.0, 0.0, 0};  // St, the span ending at T: the seed at its end
+        if (St && tcut == L) {  // wave-uniform: the last block only
+            RCarry back;
+            X = end_seed(sp, sd, dL, &back);
+            put_map(sm, wave, lane, sp, &back);
+        } else {
+            put_map(sm, wave, lane, sp);
+        }
+        if constexpr (St) m0 = sp.x0.m;
         lds_sync_lgkm();
         RMap suf = rmap_identity();
         for (int i = W - 1; i > wave; --i) suf = rcompose(get_map(sm, i, lane, dL), suf);
@@ -804,9 +980,14 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
             sm.cin[3][lane] = out.Jp;
             sm.cin_s[lane] = out.sg;
         }
-        ndw += sp.reverse(rapply(suf, cin), g, ch, eu, dec, fast_out);
+        RCarry C = rapply(suf, cin);
+        if (St && tcut == L) C = add_carry(C, X);
+        ndw += sp.template reverse<St>(C, g, ch, eu, dec, fast_out, tcut < L ? tcut : 0, sd);
         lds_sync_lgkm();
         cin = RCarry{sm.cin[0][lane], sm.cin[1][lane], sm.cin[2][lane], sm.cin[3][lane], sm.cin_s[lane]};
+    }
+    if constexpr (St) {  // cin is the carry before the first token, m0 wave 0's history mean there
+        if (wave == 0) ndw -= state_grads(P, b * P.C + c, cok, cin, m0);
     }
     put_partials(sm, P, b, tile - b * P.nct, 0, wave, lane, ndw, du);
 }
@@ -870,9 +1051,13 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     const BwdLayout l = bwd_layout(a.B, a.T, a.C);
     char* ws = static_cast<char*>(a.ws);
     const float* ckpt = static_cast<const float*>(a.ckpt);
+    const bool st = a.a_in != nullptr || a.ga_out != nullptr || a.ga_in != nullptr;  // through carried state
     if (ckpt == nullptr) {  // recompute the block-start states with the forward (no y written)
         FwdArgs f{a.B, a.T, a.C, a.bf16, a.w, a.u, a.k, a.v, nullptr, ws + l.off_ckpt, l.nblk_ck,
                   ws + l.off_fws, l.fws_bytes};
+        f.a_in = a.a_in;
+        f.b_in = a.b_in;
+        f.p_in = a.p_in;
         const hipError_t e = launch_fwd_chunk(f, stream);
         if (e != hipSuccess) return e;
         ckpt = reinterpret_cast<const float*>(ws + l.off_ckpt);
@@ -892,6 +1077,9 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     P.du = a.du;
     P.hdr = reinterpret_cast<CallHdr*>(ws);
     P.spin = spin_limit();
+    P.a_in = a.a_in; P.b_in = a.b_in; P.p_in = a.p_in;
+    P.ga_out = a.ga_out; P.gb_out = a.gb_out; P.p_out = a.p_out;
+    P.ga_in = a.ga_in; P.gb_in = a.gb_in; P.gp_in = a.gp_in;
 
     // Enough tiles to give every CU two workgroups: one workgroup per tile
     // walks the whole sequence (no carries between workgroups).
@@ -907,7 +1095,11 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
         const bool staged = WKV_BWD_STAGE && a.C % (16 / static_cast<int64_t>(sizeof(TIn))) == 0 && a16(a.k) &&
                             a16(a.v) && a16(a.gy) && (P.r == nullptr || sizeof(TIn) != 2 || a16(P.r));
         const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * kBwdTileW);
-        if (P.r != nullptr && staged)
+        if (st && staged)
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false, true, true>), grid, block, 0, stream, P);
+        else if (st)
+            hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, false, false, true>), grid, block, 0, stream, P);
+        else if (P.r != nullptr && staged)
             hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true, true>), grid, block, 0, stream, P);
         else if (P.r != nullptr)
             hipLaunchKernelGGL((bwd_tile_kernel<TIn, kBwdL, kBwdTileW, true, false>), grid, block, 0, stream, P);
@@ -922,7 +1114,10 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     P.npb = l.nblocks;
     P.carry = reinterpret_cast<float*>(ws + l.off_carry);
     P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
-    if (P.r != nullptr)
+    if (st)
+        hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW, false, true>),
+                           dim3(static_cast<unsigned>(l.ntiles * l.nblocks)), dim3(64 * kBwdW), 0, stream, P);
+    else if (P.r != nullptr)
         hipLaunchKernelGGL((bwd_chunk_kernel<TIn, kBwdL, kBwdW, true>),
                            dim3(static_cast<unsigned>(l.ntiles * l.nblocks)), dim3(64 * kBwdW), 0, stream, P);
     else

@@ -64,6 +64,18 @@ struct BwdArgs {
     // sigmoid(r) y, and dr [B, T, C] float32 receives the gradient of r
     const void* r = nullptr;
     float* dr = nullptr;
+    // optional, through carried state ([B, C] each; each triple all NULL or all set): the state before
+    // token 1 (as FwdArgs), the gradient (ga, gb) of the state after token T at the p the forward
+    // wrote, and the gradients (ga, gb, gp) of the state before token 1 (needs a_in)
+    const float* a_in = nullptr;
+    const float* b_in = nullptr;
+    const float* p_in = nullptr;
+    const float* ga_out = nullptr;
+    const float* gb_out = nullptr;
+    const float* p_out = nullptr;
+    float* ga_in = nullptr;
+    float* gb_in = nullptr;
+    float* gp_in = nullptr;
 };
 
 struct StepArgs {

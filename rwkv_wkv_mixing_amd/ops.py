@@ -219,6 +219,50 @@ def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None):
     return dk, dv, dw, du
 
 
+def wkv_backward_state(w, u, k, v, gy, *, state_in=None, grad_state_out=None, need_state_grad=True, ckpt=None,
+                       out=None, workspace=None):
+    """Gradients through a segment run by wkv_forward from state_in = (a, b, p)
+    (or the empty history) for L = sum(gy * y) + the loss carried by the state it
+    handed on.  grad_state_out: None or (ga, gb, p_out), the gradient of L with
+    respect to that state's (a_out, b_out) and the p_out the forward wrote.
+    Returns (dk, dv, dw, du, (ga_in, gb_in, gp_in)), the last None unless
+    state_in is given and need_state_grad; dw includes the history's decay."""
+    _need(k, "k", (torch.float32, torch.bfloat16))
+    dev = k.device
+    B, T, C = k.shape
+    _need(v, "v", k.dtype, (B, T, C), dev)
+    _need(gy, "gy", k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    for name, st3 in (("state_in", state_in), ("grad_state_out", grad_state_out)):
+        if st3 is not None:
+            for t, n in zip(st3, "abp"):
+                _need(t, f"{name}.{n}", torch.float32, (B, C), dev)
+    if out is None:
+        dk = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        dv = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        dw = torch.empty((C,), dtype=torch.float32, device=dev)
+        du = torch.empty((C,), dtype=torch.float32, device=dev)
+    else:
+        dk, dv, dw, du = out
+    for t, n, s in ((dk, "dk", (B, T, C)), (dv, "dv", (B, T, C)), (dw, "dw", (C,)), (du, "du", (C,))):
+        _need(t, n, torch.float32, s, dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
+    gin = None
+    if state_in is not None and need_state_grad:
+        gin = tuple(torch.empty((B, C), dtype=torch.float32, device=dev) for _ in range(3))
+    sin = state_in if state_in is not None else (None, None, None)
+    sout = grad_state_out if grad_state_out is not None else (None, None, None)
+    gi = gin if gin is not None else (None, None, None)
+    ws, ws_n = _workspace(L.WKV_OP_BACKWARD, B, T, C, k.dtype, dev, workspace)
+    st = L.lib().wkv_backward_state(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(gy),
+                                    *[_p(t) for t in sin], *[_p(t) for t in sout], _p(dk), _p(dv), _p(dw),
+                                    _p(du), *[_p(t) for t in gi], _p(ckpt), _p(ws), ws_n, _stream(dev))
+    L.check("wkv_backward_state", st)
+    return dk, dv, dw, du, gin
+
+
 def wkv_step(w, u, k, v, a, b, p, *, y=None):
     """One decode token for [L,B,C] states (a, b, p updated in place); returns y."""
     _need(k, "k", (torch.float32, torch.bfloat16))
@@ -269,6 +313,39 @@ class WKVFunction(torch.autograd.Function):
 def wkv(w, u, k, v):
     """Differentiable WKV forward (see WKVFunction)."""
     return WKVFunction.apply(w, u, k, v)
+
+
+class WKVStateFunction(torch.autograd.Function):
+    """Autograd wrapper of a segment with carried state: (y, a_out, b_out,
+    p_out) from (w, u, k, v, a, b, p), for training over a long input split into
+    segments.  The gradient flows through the handed-on state's (a_out, b_out);
+    p_out is marked non-differentiable (its gradient is a_out ga + b_out gb for
+    any loss that depends on the state only through the sums it stands for)."""
+
+    @staticmethod
+    def forward(ctx, w, u, k, v, a, b, p):
+        B, T, C = k.shape
+        ckpt = new_ckpt(B, T, C, k.device)
+        y, (a2, b2, p2) = wkv_forward(w, u, k, v, ckpt=ckpt, state_in=(a, b, p), return_state=True)
+        ctx.save_for_backward(w, u, k, v, a, b, p, p2, ckpt)
+        ctx.mark_non_differentiable(p2)
+        return y, a2, b2, p2
+
+    @staticmethod
+    def backward(ctx, gy, ga, gb, _gp):
+        w, u, k, v, a, b, p, p2, ckpt = ctx.saved_tensors
+        gy = (torch.zeros_like(k) if gy is None else gy.to(k.dtype)).contiguous()
+        ga = torch.zeros_like(a) if ga is None else ga.contiguous()
+        gb = torch.zeros_like(b) if gb is None else gb.contiguous()
+        dk, dv, dw, du, (ga_in, gb_in, gp_in) = wkv_backward_state(
+            w, u, k, v, gy, state_in=(a, b, p), grad_state_out=(ga, gb, p2), ckpt=ckpt)
+        return dw, du, dk.to(k.dtype), dv.to(v.dtype), ga_in, gb_in, gp_in
+
+
+def wkv_with_state(w, u, k, v, a, b, p):
+    """Differentiable WKV forward from a given state (a, b, p) [B, C]; returns
+    (y, a_out, b_out, p_out) (see WKVStateFunction)."""
+    return WKVStateFunction.apply(w, u, k, v, a, b, p)
 
 
 def token_shift(mu, x, *, x_prev=None, out=None):

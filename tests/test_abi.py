@@ -138,6 +138,32 @@ def test_backward_validation(lib):
     assert bwd(lib, 1, 4, 0, L.WKV_F32, *[None] * 9) == L.WKV_OK
 
 
+def bwd_state(lib, B, T, C, dt, x, sin=(None,) * 3, sout=(None,) * 3, gin=(None,) * 3, dw=None):
+    dw = x if dw is None else dw
+    return lib.wkv_backward_state(B, T, C, dt, P(x), P(x), P(x), P(x), P(x), *[P(t) for t in sin],
+                                  *[P(t) for t in sout], P(x), P(x), P(dw), P(x), *[P(t) for t in gin],
+                                  None, None, 0, None)
+
+
+def test_backward_state_validation(lib):
+    """Each state triple all NULL or all set, the given state's gradients only
+    with a given state, 4-byte alignment; checked before any HIP call."""
+    x = A16
+    three = (x, x, x)
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sin=(x, x, None)) == L.WKV_EINVAL
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sout=(None, x, x)) == L.WKV_EINVAL
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sin=three, gin=(x, None, x)) == L.WKV_EINVAL
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, gin=three) == L.WKV_EINVAL  # no given state
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sin=(x, x + 2, x)) == L.WKV_EALIGN
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sout=(x, x, x + 1)) == L.WKV_EALIGN
+    assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sin=three, gin=(x + 2, x, x)) == L.WKV_EALIGN
+    assert bwd_state(lib, 1, 4, 4, 9, x, sin=three) == L.WKV_EDTYPE
+    assert bwd_state(lib, 1, 4, 0, L.WKV_F32, x, sin=three, sout=three, gin=three) == L.WKV_OK  # C = 0
+    ws_need = lib.wkv_workspace_bytes(L.WKV_OP_BACKWARD, 1, 4, 4, L.WKV_F32)
+    if ws_need > 0:
+        assert bwd_state(lib, 1, 4, 4, L.WKV_F32, x, sin=three, sout=three, gin=three) == L.WKV_EWORKSPACE
+
+
 def test_step_validation(lib):
     x = A16
     args = [x] * 8
