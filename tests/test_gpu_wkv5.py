@@ -60,11 +60,11 @@ def dev_inputs(p):
 
 
 
-NORM_TOL = 2.0 ** -6
+NORM_TOL = 2.0 ** -7
 
 
 def check_norm(name, got, ref):
-    """Normwise accuracy on random inputs: ||got - ref|| <= 2^-6 ||ref||.  Not a rounding bound:
+    """Normwise accuracy on random inputs: ||got - ref|| <= 2^-7 ||ref||.  Not a rounding bound:
     it checks that the errors do not add up coherently, which a magnitude-sum bound cannot see
     where a signed sum cancels."""
     g = np.asarray(got, np.float64)
