@@ -939,7 +939,12 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_tile_kernel(BwdChunk 
         const SpanGeo g = span_geo<TIn, L, W>(P, b, c, cok, blk, wave);
         Chunk1<TIn, L> rg;
         if constexpr (Staged) {
-            wait_staged();
+            // after the first block, every path issued at least the 2 L dv, dk stores of the
+            // previous block after this block's copies
+            if (blk == P.nblocks - 1)
+                wait_staged();
+            else
+                wait_staged_before<2 * L>();
             cur.load_lds(stage, wave, lane);
             if constexpr (kNI == 4) rg.load_lds(stage.x[wave][3], lane);
             cur.a0 = nxt.a0;

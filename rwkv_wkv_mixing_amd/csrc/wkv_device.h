@@ -136,6 +136,14 @@ __device__ __forceinline__ void stage_rows(Rsrc r, TIn (*dst)[64], int64_t row0,
 // rows), and on its LDS reads (before a copy may overwrite them).  As asm
 // statements they also keep the compiler from moving memory accesses across.
 __device__ __forceinline__ void wait_staged() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same where at least N vector memory instructions were issued after the copies: the counter
+// drops in issue order, so this waits for the copies without waiting for the N later ones (the
+// previous block's output stores) to complete.
+template <int N>
+__device__ __forceinline__ void wait_staged_before() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // One input over L tokens of a lane (token j at soffset j * row), held in

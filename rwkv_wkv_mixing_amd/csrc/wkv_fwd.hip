@@ -575,7 +575,12 @@ __global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
     for (int64_t blk = 0; blk < P.nblocks; ++blk) {
         const FwdGeo g = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk, wave);
         uint32_t kv[L];
-        wait_staged();
+        // after the first block, every path issued at least the L output stores of the previous
+        // block after this block's copies (outputs runs corrected_outputs whenever y is wanted)
+        if (blk == 0 || P.y == nullptr)
+            wait_staged();
+        else
+            wait_staged_before<L>();
 #pragma unroll
         for (int j = 0; j < L; ++j)
             kv[j] = static_cast<uint32_t>(stage.x[wave][0][j][lane]) |
