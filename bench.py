@@ -96,19 +96,27 @@ def cpu_oracle(p, with_bwd=True):
     return float(np.median(runs)), int(used), t_np
 
 
-def kernel_source_hash():
-    """sha256 over the kernel sources and the C header: a recorded traffic
-    figure applies only to the kernels it was measured on."""
+# The sources that define each workload family's kernels and their launch paths: a recorded
+# traffic figure applies only while these are unchanged.
+KERNEL_FILES = {
+    "rwkv4": ("wkv_fwd.hip", "wkv_bwd.hip", "wkv_scan.h", "wkv_device.h", "wkv_launch.h"),
+    "step": ("wkv_step.hip", "wkv_device.h", "wkv_launch.h"),
+    "shift": ("wkv_shift.hip", "wkv_device.h", "wkv_launch.h"),
+    "matrix": ("wkv5.hip", "wkv_api.hip", "wkv_scan.h", "wkv_device.h", "wkv_launch.h"),
+}
+
+
+def kernel_source_hash(family):
+    """sha256 over the sources of one family's kernels (KERNEL_FILES)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "rwkv_wkv_mixing_amd", "csrc", "*")))
-    for f in files + [os.path.join(ROOT, "include", "wkv.h")]:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in KERNEL_FILES[family]:
+        with open(os.path.join(ROOT, "rwkv_wkv_mixing_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic(workload, call):
+def recorded_traffic(workload, call, family):
     """HBM bytes per call of `call` recorded in profiles/hbm_traffic_<workload>.md
     (FETCH_SIZE / WRITE_SIZE counters scaled by the copy-kernel calibration),
     or None when absent or measured on other kernel sources."""
@@ -124,7 +132,7 @@ def recorded_traffic(workload, call):
                 for item in line.split(":", 1)[1].split():
                     k, v = item.split("=")
                     vals[k] = int(v)
-    if src != kernel_source_hash():
+    if src != kernel_source_hash(family):
         return None
     return vals.get(call)
 
@@ -237,7 +245,7 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state
         "call_us": {"wkv_forward": fwd, "wkv_backward": bwd},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(traffic_key(p, with_bwd), dom),
+                     "traffic": recorded_traffic(traffic_key(p, with_bwd), dom, "rwkv4"),
                      "alg_bytes_per_launch": dom_bytes},
     }
     return out
@@ -296,7 +304,7 @@ def bench_step5(args):
         "call_us": {"wkv_step": st},
         "roofline": {"bound": "hbm", "kernel": "wkv_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("step_bf16_L32_B256_C4096", "wkv_step"),
+                     "traffic": recorded_traffic("step_bf16_L32_B256_C4096", "wkv_step", "step"),
                      "alg_bytes_per_launch": 32 * n},
     }
     if not args.no_cpu:
@@ -465,7 +473,7 @@ def bench_wkv6_decode(args):
         "call_us": {"wkv6_forward(T=1)": st},
         "roofline": {"bound": "hbm", "kernel": "wkv6_forward (one-token kernel)", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("wkv6decode_L32_B256_H64", "wkv6_step"),
+                     "traffic": recorded_traffic("wkv6decode_L32_B256_H64", "wkv6_step", "matrix"),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:
@@ -551,7 +559,7 @@ def bench_shift(args):
         "call_us": {"wkv_token_shift": fwd, "wkv_token_shift_backward": bwd},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("shift_bf16_B8_T1024_C4096_M3", dom),
+                     "traffic": recorded_traffic("shift_bf16_B8_T1024_C4096_M3", dom, "shift"),
                      "alg_bytes_per_launch": dom_bytes},
     }
     if not args.no_cpu:
@@ -617,7 +625,7 @@ def bench_wkv5(args):
         "call_us": {"wkv5_forward": st},
         "roofline": {"bound": "hbm", "kernel": "wkv5_forward", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("wkv5_bf16_B8_T1024_H64", "wkv5_forward"),
+                     "traffic": recorded_traffic("wkv5_bf16_B8_T1024_H64", "wkv5_forward", "matrix"),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:
@@ -685,7 +693,7 @@ def bench_wkv6(args):
         "call_us": {"wkv6_forward": st},
         "roofline": {"bound": "hbm", "kernel": "wkv6_forward", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("wkv6_bf16_B8_T1024_H64", "wkv6_forward"),
+                     "traffic": recorded_traffic("wkv6_bf16_B8_T1024_H64", "wkv6_forward", "matrix"),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:
@@ -788,7 +796,7 @@ def bench_matrix_train(args, gen, long=False):
         "call_us": {f"{n_fwd}(ckpt)": st_f, f"{n_bwd}(ckpt)": st_b},
         "roofline": {"bound": "hbm", "kernel": f"{n_bwd} (backward kernel + du{'/dw' if gen == 5 else ''} batch sum)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None if long else recorded_traffic(f"wkv{gen}train_bf16_B8_T1024_H64", f"wkv{gen}_bwd"),
+                     "traffic": None if long else recorded_traffic(f"wkv{gen}train_bf16_B8_T1024_H64", f"wkv{gen}_bwd", "matrix"),
                      "alg_bytes_per_launch": alg_b},
     }
     if not args.no_cpu:
