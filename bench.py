@@ -922,6 +922,41 @@ def bench_stream(args):
             torch.cuda.empty_cache()
             table.append({"read": nr, "write": nw, "bytes": (nr + nw) * n16 * 16, "best": best, "sweep": rows})
             print(f"stream {nr}:{nw} {total >> 20} MB: best {best}", file=sys.stderr, flush=True)
+    # the tile kernels' own access order (wkv_tile_pattern_launch): a 64-channel tile per workgroup
+    # walking B=8 T=1024 C=4096 in blocks, bf16 inputs staged through LDS, float32 outputs per lane
+    L.wkv_tile_pattern_launch.restype = ctypes.c_int
+    L.wkv_tile_pattern_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    B, T, C = 8, 1024, 4096
+    tiled = []
+    for nr, nw, what in ((2, 1, "forward: k, v in, y out"), (3, 2, "backward: k, v, gy in, dk, dv out")):
+        sets = [([torch.zeros(B * T * C, dtype=torch.bfloat16, device=dev) for _ in range(nr)],
+                 [torch.empty(B * T * C, dtype=torch.float32, device=dev) for _ in range(nw)]) for _ in range(3)]
+        ptrs = [((ctypes.c_void_p * 4)(*[t.data_ptr() for t in ins]), (ctypes.c_void_p * 4)(*[t.data_ptr() for t in outs]))
+                for ins, outs in sets]
+
+        def tlaunch(i):
+            ins, outs = ptrs[i % len(ptrs)]
+            rc = L.wkv_tile_pattern_launch(nr, nw, ins, outs, B, T, C, sptr)
+            if rc != 0:
+                raise RuntimeError(f"wkv_tile_pattern_launch failed: {rc}")
+
+        for i in range(2):
+            tlaunch(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            evs[i][0].record(stream)
+            tlaunch(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+        nbytes = B * T * C * (2 * nr + 4 * nw)
+        tiled.append({"read": nr, "write": nw, "what": what, "bytes": nbytes, "us": round(us, 2),
+                      "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+        print(f"tiled {what}: {tiled[-1]}", file=sys.stderr, flush=True)
+        del sets, ptrs
+        torch.cuda.empty_cache()
     copy = [t for t in table if t["read"] == 1 and t["write"] == 1 and t["bytes"] <= (512 << 20)][0]
     return {"metric": "HBM streaming ceiling GB/s (read + write bytes), best over grids and variants",
             "value": copy["best"]["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 2,
@@ -931,7 +966,7 @@ def bench_stream(args):
             "peak": HBM_PEAK_GBPS,
             "ceiling": [{"read": t["read"], "write": t["write"], "bytes": t["bytes"], **t["best"],
                          "frac_of_peak": round(t["best"]["gbps"] / HBM_PEAK_GBPS, 4)} for t in table],
-            "sweep": table}
+            "tiled": tiled, "sweep": table}
 
 
 def main():
