@@ -245,14 +245,17 @@ def bench_seq(args, p, with_bwd, workload_name, bytes_fwd, bytes_bwd, with_state
         "call_us": {"wkv_forward": fwd, "wkv_backward": bwd},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(traffic_key(p, with_bwd), dom, "rwkv4"),
+                     "traffic": recorded_traffic(traffic_key(p, with_bwd, gated, with_state), dom, "rwkv4"),
                      "alg_bytes_per_launch": dom_bytes},
     }
     return out
 
 
-def traffic_key(p, with_bwd):
-    return f"{'fwdbwd' if with_bwd else 'fwd'}_{p.dtype}_B{p.B}_T{p.T}_C{p.C}"
+def traffic_key(p, with_bwd, gated=False, with_state=False):
+    """Name of the HBM-traffic summary of this workload (a gated or state-carrying call runs other
+    kernel variants, measured under names of their own)."""
+    kind = ("fwdbwd" if with_bwd else "fwd") + ("gated" if gated else "") + ("state" if with_state else "")
+    return f"{kind}_{p.dtype}_B{p.B}_T{p.T}_C{p.C}"
 
 
 def bench_step5(args):

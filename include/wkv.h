@@ -40,8 +40,10 @@
  *    the next: its counters back at zero, its generation advanced (the
  *    carries between workgroups are tagged with the call's generation instead
  *    of being cleared on every call, which would take a kernel of its own).
- *    The first 16 bytes are a header; bytes 4..7 are an error word that the
- *    calls only ever set: read it with wkv_workspace_status().
+ *    Forward and backward calls of any shape may share one buffer of the
+ *    largest size they need: the counters sit at fixed offsets for every
+ *    shape.  The first 16 bytes are a header; bytes 4..7 are an error word
+ *    that the calls only ever set: read it with wkv_workspace_status().
  *  - Status codes: nothing aborts and no exception crosses the ABI.
  *    WKV_EINVAL    a dimension < 0, or a NULL pointer where data is needed;
  *    WKV_EDTYPE    unknown input dtype or op;

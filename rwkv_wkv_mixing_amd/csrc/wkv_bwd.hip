@@ -55,9 +55,11 @@ struct BwdChunk {
     const float* ckpt;
     int64_t nblk_ck;
     int64_t nct, ntiles, nblocks;
-    CallHdr* hdr;          // workspace header: tickets, error word, generation (time-split kernel)
+    CallHdr* hdr;          // workspace header: error word, finished streams, generation (time-split kernel)
+    StreamCtr* sc;         // [kMaxStreams] ticket streams (time-split kernel)
+    int64_t nstream;       // streams in use; divides ntiles
     uint32_t spin;         // polls before a carry wait gives up
-    uint32_t* ct_count;    // [nct] workgroups of each channel tile that have stored their partials
+    uint32_t* fold;        // [kFoldLines][16]: workgroups of the channel tiles ct = q mod kFoldLines that have stored their partials
     int64_t npb;           // partial rows per tile: time blocks (time-split kernel) or 1 (whole-tile)
     float* dw;             // [C] outputs, written by the last workgroup of each channel tile
     float* du;
@@ -616,7 +618,7 @@ struct BwdShared {
     double cin[4][64];      // carry at the block's end
     int cin_s[64];
     float red[W][2][64];
-    uint32_t ticket, tag;
+    uint32_t ticket;
 };
 
 // x: added to the span's offsets (St: the handed-on state's carry carried back to the span's start).
@@ -654,14 +656,16 @@ __device__ __forceinline__ RMap get_map(const BwdShared<W>& sm, int i, int lane,
 }
 
 // dw, du of a workgroup: fixed-order sum over its waves into part[slot], then
-// the fold over the channel tile's workgroups.  Each of the `rows` workgroups
-// of channel tile ct stores its partials with system-coherent stores, waits
-// for them to complete, then counts itself in ct_count[ct]; the one that
-// counts last sums the tile's partials in the fixed order (batch row, time
-// block) with coherent loads, writes dw and du, and returns the count to zero
-// (so a workspace needs zeros before its first call only).  The order of the
-// sum does not depend on which workgroup finishes last: results are bitwise
-// reproducible.
+// the fold over the channel tiles' workgroups.  The channel tiles ct with the
+// same q = ct mod kFoldLines share fold line q (one 64-byte line in the
+// workspace's fixed prefix, wkv_scan.h).  Each of their workgroups stores its
+// partials with system-coherent stores, waits for them to complete, then
+// counts itself on line q; the one that counts last sums, for each of the
+// line's channel tiles, that tile's partials in the fixed order (batch row,
+// time block) with coherent loads, writes dw and du, and returns the count to
+// zero (so a workspace needs zeros before its first call only).  The order of
+// each sum does not depend on which workgroup finishes last: results are
+// bitwise reproducible.
 template <int W>
 __device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P, int64_t b, int64_t ct,
                                              int64_t blk, int wave, int lane, float ndw, float du) {
@@ -675,50 +679,54 @@ __device__ __forceinline__ void put_partials(BwdShared<W>& sm, const BwdChunk& P
         sw += sm.red[i][0][lane];
         su += sm.red[i][1][lane];
     }
-    const int64_t rows = P.B * P.npb;
+    const int64_t rows = P.B * P.npb;  // partial rows per channel tile
     const uint32_t row_bytes = 2 * 64 * 4;
     const Rsrc rp = make_rsrc(P.part, static_cast<uint32_t>(P.ntiles * P.npb) * row_bytes);
-    auto row_off = [&](int64_t bb, int64_t j) {
-        return static_cast<uint32_t>(((bb * P.nct + ct) * P.npb + j) * row_bytes + lane * 4);
+    auto row_off = [&](int64_t c_t, int64_t bb, int64_t jb) {
+        return static_cast<uint32_t>(((bb * P.nct + c_t) * P.npb + jb) * row_bytes + lane * 4);
     };
-    const uint32_t off = row_off(b, blk);
+    const uint32_t off = row_off(ct, b, blk);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sw), rp, off, 0, kCoherent);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(su), rp, off + 64 * 4, 0, kCoherent);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int64_t q = ct % kFoldLines;
+    const int64_t nq = (P.nct - q + kFoldLines - 1) / kFoldLines;  // channel tiles on line q
     uint32_t prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(P.ct_count + ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) prev = __hip_atomic_fetch_add(P.fold + 16 * q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev + 1 != static_cast<uint32_t>(rows)) return;
-    // last of the tile's workgroups: fixed-order sum, 8 rows' loads in flight at a time
-    float tw = 0.f, tu = 0.f;
-    int64_t r = 0;
-    for (; r + 8 <= rows; r += 8) {
-        float w8[8], u8[8];
+    if (prev + 1 != static_cast<uint32_t>(rows * nq)) return;
+    // last of the line's workgroups: per channel tile, a fixed-order sum, 8 rows' loads in flight at a time
+    for (int64_t c_t = q; c_t < P.nct; c_t += kFoldLines) {
+        float tw = 0.f, tu = 0.f;
+        int64_t r = 0;
+        for (; r + 8 <= rows; r += 8) {
+            float w8[8], u8[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t bb = (r + i) / P.npb, j = (r + i) - bb * P.npb;
-            const uint32_t o = row_off(bb, j);
-            w8[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, kCoherent));
-            u8[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o + 64 * 4, 0, kCoherent));
-        }
+            for (int i = 0; i < 8; ++i) {
+                const int64_t bb = (r + i) / P.npb, jb = (r + i) - bb * P.npb;
+                const uint32_t o = row_off(c_t, bb, jb);
+                w8[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, kCoherent));
+                u8[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o + 64 * 4, 0, kCoherent));
+            }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            tw += w8[i];
-            tu += u8[i];
+            for (int i = 0; i < 8; ++i) {
+                tw += w8[i];
+                tu += u8[i];
+            }
+        }
+        for (; r < rows; ++r) {
+            const int64_t bb = r / P.npb, jb = r - bb * P.npb;
+            const uint32_t o = row_off(c_t, bb, jb);
+            tw += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, kCoherent));
+            tu += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o + 64 * 4, 0, kCoherent));
+        }
+        const int64_t c = c_t * 64 + lane;
+        if (c < P.C) {
+            P.dw[c] = tw;
+            P.du[c] = tu;
         }
     }
-    for (; r < rows; ++r) {
-        const int64_t bb = r / P.npb, j = r - bb * P.npb;
-        const uint32_t o = row_off(bb, j);
-        tw += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, kCoherent));
-        tu += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, o + 64 * 4, 0, kCoherent));
-    }
-    const int64_t c = ct * 64 + lane;
-    if (c < P.C) {
-        P.dw[c] = tw;
-        P.du[c] = tu;
-    }
-    if (lane == 0) __hip_atomic_store(P.ct_count + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(P.fold + 16 * q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- backward through carried state (St kernels) --------------------------------
@@ -812,23 +820,29 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    int64_t ticket = blockIdx.x;
-    uint32_t tag = 0;
+    // stream j = blockIdx mod K hands out the time blocks of its tiles j, j + K, ..
+    // last-in-time first (wkv_scan.h), so the awaited block is already running
+    const int64_t j = blockIdx.x % P.nstream;
+    const int64_t per = P.ntiles / P.nstream;  // tiles per stream
+    int64_t tile = blockIdx.x, rblk = 0;
+    uint32_t tag = 0, done_before = 0;
     if (P.nblocks > 1) {
         if (threadIdx.x == 0) {
-            sm.ticket = call_ticket(P.hdr, &sm.tag);
-            if (sm.ticket >= gridDim.x) hdr_flag(P.hdr, kErrTicket);  // a workspace not zeroed before first use
+            sm.ticket = stream_ticket(P.sc + j);
+            if (sm.ticket >= per * P.nblocks) hdr_flag(P.hdr, kErrTicket);  // a workspace not zeroed before first use
         }
         __syncthreads();
-        ticket = sm.ticket;
-        tag = sm.tag;
-        if (ticket >= gridDim.x) {  // uniform per workgroup: nothing to compute
-            if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
+        const int64_t k = sm.ticket;
+        if (wave == 0) tag = stream_tag(P.sc + j);  // the carry wave's
+        if (k >= per * P.nblocks) {  // uniform per workgroup: nothing to compute
+            if (wave == 0)
+                stream_finish(P.hdr, P.sc, j, stream_count(P.sc, j, lane), static_cast<uint32_t>(per * P.nblocks),
+                              static_cast<uint32_t>(P.nstream), tag, lane);
             return;
         }
+        rblk = k / per;
+        tile = j + P.nstream * (k - rblk * per);
     }
-    const int64_t rblk = ticket / P.ntiles;  // blocks are handed out last-in-time first
-    const int64_t tile = ticket - rblk * P.ntiles;
     const int64_t blk = P.nblocks - 1 - rblk;
     const int64_t b = tile / P.nct;
     const int64_t c = (tile - b * P.nct) * 64 + lane;
@@ -870,6 +884,7 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
             const uint32_t slot = (uint32_t)(((tile * P.nblocks + blk) * 64 + lane) * kCarrySlot);
             if (blk < P.nblocks - 1) cin = wait_carry(rc, slot + 64 * kCarrySlot, tag, P.spin, P.hdr);  // block blk+1
             if (blk > 0) publish_carry(rc, slot, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin), tag);
+            done_before = stream_count(P.sc, j, lane);
         }
         if (St && blk == 0)  // the carry before the first token
             hist = state_grads(P, b * P.C + c, cok, rapply(rcompose(get_map(sm, 0, lane, dL), suf), cin), sp.x0.m);
@@ -886,10 +901,9 @@ __global__ void __launch_bounds__(64 * W, WKV_BWD_OCC) bwd_chunk_kernel(BwdChunk
     const float ndw = sp.template reverse<St>(C, g, ch, eu, dec, fast_out, tcut < L ? tcut : 0, sd) - hist;
     const int64_t ct = tile - b * P.nct;
     put_partials(sm, P, b, ct, blk, wave, lane, ndw, sp.du);
-    if (P.nblocks > 1) {  // every wave is past its carry traffic
-        __syncthreads();
-        if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
-    }
+    if (P.nblocks > 1 && wave == 0)  // the carry wave
+        stream_finish(P.hdr, P.sc, j, done_before, static_cast<uint32_t>(per * P.nblocks),
+                      static_cast<uint32_t>(P.nstream), tag, lane);
 }
 
 // Whole-tile backward: one workgroup walks all time blocks of its tile from
@@ -1017,7 +1031,7 @@ static_assert(kBwdL % kCkptLen == 0, "backward spans must start on saved forward
 
 struct BwdLayout {
     int64_t nct, ntiles, nblocks, nblk_ck;
-    size_t off_ct, off_carry, carry_bytes, off_part, off_ckpt, ckpt_bytes, off_fws, fws_bytes, bytes;
+    size_t off_carry, carry_bytes, off_part, off_ckpt, ckpt_bytes, bytes;
 };
 
 BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C) {
@@ -1027,23 +1041,23 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t C) {
     l.nblocks = (T + kBwdL * kBwdW - 1) / (kBwdL * kBwdW);
     l.nblk_ck = (T + kCkptLen - 1) / kCkptLen;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    size_t off = 256;  // CallHdr
-    l.off_ct = off;    // per channel tile partial counts
-    off = up(off + static_cast<size_t>(l.nct) * 4);
-    l.off_carry = off;
+    // the counters' fixed prefix (wkv_scan.h), then the carries between workgroups at the same
+    // fixed offset for every shape, shared with the forward that recomputes the saved states when
+    // none are given (it runs first, and its carries are dead once it ends), then the dw, du
+    // partials and the recomputed states
+    const size_t fwd_ws = fwd_chunk_workspace_bytes(B, T, C);
+    const size_t fwd_carry = fwd_ws > kWsPrefix ? fwd_ws - kWsPrefix : 0;
+    l.off_carry = kWsPrefix;
     l.carry_bytes = l.nblocks > 1 ? static_cast<size_t>(l.ntiles * l.nblocks * 64) * kCarrySlot : 0;
-    off = up(off + l.carry_bytes);
+    size_t off = up(l.off_carry + (fwd_ws == SIZE_MAX ? 0 : (l.carry_bytes > fwd_carry ? l.carry_bytes : fwd_carry)));
     l.off_part = off;
     off = up(off + static_cast<size_t>(l.ntiles * l.nblocks * 2 * 64) * 4);
     l.off_ckpt = off;
     l.ckpt_bytes = static_cast<size_t>(B * l.nblk_ck * C) * 12;
-    off = up(off + l.ckpt_bytes);
-    l.off_fws = off;
-    l.fws_bytes = fwd_chunk_workspace_bytes(B, T, C);
-    l.bytes = off + l.fws_bytes;
+    l.bytes = off + l.ckpt_bytes;
     // carries and partials are addressed through 32-bit buffer resources
     if (l.carry_bytes > 0xffffffffull || static_cast<size_t>(l.ntiles * l.nblocks) * 512 > 0xffffffffull ||
-        l.fws_bytes == SIZE_MAX)
+        fwd_ws == SIZE_MAX)
         l.bytes = SIZE_MAX;
     return l;
 }
@@ -1059,7 +1073,7 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     const bool st = a.a_in != nullptr || a.ga_out != nullptr || a.ga_in != nullptr;  // through carried state
     if (ckpt == nullptr) {  // recompute the block-start states with the forward (no y written)
         FwdArgs f{a.B, a.T, a.C, a.bf16, a.w, a.u, a.k, a.v, nullptr, ws + l.off_ckpt, l.nblk_ck,
-                  ws + l.off_fws, l.fws_bytes};
+                  ws, l.off_part};
         f.a_in = a.a_in;
         f.b_in = a.b_in;
         f.p_in = a.p_in;
@@ -1077,10 +1091,12 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
     P.part = reinterpret_cast<float*>(ws + l.off_part);
     P.r = a.r;
     P.dr = a.dr;
-    P.ct_count = reinterpret_cast<uint32_t*>(ws + l.off_ct);
+    P.fold = reinterpret_cast<uint32_t*>(ws + kWsFoldOff);
     P.dw = a.dw;
     P.du = a.du;
     P.hdr = reinterpret_cast<CallHdr*>(ws);
+    P.sc = reinterpret_cast<StreamCtr*>(ws + kWsStreamOff);
+    P.nstream = 1;
     P.spin = spin_limit();
     P.a_in = a.a_in; P.b_in = a.b_in; P.p_in = a.p_in;
     P.ga_out = a.ga_out; P.gb_out = a.gb_out; P.p_out = a.p_out;
@@ -1117,6 +1133,7 @@ hipError_t launch_bwd_chunk_t(const BwdArgs& a, hipStream_t stream) {
 
     P.nblocks = l.nblocks;
     P.npb = l.nblocks;
+    P.nstream = chain_streams(l.ntiles);
     P.carry = reinterpret_cast<float*>(ws + l.off_carry);
     P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);
     if (st)

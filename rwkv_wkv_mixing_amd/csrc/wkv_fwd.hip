@@ -13,10 +13,10 @@
 //           D_t = B_loc + e^{u+k}; the end state is the sub-chunk summary S_i
 //   scan    through LDS every wave combines S_0..S_{i-1} into its prefix P_i;
 //           the last wave also waits for the inclusive state E of the
-//           previous time block of the same tile (blocks are handed out by an
-//           atomic ticket in time order, so the awaited block is already
-//           running) and publishes this block's inclusive state, tagged with
-//           the call's generation (wkv_scan.h)
+//           previous time block of the same tile (each tile's blocks are
+//           handed out by the tile's own atomic ticket in time order, so the
+//           awaited block is already running) and publishes this block's
+//           inclusive state, tagged with the tile's generation (wkv_scan.h)
 //   output  with X = d^{iL} E + P_i the state before the sub-chunk,
 //           y_t = (N_t + d^j X_A) / (D_t + d^j X_B)  for its j-th token,
 //           and the saved block-start states for the backward.
@@ -47,7 +47,9 @@ struct FwdChunk {
     int64_t nct;       // channel tiles per batch row
     int64_t ntiles;    // B * nct
     int64_t nblocks;   // time blocks per tile
-    CallHdr* hdr;      // workspace header: tickets, error word, generation (nblocks > 1)
+    CallHdr* hdr;      // workspace header: error word, finished streams, generation (nblocks > 1)
+    StreamCtr* sc;     // [kMaxStreams] ticket streams (nblocks > 1)
+    int64_t nstream;   // streams in use; divides ntiles
     uint32_t spin;     // polls before a carry wait gives up
     float* carry;      // [ntiles][nblocks][64][4] inclusive block states + tag
     uint32_t carry_bytes;
@@ -302,7 +304,7 @@ struct FwdShared {
     int s[W][64];
     float ea[64], eb[64];  // block carry-in E
     int es[64];
-    uint32_t ticket, tag;
+    uint32_t ticket;
 };
 
 // Prefix of the summaries of waves 0..wave-1 of a block.
@@ -325,23 +327,29 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    int64_t ticket = blockIdx.x;
-    uint32_t tag = 0;
+    // stream j = blockIdx mod K hands out the time blocks of its tiles j, j + K, ..
+    // in time order (wkv_scan.h), so the awaited block is already running
+    const int64_t j = blockIdx.x % P.nstream;
+    const int64_t per = P.ntiles / P.nstream;  // tiles per stream
+    int64_t tile = blockIdx.x, blk = 0;
+    uint32_t tag = 0, done_before = 0;
     if (P.nblocks > 1) {
         if (threadIdx.x == 0) {
-            sm.ticket = call_ticket(P.hdr, &sm.tag);
-            if (sm.ticket >= gridDim.x) hdr_flag(P.hdr, kErrTicket);  // a workspace not zeroed before first use
+            sm.ticket = stream_ticket(P.sc + j);
+            if (sm.ticket >= per * P.nblocks) hdr_flag(P.hdr, kErrTicket);  // a workspace not zeroed before first use
         }
         __syncthreads();
-        ticket = sm.ticket;
-        tag = sm.tag;
-        if (ticket >= gridDim.x) {  // uniform per workgroup: nothing to compute
-            if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
+        const int64_t k = sm.ticket;
+        if (wave == W - 1) tag = stream_tag(P.sc + j);  // the carry wave's
+        if (k >= per * P.nblocks) {  // uniform per workgroup: nothing to compute
+            if (wave == W - 1)
+                stream_finish(P.hdr, P.sc, j, stream_count(P.sc, j, lane), static_cast<uint32_t>(per * P.nblocks),
+                              static_cast<uint32_t>(P.nstream), tag, lane);
             return;
         }
+        blk = k / per;
+        tile = j + P.nstream * (k - blk * per);
     }
-    const int64_t blk = ticket / P.ntiles;
-    const int64_t tile = ticket - blk * P.ntiles;
     const int64_t b = tile / P.nct;
     const int64_t c = (tile - b * P.nct) * 64 + lane;
     const bool cok = c < P.C;
@@ -390,6 +398,7 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
             if (blk > 0) E = wait_state(rc, slot - 64 * 16, tag, P.spin, P.hdr);  // block blk-1, same lane
             if (blk < P.nblocks - 1)  // then this block is full
                 publish_state(rc, slot, combine(E, combine(pref, sw.st, dL), dTB), tag);
+            done_before = stream_count(P.sc, j, lane);
         }
         sm.ea[lane] = E.a;
         sm.eb[lane] = E.b;
@@ -420,10 +429,9 @@ __global__ void __launch_bounds__(64 * W, Gated ? 1 : WKV_FWD_OCC) fwd_chunk_ker
             state_to_abp(st, P.a_out[i], P.b_out[i], P.p_out[i]);
         }
     }
-    if (P.nblocks > 1) {  // every wave is past its carry traffic
-        __syncthreads();
-        if (threadIdx.x == 0) call_done(P.hdr, gridDim.x, tag);
-    }
+    if (P.nblocks > 1 && wave == W - 1)  // the carry wave
+        stream_finish(P.hdr, P.sc, j, done_before, static_cast<uint32_t>(per * P.nblocks),
+                      static_cast<uint32_t>(P.nstream), tag, lane);
 }
 
 
@@ -679,7 +687,7 @@ FwdLayout fwd_layout(int64_t B, int64_t T, int64_t C) {
     l.ntiles = B * l.nct;
     l.nblocks = (T + kFwdL * kFwdW - 1) / (kFwdL * kFwdW);
     if (l.nblocks <= 1) return l;  // no cross-workgroup carries, no workspace
-    l.off_carry = 256;  // CallHdr
+    l.off_carry = kWsPrefix;  // after the counters (wkv_scan.h)
     l.carry_bytes = static_cast<size_t>(l.ntiles * l.nblocks * 64) * 16;
     l.bytes = l.off_carry + l.carry_bytes;
     if (l.carry_bytes > 0xffffffffull) l.bytes = SIZE_MAX;  // carries are addressed through a 32-bit buffer resource
@@ -702,6 +710,7 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     P.ckpt = static_cast<float*>(a.ckpt);
     P.nblk_ck = a.nblk;
     P.nct = l.nct; P.ntiles = l.ntiles; P.nblocks = l.nblocks;
+    P.nstream = 1;
     P.r = a.r;
     P.a_in = a.a_in; P.b_in = a.b_in; P.p_in = a.p_in;
     P.a_out = a.a_out; P.b_out = a.b_out; P.p_out = a.p_out;
@@ -729,6 +738,8 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     if (l.nblocks > 1) {
         char* ws = static_cast<char*>(a.ws);
         P.hdr = reinterpret_cast<CallHdr*>(ws);
+        P.sc = reinterpret_cast<StreamCtr*>(ws + kWsStreamOff);
+        P.nstream = chain_streams(l.ntiles);
         P.spin = spin_limit();
         P.carry = reinterpret_cast<float*>(ws + l.off_carry);
         P.carry_bytes = static_cast<uint32_t>(l.carry_bytes);

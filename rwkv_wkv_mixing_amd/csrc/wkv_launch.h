@@ -17,7 +17,7 @@ uint32_t spin_limit();
 // Header at the start of a wkv_forward / wkv_backward workspace (the device
 // code's CallHdr in wkv_scan.h has this layout).
 struct CallHdrLayout {
-    uint32_t ticket, error, done, gen;
+    uint32_t unused0, error, streams_done, gen;
 };
 
 struct FwdArgs {

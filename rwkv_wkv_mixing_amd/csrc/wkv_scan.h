@@ -139,22 +139,54 @@ __device__ __forceinline__ void lds_sync_lgkm() {
 // therefore the result, independent of timing.
 //
 // Slots are not cleared between calls: a slot is valid when its tag equals
-// the call's tag, drawn from the generation word of the workspace header, so
-// what an earlier call left behind never matches.  The header (CallHdr) holds
-// the ticket counter, a sticky error word, a count of finished workgroups and
-// the generation; the last workgroup of a call to finish returns the two
-// counters to zero and advances the generation.  A workspace therefore has to
-// hold zeros before its first call only.
+// the call's tag (the workspace's generation + 1), so what an earlier call
+// left behind, of any shape, never matches.
+//
+// Every RWKV-4 workspace starts with the same fixed prefix (kWsPrefix bytes),
+// used for counters only, whatever the shape:
+//   [0, 256)        CallHdr: the sticky error word, a count of finished
+//                   streams and the generation
+//   [256, 4352)     64 stream lines (StreamCtr, 64 bytes each)
+//   [4352, 8448)    64 lines of dw/du fold counts (backward)
+// Ticket streams: the grid's workgroups are dealt to K streams (K divides the
+// tile count, at most 64; workgroup i joins stream i mod K), and stream j
+// owns the tiles j, j + K, j + 2K, ...  Each stream's atomic ticket hands out
+// its tiles' time blocks in time order (all of its tiles' first blocks, then
+// their second, ...), so the block a workgroup waits for was handed out
+// earlier on the same stream and is already running: no deadlock, whatever
+// order the hardware dispatches in.  Per-stream lines keep the atomics apart:
+// one ticket and one finish counter for the whole grid serialised every
+// workgroup on a single address, which more than doubled the time of a long
+// single sequence (8,192 workgroups).  The last workgroup of a stream returns
+// its counters to zero and counts the stream as finished; the last stream
+// returns that count to zero and advances the generation, in the header and
+// in every stream line's copy (each workgroup reads its stream's copy).  So a
+// workspace has to hold zeros before its first call only, and its counters
+// never share memory with the carries or partials, whose offsets depend on
+// the shape.
 constexpr int kCoherent = 1 | 16;  // sc0 | sc1
+constexpr int kMaxStreams = 64;
+constexpr int kFoldLines = 64;
+constexpr size_t kWsStreamOff = 256;
+constexpr size_t kWsFoldOff = kWsStreamOff + 64 * kMaxStreams;
+constexpr size_t kWsPrefix = kWsFoldOff + 64 * kFoldLines;
 
 struct CallHdr {
-    uint32_t ticket;  // next ticket of this call
-    uint32_t error;   // sticky: bit 0 a carry wait gave up, bit 1 a ticket out of range
-    uint32_t done;    // workgroups of this call that have finished
-    uint32_t gen;     // call generation; tag = gen + 1 (never 0)
+    uint32_t unused0;
+    uint32_t error;         // sticky: bit 0 a carry wait gave up, bit 1 a ticket out of range
+    uint32_t streams_done;  // streams of this call that have finished
+    uint32_t gen;           // call generation; tag = gen + 1 (never 0)
 };
 static_assert(sizeof(CallHdr) == sizeof(CallHdrLayout) && offsetof(CallHdr, error) == offsetof(CallHdrLayout, error),
               "one header layout");
+
+struct StreamCtr {
+    uint32_t ticket;  // next ticket of this stream
+    uint32_t done;    // workgroups of this stream that have finished
+    uint32_t gen;     // copy of the header's generation
+    uint32_t pad[13];
+};
+static_assert(sizeof(StreamCtr) == 64, "one line per stream");
 
 constexpr uint32_t kErrWait = 1u;
 constexpr uint32_t kErrTicket = 2u;
@@ -167,23 +199,60 @@ __device__ __forceinline__ void hdr_flag(CallHdr* h, uint32_t bits) {
     __hip_atomic_fetch_or(&h->error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One thread per workgroup, first: this workgroup's ticket and the call's tag.
-__device__ __forceinline__ uint32_t call_ticket(CallHdr* h, uint32_t* tag) {
-    const uint32_t t = __hip_atomic_fetch_add(&h->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *tag = hdr_load(&h->gen) + 1u;
-    return t;
+__device__ __forceinline__ CallHdr* ws_hdr(void* ws) { return static_cast<CallHdr*>(ws); }
+__device__ __forceinline__ StreamCtr* ws_streams(void* ws) {
+    return reinterpret_cast<StreamCtr*>(static_cast<char*>(ws) + kWsStreamOff);
 }
 
-// One thread per workgroup, after all of the workgroup's carry traffic (and
-// after call_ticket): the last of `groups` workgroups resets the counters and
-// advances the generation so that the next call's tag differs from this one's.
-__device__ __forceinline__ void call_done(CallHdr* h, uint32_t groups, uint32_t tag) {
-    const uint32_t d = __hip_atomic_fetch_add(&h->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d + 1u == groups) {
-        __hip_atomic_store(&h->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&h->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&h->gen, tag == 0xffffffffu ? 0u : tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One thread per workgroup, first: this workgroup's ticket on stream s.
+__device__ __forceinline__ uint32_t stream_ticket(StreamCtr* s) {
+    return __hip_atomic_fetch_add(&s->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The call's tag, by the wave that exchanges carries (after stream_ticket; the
+// load's latency then hides behind the work before the first exchange).
+__device__ __forceinline__ uint32_t stream_tag(StreamCtr* s) { return hdr_load(&s->gen) + 1u; }
+
+// The wave that exchanges the workgroup's carries, right after the last of
+// them: counts the workgroup as finished on stream j and returns the count
+// before it (lane 0 issues the atomic; its result is waited for only in
+// stream_finish, so the latency hides behind the rest of the workgroup's work).
+__device__ __forceinline__ uint32_t stream_count(StreamCtr* lines, int64_t j, int lane) {
+    uint32_t d = 0;
+    if (lane == 0) d = __hip_atomic_fetch_add(&lines[j].done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return d;
+}
+
+// The same wave, last: if its count was the last of stream j's `groups`
+// workgroups, reset the stream's counters and count the stream; the last of the
+// `nstreams` streams resets that count and advances the generation (header and
+// every stream line), so that the next call's tag differs from this one's.
+__device__ __forceinline__ void stream_finish(CallHdr* h, StreamCtr* lines, int64_t j, uint32_t d, uint32_t groups,
+                                              uint32_t nstreams, uint32_t tag, int lane) {
+    d = __builtin_amdgcn_readfirstlane(d);
+    if (d + 1u != groups) return;
+    uint32_t f = 0;
+    if (lane == 0) {
+        __hip_atomic_store(&lines[j].ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&lines[j].done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f = __hip_atomic_fetch_add(&h->streams_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    f = __builtin_amdgcn_readfirstlane(f);
+    if (f + 1u != nstreams) return;
+    const uint32_t g = tag == 0xffffffffu ? 0u : tag;
+    if (lane < kMaxStreams) __hip_atomic_store(&lines[lane].gen, g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+        __hip_atomic_store(&h->streams_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&h->gen, g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Streams for a grid of ntiles x nblocks chained workgroups: the largest
+// divisor of ntiles not above kMaxStreams.
+inline int64_t chain_streams(int64_t ntiles) {
+    for (int64_t k = kMaxStreams; k > 1; --k)
+        if (ntiles % k == 0) return k;
+    return 1;
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -53,9 +53,9 @@ def new_ckpt(B: int, T: int, C: int, device) -> torch.Tensor:
 
 def new_workspace(op: int, B: int, T: int, C: int, in_dtype: torch.dtype, device) -> torch.Tensor:
     """A zero-filled workspace for wkv_forward (op 0) or wkv_backward (op 1) at
-    this shape.  It may be reused by later calls of the same op on the same
-    stream (each call leaves it ready for the next); it must not be written
-    in between."""
+    this shape.  It may be reused by later calls on the same stream, of either
+    op and any shape it is large enough for (each call leaves it ready for the
+    next); it must not be written in between."""
     return torch.zeros(max(workspace_bytes(op, B, T, C, in_dtype), 1), dtype=torch.uint8, device=device)
 
 

@@ -130,3 +130,39 @@ def test_workspace_not_zero_filled_is_reported():
     finally:
         lib.wkv_debug_spin_limit(old)
     assert O.workspace_status(wsf) == L.WKV_ETIMEOUT
+
+
+def test_one_workspace_across_shapes():
+    """One zero-filled buffer serves forward and backward calls of several shapes and
+    dtypes in turn (the counters sit at fixed offsets for every shape, the carries
+    start at one fixed offset, and every carry is tagged with the call's
+    generation): each call equals the same call on a fresh workspace, bit for bit."""
+    O = ops()
+    shapes = [("bf16", 1, 2000, 64), ("f32", 2, 700, 130), ("bf16", 1, 1100, 192), ("f32", 1, 3000, 64),
+              ("bf16", 1, 2000, 64)]
+    probs = []
+    for i, (dt, B, T, C) in enumerate(shapes):
+        p = W.make_problem(B, T, C, dtype=dt, seed=300 + i, spike_frac=0.01 if dt == "bf16" else 0.0,
+                           name=f"shapes {dt} B={B} T={T} C={C}")
+        probs.append((p, problem_to_dev(p, DEV)))
+    nbytes = max(O.workspace_bytes(op, p.B, p.T, p.C, d["k"].dtype) for p, d in probs for op in (0, 1))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    for p, d in probs:
+        print(f"case {p.name}", flush=True)
+        B, T, C = p.B, p.T, p.C
+        dt = d["k"].dtype
+        ck = O.new_ckpt(B, T, C, DEV)
+        y = O.wkv_forward(d["w"], d["u"], d["k"], d["v"], ckpt=ck, workspace=ws)
+        g = O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"], ckpt=ck, workspace=ws)
+        g2 = O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"], workspace=ws)
+        ck_f = O.new_ckpt(B, T, C, DEV)
+        y_f = O.wkv_forward(d["w"], d["u"], d["k"], d["v"], ckpt=ck_f, workspace=O.new_workspace(0, B, T, C, dt, DEV))
+        g_f = O.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["gy"], ckpt=ck_f,
+                             workspace=O.new_workspace(1, B, T, C, dt, DEV))
+        torch.cuda.synchronize()
+        assert O.workspace_status(ws) == L.WKV_OK
+        assert torch.equal(y, y_f)
+        for a, b in zip(g + g2, g_f + g_f):
+            assert torch.equal(a, b)
+        check_y(p, y.cpu().numpy())
+        check_grads(p, g)
