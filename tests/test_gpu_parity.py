@@ -94,7 +94,10 @@ def test_config4_forward_long_context():
 
 # ------------------------------------------------------------ edge cases --
 
-ODD = [(1, 1, 1), (1, 2, 3), (3, 77, 13), (2, 1000, 129), (1, 4097, 7), (5, 64, 64), (2, 129, 260)]
+# The last two chain workgroups in time over 67 tiles (a prime: one ticket stream holds them all)
+# and over 130 tiles (26 streams of 5 tiles each).
+ODD = [(1, 1, 1), (1, 2, 3), (3, 77, 13), (2, 1000, 129), (1, 4097, 7), (5, 64, 64), (2, 129, 260),
+       (1, 600, 67 * 64), (2, 300, 65 * 64 - 5)]
 
 
 @pytest.mark.parametrize("B,T,C", ODD)
