@@ -105,6 +105,17 @@ __device__ __forceinline__ s4 as_s4(uint16_t a, uint16_t b, uint16_t c, uint16_t
 // four consecutive bf16 of an LDS row as an MFMA operand, unchanged
 __device__ __forceinline__ s4 raw4(const uint16_t* p) { return __builtin_bit_cast(s4, *reinterpret_cast<const u16x4*>(p)); }
 
+// The 16 x 16 x 32 product (gfx950) for the backwards' products whose operands are both staged rows,
+// unchanged: each lane gives eight consecutive bf16 (one 16-byte LDS read) of its row of A and of its
+// column of B.  Which eight of the 32 contracted indices a lane holds is the same for A and B, so
+// loading both from channels c8 .. c8 + 7, c8 = 32 J + 8 g, contracts over channels 32 J .. 32 J + 31
+// whatever the instruction's order inside the slice; the 4 outputs per lane are laid out as in the
+// 16 x 16 x 16 product.
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf8 raw8(const uint16_t* p) { return __builtin_bit_cast(bf8, *reinterpret_cast<const u16x8*>(p)); }
+__device__ __forceinline__ f4 mfma32(bf8 a, bf8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+
 // Tokens tb + 4 g + e (e = 0..3) of channel c0 + l16 of a staged 64 x 64 tile (a column) as a raw
 // MFMA operand, by one transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
 // q reads four channels of one row and lane j receives element j % 4 of lane 4 e + j / 4's read,
@@ -693,6 +704,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
     auto rd = [](const uint16_t(*X)[kN], int t, int c) { return bf(X[t][sw(t, c)]); };
     auto row4s = [](const uint16_t(*X)[kN], int t, int c4) { return row4(&X[t][sw(t, c4)]); };
     auto raw4s = [](const uint16_t(*X)[kN], int t, int c4) { return raw4(&X[t][sw(t, c4)]); };
+    auto raw8s = [](const uint16_t(*X)[kN], int t, int c8) { return raw8(&X[t][sw(t, c8)]); };
     // tokens t0 + 4 g + e (e = 0..3) of channel c0 + l16 of a staged input (a column), as a raw
     // operand, by one transposing LDS read: in each group of 16 lanes, lane q reads four
     // channels of one row and lane j receives element j % 4 of lane 4 e + j / 4's read, so lane
@@ -744,9 +756,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
         // ---- C[s][s] of this wave's tokens, from the diagonal block of GO V^T ------------
         f4 Cpp = {0.f, 0.f, 0.f, 0.f};  // lane: C[s = P0 + 4 g + e][sig = P0 + l16]
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const int j4 = 16 * J + 4 * g;
-            Cpp = mfma(raw4s(GO, P0 + l16, j4), raw4s(V, P0 + l16, j4), Cpp);
+        for (int J = 0; J < 2; ++J) {
+            const int j8 = 32 * J + 8 * g;
+            Cpp = mfma32(raw8s(GO, P0 + l16, j8), raw8s(V, P0 + l16, j8), Cpp);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)  // read back only by this wave (in order)
@@ -838,9 +850,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                     for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e > l16 ? Cq[e] : 0.f;
                 } else {
 #pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        const int j4 = 16 * J + 4 * g;
-                        Cq = mfma(raw4s(GO, 16 * Q + l16, j4), raw4s(V, sig, j4), Cq);
+                    for (int J = 0; J < 2; ++J) {
+                        const int j8 = 32 * J + 8 * g;
+                        Cq = mfma32(raw8s(GO, 16 * Q + l16, j8), raw8s(V, sig, j8), Cq);
                     }
                 }
                 aC[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
@@ -851,9 +863,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 const int i = 16 * I + l16;
                 f4 X = {0.f, 0.f, 0.f, 0.f};  // X = V G1^T
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    X = mfma(raw4s(V, sig, j4), raw4(&sm.gs[i][j4]), X);
+                for (int J = 0; J < 2; ++J) {
+                    const int j8 = 32 * J + 8 * g;
+                    X = mfma32(raw8s(V, sig, j8), raw8(&sm.gs[i][j8]), X);
                 }
                 const f4 kc = colTf(K, P0, 16 * I);
                 f4 D;
@@ -902,9 +914,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 if (Q > wv) continue;
                 f4 Cq = {0.f, 0.f, 0.f, 0.f};  // from V_Q GO_P^T
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    Cq = mfma(raw4s(V, 16 * Q + l16, j4), raw4s(GO, s_n, j4), Cq);
+                for (int J = 0; J < 2; ++J) {
+                    const int j8 = 32 * J + 8 * g;
+                    Cq = mfma32(raw8s(V, 16 * Q + l16, j8), raw8s(GO, s_n, j8), Cq);
                 }
                 if (Q == wv) {
 #pragma unroll
@@ -922,9 +934,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 const int i = 16 * I + l16;
                 f4 Y = {0.f, 0.f, 0.f, 0.f};  // Y = GO S0^T
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    Y = mfma(raw4s(GO, s_n, j4), raw4(&sm.ss[i][sw(i, j4)]), Y);
+                for (int J = 0; J < 2; ++J) {
+                    const int j8 = 32 * J + 8 * g;
+                    Y = mfma32(raw8s(GO, s_n, j8), raw8(&sm.ss[i][sw(i, j8)]), Y);
                 }
                 const f4 rc = colTf(R, P0, 16 * I);
                 f4 D;
@@ -1178,6 +1190,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
     auto rd = [](const uint16_t(*X)[kN], int t, int c) { return bf(X[t][sw(t, c)]); };
     auto row4s = [](const uint16_t(*X)[kN], int t, int c4) { return row4(&X[t][sw(t, c4)]); };
     auto raw4s = [](const uint16_t(*X)[kN], int t, int c4) { return raw4(&X[t][sw(t, c4)]); };
+    auto raw8s = [](const uint16_t(*X)[kN], int t, int c8) { return raw8(&X[t][sw(t, c8)]); };
     auto colTp = [&](const uint16_t(*X)[kPadH], int tb, int c0) {  // col_tr for the padded, unswizzled G tile
         const int t = tb + 4 * g + (l16 >> 2), c = c0 + 4 * (l16 & 3);
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)&X[t][c]);
@@ -1282,9 +1295,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
         // ---- C[s][s] of this wave's tokens -------------------------------------------------------
         f4 Cpp = {0.f, 0.f, 0.f, 0.f};  // lane: C[s = P0 + 4 g + e][sig = P0 + l16]
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const int j4 = 16 * J + 4 * g;
-            Cpp = mfma(raw4s(GO, P0 + l16, j4), raw4s(V, P0 + l16, j4), Cpp);
+        for (int J = 0; J < 2; ++J) {
+            const int j8 = 32 * J + 8 * g;
+            Cpp = mfma32(raw8s(GO, P0 + l16, j8), raw8s(V, P0 + l16, j8), Cpp);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)  // read back only by this wave (in order)
@@ -1368,9 +1381,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                     for (int e = 0; e < 4; ++e) Cq[e] = 4 * g + e > l16 ? Cq[e] : 0.f;
                 } else {
 #pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        const int j4 = 16 * J + 4 * g;
-                        Cq = mfma(raw4s(GO, 16 * Q + l16, j4), raw4s(V, sig, j4), Cq);
+                    for (int J = 0; J < 2; ++J) {
+                        const int j8 = 32 * J + 8 * g;
+                        Cq = mfma32(raw8s(GO, 16 * Q + l16, j8), raw8s(V, sig, j8), Cq);
                     }
                 }
                 aC[Q] = pack4(Cq[0], Cq[1], Cq[2], Cq[3]);
@@ -1381,9 +1394,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                 const int i = 16 * I + l16;
                 f4 X = {0.f, 0.f, 0.f, 0.f};  // X = V G1^T
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    X = mfma(raw4s(V, sig, j4), raw4(&sm.gs[i][j4]), X);
+                for (int J = 0; J < 2; ++J) {
+                    const int j8 = 32 * J + 8 * g;
+                    X = mfma32(raw8s(V, sig, j8), raw8(&sm.gs[i][j8]), X);
                 }
                 const f4 kc = colTf(K, P0, 16 * I);
                 const float en = e1(nv, i);
@@ -1438,9 +1451,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                 if (Q > wv) continue;
                 f4 Cq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    Cq = mfma(raw4s(V, 16 * Q + l16, j4), raw4s(GO, s_n, j4), Cq);
+                for (int J = 0; J < 2; ++J) {
+                    const int j8 = 32 * J + 8 * g;
+                    Cq = mfma32(raw8s(V, 16 * Q + l16, j8), raw8s(GO, s_n, j8), Cq);
                 }
                 if (Q == wv) {
 #pragma unroll
@@ -1455,9 +1468,9 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                 const int i = 16 * I + l16;
                 f4 Y = {0.f, 0.f, 0.f, 0.f};  // Y = GO S0^T
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    const int j4 = 16 * J + 4 * g;
-                    Y = mfma(raw4s(GO, s_n, j4), raw4(&SS[i][sw(i, j4)]), Y);
+                for (int J = 0; J < 2; ++J) {
+                    const int j8 = 32 * J + 8 * g;
+                    Y = mfma32(raw8s(GO, s_n, j8), raw8(&SS[i][sw(i, j8)]), Y);
                 }
                 const f4 rc = colTf(R, P0, 16 * I);
                 f4 D, p, rs = {0.f, 0.f, 0.f, 0.f};
