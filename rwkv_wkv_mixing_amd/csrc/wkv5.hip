@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
                 const int q = (lane % 8) ^ (row & 7);  // the global chunk that lands in slot lane % 8
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, 0);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, kStageKeep);
             }
         }
     };
@@ -414,7 +414,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
                 const int q = (lane % 8) ^ (row & 7);
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, 0);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, kStageKeep);
             }
         }
     };
@@ -737,7 +737,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 const int q = (lane % 8) ^ (row & 7);
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, kStageLast);
             }
         }
         {  // the state before the chunk, 8 KB of [key][value] bf16: rows P0 .. P0 + 15 by this wave
@@ -747,7 +747,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_bwd_kernel(Wkv5BwdArgs P
                 const int row = P0 + 8 * i + lane / 8;
                 const int q = (lane % 8) ^ (row & 7);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&sm.ss[P0 + 8 * i][0],
-                                                         16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, 0);
+                                                         16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, kStageLast);
             }
         }
         wait_staged();
@@ -1232,7 +1232,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                 const int q = (lane % 8) ^ (row & 7);
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[a][P0 + 8 * i][0], 16, voff, 0, 0, kStageLast);
             }
         }
         {
@@ -1242,7 +1242,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                 const int row = P0 + 8 * i + lane / 8;
                 const int q = (lane % 8) ^ (row & 7);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&sm.ss[P0 + 8 * i][0],
-                                                         16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, 0);
+                                                         16, static_cast<uint32_t>(row * kN * 2 + q * 16), 0, 0, kStageLast);
             }
         }
     };
@@ -1263,7 +1263,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_bwd_kernel(Wkv6BwdArgs P
                 const int q = (lane % 16) ^ ((t + 1) & 15);
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(t) * C) * 4 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.E[P0 + 4 * i + 1][0], 16, voff, 0, 0, 0);
+                    rs, (__attribute__((address_space(3))) void*)&sm.E[P0 + 4 * i + 1][0], 16, voff, 0, 0, kStageLast);
             }
         }
         wait_staged();
@@ -1843,7 +1843,7 @@ __global__ void __launch_bounds__(64 * kWaves5) wkv56_adj_local_kernel(AdjLocalA
                 const int sq = (lane % 8) ^ (row & 7);
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + sq * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[q][a][P0 + 8 * i][0], 16, voff, 0, 0, 0);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[q][a][P0 + 8 * i][0], 16, voff, 0, 0, kStageKeep);
             }
         }
     };

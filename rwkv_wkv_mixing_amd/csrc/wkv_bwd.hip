@@ -343,10 +343,10 @@ struct BwdStage {
 template <typename TIn, int L, int W, int NI>
 __device__ __forceinline__ void stage_span(BwdStage<TIn, L, W, NI>& st, const SpanGeo& g, int wave, int lane,
                                            int64_t c0, int64_t C) {
-    stage_rows<TIn, L>(g.rk, st.x[wave][0], int64_t{wave} * L, c0, C, lane);
-    stage_rows<TIn, L>(g.rv, st.x[wave][1], int64_t{wave} * L, c0, C, lane);
-    stage_rows<TIn, L>(g.rg, st.x[wave][2], int64_t{wave} * L, c0, C, lane);
-    if constexpr (NI == 4) stage_rows<TIn, L>(g.rr, st.x[wave][3], int64_t{wave} * L, c0, C, lane);
+    stage_rows<TIn, L, kStageLast>(g.rk, st.x[wave][0], int64_t{wave} * L, c0, C, lane);
+    stage_rows<TIn, L, kStageLast>(g.rv, st.x[wave][1], int64_t{wave} * L, c0, C, lane);
+    stage_rows<TIn, L, kStageLast>(g.rg, st.x[wave][2], int64_t{wave} * L, c0, C, lane);
+    if constexpr (NI == 4) stage_rows<TIn, L, kStageLast>(g.rr, st.x[wave][3], int64_t{wave} * L, c0, C, lane);
 }
 
 // A span's inputs, loaded ahead of use (gy holds the output gradient; with

@@ -577,8 +577,8 @@ __global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
 
     {
         const FwdGeo g0 = fwd_geo<uint16_t, L, W>(P, b, c, cok, 0, wave);
-        stage_rows<uint16_t, L>(g0.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
-        stage_rows<uint16_t, L>(g0.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
+        stage_rows<uint16_t, L, kStageKeep>(g0.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
+        stage_rows<uint16_t, L, kStageKeep>(g0.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
     }
     for (int64_t blk = 0; blk < P.nblocks; ++blk) {
         const FwdGeo g = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk, wave);
@@ -596,8 +596,8 @@ __global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
         wait_lds_reads();
         if (blk + 1 < P.nblocks) {
             const FwdGeo gn = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk + 1, wave);
-            stage_rows<uint16_t, L>(gn.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
-            stage_rows<uint16_t, L>(gn.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
+            stage_rows<uint16_t, L, kStageKeep>(gn.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
+            stage_rows<uint16_t, L, kStageKeep>(gn.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
         }
         TileWork<L> tw;
         tw.local(kv, g, ch, eu, d, lane_ok);
