@@ -38,6 +38,42 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+
+class BoundCall:
+    """One library call with its arguments checked and marshalled once (device addresses, sizes,
+    the stream): calling it launches the same call again, with no checks and no allocation, for a
+    loop that repeats one call on the same buffers (the buffers' contents may change between
+    calls, not their shapes or places).  It keeps the tensors it was bound to alive.  Returns what
+    the unbound call returns."""
+
+    __slots__ = ("name", "fn", "args", "result", "_keep")
+
+    def __init__(self, name, fn, args, result, keep):
+        self.name, self.fn, self.args, self.result, self._keep = name, fn, args, result, keep
+
+    def __call__(self):
+        L.check(self.name, self.fn(*self.args))
+        return self.result
+
+
+def _tensors(x, acc):
+    if isinstance(x, torch.Tensor):
+        acc.append(x)
+    elif isinstance(x, (tuple, list)):
+        for y in x:
+            _tensors(y, acc)
+    return acc
+
+
+def _launch(bind, name, fn, args, result, scope):
+    """Run a library call and check its status, or (bind) return it as a BoundCall holding every
+    tensor of the calling function's scope."""
+    if bind:
+        return BoundCall(name, fn, args, result, tuple(_tensors(list(scope.values()), [])))
+    L.check(name, fn(*args))
+    return result
+
+
 def workspace_bytes(op: int, B: int, T: int, C: int, in_dtype: torch.dtype) -> int:
     return int(L.lib().wkv_workspace_bytes(op, B, T, C, _DT[in_dtype]))
 
@@ -83,7 +119,7 @@ def _workspace(op, B, T, C, dt, device, workspace):
 
 
 def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None, state_in=None, state_out=None,
-                return_state=False):
+                return_state=False, bind=False):
     """y [B,T,C] float32 from w, u [C] float32 and k, v [B,T,C] (float32 or bfloat16).
 
     state_in:  None (empty history) or (a, b, p), each [B, C] float32, in the
@@ -113,11 +149,9 @@ def wkv_forward(w, u, k, v, *, y=None, ckpt=None, workspace=None, state_in=None,
     sin = state_in if state_in is not None else (None, None, None)
     sout = state_out if state_out is not None else (None, None, None)
     ws, ws_n = _workspace(L.WKV_OP_FORWARD, B, T, C, k.dtype, dev, workspace)
-    st = L.lib().wkv_forward_state(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y),
-                                   *[_p(t) for t in sin], *[_p(t) for t in sout], _p(ckpt),
-                                   _p(ws), ws_n, _stream(dev))
-    L.check("wkv_forward_state", st)
-    return (y, state_out) if return_state else y
+    args = (B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y), *[_p(t) for t in sin],
+            *[_p(t) for t in sout], _p(ckpt), _p(ws), ws_n, _stream(dev))
+    return _launch(bind, "wkv_forward_state", L.lib().wkv_forward_state, args, (y, state_out) if return_state else y, locals())
 
 
 def wkv_forward_state_noalloc(w, u, k, v, y, *, ckpt=None, state_in=None, state_out=None):
@@ -146,7 +180,7 @@ def wkv_forward_state_noalloc(w, u, k, v, y, *, ckpt=None, state_in=None, state_
     return y
 
 
-def wkv_forward_gated(w, u, k, v, r, *, out=None, ckpt=None, workspace=None):
+def wkv_forward_gated(w, u, k, v, r, *, out=None, ckpt=None, workspace=None, bind=False):
     """out = sigmoid(r) * wkv(w, u, k, v), [B,T,C] float32; r has the dtype of k."""
     _need(k, "k", (torch.float32, torch.bfloat16))
     dev = k.device
@@ -161,13 +195,12 @@ def wkv_forward_gated(w, u, k, v, r, *, out=None, ckpt=None, workspace=None):
     if ckpt is not None:
         _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
     ws, ws_n = _workspace(L.WKV_OP_FORWARD, B, T, C, k.dtype, dev, workspace)
-    st = L.lib().wkv_forward_gated(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(r), _p(out), _p(ckpt),
-                                   _p(ws), ws_n, _stream(dev))
-    L.check("wkv_forward_gated", st)
-    return out
+    args = (B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(r), _p(out), _p(ckpt), _p(ws), ws_n,
+            _stream(dev))
+    return _launch(bind, "wkv_forward_gated", L.lib().wkv_forward_gated, args, out, locals())
 
 
-def wkv_backward_gated(w, u, k, v, r, gout, *, ckpt=None, out=None, workspace=None):
+def wkv_backward_gated(w, u, k, v, r, gout, *, ckpt=None, out=None, workspace=None, bind=False):
     """(dk, dv, dr, dw, du) for L = sum(gout * sigmoid(r) * wkv).  r, gout have the dtype of k."""
     _need(k, "k", (torch.float32, torch.bfloat16))
     dev = k.device
@@ -186,13 +219,12 @@ def wkv_backward_gated(w, u, k, v, r, gout, *, ckpt=None, out=None, workspace=No
     if ckpt is not None:
         _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
     ws, ws_n = _workspace(L.WKV_OP_BACKWARD, B, T, C, k.dtype, dev, workspace)
-    st = L.lib().wkv_backward_gated(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(r), _p(gout), _p(dk),
-                                    _p(dv), _p(dr), _p(dw), _p(du), _p(ckpt), _p(ws), ws_n, _stream(dev))
-    L.check("wkv_backward_gated", st)
-    return dk, dv, dr, dw, du
+    args = (B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(r), _p(gout), _p(dk), _p(dv), _p(dr), _p(dw),
+            _p(du), _p(ckpt), _p(ws), ws_n, _stream(dev))
+    return _launch(bind, "wkv_backward_gated", L.lib().wkv_backward_gated, args, (dk, dv, dr, dw, du), locals())
 
 
-def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None):
+def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None, bind=False):
     """(dk, dv, dw, du) for L = sum(gy * y).  gy has the dtype of k."""
     _need(k, "k", (torch.float32, torch.bfloat16))
     dev = k.device
@@ -213,10 +245,9 @@ def wkv_backward(w, u, k, v, gy, *, ckpt=None, out=None, workspace=None):
     if ckpt is not None:
         _need(ckpt, "ckpt", torch.float32, (ckpt_bytes(B, T, C) // 4,), dev)
     ws, ws_n = _workspace(L.WKV_OP_BACKWARD, B, T, C, k.dtype, dev, workspace)
-    st = L.lib().wkv_backward(B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(gy), _p(dk),
-                              _p(dv), _p(dw), _p(du), _p(ckpt), _p(ws), ws_n, _stream(dev))
-    L.check("wkv_backward", st)
-    return dk, dv, dw, du
+    args = (B, T, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(gy), _p(dk), _p(dv), _p(dw), _p(du), _p(ckpt),
+            _p(ws), ws_n, _stream(dev))
+    return _launch(bind, "wkv_backward", L.lib().wkv_backward, args, (dk, dv, dw, du), locals())
 
 
 def wkv_backward_state(w, u, k, v, gy, *, state_in=None, grad_state_out=None, need_state_grad=True, ckpt=None,
@@ -263,7 +294,7 @@ def wkv_backward_state(w, u, k, v, gy, *, state_in=None, grad_state_out=None, ne
     return dk, dv, dw, du, gin
 
 
-def wkv_step(w, u, k, v, a, b, p, *, y=None):
+def wkv_step(w, u, k, v, a, b, p, *, y=None, bind=False):
     """One decode token for [L,B,C] states (a, b, p updated in place); returns y."""
     _need(k, "k", (torch.float32, torch.bfloat16))
     dev = k.device
@@ -276,10 +307,8 @@ def wkv_step(w, u, k, v, a, b, p, *, y=None):
     if y is None:
         y = torch.empty((Ln, B, C), dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, (Ln, B, C), dev)
-    st = L.lib().wkv_step(Ln, B, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y), _p(a), _p(b),
-                          _p(p), _stream(dev))
-    L.check("wkv_step", st)
-    return y
+    args = (Ln, B, C, _DT[k.dtype], _p(w), _p(u), _p(k), _p(v), _p(y), _p(a), _p(b), _p(p), _stream(dev))
+    return _launch(bind, "wkv_step", L.lib().wkv_step, args, y, locals())
 
 
 def empty_state(Ln: int, B: int, C: int, device):
@@ -348,7 +377,7 @@ def wkv_with_state(w, u, k, v, a, b, p):
     return WKVStateFunction.apply(w, u, k, v, a, b, p)
 
 
-def token_shift(mu, x, *, x_prev=None, out=None):
+def token_shift(mu, x, *, x_prev=None, out=None, bind=False):
     """The M token-shift mixes of x: out[j] = mu[j] * x_t + (1 - mu[j]) * x_{t-1}.
 
     mu [M, C] float32 (1 <= M <= 4); x [B, T, C] float32 or bfloat16; x_prev
@@ -367,12 +396,11 @@ def token_shift(mu, x, *, x_prev=None, out=None):
     if out is None:
         out = torch.empty((M, B, T, C), dtype=x.dtype, device=dev)
     _need(out, "out", x.dtype, (M, B, T, C), dev)
-    st = L.lib().wkv_token_shift(B, T, C, M, _DT[x.dtype], _p(mu), _p(x), _p(x_prev), _p(out), _stream(dev))
-    L.check("wkv_token_shift", st)
-    return out
+    args = (B, T, C, M, _DT[x.dtype], _p(mu), _p(x), _p(x_prev), _p(out), _stream(dev))
+    return _launch(bind, "wkv_token_shift", L.lib().wkv_token_shift, args, out, locals())
 
 
-def token_shift_backward(mu, x, gout, *, x_prev=None, want_dx_prev=False, out=None, workspace=None):
+def token_shift_backward(mu, x, gout, *, x_prev=None, want_dx_prev=False, out=None, workspace=None, bind=False):
     """(dx [B,T,C], dmu [M,C], dx_prev [B,C] or None), float32, for L = sum(gout * token_shift(mu, x, x_prev)).
 
     gout [M, B, T, C] has x's dtype.  dx_prev is computed when want_dx_prev
@@ -402,11 +430,9 @@ def token_shift_backward(mu, x, gout, *, x_prev=None, want_dx_prev=False, out=No
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
-    st = L.lib().wkv_token_shift_backward(B, T, C, M, _DT[x.dtype], _p(mu), _p(x), _p(x_prev), _p(gout), _p(dx),
-                                          _p(dmu), _p(dxp), _p(workspace),
-                                          workspace.numel() * workspace.element_size(), _stream(dev))
-    L.check("wkv_token_shift_backward", st)
-    return dx, dmu, dxp
+    args = (B, T, C, M, _DT[x.dtype], _p(mu), _p(x), _p(x_prev), _p(gout), _p(dx), _p(dmu), _p(dxp),
+            _p(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    return _launch(bind, "wkv_token_shift_backward", L.lib().wkv_token_shift_backward, args, (dx, dmu, dxp), locals())
 
 
 class TokenShiftFunction(torch.autograd.Function):
@@ -440,7 +466,7 @@ def new_wkv5_ckpt(B: int, T: int, H: int, device) -> torch.Tensor:
     return torch.empty(max(wkv5_ckpt_bytes(B, T, H), 1), dtype=torch.uint8, device=device)
 
 
-def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None, workspace=None, split=True):
+def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None, workspace=None, split=True, bind=False):
     """RWKV-5 matrix-state WKV: o [B, T, C] float32 from w, u [H, 64] float32 and
     r, k, v [B, T, C] bfloat16 (C = 64 H).  state_in: [B, H, 64, 64] float32 or
     None (zero).  state_out: tensor to receive the final state (may be
@@ -475,15 +501,14 @@ def wkv5_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
     nws = int(L.lib().wkv5_forward_workspace_bytes(B, T, H, 64)) if split else 0
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
-    st = L.lib().wkv5_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
-                              _p(state_out), _p(ckpt), _p(workspace),
-                              0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
-    L.check("wkv5_forward", st)
-    return (out, state_out) if return_state else out
+    args = (B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in), _p(state_out),
+            _p(ckpt), _p(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(dev))
+    return _launch(bind, "wkv5_forward", L.lib().wkv5_forward, args, (out, state_out) if return_state else out, locals())
 
 
 def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, ckpt=None,
-                  workspace=None, split=True):
+                  workspace=None, split=True, bind=False):
     """Gradients of sum <go, o> + <grad_state_out, S_T> for
     (o, S_T) = wkv5_forward(w, u, r, k, v, state_in=state_in, return_state=True):
     returns (dr, dk, dv [B, T, C] float32, dw, du [H, 64] float32 summed over
@@ -522,11 +547,10 @@ def wkv5_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
     # without split the call is told only the unsplit size, so it never splits
     wsz = workspace.numel() * workspace.element_size() if split else nbytes
-    st = lib.wkv5_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
-                           _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace),
-                           wsz, _stream(dev))
-    L.check("wkv5_backward", st)
-    return dr, dk, dv, dw, du, ds
+    args = (B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
+            _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace), wsz,
+            _stream(dev))
+    return _launch(bind, "wkv5_backward", lib.wkv5_backward, args, (dr, dk, dv, dw, du, ds), locals())
 
 
 class Wkv5Function(torch.autograd.Function):
@@ -550,7 +574,7 @@ class Wkv5Function(torch.autograd.Function):
         return dw, du, dr.to(r.dtype), dk.to(k.dtype), dv.to(v.dtype), ds
 
 
-def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None, workspace=None, split=True):
+def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=False, out=None, ckpt=None, workspace=None, split=True, bind=False):
     """RWKV-6 matrix-state WKV with per-token decay: o [B, T, C] float32 from
     w [B, T, C] float32 rates (>= 0), u [H, 64] float32 and r, k, v [B, T, C]
     bfloat16 (C = 64 H); state handling, ckpt, workspace and split as wkv5_forward."""
@@ -580,15 +604,14 @@ def wkv6_forward(w, u, r, k, v, *, state_in=None, state_out=None, return_state=F
     nws = int(L.lib().wkv6_forward_workspace_bytes(B, T, H, 64)) if split else 0
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
-    st = L.lib().wkv6_forward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in),
-                              _p(state_out), _p(ckpt), _p(workspace),
-                              0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev))
-    L.check("wkv6_forward", st)
-    return (out, state_out) if return_state else out
+    args = (B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(out), _p(state_in), _p(state_out),
+            _p(ckpt), _p(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(dev))
+    return _launch(bind, "wkv6_forward", L.lib().wkv6_forward, args, (out, state_out) if return_state else out, locals())
 
 
 def wkv6_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need_state_grad=False, ckpt=None,
-                  workspace=None, split=True):
+                  workspace=None, split=True, bind=False):
     """Gradients of sum <go, o> + <grad_state_out, S_T> for
     (o, S_T) = wkv6_forward(w, u, r, k, v, state_in=state_in, return_state=True):
     returns (dr, dk, dv, dw [B, T, C] float32 (dw per token), du [H, 64]
@@ -624,11 +647,10 @@ def wkv6_backward(w, u, r, k, v, go, *, state_in=None, grad_state_out=None, need
         raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
     # without split the call is told only the unsplit size, so it never splits
     wsz = workspace.numel() * workspace.element_size() if split else nbytes
-    st = lib.wkv6_backward(B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
-                           _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace),
-                           wsz, _stream(dev))
-    L.check("wkv6_backward", st)
-    return dr, dk, dv, dw, du, ds
+    args = (B, T, H, 64, L.WKV_BF16, _p(w), _p(u), _p(r), _p(k), _p(v), _p(go), _p(state_in),
+            _p(grad_state_out), _p(dr), _p(dk), _p(dv), _p(dw), _p(du), _p(ds), _p(ckpt), _p(workspace), wsz,
+            _stream(dev))
+    return _launch(bind, "wkv6_backward", lib.wkv6_backward, args, (dr, dk, dv, dw, du, ds), locals())
 
 
 class Wkv6Function(torch.autograd.Function):
