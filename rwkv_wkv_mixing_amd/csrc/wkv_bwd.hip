@@ -389,6 +389,10 @@ struct Seed {
     int s = 0;
 };
 
+// Largest scale step of the backward's fast path (Span::recompute): keys then weigh at most 2^60,
+// e^u at most 2^58 more, and the span's sums of key weights at most 17 * 2^60, inside float32.
+constexpr int kMaxShift = 60;
+
 template <typename TIn, int L, bool Gated>
 struct Span {
     float gpi[L], gvy[L], gr[L], grpd[L], e[L], vm[L], ld[L];
@@ -415,37 +419,52 @@ struct Span {
         x0.b = in.b0;
         x0.m = in.b0 > 0.f ? in.a0 / in.b0 : 0.f;
         // fixed span scale: the larger of the history level and the largest key
-        float kmax = -INFINITY;
+        float kmax = -INFINITY, kmin = INFINITY;
 #pragma unroll
-        for (int j = 0; j < L; ++j) kmax = fmaxf(kmax, in.kv.k(j));
+        for (int j = 0; j < L; ++j) {
+            kmax = fmaxf(kmax, in.kv.k(j));
+            kmin = fminf(kmin, in.kv.k(j));
+        }
         const int lvl0 = x0.b > 0.f ? x0.s + __builtin_amdgcn_frexp_expf(x0.b) : kSEmpty;
         const int sc = max(lvl0, key_split(kmax).n);
+        // Every denominator of the fast path is at least min_j e^{k_j} min(e^u, 1) (D_t >=
+        // e^{u+k_t}, B_t >= e^{k_t}).  Where that bound lies more than 2^96 below 2^sc (a key spike
+        // beside a very small key in a fast-decaying channel) the lane carries its span 2^shift
+        // higher, at the scale so = sc - shift: each key weight is the same exact fraction times an
+        // exact power of two, and the denominators stay above kTiny.  Otherwise the wave would take
+        // the general path, whose per-token recomputation re-reads the span's inputs O(L^2) times:
+        // two such waves among 32,768 held a whole call back by a fifth.  Only where every key
+        // weight is a normal float at 2^sc already (the shift is then exact, and no key that the
+        // wider range would hold has been flushed to zero); wider spans keep the general path.
+        const float xlo = fmaf(kmin, kL2E, -static_cast<float>(sc));
+        const float lo = xlo + fminf(ch.u2, 0.f);
+        const int shift = (lo < -96.f) & (xlo >= -125.f) ? min(static_cast<int>(-96.f - lo) + 1, kMaxShift) : 0;
         const bool keys_ok = kmax * kL2E < kNMax;
         fast = fast_out && __all(keys_ok);
         Psum = Gs = Js = Gps = Jps = 0;
         du = 0.f;
-        so = sc;
+        so = sc - shift;
         if (fast) {
             float m = x0.m;
-            float bb = ldx(x0.b, x0.s - sc);
+            float bb = ldx(x0.b, x0.s - so);
             float dmin = INFINITY;  // smallest denominator (D_t and B_t) used
             const float scf = static_cast<float>(sc);
             acc_t dp = 1;
             float xg = 0.f, xb = 0.f;  // Inj: gA and gB at the span's scale
             if (Inj && tcut > 0) {
-                xg = ldx(sd.ga, sc - sd.s);
-                xb = ldx(sd.gb, sc - sd.s);
+                xg = ldx(sd.ga, so - sd.s);
+                xb = ldx(sd.gb, so - sd.s);
             }
 #pragma unroll
             for (int j = 0; j < L; ++j) {
-                // e = e^k / 2^sc.  For the key that sets the scale fma(k, log2 e,
+                // e = e^k / 2^so.  For the key that sets the scale fma(k, log2 e,
                 // -sc) is exactly the key split's fraction, so the weight is
-                // bit-equal to the forward's; a key D binades below the span's
+                // bit-equal to the forward's (times 2^shift); a key D binades below the span's
                 // scale is rounded to ~D 2^-24 relative while its share of every
                 // denominator here is ~2^-D (the forward's saved states, where
                 // such a key might dominate later, use the exact split)
                 const float kj = in.kv.k(j);
-                const float ej = ex2(fmaf(kj, kL2E_lo, fmaf(kj, kL2E, -scf)));
+                const float ej = ldx(ex2(fmaf(kj, kL2E_lo, fmaf(kj, kL2E, -scf))), shift);
                 const float E = ej * eu;
                 const float den = bb + E;
                 dmin = fminf(dmin, den);

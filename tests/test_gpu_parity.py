@@ -157,6 +157,34 @@ def test_fast_decay_after_key_spike(C):
     check_fwd(p, run_fwd(p), stress=True)
 
 
+@pytest.mark.parametrize("C", [64, None])
+def test_backward_span_with_opposite_key_spikes(C):
+    """A key of -40 and a key of +40 inside one 16-token span of a fast-decaying channel (w = 2-5
+    per token): the span's smallest denominator lies about 2^120 below the scale of its largest
+    key, so the backward carries that span at a shifted scale (exact powers of two) instead of
+    its general path.  Spikes at every offset pair inside a span, every channel; bf16 inputs.
+    C = 64 runs the time-split backward, C = 64 ncu + 24 the whole-tile one.  Backward bound."""
+    if C is None:
+        C = 64 * torch.cuda.get_device_properties(0).multi_processor_count + 24
+    B = 1 if C == 64 else 2
+    p = W.make_problem(B, 512, C, dtype="bf16", seed=41, name=f"opposite spikes C={C}")
+    p.w[:] = np.linspace(2.0, 5.0, C).astype(np.float32)
+    p.u[:] = np.float32(-3.0)
+    k = p.k.copy()
+    for s0 in range(0, 512, 16):  # span s0: -40 at offset a, +40 at offset b, (a, b) varying by span
+        a, b = (s0 // 16) % 16, (s0 // 16 * 7 + 3) % 16
+        if a == b:
+            b = (b + 1) % 16
+        k[:, s0 + a, :] = -40.0
+        k[:, s0 + b, :] = 40.0 - (np.arange(C) % 3).astype(np.float32)
+    from rwkv_wkv_mixing_amd.workloads import bf16_round
+
+    p.k_bits, p.k = bf16_round(k)
+    print(f"case {p.name}", flush=True)
+    check_fwd(p, run_fwd(p), stress=True)
+    check_bwd(p, run_bwd(p))
+
+
 def test_zero_length_sequences():
     O = ops()
     w = torch.ones(5, device=DEV)
