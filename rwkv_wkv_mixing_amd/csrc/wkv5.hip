@@ -126,8 +126,10 @@ __device__ __forceinline__ s4 col_tr(const uint16_t (*X)[kN], int tb, int c0, in
 }
 
 // kOut = false: a state-only pass (no outputs, only the chunk-start states in P.ckpt
-// and the final state), as the backward needs.
-template <bool kOut>
+// and the final state), as the backward needs.  kLast: the call is its inputs' last reader (an
+// output pass saving no chunk-start states: no backward follows to read r, k, v again), so they
+// are staged non-temporal.
+template <bool kOut, bool kLast = false>
 __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
     __shared__ Wkv5Shared sm;
     const int lane = threadIdx.x & 63;
@@ -179,7 +181,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv5_fwd_kernel(Wkv5Args P) {
                 const int q = (lane % 8) ^ (row & 7);  // the global chunk that lands in slot lane % 8
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, kStageKeep);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, kLast ? kStageLast : kStageKeep);
             }
         }
     };
@@ -368,7 +370,8 @@ __device__ __forceinline__ f4 exp2_neg4(f4 x) {  // 2^{-x}, elementwise: e^{-x} 
 }
 
 // kOut = false: a state-only pass (the chunk-start states into P.ckpt and the final state).
-template <bool kOut>
+// kLast as for RWKV-5.
+template <bool kOut, bool kLast = false>
 __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
     __shared__ Wkv6Shared sm;
     // lane coordinates; made opaque at the top of every chunk so that lane-dependent LDS
@@ -414,7 +417,7 @@ __global__ void __launch_bounds__(64 * kWaves5, 2) wkv6_fwd_kernel(Wkv6Args P) {
                 const int q = (lane % 8) ^ (row & 7);
                 const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(row) * C) * 2 + q * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, kStageKeep);
+                    rs, (__attribute__((address_space(3))) void*)&sm.in[buf][a][16 * wv + 8 * i][0], 16, voff, 0, 0, kLast ? kStageLast : kStageKeep);
             }
         }
     };
@@ -1992,7 +1995,10 @@ hipError_t launch_wkv6_fwd(const Wkv6Args& a, hipStream_t stream) {
         hipLaunchKernelGGL(wkv6_fwd_kernel<false>, grid, dim3(64 * kWaves5), 0, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(wkv6_fwd_kernel<true>, grid, dim3(64 * kWaves5), 0, stream, a);
+    if (a.ckpt == nullptr)  // no backward will read the inputs again
+        hipLaunchKernelGGL((wkv6_fwd_kernel<true, true>), grid, dim3(64 * kWaves5), 0, stream, a);
+    else
+        hipLaunchKernelGGL((wkv6_fwd_kernel<true, false>), grid, dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -2003,7 +2009,10 @@ hipError_t launch_wkv5_fwd(const Wkv5Args& a, hipStream_t stream) {
         hipLaunchKernelGGL(wkv5_fwd_kernel<false>, grid, dim3(64 * kWaves5), 0, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(wkv5_fwd_kernel<true>, grid, dim3(64 * kWaves5), 0, stream, a);
+    if (a.ckpt == nullptr)  // no backward will read the inputs again
+        hipLaunchKernelGGL((wkv5_fwd_kernel<true, true>), grid, dim3(64 * kWaves5), 0, stream, a);
+    else
+        hipLaunchKernelGGL((wkv5_fwd_kernel<true, false>), grid, dim3(64 * kWaves5), 0, stream, a);
     return hipGetLastError();
 }
 

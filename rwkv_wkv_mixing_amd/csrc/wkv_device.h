@@ -107,10 +107,11 @@ __device__ __forceinline__ void buf_store(float v, Rsrc r, uint32_t voff, uint32
 }
 
 // Cache policies of the buffer -> LDS copies of streamed inputs.  kStageKeep
-// (the default policy) for inputs that a later call reads again: a forward's
-// inputs, which the backward of the same batch reads next and finds partly in
-// the Infinity Cache.  kStageLast (non-temporal) for the last read of an input:
-// the backwards' inputs and saved states.  Measured at B=8 T=1024 C=4096 bf16,
+// (the default policy) for inputs that a later call reads again: the inputs of
+// a forward that saves states for its backward, which reads them next and finds
+// part of them in the Infinity Cache.  kStageLast (non-temporal) for the last
+// read of an input: the backwards' inputs and saved states, and the inputs of a
+// forward that saves no states.  Measured at B=8 T=1024 C=4096 bf16,
 // forward then backward over three rotated operand sets, builds interleaved in
 // one process: backward 100.2 -> 94.8 us with its copies non-temporal; a
 // non-temporal forward as well left that backward 107.5 us (the RWKV-5

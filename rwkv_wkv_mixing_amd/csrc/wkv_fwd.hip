@@ -548,7 +548,9 @@ struct TileWork {
     }
 };
 
-template <int L, int W, bool Gated>
+// Last: no saved states are written, so no backward will read k, v again: they are staged
+// non-temporal (kStageLast); a forward saving states for its backward keeps the default policy.
+template <int L, int W, bool Gated, bool Last>
 __global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
     __shared__ TileShared<W> sm;
     __shared__ FwdStage<L, W> stage;
@@ -577,8 +579,8 @@ __global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
 
     {
         const FwdGeo g0 = fwd_geo<uint16_t, L, W>(P, b, c, cok, 0, wave);
-        stage_rows<uint16_t, L, kStageKeep>(g0.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
-        stage_rows<uint16_t, L, kStageKeep>(g0.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
+        stage_rows<uint16_t, L, Last ? kStageLast : kStageKeep>(g0.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
+        stage_rows<uint16_t, L, Last ? kStageLast : kStageKeep>(g0.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
     }
     for (int64_t blk = 0; blk < P.nblocks; ++blk) {
         const FwdGeo g = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk, wave);
@@ -596,8 +598,8 @@ __global__ void __launch_bounds__(64 * W, 4) fwd_tile_kernel(FwdChunk P) {
         wait_lds_reads();
         if (blk + 1 < P.nblocks) {
             const FwdGeo gn = fwd_geo<uint16_t, L, W>(P, b, c, cok, blk + 1, wave);
-            stage_rows<uint16_t, L, kStageKeep>(gn.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
-            stage_rows<uint16_t, L, kStageKeep>(gn.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
+            stage_rows<uint16_t, L, Last ? kStageLast : kStageKeep>(gn.rk, stage.x[wave][0], int64_t{wave} * L, c0, P.C, lane);
+            stage_rows<uint16_t, L, Last ? kStageLast : kStageKeep>(gn.rv, stage.x[wave][1], int64_t{wave} * L, c0, P.C, lane);
         }
         TileWork<L> tw;
         tw.local(kv, g, ch, eu, d, lane_ok);
@@ -727,10 +729,15 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
         if (WKV_FWD_TILE && l.ntiles >= 2 * static_cast<int64_t>(ncu) && a.C % 8 == 0 && a16(a.k) && a16(a.v)) {
             P.nblocks = (a.T + kTileL * kTileW - 1) / (kTileL * kTileW);
             const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * kTileW);
-            if (P.r != nullptr)
-                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, true>), grid, block, 0, stream, P);
+            const bool last = P.ckpt == nullptr;
+            if (P.r != nullptr && last)
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, true, true>), grid, block, 0, stream, P);
+            else if (P.r != nullptr)
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, true, false>), grid, block, 0, stream, P);
+            else if (last)
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, false, true>), grid, block, 0, stream, P);
             else
-                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, false>), grid, block, 0, stream, P);
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, false, false>), grid, block, 0, stream, P);
             return hipGetLastError();
         }
     }
