@@ -85,6 +85,15 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// A load with the non-temporal hint (NT) or the default policy.  The backward is the last reader
+// of x and of the output gradients, so it reads them non-temporal (85.0 -> 81.7 us at B=8 T=1024
+// C=4096 M=3, bf16); the forward's x keeps the default policy, since the backward reads it again.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // V elements of TIn widened to float32 (bf16: exact) and narrowed back
 // (bf16: round to nearest even, one v_cvt_pk_bf16_f32 per pair).
 template <typename TIn, int V>
@@ -92,8 +101,9 @@ struct Pack;
 
 template <>
 struct Pack<float, 4> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const float* __restrict__ p, int64_t i, float (&f)[4]) {
-        const f4 r = *reinterpret_cast<const f4*>(p + i);
+        const f4 r = ld<NT>(reinterpret_cast<const f4*>(p + i));
         f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
     }
     static __device__ __forceinline__ void store(float* __restrict__ p, int64_t i, const float (&f)[4]) {
@@ -104,7 +114,8 @@ struct Pack<float, 4> {
 
 template <>
 struct Pack<float, 1> {
-    static __device__ __forceinline__ void load(const float* __restrict__ p, int64_t i, float (&f)[1]) { f[0] = p[i]; }
+    template <bool NT = false>
+    static __device__ __forceinline__ void load(const float* __restrict__ p, int64_t i, float (&f)[1]) { f[0] = ld<NT>(p + i); }
     static __device__ __forceinline__ void store(float* __restrict__ p, int64_t i, const float (&f)[1]) {
         st_out(f[0], p + i);
     }
@@ -112,8 +123,9 @@ struct Pack<float, 1> {
 
 template <>
 struct Pack<uint16_t, 8> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t i, float (&f)[8]) {
-        const u4 r = *reinterpret_cast<const u4*>(p + i);
+        const u4 r = ld<NT>(reinterpret_cast<const u4*>(p + i));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             f[2 * q] = __uint_as_float(r[q] << 16);
@@ -134,8 +146,9 @@ struct Pack<uint16_t, 8> {
 template <>
 struct Pack<uint16_t, 4> {
     typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t i, float (&f)[4]) {
-        const u2 r = *reinterpret_cast<const u2*>(p + i);
+        const u2 r = ld<NT>(reinterpret_cast<const u2*>(p + i));
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             f[2 * q] = __uint_as_float(r[q] << 16);
@@ -155,8 +168,9 @@ struct Pack<uint16_t, 4> {
 
 template <>
 struct Pack<uint16_t, 1> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t i, float (&f)[1]) {
-        f[0] = __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+        f[0] = __uint_as_float(static_cast<uint32_t>(ld<NT>(p + i)) << 16);
     }
     static __device__ __forceinline__ void store(uint16_t* __restrict__ p, int64_t i, const float (&f)[1]) {
         st_out(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f[0])), p + i);
@@ -292,22 +306,22 @@ __global__ __launch_bounds__(kThreads) void shift_bwd_kernel(ShiftArgs P) {
 #pragma unroll
         for (int j = 0; j < M; ++j) {
             if (tail) {
-                Pack<TIn, V>::load(g, j * N + base + w.n * P.C, gn[j]);
+                Pack<TIn, V>::template load<true>(g, j * N + base + w.n * P.C, gn[j]);
             } else {
 #pragma unroll
                 for (int e = 0; e < V; ++e) gn[j][e] = 0.f;
             }
         }
-        Pack<TIn, V>::load(x, base + (w.n - 1) * P.C, xc);
+        Pack<TIn, V>::template load<true>(x, base + (w.n - 1) * P.C, xc);
         auto token = [&](int i) {  // token t0 + i, walking backwards
             float xp[V], gc[M][V], dx[V];
             if (i > 0) {
-                Pack<TIn, V>::load(x, base + (i - 1) * P.C, xp);
+                Pack<TIn, V>::template load<true>(x, base + (i - 1) * P.C, xp);
             } else {
                 load_prev<TIn, V>(P, w, xp);
             }
 #pragma unroll
-            for (int j = 0; j < M; ++j) Pack<TIn, V>::load(g, j * N + base + i * P.C, gc[j]);
+            for (int j = 0; j < M; ++j) Pack<TIn, V>::template load<true>(g, j * N + base + i * P.C, gc[j]);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 float s = 0.f;
