@@ -952,18 +952,22 @@ def bench_stream(args):
     # walking B=8 T=1024 C=4096 in blocks, bf16 inputs staged through LDS, float32 outputs per lane
     L.wkv_tile_pattern_launch.restype = ctypes.c_int
     L.wkv_tile_pattern_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     B, T, C = 8, 1024, 4096
     tiled = []
-    for nr, nw, what in ((2, 1, "forward: k, v in, y out"), (3, 2, "backward: k, v, gy in, dk, dv out")):
-        sets = [([torch.zeros(B * T * C, dtype=torch.bfloat16, device=dev) for _ in range(nr)],
-                 [torch.empty(B * T * C, dtype=torch.float32, device=dev) for _ in range(nw)]) for _ in range(3)]
+    # the dense layout (rows C elements apart), then the same walk over rows 64 elements further
+    # apart: what the power-of-two row stride alone costs
+    for nr, nw, what, ld in ((2, 1, "forward: k, v in, y out", C), (3, 2, "backward: k, v, gy in, dk, dv out", C),
+                             (2, 1, "forward, rows C + 64 apart", C + 64),
+                             (3, 2, "backward, rows C + 64 apart", C + 64)):
+        sets = [([torch.zeros(B * T * ld, dtype=torch.bfloat16, device=dev) for _ in range(nr)],
+                 [torch.empty(B * T * ld, dtype=torch.float32, device=dev) for _ in range(nw)]) for _ in range(3)]
         ptrs = [((ctypes.c_void_p * 4)(*[t.data_ptr() for t in ins]), (ctypes.c_void_p * 4)(*[t.data_ptr() for t in outs]))
                 for ins, outs in sets]
 
         def tlaunch(i):
             ins, outs = ptrs[i % len(ptrs)]
-            rc = L.wkv_tile_pattern_launch(nr, nw, ins, outs, B, T, C, sptr)
+            rc = L.wkv_tile_pattern_launch(nr, nw, ins, outs, B, T, C, ld, sptr)
             if rc != 0:
                 raise RuntimeError(f"wkv_tile_pattern_launch failed: {rc}")
 
@@ -977,7 +981,7 @@ def bench_stream(args):
         torch.cuda.synchronize()
         us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
         nbytes = B * T * C * (2 * nr + 4 * nw)
-        tiled.append({"read": nr, "write": nw, "what": what, "bytes": nbytes, "us": round(us, 2),
+        tiled.append({"read": nr, "write": nw, "what": what, "row_stride": ld, "bytes": nbytes, "us": round(us, 2),
                       "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
         print(f"tiled {what}: {tiled[-1]}", file=sys.stderr, flush=True)

@@ -72,7 +72,7 @@ typedef void (*Kern)(StreamArgs);
 struct TileArgs {
     const uint16_t* in[4];
     float* out[4];
-    int B, T, C;
+    int B, T, C, ld;
 };
 
 template <int NR, int NW, int U>
@@ -105,7 +105,9 @@ Kern select(int nr, int nw, int u, bool nt) {
 // 64-channel tile of one batch row walks the sequence in blocks of W x L tokens.  Each wave copies
 // its L rows of the NR bf16 inputs into LDS by 16-byte buffer -> LDS copies (issued once the
 // previous block is read, as the kernels do), reads its channel back, and stores NW float32
-// outputs per token, one 4-byte store per lane.  [B, T, C] arrays, channel fastest.
+// outputs per token, one 4-byte store per lane.  [B, T, C] arrays, channel fastest, rows ld >= C
+// elements apart (ld = C is the dense layout the WKV calls take; a larger ld shows what the row
+// stride alone costs).
 using Rsrc = __amdgpu_buffer_rsrc_t;
 __device__ __forceinline__ Rsrc rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
@@ -120,14 +122,14 @@ __global__ void __launch_bounds__(64 * W) tile_pattern_kernel(TileArgs a) {
     const int b = blockIdx.x / nct, c0 = (blockIdx.x % nct) * 64;
     const int nblk = a.T / (L * W);
     auto stage = [&](int blk) {
-        const int64_t row0 = (static_cast<int64_t>(b) * a.T + static_cast<int64_t>(blk) * L * W + wave * L) * a.C;
+        const int64_t row0 = (static_cast<int64_t>(b) * a.T + static_cast<int64_t>(blk) * L * W + wave * L) * a.ld;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const Rsrc rs = rsrc(a.in[r] + row0, static_cast<uint32_t>(L * a.C * 2));
+            const Rsrc rs = rsrc(a.in[r] + row0, static_cast<uint32_t>(L * a.ld * 2));
 #pragma unroll
             for (int i = 0; i < L / 8; ++i) {
                 const int j = i * 8 + lane / 8;
-                const uint32_t off = static_cast<uint32_t>((j * a.C + c0) * 2 + (lane % 8) * 16);
+                const uint32_t off = static_cast<uint32_t>((j * a.ld + c0) * 2 + (lane % 8) * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&st[wave][r][i * 8][0],
                                                          16, off, 0, 0, 0);
             }
@@ -146,15 +148,15 @@ __global__ void __launch_bounds__(64 * W) tile_pattern_kernel(TileArgs a) {
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (blk + 1 < nblk) stage(blk + 1);
-        const int64_t row0 = (static_cast<int64_t>(b) * a.T + static_cast<int64_t>(blk) * L * W + wave * L) * a.C;
+        const int64_t row0 = (static_cast<int64_t>(b) * a.T + static_cast<int64_t>(blk) * L * W + wave * L) * a.ld;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const Rsrc ro = rsrc(a.out[w] + row0, static_cast<uint32_t>(L * a.C * 4));
+            const Rsrc ro = rsrc(a.out[w] + row0, static_cast<uint32_t>(L * a.ld * 4));
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 acc = fmaf(acc, 0.5f, x[j]);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ro, static_cast<uint32_t>((c0 + lane) * 4),
-                                                      j * a.C * 4, 3);
+                                                      j * a.ld * 4, 3);
             }
         }
     }
@@ -164,18 +166,20 @@ __global__ void __launch_bounds__(64 * W) tile_pattern_kernel(TileArgs a) {
 
 // Launch one pass of the tile kernels' access order: (nr, nw) = (2, 1) as the forward (k, v in, y
 // out; 8 waves x 16 tokens per block) or (3, 2) as the backward (k, v, gy in, dk, dv out; 4 waves x
-// 16 tokens).  in[]: bf16 [B, T, C]; out[]: float32 [B, T, C].  Needs C a multiple of 64 and T of
-// the block length (128 or 64).  Returns 0, -1 for an unsupported shape, or the HIP error code.
+// 16 tokens).  in[]: bf16 [B, T, ld]; out[]: float32 [B, T, ld], of which channels 0 .. C - 1 are
+// read and written.  Needs C a multiple of 64, ld >= C and T a multiple of the block length (128 or
+// 64).  Returns 0, -1 for an unsupported shape, or the HIP error code.
 extern "C" int wkv_tile_pattern_launch(int nr, int nw, const void* const* in, void* const* out, int B, int T, int C,
-                                       void* stream) {
+                                       int ld, void* stream) {
     TileArgs a{};
     for (int r = 0; r < nr && r < 4; ++r) a.in[r] = static_cast<const uint16_t*>(in[r]);
     for (int w = 0; w < nw && w < 4; ++w) a.out[w] = static_cast<float*>(out[w]);
     a.B = B;
     a.T = T;
     a.C = C;
+    a.ld = ld;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (B <= 0 || C <= 0 || C % 64 != 0 || static_cast<int64_t>(T) * C * 4 > 0x7fffffff) return -1;
+    if (B <= 0 || C <= 0 || C % 64 != 0 || ld < C || static_cast<int64_t>(T) * ld * 4 > 0x7fffffff) return -1;
     const dim3 grid(static_cast<unsigned>(B * (C / 64)));
     if (nr == 2 && nw == 1 && T > 0 && T % 128 == 0)
         hipLaunchKernelGGL((tile_pattern_kernel<2, 1, 8, 16>), grid, dim3(512), 0, s, a);
