@@ -158,6 +158,33 @@ def config4(seed=0) -> WkvProblem:
                         with_gy=False, name="wkv4 fp32 B=1 T=32768 C=4096")
 
 
+def large_bf16_torch(B, T, C, *, seed=0, w_range=(-6.0, 1.5), spike_frac=0.01, spike_range=(20.0, 40.0),
+                     device="cuda:0"):
+    """The bf16 workload's distributions (config 3: w = exp(U(lo, hi)), u, k, v, gy ~ N(0, 1), a
+    fraction of k set to +-U(20, 40)) at sizes too large to draw on the host: w, u [C] float32 from
+    numpy's generator (as make_problem), k, v, gy [B, T, C] bf16 drawn on ``device`` with torch's
+    seeded Philox generator, spikes applied before the bf16 rounding.  Deterministic per seed."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(w_range[0], w_range[1], C)).astype(np.float32)
+    u = _normal(rng, 1.0, C)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 17)
+    out = []
+    for name in ("k", "v", "gy"):
+        x = torch.randn((B, T, C), generator=g, device=device, dtype=torch.float32)
+        if name == "k" and spike_frac > 0.0:
+            mask = torch.rand((B, T, C), generator=g, device=device) < spike_frac
+            mag = torch.empty((B, T, C), device=device).uniform_(spike_range[0], spike_range[1], generator=g)
+            sign = torch.where(torch.rand((B, T, C), generator=g, device=device) < 0.5, -1.0, 1.0)
+            x = torch.where(mask, sign * mag, x)
+            del mask, mag, sign
+        out.append(x.to(torch.bfloat16))
+        del x
+    return w, u, out[0], out[1], out[2]
+
+
 @dataclass
 class DecodeProblem:
     """Recurrent-mode workload: L layers x B streams x C channels.
