@@ -371,6 +371,32 @@ def wkv5_go(p: Wkv5Problem, *, seed=1, std=1.0) -> tuple[np.ndarray, np.ndarray]
     return bf16_round(_normal(rng, std, (p.B, p.T, p.H * 64)))
 
 
+def large_matrix_torch(gen, B, T, H, *, seed=0, rate_range=(-4.0, 1.5), spread=0.5, device="cuda:0"):
+    """make_wkv5 (gen 5) or make_wkv6 (gen 6) inputs, with go ~ N(0, 1), at sizes too large to draw
+    on the host.  Host (numpy, as those generators): the log-rates per (head, key channel) ~ U(lo,
+    hi) (gen 5: w = their exp, [H, 64]; gen 6: the per-channel base) and u ~ N(0, 1) [H, 64].
+    Device (torch's seeded Philox generator): r, k, v, go ~ N(0, 1) [B, T, 64 H] rounded to bf16,
+    and for gen 6 the per-token rates w = exp(base + spread N(0, 1)) [B, T, 64 H] float32.
+    Returns (w, u, r, k, v, go, base) with w a numpy array (gen 5) or a device tensor (gen 6) and
+    base the gen-6 log-rates (None for gen 5)."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    N = 64
+    lw = rng.uniform(rate_range[0], rate_range[1], (H, N))
+    u = _normal(rng, 1.0, (H, N))
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 29)
+    shape = (B, T, H * N)
+    r, k, v, go = (torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    if gen == 5:
+        return np.exp(lw).astype(np.float32), u, r, k, v, go, None
+    base = torch.from_numpy(lw.reshape(-1)).to(device=device, dtype=torch.float32)
+    w = torch.randn(shape, generator=g, device=device, dtype=torch.float32).mul_(spread).add_(base).exp_()
+    return w, u, r, k, v, go, lw.reshape(-1)
+
+
 def wkv5_config(seed=0) -> Wkv5Problem:
     """A 7B-shaped layer in RWKV-5 form: B=8, T=1024, C=4096 as 64 heads of 64."""
     return make_wkv5(8, 1024, 64, seed=seed, name="wkv5 bf16 B=8 T=1024 H=64 N=64")
