@@ -672,10 +672,17 @@ constexpr int kFwdW = WKV_FWD_W;  // waves per workgroup
 #define WKV_FWD_TILE_L 16
 #endif
 #ifndef WKV_FWD_TILE_W
-#define WKV_FWD_TILE_W 8
+#define WKV_FWD_TILE_W 4
+#endif
+#ifndef WKV_FWD_TILE_W_LAST
+#define WKV_FWD_TILE_W_LAST 8
 #endif
 constexpr int kTileL = WKV_FWD_TILE_L;  // whole-tile kernel: tokens per wave
-constexpr int kTileW = WKV_FWD_TILE_W;  // whole-tile kernel: waves per workgroup
+// whole-tile kernel: waves per workgroup, for a forward that saves the backward's states (a training
+// step: 4-wave workgroups make the following backward 1.5 % faster at B=8 T=1024 C=4096, with the
+// forward itself unchanged) and for one that saves none (8 waves: 4 % faster there)
+constexpr int kTileW = WKV_FWD_TILE_W;
+constexpr int kTileWLast = WKV_FWD_TILE_W_LAST;
 static_assert(kFwdL % kCkptLen == 0 && kTileL % kCkptLen == 0, "sub-chunks must start on saved-state boundaries");
 
 struct FwdLayout {
@@ -727,15 +734,16 @@ hipError_t launch_fwd_chunk_t(const FwdArgs& a, hipStream_t stream) {
     (void)a16;
     if constexpr (sizeof(TIn) == 2) {
         if (WKV_FWD_TILE && l.ntiles >= 2 * static_cast<int64_t>(ncu) && a.C % 8 == 0 && a16(a.k) && a16(a.v)) {
-            P.nblocks = (a.T + kTileL * kTileW - 1) / (kTileL * kTileW);
-            const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * kTileW);
             const bool last = P.ckpt == nullptr;
+            const int tw = last ? kTileWLast : kTileW;
+            P.nblocks = (a.T + kTileL * tw - 1) / (kTileL * tw);
+            const dim3 grid(static_cast<unsigned>(l.ntiles)), block(64 * tw);
             if (P.r != nullptr && last)
-                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, true, true>), grid, block, 0, stream, P);
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileWLast, true, true>), grid, block, 0, stream, P);
             else if (P.r != nullptr)
                 hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, true, false>), grid, block, 0, stream, P);
             else if (last)
-                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, false, true>), grid, block, 0, stream, P);
+                hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileWLast, false, true>), grid, block, 0, stream, P);
             else
                 hipLaunchKernelGGL((fwd_tile_kernel<kTileL, kTileW, false, false>), grid, block, 0, stream, P);
             return hipGetLastError();
