@@ -42,7 +42,7 @@ namespace {
 #define WKV_SHIFT_FWD_VBF 4
 #endif
 #ifndef WKV_SHIFT_BWD_CV
-#define WKV_SHIFT_BWD_CV 32
+#define WKV_SHIFT_BWD_CV 64  // with the non-temporal loads: 76.0 us against 78.2 at 32 (B=8 T=1024 C=4096 M=3)
 #endif
 #ifndef WKV_SHIFT_BWD_RUN
 #define WKV_SHIFT_BWD_RUN 32

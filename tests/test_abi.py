@@ -199,10 +199,11 @@ def shift_bwd(lib, B, T, C, M, dt, mu, x, xp, g, dx, dmu, dxp, ws=None, nws=0):
 
 
 def test_token_shift_workspace_size(lib):
-    # partial sums of dmu: one row per (batch row, block of 256 tokens), M * C floats each
-    assert lib.wkv_token_shift_workspace_bytes(8, 1024, 4096, 3) == 8 * 4 * 3 * 4096 * 4
-    assert lib.wkv_token_shift_workspace_bytes(2, 129, 7, 1) == 2 * 1 * 7 * 4
-    assert lib.wkv_token_shift_workspace_bytes(2, 257, 7, 1) == 2 * 2 * 7 * 4
+    # partial sums of dmu: one row per (batch row, block of 128 tokens), M * C floats each
+    assert lib.wkv_token_shift_workspace_bytes(8, 1024, 4096, 3) == 8 * 8 * 3 * 4096 * 4
+    assert lib.wkv_token_shift_workspace_bytes(2, 128, 7, 1) == 2 * 1 * 7 * 4
+    assert lib.wkv_token_shift_workspace_bytes(2, 129, 7, 1) == 2 * 2 * 7 * 4
+    assert lib.wkv_token_shift_workspace_bytes(2, 257, 7, 1) == 2 * 3 * 7 * 4
     assert lib.wkv_token_shift_workspace_bytes(2, 0, 7, 1) == 0
     assert lib.wkv_token_shift_workspace_bytes(2, 5, 7, 0) == 0   # M out of range
     assert lib.wkv_token_shift_workspace_bytes(2, 5, 7, 5) == 0
